@@ -1,0 +1,131 @@
+"""Seeded synthetic inputs for the Gated DeltaNet mixer.
+
+This module holds only the input recipe (random draws and their shaping); it
+contains none of the method's arithmetic, and both the HIP-path tests and the
+CPU oracle receive the same tensors from it. It imports neither the binding
+nor the oracle.
+
+Recipe (head layout from page "Qwen3.8-Flash-Next 技术总结", section 2.1:
+48 V heads, 16 QK heads, head dim 128):
+  q, k       ~ N(0, 1), then L2-normalised per (token, QK head)
+  v          ~ N(0, 1)
+  log_alpha  = -softplus(N(-2, 1)) per (token, V head)    (alpha in (0, 1))
+  beta       = sigmoid(N(0, 1)) per (token, V head)
+  init state ~ N(0, 0.02^2) per entry, when asked for
+Draws use numpy's default_rng(seed) in float64 in the fixed order
+q, k, v, log_alpha, beta, init; q/k/v are then cast to the requested dtype
+by torch (round to nearest even for bfloat16). log_alpha, beta and states
+are float32.
+"""
+import numpy as np
+import torch
+
+_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _softplus(x):
+    return np.logaddexp(0.0, x)
+
+
+def _unit_rows(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def make_prefill(seed, seq_lens, h_qk, h_v, d, dtype="bf16", init="zeros"):
+    """Packed prefill inputs for sequences of the given lengths.
+
+    init: "zeros" -> init_state None; "randn" -> N(0, 0.02^2) per sequence.
+    Returns a dict of CPU tensors: q, k [T,h_qk,d]; v [T,h_v,d];
+    log_alpha, beta [T,h_v] f32; init_state [N,h_v,d,d] f32 or None;
+    cu_seqlens int32 [N+1].
+    """
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in seq_lens]
+    T = int(sum(lens))
+    tdt = _DTYPES[dtype]
+    q = _unit_rows(rng.standard_normal((T, h_qk, d)))
+    k = _unit_rows(rng.standard_normal((T, h_qk, d)))
+    v = rng.standard_normal((T, h_v, d))
+    la = -_softplus(rng.normal(-2.0, 1.0, (T, h_v)))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((T, h_v))))
+    init_state = None
+    if init == "randn":
+        init_state = torch.from_numpy(
+            rng.normal(0.0, 0.02, (len(lens), h_v, d, d)).astype(np.float32))
+    elif init != "zeros":
+        raise ValueError(init)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return dict(
+        q=torch.from_numpy(q).to(tdt),
+        k=torch.from_numpy(k).to(tdt),
+        v=torch.from_numpy(v).to(tdt),
+        log_alpha=torch.from_numpy(la.astype(np.float32)),
+        beta=torch.from_numpy(beta.astype(np.float32)),
+        init_state=init_state,
+        cu_seqlens=torch.from_numpy(cu),
+    )
+
+
+def make_varlen_lengths(seed, n, lo, hi):
+    """n integer lengths uniform in [lo, hi] (inclusive)."""
+    rng = np.random.default_rng(seed)
+    return [int(x) for x in rng.integers(lo, hi + 1, size=n)]
+
+
+def make_decode(seed, batch, steps, h_qk, h_v, d, dtype="bf16"):
+    """Inputs for `steps` successive single-token decode steps.
+
+    Returns dict: state0 [batch,h_v,d,d] f32 ~ N(0, 0.02^2); and per-step
+    stacks q, k [steps,batch,h_qk,d]; v [steps,batch,h_v,d];
+    log_alpha, beta [steps,batch,h_v] f32.
+    """
+    rng = np.random.default_rng(seed)
+    tdt = _DTYPES[dtype]
+    state0 = rng.normal(0.0, 0.02, (batch, h_v, d, d)).astype(np.float32)
+    q = _unit_rows(rng.standard_normal((steps, batch, h_qk, d)))
+    k = _unit_rows(rng.standard_normal((steps, batch, h_qk, d)))
+    v = rng.standard_normal((steps, batch, h_v, d))
+    la = -_softplus(rng.normal(-2.0, 1.0, (steps, batch, h_v)))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((steps, batch, h_v))))
+    return dict(
+        state0=torch.from_numpy(state0),
+        q=torch.from_numpy(q).to(tdt),
+        k=torch.from_numpy(k).to(tdt),
+        v=torch.from_numpy(v).to(tdt),
+        log_alpha=torch.from_numpy(la.astype(np.float32)),
+        beta=torch.from_numpy(beta.astype(np.float32)),
+    )
+
+
+# The five workloads (sizes as named in the docs). Each entry is the
+# keyword arguments of make_prefill / make_decode.
+WORKLOADS = {
+    "tiny": dict(kind="prefill", seed=1, seq_lens=[64], h_qk=1, h_v=1, d=16,
+                 chunk=16, dtype="f32", init="zeros"),
+    "layer_4k": dict(kind="prefill", seed=2, seq_lens=[4096], h_qk=16, h_v=48,
+                     d=128, chunk=64, dtype="bf16", init="zeros"),
+    "long_64k": dict(kind="prefill", seed=3, seq_lens=[65536], h_qk=16,
+                     h_v=48, d=128, chunk=64, dtype="bf16", init="randn"),
+    "varlen_8": dict(kind="prefill", seed=4, n_seqs=8, len_lo=1024,
+                     len_hi=16384, h_qk=16, h_v=48, d=128, chunk=64,
+                     dtype="bf16", init="randn"),
+    "decode_256": dict(kind="decode", seed=5, batch=256, steps=128, h_qk=16,
+                       h_v=48, d=128, dtype="bf16"),
+}
+
+
+def workload_inputs(name, **overrides):
+    """Inputs of a named workload; overrides replace recipe fields (used to
+    shrink a workload for a quick check, e.g. steps=4)."""
+    w = dict(WORKLOADS[name])
+    w.update(overrides)
+    if w["kind"] == "decode":
+        return make_decode(w["seed"], w["batch"], w["steps"], w["h_qk"],
+                           w["h_v"], w["d"], w["dtype"])
+    if "seq_lens" in w:
+        lens = w["seq_lens"]
+    else:
+        lens = make_varlen_lengths(w["seed"] + 1000, w["n_seqs"], w["len_lo"],
+                                   w["len_hi"])
+    return make_prefill(w["seed"], lens, w["h_qk"], w["h_v"], w["d"],
+                        w["dtype"], w["init"])

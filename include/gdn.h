@@ -1,0 +1,153 @@
+/*
+ * libgdn -- Gated DeltaNet token mixer for AMD Instinct MI355X (gfx950).
+ *
+ * The method (page "Qwen3.8-Flash-Next 技术总结：Qwen4 架构的'探路者'",
+ * section 2.1 "Gated DeltaNet", state-update equation) keeps one dk x dv
+ * state per V head and updates it per token as
+ *     S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T
+ *         = a_t S_{t-1} + b_t k_t (v_t - a_t S_{t-1}^T k_t)^T
+ * with a_t in (0,1] the forget gate and b_t the delta-rule write strength.
+ * The layer output of this library is o_t = S_t^T q_t (post-update state,
+ * no scaling). Section 2.1 gives the head layout (16 QK heads, 48 V heads,
+ * head dim 128): V head h reads QK head h / (h_v / h_qk).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller,
+ *    contiguous row-major with the last dimension fastest; q, k, v, o and
+ *    states must be 16-byte aligned, log_alpha, beta and cu_seqlens 4-byte.
+ *  - The library allocates no device memory and keeps no global state
+ *    besides a thread-local error string.
+ *  - Calls enqueue work on `stream` (NULL = the default stream) and return
+ *    without synchronising; device faults surface at the caller's next sync.
+ *  - Invalid arguments return an error status before anything is enqueued;
+ *    gdn_last_error_message() then says which argument.
+ *  - Supported: dk == dv in {16, 128}; chunk in {16, 64}; h_v % h_qk == 0;
+ *    dtype GDN_DTYPE_F32 or GDN_DTYPE_BF16 for q, k, v and o. Gates and
+ *    states are always fp32.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_SUCCESS = 0,
+  GDN_ERROR_INVALID_VALUE = 1, /* bad pointer, size, alignment or shape */
+  GDN_ERROR_NOT_SUPPORTED = 2, /* valid but not built: head dim, chunk, dtype */
+  GDN_ERROR_WORKSPACE = 3,     /* workspace missing, misaligned or too small */
+  GDN_ERROR_HIP = 4            /* a HIP launch failed; see the message */
+} gdn_status_t;
+
+typedef enum {
+  GDN_DTYPE_F32 = 0,  /* IEEE float32 q, k, v, o */
+  GDN_DTYPE_BF16 = 1  /* bfloat16 q, k, v, o (fp32 accumulation and state) */
+} gdn_dtype_t;
+
+typedef struct {
+  int64_t num_seqs;     /* N >= 1: packed sequences (prefill) or batch (decode) */
+  int64_t total_tokens; /* T >= 0: packed tokens; decode: must equal num_seqs */
+  int32_t h_qk;         /* QK heads, >= 1 */
+  int32_t h_v;          /* V heads, a multiple of h_qk */
+  int32_t dk;           /* key/query head dim */
+  int32_t dv;           /* value head dim (must equal dk) */
+  int32_t chunk;        /* prefill chunk length C (ignored by decode) */
+  int32_t dtype;        /* gdn_dtype_t of q, k, v, o */
+} gdn_dims_t;
+
+/*
+ * Prefill of packed variable-length sequences with the chunkwise
+ * WY-representation algorithm that section 2.1 names (each chunk of C tokens
+ * becomes dense block products; chunks are scanned in order to carry the
+ * state), producing the same result as the token-serial update up to
+ * rounding.
+ *
+ *  q, k        [T, h_qk, dk]  dtype
+ *  v           [T, h_v, dv]   dtype
+ *  log_alpha   [T, h_v]       fp32, log a_t <= 0 (not clamped)
+ *  beta        [T, h_v]       fp32, any finite value
+ *  init_state  [N, h_v, dk, dv] fp32, or NULL for zeros
+ *  cu_seqlens  [N+1] int32 device array: 0 = c_0 <= c_1 <= ... <= c_N = T,
+ *              sequence n holds tokens [c_n, c_{n+1}); NULL means one
+ *              sequence of T tokens (N must be 1). The contents are a
+ *              precondition and are not checked. Empty sequences are allowed
+ *              (their final state equals their initial state).
+ *  o           [T, h_v, dv]   dtype, written; must not alias any input
+ *  final_state [N, h_v, dk, dv] fp32 or NULL; may alias init_state exactly
+ *  workspace   device scratch of at least gdn_chunk_fwd_workspace_bytes()
+ *              bytes, 256-byte aligned, owned by the caller; its contents on
+ *              return are unspecified. Calls that run concurrently need
+ *              distinct workspaces.
+ *
+ * Returns GDN_SUCCESS once all kernels are enqueued.
+ */
+gdn_status_t gdn_chunk_fwd(const gdn_dims_t* dims,
+                           const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta,
+                           const float* init_state, const int32_t* cu_seqlens,
+                           void* o, float* final_state,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Workspace bytes gdn_chunk_fwd needs for these dims; 0 if dims are invalid
+ * or unsupported (gdn_last_error_message() says why). The size depends on
+ * (num_seqs, total_tokens, h_qk, h_v, dk, chunk, dtype) only. */
+size_t gdn_chunk_fwd_workspace_bytes(const gdn_dims_t* dims);
+
+/*
+ * One decode step: one new token for each of N independent sequences, the
+ * single-token form of the update in section 2.1 applied in place:
+ *     p = S^T k, u = b (v - a p), S <- a S + k u^T, o = S^T q.
+ *
+ *  q, k       [N, h_qk, dk] dtype
+ *  v          [N, h_v, dv]  dtype
+ *  log_alpha  [N, h_v] fp32;  beta [N, h_v] fp32
+ *  state      [N, h_v, dk, dv] fp32, read and overwritten in place
+ *  o          [N, h_v, dv] dtype, written; must not alias any input
+ * dims->total_tokens must equal dims->num_seqs; dims->chunk is ignored.
+ */
+gdn_status_t gdn_decode_step(const gdn_dims_t* dims,
+                             const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta,
+                             float* state, void* o, hipStream_t stream);
+
+/* Static name of a status code. */
+const char* gdn_status_string(gdn_status_t status);
+
+/* Thread-local text describing the last error returned on this thread
+ * ("" if none). Valid until the next libgdn call on the same thread. */
+const char* gdn_last_error_message(void);
+
+/*
+ * Diagnostic view of gdn_chunk_fwd's workspace, for tests that compare the
+ * per-stage intermediates with a reference. Byte offsets from the workspace
+ * base; each region is described where the kernels are defined. Returns
+ * GDN_SUCCESS or the validation error of `dims`.
+ */
+typedef struct {
+  size_t chunk_table;  /* int32 [max_chunks][4]: seq, first token, length, index in seq */
+  size_t seq_chunk_offset; /* int32 [N+1]: first compact chunk of each sequence */
+  size_t gate_prefix;  /* fp32 [max_chunks][h_v][C]: in-chunk inclusive prefix of log a */
+  size_t tinv;         /* dtype [max_chunks][h_v][C][C]: (I + A)^{-1}, row-major */
+  size_t key_t;        /* dtype [max_chunks][h_qk][dk][C]: keys of the chunk, transposed */
+  size_t w;            /* dtype [max_chunks][h_v][C][dk]: W, row-major */
+  size_t u_tilde;      /* dtype, MFMA accumulator order (see the kernels) */
+  size_t u;            /* dtype, MFMA operand order (see the kernels) */
+  size_t s_chunk;      /* dtype, MFMA operand order (see the kernels) */
+  size_t total;        /* == gdn_chunk_fwd_workspace_bytes(dims) */
+  int64_t max_chunks;  /* floor(T / C) + N, the bound on the number of chunks */
+} gdn_workspace_layout_t;
+
+gdn_status_t gdn_chunk_fwd_workspace_layout(const gdn_dims_t* dims,
+                                            gdn_workspace_layout_t* layout);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,219 @@
+// C ABI of libgdn: argument validation, workspace carving and dispatch to
+// the kernel launchers. Host code only; nothing here touches the device
+// until every argument has been checked.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status_t fail(gdn_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+gdn_status_t ok() {
+  g_last_error.clear();
+  return GDN_SUCCESS;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Validation shared by both entry points. decode selects the decode rules.
+gdn_status_t check_dims(const gdn_dims_t* d, bool decode) {
+  if (!d) return fail(GDN_ERROR_INVALID_VALUE, "dims is NULL");
+  if (d->num_seqs < 1) return fail(GDN_ERROR_INVALID_VALUE, "num_seqs must be >= 1 (got %lld)", (long long)d->num_seqs);
+  if (d->total_tokens < 0) return fail(GDN_ERROR_INVALID_VALUE, "total_tokens must be >= 0");
+  if (d->total_tokens > INT32_MAX || d->num_seqs > INT32_MAX)
+    return fail(GDN_ERROR_INVALID_VALUE, "total_tokens and num_seqs must fit int32 (cu_seqlens is int32)");
+  if (d->h_qk < 1 || d->h_v < 1) return fail(GDN_ERROR_INVALID_VALUE, "h_qk and h_v must be >= 1");
+  if (d->h_v % d->h_qk) return fail(GDN_ERROR_INVALID_VALUE, "h_v (%d) must be a multiple of h_qk (%d)", d->h_v, d->h_qk);
+  if (d->h_v > 65535) return fail(GDN_ERROR_NOT_SUPPORTED, "h_v > 65535 is not supported");
+  if (d->dk < 1 || d->dv < 1) return fail(GDN_ERROR_INVALID_VALUE, "dk and dv must be >= 1");
+  if (d->dtype != GDN_DTYPE_F32 && d->dtype != GDN_DTYPE_BF16)
+    return fail(GDN_ERROR_INVALID_VALUE, "unknown dtype %d", d->dtype);
+  if (d->dk != d->dv) return fail(GDN_ERROR_NOT_SUPPORTED, "dk != dv is not supported (dk=%d dv=%d)", d->dk, d->dv);
+  if (d->dk != 16 && d->dk != 128) return fail(GDN_ERROR_NOT_SUPPORTED, "head dim %d not supported (16 or 128)", d->dk);
+  if (decode) {
+    if (d->total_tokens != d->num_seqs)
+      return fail(GDN_ERROR_INVALID_VALUE, "decode: total_tokens (%lld) must equal num_seqs (%lld)",
+                  (long long)d->total_tokens, (long long)d->num_seqs);
+  } else {
+    if (d->chunk < 1) return fail(GDN_ERROR_INVALID_VALUE, "chunk must be >= 1");
+    if (d->chunk != 16 && d->chunk != 64) return fail(GDN_ERROR_NOT_SUPPORTED, "chunk %d not supported (16 or 64)", d->chunk);
+  }
+  return GDN_SUCCESS;
+}
+
+struct Layout {
+  gdn_workspace_layout_t v;
+};
+
+// Workspace regions, each 256-byte aligned, in this order.
+Layout compute_layout(const gdn_dims_t& d) {
+  const size_t esz = d.dtype == GDN_DTYPE_F32 ? 4 : 2;
+  const size_t D = d.dk, C = d.chunk, N = d.num_seqs, T = d.total_tokens;
+  const size_t HQ = d.h_qk, HV = d.h_v;
+  const size_t CT = C / 16, DT = D / 16, CKS = (CT + 1) / 2, DKS = (DT + 1) / 2;
+  const size_t NC = T / C + N;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes, 256);
+    return o;
+  };
+  Layout L;
+  L.v.max_chunks = (int64_t)NC;
+  L.v.chunk_table = take(NC * 16);
+  L.v.seq_chunk_offset = take((N + 1) * 4);
+  L.v.gate_prefix = take(NC * HV * C * 4);
+  L.v.tinv = take(NC * HV * C * C * esz);
+  L.v.key_t = take(NC * HQ * D * C * esz);
+  L.v.w = take(NC * HV * C * D * esz);
+  L.v.u_tilde = take(NC * HV * C * D * esz);
+  L.v.u = take(NC * HV * DT * CKS * 512 * esz);
+  L.v.s_chunk = take(NC * HV * DT * DKS * 512 * esz);
+  L.v.total = off;
+  return L;
+}
+
+gdn_status_t launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(GDN_ERROR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status_t s) {
+  switch (s) {
+    case GDN_SUCCESS: return "GDN_SUCCESS";
+    case GDN_ERROR_INVALID_VALUE: return "GDN_ERROR_INVALID_VALUE";
+    case GDN_ERROR_NOT_SUPPORTED: return "GDN_ERROR_NOT_SUPPORTED";
+    case GDN_ERROR_WORKSPACE: return "GDN_ERROR_WORKSPACE";
+    case GDN_ERROR_HIP: return "GDN_ERROR_HIP";
+  }
+  return "GDN_UNKNOWN_STATUS";
+}
+
+const char* gdn_last_error_message(void) { return g_last_error.c_str(); }
+
+size_t gdn_chunk_fwd_workspace_bytes(const gdn_dims_t* dims) {
+  if (check_dims(dims, false) != GDN_SUCCESS) return 0;
+  ok();
+  return compute_layout(*dims).v.total;
+}
+
+gdn_status_t gdn_chunk_fwd_workspace_layout(const gdn_dims_t* dims, gdn_workspace_layout_t* layout) {
+  const gdn_status_t st = check_dims(dims, false);
+  if (st != GDN_SUCCESS) return st;
+  if (!layout) return fail(GDN_ERROR_INVALID_VALUE, "layout is NULL");
+  *layout = compute_layout(*dims).v;
+  return ok();
+}
+
+gdn_status_t gdn_chunk_fwd(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, const float* init_state,
+                           const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  gdn_status_t st = check_dims(dims, false);
+  if (st != GDN_SUCCESS) return st;
+  const gdn_dims_t& d = *dims;
+  if (!cu_seqlens && d.num_seqs != 1)
+    return fail(GDN_ERROR_INVALID_VALUE, "cu_seqlens is NULL but num_seqs = %lld", (long long)d.num_seqs);
+  if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(GDN_ERROR_INVALID_VALUE, "cu_seqlens is not 4-byte aligned");
+  if (d.total_tokens > 0) {
+    const void* need[] = {q, k, v, o, log_alpha, beta};
+    const char* names[] = {"q", "k", "v", "o", "log_alpha", "beta"};
+    for (int i = 0; i < 6; ++i) {
+      const size_t al = i < 4 ? 16 : 4;
+      if (!need[i]) return fail(GDN_ERROR_INVALID_VALUE, "%s is NULL", names[i]);
+      if (!aligned(need[i], al)) return fail(GDN_ERROR_INVALID_VALUE, "%s is not %zu-byte aligned", names[i], al);
+    }
+    if (o == q || o == k || o == v || o == log_alpha || o == beta)
+      return fail(GDN_ERROR_INVALID_VALUE, "o must not alias an input");
+  }
+  if (init_state && !aligned(init_state, 16)) return fail(GDN_ERROR_INVALID_VALUE, "init_state is not 16-byte aligned");
+  if (final_state && !aligned(final_state, 16)) return fail(GDN_ERROR_INVALID_VALUE, "final_state is not 16-byte aligned");
+  const Layout L = compute_layout(d);
+  if (!workspace) return fail(GDN_ERROR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.v.total);
+  if (!aligned(workspace, 256)) return fail(GDN_ERROR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < L.v.total)
+    return fail(GDN_ERROR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, L.v.total);
+
+  char* ws = static_cast<char*>(workspace);
+  gdn::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_alpha = log_alpha;
+  a.beta = beta;
+  a.init_state = init_state;
+  a.cu_seqlens = cu_seqlens;
+  a.o = o;
+  a.final_state = final_state;
+  a.chunk_table = reinterpret_cast<int32_t*>(ws + L.v.chunk_table);
+  a.seq_chunk_offset = reinterpret_cast<int32_t*>(ws + L.v.seq_chunk_offset);
+  a.gate_prefix = reinterpret_cast<float*>(ws + L.v.gate_prefix);
+  a.tinv = ws + L.v.tinv;
+  a.key_t = ws + L.v.key_t;
+  a.w = ws + L.v.w;
+  a.u_tilde = ws + L.v.u_tilde;
+  a.u = ws + L.v.u;
+  a.s_chunk = ws + L.v.s_chunk;
+  a.num_seqs = d.num_seqs;
+  a.total_tokens = d.total_tokens;
+  a.max_chunks = L.v.max_chunks;
+  a.h_qk = d.h_qk;
+  a.h_v = d.h_v;
+  a.group = d.h_v / d.h_qk;
+  return launch_status(gdn::launch_prefill(a, d.dtype, d.dk, d.chunk, stream), "gdn_chunk_fwd launch");
+}
+
+gdn_status_t gdn_decode_step(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta, float* state, void* o,
+                             hipStream_t stream) {
+  gdn_status_t st = check_dims(dims, true);
+  if (st != GDN_SUCCESS) return st;
+  const gdn_dims_t& d = *dims;
+  const void* need[] = {q, k, v, state, o, log_alpha, beta};
+  const char* names[] = {"q", "k", "v", "state", "o", "log_alpha", "beta"};
+  for (int i = 0; i < 7; ++i) {
+    const size_t al = i < 5 ? 16 : 4;
+    if (!need[i]) return fail(GDN_ERROR_INVALID_VALUE, "%s is NULL", names[i]);
+    if (!aligned(need[i], al)) return fail(GDN_ERROR_INVALID_VALUE, "%s is not %zu-byte aligned", names[i], al);
+  }
+  if (o == q || o == k || o == v || o == log_alpha || o == beta || o == state)
+    return fail(GDN_ERROR_INVALID_VALUE, "o must not alias an input");
+  gdn::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_alpha = log_alpha;
+  a.beta = beta;
+  a.state = state;
+  a.o = o;
+  a.num_seqs = d.num_seqs;
+  a.h_qk = d.h_qk;
+  a.h_v = d.h_v;
+  a.group = d.h_v / d.h_qk;
+  return launch_status(gdn::launch_decode(a, d.dtype, d.dk, stream), "gdn_decode_step launch");
+}
+
+}  // extern "C"

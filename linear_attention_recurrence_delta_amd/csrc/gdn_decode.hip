@@ -1,0 +1,113 @@
+// Decode (gdn_decode_step): one token per sequence, the single-token update
+// of page "Qwen3.8-Flash-Next 技术总结", section 2.1 (Gated DeltaNet), first
+// form of its update equation, applied to the state in place:
+//   p = S^T k,  u = b (v - a p),  S <- a S + k u^T,
+// with the output o = S_new^T q evaluated in the same pass through the
+// identity S_new^T q = a (S^T q) + u (k . q), so the state is read once and
+// written once.
+//
+// The step is a streaming read-modify-write of the fp32 state (64 KiB per
+// (sequence, V head) at head dim 128), so it is bound by HBM bandwidth. One
+// workgroup owns one (sequence, V head) state: thread (rg, cg) holds rows
+// [rg*RPT, rg*RPT+RPT) of columns [4cg, 4cg+4) in registers as 16-byte
+// vectors (each wave-wide load covers two full 512-byte rows). The column
+// sums S^T k and S^T q are reduced across the row groups through LDS, then
+// the update is applied from registers and stored. Loads and stores are
+// non-temporal: the state is touched once per step and is larger than the
+// last-level cache.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+
+template <int D> struct DecodeShape;
+template <> struct DecodeShape<128> { static constexpr int RG = 8; };
+template <> struct DecodeShape<16> { static constexpr int RG = 4; };
+
+template <typename E, int D>
+__global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_step(const DecodeArgs a) {
+  constexpr int CG = D / 4, RG = DecodeShape<D>::RG, RPT = D / RG;
+  __shared__ f32x4 red_p[RG][CG];
+  __shared__ f32x4 red_r[RG][CG];
+  __shared__ float red_kq[RG];
+  const int64_t nh = blockIdx.x;                 // sequence * h_v + V head
+  const int64_t n = nh / a.h_v;
+  const int hv = (int)(nh % a.h_v);
+  const int hq = hv / a.group;
+  const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
+
+  const E* kp = static_cast<const E*>(a.k) + (n * a.h_qk + hq) * D + rg * RPT;
+  const E* qp = static_cast<const E*>(a.q) + (n * a.h_qk + hq) * D + rg * RPT;
+  float kk[RPT], qq[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) { kk[r] = to_f(kp[r]); qq[r] = to_f(qp[r]); }
+
+  f32x4* sp = reinterpret_cast<f32x4*>(a.state + nh * D * D) + (rg * RPT) * CG + cg;
+  f32x4 s[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) s[r] = __builtin_nontemporal_load(sp + r * CG);
+
+  f32x4 p = zero4(), rq = zero4();
+  float kq = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    p += s[r] * kk[r];
+    rq += s[r] * qq[r];
+    kq += kk[r] * qq[r];
+  }
+  red_p[rg][cg] = p;
+  red_r[rg][cg] = rq;
+  if (cg == 0) red_kq[rg] = kq;
+  __syncthreads();
+  p = zero4();
+  rq = zero4();
+  kq = 0.f;
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    p += red_p[g][cg];
+    rq += red_r[g][cg];
+    kq += red_kq[g];
+  }
+
+  const float alpha = expf(a.log_alpha[nh]);
+  const float beta = a.beta[nh];
+  const E* vp = static_cast<const E*>(a.v) + nh * D + 4 * cg;
+  f32x4 u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) u[e] = beta * (to_f(vp[e]) - alpha * p[e]);
+
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) __builtin_nontemporal_store(s[r] * alpha + u * kk[r], sp + r * CG);
+
+  if (rg == 0) {
+    Half<E> h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = to_e<E>(alpha * rq[e] + u[e] * kq);
+    *reinterpret_cast<Half<E>*>(static_cast<E*>(a.o) + nh * D + 4 * cg) = h;
+  }
+}
+
+template <typename E, int D>
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
+  constexpr int threads = (D / 4) * DecodeShape<D>::RG;
+  const unsigned blocks = (unsigned)(a.num_seqs * a.h_v);
+  gdn_kd_decode_step<E, D><<<dim3(blocks), dim3(threads), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t s) {
+  if (dtype == 1) {
+    if (head_dim == 128) return launch_decode_t<bf16_t, 128>(a, s);
+    if (head_dim == 16) return launch_decode_t<bf16_t, 16>(a, s);
+  } else {
+    if (head_dim == 128) return launch_decode_t<float, 128>(a, s);
+    if (head_dim == 16) return launch_decode_t<float, 16>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

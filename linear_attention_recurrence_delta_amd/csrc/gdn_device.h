@@ -1,0 +1,99 @@
+// Device-side building blocks shared by the libgdn kernels (gfx950 only).
+//
+// MFMA tiles. Every dense product in the library is built from 16x16 output
+// tiles with fp32 accumulation:
+//   bf16 operands: v_mfma_f32_16x16x32_bf16 (one instruction per 32-deep step)
+//   fp32 operands: v_mfma_f32_16x16x4_f32   (eight instructions per step)
+// The accumulator of a 16x16 tile holds, in lane l, rows 4*(l/16)+i (i=0..3)
+// of column l%16.
+//
+// Operand fragments ("frag"): for a 32-deep contraction step starting at k0,
+// lane l holds 8 values of its row (A operand) or column (B operand) l%16,
+// at the contraction indices
+//     k0 + 4*(l/16) + e          for e = 0..3
+//     k0 + 16 + 4*(l/16) + e-4   for e = 4..7.
+// The products only need A and B to agree on this order. It is chosen so
+// that two vertically adjacent accumulator tiles (rows k0..k0+15 and
+// k0+16..k0+31) ARE a B fragment (and the A fragment of their transpose)
+// without any data movement: this is how the state and the delta rows flow
+// from one product into the next inside a wave.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+template <typename E> struct FragOf;
+template <> struct FragOf<bf16_t> { typedef bf16x8 type; typedef bf16x4 half; };
+template <> struct FragOf<float> { typedef f32x8 type; typedef f32x4 half; };
+template <typename E> using Frag = typename FragOf<E>::type;
+template <typename E> using Half = typename FragOf<E>::half;
+
+__device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mma(const f32x8& a, const f32x8& b, f32x4 c) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+  return c;
+}
+
+template <typename E> __device__ __forceinline__ E to_e(float x);
+template <> __device__ __forceinline__ float to_e<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t to_e<bf16_t>(float x) { return (bf16_t)x; }
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16_t x) { return (float)x; }
+
+template <typename E> __device__ __forceinline__ Half<E> zero_half() {
+  Half<E> z;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) z[e] = to_e<E>(0.f);
+  return z;
+}
+
+template <typename E> __device__ __forceinline__ Frag<E> join(const Half<E>& lo, const Half<E>& hi) {
+  Frag<E> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f[e] = lo[e]; f[e + 4] = hi[e]; }
+  return f;
+}
+
+// Fragment of a row-major matrix: `row` points at element [row][k0] of the
+// lane's row; `kext` is the contraction extent remaining from k0 (a multiple
+// of 16), so the upper half is present only when kext > 16.
+template <typename E>
+__device__ __forceinline__ Frag<E> load_frag(const E* row, int quad, int kext) {
+  Half<E> lo = *reinterpret_cast<const Half<E>*>(row + 4 * quad);
+  Half<E> hi = (kext > 16) ? *reinterpret_cast<const Half<E>*>(row + 16 + 4 * quad) : zero_half<E>();
+  return join<E>(lo, hi);
+}
+
+// Same, with the whole row zero when `valid` is false (rows past the end of
+// a partial chunk).
+template <typename E>
+__device__ __forceinline__ Frag<E> load_frag_masked(const E* row, int quad, int kext, bool valid) {
+  if (!valid) return join<E>(zero_half<E>(), zero_half<E>());
+  return load_frag<E>(row, quad, kext);
+}
+
+// Two vertically adjacent accumulator tiles -> operand fragment.
+template <typename E>
+__device__ __forceinline__ Frag<E> acc_to_frag(const f32x4& lo, const f32x4& hi) {
+  Frag<E> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f[e] = to_e<E>(lo[e]); f[e + 4] = to_e<E>(hi[e]); }
+  return f;
+}
+
+__device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
+
+}  // namespace gdn

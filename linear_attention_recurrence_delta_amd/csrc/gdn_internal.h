@@ -1,0 +1,59 @@
+// Internal interface between the C ABI (gdn_api.cpp) and the kernel
+// launchers (gdn_prefill.hip, gdn_decode.hip). Not installed.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Everything one gdn_chunk_fwd call needs on the device. Workspace regions
+// are typed pointers carved by the host (see the layout in gdn_api.cpp).
+struct PrefillArgs {
+  const void* q;            // [T, HQ, D]
+  const void* k;            // [T, HQ, D]
+  const void* v;            // [T, HV, D]
+  const float* log_alpha;   // [T, HV]
+  const float* beta;        // [T, HV]
+  const float* init_state;  // [N, HV, D, D] or null
+  const int32_t* cu_seqlens;  // [N+1] or null (one sequence)
+  void* o;                  // [T, HV, D]
+  float* final_state;       // [N, HV, D, D] or null
+  // workspace
+  int32_t* chunk_table;     // [NC][4]
+  int32_t* seq_chunk_offset;  // [N+1]
+  float* gate_prefix;       // [NC][HV][C]
+  void* tinv;               // [NC][HV][C][C]
+  void* key_t;              // [NC][HQ][D][C]
+  void* w;                  // [NC][HV][C][D]
+  void* u_tilde;            // [NC][HV][D/16][C/16][64][4]
+  void* u;                  // [NC][HV][D/16][ceil(C/32)][64][8]
+  void* s_chunk;            // [NC][HV][D/16][ceil(D/32)][64][8]
+  int64_t num_seqs;         // N
+  int64_t total_tokens;     // T
+  int64_t max_chunks;       // NC = floor(T/C) + N
+  int32_t h_qk;             // HQ
+  int32_t h_v;              // HV
+  int32_t group;            // HV / HQ
+};
+
+struct DecodeArgs {
+  const void* q;            // [N, HQ, D]
+  const void* k;            // [N, HQ, D]
+  const void* v;            // [N, HV, D]
+  const float* log_alpha;   // [N, HV]
+  const float* beta;        // [N, HV]
+  float* state;             // [N, HV, D, D], in place
+  void* o;                  // [N, HV, D]
+  int64_t num_seqs;
+  int32_t h_qk;
+  int32_t h_v;
+  int32_t group;
+};
+
+// dtype: 0 = fp32, 1 = bf16. Returns the first launch error, if any.
+hipError_t launch_prefill(const PrefillArgs& args, int dtype, int head_dim, int chunk,
+                          hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& args, int dtype, int head_dim, hipStream_t stream);
+
+}  // namespace gdn

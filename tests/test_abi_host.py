@@ -1,0 +1,147 @@
+"""C ABI host-side checks that need no GPU: the library loads, exports every
+function include/gdn.h declares, and rejects bad arguments with the
+documented status before enqueuing anything. Every call here fails
+validation, so none of them reaches a kernel launch on any machine."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from linear_attention_recurrence_delta_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+INVALID, NOT_SUPPORTED, WORKSPACE = 1, 2, 3
+FAKE = 0x10000  # a 256-aligned non-null address; never dereferenced here
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIBRARY_PATH):
+        pytest.skip("libgdn.so not built")
+    return B.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(gdn_\w+)\(", text, re.M)))
+
+
+def test_header_declares_expected_functions():
+    assert header_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIBRARY_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(gdn_\w+)$", out, re.M))
+    for name in header_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def dims(**kw):
+    base = dict(num_seqs=1, total_tokens=128, h_qk=16, h_v=48, dk=128, dv=128, chunk=64,
+                dtype=1)
+    base.update(kw)
+    return B.GdnDims(*[base[f] for f, _ in B.GdnDims._fields_])
+
+
+def ws_bytes(lib, d):
+    return lib.gdn_chunk_fwd_workspace_bytes(ctypes.byref(d))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_seqs=0), INVALID),
+    (dict(total_tokens=-1), INVALID),
+    (dict(h_qk=0), INVALID),
+    (dict(h_v=47), INVALID),                # not a multiple of h_qk
+    (dict(dk=0), INVALID),
+    (dict(dtype=7), INVALID),
+    (dict(chunk=0), INVALID),
+    (dict(dk=64, dv=64), NOT_SUPPORTED),
+    (dict(dk=128, dv=64), NOT_SUPPORTED),
+    (dict(chunk=32), NOT_SUPPORTED),
+])
+def test_dims_validation(lib, kw, status):
+    d = dims(**kw)
+    assert ws_bytes(lib, d) == 0
+    lay = B.GdnWorkspaceLayout()
+    assert lib.gdn_chunk_fwd_workspace_layout(ctypes.byref(d), ctypes.byref(lay)) == status
+    assert lib.gdn_last_error_message().decode() != ""
+
+
+def test_workspace_size_formula(lib):
+    # regions: chunk table, sequence offsets, gate prefixes, Tinv, K^T, W, Ut,
+    # U fragments, state fragments; each padded to 256 bytes
+    d = dims(num_seqs=3, total_tokens=1000)
+    nc = 1000 // 64 + 3
+    def up(x):
+        return (x + 255) // 256 * 256
+    want = (up(nc * 16) + up(4 * 4) + up(nc * 48 * 64 * 4) + up(nc * 48 * 64 * 64 * 2)
+            + up(nc * 16 * 128 * 64 * 2) + 3 * up(nc * 48 * 64 * 128 * 2)
+            + up(nc * 48 * 128 * 128 * 2))
+    assert ws_bytes(lib, d) == want
+    lay = B.GdnWorkspaceLayout()
+    assert lib.gdn_chunk_fwd_workspace_layout(ctypes.byref(d), ctypes.byref(lay)) == 0
+    assert lay.total == want and lay.max_chunks == nc
+    offs = [lay.chunk_table, lay.seq_chunk_offset, lay.gate_prefix, lay.tinv, lay.key_t,
+            lay.w, lay.u_tilde, lay.u, lay.s_chunk]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+
+
+def call_fwd(lib, d, q=FAKE, k=FAKE, v=FAKE, la=FAKE, b=FAKE, init=None, cu=None, o=FAKE * 2,
+             fin=None, ws=FAKE * 4, wsb=None):
+    if wsb is None:
+        wsb = ws_bytes(lib, d) if ws_bytes(lib, d) else 1 << 40
+    vp = ctypes.c_void_p
+    return lib.gdn_chunk_fwd(ctypes.byref(d), vp(q), vp(k), vp(v), vp(la), vp(b), vp(init),
+                             vp(cu), vp(o), vp(fin), vp(ws), wsb, None)
+
+
+def test_fwd_rejects_bad_pointers(lib):
+    d = dims()
+    assert call_fwd(lib, d, q=None) == INVALID
+    assert "q is NULL" in lib.gdn_last_error_message().decode()
+    assert call_fwd(lib, d, v=FAKE + 8) == INVALID               # 16-byte alignment
+    assert call_fwd(lib, d, la=FAKE + 2) == INVALID              # 4-byte alignment
+    assert call_fwd(lib, d, o=FAKE) == INVALID                   # o aliases q
+    assert call_fwd(lib, d, init=FAKE + 4) == INVALID
+    assert call_fwd(lib, d, fin=FAKE + 4) == INVALID
+    assert call_fwd(lib, dims(num_seqs=2), cu=None) == INVALID   # N > 1 needs cu_seqlens
+    assert call_fwd(lib, dims(num_seqs=2), cu=FAKE + 2) == INVALID
+
+
+def test_fwd_rejects_bad_workspace(lib):
+    d = dims()
+    need = ws_bytes(lib, d)
+    assert call_fwd(lib, d, ws=None) == WORKSPACE
+    assert call_fwd(lib, d, ws=FAKE * 4 + 16) == WORKSPACE       # 256-byte alignment
+    assert call_fwd(lib, d, wsb=need - 1) == WORKSPACE
+    assert "needed" in lib.gdn_last_error_message().decode()
+
+
+def test_fwd_rejects_unsupported(lib):
+    assert call_fwd(lib, dims(dk=64, dv=64)) == NOT_SUPPORTED
+    assert call_fwd(lib, dims(chunk=128)) == NOT_SUPPORTED
+
+
+def test_decode_validation(lib):
+    vp = ctypes.c_void_p
+    def call(d, q=FAKE, k=FAKE, v=FAKE, la=FAKE, b=FAKE, s=FAKE * 8, o=FAKE * 2):
+        return lib.gdn_decode_step(ctypes.byref(d), vp(q), vp(k), vp(v), vp(la), vp(b), vp(s),
+                                   vp(o), None)
+    d = dims(num_seqs=4, total_tokens=4)
+    assert call(dims(num_seqs=4, total_tokens=5)) == INVALID
+    assert call(d, s=None) == INVALID
+    assert call(d, s=FAKE * 8 + 4) == INVALID
+    assert call(d, o=FAKE * 8) == INVALID                        # o aliases state
+    assert call(dims(num_seqs=4, total_tokens=4, dk=32, dv=32)) == NOT_SUPPORTED
+
+
+def test_status_strings(lib):
+    for code, name in B.STATUS.items():
+        assert lib.gdn_status_string(code).decode() == name

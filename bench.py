@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of libgdn on one MI355X.
+
+One step = one pass of the whole hot path: gdn_chunk_fwd over the 64K-token
+layer (B=1, T=65536, 16 QK / 48 V heads, head dim 128, chunk 64, bf16
+q/k/v, fp32 gates and state, nonzero initial state) followed by one
+gdn_decode_step over the 256-sequence batch (fp32 state 256 x 48 x 128 x 128,
+updated in place; the step index advances through successive decode tokens).
+Inputs are generated once, moved to HBM, and are resident before timing
+starts.
+
+The prefill kernels are enqueued one stage at a time through
+gdn_chunk_fwd_stages with HIP events (torch events on the stream the kernels
+run on) between them, so every kernel's duration is measured inside the
+timed region. `value` is prefill tokens/s (T / mean prefill time); decode
+GB/s is reported beside it. Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tokens/s at T=64K (48 V heads, d=128) + decode state GB/s"
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
+STAGES = ["gdn_k1_gate_prefix", "gdn_k2_akk_inverse", "gdn_k3_wu", "gdn_k4_state_scan",
+          "gdn_k5_output"]
+DECODE_KERNEL = "gdn_kd_decode_step"
+
+
+def algorithmic_work(T, HQ, HV, D, C, N, decode_batch):
+    """Per-launch algorithmic work of each kernel (flops for the contraction
+    kernels, bytes for the bandwidth-bound ones), from the chunkwise method's
+    operation counts; see the design notes."""
+    dk = dv = D
+    work = {
+        "gdn_k1_gate_prefix": ("hbm", 2.0 * T * HV * 4),
+        "gdn_k2_akk_inverse": ("mfma", T * (HQ * 2 * C * dk + HV * C * C / 3.0)),
+        "gdn_k3_wu": ("mfma", T * HV * (2 * C * dk + 2 * C * dv)),
+        "gdn_k4_state_scan": ("mfma", T * HV * 4 * dk * dv),
+        "gdn_k5_output": ("mfma", T * (HQ * 2 * C * dk + HV * (2 * dk * dv + 2 * C * dv))),
+    }
+    total_flops = sum(w for b, w in work.values() if b == "mfma")
+    per_token = HV * (6 * dk * dv + 2 * C * dk + 4 * C * dv + C * C / 3.0) + HQ * 4 * C * dk
+    assert abs(total_flops - per_token * T) < 1e-6 * total_flops
+    state = decode_batch * HV * dk * dv * 4
+    dec_bytes = 2 * state + decode_batch * (2 * HQ * dk * 2 + 2 * HV * dv * 2 + 2 * HV * 4)
+    work[DECODE_KERNEL] = ("hbm", float(dec_bytes))
+    return work, per_token
+
+
+def load_traffic(kernel):
+    """Measured HBM traffic of `kernel` from the committed counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "linear_attention_recurrence_delta_amd", "csrc", rec["source"])
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+            return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(inp, seconds):
+    """The fp64 oracle (token-serial recurrence), as it stands, on the first
+    tokens of the same 64K-token input, all heads, one thread, for about
+    `seconds` of CPU time; returns tokens/s."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import gdn_oracle as O
+    block = 32
+    q = inp["q"].double().numpy()
+    k = inp["k"].double().numpy()
+    v = inp["v"].double().numpy()
+    la = inp["log_alpha"].double().numpy()
+    b = inp["beta"].double().numpy()
+    state = inp["init_state"].double().numpy()
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - t0 < seconds and done + block <= q.shape[0]:
+            s = slice(done, done + block)
+            _, state = O.recurrent_form1(q[s], k[s], v[s], la[s], b[s], state)
+            done += block
+    dt = time.perf_counter() - t0
+    assert np.isfinite(state).all()
+    return done / dt, done, dt
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_attention_recurrence_delta_amd as gdn
+    from linear_attention_recurrence_delta_amd import inputs as I
+
+    gdn.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = I.WORKLOADS["long_64k"]
+    dspec = I.WORKLOADS["decode_256"]
+    T, HQ, HV, D, C = spec["seq_lens"][0], spec["h_qk"], spec["h_v"], spec["d"], spec["chunk"]
+    NB = dspec["batch"]
+    n_dec = min(dspec["steps"], args.warmup + args.steps)
+
+    inp_cpu = I.workload_inputs("long_64k")
+    inp = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp_cpu.items()}
+    dec = I.workload_inputs("decode_256", steps=n_dec)
+    dec = {k: v.to(dev) for k, v in dec.items()}
+    state = dec["state0"].clone()
+    dims = gdn.make_dims(1, T, HQ, HV, D, D, C, torch.bfloat16)
+    ws = torch.empty(gdn.gdn_chunk_fwd_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(inp["v"])
+    fin = torch.empty_like(inp["init_state"])
+    o_dec = torch.empty_like(dec["v"][0])
+    stream = torch.cuda.current_stream(dev)
+
+    def prefill_stage(s):
+        gdn.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                          inp["init_state"], None, chunk=C, workspace=ws, o=o, final_state=fin,
+                          stages=(s, s))
+
+    def decode(i):
+        j = i % n_dec
+        gdn.gdn_decode_step(dec["q"][j], dec["k"][j], dec["v"][j], dec["log_alpha"][j],
+                            dec["beta"][j], state, o=o_dec)
+
+    for i in range(args.warmup):
+        for s in range(1, 6):
+            prefill_stage(s)
+        decode(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        for s in range(5):
+            ev[i][s].record(stream)
+            prefill_stage(s + 1)
+        ev[i][5].record(stream)
+        decode(args.warmup + i)
+        ev[i][6].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = STAGES + [DECODE_KERNEL]
+    ms = {n: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K
+          for j, n in enumerate(names)}
+    prefill_ms = sum(ev[i][0].elapsed_time(ev[i][5]) for i in range(K)) / K
+    decode_ms = ms[DECODE_KERNEL]
+    work, per_token = algorithmic_work(T, HQ, HV, D, C, 1, NB)
+    kernels = {}
+    for n in names:
+        bound, amount = work[n]
+        rate = amount / (ms[n] * 1e-3)
+        peak = PEAK_BF16_FLOPS if bound == "mfma" else PEAK_HBM_BYTES
+        kernels[n] = {"ms": round(ms[n], 4), "bound": bound,
+                      "achieved": round(rate / (1e12 if bound == "mfma" else 1e9), 3),
+                      "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                      "frac": round(rate / peak, 4)}
+    dominant = max(names, key=lambda n: ms[n])
+    dk = kernels[dominant]
+    roofline = {"kernel": dominant, "bound": dk["bound"], "achieved": dk["achieved"],
+                "peak": 2500.0 if dk["bound"] == "mfma" else 8000.0, "unit": dk["unit"],
+                "frac": dk["frac"], "traffic": load_traffic(dominant)}
+    dec_bytes = work[DECODE_KERNEL][1]
+    tokens_per_s = T / (prefill_ms * 1e-3)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "64K-token GDN layer prefill (B=1, T=65536, 16 QK / 48 V heads, "
+                               "d=128, chunk 64, bf16 q/k/v, fp32 gates/state, N(0,0.02^2) "
+                               "init) + one batched decode step (256 sequences, fp32 state "
+                               "256x48x128x128 in place)",
+                   "tokens": T, "chunk": C, "decode_batch": NB},
+        "prefill_ms": round(prefill_ms, 4),
+        "prefill_mfma_frac": round(per_token * T / (prefill_ms * 1e-3) / PEAK_BF16_FLOPS, 4),
+        "decode_ms": round(decode_ms, 4),
+        "decode_GBps": round(dec_bytes / (decode_ms * 1e-3) / 1e9, 1),
+        "decode_hbm_frac": round(dec_bytes / (decode_ms * 1e-3) / PEAK_HBM_BYTES, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rate, n_tok, secs = cpu_baseline(inp_cpu, args.cpu_seconds)
+        line["cpu_baseline"] = {
+            "value": round(rate, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n_tok} tokens of the same 64K-token input, all 48 V heads, "
+                      f"token-serial fp64 recurrence, one thread, {secs:.1f} s"}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -94,6 +94,25 @@ gdn_status_t gdn_chunk_fwd(const gdn_dims_t* dims,
                            void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/*
+ * Diagnostic variant of gdn_chunk_fwd that enqueues only kernels
+ * first_stage..last_stage (1 = gate prefix and chunk table, 2 = K K^T and
+ * (I + A)^{-1}, 3 = W and Ut, 4 = state scan, 5 = outputs), so a profiler or
+ * benchmark can put events between them. Arguments are those of
+ * gdn_chunk_fwd. Stages after the first read what earlier stages left in
+ * `workspace`, so a call starting at stage s > 1 must follow calls that ran
+ * stages 1..s-1 with identical arguments and workspace on the same stream.
+ * gdn_chunk_fwd is gdn_chunk_fwd_stages(..., 1, 5). Returns
+ * GDN_ERROR_INVALID_VALUE unless 1 <= first_stage <= last_stage <= 5.
+ */
+gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims,
+                                  const void* q, const void* k, const void* v,
+                                  const float* log_alpha, const float* beta,
+                                  const float* init_state, const int32_t* cu_seqlens,
+                                  void* o, float* final_state,
+                                  void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream, int first_stage, int last_stage);
+
 /* Workspace bytes gdn_chunk_fwd needs for these dims; 0 if dims are invalid
  * or unsupported (gdn_last_error_message() says why). The size depends on
  * (num_seqs, total_tokens, h_qk, h_v, dk, chunk, dtype) only. */

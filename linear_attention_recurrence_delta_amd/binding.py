@@ -18,8 +18,8 @@ STATUS = {0: "GDN_SUCCESS", 1: "GDN_ERROR_INVALID_VALUE", 2: "GDN_ERROR_NOT_SUPP
           3: "GDN_ERROR_WORKSPACE", 4: "GDN_ERROR_HIP"}
 
 # Names the library must export (every function declared in include/gdn.h).
-EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_decode_step",
-           "gdn_status_string", "gdn_last_error_message",
+EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_stages", "gdn_chunk_fwd_workspace_bytes",
+           "gdn_decode_step", "gdn_status_string", "gdn_last_error_message",
            "gdn_chunk_fwd_workspace_layout")
 
 
@@ -62,6 +62,9 @@ def load_library(path=None):
     dims_p = ctypes.POINTER(GdnDims)
     lib.gdn_chunk_fwd.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_chunk_fwd.restype = i32
+    lib.gdn_chunk_fwd_stages.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                         i32, i32]
+    lib.gdn_chunk_fwd_stages.restype = i32
     lib.gdn_chunk_fwd_workspace_bytes.argtypes = [dims_p]
     lib.gdn_chunk_fwd_workspace_bytes.restype = sz
     lib.gdn_chunk_fwd_workspace_layout.argtypes = [dims_p, ctypes.POINTER(GdnWorkspaceLayout)]
@@ -124,11 +127,13 @@ def gdn_chunk_fwd_workspace_layout(dims):
 
 
 def gdn_chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, chunk=64,
-                  output_final_state=True, workspace=None, o=None, final_state=None):
+                  output_final_state=True, workspace=None, o=None, final_state=None,
+                  stages=None):
     """Prefill through gdn_chunk_fwd. Shapes: q, k [T,Hqk,d]; v [T,Hv,d];
     log_alpha, beta [T,Hv] fp32; init_state [N,Hv,d,d] fp32 or None;
     cu_seqlens int32 [N+1] or None. Returns (o, final_state or None).
-    `workspace` (uint8 CUDA tensor) may be passed to reuse scratch memory."""
+    `workspace` (uint8 CUDA tensor) may be passed to reuse scratch memory.
+    `stages=(first, last)` calls gdn_chunk_fwd_stages instead (diagnostic)."""
     lib = load_library()
     dev = q.device
     if dev.type != "cuda":
@@ -159,10 +164,13 @@ def gdn_chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, ch
         final_state = torch.empty((n, h_v, d, v.shape[2]), dtype=torch.float32, device=dev)
     if final_state is not None:
         _need(final_state, "final_state", dev, torch.float32, (n, h_v, d, v.shape[2]))
-    _check(lib.gdn_chunk_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-                             _ptr(beta), _ptr(init_state), _ptr(cu_seqlens), _ptr(o),
-                             _ptr(final_state), _ptr(workspace), workspace.numel(),
-                             _stream(dev)))
+    args = (ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+            _ptr(init_state), _ptr(cu_seqlens), _ptr(o), _ptr(final_state), _ptr(workspace),
+            workspace.numel(), _stream(dev))
+    if stages is None:
+        _check(lib.gdn_chunk_fwd(*args))
+    else:
+        _check(lib.gdn_chunk_fwd_stages(*args, int(stages[0]), int(stages[1])))
     return o, final_state
 
 

@@ -131,6 +131,17 @@ gdn_status_t gdn_chunk_fwd(const gdn_dims_t* dims, const void* q, const void* k,
                            const float* log_alpha, const float* beta, const float* init_state,
                            const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
+  return gdn_chunk_fwd_stages(dims, q, k, v, log_alpha, beta, init_state, cu_seqlens, o, final_state,
+                              workspace, workspace_bytes, stream, 1, 5);
+}
+
+gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+                                  const float* log_alpha, const float* beta, const float* init_state,
+                                  const int32_t* cu_seqlens, void* o, float* final_state,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                  int first_stage, int last_stage) {
+  if (first_stage < 1 || last_stage > 5 || first_stage > last_stage)
+    return fail(GDN_ERROR_INVALID_VALUE, "stages %d..%d: need 1 <= first <= last <= 5", first_stage, last_stage);
   gdn_status_t st = check_dims(dims, false);
   if (st != GDN_SUCCESS) return st;
   const gdn_dims_t& d = *dims;
@@ -183,7 +194,8 @@ gdn_status_t gdn_chunk_fwd(const gdn_dims_t* dims, const void* q, const void* k,
   a.h_qk = d.h_qk;
   a.h_v = d.h_v;
   a.group = d.h_v / d.h_qk;
-  return launch_status(gdn::launch_prefill(a, d.dtype, d.dk, d.chunk, stream), "gdn_chunk_fwd launch");
+  return launch_status(gdn::launch_prefill(a, d.dtype, d.dk, d.chunk, stream, first_stage, last_stage),
+                       "gdn_chunk_fwd launch");
 }
 
 gdn_status_t gdn_decode_step(const gdn_dims_t* dims, const void* q, const void* k, const void* v,

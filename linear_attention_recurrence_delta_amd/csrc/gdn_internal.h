@@ -52,8 +52,9 @@ struct DecodeArgs {
 };
 
 // dtype: 0 = fp32, 1 = bf16. Returns the first launch error, if any.
+// Stages first..last of the five prefill kernels (1-based, inclusive).
 hipError_t launch_prefill(const PrefillArgs& args, int dtype, int head_dim, int chunk,
-                          hipStream_t stream);
+                          hipStream_t stream, int first_stage, int last_stage);
 hipError_t launch_decode(const DecodeArgs& args, int dtype, int head_dim, hipStream_t stream);
 
 }  // namespace gdn

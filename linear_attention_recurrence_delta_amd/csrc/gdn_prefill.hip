@@ -425,31 +425,37 @@ __global__ __launch_bounds__(kBlock) void gdn_k5_output(const PrefillArgs a) {
 }
 
 template <typename E, int D, int C>
-hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
+hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int last) {
   const unsigned nc = (unsigned)a.max_chunks;
-  gdn_k1_gate_prefix<C><<<dim3(nc), dim3(kBlock), 0, s>>>(a);
-  gdn_k2_akk_inverse<E, D, C><<<dim3(nc, a.h_qk), dim3(kBlock), 0, s>>>(a);
-  gdn_k3_wu<E, D, C><<<dim3(nc, a.h_v), dim3(kBlock), 0, s>>>(a);
   const unsigned scan_waves = (unsigned)(a.num_seqs * a.h_v * (D / 16));
-  gdn_k4_state_scan<E, D, C><<<dim3(scan_waves), dim3(64), 0, s>>>(a);
-  gdn_k5_output<E, D, C><<<dim3(nc, a.h_v), dim3(kBlock), 0, s>>>(a);
+  for (int stage = first; stage <= last; ++stage) {
+    switch (stage) {
+      case 1: gdn_k1_gate_prefix<C><<<dim3(nc), dim3(kBlock), 0, s>>>(a); break;
+      case 2: gdn_k2_akk_inverse<E, D, C><<<dim3(nc, a.h_qk), dim3(kBlock), 0, s>>>(a); break;
+      case 3: gdn_k3_wu<E, D, C><<<dim3(nc, a.h_v), dim3(kBlock), 0, s>>>(a); break;
+      case 4: gdn_k4_state_scan<E, D, C><<<dim3(scan_waves), dim3(64), 0, s>>>(a); break;
+      case 5: gdn_k5_output<E, D, C><<<dim3(nc, a.h_v), dim3(kBlock), 0, s>>>(a); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
   return hipGetLastError();
 }
 
 template <typename E>
-hipError_t launch_prefill_e(const PrefillArgs& a, int d, int c, hipStream_t s) {
-  if (d == 128 && c == 64) return launch_prefill_t<E, 128, 64>(a, s);
-  if (d == 128 && c == 16) return launch_prefill_t<E, 128, 16>(a, s);
-  if (d == 16 && c == 64) return launch_prefill_t<E, 16, 64>(a, s);
-  if (d == 16 && c == 16) return launch_prefill_t<E, 16, 16>(a, s);
+hipError_t launch_prefill_e(const PrefillArgs& a, int d, int c, hipStream_t s, int first, int last) {
+  if (d == 128 && c == 64) return launch_prefill_t<E, 128, 64>(a, s, first, last);
+  if (d == 128 && c == 16) return launch_prefill_t<E, 128, 16>(a, s, first, last);
+  if (d == 16 && c == 64) return launch_prefill_t<E, 16, 64>(a, s, first, last);
+  if (d == 16 && c == 16) return launch_prefill_t<E, 16, 16>(a, s, first, last);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int chunk, hipStream_t s) {
-  if (dtype == 1) return launch_prefill_e<bf16_t>(a, head_dim, chunk, s);
-  return launch_prefill_e<float>(a, head_dim, chunk, s);
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int chunk, hipStream_t s,
+                          int first_stage, int last_stage) {
+  if (dtype == 1) return launch_prefill_e<bf16_t>(a, head_dim, chunk, s, first_stage, last_stage);
+  return launch_prefill_e<float>(a, head_dim, chunk, s, first_stage, last_stage);
 }
 
 }  // namespace gdn

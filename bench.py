@@ -30,8 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN prefill tokens/s at T=64K (48 V heads, d=128) + decode state GB/s"
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
-STAGES = ["gdn_k1_gate_prefix", "gdn_k2_akk_inverse", "gdn_k3_wu", "gdn_k4_state_scan",
-          "gdn_k5_output"]
+STAGES = ["gdn_k1_gate_prefix", "gdn_k2_akk_inverse", "gdn_k3_scan"]
 DECODE_KERNEL = "gdn_kd_decode_step"
 
 
@@ -41,11 +40,12 @@ def algorithmic_work(T, HQ, HV, D, C, N, decode_batch):
     operation counts; see the design notes."""
     dk = dv = D
     work = {
-        "gdn_k1_gate_prefix": ("hbm", 2.0 * T * HV * 4),
-        "gdn_k2_akk_inverse": ("mfma", T * (HQ * 2 * C * dk + HV * C * C / 3.0)),
-        "gdn_k3_wu": ("mfma", T * HV * (2 * C * dk + 2 * C * dv)),
-        "gdn_k4_state_scan": ("mfma", T * HV * 4 * dk * dv),
-        "gdn_k5_output": ("mfma", T * (HQ * 2 * C * dk + HV * (2 * dk * dv + 2 * C * dv))),
+        # reads log a and b, writes g and per-chunk b
+        "gdn_k1_gate_prefix": ("hbm", 4.0 * T * HV * 4),
+        # K K^T and Q K^T per QK head, the triangular inverse per V head
+        "gdn_k2_akk_inverse": ("mfma", T * (HQ * 4 * C * dk + HV * C * C / 3.0)),
+        # W, Ut, W S, K^T U, Q S and (Q K^T) U per V head
+        "gdn_k3_scan": ("mfma", T * HV * (6 * dk * dv + 2 * C * dk + 4 * C * dv)),
     }
     total_flops = sum(w for b, w in work.values() if b == "mfma")
     per_token = HV * (6 * dk * dv + 2 * C * dk + 4 * C * dv + C * C / 3.0) + HQ * 4 * C * dk
@@ -148,29 +148,30 @@ def main():
                             dec["beta"][j], state, o=o_dec)
 
     for i in range(args.warmup):
-        for s in range(1, 6):
+        for s in range(1, len(STAGES) + 1):
             prefill_stage(s)
         decode(i)
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
+    NST = len(STAGES)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(NST + 2)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        for s in range(5):
+        for s in range(NST):
             ev[i][s].record(stream)
             prefill_stage(s + 1)
-        ev[i][5].record(stream)
+        ev[i][NST].record(stream)
         decode(args.warmup + i)
-        ev[i][6].record(stream)
+        ev[i][NST + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     names = STAGES + [DECODE_KERNEL]
     ms = {n: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K
           for j, n in enumerate(names)}
-    prefill_ms = sum(ev[i][0].elapsed_time(ev[i][5]) for i in range(K)) / K
+    prefill_ms = sum(ev[i][0].elapsed_time(ev[i][NST]) for i in range(K)) / K
     decode_ms = ms[DECODE_KERNEL]
     work, per_token = algorithmic_work(T, HQ, HV, D, C, 1, NB)
     kernels = {}

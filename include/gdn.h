@@ -22,8 +22,9 @@
  *  - Invalid arguments return an error status before anything is enqueued;
  *    gdn_last_error_message() then says which argument.
  *  - Supported: dk == dv in {16, 128}; chunk in {16, 64}; h_v % h_qk == 0;
- *    dtype GDN_DTYPE_F32 or GDN_DTYPE_BF16 for q, k, v and o. Gates and
- *    states are always fp32.
+ *    dtype GDN_DTYPE_F32 or GDN_DTYPE_BF16 for q, k, v and o, except fp32
+ *    prefill at head dim 128 with chunk 64 (GDN_ERROR_NOT_SUPPORTED; use
+ *    chunk 16). Gates and states are always fp32.
  */
 #ifndef GDN_H_
 #define GDN_H_
@@ -95,15 +96,16 @@ gdn_status_t gdn_chunk_fwd(const gdn_dims_t* dims,
                            hipStream_t stream);
 
 /*
- * Diagnostic variant of gdn_chunk_fwd that enqueues only kernels
- * first_stage..last_stage (1 = gate prefix and chunk table, 2 = K K^T and
- * (I + A)^{-1}, 3 = W and Ut, 4 = state scan, 5 = outputs), so a profiler or
- * benchmark can put events between them. Arguments are those of
- * gdn_chunk_fwd. Stages after the first read what earlier stages left in
- * `workspace`, so a call starting at stage s > 1 must follow calls that ran
- * stages 1..s-1 with identical arguments and workspace on the same stream.
- * gdn_chunk_fwd is gdn_chunk_fwd_stages(..., 1, 5). Returns
- * GDN_ERROR_INVALID_VALUE unless 1 <= first_stage <= last_stage <= 5.
+ * Diagnostic variant of gdn_chunk_fwd that enqueues only launches
+ * first_stage..last_stage, so a profiler or benchmark can put events between
+ * them: 1 = gate prefix sums and chunk table; 2 = K K^T, Q K^T and
+ * (I + A)^{-1}; 3 = the fused W/U construction, inter-chunk state scan and
+ * output products. Arguments are those of gdn_chunk_fwd. Stages after the
+ * first read what earlier stages left in `workspace`, so a call starting at
+ * stage s > 1 must follow calls that ran stages 1..s-1 with identical
+ * arguments and workspace on the same stream. gdn_chunk_fwd is
+ * gdn_chunk_fwd_stages(..., 1, 3). Returns GDN_ERROR_INVALID_VALUE unless
+ * 1 <= first_stage <= last_stage <= 3.
  */
 gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims,
                                   const void* q, const void* k, const void* v,
@@ -152,12 +154,10 @@ typedef struct {
   size_t chunk_table;  /* int32 [max_chunks][4]: seq, first token, length, index in seq */
   size_t seq_chunk_offset; /* int32 [N+1]: first compact chunk of each sequence */
   size_t gate_prefix;  /* fp32 [max_chunks][h_v][C]: in-chunk inclusive prefix of log a */
-  size_t tinv;         /* dtype [max_chunks][h_v][C][C]: (I + A)^{-1}, row-major */
-  size_t key_t;        /* dtype [max_chunks][h_qk][dk][C]: keys of the chunk, transposed */
-  size_t w;            /* dtype [max_chunks][h_v][C][dk]: W, row-major */
-  size_t u_tilde;      /* dtype, MFMA accumulator order (see the kernels) */
-  size_t u;            /* dtype, MFMA operand order (see the kernels) */
-  size_t s_chunk;      /* dtype, MFMA operand order (see the kernels) */
+  size_t beta_chunk;   /* fp32 [max_chunks][h_v][C]: b of each chunk row, 0 past its end */
+  size_t tinv;         /* dtype [max_chunks][h_v]: (I + A)^{-1} as MFMA fragments */
+  size_t key_t;        /* dtype [max_chunks][h_qk]: K^T as MFMA fragments */
+  size_t qk;           /* dtype [max_chunks][h_qk]: q_r . k_j (j-tile <= r-tile) as fragments */
   size_t total;        /* == gdn_chunk_fwd_workspace_bytes(dims) */
   int64_t max_chunks;  /* floor(T / C) + N, the bound on the number of chunks */
 } gdn_workspace_layout_t;

@@ -32,10 +32,9 @@ class GdnDims(ctypes.Structure):
 
 class GdnWorkspaceLayout(ctypes.Structure):
     _fields_ = [("chunk_table", ctypes.c_size_t), ("seq_chunk_offset", ctypes.c_size_t),
-                ("gate_prefix", ctypes.c_size_t), ("tinv", ctypes.c_size_t),
-                ("key_t", ctypes.c_size_t), ("w", ctypes.c_size_t),
-                ("u_tilde", ctypes.c_size_t), ("u", ctypes.c_size_t),
-                ("s_chunk", ctypes.c_size_t), ("total", ctypes.c_size_t),
+                ("gate_prefix", ctypes.c_size_t), ("beta_chunk", ctypes.c_size_t),
+                ("tinv", ctypes.c_size_t), ("key_t", ctypes.c_size_t),
+                ("qk", ctypes.c_size_t), ("total", ctypes.c_size_t),
                 ("max_chunks", ctypes.c_int64)]
 
 
@@ -116,6 +115,8 @@ def _need(t, name, device, dtype=None, shape=None):
 def gdn_chunk_fwd_workspace_bytes(dims):
     n = load_library().gdn_chunk_fwd_workspace_bytes(ctypes.byref(dims))
     if n == 0:
+        # the size query has no status; the layout query reports the reason
+        gdn_chunk_fwd_workspace_layout(dims)
         raise GdnError(1, load_library().gdn_last_error_message().decode())
     return n
 

@@ -19,8 +19,11 @@ LIBRARY = os.path.join(HERE, "libgdn.so")
 SOURCES = ["gdn_api.cpp", "gdn_prefill.hip", "gdn_decode.hip"]
 ARCH = "gfx950"
 
-# Packed-fp32 instructions are disabled for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed-fp32 instructions are disabled for all device code. MFMA results
+# are kept in ordinary VGPRs (the accumulation-register form makes the
+# compiler shuffle accumulator arrays through v_accvgpr moves every loop).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc():

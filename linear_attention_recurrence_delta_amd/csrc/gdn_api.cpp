@@ -55,6 +55,8 @@ gdn_status_t check_dims(const gdn_dims_t* d, bool decode) {
   } else {
     if (d->chunk < 1) return fail(GDN_ERROR_INVALID_VALUE, "chunk must be >= 1");
     if (d->chunk != 16 && d->chunk != 64) return fail(GDN_ERROR_NOT_SUPPORTED, "chunk %d not supported (16 or 64)", d->chunk);
+    if (!gdn::prefill_supported(d->dtype, d->dk, d->chunk))
+      return fail(GDN_ERROR_NOT_SUPPORTED, "prefill with fp32 inputs at head dim %d needs chunk 16", d->dk);
   }
   return GDN_SUCCESS;
 }
@@ -68,7 +70,7 @@ Layout compute_layout(const gdn_dims_t& d) {
   const size_t esz = d.dtype == GDN_DTYPE_F32 ? 4 : 2;
   const size_t D = d.dk, C = d.chunk, N = d.num_seqs, T = d.total_tokens;
   const size_t HQ = d.h_qk, HV = d.h_v;
-  const size_t CT = C / 16, DT = D / 16, CKS = (CT + 1) / 2, DKS = (DT + 1) / 2;
+  const size_t CT = C / 16, DT = D / 16, CKS = (CT + 1) / 2;
   const size_t NC = T / C + N;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -81,12 +83,10 @@ Layout compute_layout(const gdn_dims_t& d) {
   L.v.chunk_table = take(NC * 16);
   L.v.seq_chunk_offset = take((N + 1) * 4);
   L.v.gate_prefix = take(NC * HV * C * 4);
-  L.v.tinv = take(NC * HV * C * C * esz);
-  L.v.key_t = take(NC * HQ * D * C * esz);
-  L.v.w = take(NC * HV * C * D * esz);
-  L.v.u_tilde = take(NC * HV * C * D * esz);
-  L.v.u = take(NC * HV * DT * CKS * 512 * esz);
-  L.v.s_chunk = take(NC * HV * DT * DKS * 512 * esz);
+  L.v.beta_chunk = take(NC * HV * C * 4);
+  L.v.tinv = take(NC * HV * CT * CKS * 512 * esz);
+  L.v.key_t = take(NC * HQ * DT * CKS * 512 * esz);
+  L.v.qk = take(NC * HQ * CT * CKS * 512 * esz);
   L.v.total = off;
   return L;
 }
@@ -132,7 +132,7 @@ gdn_status_t gdn_chunk_fwd(const gdn_dims_t* dims, const void* q, const void* k,
                            const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
   return gdn_chunk_fwd_stages(dims, q, k, v, log_alpha, beta, init_state, cu_seqlens, o, final_state,
-                              workspace, workspace_bytes, stream, 1, 5);
+                              workspace, workspace_bytes, stream, 1, gdn::kPrefillStages);
 }
 
 gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
@@ -140,8 +140,9 @@ gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims, const void* q, const v
                                   const int32_t* cu_seqlens, void* o, float* final_state,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream,
                                   int first_stage, int last_stage) {
-  if (first_stage < 1 || last_stage > 5 || first_stage > last_stage)
-    return fail(GDN_ERROR_INVALID_VALUE, "stages %d..%d: need 1 <= first <= last <= 5", first_stage, last_stage);
+  if (first_stage < 1 || last_stage > gdn::kPrefillStages || first_stage > last_stage)
+    return fail(GDN_ERROR_INVALID_VALUE, "stages %d..%d: need 1 <= first <= last <= %d", first_stage,
+                last_stage, gdn::kPrefillStages);
   gdn_status_t st = check_dims(dims, false);
   if (st != GDN_SUCCESS) return st;
   const gdn_dims_t& d = *dims;
@@ -182,12 +183,10 @@ gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims, const void* q, const v
   a.chunk_table = reinterpret_cast<int32_t*>(ws + L.v.chunk_table);
   a.seq_chunk_offset = reinterpret_cast<int32_t*>(ws + L.v.seq_chunk_offset);
   a.gate_prefix = reinterpret_cast<float*>(ws + L.v.gate_prefix);
+  a.beta_chunk = reinterpret_cast<float*>(ws + L.v.beta_chunk);
   a.tinv = ws + L.v.tinv;
   a.key_t = ws + L.v.key_t;
-  a.w = ws + L.v.w;
-  a.u_tilde = ws + L.v.u_tilde;
-  a.u = ws + L.v.u;
-  a.s_chunk = ws + L.v.s_chunk;
+  a.qk = ws + L.v.qk;
   a.num_seqs = d.num_seqs;
   a.total_tokens = d.total_tokens;
   a.max_chunks = L.v.max_chunks;

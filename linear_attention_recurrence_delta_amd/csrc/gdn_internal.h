@@ -19,16 +19,14 @@ struct PrefillArgs {
   const int32_t* cu_seqlens;  // [N+1] or null (one sequence)
   void* o;                  // [T, HV, D]
   float* final_state;       // [N, HV, D, D] or null
-  // workspace
-  int32_t* chunk_table;     // [NC][4]
+  // workspace (MFMA fragment layouts are described in gdn_prefill.hip)
+  int32_t* chunk_table;     // [NC][4]: sequence, first token, length, index in sequence
   int32_t* seq_chunk_offset;  // [N+1]
-  float* gate_prefix;       // [NC][HV][C]
-  void* tinv;               // [NC][HV][C][C]
-  void* key_t;              // [NC][HQ][D][C]
-  void* w;                  // [NC][HV][C][D]
-  void* u_tilde;            // [NC][HV][D/16][C/16][64][4]
-  void* u;                  // [NC][HV][D/16][ceil(C/32)][64][8]
-  void* s_chunk;            // [NC][HV][D/16][ceil(D/32)][64][8]
+  float* gate_prefix;       // [NC][HV][C]  in-chunk inclusive prefix of log a
+  float* beta_chunk;        // [NC][HV][C]  b per chunk row (0 past the chunk end)
+  void* tinv;               // [NC][HV] fragments of (I + A)^{-1}
+  void* key_t;              // [NC][HQ] fragments of K^T
+  void* qk;                 // [NC][HQ] fragments of (q_r . k_j)
   int64_t num_seqs;         // N
   int64_t total_tokens;     // T
   int64_t max_chunks;       // NC = floor(T/C) + N
@@ -51,8 +49,14 @@ struct DecodeArgs {
   int32_t group;
 };
 
+// Prefill launch stages (1-based): 1 gate prefix, 2 (I + A)^{-1}, 3 fused scan.
+constexpr int kPrefillStages = 3;
+
+// True when the fused scan kernel has an instance for (dtype, head_dim, chunk).
+bool prefill_supported(int dtype, int head_dim, int chunk);
+
 // dtype: 0 = fp32, 1 = bf16. Returns the first launch error, if any.
-// Stages first..last of the five prefill kernels (1-based, inclusive).
+// Runs stages first..last (1-based, inclusive).
 hipError_t launch_prefill(const PrefillArgs& args, int dtype, int head_dim, int chunk,
                           hipStream_t stream, int first_stage, int last_stage);
 hipError_t launch_decode(const DecodeArgs& args, int dtype, int head_dim, hipStream_t stream);

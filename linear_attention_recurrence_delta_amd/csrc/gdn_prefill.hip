@@ -6,20 +6,34 @@
 // the first form of its update equation. For one V head and a chunk of L <= C
 // tokens entering with state S0 (r, i index tokens in the chunk):
 //
-//   g_r    = sum_{j<=r} log a_j                               kernel 1
-//   A[r,i] = b_r (k_r . k_i) exp(g_r - g_i)  (i < r)          kernel 2
-//   Tinv   = (I + A)^{-1}                                     kernel 2
-//   W      = Tinv diag(b exp(g)) K,  Ut = Tinv diag(b) V      kernel 3
-//   U      = Ut - W S0                                        kernel 4
-//   S_end  = exp(g_L) S0 + (exp(g_L - g) * K)^T U             kernel 4
-//   O      = diag(exp(g)) Q S0 + (Q K^T * Dincl) U            kernel 5
+//   g_r    = sum_{j<=r} log a_j                          kernel 1
+//   A[r,i] = b_r (k_r . k_i) exp(g_r - g_i)  (i < r)     kernel 2
+//   Tinv   = (I + A)^{-1}                                kernel 2
+//   W      = Tinv diag(b exp(g)) K                       kernel 3 (producer waves)
+//   Ut     = Tinv diag(b) V                              kernel 3 (producer waves)
+//   U      = Ut - W S0                                   kernel 3 (scan waves)
+//   S_end  = exp(g_L) S0 + (exp(g_L - g) * K)^T U        kernel 3 (scan waves)
+//   O      = diag(exp(g)) Q S0 + (Q K^T * Dincl) U       kernel 3 (scan waves)
 //            Dincl[r,i] = exp(g_r - g_i) for i <= r, else 0
 //
 // The rows of U are the delta vectors u_r = b_r (v_r - a_r S_{r-1}^T k_r)
 // of the token-serial form, and O is o_r = S_r^T q_r with the post-update
-// state. Every column of the state (a dv index) evolves independently, which
-// is what lets kernel 4 give each wave a 16-column slice of one head's state.
-// exp() is only ever taken of g_r - g_i with i <= r (a non-positive number).
+// state. Every column (dv index) of the state evolves independently, so the
+// scan splits a head's state into 16-column slices. exp() is only ever taken
+// of g_r - g_i with i <= r, a non-positive number.
+//
+// Kernel 3 fuses the W/Ut construction, the inter-chunk state scan and the
+// output products: W, Ut, U and the per-chunk states never leave the chip.
+//
+// Fragment layouts (see gdn_device.h for the lane/element order): a
+// "fragment" is 64 lanes x 8 elements; "frag (a, s)" of a matrix X means
+// lane l holds row/col a*16 + l%16 and the 8 contraction indices of step s.
+//   key_t [c][hq][D/16][C32] : frag (dt, s) of K^T   (row d,     k = token i)
+//   tinv  [c][hv][C/16][C32] : frag (rt, s) of Tinv  (row r,     k = token i)
+//   qk    [c][hq][C/16][C32] : frag (nt, s) of (q_r . k_j) (col r = query, k = key j)
+// with C32 = ceil(C/32); entries past the chunk end are zero.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -29,14 +43,40 @@ namespace {
 
 constexpr int kBlock = 256;
 
+template <typename E, int D, int C>
+struct Cfg {
+  static constexpr int DT = D / 16, CT = C / 16;
+  static constexpr int DKS = (DT + 1) / 2, CKS = (CT + 1) / 2;
+  static constexpr int NS = DT >= 2 ? 2 : 1;   // 16-column state slices per scan workgroup
+  static constexpr int BV = 16 * NS;           // state columns per scan workgroup
+  static constexpr int NCB = D / BV;           // scan workgroups per (sequence, V head)
+  static constexpr int NW = 4;                 // waves per scan workgroup
+  static constexpr int NPROD = NW - NS;        // producer waves
+  static constexpr int KT_FR = DT * CKS;       // K^T fragments per chunk
+  static constexpr int T_FR = CT * CKS;        // Tinv fragments per chunk
+  static constexpr int QK_FR = CT * CKS;       // q.k fragments per chunk
+  static constexpr int Q_FR = CT * DKS;        // Q fragments per chunk
+  static constexpr int W_FR = CT * DKS;        // W fragments per chunk
+  static constexpr int VLD = C + 8;            // row stride of the transposed V slice
+};
+
+// Contraction index of fragment element e at 32-step s for lane quad q.
+__device__ __forceinline__ int frag_k(int s, int quad, int e) {
+  return 32 * s + (e < 4 ? 4 * quad + e : 16 + 4 * quad + (e - 4));
+}
+
+// True when fragment step s of query tile nt holds only keys after every
+// query of the tile (the causal mask makes it zero).
+__device__ __forceinline__ constexpr bool causal_zero(int nt, int s) { return 32 * s > 16 * nt + 15; }
+
 // --------------------------------------------------------------------------
-// Kernel 1: chunk table and in-chunk prefix sums of log a.
+// Kernel 1: chunk table, in-chunk prefix sums of log a and per-chunk b.
 // One workgroup per compact chunk slot c in [0, floor(T/C) + N). Each group
 // scans the per-sequence chunk counts ceil(L_n / C) to find which sequence
 // owns slot c (slots past the last chunk are marked seq = -1); group 0 also
 // publishes the per-sequence first-chunk offsets. Then one thread per V head
-// writes g[c][h][r] for r < C; rows past a partial chunk's end repeat the
-// last valid prefix (their log a is taken as 0).
+// writes g[c][h][r] and b[c][h][r] for r < C; past a partial chunk's end g
+// repeats the last valid prefix (log a taken as 0) and b is 0.
 // --------------------------------------------------------------------------
 template <int C>
 __global__ __launch_bounds__(kBlock) void gdn_k1_gate_prefix(const PrefillArgs a) {
@@ -88,26 +128,35 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_gate_prefix(const PrefillArgs a
   for (int h = tid; h < a.h_v; h += kBlock) {
     float acc = 0.f;
     float* gout = a.gate_prefix + (c * a.h_v + h) * C;
+    float* bout = a.beta_chunk + (c * a.h_v + h) * C;
     for (int r = 0; r < C; ++r) {
-      if (r < len) acc += a.log_alpha[(int64_t)(start + r) * a.h_v + h];
+      float b = 0.f;
+      if (r < len) {
+        acc += a.log_alpha[(int64_t)(start + r) * a.h_v + h];
+        b = a.beta[(int64_t)(start + r) * a.h_v + h];
+      }
       gout[r] = acc;
+      bout[r] = b;
     }
   }
 }
 
 // --------------------------------------------------------------------------
-// Kernel 2: A = strict_lower(b_r (k_r . k_i) exp(g_r - g_i)) and
-// Tinv = (I + A)^{-1}. One workgroup per (chunk, QK head): K K^T is formed
-// once with MFMA and shared by the QK head's V heads; each wave then inverts
-// one V head's unit lower-triangular I + A by forward substitution with one
-// lane per column j (x_r = delta_rj - sum_{i<r} A[r,i] x_i, fp32 in
-// registers, A read from LDS as a broadcast). Also writes the chunk's keys
-// transposed ([d][r], zero past the chunk end) for kernels 3 and 4.
+// Kernel 2: per (chunk, QK head): K^T fragments, the q.k fragments, and for
+// each of the QK head's V heads A = strict_lower(b_r (k_r . k_i)
+// exp(g_r - g_i)) and Tinv = (I + A)^{-1}.
+// K K^T and Q K^T are formed once with MFMA and shared by the V heads. Each
+// wave inverts one V head's unit lower-triangular I + A by forward
+// substitution, one lane per column j: x_r = delta_rj - sum_{i<r} A[r,i] x_i
+// in fp32 registers (four partial sums break the dependency chain), A read
+// from LDS as a broadcast. Tinv is then re-read from LDS as fragments.
 // --------------------------------------------------------------------------
 template <typename E, int D, int C>
 __global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a) {
-  constexpr int CT = C / 16, DKS = (D / 16 + 1) / 2, KLD = D + 8, NW = kBlock / 64;
+  using G = Cfg<E, D, C>;
+  constexpr int CT = G::CT, CKS = G::CKS, DKS = G::DKS, KLD = D + 8, NW = kBlock / 64;
   __shared__ __attribute__((aligned(16))) E Ks[C * KLD];
+  __shared__ __attribute__((aligned(16))) E Qs[C * KLD];
   __shared__ __attribute__((aligned(16))) float KK[C * C];
   __shared__ __attribute__((aligned(16))) float Ab[NW][C * C];
   __shared__ float sb[NW][C];
@@ -117,38 +166,73 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a
   const int start = tab.y, len = tab.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, l16 = lane & 15;
   const E* kg = static_cast<const E*>(a.k);
+  const E* qg = static_cast<const E*>(a.q);
 
   for (int idx = tid; idx < C * D; idx += kBlock) {
     const int r = idx / D, d = idx % D;
-    Ks[r * KLD + d] = (r < len) ? kg[((int64_t)(start + r) * a.h_qk + hq) * D + d] : to_e<E>(0.f);
+    const int64_t gi = ((int64_t)(start + r) * a.h_qk + hq) * D + d;
+    Ks[r * KLD + d] = (r < len) ? kg[gi] : to_e<E>(0.f);
+    Qs[r * KLD + d] = (r < len) ? qg[gi] : to_e<E>(0.f);
   }
   __syncthreads();
-  E* ktg = static_cast<E*>(a.key_t) + ((int64_t)c * a.h_qk + hq) * D * C;
-  for (int idx = tid; idx < C * D; idx += kBlock) {
-    const int d = idx / C, r = idx % C;
-    ktg[idx] = Ks[r * KLD + d];
+
+  // K^T fragments: frag (dt, s), lane row d, elements token i.
+  Frag<E>* ktg = reinterpret_cast<Frag<E>*>(a.key_t) + ((int64_t)c * a.h_qk + hq) * G::KT_FR * 64;
+  for (int it = tid; it < G::KT_FR * 64; it += kBlock) {
+    const int f = it / 64, ln = it % 64, dt = f / CKS, s = f % CKS, q4 = ln >> 4;
+    const int d = 16 * dt + (ln & 15);
+    Frag<E> v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = frag_k(s, q4, e);
+      v[e] = (i < C) ? Ks[i * KLD + d] : to_e<E>(0.f);
+    }
+    ktg[it] = v;
   }
-  for (int t = wave; t < CT * CT; t += NW) {
-    const int mi = t / CT, ni = t % CT;
-    if (ni > mi) continue;
+
+  // K K^T (lower tiles, into KK) and q.k (tiles with key tile <= query tile,
+  // into Ab[0] as [query r][key j]).
+  float* QKl = Ab[0];
+  for (int t = wave; t < 2 * CT * CT; t += NW) {
+    const bool is_qk = t >= CT * CT;
+    const int tt = is_qk ? t - CT * CT : t;
+    const int mi = tt / CT, ni = tt % CT;   // KK: row tile mi, col tile ni; q.k: key tile mi, query tile ni
+    if (ni > mi && !is_qk) continue;
+    if (mi > ni && is_qk) continue;
+    const E* brow = is_qk ? &Qs[(16 * ni + l16) * KLD] : &Ks[(16 * ni + l16) * KLD];
     f32x4 acc = zero4();
 #pragma unroll
-    for (int ks = 0; ks < DKS; ++ks) {
-      const Frag<E> fa = load_frag<E>(&Ks[(16 * mi + l16) * KLD + 32 * ks], quad, D - 32 * ks);
-      const Frag<E> fb = load_frag<E>(&Ks[(16 * ni + l16) * KLD + 32 * ks], quad, D - 32 * ks);
-      acc = mma(fa, fb, acc);
-    }
+    for (int ks = 0; ks < DKS; ++ks)
+      acc = mma(load_frag<E>(&Ks[(16 * mi + l16) * KLD + 32 * ks], quad, D - 32 * ks),
+                load_frag<E>(brow + 32 * ks, quad, D - 32 * ks), acc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) KK[(16 * mi + 4 * quad + i) * C + 16 * ni + l16] = acc[i];
+    for (int i = 0; i < 4; ++i) {
+      if (!is_qk) KK[(16 * mi + 4 * quad + i) * C + 16 * ni + l16] = acc[i];
+      else QKl[(16 * ni + l16) * C + 16 * mi + 4 * quad + i] = acc[i];
+    }
+  }
+  __syncthreads();
+  // q.k fragments: frag (nt, s), lane col = query r, elements key j.
+  Frag<E>* qkg = reinterpret_cast<Frag<E>*>(a.qk) + ((int64_t)c * a.h_qk + hq) * G::QK_FR * 64;
+  for (int it = tid; it < G::QK_FR * 64; it += kBlock) {
+    const int f = it / 64, ln = it % 64, nt = f / CKS, s = f % CKS, q4 = ln >> 4;
+    const int r = 16 * nt + (ln & 15);
+    Frag<E> v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = frag_k(s, q4, e);
+      v[e] = (j < C && (j >> 4) <= nt) ? to_e<E>(QKl[r * C + j]) : to_e<E>(0.f);
+    }
+    qkg[it] = v;
   }
   __syncthreads();
 
   const float* gch = a.gate_prefix + (int64_t)c * a.h_v * C;
+  const float* bch = a.beta_chunk + (int64_t)c * a.h_v * C;
   for (int h0 = 0; h0 < a.group; h0 += NW) {
     const int nh = min(NW, a.group - h0);
     for (int w = 0; w < nh; ++w) {
-      const int hv = hq * a.group + h0 + w;
-      if (tid < C) sb[w][tid] = (tid < len) ? a.beta[(int64_t)(start + tid) * a.h_v + hv] : 0.f;
+      if (tid < C) sb[w][tid] = bch[(int64_t)(hq * a.group + h0 + w) * C + tid];
     }
     __syncthreads();
     for (int w = 0; w < nh; ++w) {
@@ -156,26 +240,47 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a
       for (int idx = tid; idx < C * C; idx += kBlock) {
         const int r = idx / C, i = idx % C;
         float val = 0.f;
-        if (i < r && r < len) val = sb[w][r] * KK[idx] * expf(gh[r] - gh[i]);
+        if (i < r && r < len) val = sb[w][r] * KK[idx] * __expf(gh[r] - gh[i]);
         Ab[w][idx] = val;
       }
     }
     __syncthreads();
     if (wave < nh) {
       const int hv = hq * a.group + h0 + wave;
-      const float* Aw = Ab[wave];
+      float* Aw = Ab[wave];
       float x[C];
 #pragma unroll
       for (int r = 0; r < C; ++r) {
-        float s = (r == lane) ? 1.f : 0.f;
+        float s0 = (r == lane) ? 1.f : 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
-        for (int i = 0; i < r; ++i) s -= Aw[r * C + i] * x[i];
-        x[r] = s;
+        for (int i = 0; i + 3 < r; i += 4) {
+          s0 -= Aw[r * C + i] * x[i];
+          s1 -= Aw[r * C + i + 1] * x[i + 1];
+          s2 -= Aw[r * C + i + 2] * x[i + 2];
+          s3 -= Aw[r * C + i + 3] * x[i + 3];
+        }
+#pragma unroll
+        for (int i = r & ~3; i < r; ++i) s0 -= Aw[r * C + i] * x[i];
+        x[r] = (s0 + s1) + (s2 + s3);
       }
+      // every lane's reads of A are complete (their values were consumed
+      // above); the wave now overwrites its own buffer with Tinv (row-major)
       if (lane < C) {
-        E* tg = static_cast<E*>(a.tinv) + ((int64_t)c * a.h_v + hv) * C * C;
 #pragma unroll
-        for (int r = 0; r < C; ++r) tg[r * C + lane] = to_e<E>(x[r]);
+        for (int r = 0; r < C; ++r) Aw[r * C + lane] = x[r];
+      }
+      Frag<E>* tg = reinterpret_cast<Frag<E>*>(a.tinv) + ((int64_t)c * a.h_v + hv) * G::T_FR * 64;
+#pragma unroll
+      for (int f = 0; f < G::T_FR; ++f) {
+        const int rt = f / CKS, s = f % CKS;
+        const int r = 16 * rt + l16;
+        Frag<E> v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = frag_k(s, quad, e);
+          v[e] = (i < C) ? to_e<E>(Aw[r * C + i]) : to_e<E>(0.f);
+        }
+        tg[f * 64 + lane] = v;
       }
     }
     __syncthreads();
@@ -183,242 +288,377 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a
 }
 
 // --------------------------------------------------------------------------
-// Kernel 3: W = Tinv diag(b exp(g)) K and Ut = Tinv diag(b) V. One
-// workgroup per (chunk, V head); Tinv and the two right operands (stored
-// transposed, contraction index contiguous) are staged in LDS, and the
-// 2 x (C/16) x (D/16) output tiles are spread over the four waves. W is
-// written row-major; Ut is written in accumulator order
-// ([D/16 col tile][C/16 row tile][lane][4]) so kernel 4 reads it back in the
-// register layout it needs with one vector load per tile.
+// Kernel 3: fused W/Ut construction, inter-chunk state scan and outputs.
+// One workgroup per (sequence, V head, block of BV state columns), eight
+// waves, looping over the sequence's chunks in order with a software
+// pipeline:
+//   scan waves (one per 16-column slice) process chunk c: with the slice of
+//     the state S (D x 16 fp32) held in MFMA accumulators for the whole
+//     sequence,
+//       O^T  = diag(exp(g)) applied to S^T Q^T      (inter-chunk output)
+//       U    = Ut - W S                            (S's accumulator tiles are
+//                                                   the B fragments here)
+//       O^T += U^T (Q K^T * Dincl)^T                (U's tiles are the A fragments)
+//       S    = exp(g_L) S + K^T (exp(g_L - g) * U)
+//     and store the chunk's outputs for their columns;
+//   producer waves build chunk c+1's W and Ut fragments and the masked,
+//     decayed (q.k) fragments in LDS, and double as loaders: they fetch
+//     chunk c+3's K^T, Tinv, q.k, g, b and V slice (and chunk c+2's Q) into
+//     one of two register sets while the other set, fetched one iteration
+//     earlier, is written into LDS for chunk c+2 between the barriers.
+// Every LDS region is either double-buffered by chunk parity or written only
+// between the two barriers of an iteration after its last reader is done.
 // --------------------------------------------------------------------------
+constexpr int kScanBlock = 512;
+
 template <typename E, int D, int C>
-__global__ __launch_bounds__(kBlock) void gdn_k3_wu(const PrefillArgs a) {
-  constexpr int CT = C / 16, DT = D / 16, CKS = (CT + 1) / 2, LD = C + 8, NW = kBlock / 64;
-  __shared__ __attribute__((aligned(16))) E Ts[C * LD];
-  __shared__ __attribute__((aligned(16))) E Kb[D * LD];
-  __shared__ __attribute__((aligned(16))) E Vb[D * LD];
-  __shared__ float sb[C], sbg[C];
-  const int c = blockIdx.x, hv = blockIdx.y;
-  const int4 tab = reinterpret_cast<const int4*>(a.chunk_table)[c];
-  if (tab.x < 0) return;
-  const int start = tab.y, len = tab.z;
-  const int hq = hv / a.group;
+struct ScanSmem {
+  using G = Cfg<E, D, C>;
+  Frag<E> kt[2][G::KT_FR * 64];        // K^T fragments, by chunk parity
+  Frag<E> qf[G::Q_FR * 64];            // Q fragments of the chunk being scanned
+  Frag<E> tf[G::T_FR * 64];            // Tinv fragments of the chunk being produced
+  Frag<E> qk[G::QK_FR * 64];           // q.k fragments of the chunk being produced
+  Frag<E> wf[2][G::W_FR * 64];         // W fragments, by chunk parity
+  Frag<E> pf[2][G::QK_FR * 64];        // masked, decayed q.k fragments, by parity
+  f32x4 uf[2][G::NS * G::CT * 64];     // Ut accumulator tiles, by parity
+  E vt[G::BV * G::VLD];                // V slice of the chunk being produced, transposed
+  float gb[2][2][C];                   // g and b, by chunk parity
+};
+
+// One register set of loader data: a chunk's operands plus the next chunk's Q.
+template <typename E, int D, int C>
+struct ScanFetch {
+  using G = Cfg<E, D, C>;
+  static constexpr int NL = kScanBlock - 64 * G::NS;                 // loader threads
+  static constexpr int FR16 = (int)sizeof(Frag<E>) / 16;             // 16-byte units per lane-fragment
+  static constexpr int N_KT = G::KT_FR * 64 * FR16, N_T = G::T_FR * 64 * FR16, N_QK = G::QK_FR * 64 * FR16;
+  static constexpr int N_GB = 2 * C * 4 / 16;
+  static constexpr int VU = 16 / (int)sizeof(E);                     // V elements per 16-byte unit
+  static constexpr int N_V = C * G::BV / VU;
+  static constexpr int N_Q = G::Q_FR * 64;                           // lane-fragments of Q
+  static constexpr int P_KT = (N_KT + NL - 1) / NL, P_T = (N_T + NL - 1) / NL;
+  static constexpr int P_QK = (N_QK + NL - 1) / NL, P_V = (N_V + NL - 1) / NL;
+  static constexpr int P_Q = (N_Q + NL - 1) / NL, P_GB = (N_GB + NL - 1) / NL;
+  typedef E VUnit __attribute__((ext_vector_type(VU)));             // one 16-byte unit of V
+  u32x4 kt[P_KT], t[P_T], qk[P_QK], gb[P_GB];
+  VUnit v[P_V];
+  Frag<E> q[P_Q];
+};
+
+template <typename E, int D, int C>
+__global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
+  using G = Cfg<E, D, C>;
+  using F = ScanFetch<E, D, C>;
+  constexpr int DT = G::DT, CT = G::CT, DKS = G::DKS, CKS = G::CKS, NS = G::NS, BV = G::BV;
+  constexpr int NPROD = kScanBlock / 64 - NS;
+  __shared__ ScanSmem<E, D, C> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, l16 = lane & 15;
-  const int64_t chv = (int64_t)c * a.h_v + hv;
-
-  if (tid < C) {
-    const float b = (tid < len) ? a.beta[(int64_t)(start + tid) * a.h_v + hv] : 0.f;
-    sb[tid] = b;
-    sbg[tid] = b * expf(a.gate_prefix[chv * C + tid]);
-  }
-  const E* tg = static_cast<const E*>(a.tinv) + chv * C * C;
-  for (int idx = tid; idx < C * C; idx += kBlock) Ts[(idx / C) * LD + idx % C] = tg[idx];
-  __syncthreads();
-  const E* ktg = static_cast<const E*>(a.key_t) + ((int64_t)c * a.h_qk + hq) * D * C;
-  for (int idx = tid; idx < C * D; idx += kBlock) {
-    const int d = idx / C, i = idx % C;
-    Kb[d * LD + i] = to_e<E>(to_f(ktg[idx]) * sbg[i]);
-  }
-  const E* vg = static_cast<const E*>(a.v);
-  for (int idx = tid; idx < C * D; idx += kBlock) {
-    const int i = idx / D, d = idx % D;
-    Vb[d * LD + i] = (i < len) ? to_e<E>(to_f(vg[((int64_t)(start + i) * a.h_v + hv) * D + d]) * sb[i])
-                               : to_e<E>(0.f);
-  }
-  __syncthreads();
-
-  E* wg = static_cast<E*>(a.w) + chv * C * D;
-  E* utg = static_cast<E*>(a.u_tilde) + chv * C * D;
-  for (int t = wave; t < 2 * CT * DT; t += NW) {
-    const bool is_u = t >= CT * DT;
-    const int tt = is_u ? t - CT * DT : t;
-    const int mt = tt / DT, nt = tt % DT;
-    const E* B = is_u ? Vb : Kb;
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int ks = 0; ks < CKS; ++ks) {
-      const Frag<E> fa = load_frag<E>(&Ts[(16 * mt + l16) * LD + 32 * ks], quad, C - 32 * ks);
-      const Frag<E> fb = load_frag<E>(&B[(16 * nt + l16) * LD + 32 * ks], quad, C - 32 * ks);
-      acc = mma(fa, fb, acc);
-    }
-    if (!is_u) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wg[(16 * mt + 4 * quad + i) * D + 16 * nt + l16] = to_e<E>(acc[i]);
-    } else {
-      Half<E> h;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) h[i] = to_e<E>(acc[i]);
-      *reinterpret_cast<Half<E>*>(utg + ((nt * CT + mt) * 64 + lane) * 4) = h;
-    }
-  }
-}
-
-// --------------------------------------------------------------------------
-// Kernel 4: inter-chunk state scan. One wave per (sequence, V head, 16-column
-// slice of the state); the slice (D x 16 fp32) lives in MFMA accumulators for
-// the whole sequence. Per chunk, in order:
-//   Sc = S (stored as operand fragments for kernel 5)
-//   U  = Ut - W Sc                     (the state's accumulator tiles are
-//                                       already the B fragments of this product)
-//   S  = exp(g_L) Sc + K^T (exp(g_L - g) * U)
-//                                      (U's accumulator tiles are the B fragments)
-// U is stored (undecayed) as operand fragments for kernel 5. Loads of W, Ut
-// and K^T do not depend on S and are issued ahead by the compiler.
-// --------------------------------------------------------------------------
-template <typename E, int D, int C>
-__global__ __launch_bounds__(64) void gdn_k4_state_scan(const PrefillArgs a) {
-  constexpr int CT = C / 16, DT = D / 16, CKS = (CT + 1) / 2, DKS = (DT + 1) / 2;
-  const int lane = threadIdx.x, quad = lane >> 4, l16 = lane & 15;
   const int64_t bid = blockIdx.x;
-  const int nb = (int)(bid % DT);
-  const int hv = (int)((bid / DT) % a.h_v);
-  const int64_t n = bid / ((int64_t)DT * a.h_v);
+  const int cb = (int)(bid % G::NCB);
+  const int hv = (int)((bid / G::NCB) % a.h_v);
+  const int64_t n = bid / ((int64_t)G::NCB * a.h_v);
   const int hq = hv / a.group;
-  const int col = 16 * nb + l16;
+  const int c0 = a.seq_chunk_offset[n], c1 = a.seq_chunk_offset[n + 1];
+  // chunk x of this sequence starts at seq_start + (x - c0) * C; computing
+  // start and length here keeps table reads off the per-chunk critical path
+  const int seq_start = a.cu_seqlens ? a.cu_seqlens[n] : 0;
+  const int seq_end = a.cu_seqlens ? a.cu_seqlens[n + 1] : (int)a.total_tokens;
+  auto chunk_start = [&](int x) { return seq_start + (x - c0) * C; };
+  auto chunk_len = [&](int x) { return min(C, seq_end - chunk_start(x)); };
+  const bool is_scan = wave < NS;
+  const int slice = wave;                      // scan waves: slice index
+  const int pw = wave - NS;                    // producer waves: index
+  const int lt = tid - 64 * NS;                // loader thread index (producers only)
+  const int col0 = cb * BV;                    // first state column of this workgroup
   const int64_t state_base = (n * a.h_v + hv) * D * D;
 
+  // ---- loaders: global -> registers (chunk x's operands, chunk xq's Q) ----
+  auto fetch = [&](F& fr, int x, int xq) __attribute__((always_inline)) {
+    if (is_scan) return;
+    if (x < c1) {
+      const u32x4* ktg = reinterpret_cast<const u32x4*>(
+          reinterpret_cast<const Frag<E>*>(a.key_t) + ((int64_t)x * a.h_qk + hq) * G::KT_FR * 64);
+      const u32x4* tg = reinterpret_cast<const u32x4*>(
+          reinterpret_cast<const Frag<E>*>(a.tinv) + ((int64_t)x * a.h_v + hv) * G::T_FR * 64);
+      const u32x4* qkg = reinterpret_cast<const u32x4*>(
+          reinterpret_cast<const Frag<E>*>(a.qk) + ((int64_t)x * a.h_qk + hq) * G::QK_FR * 64);
+#pragma unroll
+      for (int p = 0; p < F::P_KT; ++p) { const int u = lt + p * F::NL; if (u < F::N_KT) fr.kt[p] = ktg[u]; }
+#pragma unroll
+      for (int p = 0; p < F::P_T; ++p) { const int u = lt + p * F::NL; if (u < F::N_T) fr.t[p] = tg[u]; }
+#pragma unroll
+      for (int p = 0; p < F::P_QK; ++p) { const int u = lt + p * F::NL; if (u < F::N_QK) fr.qk[p] = qkg[u]; }
+#pragma unroll
+      for (int p = 0; p < F::P_GB; ++p) {
+        const int u = lt + p * F::NL, half = F::N_GB / 2;
+        if (u < F::N_GB) {
+          const float* src = (u < half ? a.gate_prefix : a.beta_chunk) + ((int64_t)x * a.h_v + hv) * C;
+          fr.gb[p] = reinterpret_cast<const u32x4*>(src)[u % half];
+        }
+      }
+      const int x_start = chunk_start(x), x_len = chunk_len(x);
+      const E* vg = static_cast<const E*>(a.v);
+#pragma unroll
+      for (int p = 0; p < F::P_V; ++p) {
+        const int u = lt + p * F::NL;
+        if (u < F::N_V) {
+          const int i = u / (BV / F::VU), part = u % (BV / F::VU);
+#pragma unroll
+          for (int e = 0; e < F::VU; ++e) fr.v[p][e] = to_e<E>(0.f);
+          if (i < x_len)
+            fr.v[p] = *reinterpret_cast<const typename F::VUnit*>(
+                vg + ((int64_t)(x_start + i) * a.h_v + hv) * D + col0 + part * F::VU);
+        }
+      }
+    }
+    if (xq >= c0 && xq < c1) {
+      const int q_start = chunk_start(xq), q_len = chunk_len(xq);
+      const E* qg = static_cast<const E*>(a.q);
+#pragma unroll
+      for (int p = 0; p < F::P_Q; ++p) {
+        const int u = lt + p * F::NL;
+        if (u < F::N_Q) {
+          const int f = u / 64, ln = u % 64, nt = f / DKS, s = f % DKS;
+          const int r = 16 * nt + (ln & 15);
+          fr.q[p] = load_frag_masked<E>(qg + ((int64_t)(q_start + r) * a.h_qk + hq) * D + 32 * s, ln >> 4,
+                                        D - 32 * s, r < q_len);
+        }
+      }
+    }
+  };
+  // ---- loaders: registers -> LDS ----
+  auto store = [&](const F& fr, int x, int xq) __attribute__((always_inline)) {
+    if (is_scan) return;
+    if (x < c1) {
+      u32x4* kt = reinterpret_cast<u32x4*>(sm.kt[x & 1]);
+      u32x4* tf = reinterpret_cast<u32x4*>(sm.tf);
+      u32x4* qk = reinterpret_cast<u32x4*>(sm.qk);
+#pragma unroll
+      for (int p = 0; p < F::P_KT; ++p) { const int u = lt + p * F::NL; if (u < F::N_KT) kt[u] = fr.kt[p]; }
+#pragma unroll
+      for (int p = 0; p < F::P_T; ++p) { const int u = lt + p * F::NL; if (u < F::N_T) tf[u] = fr.t[p]; }
+#pragma unroll
+      for (int p = 0; p < F::P_QK; ++p) { const int u = lt + p * F::NL; if (u < F::N_QK) qk[u] = fr.qk[p]; }
+#pragma unroll
+      for (int p = 0; p < F::P_GB; ++p) {
+        const int u = lt + p * F::NL;
+        if (u < F::N_GB) reinterpret_cast<u32x4*>(&sm.gb[x & 1][0][0])[u] = fr.gb[p];
+      }
+#pragma unroll
+      for (int p = 0; p < F::P_V; ++p) {
+        const int u = lt + p * F::NL;
+        if (u < F::N_V) {
+          const int i = u / (BV / F::VU), part = u % (BV / F::VU);
+#pragma unroll
+          for (int e = 0; e < F::VU; ++e) sm.vt[(part * F::VU + e) * G::VLD + i] = fr.v[p][e];
+        }
+      }
+    }
+    if (xq >= c0 && xq < c1) {
+#pragma unroll
+      for (int p = 0; p < F::P_Q; ++p) { const int u = lt + p * F::NL; if (u < F::N_Q) sm.qf[u] = fr.q[p]; }
+    }
+  };
+
+  // scan waves: the slice's D x 16 state columns in accumulator tiles
   f32x4 S[DT];
-#pragma unroll
-  for (int mt = 0; mt < DT; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      S[mt][i] = a.init_state ? a.init_state[state_base + (int64_t)(16 * mt + 4 * quad + i) * D + col] : 0.f;
-  }
-  const int4* table = reinterpret_cast<const int4*>(a.chunk_table);
-  const int c0 = a.seq_chunk_offset[n], c1 = a.seq_chunk_offset[n + 1];
-  for (int c = c0; c < c1; ++c) {
-    const int len = table[c].z;
-    const int64_t chv = (int64_t)c * a.h_v + hv;
+
+  auto scan_chunk = [&](int c) __attribute__((always_inline)) {
+    const int start = chunk_start(c), len = chunk_len(c), par = c & 1;
+    const float* gs = sm.gb[par][0];
     Frag<E> Sf[DKS];
 #pragma unroll
     for (int ks = 0; ks < DKS; ++ks) Sf[ks] = acc_to_frag<E>(S[2 * ks], (2 * ks + 1 < DT) ? S[2 * ks + 1] : zero4());
-    Frag<E>* scg = reinterpret_cast<Frag<E>*>(static_cast<E*>(a.s_chunk)) + (chv * DT + nb) * DKS * 64;
+    // inter-chunk output: O^T[col][r] = sum_d S[d][col] q_r[d], times exp(g_r)
+    f32x4 O[CT];
 #pragma unroll
-    for (int ks = 0; ks < DKS; ++ks) scg[ks * 64 + lane] = Sf[ks];
-
-    const E* wg = static_cast<const E*>(a.w) + chv * C * D;
-    const Half<E>* utg = reinterpret_cast<const Half<E>*>(static_cast<const E*>(a.u_tilde) + chv * C * D) + nb * CT * 64;
+    for (int nt = 0; nt < CT; ++nt) {
+      O[nt] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks) O[nt] = mma(Sf[ks], sm.qf[(nt * DKS + ks) * 64 + lane], O[nt]);
+    }
+    // U = Ut - W S
     f32x4 U[CT];
 #pragma unroll
-    for (int mt = 0; mt < CT; ++mt) {
+    for (int rt = 0; rt < CT; ++rt) {
       f32x4 acc = zero4();
 #pragma unroll
-      for (int ks = 0; ks < DKS; ++ks)
-        acc = mma(load_frag<E>(wg + (16 * mt + l16) * D + 32 * ks, quad, D - 32 * ks), Sf[ks], acc);
-      const Half<E> ut = utg[mt * 64 + lane];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) U[mt][i] = to_f(ut[i]) - acc[i];
+      for (int ks = 0; ks < DKS; ++ks) acc = mma(sm.wf[par][(rt * DKS + ks) * 64 + lane], Sf[ks], acc);
+      U[rt] = sm.uf[par][(slice * CT + rt) * 64 + lane] - acc;
     }
-    Frag<E>* ug = reinterpret_cast<Frag<E>*>(static_cast<E*>(a.u)) + (chv * DT + nb) * CKS * 64;
 #pragma unroll
-    for (int ks = 0; ks < CKS; ++ks)
-      ug[ks * 64 + lane] = acc_to_frag<E>(U[2 * ks], (2 * ks + 1 < CT) ? U[2 * ks + 1] : zero4());
-
-    const float* gch = a.gate_prefix + chv * C;
-    const float g_last = gch[len - 1];
+    for (int nt = 0; nt < CT; ++nt) {
+      const int r = 16 * nt + l16;
+      O[nt] *= (r < len) ? __expf(gs[r]) : 0.f;
+    }
+    Frag<E> Uk[CKS];
 #pragma unroll
-    for (int mt = 0; mt < CT; ++mt) {
+    for (int ks = 0; ks < CKS; ++ks) Uk[ks] = acc_to_frag<E>(U[2 * ks], (2 * ks + 1 < CT) ? U[2 * ks + 1] : zero4());
+    // S <- exp(g_L) S + K^T (exp(g_L - g) * U)
+    const float g_last = gs[len - 1];
+#pragma unroll
+    for (int rt = 0; rt < CT; ++rt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * mt + 4 * quad + i;
-        U[mt][i] *= (r < len) ? expf(g_last - gch[r]) : 0.f;
+        const int r = 16 * rt + 4 * quad + i;
+        U[rt][i] *= (r < len) ? __expf(g_last - gs[r]) : 0.f;
       }
     }
     Frag<E> Ud[CKS];
 #pragma unroll
     for (int ks = 0; ks < CKS; ++ks) Ud[ks] = acc_to_frag<E>(U[2 * ks], (2 * ks + 1 < CT) ? U[2 * ks + 1] : zero4());
-    const float gam = expf(g_last);
-    const E* ktg = static_cast<const E*>(a.key_t) + ((int64_t)c * a.h_qk + hq) * D * C;
+    const float gam = __expf(g_last);
 #pragma unroll
-    for (int mt = 0; mt < DT; ++mt) {
-      f32x4 acc = S[mt] * gam;
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x4 acc = S[dt] * gam;
 #pragma unroll
-      for (int ks = 0; ks < CKS; ++ks)
-        acc = mma(load_frag<E>(ktg + (16 * mt + l16) * C + 32 * ks, quad, C - 32 * ks), Ud[ks], acc);
-      S[mt] = acc;
+      for (int ks = 0; ks < CKS; ++ks) acc = mma(sm.kt[par][(dt * CKS + ks) * 64 + lane], Ud[ks], acc);
+      S[dt] = acc;
     }
-  }
-  if (a.final_state) {
+    // intra-chunk output: O^T += U^T P^T
 #pragma unroll
-    for (int mt = 0; mt < DT; ++mt) {
+    for (int nt = 0; nt < CT; ++nt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a.final_state[state_base + (int64_t)(16 * mt + 4 * quad + i) * D + col] = S[mt][i];
-    }
-  }
-}
-
-// --------------------------------------------------------------------------
-// Kernel 5: outputs, computed transposed so that every operand is either a
-// plain row-major load or a fragment written by kernel 4:
-//   O^T = U^T (K Q^T * Dincl^T) + Sc^T (diag(exp(g)) Q)^T.
-// One workgroup per (chunk, V head); wave w handles query tiles w, w+4, ...
-// The K Q^T tile is formed in accumulators, masked/decayed in place, and
-// used directly as the B fragment of the U^T product.
-// --------------------------------------------------------------------------
-template <typename E, int D, int C>
-__global__ __launch_bounds__(kBlock) void gdn_k5_output(const PrefillArgs a) {
-  constexpr int CT = C / 16, DT = D / 16, CKS = (CT + 1) / 2, DKS = (DT + 1) / 2, NW = kBlock / 64;
-  __shared__ float gs[C];
-  const int c = blockIdx.x, hv = blockIdx.y;
-  const int4 tab = reinterpret_cast<const int4*>(a.chunk_table)[c];
-  if (tab.x < 0) return;
-  const int start = tab.y, len = tab.z;
-  const int hq = hv / a.group;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, l16 = lane & 15;
-  const int64_t chv = (int64_t)c * a.h_v + hv;
-  if (tid < C) gs[tid] = a.gate_prefix[chv * C + tid];
-  __syncthreads();
-  const E* qg = static_cast<const E*>(a.q);
-  const E* kg = static_cast<const E*>(a.k);
-  const Frag<E>* ufr = reinterpret_cast<const Frag<E>*>(static_cast<const E*>(a.u)) + chv * DT * CKS * 64;
-  const Frag<E>* sfr = reinterpret_cast<const Frag<E>*>(static_cast<const E*>(a.s_chunk)) + chv * DT * DKS * 64;
-  E* og = static_cast<E*>(a.o);
-
-  for (int nt = wave; nt < CT; nt += NW) {
-    const int r = 16 * nt + l16;
-    const bool r_ok = r < len;
-    const E* qrow = qg + ((int64_t)(start + r) * a.h_qk + hq) * D;
-    f32x4 P[CT];
-#pragma unroll
-    for (int kt = 0; kt < CT; ++kt) {
-      const int jrow = 16 * kt + l16;
-      const E* krow = kg + ((int64_t)(start + jrow) * a.h_qk + hq) * D;
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int ks = 0; ks < DKS; ++ks)
-        acc = mma(load_frag_masked<E>(krow + 32 * ks, quad, D - 32 * ks, jrow < len),
-                  load_frag_masked<E>(qrow + 32 * ks, quad, D - 32 * ks, r_ok), acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 16 * kt + 4 * quad + i;
-        acc[i] = (j <= r && r_ok) ? acc[i] * expf(gs[r] - gs[j]) : 0.f;
+      for (int ks = 0; ks < CKS; ++ks) {
+        if (causal_zero(nt, ks)) continue;
+        O[nt] = mma(Uk[ks], sm.pf[par][(nt * CKS + ks) * 64 + lane], O[nt]);
       }
-      P[kt] = acc;
     }
-    Frag<E> Pf[CKS];
+    E* og = static_cast<E*>(a.o);
 #pragma unroll
-    for (int ks = 0; ks < CKS; ++ks) Pf[ks] = acc_to_frag<E>(P[2 * ks], (2 * ks + 1 < CT) ? P[2 * ks + 1] : zero4());
-    const float gr = r_ok ? expf(gs[r]) : 0.f;
-    Frag<E> Qf[DKS];
-#pragma unroll
-    for (int ks = 0; ks < DKS; ++ks) {
-      const Frag<E> raw = load_frag_masked<E>(qrow + 32 * ks, quad, D - 32 * ks, r_ok);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Qf[ks][e] = to_e<E>(to_f(raw[e]) * gr);
-    }
-#pragma unroll
-    for (int mt = 0; mt < DT; ++mt) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int ks = 0; ks < CKS; ++ks) acc = mma(ufr[(mt * CKS + ks) * 64 + lane], Pf[ks], acc);
-#pragma unroll
-      for (int ks = 0; ks < DKS; ++ks) acc = mma(sfr[(mt * DKS + ks) * 64 + lane], Qf[ks], acc);
-      if (r_ok) {
+    for (int nt = 0; nt < CT; ++nt) {
+      const int r = 16 * nt + l16;
+      if (r < len) {
         Half<E> h;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = to_e<E>(acc[i]);
-        *reinterpret_cast<Half<E>*>(og + ((int64_t)(start + r) * a.h_v + hv) * D + 16 * mt + 4 * quad) = h;
+        for (int i = 0; i < 4; ++i) h[i] = to_e<E>(O[nt][i]);
+        *reinterpret_cast<Half<E>*>(og + ((int64_t)(start + r) * a.h_v + hv) * D + col0 + 16 * slice + 4 * quad) = h;
+      }
+    }
+  };
+
+  auto produce_chunk = [&](int p) __attribute__((always_inline)) {
+    const int par = p & 1;
+    const int len = chunk_len(p);
+    const float* gp = sm.gb[par][0];
+    const float* bp = sm.gb[par][1];
+    constexpr int NITEM = DKS + NS + CT;
+    for (int item = pw; item < NITEM; item += NPROD) {
+      if (item < DKS + NS) {
+        // W fragments (item < DKS) or Ut tiles of one slice: both scale Tinv's
+        // columns, by b_i exp(g_i) for W and by b_i for Ut
+        const bool is_w = item < DKS;
+        float sc[CKS][8];
+#pragma unroll
+        for (int s = 0; s < CKS; ++s) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int i = frag_k(s, quad, e);
+            sc[s][e] = (i < C) ? (is_w ? bp[i] * __expf(gp[i]) : bp[i]) : 0.f;
+          }
+        }
+        const int ksd = item, sl = item - DKS;
+        const E* vrow = &sm.vt[(16 * (is_w ? 0 : sl) + l16) * G::VLD];
+#pragma unroll
+        for (int rt = 0; rt < CT; ++rt) {
+          f32x4 acc0 = zero4(), acc1 = zero4();
+#pragma unroll
+          for (int s = 0; s < CKS; ++s) {
+            if (causal_zero(rt, s)) continue;            // Tinv is lower triangular
+            Frag<E> tb = sm.tf[(rt * CKS + s) * 64 + lane];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tb[e] = to_e<E>(to_f(tb[e]) * sc[s][e]);
+            if (is_w) {
+              acc0 = mma(sm.kt[par][((2 * ksd) * CKS + s) * 64 + lane], tb, acc0);
+              if (2 * ksd + 1 < DT) acc1 = mma(sm.kt[par][((2 * ksd + 1) * CKS + s) * 64 + lane], tb, acc1);
+            } else {
+              acc0 = mma(tb, load_frag<E>(vrow + 32 * s, quad, C - 32 * s), acc0);
+            }
+          }
+          if (is_w) sm.wf[par][(rt * DKS + ksd) * 64 + lane] = acc_to_frag<E>(acc0, acc1);
+          else sm.uf[par][(sl * CT + rt) * 64 + lane] = acc0;
+        }
+      } else {
+        // masked, decayed q.k fragments of query tile nt
+        const int nt = item - DKS - NS;
+        const int r = 16 * nt + l16;
+        const float gr = gp[r];
+#pragma unroll
+        for (int s = 0; s < CKS; ++s) {
+          if (causal_zero(nt, s)) continue;
+          const Frag<E> raw = sm.qk[(nt * CKS + s) * 64 + lane];
+          Frag<E> v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = frag_k(s, quad, e);
+            v[e] = (j <= r && r < len) ? to_e<E>(to_f(raw[e]) * __expf(gr - gp[j])) : to_e<E>(0.f);
+          }
+          sm.pf[par][(nt * CKS + s) * 64 + lane] = v;
+        }
+      }
+    }
+  };
+
+  // The two roles run separate loops with the same barrier sequence (one
+  // after the prologue, two per iteration), so each loop keeps only its own
+  // registers live: the scan waves the state, the producers the two loader
+  // register sets. Iteration c: scan chunk c; produce chunk c + 1; fetch
+  // chunk c + 3 (and Q of chunk c + 2) into one set; between the barriers
+  // stage the other set (chunk c + 2 and Q of chunk c + 1, fetched one
+  // iteration earlier) into LDS.
+  if (c1 > c0) {
+    if (is_scan) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          S[dt][i] = a.init_state
+                         ? a.init_state[state_base + (int64_t)(16 * dt + 4 * quad + i) * D + col0 + 16 * slice + l16]
+                         : 0.f;
+      }
+      __syncthreads();
+      for (int c = c0 - 1; c < c1; ++c) {
+        if (c >= c0) scan_chunk(c);
+        __syncthreads();
+        __syncthreads();
+      }
+      if (a.final_state) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            a.final_state[state_base + (int64_t)(16 * dt + 4 * quad + i) * D + col0 + 16 * slice + l16] = S[dt][i];
+        }
+      }
+    } else {
+      F fa, fb;
+      fetch(fa, c0, -1);
+      store(fa, c0, -1);
+      __syncthreads();
+      fetch(fa, c0 + 1, c0);
+      for (int c = c0 - 1; c < c1; c += 2) {
+        fetch(fb, c + 3, c + 2);
+        if (c + 1 < c1) produce_chunk(c + 1);
+        __syncthreads();
+        store(fa, c + 2, c + 1);
+        __syncthreads();
+        if (c + 1 < c1) {
+          fetch(fa, c + 4, c + 3);
+          if (c + 2 < c1) produce_chunk(c + 2);
+          __syncthreads();
+          store(fb, c + 3, c + 2);
+          __syncthreads();
+        }
+      }
+    }
+  } else if (is_scan && a.final_state) {
+    // empty sequence: the final state is the initial state
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t idx = state_base + (int64_t)(16 * dt + 4 * quad + i) * D + col0 + 16 * slice + l16;
+        a.final_state[idx] = a.init_state ? a.init_state[idx] : 0.f;
       }
     }
   }
@@ -426,15 +666,14 @@ __global__ __launch_bounds__(kBlock) void gdn_k5_output(const PrefillArgs a) {
 
 template <typename E, int D, int C>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int last) {
+  using G = Cfg<E, D, C>;
   const unsigned nc = (unsigned)a.max_chunks;
-  const unsigned scan_waves = (unsigned)(a.num_seqs * a.h_v * (D / 16));
+  const unsigned scan_groups = (unsigned)(a.num_seqs * a.h_v * G::NCB);
   for (int stage = first; stage <= last; ++stage) {
     switch (stage) {
       case 1: gdn_k1_gate_prefix<C><<<dim3(nc), dim3(kBlock), 0, s>>>(a); break;
       case 2: gdn_k2_akk_inverse<E, D, C><<<dim3(nc, a.h_qk), dim3(kBlock), 0, s>>>(a); break;
-      case 3: gdn_k3_wu<E, D, C><<<dim3(nc, a.h_v), dim3(kBlock), 0, s>>>(a); break;
-      case 4: gdn_k4_state_scan<E, D, C><<<dim3(scan_waves), dim3(64), 0, s>>>(a); break;
-      case 5: gdn_k5_output<E, D, C><<<dim3(nc, a.h_v), dim3(kBlock), 0, s>>>(a); break;
+      case 3: gdn_k3_scan<E, D, C><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a); break;
       default: return hipErrorInvalidValue;
     }
   }
@@ -443,7 +682,12 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
 
 template <typename E>
 hipError_t launch_prefill_e(const PrefillArgs& a, int d, int c, hipStream_t s, int first, int last) {
-  if (d == 128 && c == 64) return launch_prefill_t<E, 128, 64>(a, s, first, last);
+  if (d == 128 && c == 64) {
+    // fp32 at head dim 128 with 64-token chunks would need ~250 KB of LDS
+    // for the fused scan's double-buffered fragments; it is not built.
+    if constexpr (std::is_same<E, float>::value) return hipErrorInvalidValue;
+    else return launch_prefill_t<E, 128, 64>(a, s, first, last);
+  }
   if (d == 128 && c == 16) return launch_prefill_t<E, 128, 16>(a, s, first, last);
   if (d == 16 && c == 64) return launch_prefill_t<E, 16, 64>(a, s, first, last);
   if (d == 16 && c == 16) return launch_prefill_t<E, 16, 16>(a, s, first, last);
@@ -451,6 +695,13 @@ hipError_t launch_prefill_e(const PrefillArgs& a, int d, int c, hipStream_t s, i
 }
 
 }  // namespace
+
+bool prefill_supported(int dtype, int head_dim, int chunk) {
+  if (head_dim != 16 && head_dim != 128) return false;
+  if (chunk != 16 && chunk != 64) return false;
+  if (dtype == 0 && head_dim == 128 && chunk == 64) return false;
+  return dtype == 0 || dtype == 1;
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int chunk, hipStream_t s,
                           int first_stage, int last_stage) {

@@ -65,6 +65,7 @@ def ws_bytes(lib, d):
     (dict(dk=64, dv=64), NOT_SUPPORTED),
     (dict(dk=128, dv=64), NOT_SUPPORTED),
     (dict(chunk=32), NOT_SUPPORTED),
+    (dict(dtype=0), NOT_SUPPORTED),          # fp32 at head dim 128 needs chunk 16
 ])
 def test_dims_validation(lib, kw, status):
     d = dims(**kw)
@@ -75,21 +76,22 @@ def test_dims_validation(lib, kw, status):
 
 
 def test_workspace_size_formula(lib):
-    # regions: chunk table, sequence offsets, gate prefixes, Tinv, K^T, W, Ut,
-    # U fragments, state fragments; each padded to 256 bytes
+    # regions: chunk table, sequence offsets, gate prefixes, per-chunk b,
+    # Tinv fragments (per V head), K^T and q.k fragments (per QK head); each
+    # padded to 256 bytes. Fragments of a C x C tile take C*C elements, of a
+    # D x C tile D*C elements (C = 64 is a whole number of 32-steps).
     d = dims(num_seqs=3, total_tokens=1000)
     nc = 1000 // 64 + 3
     def up(x):
         return (x + 255) // 256 * 256
-    want = (up(nc * 16) + up(4 * 4) + up(nc * 48 * 64 * 4) + up(nc * 48 * 64 * 64 * 2)
-            + up(nc * 16 * 128 * 64 * 2) + 3 * up(nc * 48 * 64 * 128 * 2)
-            + up(nc * 48 * 128 * 128 * 2))
+    want = (up(nc * 16) + up(4 * 4) + 2 * up(nc * 48 * 64 * 4) + up(nc * 48 * 64 * 64 * 2)
+            + up(nc * 16 * 128 * 64 * 2) + up(nc * 16 * 64 * 64 * 2))
     assert ws_bytes(lib, d) == want
     lay = B.GdnWorkspaceLayout()
     assert lib.gdn_chunk_fwd_workspace_layout(ctypes.byref(d), ctypes.byref(lay)) == 0
     assert lay.total == want and lay.max_chunks == nc
-    offs = [lay.chunk_table, lay.seq_chunk_offset, lay.gate_prefix, lay.tinv, lay.key_t,
-            lay.w, lay.u_tilde, lay.u, lay.s_chunk]
+    offs = [lay.chunk_table, lay.seq_chunk_offset, lay.gate_prefix, lay.beta_chunk, lay.tinv,
+            lay.key_t, lay.qk]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
 
 
@@ -127,6 +129,19 @@ def test_fwd_rejects_bad_workspace(lib):
 def test_fwd_rejects_unsupported(lib):
     assert call_fwd(lib, dims(dk=64, dv=64)) == NOT_SUPPORTED
     assert call_fwd(lib, dims(chunk=128)) == NOT_SUPPORTED
+    assert call_fwd(lib, dims(dtype=0)) == NOT_SUPPORTED
+    assert ws_bytes(lib, dims(dtype=0, chunk=16)) > 0
+    assert ws_bytes(lib, dims(dtype=0, dk=16, dv=16)) > 0
+
+
+def test_stage_range_validation(lib):
+    d = dims()
+    vp = ctypes.c_void_p
+    for first, last in ((0, 3), (1, 4), (3, 2)):
+        st = lib.gdn_chunk_fwd_stages(ctypes.byref(d), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+                                      vp(FAKE), None, None, vp(FAKE * 2), None, vp(FAKE * 4),
+                                      ws_bytes(lib, d), None, first, last)
+        assert st == INVALID
 
 
 def test_decode_validation(lib):

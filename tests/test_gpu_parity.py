@@ -80,7 +80,7 @@ def test_tiny_fp32_workload():
 
 @pytest.mark.parametrize("d,chunk,dtype", [
     (128, 64, "bf16"), (128, 16, "bf16"), (16, 64, "bf16"), (16, 16, "bf16"),
-    (128, 64, "f32"), (16, 16, "f32"), (128, 16, "f32"), (16, 64, "f32")])
+    (16, 16, "f32"), (128, 16, "f32"), (16, 64, "f32")])
 def test_prefill_ragged_single_sequence(d, chunk, dtype):
     say(f"prefill T=300 d={d} C={chunk} {dtype}")
     inp = random_prefill(100 + d + chunk, [300], 2, 6, d, dtype)
@@ -91,12 +91,12 @@ def test_prefill_ragged_single_sequence(d, chunk, dtype):
     check(fin, want_f, tdt, "final")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_prefill_varlen_with_empty_and_short_sequences(dtype):
+@pytest.mark.parametrize("dtype,chunk", [("bf16", 64), ("f32", 16)])
+def test_prefill_varlen_with_empty_and_short_sequences(dtype, chunk):
     lens = [0, 1, 63, 64, 65, 200, 0, 7, 130]
-    say(f"varlen {lens} {dtype}")
+    say(f"varlen {lens} {dtype} C={chunk}")
     inp = random_prefill(7, lens, 2, 6, 128, dtype)
-    o, fin = run_gpu(inp, 64)
+    o, fin = run_gpu(inp, chunk)
     want_o, want_f = O.recurrent_form1(**oracle_args(inp))
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     check(o, want_o, tdt, "o")
@@ -123,11 +123,18 @@ def test_head_group_of_four():
     check(fin, want_f, torch.bfloat16, "final")
 
 
+def test_fp32_head_dim_128_chunk_64_is_rejected():
+    say("fp32 d=128 C=64 -> not supported")
+    inp = random_prefill(18, [70], 1, 3, 128, "f32")
+    with pytest.raises(gdn.GdnError, match="NOT_SUPPORTED"):
+        run_gpu(inp, 64, use_cu=False)
+
+
 def test_invariants_beta_zero_and_exact_recall():
     say("beta=0 decay and exact recall, d=128 f32")
     inp = random_prefill(10, [130], 1, 3, 128, "f32")
     inp["beta"].zero_()
-    o, fin = run_gpu(inp, 64, use_cu=False)
+    o, fin = run_gpu(inp, 16, use_cu=False)
     g = inp["log_alpha"].double().sum(0)
     want = torch.exp(g)[:, None, None] * inp["init_state"][0].double()
     check(fin[0], want.numpy(), torch.float32, "beta=0 final")
@@ -136,40 +143,80 @@ def test_invariants_beta_zero_and_exact_recall():
     inp["log_alpha"].zero_()
     inp["beta"].fill_(1.0)
     inp["q"] = inp["k"].clone()
-    o, _ = run_gpu(inp, 64, use_cu=False)
+    o, _ = run_gpu(inp, 16, use_cu=False)
     check(o, np64(inp["v"]), torch.float32, "exact recall")
 
 
 # --- per-kernel stages (workspace) against the oracle's chunk stages ---------
 
-def test_stage_outputs_match_oracle_chunks():
-    say("stage outputs T=200 d=128 C=64 f32")
-    inp = random_prefill(12, [77, 123], 2, 6, 128, "f32")
+def frag_k(s, quad, e):
+    """Contraction index of fragment element e, 32-step s, lane quad."""
+    return 32 * s + (4 * quad + e if e < 4 else 16 + 4 * quad + e - 4)
+
+
+def unfrag(frags, rows, kdim):
+    """[tiles][steps][64][8] fragment array -> dense [rows][kdim] matrix."""
+    out = np.zeros((rows, kdim))
+    n_t, n_s = frags.shape[0], frags.shape[1]
+    for t in range(n_t):
+        for s in range(n_s):
+            for ln in range(64):
+                for e in range(8):
+                    k = frag_k(s, ln // 16, e)
+                    if k < kdim:
+                        out[16 * t + ln % 16, k] = frags[t, s, ln, e]
+    return out
+
+
+@pytest.mark.parametrize("chunk", [64, 16])
+def test_stage_outputs_match_oracle_chunks(chunk):
+    say(f"stage outputs T=200 d=128 C={chunk} bf16")
+    inp = random_prefill(12, [77, 123], 2, 6, 128, "bf16")
     d = on_dev(inp)
-    dims = gdn.make_dims(2, 200, 2, 6, 128, 128, 64, torch.float32)
+    dims = gdn.make_dims(2, 200, 2, 6, 128, 128, chunk, torch.bfloat16)
     lay = gdn.gdn_chunk_fwd_workspace_layout(dims)
     ws = torch.zeros(lay.total, dtype=torch.uint8, device=DEV)
     gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["init_state"],
-                      d["cu_seqlens"], chunk=64, workspace=ws)
+                      d["cu_seqlens"], chunk=chunk, workspace=ws)
     torch.cuda.synchronize()
     wsc = ws.cpu()
     nc = lay.max_chunks
+    ct, cks = chunk // 16, (chunk // 16 + 1) // 2
 
     def region(off, count, dt):
         return wsc[off:off + count * torch.tensor([], dtype=dt).element_size()].view(dt)
 
     table = region(lay.chunk_table, nc * 4, torch.int32).view(nc, 4).numpy()
-    g = region(lay.gate_prefix, nc * 6 * 64, torch.float32).view(nc, 6, 64).double().numpy()
-    tinv = region(lay.tinv, nc * 6 * 64 * 64, torch.float32).view(nc, 6, 64, 64).double().numpy()
-    w = region(lay.w, nc * 6 * 64 * 128, torch.float32).view(nc, 6, 64, 128).double().numpy()
-    _, _, stages = O.chunkwise(**oracle_args(inp), chunk=64, keep_stages=True)
-    assert len(stages) == 2 + 2
+    g = region(lay.gate_prefix, nc * 6 * chunk, torch.float32).view(nc, 6, chunk).double().numpy()
+    b = region(lay.beta_chunk, nc * 6 * chunk, torch.float32).view(nc, 6, chunk).double().numpy()
+    tf = region(lay.tinv, nc * 6 * ct * cks * 512, torch.bfloat16).view(
+        nc, 6, ct, cks, 64, 8).double().numpy()
+    kt = region(lay.key_t, nc * 2 * 8 * cks * 512, torch.bfloat16).view(
+        nc, 2, 8, cks, 64, 8).double().numpy()
+    qk = region(lay.qk, nc * 2 * ct * cks * 512, torch.bfloat16).view(
+        nc, 2, ct, cks, 64, 8).double().numpy()
+    _, _, stages = O.chunkwise(**oracle_args(inp), chunk=chunk, keep_stages=True)
+    q64, k64, b64 = np64(inp["q"]), np64(inp["k"]), np64(inp["beta"])
+    n_seq0 = -(-77 // chunk)
+    assert len(stages) == n_seq0 + -(-123 // chunk)
     for c, st in enumerate(stages):
-        L = st["len"]
-        assert list(table[c]) == [st["seq"], st["start"], L, c - (0 if st["seq"] == 0 else 2)]
+        L, t0 = st["len"], st["start"]
+        assert list(table[c]) == [st["seq"], t0, L, c - (0 if st["seq"] == 0 else n_seq0)]
         check(g[c][:, :L], st["g"], torch.float32, f"g chunk {c}")
-        check(tinv[c][:, :L, :L], st["T"], torch.float32, f"Tinv chunk {c}")
-        check(w[c][:, :L], st["W"], torch.float32, f"W chunk {c}")
+        assert (b[c][:, :L] == b64[t0:t0 + L].T).all() and (b[c][:, L:] == 0).all()
+        for h in range(6):
+            tm = unfrag(tf[c, h], chunk, chunk)
+            check(tm[:L, :L], st["T"][h], torch.bfloat16, f"Tinv chunk {c} head {h}")
+            assert np.allclose(tm[L:, :L], 0) and np.allclose(tm[:L, L:], 0)
+        for hq in range(2):
+            ktm = unfrag(kt[c, hq], 128, chunk)            # [d][i]
+            assert np.array_equal(ktm[:, :L], k64[t0:t0 + L, hq].T) and (ktm[:, L:] == 0).all()
+            qkm = unfrag(qk[c, hq], chunk, chunk)          # [query r][key j]
+            want = q64[t0:t0 + L, hq] @ k64[t0:t0 + L, hq].T
+            causal = np.tril(np.ones((L, L)), 0) > 0
+            tiles = (np.arange(L)[None, :] // 16) <= (np.arange(L)[:, None] // 16)
+            assert np.abs(qkm[:L, :L][causal] - want[causal]).max() < 2e-2
+            assert (qkm[:L, :L][~tiles] == 0).all()
     assert (table[len(stages):, 0] == -1).all()
 
 

@@ -84,7 +84,7 @@ Layout compute_layout(const gdn_dims_t& d) {
   L.v.seq_chunk_offset = take((N + 1) * 4);
   L.v.gate_prefix = take(NC * HV * C * 4);
   L.v.beta_chunk = take(NC * HV * C * 4);
-  L.v.tinv = take(NC * HV * CT * CKS * 512 * esz);
+  L.v.tinv = take(2 * NC * HV * CT * CKS * 512 * esz);
   L.v.key_t = take(NC * HQ * DT * CKS * 512 * esz);
   L.v.qk = take(NC * HQ * CT * CKS * 512 * esz);
   L.v.total = off;

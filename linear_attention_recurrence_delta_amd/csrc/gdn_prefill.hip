@@ -146,20 +146,49 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_gate_prefix(const PrefillArgs a
 // each of the QK head's V heads A = strict_lower(b_r (k_r . k_i)
 // exp(g_r - g_i)) and Tinv = (I + A)^{-1}.
 // K K^T and Q K^T are formed once with MFMA and shared by the V heads. Each
-// wave inverts one V head's unit lower-triangular I + A by forward
-// substitution, one lane per column j: x_r = delta_rj - sum_{i<r} A[r,i] x_i
-// in fp32 registers (four partial sums break the dependency chain), A read
-// from LDS as a broadcast. Tinv is then re-read from LDS as fragments.
+// wave inverts one V head's unit lower-triangular I + A blockwise in fp32:
+// the 16 x 16 diagonal blocks by forward substitution (one lane per column),
+// then the blocks below them in order of distance from the diagonal,
+//   Tinv_ij = -Tinv_ii sum_{j<=m<i} A_im Tinv_mj,
+// with fp32 16x16x4 MFMAs. Tinv is then re-read from LDS as fragments.
 // --------------------------------------------------------------------------
+
+// acc += X Y for 16 x 16 fp32 tiles in LDS (row-major, leading dims lx, ly)
+__device__ __forceinline__ f32x4 mma16_f32(const float* X, int lx, const float* Y, int ly, f32x4 acc,
+                                           int lane) {
+  const int m = lane & 15, k = lane >> 4;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[m * lx + 4 * kk + k], Y[(4 * kk + k) * ly + m], acc, 0, 0, 0);
+  return acc;
+}
+
+template <typename E, int D, int C>
+struct InvSmem {
+  static constexpr int KLD = D + 8, NW = kBlock / 64;
+  union {
+    struct {
+      E ks[C * KLD];                   // keys of the chunk, rows past its end zero
+      E qs[C * KLD];                   // queries of the chunk
+    } in;
+    struct {
+      float t[NW][C * C];              // Tinv being assembled, one per wave
+      float x[NW][256];                // 16 x 16 scratch tile, one per wave
+    } out;
+  } u;
+  float kk[C * C];                     // K K^T (lower tiles), kept for every head group
+  float ab[NW][C * C];                 // A per wave; ab[0] first stages q.k
+  float sb[NW][C];
+};
+
 template <typename E, int D, int C>
 __global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
-  constexpr int CT = G::CT, CKS = G::CKS, DKS = G::DKS, KLD = D + 8, NW = kBlock / 64;
-  __shared__ __attribute__((aligned(16))) E Ks[C * KLD];
-  __shared__ __attribute__((aligned(16))) E Qs[C * KLD];
-  __shared__ __attribute__((aligned(16))) float KK[C * C];
-  __shared__ __attribute__((aligned(16))) float Ab[NW][C * C];
-  __shared__ float sb[NW][C];
+  using SM = InvSmem<E, D, C>;
+  constexpr int CT = G::CT, CKS = G::CKS, DKS = G::DKS, KLD = SM::KLD, NW = SM::NW;
+  constexpr int VE = 16 / (int)sizeof(E);                 // elements per 16-byte load
+  typedef E VLoad __attribute__((ext_vector_type(VE)));
+  __shared__ SM sm;
   const int c = blockIdx.x, hq = blockIdx.y;
   const int4 tab = reinterpret_cast<const int4*>(a.chunk_table)[c];
   if (tab.x < 0) return;
@@ -168,11 +197,18 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a
   const E* kg = static_cast<const E*>(a.k);
   const E* qg = static_cast<const E*>(a.q);
 
-  for (int idx = tid; idx < C * D; idx += kBlock) {
-    const int r = idx / D, d = idx % D;
-    const int64_t gi = ((int64_t)(start + r) * a.h_qk + hq) * D + d;
-    Ks[r * KLD + d] = (r < len) ? kg[gi] : to_e<E>(0.f);
-    Qs[r * KLD + d] = (r < len) ? qg[gi] : to_e<E>(0.f);
+  for (int idx = tid; idx < C * D / VE; idx += kBlock) {
+    const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
+    VLoad kv, qv;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) { kv[e] = to_e<E>(0.f); qv[e] = to_e<E>(0.f); }
+    if (r < len) {
+      const int64_t gi = ((int64_t)(start + r) * a.h_qk + hq) * D + d;
+      kv = *reinterpret_cast<const VLoad*>(kg + gi);
+      qv = *reinterpret_cast<const VLoad*>(qg + gi);
+    }
+#pragma unroll
+    for (int e = 0; e < VE; ++e) { sm.u.in.ks[r * KLD + d + e] = kv[e]; sm.u.in.qs[r * KLD + d + e] = qv[e]; }
   }
   __syncthreads();
 
@@ -185,30 +221,30 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int i = frag_k(s, q4, e);
-      v[e] = (i < C) ? Ks[i * KLD + d] : to_e<E>(0.f);
+      v[e] = (i < C) ? sm.u.in.ks[i * KLD + d] : to_e<E>(0.f);
     }
     ktg[it] = v;
   }
 
-  // K K^T (lower tiles, into KK) and q.k (tiles with key tile <= query tile,
-  // into Ab[0] as [query r][key j]).
-  float* QKl = Ab[0];
+  // K K^T (lower tiles) and q.k (tiles with key tile <= query tile, stored
+  // as [query r][key j] in ab[0])
+  float* qkl = sm.ab[0];
   for (int t = wave; t < 2 * CT * CT; t += NW) {
     const bool is_qk = t >= CT * CT;
     const int tt = is_qk ? t - CT * CT : t;
     const int mi = tt / CT, ni = tt % CT;   // KK: row tile mi, col tile ni; q.k: key tile mi, query tile ni
     if (ni > mi && !is_qk) continue;
     if (mi > ni && is_qk) continue;
-    const E* brow = is_qk ? &Qs[(16 * ni + l16) * KLD] : &Ks[(16 * ni + l16) * KLD];
+    const E* brow = is_qk ? &sm.u.in.qs[(16 * ni + l16) * KLD] : &sm.u.in.ks[(16 * ni + l16) * KLD];
     f32x4 acc = zero4();
 #pragma unroll
     for (int ks = 0; ks < DKS; ++ks)
-      acc = mma(load_frag<E>(&Ks[(16 * mi + l16) * KLD + 32 * ks], quad, D - 32 * ks),
+      acc = mma(load_frag<E>(&sm.u.in.ks[(16 * mi + l16) * KLD + 32 * ks], quad, D - 32 * ks),
                 load_frag<E>(brow + 32 * ks, quad, D - 32 * ks), acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (!is_qk) KK[(16 * mi + 4 * quad + i) * C + 16 * ni + l16] = acc[i];
-      else QKl[(16 * ni + l16) * C + 16 * mi + 4 * quad + i] = acc[i];
+      if (!is_qk) sm.kk[(16 * mi + 4 * quad + i) * C + 16 * ni + l16] = acc[i];
+      else qkl[(16 * ni + l16) * C + 16 * mi + 4 * quad + i] = acc[i];
     }
   }
   __syncthreads();
@@ -221,7 +257,7 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = frag_k(s, q4, e);
-      v[e] = (j < C && (j >> 4) <= nt) ? to_e<E>(QKl[r * C + j]) : to_e<E>(0.f);
+      v[e] = (j < C && (j >> 4) <= nt) ? to_e<E>(qkl[r * C + j]) : to_e<E>(0.f);
     }
     qkg[it] = v;
   }
@@ -232,55 +268,78 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a
   for (int h0 = 0; h0 < a.group; h0 += NW) {
     const int nh = min(NW, a.group - h0);
     for (int w = 0; w < nh; ++w) {
-      if (tid < C) sb[w][tid] = bch[(int64_t)(hq * a.group + h0 + w) * C + tid];
+      if (tid < C) sm.sb[w][tid] = bch[(int64_t)(hq * a.group + h0 + w) * C + tid];
     }
     __syncthreads();
+    // A below the diagonal only (the inverse never reads the rest)
     for (int w = 0; w < nh; ++w) {
       const float* gh = gch + (int64_t)(hq * a.group + h0 + w) * C;
       for (int idx = tid; idx < C * C; idx += kBlock) {
         const int r = idx / C, i = idx % C;
-        float val = 0.f;
-        if (i < r && r < len) val = sb[w][r] * KK[idx] * __expf(gh[r] - gh[i]);
-        Ab[w][idx] = val;
+        if (i < r) sm.ab[w][idx] = (r < len) ? sm.sb[w][r] * sm.kk[idx] * __expf(gh[r] - gh[i]) : 0.f;
       }
     }
     __syncthreads();
     if (wave < nh) {
       const int hv = hq * a.group + h0 + wave;
-      float* Aw = Ab[wave];
-      float x[C];
+      const float* A = sm.ab[wave];
+      float* Tm = sm.u.out.t[wave];
+      float* X = sm.u.out.x[wave];
+      // blocks above the diagonal are zero
+      for (int idx = lane; idx < C * C; idx += 64)
+        if ((idx % C) / 16 > (idx / C) / 16) Tm[idx] = 0.f;
+      // diagonal blocks: lane = 16 b + j solves column j of block b
+      if (lane < 16 * CT) {
+        const int b = lane >> 4, j = lane & 15, o = 16 * b;
+        float x[16];
 #pragma unroll
-      for (int r = 0; r < C; ++r) {
-        float s0 = (r == lane) ? 1.f : 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          float s0 = (r == j) ? 1.f : 0.f, s1 = 0.f;
 #pragma unroll
-        for (int i = 0; i + 3 < r; i += 4) {
-          s0 -= Aw[r * C + i] * x[i];
-          s1 -= Aw[r * C + i + 1] * x[i + 1];
-          s2 -= Aw[r * C + i + 2] * x[i + 2];
-          s3 -= Aw[r * C + i + 3] * x[i + 3];
+          for (int i = 0; i < r; ++i) {
+            if (i & 1) s1 -= A[(o + r) * C + o + i] * x[i];
+            else s0 -= A[(o + r) * C + o + i] * x[i];
+          }
+          x[r] = s0 + s1;
         }
 #pragma unroll
-        for (int i = r & ~3; i < r; ++i) s0 -= Aw[r * C + i] * x[i];
-        x[r] = (s0 + s1) + (s2 + s3);
+        for (int r = 0; r < 16; ++r) Tm[(o + r) * C + o + j] = x[r];
       }
-      // every lane's reads of A are complete (their values were consumed
-      // above); the wave now overwrites its own buffer with Tinv (row-major)
-      if (lane < C) {
+      // blocks below the diagonal, by distance from it
 #pragma unroll
-        for (int r = 0; r < C; ++r) Aw[r * C + lane] = x[r];
+      for (int dist = 1; dist < CT; ++dist) {
+#pragma unroll
+        for (int bi = dist; bi < CT; ++bi) {
+          const int bj = bi - dist;
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int bm = bj; bm < bi; ++bm)
+            acc = mma16_f32(&A[(16 * bi) * C + 16 * bm], C, &Tm[(16 * bm) * C + 16 * bj], C, acc, lane);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) X[(4 * quad + i) * 16 + l16] = acc[i];
+          acc = mma16_f32(&Tm[(16 * bi) * C + 16 * bi], C, X, 16, zero4(), lane);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Tm[(16 * bi + 4 * quad + i) * C + 16 * bj + l16] = -acc[i];
+        }
       }
-      Frag<E>* tg = reinterpret_cast<Frag<E>*>(a.tinv) + ((int64_t)c * a.h_v + hv) * G::T_FR * 64;
+      // Tinv diag(b) and Tinv diag(b exp(g)) fragments (the right factors of
+      // Ut and W), written one after the other
+      Frag<E>* tg = reinterpret_cast<Frag<E>*>(a.tinv) + ((int64_t)c * a.h_v + hv) * 2 * G::T_FR * 64;
+      const float* gh = gch + (int64_t)hv * C;
 #pragma unroll
       for (int f = 0; f < G::T_FR; ++f) {
         const int rt = f / CKS, s = f % CKS;
         const int r = 16 * rt + l16;
-        Frag<E> v;
+        Frag<E> vb, vg;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = frag_k(s, quad, e);
-          v[e] = (i < C) ? to_e<E>(Aw[r * C + i]) : to_e<E>(0.f);
+          const float t = (i < C) ? Tm[r * C + i] * sm.sb[wave][i] : 0.f;
+          vb[e] = to_e<E>(t);
+          vg[e] = to_e<E>((i < C) ? t * __expf(gh[i]) : 0.f);
         }
-        tg[f * 64 + lane] = v;
+        tg[f * 64 + lane] = vb;
+        tg[(G::T_FR + f) * 64 + lane] = vg;
       }
     }
     __syncthreads();
@@ -316,7 +375,7 @@ struct ScanSmem {
   using G = Cfg<E, D, C>;
   Frag<E> kt[2][G::KT_FR * 64];        // K^T fragments, by chunk parity
   Frag<E> qf[G::Q_FR * 64];            // Q fragments of the chunk being scanned
-  Frag<E> tf[G::T_FR * 64];            // Tinv fragments of the chunk being produced
+  Frag<E> tf[2][G::T_FR * 64];         // Tinv diag(b), Tinv diag(b exp(g)) of the chunk being produced
   Frag<E> qk[G::QK_FR * 64];           // q.k fragments of the chunk being produced
   Frag<E> wf[2][G::W_FR * 64];         // W fragments, by chunk parity
   Frag<E> pf[2][G::QK_FR * 64];        // masked, decayed q.k fragments, by parity
@@ -331,7 +390,7 @@ struct ScanFetch {
   using G = Cfg<E, D, C>;
   static constexpr int NL = kScanBlock - 64 * G::NS;                 // loader threads
   static constexpr int FR16 = (int)sizeof(Frag<E>) / 16;             // 16-byte units per lane-fragment
-  static constexpr int N_KT = G::KT_FR * 64 * FR16, N_T = G::T_FR * 64 * FR16, N_QK = G::QK_FR * 64 * FR16;
+  static constexpr int N_KT = G::KT_FR * 64 * FR16, N_T = 2 * G::T_FR * 64 * FR16, N_QK = G::QK_FR * 64 * FR16;
   static constexpr int N_GB = 2 * C * 4 / 16;
   static constexpr int VU = 16 / (int)sizeof(E);                     // V elements per 16-byte unit
   static constexpr int N_V = C * G::BV / VU;
@@ -378,8 +437,9 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     if (x < c1) {
       const u32x4* ktg = reinterpret_cast<const u32x4*>(
           reinterpret_cast<const Frag<E>*>(a.key_t) + ((int64_t)x * a.h_qk + hq) * G::KT_FR * 64);
+      // both scaled Tinv fragment sets of chunk x are contiguous
       const u32x4* tg = reinterpret_cast<const u32x4*>(
-          reinterpret_cast<const Frag<E>*>(a.tinv) + ((int64_t)x * a.h_v + hv) * G::T_FR * 64);
+          reinterpret_cast<const Frag<E>*>(a.tinv) + ((int64_t)x * a.h_v + hv) * 2 * G::T_FR * 64);
       const u32x4* qkg = reinterpret_cast<const u32x4*>(
           reinterpret_cast<const Frag<E>*>(a.qk) + ((int64_t)x * a.h_qk + hq) * G::QK_FR * 64);
 #pragma unroll
@@ -431,7 +491,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     if (is_scan) return;
     if (x < c1) {
       u32x4* kt = reinterpret_cast<u32x4*>(sm.kt[x & 1]);
-      u32x4* tf = reinterpret_cast<u32x4*>(sm.tf);
+      u32x4* tf = reinterpret_cast<u32x4*>(sm.tf[0]);
       u32x4* qk = reinterpret_cast<u32x4*>(sm.qk);
 #pragma unroll
       for (int p = 0; p < F::P_KT; ++p) { const int u = lt + p * F::NL; if (u < F::N_KT) kt[u] = fr.kt[p]; }
@@ -541,42 +601,46 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     const int par = p & 1;
     const int len = chunk_len(p);
     const float* gp = sm.gb[par][0];
-    const float* bp = sm.gb[par][1];
     constexpr int NITEM = DKS + NS + CT;
     for (int item = pw; item < NITEM; item += NPROD) {
-      if (item < DKS + NS) {
-        // W fragments (item < DKS) or Ut tiles of one slice: both scale Tinv's
-        // columns, by b_i exp(g_i) for W and by b_i for Ut
-        const bool is_w = item < DKS;
-        float sc[CKS][8];
+      if (item < DKS) {
+        // W fragments (rt, ks_d) for every rt: the W^T tiles of d-tiles
+        // 2 ks_d and 2 ks_d + 1, from Tinv diag(b exp(g)) and K^T
+        const int ksd = item;
+        Frag<E> ka[CKS], kb[CKS];
 #pragma unroll
         for (int s = 0; s < CKS; ++s) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int i = frag_k(s, quad, e);
-            sc[s][e] = (i < C) ? (is_w ? bp[i] * __expf(gp[i]) : bp[i]) : 0.f;
-          }
+          ka[s] = sm.kt[par][((2 * ksd) * CKS + s) * 64 + lane];
+          if (2 * ksd + 1 < DT) kb[s] = sm.kt[par][((2 * ksd + 1) * CKS + s) * 64 + lane];
         }
-        const int ksd = item, sl = item - DKS;
-        const E* vrow = &sm.vt[(16 * (is_w ? 0 : sl) + l16) * G::VLD];
 #pragma unroll
         for (int rt = 0; rt < CT; ++rt) {
           f32x4 acc0 = zero4(), acc1 = zero4();
 #pragma unroll
           for (int s = 0; s < CKS; ++s) {
             if (causal_zero(rt, s)) continue;            // Tinv is lower triangular
-            Frag<E> tb = sm.tf[(rt * CKS + s) * 64 + lane];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tb[e] = to_e<E>(to_f(tb[e]) * sc[s][e]);
-            if (is_w) {
-              acc0 = mma(sm.kt[par][((2 * ksd) * CKS + s) * 64 + lane], tb, acc0);
-              if (2 * ksd + 1 < DT) acc1 = mma(sm.kt[par][((2 * ksd + 1) * CKS + s) * 64 + lane], tb, acc1);
-            } else {
-              acc0 = mma(tb, load_frag<E>(vrow + 32 * s, quad, C - 32 * s), acc0);
-            }
+            const Frag<E> tb = sm.tf[1][(rt * CKS + s) * 64 + lane];
+            acc0 = mma(ka[s], tb, acc0);
+            if (2 * ksd + 1 < DT) acc1 = mma(kb[s], tb, acc1);
           }
-          if (is_w) sm.wf[par][(rt * DKS + ksd) * 64 + lane] = acc_to_frag<E>(acc0, acc1);
-          else sm.uf[par][(sl * CT + rt) * 64 + lane] = acc0;
+          sm.wf[par][(rt * DKS + ksd) * 64 + lane] = acc_to_frag<E>(acc0, acc1);
+        }
+      } else if (item < DKS + NS) {
+        // Ut accumulator tiles of slice sl: Tinv diag(b) V
+        const int sl = item - DKS;
+        const E* vrow = &sm.vt[(16 * sl + l16) * G::VLD];
+        Frag<E> vf[CKS];
+#pragma unroll
+        for (int s = 0; s < CKS; ++s) vf[s] = load_frag<E>(vrow + 32 * s, quad, C - 32 * s);
+#pragma unroll
+        for (int rt = 0; rt < CT; ++rt) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int s = 0; s < CKS; ++s) {
+            if (causal_zero(rt, s)) continue;
+            acc = mma(sm.tf[0][(rt * CKS + s) * 64 + lane], vf[s], acc);
+          }
+          sm.uf[par][(sl * CT + rt) * 64 + lane] = acc;
         }
       } else {
         // masked, decayed q.k fragments of query tile nt

@@ -432,63 +432,53 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   const int64_t state_base = (n * a.h_v + hv) * D * D;
 
   // ---- loaders: global -> registers (chunk x's operands, chunk xq's Q) ----
+  // Branch-free: every loader issues the same loads, with indices clamped
+  // into range (the last valid unit, row or chunk); what lies outside is
+  // masked when the registers are stored. Keeping the loads unconditional
+  // lets them stay in flight across the pipeline's barriers.
   auto fetch = [&](F& fr, int x, int xq) __attribute__((always_inline)) {
-    if (is_scan) return;
-    if (x < c1) {
-      const u32x4* ktg = reinterpret_cast<const u32x4*>(
-          reinterpret_cast<const Frag<E>*>(a.key_t) + ((int64_t)x * a.h_qk + hq) * G::KT_FR * 64);
-      // both scaled Tinv fragment sets of chunk x are contiguous
-      const u32x4* tg = reinterpret_cast<const u32x4*>(
-          reinterpret_cast<const Frag<E>*>(a.tinv) + ((int64_t)x * a.h_v + hv) * 2 * G::T_FR * 64);
-      const u32x4* qkg = reinterpret_cast<const u32x4*>(
-          reinterpret_cast<const Frag<E>*>(a.qk) + ((int64_t)x * a.h_qk + hq) * G::QK_FR * 64);
+    const int xc = min(x, c1 - 1);
+    const u32x4* ktg = reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const Frag<E>*>(a.key_t) + ((int64_t)xc * a.h_qk + hq) * G::KT_FR * 64);
+    // both scaled Tinv fragment sets of chunk x are contiguous
+    const u32x4* tg = reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const Frag<E>*>(a.tinv) + ((int64_t)xc * a.h_v + hv) * 2 * G::T_FR * 64);
+    const u32x4* qkg = reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const Frag<E>*>(a.qk) + ((int64_t)xc * a.h_qk + hq) * G::QK_FR * 64);
 #pragma unroll
-      for (int p = 0; p < F::P_KT; ++p) { const int u = lt + p * F::NL; if (u < F::N_KT) fr.kt[p] = ktg[u]; }
+    for (int p = 0; p < F::P_KT; ++p) fr.kt[p] = ktg[min(lt + p * F::NL, F::N_KT - 1)];
 #pragma unroll
-      for (int p = 0; p < F::P_T; ++p) { const int u = lt + p * F::NL; if (u < F::N_T) fr.t[p] = tg[u]; }
+    for (int p = 0; p < F::P_T; ++p) fr.t[p] = tg[min(lt + p * F::NL, F::N_T - 1)];
 #pragma unroll
-      for (int p = 0; p < F::P_QK; ++p) { const int u = lt + p * F::NL; if (u < F::N_QK) fr.qk[p] = qkg[u]; }
+    for (int p = 0; p < F::P_QK; ++p) fr.qk[p] = qkg[min(lt + p * F::NL, F::N_QK - 1)];
 #pragma unroll
-      for (int p = 0; p < F::P_GB; ++p) {
-        const int u = lt + p * F::NL, half = F::N_GB / 2;
-        if (u < F::N_GB) {
-          const float* src = (u < half ? a.gate_prefix : a.beta_chunk) + ((int64_t)x * a.h_v + hv) * C;
-          fr.gb[p] = reinterpret_cast<const u32x4*>(src)[u % half];
-        }
-      }
-      const int x_start = chunk_start(x), x_len = chunk_len(x);
-      const E* vg = static_cast<const E*>(a.v);
-#pragma unroll
-      for (int p = 0; p < F::P_V; ++p) {
-        const int u = lt + p * F::NL;
-        if (u < F::N_V) {
-          const int i = u / (BV / F::VU), part = u % (BV / F::VU);
-#pragma unroll
-          for (int e = 0; e < F::VU; ++e) fr.v[p][e] = to_e<E>(0.f);
-          if (i < x_len)
-            fr.v[p] = *reinterpret_cast<const typename F::VUnit*>(
-                vg + ((int64_t)(x_start + i) * a.h_v + hv) * D + col0 + part * F::VU);
-        }
-      }
+    for (int p = 0; p < F::P_GB; ++p) {
+      const int u = min(lt + p * F::NL, F::N_GB - 1), half = F::N_GB / 2;
+      const float* src = (u < half ? a.gate_prefix : a.beta_chunk) + ((int64_t)xc * a.h_v + hv) * C;
+      fr.gb[p] = reinterpret_cast<const u32x4*>(src)[u % half];
     }
-    if (xq >= c0 && xq < c1) {
-      const int q_start = chunk_start(xq), q_len = chunk_len(xq);
-      const E* qg = static_cast<const E*>(a.q);
+    const int x_start = chunk_start(xc), x_last = chunk_len(xc) - 1;
+    const E* vg = static_cast<const E*>(a.v);
 #pragma unroll
-      for (int p = 0; p < F::P_Q; ++p) {
-        const int u = lt + p * F::NL;
-        if (u < F::N_Q) {
-          const int f = u / 64, ln = u % 64, nt = f / DKS, s = f % DKS;
-          const int r = 16 * nt + (ln & 15);
-          fr.q[p] = load_frag_masked<E>(qg + ((int64_t)(q_start + r) * a.h_qk + hq) * D + 32 * s, ln >> 4,
-                                        D - 32 * s, r < q_len);
-        }
-      }
+    for (int p = 0; p < F::P_V; ++p) {
+      const int u = min(lt + p * F::NL, F::N_V - 1);
+      const int i = min(u / (BV / F::VU), x_last), part = u % (BV / F::VU);
+      fr.v[p] = *reinterpret_cast<const typename F::VUnit*>(
+          vg + ((int64_t)(x_start + i) * a.h_v + hv) * D + col0 + part * F::VU);
+    }
+    const int xqc = min(max(xq, c0), c1 - 1);
+    const int q_start = chunk_start(xqc), q_last = chunk_len(xqc) - 1;
+    const E* qg = static_cast<const E*>(a.q);
+#pragma unroll
+    for (int p = 0; p < F::P_Q; ++p) {
+      const int u = min(lt + p * F::NL, F::N_Q - 1);
+      const int f = u / 64, ln = u % 64, nt = f / DKS, s = f % DKS;
+      const int r = min(16 * nt + (ln & 15), q_last);
+      fr.q[p] = load_frag<E>(qg + ((int64_t)(q_start + r) * a.h_qk + hq) * D + 32 * s, ln >> 4, D - 32 * s);
     }
   };
-  // ---- loaders: registers -> LDS ----
+  // ---- loaders: registers -> LDS, masking what the fetch clamped ----
   auto store = [&](const F& fr, int x, int xq) __attribute__((always_inline)) {
-    if (is_scan) return;
     if (x < c1) {
       u32x4* kt = reinterpret_cast<u32x4*>(sm.kt[x & 1]);
       u32x4* tf = reinterpret_cast<u32x4*>(sm.tf[0]);
@@ -504,19 +494,33 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
         const int u = lt + p * F::NL;
         if (u < F::N_GB) reinterpret_cast<u32x4*>(&sm.gb[x & 1][0][0])[u] = fr.gb[p];
       }
+      const int x_len = chunk_len(x);
 #pragma unroll
       for (int p = 0; p < F::P_V; ++p) {
         const int u = lt + p * F::NL;
         if (u < F::N_V) {
           const int i = u / (BV / F::VU), part = u % (BV / F::VU);
 #pragma unroll
-          for (int e = 0; e < F::VU; ++e) sm.vt[(part * F::VU + e) * G::VLD + i] = fr.v[p][e];
+          for (int e = 0; e < F::VU; ++e)
+            sm.vt[(part * F::VU + e) * G::VLD + i] = (i < x_len) ? fr.v[p][e] : to_e<E>(0.f);
         }
       }
     }
     if (xq >= c0 && xq < c1) {
+      const int q_len = chunk_len(xq);
 #pragma unroll
-      for (int p = 0; p < F::P_Q; ++p) { const int u = lt + p * F::NL; if (u < F::N_Q) sm.qf[u] = fr.q[p]; }
+      for (int p = 0; p < F::P_Q; ++p) {
+        const int u = lt + p * F::NL;
+        if (u < F::N_Q) {
+          const int nt = (u / 64) / DKS, r = 16 * nt + (u % 64 & 15);
+          Frag<E> v = fr.q[p];
+          if (r >= q_len) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = to_e<E>(0.f);
+          }
+          sm.qf[u] = v;
+        }
+      }
     }
   };
 
@@ -529,60 +533,84 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     Frag<E> Sf[DKS];
 #pragma unroll
     for (int ks = 0; ks < DKS; ++ks) Sf[ks] = acc_to_frag<E>(S[2 * ks], (2 * ks + 1 < DT) ? S[2 * ks + 1] : zero4());
-    // inter-chunk output: O^T[col][r] = sum_d S[d][col] q_r[d], times exp(g_r)
-    f32x4 O[CT];
+    // Both products that read the state run together, contraction step
+    // outermost so that 2 CT independent accumulators interleave, with the
+    // next step's LDS fragments loaded before this step's MFMAs:
+    //   O^T[col][r] = sum_d S[d][col] q_r[d]   (inter-chunk output)
+    //   WS[r][col]  = sum_d W[r][d] S[d][col]
+    f32x4 O[CT], WS[CT];
 #pragma unroll
-    for (int nt = 0; nt < CT; ++nt) {
-      O[nt] = zero4();
+    for (int t = 0; t < CT; ++t) { O[t] = zero4(); WS[t] = zero4(); }
+    Frag<E> qa[CT], wa[CT];
 #pragma unroll
-      for (int ks = 0; ks < DKS; ++ks) O[nt] = mma(Sf[ks], sm.qf[(nt * DKS + ks) * 64 + lane], O[nt]);
+    for (int t = 0; t < CT; ++t) {
+      qa[t] = sm.qf[(t * DKS) * 64 + lane];
+      wa[t] = sm.wf[par][(t * DKS) * 64 + lane];
     }
-    // U = Ut - W S
+#pragma unroll
+    for (int ks = 0; ks < DKS; ++ks) {
+      Frag<E> qn[CT], wn[CT];
+      if (ks + 1 < DKS) {
+#pragma unroll
+        for (int t = 0; t < CT; ++t) {
+          qn[t] = sm.qf[(t * DKS + ks + 1) * 64 + lane];
+          wn[t] = sm.wf[par][(t * DKS + ks + 1) * 64 + lane];
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < CT; ++t) {
+        O[t] = mma(Sf[ks], qa[t], O[t]);
+        WS[t] = mma(wa[t], Sf[ks], WS[t]);
+      }
+      if (ks + 1 < DKS) {
+#pragma unroll
+        for (int t = 0; t < CT; ++t) { qa[t] = qn[t]; wa[t] = wn[t]; }
+      }
+    }
+    // U = Ut - W S; the inter-chunk output takes exp(g_r) (rows past the
+    // chunk end are zeroed by multiplying, not branching)
     f32x4 U[CT];
 #pragma unroll
-    for (int rt = 0; rt < CT; ++rt) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int ks = 0; ks < DKS; ++ks) acc = mma(sm.wf[par][(rt * DKS + ks) * 64 + lane], Sf[ks], acc);
-      U[rt] = sm.uf[par][(slice * CT + rt) * 64 + lane] - acc;
-    }
-#pragma unroll
-    for (int nt = 0; nt < CT; ++nt) {
-      const int r = 16 * nt + l16;
-      O[nt] *= (r < len) ? __expf(gs[r]) : 0.f;
+    for (int t = 0; t < CT; ++t) {
+      U[t] = sm.uf[par][(slice * CT + t) * 64 + lane] - WS[t];
+      const int r = 16 * t + l16;
+      O[t] *= __expf(gs[r]) * (float)(r < len);
     }
     Frag<E> Uk[CKS];
 #pragma unroll
     for (int ks = 0; ks < CKS; ++ks) Uk[ks] = acc_to_frag<E>(U[2 * ks], (2 * ks + 1 < CT) ? U[2 * ks + 1] : zero4());
-    // S <- exp(g_L) S + K^T (exp(g_L - g) * U)
+    // decayed rows exp(g_L - g_r) U_r
     const float g_last = gs[len - 1];
 #pragma unroll
-    for (int rt = 0; rt < CT; ++rt) {
+    for (int t = 0; t < CT; ++t) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * quad + i;
-        U[rt][i] *= (r < len) ? __expf(g_last - gs[r]) : 0.f;
+        const int r = 16 * t + 4 * quad + i;
+        U[t][i] *= __expf(fminf(g_last - gs[r], 0.f)) * (float)(r < len);
       }
     }
     Frag<E> Ud[CKS];
 #pragma unroll
     for (int ks = 0; ks < CKS; ++ks) Ud[ks] = acc_to_frag<E>(U[2 * ks], (2 * ks + 1 < CT) ? U[2 * ks + 1] : zero4());
+    // S <- exp(g_L) S + K^T Ud (DT independent accumulators per step), and
+    // the intra-chunk output O^T += U^T P^T
     const float gam = __expf(g_last);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      f32x4 acc = S[dt] * gam;
+    for (int dt = 0; dt < DT; ++dt) S[dt] *= gam;
 #pragma unroll
-      for (int ks = 0; ks < CKS; ++ks) acc = mma(sm.kt[par][(dt * CKS + ks) * 64 + lane], Ud[ks], acc);
-      S[dt] = acc;
-    }
-    // intra-chunk output: O^T += U^T P^T
+    for (int ks = 0; ks < CKS; ++ks) {
+      Frag<E> ka[DT];
 #pragma unroll
-    for (int nt = 0; nt < CT; ++nt) {
+      for (int dt = 0; dt < DT; ++dt) ka[dt] = sm.kt[par][(dt * CKS + ks) * 64 + lane];
+      Frag<E> pa[CT];
 #pragma unroll
-      for (int ks = 0; ks < CKS; ++ks) {
-        if (causal_zero(nt, ks)) continue;
-        O[nt] = mma(Uk[ks], sm.pf[par][(nt * CKS + ks) * 64 + lane], O[nt]);
-      }
+      for (int nt = 0; nt < CT; ++nt)
+        if (!causal_zero(nt, ks)) pa[nt] = sm.pf[par][(nt * CKS + ks) * 64 + lane];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) S[dt] = mma(ka[dt], Ud[ks], S[dt]);
+#pragma unroll
+      for (int nt = 0; nt < CT; ++nt)
+        if (!causal_zero(nt, ks)) O[nt] = mma(Uk[ks], pa[nt], O[nt]);
     }
     E* og = static_cast<E*>(a.o);
 #pragma unroll
@@ -613,18 +641,24 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
           ka[s] = sm.kt[par][((2 * ksd) * CKS + s) * 64 + lane];
           if (2 * ksd + 1 < DT) kb[s] = sm.kt[par][((2 * ksd + 1) * CKS + s) * 64 + lane];
         }
+        f32x4 acc0[CT], acc1[CT];
 #pragma unroll
-        for (int rt = 0; rt < CT; ++rt) {
-          f32x4 acc0 = zero4(), acc1 = zero4();
+        for (int rt = 0; rt < CT; ++rt) { acc0[rt] = zero4(); acc1[rt] = zero4(); }
 #pragma unroll
-          for (int s = 0; s < CKS; ++s) {
+        for (int s = 0; s < CKS; ++s) {
+          Frag<E> tb[CT];
+#pragma unroll
+          for (int rt = 0; rt < CT; ++rt)
+            if (!causal_zero(rt, s)) tb[rt] = sm.tf[1][(rt * CKS + s) * 64 + lane];
+#pragma unroll
+          for (int rt = 0; rt < CT; ++rt) {
             if (causal_zero(rt, s)) continue;            // Tinv is lower triangular
-            const Frag<E> tb = sm.tf[1][(rt * CKS + s) * 64 + lane];
-            acc0 = mma(ka[s], tb, acc0);
-            if (2 * ksd + 1 < DT) acc1 = mma(kb[s], tb, acc1);
+            acc0[rt] = mma(ka[s], tb[rt], acc0[rt]);
+            if (2 * ksd + 1 < DT) acc1[rt] = mma(kb[s], tb[rt], acc1[rt]);
           }
-          sm.wf[par][(rt * DKS + ksd) * 64 + lane] = acc_to_frag<E>(acc0, acc1);
         }
+#pragma unroll
+        for (int rt = 0; rt < CT; ++rt) sm.wf[par][(rt * DKS + ksd) * 64 + lane] = acc_to_frag<E>(acc0[rt], acc1[rt]);
       } else if (item < DKS + NS) {
         // Ut accumulator tiles of slice sl: Tinv diag(b) V
         const int sl = item - DKS;
@@ -632,16 +666,21 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
         Frag<E> vf[CKS];
 #pragma unroll
         for (int s = 0; s < CKS; ++s) vf[s] = load_frag<E>(vrow + 32 * s, quad, C - 32 * s);
+        f32x4 acc[CT];
 #pragma unroll
-        for (int rt = 0; rt < CT; ++rt) {
-          f32x4 acc = zero4();
+        for (int rt = 0; rt < CT; ++rt) acc[rt] = zero4();
 #pragma unroll
-          for (int s = 0; s < CKS; ++s) {
-            if (causal_zero(rt, s)) continue;
-            acc = mma(sm.tf[0][(rt * CKS + s) * 64 + lane], vf[s], acc);
-          }
-          sm.uf[par][(sl * CT + rt) * 64 + lane] = acc;
+        for (int s = 0; s < CKS; ++s) {
+          Frag<E> tb[CT];
+#pragma unroll
+          for (int rt = 0; rt < CT; ++rt)
+            if (!causal_zero(rt, s)) tb[rt] = sm.tf[0][(rt * CKS + s) * 64 + lane];
+#pragma unroll
+          for (int rt = 0; rt < CT; ++rt)
+            if (!causal_zero(rt, s)) acc[rt] = mma(tb[rt], vf[s], acc[rt]);
         }
+#pragma unroll
+        for (int rt = 0; rt < CT; ++rt) sm.uf[par][(sl * CT + rt) * 64 + lane] = acc[rt];
       } else {
         // masked, decayed q.k fragments of query tile nt
         const int nt = item - DKS - NS;
@@ -655,7 +694,10 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int j = frag_k(s, quad, e);
-            v[e] = (j <= r && r < len) ? to_e<E>(to_f(raw[e]) * __expf(gr - gp[j])) : to_e<E>(0.f);
+            // the exponent is clamped at 0 so that masked entries (j > r,
+            // where g_r - g_j >= 0) cannot overflow before being zeroed
+            const float m = (float)(j <= r && r < len);
+            v[e] = to_e<E>(to_f(raw[e]) * (__expf(fminf(gr - gp[j], 0.f)) * m));
           }
           sm.pf[par][(nt * CKS + s) * 64 + lane] = v;
         }

@@ -142,15 +142,17 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_gate_prefix(const PrefillArgs a
 }
 
 // --------------------------------------------------------------------------
-// Kernel 2: per (chunk, QK head): K^T fragments, the q.k fragments, and for
-// each of the QK head's V heads A = strict_lower(b_r (k_r . k_i)
-// exp(g_r - g_i)) and Tinv = (I + A)^{-1}.
-// K K^T and Q K^T are formed once with MFMA and shared by the V heads. Each
-// wave inverts one V head's unit lower-triangular I + A blockwise in fp32:
-// the 16 x 16 diagonal blocks by forward substitution (one lane per column),
-// then the blocks below them in order of distance from the diagonal,
+// Kernel 2: per (chunk, V head): A = strict_lower(b_r (k_r . k_i)
+// exp(g_r - g_i)), Tinv = (I + A)^{-1}, written as the fragments of
+// Tinv diag(b) and Tinv diag(b exp(g)) (the right factors of Ut and W).
+// The first V head of each QK group also writes the chunk's K^T and q.k
+// fragments, which the QK group's V heads share.
+// K K^T (and Q K^T) are formed with MFMA. Tinv is assembled blockwise in
+// fp32 over the four waves: the 16 x 16 diagonal blocks by forward
+// substitution (one lane per column), then the blocks below them in order
+// of distance from the diagonal,
 //   Tinv_ij = -Tinv_ii sum_{j<=m<i} A_im Tinv_mj,
-// with fp32 16x16x4 MFMAs. Tinv is then re-read from LDS as fragments.
+// with fp32 16x16x4 MFMAs, one block per wave per distance.
 // --------------------------------------------------------------------------
 
 // acc += X Y for 16 x 16 fp32 tiles in LDS (row-major, leading dims lx, ly)
@@ -165,34 +167,39 @@ __device__ __forceinline__ f32x4 mma16_f32(const float* X, int lx, const float* 
 
 template <typename E, int D, int C>
 struct InvSmem {
-  static constexpr int KLD = D + 8, NW = kBlock / 64;
+  static constexpr int KLD = D + 8;    // bf16/fp32 row stride of the staged keys and queries
+  static constexpr int FLD = C + 4;    // fp32 row stride of C x C tiles (spreads rows over banks)
+  static constexpr int XLD = 20;       // row stride of the 16 x 16 scratch tiles
   union {
     struct {
       E ks[C * KLD];                   // keys of the chunk, rows past its end zero
       E qs[C * KLD];                   // queries of the chunk
     } in;
     struct {
-      float t[NW][C * C];              // Tinv being assembled, one per wave
-      float x[NW][256];                // 16 x 16 scratch tile, one per wave
+      float t[C * FLD];                // Tinv being assembled
+      float x[4][16 * XLD];            // one 16 x 16 scratch tile per wave
     } out;
   } u;
-  float kk[C * C];                     // K K^T (lower tiles), kept for every head group
-  float ab[NW][C * C];                 // A per wave; ab[0] first stages q.k
-  float sb[NW][C];
+  float kk[C * FLD];                   // K K^T (lower tiles), later q.k staging
+  float a[C * FLD];                    // A (below the diagonal)
+  float gb[2][C];                      // g and b of this V head
 };
 
 template <typename E, int D, int C>
 __global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   using SM = InvSmem<E, D, C>;
-  constexpr int CT = G::CT, CKS = G::CKS, DKS = G::DKS, KLD = SM::KLD, NW = SM::NW;
+  constexpr int CT = G::CT, CKS = G::CKS, DKS = G::DKS, KLD = SM::KLD, FLD = SM::FLD, XLD = SM::XLD;
+  constexpr int NW = kBlock / 64;
   constexpr int VE = 16 / (int)sizeof(E);                 // elements per 16-byte load
   typedef E VLoad __attribute__((ext_vector_type(VE)));
   __shared__ SM sm;
-  const int c = blockIdx.x, hq = blockIdx.y;
+  const int c = blockIdx.x, hv = blockIdx.y;
   const int4 tab = reinterpret_cast<const int4*>(a.chunk_table)[c];
   if (tab.x < 0) return;
   const int start = tab.y, len = tab.z;
+  const int hq = hv / a.group;
+  const bool lead = (hv % a.group) == 0;          // writes the QK head's shared fragments
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, l16 = lane & 15;
   const E* kg = static_cast<const E*>(a.k);
   const E* qg = static_cast<const E*>(a.q);
@@ -205,144 +212,146 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a
     if (r < len) {
       const int64_t gi = ((int64_t)(start + r) * a.h_qk + hq) * D + d;
       kv = *reinterpret_cast<const VLoad*>(kg + gi);
-      qv = *reinterpret_cast<const VLoad*>(qg + gi);
+      if (lead) qv = *reinterpret_cast<const VLoad*>(qg + gi);
     }
-#pragma unroll
-    for (int e = 0; e < VE; ++e) { sm.u.in.ks[r * KLD + d + e] = kv[e]; sm.u.in.qs[r * KLD + d + e] = qv[e]; }
+    *reinterpret_cast<VLoad*>(&sm.u.in.ks[r * KLD + d]) = kv;
+    if (lead) *reinterpret_cast<VLoad*>(&sm.u.in.qs[r * KLD + d]) = qv;
+  }
+  if (tid < 2 * C) {
+    const int64_t o = ((int64_t)c * a.h_v + hv) * C + (tid % C);
+    sm.gb[tid / C][tid % C] = (tid < C) ? a.gate_prefix[o] : a.beta_chunk[o];
   }
   __syncthreads();
 
-  // K^T fragments: frag (dt, s), lane row d, elements token i.
-  Frag<E>* ktg = reinterpret_cast<Frag<E>*>(a.key_t) + ((int64_t)c * a.h_qk + hq) * G::KT_FR * 64;
-  for (int it = tid; it < G::KT_FR * 64; it += kBlock) {
-    const int f = it / 64, ln = it % 64, dt = f / CKS, s = f % CKS, q4 = ln >> 4;
-    const int d = 16 * dt + (ln & 15);
-    Frag<E> v;
+  if (lead) {
+    // K^T fragments: frag (dt, s), lane row d, elements token i.
+    Frag<E>* ktg = reinterpret_cast<Frag<E>*>(a.key_t) + ((int64_t)c * a.h_qk + hq) * G::KT_FR * 64;
+    for (int it = tid; it < G::KT_FR * 64; it += kBlock) {
+      const int f = it / 64, ln = it % 64, dt = f / CKS, s = f % CKS, q4 = ln >> 4;
+      const int d = 16 * dt + (ln & 15);
+      Frag<E> v;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int i = frag_k(s, q4, e);
-      v[e] = (i < C) ? sm.u.in.ks[i * KLD + d] : to_e<E>(0.f);
+      for (int e = 0; e < 8; ++e) {
+        const int i = frag_k(s, q4, e);
+        v[e] = (i < C) ? sm.u.in.ks[i * KLD + d] : to_e<E>(0.f);
+      }
+      ktg[it] = v;
     }
-    ktg[it] = v;
   }
 
-  // K K^T (lower tiles) and q.k (tiles with key tile <= query tile, stored
-  // as [query r][key j] in ab[0])
-  float* qkl = sm.ab[0];
-  for (int t = wave; t < 2 * CT * CT; t += NW) {
-    const bool is_qk = t >= CT * CT;
-    const int tt = is_qk ? t - CT * CT : t;
-    const int mi = tt / CT, ni = tt % CT;   // KK: row tile mi, col tile ni; q.k: key tile mi, query tile ni
-    if (ni > mi && !is_qk) continue;
-    if (mi > ni && is_qk) continue;
-    const E* brow = is_qk ? &sm.u.in.qs[(16 * ni + l16) * KLD] : &sm.u.in.ks[(16 * ni + l16) * KLD];
+  // K K^T lower tiles: CT (CT + 1) / 2 tiles over the waves
+  for (int t = wave; t < CT * CT; t += NW) {
+    const int mi = t / CT, ni = t % CT;
+    if (ni > mi) continue;
     f32x4 acc = zero4();
 #pragma unroll
     for (int ks = 0; ks < DKS; ++ks)
       acc = mma(load_frag<E>(&sm.u.in.ks[(16 * mi + l16) * KLD + 32 * ks], quad, D - 32 * ks),
-                load_frag<E>(brow + 32 * ks, quad, D - 32 * ks), acc);
+                load_frag<E>(&sm.u.in.ks[(16 * ni + l16) * KLD + 32 * ks], quad, D - 32 * ks), acc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (!is_qk) sm.kk[(16 * mi + 4 * quad + i) * C + 16 * ni + l16] = acc[i];
-      else qkl[(16 * ni + l16) * C + 16 * mi + 4 * quad + i] = acc[i];
+    for (int i = 0; i < 4; ++i) sm.kk[(16 * mi + 4 * quad + i) * FLD + 16 * ni + l16] = acc[i];
+  }
+  __syncthreads();
+  // A below the diagonal (the inverse never reads the rest)
+  for (int idx = tid; idx < C * C; idx += kBlock) {
+    const int r = idx / C, i = idx % C;
+    if (i < r)
+      sm.a[r * FLD + i] = sm.gb[1][r] * sm.kk[r * FLD + i] * __expf(fminf(sm.gb[0][r] - sm.gb[0][i], 0.f));
+  }
+  if (lead) {
+    // q.k tiles with key tile <= query tile, staged [query r][key j] in kk
+    // (K K^T is consumed by now; a barrier separates the two)
+  }
+  __syncthreads();
+  if (lead) {
+    for (int t = wave; t < CT * CT; t += NW) {
+      const int kt = t / CT, nt = t % CT;     // key tile, query tile
+      if (kt > nt) continue;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks)
+        acc = mma(load_frag<E>(&sm.u.in.ks[(16 * kt + l16) * KLD + 32 * ks], quad, D - 32 * ks),
+                  load_frag<E>(&sm.u.in.qs[(16 * nt + l16) * KLD + 32 * ks], quad, D - 32 * ks), acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.kk[(16 * nt + l16) * FLD + 16 * kt + 4 * quad + i] = acc[i];
     }
   }
   __syncthreads();
-  // q.k fragments: frag (nt, s), lane col = query r, elements key j.
-  Frag<E>* qkg = reinterpret_cast<Frag<E>*>(a.qk) + ((int64_t)c * a.h_qk + hq) * G::QK_FR * 64;
-  for (int it = tid; it < G::QK_FR * 64; it += kBlock) {
-    const int f = it / 64, ln = it % 64, nt = f / CKS, s = f % CKS, q4 = ln >> 4;
-    const int r = 16 * nt + (ln & 15);
-    Frag<E> v;
+  if (lead) {
+    // q.k fragments: frag (nt, s), lane col = query r, elements key j.
+    Frag<E>* qkg = reinterpret_cast<Frag<E>*>(a.qk) + ((int64_t)c * a.h_qk + hq) * G::QK_FR * 64;
+    for (int it = tid; it < G::QK_FR * 64; it += kBlock) {
+      const int f = it / 64, ln = it % 64, nt = f / CKS, s = f % CKS, q4 = ln >> 4;
+      const int r = 16 * nt + (ln & 15);
+      Frag<E> v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = frag_k(s, q4, e);
+        v[e] = (j < C && (j >> 4) <= nt) ? to_e<E>(sm.kk[r * FLD + j]) : to_e<E>(0.f);
+      }
+      qkg[it] = v;
+    }
+  }
+  __syncthreads();     // staged keys and queries are dead from here on; out.t reuses them
+
+  float* Tm = sm.u.out.t;
+  // blocks above the diagonal are zero
+  for (int idx = tid; idx < C * C; idx += kBlock) {
+    const int r = idx / C, i = idx % C;
+    if ((i >> 4) > (r >> 4)) Tm[r * FLD + i] = 0.f;
+  }
+  // diagonal blocks: wave b solves block b, lane j its column j
+  for (int b = wave; b < CT; b += NW) {
+    if (lane < 16) {
+      const int j = lane, o = 16 * b;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float s0 = (r == j) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < r; ++i) {
+          if (i & 1) s1 -= sm.a[(o + r) * FLD + o + i] * x[i];
+          else s0 -= sm.a[(o + r) * FLD + o + i] * x[i];
+        }
+        x[r] = s0 + s1;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Tm[(o + r) * FLD + o + j] = x[r];
+    }
+  }
+  __syncthreads();
+  // blocks below the diagonal, by distance; one block per wave per distance
+#pragma unroll
+  for (int dist = 1; dist < CT; ++dist) {
+    for (int bi = dist + wave; bi < CT; bi += NW) {
+      const int bj = bi - dist;
+      float* X = sm.u.out.x[wave];
+      f32x4 acc = zero4();
+      for (int bm = bj; bm < bi; ++bm)
+        acc = mma16_f32(&sm.a[(16 * bi) * FLD + 16 * bm], FLD, &Tm[(16 * bm) * FLD + 16 * bj], FLD, acc, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) X[(4 * quad + i) * XLD + l16] = acc[i];
+      acc = mma16_f32(&Tm[(16 * bi) * FLD + 16 * bi], FLD, X, XLD, zero4(), lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Tm[(16 * bi + 4 * quad + i) * FLD + 16 * bj + l16] = -acc[i];
+    }
+    __syncthreads();
+  }
+  // Tinv diag(b) and Tinv diag(b exp(g)) fragments, written one after the other
+  Frag<E>* tg = reinterpret_cast<Frag<E>*>(a.tinv) + ((int64_t)c * a.h_v + hv) * 2 * G::T_FR * 64;
+  for (int it = tid; it < G::T_FR * 64; it += kBlock) {
+    const int f = it / 64, ln = it % 64, rt = f / CKS, s = f % CKS, q4 = ln >> 4;
+    const int r = 16 * rt + (ln & 15);
+    Frag<E> vb, vg;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int j = frag_k(s, q4, e);
-      v[e] = (j < C && (j >> 4) <= nt) ? to_e<E>(qkl[r * C + j]) : to_e<E>(0.f);
+      const int i = frag_k(s, q4, e);
+      const float t = (i < C) ? Tm[r * FLD + i] * sm.gb[1][i] : 0.f;
+      vb[e] = to_e<E>(t);
+      vg[e] = to_e<E>((i < C) ? t * __expf(sm.gb[0][i]) : 0.f);
     }
-    qkg[it] = v;
-  }
-  __syncthreads();
-
-  const float* gch = a.gate_prefix + (int64_t)c * a.h_v * C;
-  const float* bch = a.beta_chunk + (int64_t)c * a.h_v * C;
-  for (int h0 = 0; h0 < a.group; h0 += NW) {
-    const int nh = min(NW, a.group - h0);
-    for (int w = 0; w < nh; ++w) {
-      if (tid < C) sm.sb[w][tid] = bch[(int64_t)(hq * a.group + h0 + w) * C + tid];
-    }
-    __syncthreads();
-    // A below the diagonal only (the inverse never reads the rest)
-    for (int w = 0; w < nh; ++w) {
-      const float* gh = gch + (int64_t)(hq * a.group + h0 + w) * C;
-      for (int idx = tid; idx < C * C; idx += kBlock) {
-        const int r = idx / C, i = idx % C;
-        if (i < r) sm.ab[w][idx] = (r < len) ? sm.sb[w][r] * sm.kk[idx] * __expf(gh[r] - gh[i]) : 0.f;
-      }
-    }
-    __syncthreads();
-    if (wave < nh) {
-      const int hv = hq * a.group + h0 + wave;
-      const float* A = sm.ab[wave];
-      float* Tm = sm.u.out.t[wave];
-      float* X = sm.u.out.x[wave];
-      // blocks above the diagonal are zero
-      for (int idx = lane; idx < C * C; idx += 64)
-        if ((idx % C) / 16 > (idx / C) / 16) Tm[idx] = 0.f;
-      // diagonal blocks: lane = 16 b + j solves column j of block b
-      if (lane < 16 * CT) {
-        const int b = lane >> 4, j = lane & 15, o = 16 * b;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float s0 = (r == j) ? 1.f : 0.f, s1 = 0.f;
-#pragma unroll
-          for (int i = 0; i < r; ++i) {
-            if (i & 1) s1 -= A[(o + r) * C + o + i] * x[i];
-            else s0 -= A[(o + r) * C + o + i] * x[i];
-          }
-          x[r] = s0 + s1;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Tm[(o + r) * C + o + j] = x[r];
-      }
-      // blocks below the diagonal, by distance from it
-#pragma unroll
-      for (int dist = 1; dist < CT; ++dist) {
-#pragma unroll
-        for (int bi = dist; bi < CT; ++bi) {
-          const int bj = bi - dist;
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int bm = bj; bm < bi; ++bm)
-            acc = mma16_f32(&A[(16 * bi) * C + 16 * bm], C, &Tm[(16 * bm) * C + 16 * bj], C, acc, lane);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) X[(4 * quad + i) * 16 + l16] = acc[i];
-          acc = mma16_f32(&Tm[(16 * bi) * C + 16 * bi], C, X, 16, zero4(), lane);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) Tm[(16 * bi + 4 * quad + i) * C + 16 * bj + l16] = -acc[i];
-        }
-      }
-      // Tinv diag(b) and Tinv diag(b exp(g)) fragments (the right factors of
-      // Ut and W), written one after the other
-      Frag<E>* tg = reinterpret_cast<Frag<E>*>(a.tinv) + ((int64_t)c * a.h_v + hv) * 2 * G::T_FR * 64;
-      const float* gh = gch + (int64_t)hv * C;
-#pragma unroll
-      for (int f = 0; f < G::T_FR; ++f) {
-        const int rt = f / CKS, s = f % CKS;
-        const int r = 16 * rt + l16;
-        Frag<E> vb, vg;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = frag_k(s, quad, e);
-          const float t = (i < C) ? Tm[r * C + i] * sm.sb[wave][i] : 0.f;
-          vb[e] = to_e<E>(t);
-          vg[e] = to_e<E>((i < C) ? t * __expf(gh[i]) : 0.f);
-        }
-        tg[f * 64 + lane] = vb;
-        tg[(G::T_FR + f) * 64 + lane] = vg;
-      }
-    }
-    __syncthreads();
+    tg[it] = vb;
+    tg[G::T_FR * 64 + it] = vg;
   }
 }
 
@@ -778,7 +787,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
   for (int stage = first; stage <= last; ++stage) {
     switch (stage) {
       case 1: gdn_k1_gate_prefix<C><<<dim3(nc), dim3(kBlock), 0, s>>>(a); break;
-      case 2: gdn_k2_akk_inverse<E, D, C><<<dim3(nc, a.h_qk), dim3(kBlock), 0, s>>>(a); break;
+      case 2: gdn_k2_akk_inverse<E, D, C><<<dim3(nc, a.h_v), dim3(kBlock), 0, s>>>(a); break;
       case 3: gdn_k3_scan<E, D, C><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a); break;
       default: return hipErrorInvalidValue;
     }

@@ -57,7 +57,8 @@ def algorithmic_work(T, HQ, HV, D, C, N, decode_batch):
 
 
 def load_traffic(kernel):
-    """Measured HBM traffic of `kernel` from the committed counter summary, or
+    """Measured HBM bytes per launch of `kernel` from the committed counter
+    summary (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or
     None when there is none or the kernel source changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -106,7 +107,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (read BYTES, write BYTES) a few "
+                         "times, as the reference for scaling HBM byte counters")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr)
@@ -215,6 +229,10 @@ def main():
         "decode_GBps": round(dec_bytes / (decode_ms * 1e-3) / 1e9, 1),
         "decode_hbm_frac": round(dec_bytes / (decode_ms * 1e-3) / PEAK_HBM_BYTES, 4),
         "roofline": roofline,
+        "roofline_decode": {"kernel": DECODE_KERNEL, "bound": "hbm",
+                            "achieved": kernels[DECODE_KERNEL]["achieved"], "peak": 8000.0,
+                            "unit": "GB/s", "frac": kernels[DECODE_KERNEL]["frac"],
+                            "traffic": load_traffic(DECODE_KERNEL)},
         "kernels": kernels,
         "cpu_baseline": None,
     }

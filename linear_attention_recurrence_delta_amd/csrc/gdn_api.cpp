@@ -43,6 +43,8 @@ gdn_status_t check_dims(const gdn_dims_t* d, bool decode) {
   if (d->h_qk < 1 || d->h_v < 1) return fail(GDN_ERROR_INVALID_VALUE, "h_qk and h_v must be >= 1");
   if (d->h_v % d->h_qk) return fail(GDN_ERROR_INVALID_VALUE, "h_v (%d) must be a multiple of h_qk (%d)", d->h_v, d->h_qk);
   if (d->h_v > 65535) return fail(GDN_ERROR_NOT_SUPPORTED, "h_v > 65535 is not supported");
+  if (!decode && (d->total_tokens / (d->chunk > 0 ? d->chunk : 1) + d->num_seqs) * d->h_v > INT32_MAX)
+    return fail(GDN_ERROR_NOT_SUPPORTED, "too many (chunk, V head) pairs for one launch");
   if (d->dk < 1 || d->dv < 1) return fail(GDN_ERROR_INVALID_VALUE, "dk and dv must be >= 1");
   if (d->dtype != GDN_DTYPE_F32 && d->dtype != GDN_DTYPE_BF16)
     return fail(GDN_ERROR_INVALID_VALUE, "unknown dtype %d", d->dtype);

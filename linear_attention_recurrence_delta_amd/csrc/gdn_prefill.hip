@@ -60,6 +60,16 @@ struct Cfg {
   static constexpr int VLD = C + 8;            // row stride of the transposed V slice
 };
 
+// Workgroups are dispatched round-robin over the chip's 8 XCDs (each with
+// its own L2): workgroup b runs on XCD b % 8. Renumbering so that logical
+// ids [k n/8, (k+1) n/8) all run on XCD k keeps workgroups that read the
+// same operands (consecutive logical ids) behind one L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_local_id(int64_t b, int64_t n) {
+  if (n % kXcds) return b;
+  return (b % kXcds) * (n / kXcds) + b / kXcds;
+}
+
 // Contraction index of fragment element e at 32-step s for lane quad q.
 __device__ __forceinline__ int frag_k(int s, int quad, int e) {
   return 32 * s + (e < 4 ? 4 * quad + e : 16 + 4 * quad + (e - 4));
@@ -194,7 +204,10 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a
   constexpr int VE = 16 / (int)sizeof(E);                 // elements per 16-byte load
   typedef E VLoad __attribute__((ext_vector_type(VE)));
   __shared__ SM sm;
-  const int c = blockIdx.x, hv = blockIdx.y;
+  // the V heads of one (chunk, QK head), which read the same keys, are
+  // consecutive logical ids and so share an XCD
+  const int64_t lid = xcd_local_id(blockIdx.x, gridDim.x);
+  const int c = (int)(lid / a.h_v), hv = (int)(lid % a.h_v);
   const int4 tab = reinterpret_cast<const int4*>(a.chunk_table)[c];
   if (tab.x < 0) return;
   const int start = tab.y, len = tab.z;
@@ -421,7 +434,9 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   constexpr int NPROD = kScanBlock / 64 - NS;
   __shared__ ScanSmem<E, D, C> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, l16 = lane & 15;
-  const int64_t bid = blockIdx.x;
+  // the column blocks and V heads of one QK head, which read the same K^T,
+  // q.k and Q fragments, are consecutive logical ids and so share an XCD
+  const int64_t bid = xcd_local_id(blockIdx.x, gridDim.x);
   const int cb = (int)(bid % G::NCB);
   const int hv = (int)((bid / G::NCB) % a.h_v);
   const int64_t n = bid / ((int64_t)G::NCB * a.h_v);
@@ -787,7 +802,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
   for (int stage = first; stage <= last; ++stage) {
     switch (stage) {
       case 1: gdn_k1_gate_prefix<C><<<dim3(nc), dim3(kBlock), 0, s>>>(a); break;
-      case 2: gdn_k2_akk_inverse<E, D, C><<<dim3(nc, a.h_v), dim3(kBlock), 0, s>>>(a); break;
+      case 2: gdn_k2_akk_inverse<E, D, C><<<dim3(nc * (unsigned)a.h_v), dim3(kBlock), 0, s>>>(a); break;
       case 3: gdn_k3_scan<E, D, C><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a); break;
       default: return hipErrorInvalidValue;
     }

@@ -1,0 +1,114 @@
+"""Summaries of rocprofv3 output for the committed profiles.
+
+    python -m linear_attention_recurrence_delta_amd.profiling stats KERNEL_STATS_CSV --title T --command C
+        -> markdown table of per-kernel launch counts and durations
+    python -m linear_attention_recurrence_delta_amd.profiling traffic \
+        --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV --copy-bytes N [--out JSON]
+        -> HBM bytes per launch of each libgdn kernel
+
+FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
+counter reads for a plain device copy of known size (bench.py
+--copy-calibration N reads N bytes and writes N bytes per launch), so that
+the reported bytes are in the copy's units.
+"""
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import statistics
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+# kernel -> source file that defines it
+SOURCES = {"gdn_k1_gate_prefix": "gdn_prefill.hip", "gdn_k2_akk_inverse": "gdn_prefill.hip",
+           "gdn_k3_scan": "gdn_prefill.hip", "gdn_kd_decode_step": "gdn_decode.hip"}
+
+
+def short_name(name):
+    m = re.search(r"(gdn_k\w+?)(?:I|\(|<|E|$)", name)
+    if m:
+        return m.group(1)
+    return name.split("(")[0][:60]
+
+
+def kernel_stats(path):
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append(r)
+    out = ["| kernel | calls | avg (us) | min (us) | max (us) | total (us) | % |",
+           "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        ns = lambda k: float(r[k]) / 1000.0  # noqa: E731
+        out.append(f"| {short_name(r['Name'])} | {r['Calls']} | {ns('AverageNs'):.1f} | "
+                   f"{ns('MinNs'):.1f} | {ns('MaxNs'):.1f} | {ns('TotalDurationNs'):.1f} | "
+                   f"{float(r['Percentage']):.1f} |")
+    return "\n".join(out)
+
+
+def counter_per_kernel(path, counter):
+    vals = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(short_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return {k: statistics.median(v) for k, v in vals.items()}
+
+
+def copy_counter(path, counter):
+    vals = [v for k, v in counter_per_kernel(path, counter).items() if "gdn_" not in k]
+    if not vals:
+        raise SystemExit(f"no copy kernel in {path}")
+    return max(vals)
+
+
+def traffic(fetch, write, copy_fetch, copy_write, copy_bytes):
+    fsc = copy_bytes / (copy_counter(copy_fetch, "FETCH_SIZE") * 1024.0)
+    wsc = copy_bytes / (copy_counter(copy_write, "WRITE_SIZE") * 1024.0)
+    f = counter_per_kernel(fetch, "FETCH_SIZE")
+    w = counter_per_kernel(write, "WRITE_SIZE")
+    out = {"_calibration": {"copy_bytes_each_way": copy_bytes, "fetch_scale": round(fsc, 4),
+                            "write_scale": round(wsc, 4)}}
+    for k in sorted(set(f) & set(w)):
+        if k not in SOURCES:
+            continue
+        src = os.path.join(HERE, "csrc", SOURCES[k])
+        with open(src, "rb") as fh:
+            sha = hashlib.sha256(fh.read()).hexdigest()
+        fb, wb = f[k] * 1024.0 * fsc, w[k] * 1024.0 * wsc
+        out[k] = {"source": SOURCES[k], "source_sha256": sha, "fetch_kib_raw": f[k],
+                  "write_kib_raw": w[k], "fetch_bytes": round(fb), "write_bytes": round(wb),
+                  "bytes_per_launch": round(fb + wb)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--title", default="Kernel trace")
+    s.add_argument("--command", default="")
+    t = sub.add_parser("traffic")
+    for a in ("--fetch", "--write", "--copy-fetch", "--copy-write"):
+        t.add_argument(a, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--out")
+    args = ap.parse_args()
+    if args.cmd == "stats":
+        print(f"# {args.title}\n\nCommand (GPU box, repo root):\n\n    {args.command}\n")
+        print(kernel_stats(args.csv))
+    else:
+        res = traffic(args.fetch, args.write, args.copy_fetch, args.copy_write, args.copy_bytes)
+        text = json.dumps(res, indent=1)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text + "\n")
+        print(text)
+
+
+if __name__ == "__main__":
+    main()

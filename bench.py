@@ -30,30 +30,43 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN prefill tokens/s at T=64K (48 V heads, d=128) + decode state GB/s"
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
-STAGES = ["gdn_k1_gate_prefix", "gdn_k2_akk_inverse", "gdn_k3_scan"]
+STAGES = ["gdn_k1_chunk_prep", "gdn_k2_inverse_w", "gdn_k3_scan"]
 DECODE_KERNEL = "gdn_kd_decode_step"
 
 
 def algorithmic_work(T, HQ, HV, D, C, N, decode_batch):
-    """Per-launch algorithmic work of each kernel (flops for the contraction
-    kernels, bytes for the bandwidth-bound ones), from the chunkwise method's
-    operation counts; see the design notes."""
+    """Per-launch algorithmic flops and HBM bytes of each kernel, from the
+    chunkwise method's operation counts (dense C x C in-chunk products, bf16
+    q/k/v/o and fragments, fp32 gates and states), and the resource that
+    bounds it (the one whose time at peak is larger); see the design notes.
+    Returns ({kernel: (bound, flops, bytes)}, flops per token)."""
     dk = dv = D
+    e = 2                                       # bytes per bf16 element
+    gates = T * HV * 8                          # log a and b (fp32), or g and b
     work = {
-        # reads log a and b, writes g and per-chunk b
-        "gdn_k1_gate_prefix": ("hbm", 4.0 * T * HV * 4),
-        # K K^T and Q K^T per QK head, the triangular inverse per V head
-        "gdn_k2_akk_inverse": ("mfma", T * (HQ * 4 * C * dk + HV * C * C / 3.0)),
-        # W, Ut, W S, K^T U, Q S and (Q K^T) U per V head
-        "gdn_k3_scan": ("mfma", T * HV * (6 * dk * dv + 2 * C * dk + 4 * C * dv)),
+        # Q K^T per QK head; reads q, k, log a, b; writes K^T, q.k, g, b
+        "gdn_k1_chunk_prep": (T * HQ * 2 * C * dk,
+                              2 * T * HQ * dk * e + gates + T * HQ * (dk + C) * e + gates),
+        # K K^T per QK head, the triangular inverse and W per V head; reads k,
+        # K^T, g, b; writes Tinv diag(b) and W
+        "gdn_k2_inverse_w": (T * (HQ * 2 * C * dk + HV * (C * C / 3.0 + 2 * C * dk)),
+                             2 * T * HQ * dk * e + gates + T * HV * (C + dk) * e),
+        # Ut, W S, Q S, K^T U, (Q K^T) U per V head; reads q, v, K^T, q.k,
+        # Tinv diag(b), W, g, b and the initial states; writes o, final states
+        "gdn_k3_scan": (T * HV * (6 * dk * dv + 4 * C * dv),
+                        T * HQ * (2 * dk + C) * e + T * HV * (dv + C + dk) * e + gates
+                        + T * HV * dv * e + 2 * N * HV * dk * dv * 4),
     }
-    total_flops = sum(w for b, w in work.values() if b == "mfma")
     per_token = HV * (6 * dk * dv + 2 * C * dk + 4 * C * dv + C * C / 3.0) + HQ * 4 * C * dk
+    total_flops = sum(f for f, _ in work.values())
     assert abs(total_flops - per_token * T) < 1e-6 * total_flops
+    out = {}
+    for k, (f, b) in work.items():
+        out[k] = ("mfma" if f / PEAK_BF16_FLOPS > b / PEAK_HBM_BYTES else "hbm", float(f), float(b))
     state = decode_batch * HV * dk * dv * 4
     dec_bytes = 2 * state + decode_batch * (2 * HQ * dk * 2 + 2 * HV * dv * 2 + 2 * HV * 4)
-    work[DECODE_KERNEL] = ("hbm", float(dec_bytes))
-    return work, per_token
+    out[DECODE_KERNEL] = ("hbm", 0.0, float(dec_bytes))
+    return out, per_token
 
 
 def load_traffic(kernel):
@@ -190,7 +203,8 @@ def main():
     work, per_token = algorithmic_work(T, HQ, HV, D, C, 1, NB)
     kernels = {}
     for n in names:
-        bound, amount = work[n]
+        bound, flops, nbytes = work[n]
+        amount = flops if bound == "mfma" else nbytes
         rate = amount / (ms[n] * 1e-3)
         peak = PEAK_BF16_FLOPS if bound == "mfma" else PEAK_HBM_BYTES
         kernels[n] = {"ms": round(ms[n], 4), "bound": bound,
@@ -202,7 +216,7 @@ def main():
     roofline = {"kernel": dominant, "bound": dk["bound"], "achieved": dk["achieved"],
                 "peak": 2500.0 if dk["bound"] == "mfma" else 8000.0, "unit": dk["unit"],
                 "frac": dk["frac"], "traffic": load_traffic(dominant)}
-    dec_bytes = work[DECODE_KERNEL][1]
+    dec_bytes = work[DECODE_KERNEL][2]
     tokens_per_s = T / (prefill_ms * 1e-3)
 
     line = {

@@ -98,9 +98,9 @@ gdn_status_t gdn_chunk_fwd(const gdn_dims_t* dims,
 /*
  * Diagnostic variant of gdn_chunk_fwd that enqueues only launches
  * first_stage..last_stage, so a profiler or benchmark can put events between
- * them: 1 = gate prefix sums and chunk table; 2 = K K^T, Q K^T and
- * (I + A)^{-1}; 3 = the fused W/U construction, inter-chunk state scan and
- * output products. Arguments are those of gdn_chunk_fwd. Stages after the
+ * them: 1 = chunk table, gate prefix sums, K^T and Q K^T; 2 = K K^T,
+ * (I + A)^{-1} and W; 3 = the fused U construction, inter-chunk state scan
+ * and output products. Arguments are those of gdn_chunk_fwd. Stages after the
  * first read what earlier stages left in `workspace`, so a call starting at
  * stage s > 1 must follow calls that ran stages 1..s-1 with identical
  * arguments and workspace on the same stream. gdn_chunk_fwd is
@@ -155,7 +155,8 @@ typedef struct {
   size_t seq_chunk_offset; /* int32 [N+1]: first compact chunk of each sequence */
   size_t gate_prefix;  /* fp32 [max_chunks][h_v][C]: in-chunk inclusive prefix of log a */
   size_t beta_chunk;   /* fp32 [max_chunks][h_v][C]: b of each chunk row, 0 past its end */
-  size_t tinv;         /* dtype [max_chunks][h_v]: (I + A)^{-1} as MFMA fragments */
+  size_t tinv;         /* dtype [max_chunks][h_v]: (I + A)^{-1} diag(b) as MFMA fragments */
+  size_t w;            /* dtype [max_chunks][h_v]: W = (I + A)^{-1} diag(b exp(g)) K as MFMA fragments */
   size_t key_t;        /* dtype [max_chunks][h_qk]: K^T as MFMA fragments */
   size_t qk;           /* dtype [max_chunks][h_qk]: q_r . k_j (j-tile <= r-tile) as fragments */
   size_t total;        /* == gdn_chunk_fwd_workspace_bytes(dims) */

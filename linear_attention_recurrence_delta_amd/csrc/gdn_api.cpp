@@ -86,7 +86,8 @@ Layout compute_layout(const gdn_dims_t& d) {
   L.v.seq_chunk_offset = take((N + 1) * 4);
   L.v.gate_prefix = take(NC * HV * C * 4);
   L.v.beta_chunk = take(NC * HV * C * 4);
-  L.v.tinv = take(2 * NC * HV * CT * CKS * 512 * esz);
+  L.v.tinv = take(NC * HV * CT * CKS * 512 * esz);
+  L.v.w = take(NC * HV * CT * ((DT + 1) / 2) * 512 * esz);
   L.v.key_t = take(NC * HQ * DT * CKS * 512 * esz);
   L.v.qk = take(NC * HQ * CT * CKS * 512 * esz);
   L.v.total = off;
@@ -187,6 +188,7 @@ gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims, const void* q, const v
   a.gate_prefix = reinterpret_cast<float*>(ws + L.v.gate_prefix);
   a.beta_chunk = reinterpret_cast<float*>(ws + L.v.beta_chunk);
   a.tinv = ws + L.v.tinv;
+  a.w = ws + L.v.w;
   a.key_t = ws + L.v.key_t;
   a.qk = ws + L.v.qk;
   a.num_seqs = d.num_seqs;

@@ -24,7 +24,8 @@ struct PrefillArgs {
   int32_t* seq_chunk_offset;  // [N+1]
   float* gate_prefix;       // [NC][HV][C]  in-chunk inclusive prefix of log a
   float* beta_chunk;        // [NC][HV][C]  b per chunk row (0 past the chunk end)
-  void* tinv;               // [NC][HV] fragments of (I + A)^{-1}
+  void* tinv;               // [NC][HV] fragments of (I + A)^{-1} diag(b)
+  void* w;                  // [NC][HV] fragments of W = (I + A)^{-1} diag(b exp(g)) K
   void* key_t;              // [NC][HQ] fragments of K^T
   void* qk;                 // [NC][HQ] fragments of (q_r . k_j)
   int64_t num_seqs;         // N
@@ -49,7 +50,8 @@ struct DecodeArgs {
   int32_t group;
 };
 
-// Prefill launch stages (1-based): 1 gate prefix, 2 (I + A)^{-1}, 3 fused scan.
+// Prefill launch stages (1-based): 1 chunk preparation (table, gate prefix sums,
+// K^T and q.k), 2 (I + A)^{-1} and W, 3 fused scan.
 constexpr int kPrefillStages = 3;
 
 // True when the fused scan kernel has an instance for (dtype, head_dim, chunk).

@@ -9,7 +9,7 @@
 //   g_r    = sum_{j<=r} log a_j                          kernel 1
 //   A[r,i] = b_r (k_r . k_i) exp(g_r - g_i)  (i < r)     kernel 2
 //   Tinv   = (I + A)^{-1}                                kernel 2
-//   W      = Tinv diag(b exp(g)) K                       kernel 3 (producer waves)
+//   W      = Tinv diag(b exp(g)) K                       kernel 2
 //   Ut     = Tinv diag(b) V                              kernel 3 (producer waves)
 //   U      = Ut - W S0                                   kernel 3 (scan waves)
 //   S_end  = exp(g_L) S0 + (exp(g_L - g) * K)^T U        kernel 3 (scan waves)
@@ -22,16 +22,19 @@
 // scan splits a head's state into 16-column slices. exp() is only ever taken
 // of g_r - g_i with i <= r, a non-positive number.
 //
-// Kernel 3 fuses the W/Ut construction, the inter-chunk state scan and the
-// output products: W, Ut, U and the per-chunk states never leave the chip.
+// Kernel 1 also lays out K^T and the q.k products once per QK head, which
+// every V head of the group reads. Kernel 3 fuses the Ut construction, the
+// inter-chunk state scan and the output products: Ut, U and the per-chunk
+// states never leave the chip.
 //
 // Fragment layouts (see gdn_device.h for the lane/element order): a
 // "fragment" is 64 lanes x 8 elements; "frag (a, s)" of a matrix X means
 // lane l holds row/col a*16 + l%16 and the 8 contraction indices of step s.
 //   key_t [c][hq][D/16][C32] : frag (dt, s) of K^T   (row d,     k = token i)
-//   tinv  [c][hv][C/16][C32] : frag (rt, s) of Tinv  (row r,     k = token i)
+//   tinv  [c][hv][C/16][C32] : frag (rt, s) of Tinv diag(b) (row r, k = token i)
+//   w     [c][hv][C/16][D32] : frag (rt, s) of W     (row r,     k = d)
 //   qk    [c][hq][C/16][C32] : frag (nt, s) of (q_r . k_j) (col r = query, k = key j)
-// with C32 = ceil(C/32); entries past the chunk end are zero.
+// with C32 = ceil(C/32), D32 = ceil(D/32); entries past the chunk end are zero.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -80,21 +83,42 @@ __device__ __forceinline__ int frag_k(int s, int quad, int e) {
 __device__ __forceinline__ constexpr bool causal_zero(int nt, int s) { return 32 * s > 16 * nt + 15; }
 
 // --------------------------------------------------------------------------
-// Kernel 1: chunk table, in-chunk prefix sums of log a and per-chunk b.
-// One workgroup per compact chunk slot c in [0, floor(T/C) + N). Each group
-// scans the per-sequence chunk counts ceil(L_n / C) to find which sequence
-// owns slot c (slots past the last chunk are marked seq = -1); group 0 also
-// publishes the per-sequence first-chunk offsets. Then one thread per V head
-// writes g[c][h][r] and b[c][h][r] for r < C; past a partial chunk's end g
-// repeats the last valid prefix (log a taken as 0) and b is 0.
+// Kernel 1: per (chunk slot c, QK head hq): the chunk table, the in-chunk
+// prefix sums of log a and the per-chunk b of the QK head's V heads, and the
+// chunk's K^T and q.k fragments (both shared by the QK head's V heads).
+// Every group scans the per-sequence chunk counts ceil(L_n / C) to find
+// which sequence owns slot c (slots past the last chunk are marked
+// seq = -1); the groups of QK head 0 publish the table entry, and slot 0's
+// the per-sequence first-chunk offsets. One wave per V head forms g with a
+// wavefront prefix sum; past a partial chunk's end g repeats the last valid
+// prefix (log a taken as 0) and b is 0. The q.k fragment (nt, s) is the pair
+// of accumulator tiles K_j Q_r^T of key tiles 2s and 2s + 1 (a tile after
+// the query tile nt stays zero): two vertically adjacent accumulator tiles
+// are a fragment as they stand.
 // --------------------------------------------------------------------------
-template <int C>
-__global__ __launch_bounds__(kBlock) void gdn_k1_gate_prefix(const PrefillArgs a) {
-  __shared__ int s_scan[kBlock];
-  __shared__ int s_hit[2];
-  const int tid = threadIdx.x;
+template <typename E, int D, int C>
+struct PrepSmem {
+  static constexpr int KLD = D + 8;    // row stride of the staged keys and queries
+  E ks[C * KLD];
+  E qs[C * KLD];
+  int scan[kBlock];
+  int hit[2];
+};
+
+template <typename E, int D, int C>
+__global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a) {
+  using G = Cfg<E, D, C>;
+  using SM = PrepSmem<E, D, C>;
+  constexpr int CT = G::CT, CKS = G::CKS, DKS = G::DKS, KLD = SM::KLD;
+  constexpr int NW = kBlock / 64;
+  constexpr int VE = 16 / (int)sizeof(E);                 // elements per 16-byte load
+  typedef E VLoad __attribute__((ext_vector_type(VE)));
+  __shared__ SM sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, l16 = lane & 15;
   const int64_t c = blockIdx.x;
-  if (tid == 0) { s_hit[0] = -1; s_hit[1] = 0; }
+  const int hq = blockIdx.y;
+  const bool publish = hq == 0;
+  if (tid == 0) { sm.hit[0] = -1; sm.hit[1] = 0; }
   __syncthreads();
   int carry = 0;
   for (int64_t base = 0; base < a.num_seqs; base += kBlock) {
@@ -105,118 +129,58 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_gate_prefix(const PrefillArgs a
       const int s1 = a.cu_seqlens ? a.cu_seqlens[n + 1] : (int)a.total_tokens;
       cnt = (s1 - s0 + C - 1) / C;
     }
-    s_scan[tid] = cnt;
+    sm.scan[tid] = cnt;
     __syncthreads();
     for (int off = 1; off < kBlock; off <<= 1) {
-      const int x = (tid >= off) ? s_scan[tid - off] : 0;
+      const int x = (tid >= off) ? sm.scan[tid - off] : 0;
       __syncthreads();
-      s_scan[tid] += x;
+      sm.scan[tid] += x;
       __syncthreads();
     }
-    const int incl = carry + s_scan[tid];
+    const int incl = carry + sm.scan[tid];
     const int excl = incl - cnt;
     if (n < a.num_seqs) {
-      if (c >= excl && c < incl) { s_hit[0] = (int)n; s_hit[1] = (int)(c - excl); }
-      if (c == 0) a.seq_chunk_offset[n] = excl;
+      if (c >= excl && c < incl) { sm.hit[0] = (int)n; sm.hit[1] = (int)(c - excl); }
+      if (c == 0 && publish) a.seq_chunk_offset[n] = excl;
     }
-    carry += s_scan[kBlock - 1];
+    carry += sm.scan[kBlock - 1];
     __syncthreads();
   }
-  if (c == 0 && tid == 0) a.seq_chunk_offset[a.num_seqs] = carry;
-  const int n = s_hit[0];
+  if (c == 0 && publish && tid == 0) a.seq_chunk_offset[a.num_seqs] = carry;
+  const int n = sm.hit[0];
   int4* table = reinterpret_cast<int4*>(a.chunk_table);
   if (n < 0) {
-    if (tid == 0) table[c] = make_int4(-1, 0, 0, 0);
+    if (publish && tid == 0) table[c] = make_int4(-1, 0, 0, 0);
     return;
   }
-  const int j = s_hit[1];
+  const int j = sm.hit[1];
   const int s0 = a.cu_seqlens ? a.cu_seqlens[n] : 0;
   const int s1 = a.cu_seqlens ? a.cu_seqlens[n + 1] : (int)a.total_tokens;
   const int start = s0 + j * C;
   const int len = min(C, s1 - start);
-  if (tid == 0) table[c] = make_int4(n, start, len, j);
-  for (int h = tid; h < a.h_v; h += kBlock) {
-    float acc = 0.f;
-    float* gout = a.gate_prefix + (c * a.h_v + h) * C;
-    float* bout = a.beta_chunk + (c * a.h_v + h) * C;
-    for (int r = 0; r < C; ++r) {
-      float b = 0.f;
-      if (r < len) {
-        acc += a.log_alpha[(int64_t)(start + r) * a.h_v + h];
-        b = a.beta[(int64_t)(start + r) * a.h_v + h];
-      }
-      gout[r] = acc;
-      bout[r] = b;
+  if (publish && tid == 0) table[c] = make_int4(n, start, len, j);
+
+  // gates: one wave per V head of the group, lane r holding token r
+  for (int h = wave; h < a.group; h += NW) {
+    const int hv = hq * a.group + h;
+    float g = 0.f, b = 0.f;
+    if (lane < len) {
+      g = a.log_alpha[(int64_t)(start + lane) * a.h_v + hv];
+      b = a.beta[(int64_t)(start + lane) * a.h_v + hv];
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float x = __shfl_up(g, off);
+      if (lane >= off) g += x;
+    }
+    if (lane < C) {
+      a.gate_prefix[(c * a.h_v + hv) * C + lane] = g;
+      a.beta_chunk[(c * a.h_v + hv) * C + lane] = b;
     }
   }
-}
 
-// --------------------------------------------------------------------------
-// Kernel 2: per (chunk, V head): A = strict_lower(b_r (k_r . k_i)
-// exp(g_r - g_i)), Tinv = (I + A)^{-1}, written as the fragments of
-// Tinv diag(b) and Tinv diag(b exp(g)) (the right factors of Ut and W).
-// The first V head of each QK group also writes the chunk's K^T and q.k
-// fragments, which the QK group's V heads share.
-// K K^T (and Q K^T) are formed with MFMA. Tinv is assembled blockwise in
-// fp32 over the four waves: the 16 x 16 diagonal blocks by forward
-// substitution (one lane per column), then the blocks below them in order
-// of distance from the diagonal,
-//   Tinv_ij = -Tinv_ii sum_{j<=m<i} A_im Tinv_mj,
-// with fp32 16x16x4 MFMAs, one block per wave per distance.
-// --------------------------------------------------------------------------
-
-// acc += X Y for 16 x 16 fp32 tiles in LDS (row-major, leading dims lx, ly)
-__device__ __forceinline__ f32x4 mma16_f32(const float* X, int lx, const float* Y, int ly, f32x4 acc,
-                                           int lane) {
-  const int m = lane & 15, k = lane >> 4;
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[m * lx + 4 * kk + k], Y[(4 * kk + k) * ly + m], acc, 0, 0, 0);
-  return acc;
-}
-
-template <typename E, int D, int C>
-struct InvSmem {
-  static constexpr int KLD = D + 8;    // bf16/fp32 row stride of the staged keys and queries
-  static constexpr int FLD = C + 4;    // fp32 row stride of C x C tiles (spreads rows over banks)
-  static constexpr int XLD = 20;       // row stride of the 16 x 16 scratch tiles
-  union {
-    struct {
-      E ks[C * KLD];                   // keys of the chunk, rows past its end zero
-      E qs[C * KLD];                   // queries of the chunk
-    } in;
-    struct {
-      float t[C * FLD];                // Tinv being assembled
-      float x[4][16 * XLD];            // one 16 x 16 scratch tile per wave
-    } out;
-  } u;
-  float kk[C * FLD];                   // K K^T (lower tiles), later q.k staging
-  float a[C * FLD];                    // A (below the diagonal)
-  float gb[2][C];                      // g and b of this V head
-};
-
-template <typename E, int D, int C>
-__global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a) {
-  using G = Cfg<E, D, C>;
-  using SM = InvSmem<E, D, C>;
-  constexpr int CT = G::CT, CKS = G::CKS, DKS = G::DKS, KLD = SM::KLD, FLD = SM::FLD, XLD = SM::XLD;
-  constexpr int NW = kBlock / 64;
-  constexpr int VE = 16 / (int)sizeof(E);                 // elements per 16-byte load
-  typedef E VLoad __attribute__((ext_vector_type(VE)));
-  __shared__ SM sm;
-  // the V heads of one (chunk, QK head), which read the same keys, are
-  // consecutive logical ids and so share an XCD
-  const int64_t lid = xcd_local_id(blockIdx.x, gridDim.x);
-  const int c = (int)(lid / a.h_v), hv = (int)(lid % a.h_v);
-  const int4 tab = reinterpret_cast<const int4*>(a.chunk_table)[c];
-  if (tab.x < 0) return;
-  const int start = tab.y, len = tab.z;
-  const int hq = hv / a.group;
-  const bool lead = (hv % a.group) == 0;          // writes the QK head's shared fragments
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, l16 = lane & 15;
   const E* kg = static_cast<const E*>(a.k);
   const E* qg = static_cast<const E*>(a.q);
-
   for (int idx = tid; idx < C * D / VE; idx += kBlock) {
     const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
     VLoad kv, qv;
@@ -225,112 +189,190 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a
     if (r < len) {
       const int64_t gi = ((int64_t)(start + r) * a.h_qk + hq) * D + d;
       kv = *reinterpret_cast<const VLoad*>(kg + gi);
-      if (lead) qv = *reinterpret_cast<const VLoad*>(qg + gi);
+      qv = *reinterpret_cast<const VLoad*>(qg + gi);
     }
-    *reinterpret_cast<VLoad*>(&sm.u.in.ks[r * KLD + d]) = kv;
-    if (lead) *reinterpret_cast<VLoad*>(&sm.u.in.qs[r * KLD + d]) = qv;
+    *reinterpret_cast<VLoad*>(&sm.ks[r * KLD + d]) = kv;
+    *reinterpret_cast<VLoad*>(&sm.qs[r * KLD + d]) = qv;
+  }
+  __syncthreads();
+
+  // K^T fragments: frag (dt, s), lane row d, elements token i
+  Frag<E>* ktg = reinterpret_cast<Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
+  for (int it = tid; it < G::KT_FR * 64; it += kBlock) {
+    const int f = it / 64, ln = it % 64, dt = f / CKS, s = f % CKS, q4 = ln >> 4;
+    const int d = 16 * dt + (ln & 15);
+    Frag<E> v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = frag_k(s, q4, e);
+      v[e] = (i < C) ? sm.ks[i * KLD + d] : to_e<E>(0.f);
+    }
+    ktg[it] = v;
+  }
+  // q.k fragments: frag (nt, s), lane col = query r, elements key j
+  Frag<E>* qkg = reinterpret_cast<Frag<E>*>(a.qk) + (c * a.h_qk + hq) * G::QK_FR * 64;
+  for (int f = wave; f < G::QK_FR; f += NW) {
+    const int nt = f / CKS, s = f % CKS;
+    f32x4 t2[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kt = 2 * s + h;
+      if (kt > nt || kt >= CT) continue;
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks)
+        t2[h] = mma(load_frag<E>(&sm.ks[(16 * kt + l16) * KLD + 32 * ks], quad, D - 32 * ks),
+                    load_frag<E>(&sm.qs[(16 * nt + l16) * KLD + 32 * ks], quad, D - 32 * ks), t2[h]);
+    }
+    qkg[f * 64 + lane] = acc_to_frag<E>(t2[0], t2[1]);
+  }
+}
+
+// --------------------------------------------------------------------------
+// Kernel 2: per (chunk, V head): A = strict_lower(b_r (k_r . k_i)
+// exp(g_r - g_i)), Tinv = (I + A)^{-1}, and the two operands the scan takes
+// from it: the fragments of Tinv diag(b) (the right factor of Ut) and of
+// W = Tinv diag(b exp(g)) K.
+// K K^T is formed with MFMA from the staged keys; A's entries are made in
+// the products' epilogue. A and Tinv share one C x C fp32 array in LDS (over
+// the keys, which are dead by then): A's blocks below the diagonal stay in
+// place, Tinv's diagonal blocks replace A's, and Tinv's blocks below the
+// diagonal are stored transposed in the blocks above it, so that
+// Tinv[r][i] sits at [i][r] when r's block is below i's. Tinv is assembled
+// blockwise in fp32: the 16 x 16 diagonal blocks by forward substitution
+// (one lane per column, the four blocks side by side in one wave), then the
+// blocks below them in order of distance from the diagonal,
+//   Tinv_ij = -Tinv_ii sum_{j<=m<i} A_im Tinv_mj,
+// with fp32 16x16x4 MFMAs, one block per wave per distance. W^T = K^T
+// (Tinv diag(b exp(g)))^T is contracted over tokens, wave w taking d-tiles
+// 2w and 2w + 1, whose accumulator pairs are W's fragments (rt, w).
+// --------------------------------------------------------------------------
+
+// acc += X Y for 16 x 16 fp32 tiles in LDS; X(m, k) = X[m xr + k xc] and
+// Y(k, m) = Y[k yr + m yc] (strides give either storage order)
+__device__ __forceinline__ f32x4 mma16_f32(const float* X, int xr, int xc, const float* Y, int yr, int yc,
+                                           f32x4 acc, int lane) {
+  const int m = lane & 15, k = lane >> 4;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[m * xr + (4 * kk + k) * xc], Y[(4 * kk + k) * yr + m * yc], acc,
+                                               0, 0, 0);
+  return acc;
+}
+
+template <typename E, int D, int C>
+struct InvSmem {
+  using G = Cfg<E, D, C>;
+  static constexpr int KLD = D + 8;    // row stride of the staged keys
+  static constexpr int FLD = C + 4;    // fp32 row stride of the C x C array (spreads rows over banks)
+  static constexpr int XLD = 20;       // row stride of the 16 x 16 scratch tiles
+  union {
+    E ks[C * KLD];                     // keys of the chunk, rows past its end zero
+    float at[C * FLD];                 // A and Tinv (see above)
+  } u;
+  float x[4][16 * XLD];                // one 16 x 16 scratch tile per wave
+  Frag<E> tbg[G::T_FR * 64];           // Tinv diag(b exp(g)) fragments
+  float gb[2][C];                      // g and b of this V head
+};
+
+template <typename E, int D, int C>
+__global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) {
+  using G = Cfg<E, D, C>;
+  using SM = InvSmem<E, D, C>;
+  constexpr int CT = G::CT, CKS = G::CKS, DT = G::DT, DKS = G::DKS, KLD = SM::KLD, FLD = SM::FLD, XLD = SM::XLD;
+  constexpr int NW = kBlock / 64;
+  static_assert(DKS <= NW && CT <= 4, "one W d-step pair per wave, diagonal blocks in one wave");
+  constexpr int VE = 16 / (int)sizeof(E);                 // elements per 16-byte load
+  typedef E VLoad __attribute__((ext_vector_type(VE)));
+  __shared__ SM sm;
+  // the V heads of one (chunk, QK head), which read the same keys, are
+  // consecutive logical ids and so share an XCD
+  const int64_t lid = xcd_local_id(blockIdx.x, gridDim.x);
+  const int64_t c = lid / a.h_v;
+  const int hv = (int)(lid % a.h_v);
+  const int4 tab = reinterpret_cast<const int4*>(a.chunk_table)[c];
+  if (tab.x < 0) return;
+  const int start = tab.y, len = tab.z;
+  const int hq = hv / a.group;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, l16 = lane & 15;
+  float* at = sm.u.at;
+
+  // K^T fragments of this wave's W d-tiles, from kernel 1; issued first so
+  // that they arrive during the inverse
+  const int ksd = wave;
+  Frag<E> kta[CKS], ktb[CKS];
+  if (ksd < DKS) {
+    const Frag<E>* ktg = reinterpret_cast<const Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
+#pragma unroll
+    for (int s = 0; s < CKS; ++s) {
+      kta[s] = ktg[((2 * ksd) * CKS + s) * 64 + lane];
+      if (2 * ksd + 1 < DT) ktb[s] = ktg[((2 * ksd + 1) * CKS + s) * 64 + lane];
+    }
+  }
+  const E* kg = static_cast<const E*>(a.k);
+  for (int idx = tid; idx < C * D / VE; idx += kBlock) {
+    const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
+    VLoad kv;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) kv[e] = to_e<E>(0.f);
+    if (r < len) kv = *reinterpret_cast<const VLoad*>(kg + ((int64_t)(start + r) * a.h_qk + hq) * D + d);
+    *reinterpret_cast<VLoad*>(&sm.u.ks[r * KLD + d]) = kv;
   }
   if (tid < 2 * C) {
-    const int64_t o = ((int64_t)c * a.h_v + hv) * C + (tid % C);
+    const int64_t o = (c * a.h_v + hv) * C + (tid % C);
     sm.gb[tid / C][tid % C] = (tid < C) ? a.gate_prefix[o] : a.beta_chunk[o];
   }
   __syncthreads();
 
-  if (lead) {
-    // K^T fragments: frag (dt, s), lane row d, elements token i.
-    Frag<E>* ktg = reinterpret_cast<Frag<E>*>(a.key_t) + ((int64_t)c * a.h_qk + hq) * G::KT_FR * 64;
-    for (int it = tid; it < G::KT_FR * 64; it += kBlock) {
-      const int f = it / 64, ln = it % 64, dt = f / CKS, s = f % CKS, q4 = ln >> 4;
-      const int d = 16 * dt + (ln & 15);
-      Frag<E> v;
+  // K K^T tiles on and below the diagonal, lower tile t -> (mi, ni)
+  constexpr int NTILE = CT * (CT + 1) / 2, TPW = (NTILE + NW - 1) / NW;
+  f32x4 kk[TPW];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = frag_k(s, q4, e);
-        v[e] = (i < C) ? sm.u.in.ks[i * KLD + d] : to_e<E>(0.f);
-      }
-      ktg[it] = v;
-    }
-  }
-
-  // K K^T lower tiles: CT (CT + 1) / 2 tiles over the waves
-  for (int t = wave; t < CT * CT; t += NW) {
-    const int mi = t / CT, ni = t % CT;
-    if (ni > mi) continue;
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int ks = 0; ks < DKS; ++ks)
-      acc = mma(load_frag<E>(&sm.u.in.ks[(16 * mi + l16) * KLD + 32 * ks], quad, D - 32 * ks),
-                load_frag<E>(&sm.u.in.ks[(16 * ni + l16) * KLD + 32 * ks], quad, D - 32 * ks), acc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm.kk[(16 * mi + 4 * quad + i) * FLD + 16 * ni + l16] = acc[i];
-  }
-  __syncthreads();
-  // A below the diagonal (the inverse never reads the rest)
-  for (int idx = tid; idx < C * C; idx += kBlock) {
-    const int r = idx / C, i = idx % C;
-    if (i < r)
-      sm.a[r * FLD + i] = sm.gb[1][r] * sm.kk[r * FLD + i] * __expf(fminf(sm.gb[0][r] - sm.gb[0][i], 0.f));
-  }
-  if (lead) {
-    // q.k tiles with key tile <= query tile, staged [query r][key j] in kk
-    // (K K^T is consumed by now; a barrier separates the two)
-  }
-  __syncthreads();
-  if (lead) {
-    for (int t = wave; t < CT * CT; t += NW) {
-      const int kt = t / CT, nt = t % CT;     // key tile, query tile
-      if (kt > nt) continue;
-      f32x4 acc = zero4();
+  for (int u = 0; u < TPW; ++u) {
+    const int t = wave + u * NW;
+    kk[u] = zero4();
+    if (t < NTILE) {
+      int mi = 0;
+      while ((mi + 1) * (mi + 2) / 2 <= t) ++mi;
+      const int ni = t - mi * (mi + 1) / 2;
 #pragma unroll
       for (int ks = 0; ks < DKS; ++ks)
-        acc = mma(load_frag<E>(&sm.u.in.ks[(16 * kt + l16) * KLD + 32 * ks], quad, D - 32 * ks),
-                  load_frag<E>(&sm.u.in.qs[(16 * nt + l16) * KLD + 32 * ks], quad, D - 32 * ks), acc);
+        kk[u] = mma(load_frag<E>(&sm.u.ks[(16 * mi + l16) * KLD + 32 * ks], quad, D - 32 * ks),
+                    load_frag<E>(&sm.u.ks[(16 * ni + l16) * KLD + 32 * ks], quad, D - 32 * ks), kk[u]);
+    }
+  }
+  __syncthreads();     // the keys are dead from here on; their LDS holds A and Tinv
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.kk[(16 * nt + l16) * FLD + 16 * kt + 4 * quad + i] = acc[i];
+  for (int u = 0; u < TPW; ++u) {
+    const int t = wave + u * NW;
+    if (t >= NTILE) continue;
+    int mi = 0;
+    while ((mi + 1) * (mi + 2) / 2 <= t) ++mi;
+    const int ni = t - mi * (mi + 1) / 2;
+    const int i = 16 * ni + l16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * mi + 4 * quad + e;
+      if (i < r) at[r * FLD + i] = sm.gb[1][r] * kk[u][e] * __expf(fminf(sm.gb[0][r] - sm.gb[0][i], 0.f));
     }
   }
   __syncthreads();
-  if (lead) {
-    // q.k fragments: frag (nt, s), lane col = query r, elements key j.
-    Frag<E>* qkg = reinterpret_cast<Frag<E>*>(a.qk) + ((int64_t)c * a.h_qk + hq) * G::QK_FR * 64;
-    for (int it = tid; it < G::QK_FR * 64; it += kBlock) {
-      const int f = it / 64, ln = it % 64, nt = f / CKS, s = f % CKS, q4 = ln >> 4;
-      const int r = 16 * nt + (ln & 15);
-      Frag<E> v;
+  // diagonal blocks: lanes 16b .. 16b + 15 of wave 0 solve block b, lane
+  // 16b + j its column j; the block then holds Tinv's diagonal block
+  if (wave == 0 && quad < CT) {
+    const int j = l16, o = 16 * quad;
+    float x[16];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = frag_k(s, q4, e);
-        v[e] = (j < C && (j >> 4) <= nt) ? to_e<E>(sm.kk[r * FLD + j]) : to_e<E>(0.f);
+    for (int r = 0; r < 16; ++r) {
+      float s0 = (r == j) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < r; ++i) {
+        if (i & 1) s1 -= at[(o + r) * FLD + o + i] * x[i];
+        else s0 -= at[(o + r) * FLD + o + i] * x[i];
       }
-      qkg[it] = v;
+      x[r] = s0 + s1;
     }
-  }
-  __syncthreads();     // staged keys and queries are dead from here on; out.t reuses them
-
-  float* Tm = sm.u.out.t;
-  // blocks above the diagonal are zero
-  for (int idx = tid; idx < C * C; idx += kBlock) {
-    const int r = idx / C, i = idx % C;
-    if ((i >> 4) > (r >> 4)) Tm[r * FLD + i] = 0.f;
-  }
-  // diagonal blocks: wave b solves block b, lane j its column j
-  for (int b = wave; b < CT; b += NW) {
-    if (lane < 16) {
-      const int j = lane, o = 16 * b;
-      float x[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s0 = (r == j) ? 1.f : 0.f, s1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < r; ++i) {
-          if (i & 1) s1 -= sm.a[(o + r) * FLD + o + i] * x[i];
-          else s0 -= sm.a[(o + r) * FLD + o + i] * x[i];
-        }
-        x[r] = s0 + s1;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Tm[(o + r) * FLD + o + j] = x[r];
-    }
+    for (int r = 0; r < 16; ++r) at[(o + r) * FLD + o + j] = x[r];
   }
   __syncthreads();
   // blocks below the diagonal, by distance; one block per wave per distance
@@ -338,20 +380,23 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a
   for (int dist = 1; dist < CT; ++dist) {
     for (int bi = dist + wave; bi < CT; bi += NW) {
       const int bj = bi - dist;
-      float* X = sm.u.out.x[wave];
+      float* X = sm.x[wave];
       f32x4 acc = zero4();
-      for (int bm = bj; bm < bi; ++bm)
-        acc = mma16_f32(&sm.a[(16 * bi) * FLD + 16 * bm], FLD, &Tm[(16 * bm) * FLD + 16 * bj], FLD, acc, lane);
+      for (int bm = bj; bm < bi; ++bm) {
+        const float* Am = &at[(16 * bi) * FLD + 16 * bm];
+        acc = (bm == bj) ? mma16_f32(Am, FLD, 1, &at[(16 * bj) * FLD + 16 * bj], FLD, 1, acc, lane)
+                         : mma16_f32(Am, FLD, 1, &at[(16 * bj) * FLD + 16 * bm], 1, FLD, acc, lane);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) X[(4 * quad + i) * XLD + l16] = acc[i];
-      acc = mma16_f32(&Tm[(16 * bi) * FLD + 16 * bi], FLD, X, XLD, zero4(), lane);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Tm[(16 * bi + 4 * quad + i) * FLD + 16 * bj + l16] = -acc[i];
+      for (int e = 0; e < 4; ++e) X[(4 * quad + e) * XLD + l16] = acc[e];
+      acc = mma16_f32(&at[(16 * bi) * FLD + 16 * bi], FLD, 1, X, XLD, 1, zero4(), lane);
+      // Tinv_ij, stored transposed: element (4 quad + e, l16) at [16 bj + l16][16 bi + 4 quad + e]
+      *reinterpret_cast<f32x4*>(&at[(16 * bj + l16) * FLD + 16 * bi + 4 * quad]) = -acc;
     }
     __syncthreads();
   }
-  // Tinv diag(b) and Tinv diag(b exp(g)) fragments, written one after the other
-  Frag<E>* tg = reinterpret_cast<Frag<E>*>(a.tinv) + ((int64_t)c * a.h_v + hv) * 2 * G::T_FR * 64;
+  // Tinv diag(b) fragments to the workspace, Tinv diag(b exp(g)) to LDS
+  Frag<E>* tg = reinterpret_cast<Frag<E>*>(a.tinv) + (c * a.h_v + hv) * G::T_FR * 64;
   for (int it = tid; it < G::T_FR * 64; it += kBlock) {
     const int f = it / 64, ln = it % 64, rt = f / CKS, s = f % CKS, q4 = ln >> 4;
     const int r = 16 * rt + (ln & 15);
@@ -359,17 +404,37 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int i = frag_k(s, q4, e);
-      const float t = (i < C) ? Tm[r * FLD + i] * sm.gb[1][i] : 0.f;
+      float t = 0.f;
+      if (i < C) {
+        const float tri = ((r >> 4) > (i >> 4)) ? at[i * FLD + r] : (((r >> 4) == (i >> 4)) ? at[r * FLD + i] : 0.f);
+        t = tri * sm.gb[1][i];
+      }
       vb[e] = to_e<E>(t);
       vg[e] = to_e<E>((i < C) ? t * __expf(sm.gb[0][i]) : 0.f);
     }
     tg[it] = vb;
-    tg[G::T_FR * 64 + it] = vg;
+    sm.tbg[it] = vg;
+  }
+  __syncthreads();
+  if (ksd < DKS) {
+    Frag<E>* wg = reinterpret_cast<Frag<E>*>(a.w) + (c * a.h_v + hv) * G::W_FR * 64;
+#pragma unroll
+    for (int rt = 0; rt < CT; ++rt) {
+      f32x4 acc0 = zero4(), acc1 = zero4();
+#pragma unroll
+      for (int s = 0; s < CKS; ++s) {
+        if (causal_zero(rt, s)) continue;              // Tinv is lower triangular
+        const Frag<E> tb = sm.tbg[(rt * CKS + s) * 64 + lane];
+        acc0 = mma(kta[s], tb, acc0);
+        if (2 * ksd + 1 < DT) acc1 = mma(ktb[s], tb, acc1);
+      }
+      wg[(rt * DKS + ksd) * 64 + lane] = acc_to_frag<E>(acc0, acc1);
+    }
   }
 }
 
 // --------------------------------------------------------------------------
-// Kernel 3: fused W/Ut construction, inter-chunk state scan and outputs.
+// Kernel 3: fused Ut construction, inter-chunk state scan and outputs.
 // One workgroup per (sequence, V head, block of BV state columns), eight
 // waves, looping over the sequence's chunks in order with a software
 // pipeline:
@@ -382,9 +447,9 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_akk_inverse(const PrefillArgs a
 //       O^T += U^T (Q K^T * Dincl)^T                (U's tiles are the A fragments)
 //       S    = exp(g_L) S + K^T (exp(g_L - g) * U)
 //     and store the chunk's outputs for their columns;
-//   producer waves build chunk c+1's W and Ut fragments and the masked,
-//     decayed (q.k) fragments in LDS, and double as loaders: they fetch
-//     chunk c+3's K^T, Tinv, q.k, g, b and V slice (and chunk c+2's Q) into
+//   producer waves build chunk c+1's Ut tiles and the masked, decayed
+//     (q.k) fragments in LDS, and double as loaders: they fetch chunk
+//     c+3's K^T, W, Tinv diag(b), q.k, g, b and V slice (and chunk c+2's Q) into
 //     one of two register sets while the other set, fetched one iteration
 //     earlier, is written into LDS for chunk c+2 between the barriers.
 // Every LDS region is either double-buffered by chunk parity or written only
@@ -397,7 +462,7 @@ struct ScanSmem {
   using G = Cfg<E, D, C>;
   Frag<E> kt[2][G::KT_FR * 64];        // K^T fragments, by chunk parity
   Frag<E> qf[G::Q_FR * 64];            // Q fragments of the chunk being scanned
-  Frag<E> tf[2][G::T_FR * 64];         // Tinv diag(b), Tinv diag(b exp(g)) of the chunk being produced
+  Frag<E> tf[G::T_FR * 64];            // Tinv diag(b) of the chunk being produced
   Frag<E> qk[G::QK_FR * 64];           // q.k fragments of the chunk being produced
   Frag<E> wf[2][G::W_FR * 64];         // W fragments, by chunk parity
   Frag<E> pf[2][G::QK_FR * 64];        // masked, decayed q.k fragments, by parity
@@ -412,16 +477,17 @@ struct ScanFetch {
   using G = Cfg<E, D, C>;
   static constexpr int NL = kScanBlock - 64 * G::NS;                 // loader threads
   static constexpr int FR16 = (int)sizeof(Frag<E>) / 16;             // 16-byte units per lane-fragment
-  static constexpr int N_KT = G::KT_FR * 64 * FR16, N_T = 2 * G::T_FR * 64 * FR16, N_QK = G::QK_FR * 64 * FR16;
+  static constexpr int N_KT = G::KT_FR * 64 * FR16, N_T = G::T_FR * 64 * FR16, N_QK = G::QK_FR * 64 * FR16;
+  static constexpr int N_W = G::W_FR * 64 * FR16;
   static constexpr int N_GB = 2 * C * 4 / 16;
   static constexpr int VU = 16 / (int)sizeof(E);                     // V elements per 16-byte unit
   static constexpr int N_V = C * G::BV / VU;
   static constexpr int N_Q = G::Q_FR * 64;                           // lane-fragments of Q
-  static constexpr int P_KT = (N_KT + NL - 1) / NL, P_T = (N_T + NL - 1) / NL;
+  static constexpr int P_KT = (N_KT + NL - 1) / NL, P_T = (N_T + NL - 1) / NL, P_W = (N_W + NL - 1) / NL;
   static constexpr int P_QK = (N_QK + NL - 1) / NL, P_V = (N_V + NL - 1) / NL;
   static constexpr int P_Q = (N_Q + NL - 1) / NL, P_GB = (N_GB + NL - 1) / NL;
   typedef E VUnit __attribute__((ext_vector_type(VU)));             // one 16-byte unit of V
-  u32x4 kt[P_KT], t[P_T], qk[P_QK], gb[P_GB];
+  u32x4 kt[P_KT], t[P_T], w[P_W], qk[P_QK], gb[P_GB];
   VUnit v[P_V];
   Frag<E> q[P_Q];
 };
@@ -464,15 +530,18 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     const int xc = min(x, c1 - 1);
     const u32x4* ktg = reinterpret_cast<const u32x4*>(
         reinterpret_cast<const Frag<E>*>(a.key_t) + ((int64_t)xc * a.h_qk + hq) * G::KT_FR * 64);
-    // both scaled Tinv fragment sets of chunk x are contiguous
     const u32x4* tg = reinterpret_cast<const u32x4*>(
-        reinterpret_cast<const Frag<E>*>(a.tinv) + ((int64_t)xc * a.h_v + hv) * 2 * G::T_FR * 64);
+        reinterpret_cast<const Frag<E>*>(a.tinv) + ((int64_t)xc * a.h_v + hv) * G::T_FR * 64);
+    const u32x4* wg = reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const Frag<E>*>(a.w) + ((int64_t)xc * a.h_v + hv) * G::W_FR * 64);
     const u32x4* qkg = reinterpret_cast<const u32x4*>(
         reinterpret_cast<const Frag<E>*>(a.qk) + ((int64_t)xc * a.h_qk + hq) * G::QK_FR * 64);
 #pragma unroll
     for (int p = 0; p < F::P_KT; ++p) fr.kt[p] = ktg[min(lt + p * F::NL, F::N_KT - 1)];
 #pragma unroll
     for (int p = 0; p < F::P_T; ++p) fr.t[p] = tg[min(lt + p * F::NL, F::N_T - 1)];
+#pragma unroll
+    for (int p = 0; p < F::P_W; ++p) fr.w[p] = wg[min(lt + p * F::NL, F::N_W - 1)];
 #pragma unroll
     for (int p = 0; p < F::P_QK; ++p) fr.qk[p] = qkg[min(lt + p * F::NL, F::N_QK - 1)];
 #pragma unroll
@@ -505,12 +574,15 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   auto store = [&](const F& fr, int x, int xq) __attribute__((always_inline)) {
     if (x < c1) {
       u32x4* kt = reinterpret_cast<u32x4*>(sm.kt[x & 1]);
-      u32x4* tf = reinterpret_cast<u32x4*>(sm.tf[0]);
+      u32x4* tf = reinterpret_cast<u32x4*>(sm.tf);
+      u32x4* wf = reinterpret_cast<u32x4*>(sm.wf[x & 1]);
       u32x4* qk = reinterpret_cast<u32x4*>(sm.qk);
 #pragma unroll
       for (int p = 0; p < F::P_KT; ++p) { const int u = lt + p * F::NL; if (u < F::N_KT) kt[u] = fr.kt[p]; }
 #pragma unroll
       for (int p = 0; p < F::P_T; ++p) { const int u = lt + p * F::NL; if (u < F::N_T) tf[u] = fr.t[p]; }
+#pragma unroll
+      for (int p = 0; p < F::P_W; ++p) { const int u = lt + p * F::NL; if (u < F::N_W) wf[u] = fr.w[p]; }
 #pragma unroll
       for (int p = 0; p < F::P_QK; ++p) { const int u = lt + p * F::NL; if (u < F::N_QK) qk[u] = fr.qk[p]; }
 #pragma unroll
@@ -653,39 +725,11 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     const int par = p & 1;
     const int len = chunk_len(p);
     const float* gp = sm.gb[par][0];
-    constexpr int NITEM = DKS + NS + CT;
+    constexpr int NITEM = NS + CT;
     for (int item = pw; item < NITEM; item += NPROD) {
-      if (item < DKS) {
-        // W fragments (rt, ks_d) for every rt: the W^T tiles of d-tiles
-        // 2 ks_d and 2 ks_d + 1, from Tinv diag(b exp(g)) and K^T
-        const int ksd = item;
-        Frag<E> ka[CKS], kb[CKS];
-#pragma unroll
-        for (int s = 0; s < CKS; ++s) {
-          ka[s] = sm.kt[par][((2 * ksd) * CKS + s) * 64 + lane];
-          if (2 * ksd + 1 < DT) kb[s] = sm.kt[par][((2 * ksd + 1) * CKS + s) * 64 + lane];
-        }
-        f32x4 acc0[CT], acc1[CT];
-#pragma unroll
-        for (int rt = 0; rt < CT; ++rt) { acc0[rt] = zero4(); acc1[rt] = zero4(); }
-#pragma unroll
-        for (int s = 0; s < CKS; ++s) {
-          Frag<E> tb[CT];
-#pragma unroll
-          for (int rt = 0; rt < CT; ++rt)
-            if (!causal_zero(rt, s)) tb[rt] = sm.tf[1][(rt * CKS + s) * 64 + lane];
-#pragma unroll
-          for (int rt = 0; rt < CT; ++rt) {
-            if (causal_zero(rt, s)) continue;            // Tinv is lower triangular
-            acc0[rt] = mma(ka[s], tb[rt], acc0[rt]);
-            if (2 * ksd + 1 < DT) acc1[rt] = mma(kb[s], tb[rt], acc1[rt]);
-          }
-        }
-#pragma unroll
-        for (int rt = 0; rt < CT; ++rt) sm.wf[par][(rt * DKS + ksd) * 64 + lane] = acc_to_frag<E>(acc0[rt], acc1[rt]);
-      } else if (item < DKS + NS) {
+      if (item < NS) {
         // Ut accumulator tiles of slice sl: Tinv diag(b) V
-        const int sl = item - DKS;
+        const int sl = item;
         const E* vrow = &sm.vt[(16 * sl + l16) * G::VLD];
         Frag<E> vf[CKS];
 #pragma unroll
@@ -698,7 +742,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
           Frag<E> tb[CT];
 #pragma unroll
           for (int rt = 0; rt < CT; ++rt)
-            if (!causal_zero(rt, s)) tb[rt] = sm.tf[0][(rt * CKS + s) * 64 + lane];
+            if (!causal_zero(rt, s)) tb[rt] = sm.tf[(rt * CKS + s) * 64 + lane];
 #pragma unroll
           for (int rt = 0; rt < CT; ++rt)
             if (!causal_zero(rt, s)) acc[rt] = mma(tb[rt], vf[s], acc[rt]);
@@ -707,7 +751,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
         for (int rt = 0; rt < CT; ++rt) sm.uf[par][(sl * CT + rt) * 64 + lane] = acc[rt];
       } else {
         // masked, decayed q.k fragments of query tile nt
-        const int nt = item - DKS - NS;
+        const int nt = item - NS;
         const int r = 16 * nt + l16;
         const float gr = gp[r];
 #pragma unroll
@@ -801,8 +845,8 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
   const unsigned scan_groups = (unsigned)(a.num_seqs * a.h_v * G::NCB);
   for (int stage = first; stage <= last; ++stage) {
     switch (stage) {
-      case 1: gdn_k1_gate_prefix<C><<<dim3(nc), dim3(kBlock), 0, s>>>(a); break;
-      case 2: gdn_k2_akk_inverse<E, D, C><<<dim3(nc * (unsigned)a.h_v), dim3(kBlock), 0, s>>>(a); break;
+      case 1: gdn_k1_chunk_prep<E, D, C><<<dim3(nc, (unsigned)a.h_qk), dim3(kBlock), 0, s>>>(a); break;
+      case 2: gdn_k2_inverse_w<E, D, C><<<dim3(nc * (unsigned)a.h_v), dim3(kBlock), 0, s>>>(a); break;
       case 3: gdn_k3_scan<E, D, C><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a); break;
       default: return hipErrorInvalidValue;
     }

@@ -189,8 +189,10 @@ def test_stage_outputs_match_oracle_chunks(chunk):
     table = region(lay.chunk_table, nc * 4, torch.int32).view(nc, 4).numpy()
     g = region(lay.gate_prefix, nc * 6 * chunk, torch.float32).view(nc, 6, chunk).double().numpy()
     b = region(lay.beta_chunk, nc * 6 * chunk, torch.float32).view(nc, 6, chunk).double().numpy()
-    tf = region(lay.tinv, nc * 6 * 2 * ct * cks * 512, torch.bfloat16).view(
-        nc, 6, 2, ct, cks, 64, 8).double().numpy()
+    tf = region(lay.tinv, nc * 6 * ct * cks * 512, torch.bfloat16).view(
+        nc, 6, ct, cks, 64, 8).double().numpy()
+    wf = region(lay.w, nc * 6 * ct * 4 * 512, torch.bfloat16).view(
+        nc, 6, ct, 4, 64, 8).double().numpy()
     kt = region(lay.key_t, nc * 2 * 8 * cks * 512, torch.bfloat16).view(
         nc, 2, 8, cks, 64, 8).double().numpy()
     qk = region(lay.qk, nc * 2 * ct * cks * 512, torch.bfloat16).view(
@@ -205,13 +207,14 @@ def test_stage_outputs_match_oracle_chunks(chunk):
         check(g[c][:, :L], st["g"], torch.float32, f"g chunk {c}")
         assert (b[c][:, :L] == b64[t0:t0 + L].T).all() and (b[c][:, L:] == 0).all()
         for h in range(6):
-            # Tinv diag(b) and Tinv diag(b exp(g)) against the oracle's Tinv
-            bh, gam = b64[t0:t0 + L, h], np.exp(st["g"][h])
-            for which, scale in ((0, bh), (1, bh * gam)):
-                tm = unfrag(tf[c, h, which], chunk, chunk)
-                check(tm[:L, :L], st["T"][h] * scale[None, :], torch.bfloat16,
-                      f"Tinv scaled {which} chunk {c} head {h}")
-                assert np.allclose(tm[L:, :], 0) and np.allclose(tm[:, L:], 0)
+            # Tinv diag(b) against the oracle's Tinv, W against the oracle's W
+            bh = b64[t0:t0 + L, h]
+            tm = unfrag(tf[c, h], chunk, chunk)
+            check(tm[:L, :L], st["T"][h] * bh[None, :], torch.bfloat16, f"Tinv diag(b) chunk {c} head {h}")
+            assert np.allclose(tm[L:, :], 0) and np.allclose(tm[:, L:], 0)
+            wm = unfrag(wf[c, h], chunk, 128)              # [token r][d]
+            check(wm[:L], st["W"][h], torch.bfloat16, f"W chunk {c} head {h}")
+            assert (wm[L:] == 0).all()
         for hq in range(2):
             ktm = unfrag(kt[c, hq], 128, chunk)            # [d][i]
             assert np.array_equal(ktm[:, :L], k64[t0:t0 + L, hq].T) and (ktm[:, L:] == 0).all()

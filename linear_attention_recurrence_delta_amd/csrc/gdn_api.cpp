@@ -90,6 +90,7 @@ Layout compute_layout(const gdn_dims_t& d) {
   L.v.w = take(NC * HV * CT * ((DT + 1) / 2) * 512 * esz);
   L.v.key_t = take(NC * HQ * DT * CKS * 512 * esz);
   L.v.qk = take(NC * HQ * CT * CKS * 512 * esz);
+  L.v.q_frag = take(NC * HQ * CT * ((DT + 1) / 2) * 512 * esz);
   L.v.total = off;
   return L;
 }
@@ -191,6 +192,7 @@ gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims, const void* q, const v
   a.w = ws + L.v.w;
   a.key_t = ws + L.v.key_t;
   a.qk = ws + L.v.qk;
+  a.q_frag = ws + L.v.q_frag;
   a.num_seqs = d.num_seqs;
   a.total_tokens = d.total_tokens;
   a.max_chunks = L.v.max_chunks;

@@ -28,6 +28,7 @@ struct PrefillArgs {
   void* w;                  // [NC][HV] fragments of W = (I + A)^{-1} diag(b exp(g)) K
   void* key_t;              // [NC][HQ] fragments of K^T
   void* qk;                 // [NC][HQ] fragments of (q_r . k_j)
+  void* q_frag;             // [NC][HQ] fragments of Q
   int64_t num_seqs;         // N
   int64_t total_tokens;     // T
   int64_t max_chunks;       // NC = floor(T/C) + N

@@ -34,6 +34,7 @@
 //   tinv  [c][hv][C/16][C32] : frag (rt, s) of Tinv diag(b) (row r, k = token i)
 //   w     [c][hv][C/16][D32] : frag (rt, s) of W     (row r,     k = d)
 //   qk    [c][hq][C/16][C32] : frag (nt, s) of (q_r . k_j) (col r = query, k = key j)
+//   q_frag[c][hq][C/16][D32] : frag (nt, s) of Q     (row r,     k = d)
 // with C32 = ceil(C/32), D32 = ceil(D/32); entries past the chunk end are zero.
 #include <type_traits>
 
@@ -85,7 +86,7 @@ __device__ __forceinline__ constexpr bool causal_zero(int nt, int s) { return 32
 // --------------------------------------------------------------------------
 // Kernel 1: per (chunk slot c, QK head hq): the chunk table, the in-chunk
 // prefix sums of log a and the per-chunk b of the QK head's V heads, and the
-// chunk's K^T and q.k fragments (both shared by the QK head's V heads).
+// chunk's K^T, Q and q.k fragments (shared by the QK head's V heads).
 // Every group scans the per-sequence chunk counts ceil(L_n / C) to find
 // which sequence owns slot c (slots past the last chunk are marked
 // seq = -1); the groups of QK head 0 publish the table entry, and slot 0's
@@ -208,6 +209,12 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
       v[e] = (i < C) ? sm.ks[i * KLD + d] : to_e<E>(0.f);
     }
     ktg[it] = v;
+  }
+  // Q fragments: frag (nt, s), lane row r, elements d
+  Frag<E>* qfg = reinterpret_cast<Frag<E>*>(a.q_frag) + (c * a.h_qk + hq) * G::Q_FR * 64;
+  for (int it = tid; it < G::Q_FR * 64; it += kBlock) {
+    const int f = it / 64, ln = it % 64, nt = f / DKS, s = f % DKS;
+    qfg[it] = load_frag<E>(&sm.qs[(16 * nt + (ln & 15)) * KLD + 32 * s], ln >> 4, D - 32 * s);
   }
   // q.k fragments: frag (nt, s), lane col = query r, elements key j
   Frag<E>* qkg = reinterpret_cast<Frag<E>*>(a.qk) + (c * a.h_qk + hq) * G::QK_FR * 64;
@@ -469,6 +476,10 @@ struct ScanSmem {
   f32x4 uf[2][G::NS * G::CT * 64];     // Ut accumulator tiles, by parity
   E vt[G::BV * G::VLD];                // V slice of the chunk being produced, transposed
   float gb[2][2][C];                   // g and b, by chunk parity
+  // per chunk, by parity: exp(g_r) and exp(min(g_L - g_r, 0)), both zero
+  // past the chunk end, and exp(g_L)
+  float dtab[2][2][C] __attribute__((aligned(16)));
+  float gam[2];
 };
 
 // One register set of loader data: a chunk's operands plus the next chunk's Q.
@@ -482,14 +493,14 @@ struct ScanFetch {
   static constexpr int N_GB = 2 * C * 4 / 16;
   static constexpr int VU = 16 / (int)sizeof(E);                     // V elements per 16-byte unit
   static constexpr int N_V = C * G::BV / VU;
-  static constexpr int N_Q = G::Q_FR * 64;                           // lane-fragments of Q
+  static constexpr int N_Q = G::Q_FR * 64 * FR16;                    // 16-byte units of Q fragments
   static constexpr int P_KT = (N_KT + NL - 1) / NL, P_T = (N_T + NL - 1) / NL, P_W = (N_W + NL - 1) / NL;
   static constexpr int P_QK = (N_QK + NL - 1) / NL, P_V = (N_V + NL - 1) / NL;
   static constexpr int P_Q = (N_Q + NL - 1) / NL, P_GB = (N_GB + NL - 1) / NL;
   typedef E VUnit __attribute__((ext_vector_type(VU)));             // one 16-byte unit of V
   u32x4 kt[P_KT], t[P_T], w[P_W], qk[P_QK], gb[P_GB];
   VUnit v[P_V];
-  Frag<E> q[P_Q];
+  u32x4 q[P_Q];
 };
 
 template <typename E, int D, int C>
@@ -560,15 +571,10 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
           vg + ((int64_t)(x_start + i) * a.h_v + hv) * D + col0 + part * F::VU);
     }
     const int xqc = min(max(xq, c0), c1 - 1);
-    const int q_start = chunk_start(xqc), q_last = chunk_len(xqc) - 1;
-    const E* qg = static_cast<const E*>(a.q);
+    const u32x4* qg = reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const Frag<E>*>(a.q_frag) + ((int64_t)xqc * a.h_qk + hq) * G::Q_FR * 64);
 #pragma unroll
-    for (int p = 0; p < F::P_Q; ++p) {
-      const int u = min(lt + p * F::NL, F::N_Q - 1);
-      const int f = u / 64, ln = u % 64, nt = f / DKS, s = f % DKS;
-      const int r = min(16 * nt + (ln & 15), q_last);
-      fr.q[p] = load_frag<E>(qg + ((int64_t)(q_start + r) * a.h_qk + hq) * D + 32 * s, ln >> 4, D - 32 * s);
-    }
+    for (int p = 0; p < F::P_Q; ++p) fr.q[p] = qg[min(lt + p * F::NL, F::N_Q - 1)];
   };
   // ---- loaders: registers -> LDS, masking what the fetch clamped ----
   auto store = [&](const F& fr, int x, int xq) __attribute__((always_inline)) {
@@ -603,20 +609,9 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       }
     }
     if (xq >= c0 && xq < c1) {
-      const int q_len = chunk_len(xq);
+      u32x4* qf = reinterpret_cast<u32x4*>(sm.qf);
 #pragma unroll
-      for (int p = 0; p < F::P_Q; ++p) {
-        const int u = lt + p * F::NL;
-        if (u < F::N_Q) {
-          const int nt = (u / 64) / DKS, r = 16 * nt + (u % 64 & 15);
-          Frag<E> v = fr.q[p];
-          if (r >= q_len) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = to_e<E>(0.f);
-          }
-          sm.qf[u] = v;
-        }
-      }
+      for (int p = 0; p < F::P_Q; ++p) { const int u = lt + p * F::NL; if (u < F::N_Q) qf[u] = fr.q[p]; }
     }
   };
 
@@ -625,7 +620,6 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
 
   auto scan_chunk = [&](int c) __attribute__((always_inline)) {
     const int start = chunk_start(c), len = chunk_len(c), par = c & 1;
-    const float* gs = sm.gb[par][0];
     Frag<E> Sf[DKS];
 #pragma unroll
     for (int ks = 0; ks < DKS; ++ks) Sf[ks] = acc_to_frag<E>(S[2 * ks], (2 * ks + 1 < DT) ? S[2 * ks + 1] : zero4());
@@ -665,32 +659,38 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     }
     // U = Ut - W S; the inter-chunk output takes exp(g_r) (rows past the
     // chunk end are zeroed by multiplying, not branching)
+    // (the row factors come from the producers' per-chunk tables)
+    const float* ea = sm.dtab[par][0];
+    const float* ed = sm.dtab[par][1];
     f32x4 U[CT];
 #pragma unroll
     for (int t = 0; t < CT; ++t) {
       U[t] = sm.uf[par][(slice * CT + t) * 64 + lane] - WS[t];
-      const int r = 16 * t + l16;
-      O[t] *= __expf(gs[r]) * (float)(r < len);
+      O[t] *= ea[16 * t + l16];
     }
     Frag<E> Uk[CKS];
 #pragma unroll
     for (int ks = 0; ks < CKS; ++ks) Uk[ks] = acc_to_frag<E>(U[2 * ks], (2 * ks + 1 < CT) ? U[2 * ks + 1] : zero4());
     // decayed rows exp(g_L - g_r) U_r
-    const float g_last = gs[len - 1];
 #pragma unroll
-    for (int t = 0; t < CT; ++t) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * t + 4 * quad + i;
-        U[t][i] *= __expf(fminf(g_last - gs[r], 0.f)) * (float)(r < len);
-      }
-    }
+    for (int t = 0; t < CT; ++t) U[t] *= *reinterpret_cast<const f32x4*>(&ed[16 * t + 4 * quad]);
     Frag<E> Ud[CKS];
 #pragma unroll
     for (int ks = 0; ks < CKS; ++ks) Ud[ks] = acc_to_frag<E>(U[2 * ks], (2 * ks + 1 < CT) ? U[2 * ks + 1] : zero4());
-    // S <- exp(g_L) S + K^T Ud (DT independent accumulators per step), and
-    // the intra-chunk output O^T += U^T P^T
-    const float gam = __expf(g_last);
+    // the intra-chunk output O^T += U^T P^T first, so that O is final while
+    // the state update S <- exp(g_L) S + K^T Ud runs (DT independent
+    // accumulators per step)
+#pragma unroll
+    for (int ks = 0; ks < CKS; ++ks) {
+      Frag<E> pa[CT];
+#pragma unroll
+      for (int nt = 0; nt < CT; ++nt)
+        if (!causal_zero(nt, ks)) pa[nt] = sm.pf[par][(nt * CKS + ks) * 64 + lane];
+#pragma unroll
+      for (int nt = 0; nt < CT; ++nt)
+        if (!causal_zero(nt, ks)) O[nt] = mma(Uk[ks], pa[nt], O[nt]);
+    }
+    const float gam = sm.gam[par];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) S[dt] *= gam;
 #pragma unroll
@@ -698,15 +698,8 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       Frag<E> ka[DT];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) ka[dt] = sm.kt[par][(dt * CKS + ks) * 64 + lane];
-      Frag<E> pa[CT];
-#pragma unroll
-      for (int nt = 0; nt < CT; ++nt)
-        if (!causal_zero(nt, ks)) pa[nt] = sm.pf[par][(nt * CKS + ks) * 64 + lane];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) S[dt] = mma(ka[dt], Ud[ks], S[dt]);
-#pragma unroll
-      for (int nt = 0; nt < CT; ++nt)
-        if (!causal_zero(nt, ks)) O[nt] = mma(Uk[ks], pa[nt], O[nt]);
     }
     E* og = static_cast<E*>(a.o);
 #pragma unroll
@@ -725,7 +718,21 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     const int par = p & 1;
     const int len = chunk_len(p);
     const float* gp = sm.gb[par][0];
-    constexpr int NITEM = NS + CT;
+    if (pw == NPROD - 1 && lane < C) {
+      // the scan's row factors for this chunk
+      const float gl = gp[len - 1], valid = (float)(lane < len);
+      sm.dtab[par][0][lane] = __expf(gp[lane]) * valid;
+      sm.dtab[par][1][lane] = __expf(fminf(gl - gp[lane], 0.f)) * valid;
+      if (lane == 0) sm.gam[par] = __expf(gl);
+    }
+    // items: the Ut tiles of each slice, then one per q.k fragment that the
+    // causal mask does not zero
+    constexpr int NPF = [] {
+      int n = 0;
+      for (int f = 0; f < CT * CKS; ++f) n += causal_zero(f / CKS, f % CKS) ? 0 : 1;
+      return n;
+    }();
+    constexpr int NITEM = NS + NPF;
     for (int item = pw; item < NITEM; item += NPROD) {
       if (item < NS) {
         // Ut accumulator tiles of slice sl: Tinv diag(b) V
@@ -750,22 +757,32 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
 #pragma unroll
         for (int rt = 0; rt < CT; ++rt) sm.uf[par][(sl * CT + rt) * 64 + lane] = acc[rt];
       } else {
-        // masked, decayed q.k fragments of query tile nt
-        const int nt = item - NS;
-        const int r = 16 * nt + l16;
-        const float gr = gp[r];
+        // a masked, decayed q.k fragment (nt, s)
+        int nt = 0, s = 0;
+        {
+          int k = item - NS;
 #pragma unroll
-        for (int s = 0; s < CKS; ++s) {
-          if (causal_zero(nt, s)) continue;
+          for (int f = 0; f < CT * CKS; ++f) {
+            if (causal_zero(f / CKS, f % CKS)) continue;
+            if (k == 0) { nt = f / CKS; s = f % CKS; }
+            --k;
+          }
+        }
+        const int r = 16 * nt + l16;
+        const float gr = gp[r], vr = (float)(r < len);
+        {
           const Frag<E> raw = sm.qk[(nt * CKS + s) * 64 + lane];
+          // g of the fragment's keys: two runs of four
+          const f32x4 g0 = *reinterpret_cast<const f32x4*>(&gp[32 * s + 4 * quad]);
+          const f32x4 g1 = (32 * s + 16 < C) ? *reinterpret_cast<const f32x4*>(&gp[32 * s + 16 + 4 * quad]) : zero4();
           Frag<E> v;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int j = frag_k(s, quad, e);
             // the exponent is clamped at 0 so that masked entries (j > r,
             // where g_r - g_j >= 0) cannot overflow before being zeroed
-            const float m = (float)(j <= r && r < len);
-            v[e] = to_e<E>(to_f(raw[e]) * (__expf(fminf(gr - gp[j], 0.f)) * m));
+            const float m = (float)(j <= r) * vr;
+            v[e] = to_e<E>(to_f(raw[e]) * (__expf(fminf(gr - (e < 4 ? g0[e] : g1[e - 4]), 0.f)) * m));
           }
           sm.pf[par][(nt * CKS + s) * 64 + lane] = v;
         }

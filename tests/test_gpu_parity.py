@@ -197,6 +197,8 @@ def test_stage_outputs_match_oracle_chunks(chunk):
         nc, 2, 8, cks, 64, 8).double().numpy()
     qk = region(lay.qk, nc * 2 * ct * cks * 512, torch.bfloat16).view(
         nc, 2, ct, cks, 64, 8).double().numpy()
+    qf = region(lay.q_frag, nc * 2 * ct * 4 * 512, torch.bfloat16).view(
+        nc, 2, ct, 4, 64, 8).double().numpy()
     _, _, stages = O.chunkwise(**oracle_args(inp), chunk=chunk, keep_stages=True)
     q64, k64, b64 = np64(inp["q"]), np64(inp["k"]), np64(inp["beta"])
     n_seq0 = -(-77 // chunk)
@@ -218,6 +220,8 @@ def test_stage_outputs_match_oracle_chunks(chunk):
         for hq in range(2):
             ktm = unfrag(kt[c, hq], 128, chunk)            # [d][i]
             assert np.array_equal(ktm[:, :L], k64[t0:t0 + L, hq].T) and (ktm[:, L:] == 0).all()
+            qfm = unfrag(qf[c, hq], chunk, 128)            # [r][d]
+            assert np.array_equal(qfm[:L], q64[t0:t0 + L, hq]) and (qfm[L:] == 0).all()
             qkm = unfrag(qk[c, hq], chunk, chunk)          # [query r][key j]
             want = q64[t0:t0 + L, hq] @ k64[t0:t0 + L, hq].T
             causal = np.tril(np.ones((L, L)), 0) > 0

@@ -442,9 +442,9 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
 
 // --------------------------------------------------------------------------
 // Kernel 3: fused Ut construction, inter-chunk state scan and outputs.
-// One workgroup per (sequence, V head, block of BV state columns), eight
-// waves, looping over the sequence's chunks in order with a software
-// pipeline:
+// One workgroup per (sequence, V head, block of BV state columns), twelve
+// waves, looping over the sequence's chunks in order with one barrier per
+// chunk:
 //   scan waves (one per 16-column slice) process chunk c: with the slice of
 //     the state S (D x 16 fp32) held in MFMA accumulators for the whole
 //     sequence,
@@ -454,63 +454,66 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
 //       O^T += U^T (Q K^T * Dincl)^T                (U's tiles are the A fragments)
 //       S    = exp(g_L) S + K^T (exp(g_L - g) * U)
 //     and store the chunk's outputs for their columns;
-//   producer waves build chunk c+1's Ut tiles and the masked, decayed
-//     (q.k) fragments in LDS, and double as loaders: they fetch chunk
-//     c+3's K^T, W, Tinv diag(b), q.k, g, b and V slice (and chunk c+2's Q) into
-//     one of two register sets while the other set, fetched one iteration
-//     earlier, is written into LDS for chunk c+2 between the barriers.
-// Every LDS region is either double-buffered by chunk parity or written only
-// between the two barriers of an iteration after its last reader is done.
+//   producer waves, meanwhile, build chunk c+1's Ut tiles, masked and
+//     decayed q.k fragments and row-factor tables in LDS; Tinv diag(b),
+//     which only the Ut wave reads, goes to that wave's registers two
+//     chunks ahead;
+//   loader waves copy chunk c+1's K^T, W and Q fragments and chunk c+2's
+//     q.k fragments, V columns, g and b from global memory straight into
+//     LDS (direct global-to-LDS loads, 1 KB per wave instruction, no
+//     register staging) and wait for them before the barrier.
+// Every LDS region is double-buffered by chunk parity; between two barriers
+// a slot is either only read or only written.
 // --------------------------------------------------------------------------
-constexpr int kScanBlock = 512;
+constexpr int kScanBlock = 768;
 
 template <typename E, int D, int C>
 struct ScanSmem {
   using G = Cfg<E, D, C>;
-  Frag<E> kt[2][G::KT_FR * 64];        // K^T fragments, by chunk parity
-  Frag<E> qf[G::Q_FR * 64];            // Q fragments of the chunk being scanned
-  Frag<E> tf[G::T_FR * 64];            // Tinv diag(b) of the chunk being produced
-  Frag<E> qk[G::QK_FR * 64];           // q.k fragments of the chunk being produced
-  Frag<E> wf[2][G::W_FR * 64];         // W fragments, by chunk parity
-  Frag<E> pf[2][G::QK_FR * 64];        // masked, decayed q.k fragments, by parity
-  f32x4 uf[2][G::NS * G::CT * 64];     // Ut accumulator tiles, by parity
-  E vt[G::BV * G::VLD];                // V slice of the chunk being produced, transposed
-  float gb[2][2][C];                   // g and b, by chunk parity
-  // per chunk, by parity: exp(g_r) and exp(min(g_L - g_r, 0)), both zero
-  // past the chunk end, and exp(g_L)
+  Frag<E> kt[2][G::KT_FR * 64];        // K^T fragments
+  Frag<E> wf[2][G::W_FR * 64];         // W fragments
+  Frag<E> qf[2][G::Q_FR * 64];         // Q fragments
+  Frag<E> qk[2][G::QK_FR * 64];        // q.k fragments
+  Frag<E> pf[2][G::QK_FR * 64];        // masked, decayed q.k fragments
+  f32x4 uf[2][G::NS * G::CT * 64];     // Ut accumulator tiles
+  E vr[2][C * G::BV];                  // the block's V columns, row-major
+  float gb[2][2][C] __attribute__((aligned(16)));    // g and b
+  // exp(g_r) and exp(min(g_L - g_r, 0)), both zero past the chunk end
   float dtab[2][2][C] __attribute__((aligned(16)));
-  float gam[2];
+  float gam[2];                        // exp(g_L)
 };
 
-// One register set of loader data: a chunk's operands plus the next chunk's Q.
-template <typename E, int D, int C>
-struct ScanFetch {
-  using G = Cfg<E, D, C>;
-  static constexpr int NL = kScanBlock - 64 * G::NS;                 // loader threads
-  static constexpr int FR16 = (int)sizeof(Frag<E>) / 16;             // 16-byte units per lane-fragment
-  static constexpr int N_KT = G::KT_FR * 64 * FR16, N_T = G::T_FR * 64 * FR16, N_QK = G::QK_FR * 64 * FR16;
-  static constexpr int N_W = G::W_FR * 64 * FR16;
-  static constexpr int N_GB = 2 * C * 4 / 16;
-  static constexpr int VU = 16 / (int)sizeof(E);                     // V elements per 16-byte unit
-  static constexpr int N_V = C * G::BV / VU;
-  static constexpr int N_Q = G::Q_FR * 64 * FR16;                    // 16-byte units of Q fragments
-  static constexpr int P_KT = (N_KT + NL - 1) / NL, P_T = (N_T + NL - 1) / NL, P_W = (N_W + NL - 1) / NL;
-  static constexpr int P_QK = (N_QK + NL - 1) / NL, P_V = (N_V + NL - 1) / NL;
-  static constexpr int P_Q = (N_Q + NL - 1) / NL, P_GB = (N_GB + NL - 1) / NL;
-  typedef E VUnit __attribute__((ext_vector_type(VU)));             // one 16-byte unit of V
-  u32x4 kt[P_KT], t[P_T], w[P_W], qk[P_QK], gb[P_GB];
-  VUnit v[P_V];
-  u32x4 q[P_Q];
-};
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Workgroup barrier for the scan waves: it waits only for this wave's LDS
+// operations, not for its global stores (nothing in the workgroup reads
+// them back).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One direct global-to-LDS copy of up to 1 KB: lane l copies the 16 bytes
+// at src + 16 l to dst + 16 l (dst is the same for the whole wave); lanes
+// at or past `bytes` copy nothing.
+__device__ __forceinline__ void copy_1k(const char* src, char* dst, int bytes, int lane) {
+  if (16 * lane < bytes) __builtin_amdgcn_global_load_lds(src + 16 * lane, (lds_ptr_t)dst, 16, 0, 0);
+}
 
 template <typename E, int D, int C>
 __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
-  using F = ScanFetch<E, D, C>;
   constexpr int DT = G::DT, CT = G::CT, DKS = G::DKS, CKS = G::CKS, NS = G::NS, BV = G::BV;
-  constexpr int NPROD = kScanBlock / 64 - NS;
+  // roles: NS scan waves, NLD loader waves (direct copies only, so that
+  // their stalls on the memory pipeline hold up nothing else) and NPROD
+  // producer waves
+  constexpr int NLD = 6;
+  constexpr int NPROD = kScanBlock / 64 - NS - NLD;
+  static_assert(NPROD >= 2, "a Ut wave and at least one q.k wave");
+  constexpr int FB = (int)sizeof(Frag<E>) * 64;            // bytes per fragment
+  constexpr int ESZ = (int)sizeof(E);
   __shared__ ScanSmem<E, D, C> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, quad = lane >> 4, l16 = lane & 15;
+  // the wave index in a scalar register, so that role and job selection
+  // compile to scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // the column blocks and V heads of one QK head, which read the same K^T,
   // q.k and Q fragments, are consecutive logical ids and so share an XCD
   const int64_t bid = xcd_local_id(blockIdx.x, gridDim.x);
@@ -525,94 +528,66 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   const int seq_end = a.cu_seqlens ? a.cu_seqlens[n + 1] : (int)a.total_tokens;
   auto chunk_start = [&](int x) { return seq_start + (x - c0) * C; };
   auto chunk_len = [&](int x) { return min(C, seq_end - chunk_start(x)); };
-  const bool is_scan = wave < NS;
+  const bool is_scan = wave < NS, is_loader = !is_scan && wave < NS + NLD;
   const int slice = wave;                      // scan waves: slice index
-  const int pw = wave - NS;                    // producer waves: index
-  const int lt = tid - 64 * NS;                // loader thread index (producers only)
+  const int lw = wave - NS;                    // loader waves: index
+  const int pw = wave - NS - NLD;              // producer waves: index
   const int col0 = cb * BV;                    // first state column of this workgroup
   const int64_t state_base = (n * a.h_v + hv) * D * D;
 
-  // ---- loaders: global -> registers (chunk x's operands, chunk xq's Q) ----
-  // Branch-free: every loader issues the same loads, with indices clamped
-  // into range (the last valid unit, row or chunk); what lies outside is
-  // masked when the registers are stored. Keeping the loads unconditional
-  // lets them stay in flight across the pipeline's barriers.
-  auto fetch = [&](F& fr, int x, int xq) __attribute__((always_inline)) {
-    const int xc = min(x, c1 - 1);
-    const u32x4* ktg = reinterpret_cast<const u32x4*>(
-        reinterpret_cast<const Frag<E>*>(a.key_t) + ((int64_t)xc * a.h_qk + hq) * G::KT_FR * 64);
-    const u32x4* tg = reinterpret_cast<const u32x4*>(
-        reinterpret_cast<const Frag<E>*>(a.tinv) + ((int64_t)xc * a.h_v + hv) * G::T_FR * 64);
-    const u32x4* wg = reinterpret_cast<const u32x4*>(
-        reinterpret_cast<const Frag<E>*>(a.w) + ((int64_t)xc * a.h_v + hv) * G::W_FR * 64);
-    const u32x4* qkg = reinterpret_cast<const u32x4*>(
-        reinterpret_cast<const Frag<E>*>(a.qk) + ((int64_t)xc * a.h_qk + hq) * G::QK_FR * 64);
-#pragma unroll
-    for (int p = 0; p < F::P_KT; ++p) fr.kt[p] = ktg[min(lt + p * F::NL, F::N_KT - 1)];
-#pragma unroll
-    for (int p = 0; p < F::P_T; ++p) fr.t[p] = tg[min(lt + p * F::NL, F::N_T - 1)];
-#pragma unroll
-    for (int p = 0; p < F::P_W; ++p) fr.w[p] = wg[min(lt + p * F::NL, F::N_W - 1)];
-#pragma unroll
-    for (int p = 0; p < F::P_QK; ++p) fr.qk[p] = qkg[min(lt + p * F::NL, F::N_QK - 1)];
-#pragma unroll
-    for (int p = 0; p < F::P_GB; ++p) {
-      const int u = min(lt + p * F::NL, F::N_GB - 1), half = F::N_GB / 2;
-      const float* src = (u < half ? a.gate_prefix : a.beta_chunk) + ((int64_t)xc * a.h_v + hv) * C;
-      fr.gb[p] = reinterpret_cast<const u32x4*>(src)[u % half];
-    }
-    const int x_start = chunk_start(xc), x_last = chunk_len(xc) - 1;
-    const E* vg = static_cast<const E*>(a.v);
-#pragma unroll
-    for (int p = 0; p < F::P_V; ++p) {
-      const int u = min(lt + p * F::NL, F::N_V - 1);
-      const int i = min(u / (BV / F::VU), x_last), part = u % (BV / F::VU);
-      fr.v[p] = *reinterpret_cast<const typename F::VUnit*>(
-          vg + ((int64_t)(x_start + i) * a.h_v + hv) * D + col0 + part * F::VU);
-    }
-    const int xqc = min(max(xq, c0), c1 - 1);
-    const u32x4* qg = reinterpret_cast<const u32x4*>(
-        reinterpret_cast<const Frag<E>*>(a.q_frag) + ((int64_t)xqc * a.h_qk + hq) * G::Q_FR * 64);
-#pragma unroll
-    for (int p = 0; p < F::P_Q; ++p) fr.q[p] = qg[min(lt + p * F::NL, F::N_Q - 1)];
+  // ---- direct copies into LDS: chunk xs's scan operands, chunk xp's
+  // producer data; the window's jobs are dealt round-robin to the loader
+  // waves ----
+  constexpr int B_KT = G::KT_FR * FB, B_W = G::W_FR * FB, B_Q = G::Q_FR * FB, B_QK = G::QK_FR * FB;
+  constexpr int B_V = C * BV * ESZ, B_G = C * 4;
+  constexpr int NREG = 7;
+  constexpr int JOBS[NREG] = {(B_KT + 1023) / 1024, (B_W + 1023) / 1024, (B_Q + 1023) / 1024,
+                              (B_QK + 1023) / 1024, (B_V + 1023) / 1024, (B_G + 1023) / 1024,
+                              (B_G + 1023) / 1024};
+  constexpr int CUM[NREG] = {0, JOBS[0], JOBS[0] + JOBS[1], JOBS[0] + JOBS[1] + JOBS[2],
+                             JOBS[0] + JOBS[1] + JOBS[2] + JOBS[3],
+                             JOBS[0] + JOBS[1] + JOBS[2] + JOBS[3] + JOBS[4],
+                             JOBS[0] + JOBS[1] + JOBS[2] + JOBS[3] + JOBS[4] + JOBS[5]};
+  // loader wave lw takes the jobs whose window-wide index is lw mod NLD
+  auto copy_region = [&](int r, const char* src, char* dst, int bytes) __attribute__((always_inline)) {
+    for (int jj = ((lw - CUM[r]) % NLD + NLD) % NLD; jj < JOBS[r]; jj += NLD)
+      copy_1k(src + 1024 * jj, dst + 1024 * jj, bytes - 1024 * jj, lane);
   };
-  // ---- loaders: registers -> LDS, masking what the fetch clamped ----
-  auto store = [&](const F& fr, int x, int xq) __attribute__((always_inline)) {
-    if (x < c1) {
-      u32x4* kt = reinterpret_cast<u32x4*>(sm.kt[x & 1]);
-      u32x4* tf = reinterpret_cast<u32x4*>(sm.tf);
-      u32x4* wf = reinterpret_cast<u32x4*>(sm.wf[x & 1]);
-      u32x4* qk = reinterpret_cast<u32x4*>(sm.qk);
-#pragma unroll
-      for (int p = 0; p < F::P_KT; ++p) { const int u = lt + p * F::NL; if (u < F::N_KT) kt[u] = fr.kt[p]; }
-#pragma unroll
-      for (int p = 0; p < F::P_T; ++p) { const int u = lt + p * F::NL; if (u < F::N_T) tf[u] = fr.t[p]; }
-#pragma unroll
-      for (int p = 0; p < F::P_W; ++p) { const int u = lt + p * F::NL; if (u < F::N_W) wf[u] = fr.w[p]; }
-#pragma unroll
-      for (int p = 0; p < F::P_QK; ++p) { const int u = lt + p * F::NL; if (u < F::N_QK) qk[u] = fr.qk[p]; }
-#pragma unroll
-      for (int p = 0; p < F::P_GB; ++p) {
-        const int u = lt + p * F::NL;
-        if (u < F::N_GB) reinterpret_cast<u32x4*>(&sm.gb[x & 1][0][0])[u] = fr.gb[p];
-      }
-      const int x_len = chunk_len(x);
-#pragma unroll
-      for (int p = 0; p < F::P_V; ++p) {
-        const int u = lt + p * F::NL;
-        if (u < F::N_V) {
-          const int i = u / (BV / F::VU), part = u % (BV / F::VU);
-#pragma unroll
-          for (int e = 0; e < F::VU; ++e)
-            sm.vt[(part * F::VU + e) * G::VLD + i] = (i < x_len) ? fr.v[p][e] : to_e<E>(0.f);
-        }
-      }
+  auto copy_window = [&](int xs, int xp) __attribute__((always_inline)) {
+    if (xs < c1) {
+      copy_region(0, static_cast<const char*>(a.key_t) + ((int64_t)xs * a.h_qk + hq) * B_KT,
+                  reinterpret_cast<char*>(sm.kt[xs & 1]), B_KT);
+      copy_region(1, static_cast<const char*>(a.w) + ((int64_t)xs * a.h_v + hv) * B_W,
+                  reinterpret_cast<char*>(sm.wf[xs & 1]), B_W);
+      copy_region(2, static_cast<const char*>(a.q_frag) + ((int64_t)xs * a.h_qk + hq) * B_Q,
+                  reinterpret_cast<char*>(sm.qf[xs & 1]), B_Q);
     }
-    if (xq >= c0 && xq < c1) {
-      u32x4* qf = reinterpret_cast<u32x4*>(sm.qf);
-#pragma unroll
-      for (int p = 0; p < F::P_Q; ++p) { const int u = lt + p * F::NL; if (u < F::N_Q) qf[u] = fr.q[p]; }
+    if (xp < c1) {
+      copy_region(3, static_cast<const char*>(a.qk) + ((int64_t)xp * a.h_qk + hq) * B_QK,
+                  reinterpret_cast<char*>(sm.qk[xp & 1]), B_QK);
+      // the V columns, row i of the chunk at byte 16 l of its job; rows
+      // past the chunk end repeat its last row (Tinv diag(b) has zero
+      // columns there)
+      const int p_start = chunk_start(xp), p_last = chunk_len(xp) - 1;
+      char* vdst = reinterpret_cast<char*>(sm.vr[xp & 1]);
+      for (int jj = ((lw - CUM[4]) % NLD + NLD) % NLD; jj < JOBS[4]; jj += NLD) {
+        const int o = 1024 * jj + 16 * lane;
+        const int i = min(o / (BV * ESZ), p_last);
+        const char* vsrc = static_cast<const char*>(a.v) +
+                           (((int64_t)(p_start + i) * a.h_v + hv) * D + col0) * ESZ + o % (BV * ESZ);
+        if (o < B_V) __builtin_amdgcn_global_load_lds(vsrc, (lds_ptr_t)(vdst + 1024 * jj), 16, 0, 0);
+      }
+      copy_region(5, reinterpret_cast<const char*>(a.gate_prefix + ((int64_t)xp * a.h_v + hv) * C),
+                  reinterpret_cast<char*>(sm.gb[xp & 1][0]), B_G);
+      copy_region(6, reinterpret_cast<const char*>(a.beta_chunk + ((int64_t)xp * a.h_v + hv) * C),
+                  reinterpret_cast<char*>(sm.gb[xp & 1][1]), B_G);
     }
+  };
+  // Tinv diag(b) fragments of chunk x into registers (the Ut wave)
+  auto load_tb = [&](Frag<E> (&tb)[G::T_FR], int x) __attribute__((always_inline)) {
+    const Frag<E>* tg = reinterpret_cast<const Frag<E>*>(a.tinv) + ((int64_t)min(x, c1 - 1) * a.h_v + hv) * G::T_FR * 64;
+#pragma unroll
+    for (int f = 0; f < G::T_FR; ++f) tb[f] = tg[f * 64 + lane];
   };
 
   // scan waves: the slice's D x 16 state columns in accumulator tiles
@@ -634,7 +609,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     Frag<E> qa[CT], wa[CT];
 #pragma unroll
     for (int t = 0; t < CT; ++t) {
-      qa[t] = sm.qf[(t * DKS) * 64 + lane];
+      qa[t] = sm.qf[par][(t * DKS) * 64 + lane];
       wa[t] = sm.wf[par][(t * DKS) * 64 + lane];
     }
 #pragma unroll
@@ -643,7 +618,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       if (ks + 1 < DKS) {
 #pragma unroll
         for (int t = 0; t < CT; ++t) {
-          qn[t] = sm.qf[(t * DKS + ks + 1) * 64 + lane];
+          qn[t] = sm.qf[par][(t * DKS + ks + 1) * 64 + lane];
           wn[t] = sm.wf[par][(t * DKS + ks + 1) * 64 + lane];
         }
       }
@@ -657,9 +632,8 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
         for (int t = 0; t < CT; ++t) { qa[t] = qn[t]; wa[t] = wn[t]; }
       }
     }
-    // U = Ut - W S; the inter-chunk output takes exp(g_r) (rows past the
-    // chunk end are zeroed by multiplying, not branching)
-    // (the row factors come from the producers' per-chunk tables)
+    // U = Ut - W S; the inter-chunk output takes exp(g_r); the row factors
+    // come from the producers' per-chunk tables (zero past the chunk end)
     const float* ea = sm.dtab[par][0];
     const float* ed = sm.dtab[par][1];
     f32x4 U[CT];
@@ -714,89 +688,91 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     }
   };
 
-  auto produce_chunk = [&](int p) __attribute__((always_inline)) {
+  // producer work for chunk p (whose q.k, V, g and b are in slot p & 1):
+  // the Ut wave (producer 0) forms every slice's Ut tiles from Tinv diag(b)
+  // in `tb`; the others each take masked, decayed q.k fragments in turn,
+  // and the last also the row-factor tables.
+  auto produce_chunk = [&](int p, const Frag<E> (&tb)[G::T_FR]) __attribute__((always_inline)) {
     const int par = p & 1;
     const int len = chunk_len(p);
     const float* gp = sm.gb[par][0];
     if (pw == NPROD - 1 && lane < C) {
-      // the scan's row factors for this chunk
       const float gl = gp[len - 1], valid = (float)(lane < len);
       sm.dtab[par][0][lane] = __expf(gp[lane]) * valid;
       sm.dtab[par][1][lane] = __expf(fminf(gl - gp[lane], 0.f)) * valid;
       if (lane == 0) sm.gam[par] = __expf(gl);
     }
-    // items: the Ut tiles of each slice, then one per q.k fragment that the
-    // causal mask does not zero
-    constexpr int NPF = [] {
-      int n = 0;
-      for (int f = 0; f < CT * CKS; ++f) n += causal_zero(f / CKS, f % CKS) ? 0 : 1;
-      return n;
-    }();
-    constexpr int NITEM = NS + NPF;
-    for (int item = pw; item < NITEM; item += NPROD) {
-      if (item < NS) {
-        // Ut accumulator tiles of slice sl: Tinv diag(b) V
-        const int sl = item;
-        const E* vrow = &sm.vt[(16 * sl + l16) * G::VLD];
+    if (pw == 0) {
+      // Ut = Tinv diag(b) V, slice by slice; V's fragments (col = state
+      // column, k = token) are gathered from the row-major V columns
+      const E* vr = sm.vr[par];
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) {
         Frag<E> vf[CKS];
 #pragma unroll
-        for (int s = 0; s < CKS; ++s) vf[s] = load_frag<E>(vrow + 32 * s, quad, C - 32 * s);
+        for (int s = 0; s < CKS; ++s) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int i = frag_k(s, quad, e);
+            vf[s][e] = (i < C) ? vr[i * BV + 16 * sl + l16] : to_e<E>(0.f);
+          }
+        }
         f32x4 acc[CT];
 #pragma unroll
         for (int rt = 0; rt < CT; ++rt) acc[rt] = zero4();
 #pragma unroll
         for (int s = 0; s < CKS; ++s) {
-          Frag<E> tb[CT];
 #pragma unroll
           for (int rt = 0; rt < CT; ++rt)
-            if (!causal_zero(rt, s)) tb[rt] = sm.tf[(rt * CKS + s) * 64 + lane];
-#pragma unroll
-          for (int rt = 0; rt < CT; ++rt)
-            if (!causal_zero(rt, s)) acc[rt] = mma(tb[rt], vf[s], acc[rt]);
+            if (!causal_zero(rt, s)) acc[rt] = mma(tb[rt * CKS + s], vf[s], acc[rt]);
         }
 #pragma unroll
         for (int rt = 0; rt < CT; ++rt) sm.uf[par][(sl * CT + rt) * 64 + lane] = acc[rt];
-      } else {
-        // a masked, decayed q.k fragment (nt, s)
-        int nt = 0, s = 0;
-        {
-          int k = item - NS;
+      }
+      return;
+    }
+    // q.k fragments that the causal mask does not zero, in order
+    constexpr int NPF = [] {
+      int k = 0;
+      for (int f = 0; f < CT * CKS; ++f) k += causal_zero(f / CKS, f % CKS) ? 0 : 1;
+      return k;
+    }();
+    for (int item = pw - 1; item < NPF; item += NPROD - 1) {
+      int nt = 0, s = 0;
+      {
+        int k = item;
 #pragma unroll
-          for (int f = 0; f < CT * CKS; ++f) {
-            if (causal_zero(f / CKS, f % CKS)) continue;
-            if (k == 0) { nt = f / CKS; s = f % CKS; }
-            --k;
-          }
-        }
-        const int r = 16 * nt + l16;
-        const float gr = gp[r], vr = (float)(r < len);
-        {
-          const Frag<E> raw = sm.qk[(nt * CKS + s) * 64 + lane];
-          // g of the fragment's keys: two runs of four
-          const f32x4 g0 = *reinterpret_cast<const f32x4*>(&gp[32 * s + 4 * quad]);
-          const f32x4 g1 = (32 * s + 16 < C) ? *reinterpret_cast<const f32x4*>(&gp[32 * s + 16 + 4 * quad]) : zero4();
-          Frag<E> v;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = frag_k(s, quad, e);
-            // the exponent is clamped at 0 so that masked entries (j > r,
-            // where g_r - g_j >= 0) cannot overflow before being zeroed
-            const float m = (float)(j <= r) * vr;
-            v[e] = to_e<E>(to_f(raw[e]) * (__expf(fminf(gr - (e < 4 ? g0[e] : g1[e - 4]), 0.f)) * m));
-          }
-          sm.pf[par][(nt * CKS + s) * 64 + lane] = v;
+        for (int f = 0; f < CT * CKS; ++f) {
+          if (causal_zero(f / CKS, f % CKS)) continue;
+          if (k == 0) { nt = f / CKS; s = f % CKS; }
+          --k;
         }
       }
+      const int r = 16 * nt + l16;
+      const float gr = gp[r], vr = (float)(r < len);
+      const Frag<E> raw = sm.qk[par][(nt * CKS + s) * 64 + lane];
+      // g of the fragment's keys: two runs of four
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(&gp[32 * s + 4 * quad]);
+      const f32x4 g1 = (32 * s + 16 < C) ? *reinterpret_cast<const f32x4*>(&gp[32 * s + 16 + 4 * quad]) : zero4();
+      Frag<E> v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = frag_k(s, quad, e);
+        // the exponent is clamped at 0 so that masked entries (j > r,
+        // where g_r - g_j >= 0) cannot overflow before being zeroed
+        const float m = (float)(j <= r) * vr;
+        v[e] = to_e<E>(to_f(raw[e]) * (__expf(fminf(gr - (e < 4 ? g0[e] : g1[e - 4]), 0.f)) * m));
+      }
+      sm.pf[par][(nt * CKS + s) * 64 + lane] = v;
     }
   };
 
-  // The two roles run separate loops with the same barrier sequence (one
-  // after the prologue, two per iteration), so each loop keeps only its own
-  // registers live: the scan waves the state, the producers the two loader
-  // register sets. Iteration c: scan chunk c; produce chunk c + 1; fetch
-  // chunk c + 3 (and Q of chunk c + 2) into one set; between the barriers
-  // stage the other set (chunk c + 2 and Q of chunk c + 1, fetched one
-  // iteration earlier) into LDS.
+  // The three roles run separate loops with the same barrier sequence (one
+  // after the prologue, one per iteration), so each keeps only its own
+  // registers live. Iteration c: the scan waves process chunk c; the
+  // loaders copy chunk c+1's scan operands and chunk c+2's producer data
+  // into LDS and wait for them; the producers produce chunk c+1 (and the
+  // Ut wave loads chunk c+2's Tinv diag(b)).
   if (c1 > c0) {
     if (is_scan) {
 #pragma unroll
@@ -810,8 +786,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       __syncthreads();
       for (int c = c0 - 1; c < c1; ++c) {
         if (c >= c0) scan_chunk(c);
-        __syncthreads();
-        __syncthreads();
+        lds_barrier();
       }
       if (a.final_state) {
 #pragma unroll
@@ -821,23 +796,30 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
             a.final_state[state_base + (int64_t)(16 * dt + 4 * quad + i) * D + col0 + 16 * slice + l16] = S[dt][i];
         }
       }
-    } else {
-      F fa, fb;
-      fetch(fa, c0, -1);
-      store(fa, c0, -1);
+    } else if (is_loader) {
+      // prologue: chunk c0's producer data (the scan-operand jobs are
+      // switched off by passing a chunk past the end)
+      copy_window(c1, c0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      fetch(fa, c0 + 1, c0);
-      for (int c = c0 - 1; c < c1; c += 2) {
-        fetch(fb, c + 3, c + 2);
-        if (c + 1 < c1) produce_chunk(c + 1);
+      for (int c = c0 - 1; c < c1; ++c) {
+        copy_window(c + 1, c + 2);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        store(fa, c + 2, c + 1);
+      }
+    } else {
+      Frag<E> ta[G::T_FR], tbn[G::T_FR];
+      if (pw == 0) load_tb(ta, c0);
+      __syncthreads();
+      // iteration c: produce chunk c+1 from one register set while chunk
+      // c+2's Tinv diag(b) arrives in the other
+      for (int c = c0 - 1; c < c1; c += 2) {
+        if (pw == 0) load_tb(tbn, c + 2);
+        if (c + 1 < c1) produce_chunk(c + 1, ta);
         __syncthreads();
         if (c + 1 < c1) {
-          fetch(fa, c + 4, c + 3);
-          if (c + 2 < c1) produce_chunk(c + 2);
-          __syncthreads();
-          store(fb, c + 3, c + 2);
+          if (pw == 0) load_tb(ta, c + 3);
+          if (c + 2 < c1) produce_chunk(c + 2, tbn);
           __syncthreads();
         }
       }

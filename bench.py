@@ -44,9 +44,10 @@ def algorithmic_work(T, HQ, HV, D, C, N, decode_batch):
     e = 2                                       # bytes per bf16 element
     gates = T * HV * 8                          # log a and b (fp32), or g and b
     work = {
-        # Q K^T per QK head; reads q, k, log a, b; writes K^T, q.k, g, b
+        # Q K^T per QK head; reads q, k, log a, b; writes K^T, Q and q.k
+        # fragments, g, b
         "gdn_k1_chunk_prep": (T * HQ * 2 * C * dk,
-                              2 * T * HQ * dk * e + gates + T * HQ * (dk + C) * e + gates),
+                              2 * T * HQ * dk * e + gates + T * HQ * (2 * dk + C) * e + gates),
         # K K^T per QK head, the triangular inverse and W per V head; reads k,
         # K^T, g, b; writes Tinv diag(b) and W
         "gdn_k2_inverse_w": (T * (HQ * 2 * C * dk + HV * (C * C / 3.0 + 2 * C * dk)),

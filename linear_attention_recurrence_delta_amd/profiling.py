@@ -22,7 +22,7 @@ import statistics
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 # kernel -> source file that defines it
-SOURCES = {"gdn_k1_gate_prefix": "gdn_prefill.hip", "gdn_k2_akk_inverse": "gdn_prefill.hip",
+SOURCES = {"gdn_k1_chunk_prep": "gdn_prefill.hip", "gdn_k2_inverse_w": "gdn_prefill.hip",
            "gdn_k3_scan": "gdn_prefill.hip", "gdn_kd_decode_step": "gdn_decode.hip"}
 
 

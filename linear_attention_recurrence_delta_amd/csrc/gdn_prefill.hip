@@ -481,13 +481,15 @@ struct ScanSmem {
   // exp(g_r) and exp(min(g_L - g_r, 0)), both zero past the chunk end
   float dtab[2][2][C] __attribute__((aligned(16)));
   float gam[2];                        // exp(g_L)
+  float touch[kScanBlock / 64][64];    // landing place of the L2 warm-up loads
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Workgroup barrier for the scan waves: it waits only for this wave's LDS
-// operations, not for its global stores (nothing in the workgroup reads
-// them back).
+// Workgroup barrier for the scan and producer waves: it waits only for this
+// wave's LDS operations, not for global stores or L2 warm-up loads (nothing
+// in the workgroup reads those back); loads into registers are waited for
+// where their values are used.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // One direct global-to-LDS copy of up to 1 KB: lane l copies the 16 bytes
@@ -588,6 +590,47 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     const Frag<E>* tg = reinterpret_cast<const Frag<E>*>(a.tinv) + ((int64_t)min(x, c1 - 1) * a.h_v + hv) * G::T_FR * 64;
 #pragma unroll
     for (int f = 0; f < G::T_FR; ++f) tb[f] = tg[f * 64 + lane];
+  };
+
+  // L2 warm-up, issued by the q.k producer waves after their chunk's work
+  // (they load nothing into registers, so nothing ever waits on these)
+  // three chunks ahead: one 4-byte load per 128-byte line of
+  // the chunk's streamed operands, each line touched by one of the
+  // workgroups that read it (per V head: W, Tinv diag(b), g and b, shared by
+  // the NCB column blocks; per QK head: K^T, Q and q.k, shared by the
+  // group's V heads too), plus this workgroup's own V rows. The loaded words
+  // land in a scratch LDS slot.
+  constexpr int B_T = G::T_FR * FB;
+  constexpr int LV = (B_W + B_T + 2 * B_G + 127) / 128;           // lines per (chunk, V head)
+  constexpr int LQ = (B_KT + B_Q + B_QK + 127) / 128;             // lines per (chunk, QK head)
+  const int gi = hv % a.group;
+  const int nv = (LV - cb + G::NCB - 1) / G::NCB;                 // this group's share of each
+  const int qs = gi * G::NCB + cb, qstride = a.group * G::NCB;
+  const int nq = qs < LQ ? (LQ - qs + qstride - 1) / qstride : 0;
+  auto line_addr = [&](int x, int t) -> const char* {
+    if (t < nv) {
+      const int o = 128 * (cb + G::NCB * t);
+      return o < B_W ? static_cast<const char*>(a.w) + ((int64_t)x * a.h_v + hv) * B_W + o
+           : o < B_W + B_T ? static_cast<const char*>(a.tinv) + ((int64_t)x * a.h_v + hv) * B_T + (o - B_W)
+           : o < B_W + B_T + B_G ? reinterpret_cast<const char*>(a.gate_prefix + ((int64_t)x * a.h_v + hv) * C) + (o - B_W - B_T)
+           : reinterpret_cast<const char*>(a.beta_chunk + ((int64_t)x * a.h_v + hv) * C) + min(o - B_W - B_T - B_G, B_G - 4);
+    }
+    t -= nv;
+    if (t < nq) {
+      const int o = 128 * (qs + qstride * t);
+      return o < B_KT ? static_cast<const char*>(a.key_t) + ((int64_t)x * a.h_qk + hq) * B_KT + o
+           : o < B_KT + B_Q ? static_cast<const char*>(a.q_frag) + ((int64_t)x * a.h_qk + hq) * B_Q + (o - B_KT)
+           : static_cast<const char*>(a.qk) + ((int64_t)x * a.h_qk + hq) * B_QK + min(o - B_KT - B_Q, B_QK - 4);
+    }
+    t -= nq;
+    const int i = min(t, chunk_len(x) - 1);
+    return static_cast<const char*>(a.v) + (((int64_t)(chunk_start(x) + i) * a.h_v + hv) * D + col0) * ESZ;
+  };
+  auto warm = [&](int x) __attribute__((always_inline)) {
+    if (x >= c1) return;
+    const int total = nv + nq + C;
+    for (int t = 64 * (pw - 1) + lane; t < total; t += 64 * (NPROD - 1))
+      __builtin_amdgcn_global_load_lds(line_addr(x, t), (lds_ptr_t)sm.touch[wave], 4, 0, 0);
   };
 
   // scan waves: the slice's D x 16 state columns in accumulator tiles
@@ -810,17 +853,20 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     } else {
       Frag<E> ta[G::T_FR], tbn[G::T_FR];
       if (pw == 0) load_tb(ta, c0);
+      else { warm(c0 + 1); warm(c0 + 2); }
       __syncthreads();
       // iteration c: produce chunk c+1 from one register set while chunk
       // c+2's Tinv diag(b) arrives in the other
       for (int c = c0 - 1; c < c1; c += 2) {
         if (pw == 0) load_tb(tbn, c + 2);
         if (c + 1 < c1) produce_chunk(c + 1, ta);
-        __syncthreads();
+        if (pw != 0) warm(c + 3);
+        lds_barrier();
         if (c + 1 < c1) {
           if (pw == 0) load_tb(ta, c + 3);
           if (c + 2 < c1) produce_chunk(c + 2, tbn);
-          __syncthreads();
+          if (pw != 0) warm(c + 4);
+          lds_barrier();
         }
       }
     }

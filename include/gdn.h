@@ -99,8 +99,8 @@ gdn_status_t gdn_chunk_fwd(const gdn_dims_t* dims,
  * Diagnostic variant of gdn_chunk_fwd that enqueues only launches
  * first_stage..last_stage, so a profiler or benchmark can put events between
  * them: 1 = chunk table, gate prefix sums, K^T, Q and Q K^T; 2 = K K^T,
- * (I + A)^{-1} and W; 3 = the fused U construction, inter-chunk state scan
- * and output products. Arguments are those of gdn_chunk_fwd. Stages after the
+ * (I + A)^{-1}, W, the masked and decayed Q K^T and the row factors; 3 = the
+ * fused U construction, inter-chunk state scan and output products. Arguments are those of gdn_chunk_fwd. Stages after the
  * first read what earlier stages left in `workspace`, so a call starting at
  * stage s > 1 must follow calls that ran stages 1..s-1 with identical
  * arguments and workspace on the same stream. gdn_chunk_fwd is
@@ -160,6 +160,8 @@ typedef struct {
   size_t key_t;        /* dtype [max_chunks][h_qk]: K^T as MFMA fragments */
   size_t qk;           /* dtype [max_chunks][h_qk]: q_r . k_j (j-tile <= r-tile) as fragments */
   size_t q_frag;       /* dtype [max_chunks][h_qk]: Q as MFMA fragments */
+  size_t pmask;        /* dtype [max_chunks][h_v]: q_r . k_j exp(g_r - g_j), j <= r, as fragments */
+  size_t dtab;         /* fp32 [max_chunks][h_v][2C+4]: exp(g_r), exp(g_L - g_r), exp(g_L), pad */
   size_t total;        /* == gdn_chunk_fwd_workspace_bytes(dims) */
   int64_t max_chunks;  /* floor(T / C) + N, the bound on the number of chunks */
 } gdn_workspace_layout_t;

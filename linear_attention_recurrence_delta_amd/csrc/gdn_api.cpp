@@ -91,6 +91,8 @@ Layout compute_layout(const gdn_dims_t& d) {
   L.v.key_t = take(NC * HQ * DT * CKS * 512 * esz);
   L.v.qk = take(NC * HQ * CT * CKS * 512 * esz);
   L.v.q_frag = take(NC * HQ * CT * ((DT + 1) / 2) * 512 * esz);
+  L.v.pmask = take(NC * HV * CT * CKS * 512 * esz);
+  L.v.dtab = take(NC * HV * (2 * C + 4) * 4);
   L.v.total = off;
   return L;
 }
@@ -193,6 +195,8 @@ gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims, const void* q, const v
   a.key_t = ws + L.v.key_t;
   a.qk = ws + L.v.qk;
   a.q_frag = ws + L.v.q_frag;
+  a.pmask = ws + L.v.pmask;
+  a.dtab = reinterpret_cast<float*>(ws + L.v.dtab);
   a.num_seqs = d.num_seqs;
   a.total_tokens = d.total_tokens;
   a.max_chunks = L.v.max_chunks;

@@ -29,6 +29,8 @@ struct PrefillArgs {
   void* key_t;              // [NC][HQ] fragments of K^T
   void* qk;                 // [NC][HQ] fragments of (q_r . k_j)
   void* q_frag;             // [NC][HQ] fragments of Q
+  void* pmask;              // [NC][HV] fragments of the masked, decayed q.k products
+  float* dtab;              // [NC][HV][2C+4] scan row factors exp(g), exp(g_L - g), exp(g_L)
   int64_t num_seqs;         // N
   int64_t total_tokens;     // T
   int64_t max_chunks;       // NC = floor(T/C) + N

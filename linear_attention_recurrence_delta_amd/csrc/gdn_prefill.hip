@@ -236,9 +236,10 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
 
 // --------------------------------------------------------------------------
 // Kernel 2: per (chunk, V head): A = strict_lower(b_r (k_r . k_i)
-// exp(g_r - g_i)), Tinv = (I + A)^{-1}, and the two operands the scan takes
-// from it: the fragments of Tinv diag(b) (the right factor of Ut) and of
-// W = Tinv diag(b exp(g)) K.
+// exp(g_r - g_i)), Tinv = (I + A)^{-1}, and the operands the scan takes from
+// it: the fragments of Tinv diag(b) (the right factor of Ut) and of
+// W = Tinv diag(b exp(g)) K; also the V head's masked, decayed q.k
+// fragments and the scan's row-factor table.
 // K K^T is formed with MFMA from the staged keys; A's entries are made in
 // the products' epilogue. A and Tinv share one C x C fp32 array in LDS (over
 // the keys, which are dead by then): A's blocks below the diagonal stay in
@@ -315,6 +316,15 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
       if (2 * ksd + 1 < DT) ktb[s] = ktg[((2 * ksd + 1) * CKS + s) * 64 + lane];
     }
   }
+  // the QK head's q.k fragments, which this V head masks and decays below
+  constexpr int PQ = (G::QK_FR * 64 + kBlock - 1) / kBlock;
+  Frag<E> qkr[PQ];
+  {
+    const Frag<E>* qkg = reinterpret_cast<const Frag<E>*>(a.qk) + (c * a.h_qk + hq) * G::QK_FR * 64;
+#pragma unroll
+    for (int p = 0; p < PQ; ++p)
+      if (tid + p * kBlock < G::QK_FR * 64) qkr[p] = qkg[tid + p * kBlock];
+  }
   const E* kg = static_cast<const E*>(a.k);
   for (int idx = tid; idx < C * D / VE; idx += kBlock) {
     const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
@@ -329,6 +339,40 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
     sm.gb[tid / C][tid % C] = (tid < C) ? a.gate_prefix[o] : a.beta_chunk[o];
   }
   __syncthreads();
+
+  // The scan's operands that depend on g: P = the masked, decayed q.k
+  // fragments, P[r][j] = (q_r . k_j) exp(g_r - g_j) for j <= r < len, else 0
+  // (the exponent is clamped at 0 so that masked entries cannot overflow
+  // before being zeroed), and the row-factor table exp(g_r), exp(min(g_L -
+  // g_r, 0)) (both zero past the chunk end), exp(g_L).
+  {
+    Frag<E>* pg = reinterpret_cast<Frag<E>*>(a.pmask) + (c * a.h_v + hv) * G::QK_FR * 64;
+#pragma unroll
+    for (int p = 0; p < PQ; ++p) {
+      const int it = tid + p * kBlock;
+      if (it >= G::QK_FR * 64) continue;
+      const int f = it / 64, ln = it % 64, nt = f / CKS, s = f % CKS, q4 = ln >> 4;
+      const int r = 16 * nt + (ln & 15);
+      const float gr = sm.gb[0][r], vr = (float)(r < len);
+      Frag<E> v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = frag_k(s, q4, e);
+        const float m = (float)(j <= r) * vr;
+        v[e] = to_e<E>(to_f(qkr[p][e]) * (__expf(fminf(gr - sm.gb[0][min(j, C - 1)], 0.f)) * m));
+      }
+      pg[it] = v;
+    }
+    float* dtg = a.dtab + (c * a.h_v + hv) * (2 * C + 4);
+    const float gl = sm.gb[0][len - 1];
+    if (tid < C) {
+      const float valid = (float)(tid < len);
+      dtg[tid] = __expf(sm.gb[0][tid]) * valid;
+      dtg[C + tid] = __expf(fminf(gl - sm.gb[0][tid], 0.f)) * valid;
+    } else if (tid < C + 4) {
+      dtg[C + tid] = (tid == C) ? __expf(gl) : 0.f;
+    }
+  }
 
   // K K^T tiles on and below the diagonal, lower tile t -> (mi, ni)
   constexpr int NTILE = CT * (CT + 1) / 2, TPW = (NTILE + NW - 1) / NW;
@@ -451,17 +495,16 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
 //       O^T  = diag(exp(g)) applied to S^T Q^T      (inter-chunk output)
 //       U    = Ut - W S                            (S's accumulator tiles are
 //                                                   the B fragments here)
-//       O^T += U^T (Q K^T * Dincl)^T                (U's tiles are the A fragments)
+//       O^T += U^T P^T, P = (Q K^T * Dincl)         (U's tiles are the A fragments)
 //       S    = exp(g_L) S + K^T (exp(g_L - g) * U)
 //     and store the chunk's outputs for their columns;
-//   producer waves, meanwhile, build chunk c+1's Ut tiles, masked and
-//     decayed q.k fragments and row-factor tables in LDS; Tinv diag(b),
-//     which only the Ut wave reads, goes to that wave's registers two
-//     chunks ahead;
-//   loader waves copy chunk c+1's K^T, W and Q fragments and chunk c+2's
-//     q.k fragments, V columns, g and b from global memory straight into
-//     LDS (direct global-to-LDS loads, 1 KB per wave instruction, no
-//     register staging) and wait for them before the barrier.
+//   Ut waves (one per slice), meanwhile, form chunk c+1's Ut tiles
+//     Tinv diag(b) V in LDS;
+//   loader waves copy chunk c+1's K^T, W, Q and P fragments and row-factor
+//     table, and chunk c+2's Tinv diag(b) fragments and V columns, from
+//     global memory straight into LDS (direct global-to-LDS loads, 1 KB per
+//     wave instruction, no register staging) and wait for them before the
+//     barrier.
 // Every LDS region is double-buffered by chunk parity; between two barriers
 // a slot is either only read or only written.
 // --------------------------------------------------------------------------
@@ -473,23 +516,20 @@ struct ScanSmem {
   Frag<E> kt[2][G::KT_FR * 64];        // K^T fragments
   Frag<E> wf[2][G::W_FR * 64];         // W fragments
   Frag<E> qf[2][G::Q_FR * 64];         // Q fragments
-  Frag<E> qk[2][G::QK_FR * 64];        // q.k fragments
   Frag<E> pf[2][G::QK_FR * 64];        // masked, decayed q.k fragments
+  Frag<E> tf[2][G::T_FR * 64];         // Tinv diag(b) fragments
   f32x4 uf[2][G::NS * G::CT * 64];     // Ut accumulator tiles
   E vr[2][C * G::BV];                  // the block's V columns, row-major
-  float gb[2][2][C] __attribute__((aligned(16)));    // g and b
-  // exp(g_r) and exp(min(g_L - g_r, 0)), both zero past the chunk end
-  float dtab[2][2][C] __attribute__((aligned(16)));
-  float gam[2];                        // exp(g_L)
+  // exp(g_r) [C], exp(min(g_L - g_r, 0)) [C], exp(g_L), 3 pad
+  float dtab[2][2 * C + 4] __attribute__((aligned(16)));
   float touch[kScanBlock / 64][64];    // landing place of the L2 warm-up loads
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Workgroup barrier for the scan and producer waves: it waits only for this
+// Workgroup barrier for the scan and Ut waves: it waits only for this
 // wave's LDS operations, not for global stores or L2 warm-up loads (nothing
-// in the workgroup reads those back); loads into registers are waited for
-// where their values are used.
+// in the workgroup reads those back).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // One direct global-to-LDS copy of up to 1 KB: lane l copies the 16 bytes
@@ -503,12 +543,9 @@ template <typename E, int D, int C>
 __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   constexpr int DT = G::DT, CT = G::CT, DKS = G::DKS, CKS = G::CKS, NS = G::NS, BV = G::BV;
-  // roles: NS scan waves, NLD loader waves (direct copies only, so that
-  // their stalls on the memory pipeline hold up nothing else) and NPROD
-  // producer waves
-  constexpr int NLD = 6;
-  constexpr int NPROD = kScanBlock / 64 - NS - NLD;
-  static_assert(NPROD >= 2, "a Ut wave and at least one q.k wave");
+  // roles: NS scan waves, NS Ut waves, and loader waves (direct copies only,
+  // so that their stalls on the memory pipeline hold up nothing else)
+  constexpr int NLD = kScanBlock / 64 - 2 * NS;
   constexpr int FB = (int)sizeof(Frag<E>) * 64;            // bytes per fragment
   constexpr int ESZ = (int)sizeof(E);
   __shared__ ScanSmem<E, D, C> sm;
@@ -516,8 +553,8 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   // the wave index in a scalar register, so that role and job selection
   // compile to scalar branches
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // the column blocks and V heads of one QK head, which read the same K^T,
-  // q.k and Q fragments, are consecutive logical ids and so share an XCD
+  // the column blocks and V heads of one QK head, which read the same K^T
+  // and Q fragments, are consecutive logical ids and so share an XCD
   const int64_t bid = xcd_local_id(blockIdx.x, gridDim.x);
   const int cb = (int)(bid % G::NCB);
   const int hv = (int)((bid / G::NCB) % a.h_v);
@@ -533,19 +570,18 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   const bool is_scan = wave < NS, is_loader = !is_scan && wave < NS + NLD;
   const int slice = wave;                      // scan waves: slice index
   const int lw = wave - NS;                    // loader waves: index
-  const int pw = wave - NS - NLD;              // producer waves: index
+  const int uw = wave - NS - NLD;              // Ut waves: slice index
   const int col0 = cb * BV;                    // first state column of this workgroup
   const int64_t state_base = (n * a.h_v + hv) * D * D;
 
-  // ---- direct copies into LDS: chunk xs's scan operands, chunk xp's
-  // producer data; the window's jobs are dealt round-robin to the loader
-  // waves ----
-  constexpr int B_KT = G::KT_FR * FB, B_W = G::W_FR * FB, B_Q = G::Q_FR * FB, B_QK = G::QK_FR * FB;
-  constexpr int B_V = C * BV * ESZ, B_G = C * 4;
+  // ---- direct copies into LDS: chunk xs's scan operands, chunk xp's Ut
+  // operands; the window's jobs are dealt round-robin to the loader waves ----
+  constexpr int B_KT = G::KT_FR * FB, B_W = G::W_FR * FB, B_Q = G::Q_FR * FB, B_P = G::QK_FR * FB;
+  constexpr int B_T = G::T_FR * FB, B_V = C * BV * ESZ, B_D = (2 * C + 4) * 4;
   constexpr int NREG = 7;
   constexpr int JOBS[NREG] = {(B_KT + 1023) / 1024, (B_W + 1023) / 1024, (B_Q + 1023) / 1024,
-                              (B_QK + 1023) / 1024, (B_V + 1023) / 1024, (B_G + 1023) / 1024,
-                              (B_G + 1023) / 1024};
+                              (B_P + 1023) / 1024,  (B_D + 1023) / 1024, (B_T + 1023) / 1024,
+                              (B_V + 1023) / 1024};
   constexpr int CUM[NREG] = {0, JOBS[0], JOBS[0] + JOBS[1], JOBS[0] + JOBS[1] + JOBS[2],
                              JOBS[0] + JOBS[1] + JOBS[2] + JOBS[3],
                              JOBS[0] + JOBS[1] + JOBS[2] + JOBS[3] + JOBS[4],
@@ -563,64 +599,57 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
                   reinterpret_cast<char*>(sm.wf[xs & 1]), B_W);
       copy_region(2, static_cast<const char*>(a.q_frag) + ((int64_t)xs * a.h_qk + hq) * B_Q,
                   reinterpret_cast<char*>(sm.qf[xs & 1]), B_Q);
+      copy_region(3, static_cast<const char*>(a.pmask) + ((int64_t)xs * a.h_v + hv) * B_P,
+                  reinterpret_cast<char*>(sm.pf[xs & 1]), B_P);
+      copy_region(4, reinterpret_cast<const char*>(a.dtab + ((int64_t)xs * a.h_v + hv) * (2 * C + 4)),
+                  reinterpret_cast<char*>(sm.dtab[xs & 1]), B_D);
     }
     if (xp < c1) {
-      copy_region(3, static_cast<const char*>(a.qk) + ((int64_t)xp * a.h_qk + hq) * B_QK,
-                  reinterpret_cast<char*>(sm.qk[xp & 1]), B_QK);
+      copy_region(5, static_cast<const char*>(a.tinv) + ((int64_t)xp * a.h_v + hv) * B_T,
+                  reinterpret_cast<char*>(sm.tf[xp & 1]), B_T);
       // the V columns, row i of the chunk at byte 16 l of its job; rows
       // past the chunk end repeat its last row (Tinv diag(b) has zero
       // columns there)
       const int p_start = chunk_start(xp), p_last = chunk_len(xp) - 1;
       char* vdst = reinterpret_cast<char*>(sm.vr[xp & 1]);
-      for (int jj = ((lw - CUM[4]) % NLD + NLD) % NLD; jj < JOBS[4]; jj += NLD) {
+      for (int jj = ((lw - CUM[6]) % NLD + NLD) % NLD; jj < JOBS[6]; jj += NLD) {
         const int o = 1024 * jj + 16 * lane;
         const int i = min(o / (BV * ESZ), p_last);
         const char* vsrc = static_cast<const char*>(a.v) +
                            (((int64_t)(p_start + i) * a.h_v + hv) * D + col0) * ESZ + o % (BV * ESZ);
         if (o < B_V) __builtin_amdgcn_global_load_lds(vsrc, (lds_ptr_t)(vdst + 1024 * jj), 16, 0, 0);
       }
-      copy_region(5, reinterpret_cast<const char*>(a.gate_prefix + ((int64_t)xp * a.h_v + hv) * C),
-                  reinterpret_cast<char*>(sm.gb[xp & 1][0]), B_G);
-      copy_region(6, reinterpret_cast<const char*>(a.beta_chunk + ((int64_t)xp * a.h_v + hv) * C),
-                  reinterpret_cast<char*>(sm.gb[xp & 1][1]), B_G);
     }
   };
-  // Tinv diag(b) fragments of chunk x into registers (the Ut wave)
-  auto load_tb = [&](Frag<E> (&tb)[G::T_FR], int x) __attribute__((always_inline)) {
-    const Frag<E>* tg = reinterpret_cast<const Frag<E>*>(a.tinv) + ((int64_t)min(x, c1 - 1) * a.h_v + hv) * G::T_FR * 64;
-#pragma unroll
-    for (int f = 0; f < G::T_FR; ++f) tb[f] = tg[f * 64 + lane];
-  };
 
-  // L2 warm-up, issued by the q.k producer waves after their chunk's work
-  // (they load nothing into registers, so nothing ever waits on these)
-  // three chunks ahead: one 4-byte load per 128-byte line of
-  // the chunk's streamed operands, each line touched by one of the
-  // workgroups that read it (per V head: W, Tinv diag(b), g and b, shared by
-  // the NCB column blocks; per QK head: K^T, Q and q.k, shared by the
-  // group's V heads too), plus this workgroup's own V rows. The loaded words
-  // land in a scratch LDS slot.
-  constexpr int B_T = G::T_FR * FB;
-  constexpr int LV = (B_W + B_T + 2 * B_G + 127) / 128;           // lines per (chunk, V head)
-  constexpr int LQ = (B_KT + B_Q + B_QK + 127) / 128;             // lines per (chunk, QK head)
+  // L2 warm-up, issued by the Ut waves after their chunk's work (they load
+  // nothing into registers, so nothing ever waits on these) three chunks
+  // ahead: one 4-byte load per 128-byte line of the chunk's streamed
+  // operands, each line touched by one of the workgroups that read it (per V
+  // head: W, P, the row-factor table and Tinv diag(b), shared by the NCB
+  // column blocks; per QK head: K^T and Q, shared by the group's V heads
+  // too), plus this workgroup's own V rows. The loaded words land in a
+  // scratch LDS slot.
+  constexpr int LV = (B_W + B_P + B_T + B_D + 127) / 128;        // lines per (chunk, V head)
+  constexpr int LQ = (B_KT + B_Q + 127) / 128;                   // lines per (chunk, QK head)
   const int gi = hv % a.group;
-  const int nv = (LV - cb + G::NCB - 1) / G::NCB;                 // this group's share of each
+  const int nv = (LV - cb + G::NCB - 1) / G::NCB;
   const int qs = gi * G::NCB + cb, qstride = a.group * G::NCB;
   const int nq = qs < LQ ? (LQ - qs + qstride - 1) / qstride : 0;
   auto line_addr = [&](int x, int t) -> const char* {
     if (t < nv) {
       const int o = 128 * (cb + G::NCB * t);
       return o < B_W ? static_cast<const char*>(a.w) + ((int64_t)x * a.h_v + hv) * B_W + o
-           : o < B_W + B_T ? static_cast<const char*>(a.tinv) + ((int64_t)x * a.h_v + hv) * B_T + (o - B_W)
-           : o < B_W + B_T + B_G ? reinterpret_cast<const char*>(a.gate_prefix + ((int64_t)x * a.h_v + hv) * C) + (o - B_W - B_T)
-           : reinterpret_cast<const char*>(a.beta_chunk + ((int64_t)x * a.h_v + hv) * C) + min(o - B_W - B_T - B_G, B_G - 4);
+           : o < B_W + B_P ? static_cast<const char*>(a.pmask) + ((int64_t)x * a.h_v + hv) * B_P + (o - B_W)
+           : o < B_W + B_P + B_T ? static_cast<const char*>(a.tinv) + ((int64_t)x * a.h_v + hv) * B_T + (o - B_W - B_P)
+           : reinterpret_cast<const char*>(a.dtab + ((int64_t)x * a.h_v + hv) * (2 * C + 4)) +
+                 min(o - B_W - B_P - B_T, B_D - 4);
     }
     t -= nv;
     if (t < nq) {
       const int o = 128 * (qs + qstride * t);
       return o < B_KT ? static_cast<const char*>(a.key_t) + ((int64_t)x * a.h_qk + hq) * B_KT + o
-           : o < B_KT + B_Q ? static_cast<const char*>(a.q_frag) + ((int64_t)x * a.h_qk + hq) * B_Q + (o - B_KT)
-           : static_cast<const char*>(a.qk) + ((int64_t)x * a.h_qk + hq) * B_QK + min(o - B_KT - B_Q, B_QK - 4);
+           : static_cast<const char*>(a.q_frag) + ((int64_t)x * a.h_qk + hq) * B_Q + min(o - B_KT, B_Q - 4);
     }
     t -= nq;
     const int i = min(t, chunk_len(x) - 1);
@@ -629,7 +658,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   auto warm = [&](int x) __attribute__((always_inline)) {
     if (x >= c1) return;
     const int total = nv + nq + C;
-    for (int t = 64 * (pw - 1) + lane; t < total; t += 64 * (NPROD - 1))
+    for (int t = 64 * uw + lane; t < total; t += 64 * NS)
       __builtin_amdgcn_global_load_lds(line_addr(x, t), (lds_ptr_t)sm.touch[wave], 4, 0, 0);
   };
 
@@ -676,9 +705,9 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       }
     }
     // U = Ut - W S; the inter-chunk output takes exp(g_r); the row factors
-    // come from the producers' per-chunk tables (zero past the chunk end)
-    const float* ea = sm.dtab[par][0];
-    const float* ed = sm.dtab[par][1];
+    // come from the chunk's table (zero past the chunk end)
+    const float* ea = sm.dtab[par];
+    const float* ed = sm.dtab[par] + C;
     f32x4 U[CT];
 #pragma unroll
     for (int t = 0; t < CT; ++t) {
@@ -707,7 +736,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       for (int nt = 0; nt < CT; ++nt)
         if (!causal_zero(nt, ks)) O[nt] = mma(Uk[ks], pa[nt], O[nt]);
     }
-    const float gam = sm.gam[par];
+    const float gam = sm.dtab[par][2 * C];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) S[dt] *= gam;
 #pragma unroll
@@ -731,91 +760,44 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     }
   };
 
-  // producer work for chunk p (whose q.k, V, g and b are in slot p & 1):
-  // the Ut wave (producer 0) forms every slice's Ut tiles from Tinv diag(b)
-  // in `tb`; the others each take masked, decayed q.k fragments in turn,
-  // and the last also the row-factor tables.
-  auto produce_chunk = [&](int p, const Frag<E> (&tb)[G::T_FR]) __attribute__((always_inline)) {
+  // Ut wave uw: chunk p's Ut tiles Tinv diag(b) V of slice uw; V's
+  // fragments (col = state column, k = token) are gathered from the
+  // row-major V columns
+  auto produce_chunk = [&](int p) __attribute__((always_inline)) {
     const int par = p & 1;
-    const int len = chunk_len(p);
-    const float* gp = sm.gb[par][0];
-    if (pw == NPROD - 1 && lane < C) {
-      const float gl = gp[len - 1], valid = (float)(lane < len);
-      sm.dtab[par][0][lane] = __expf(gp[lane]) * valid;
-      sm.dtab[par][1][lane] = __expf(fminf(gl - gp[lane], 0.f)) * valid;
-      if (lane == 0) sm.gam[par] = __expf(gl);
-    }
-    if (pw == 0) {
-      // Ut = Tinv diag(b) V, slice by slice; V's fragments (col = state
-      // column, k = token) are gathered from the row-major V columns
-      const E* vr = sm.vr[par];
+    const E* vr = sm.vr[par];
+    Frag<E> vf[CKS];
 #pragma unroll
-      for (int sl = 0; sl < NS; ++sl) {
-        Frag<E> vf[CKS];
-#pragma unroll
-        for (int s = 0; s < CKS; ++s) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int i = frag_k(s, quad, e);
-            vf[s][e] = (i < C) ? vr[i * BV + 16 * sl + l16] : to_e<E>(0.f);
-          }
-        }
-        f32x4 acc[CT];
-#pragma unroll
-        for (int rt = 0; rt < CT; ++rt) acc[rt] = zero4();
-#pragma unroll
-        for (int s = 0; s < CKS; ++s) {
-#pragma unroll
-          for (int rt = 0; rt < CT; ++rt)
-            if (!causal_zero(rt, s)) acc[rt] = mma(tb[rt * CKS + s], vf[s], acc[rt]);
-        }
-#pragma unroll
-        for (int rt = 0; rt < CT; ++rt) sm.uf[par][(sl * CT + rt) * 64 + lane] = acc[rt];
-      }
-      return;
-    }
-    // q.k fragments that the causal mask does not zero, in order
-    constexpr int NPF = [] {
-      int k = 0;
-      for (int f = 0; f < CT * CKS; ++f) k += causal_zero(f / CKS, f % CKS) ? 0 : 1;
-      return k;
-    }();
-    for (int item = pw - 1; item < NPF; item += NPROD - 1) {
-      int nt = 0, s = 0;
-      {
-        int k = item;
-#pragma unroll
-        for (int f = 0; f < CT * CKS; ++f) {
-          if (causal_zero(f / CKS, f % CKS)) continue;
-          if (k == 0) { nt = f / CKS; s = f % CKS; }
-          --k;
-        }
-      }
-      const int r = 16 * nt + l16;
-      const float gr = gp[r], vr = (float)(r < len);
-      const Frag<E> raw = sm.qk[par][(nt * CKS + s) * 64 + lane];
-      // g of the fragment's keys: two runs of four
-      const f32x4 g0 = *reinterpret_cast<const f32x4*>(&gp[32 * s + 4 * quad]);
-      const f32x4 g1 = (32 * s + 16 < C) ? *reinterpret_cast<const f32x4*>(&gp[32 * s + 16 + 4 * quad]) : zero4();
-      Frag<E> v;
+    for (int s = 0; s < CKS; ++s) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int j = frag_k(s, quad, e);
-        // the exponent is clamped at 0 so that masked entries (j > r,
-        // where g_r - g_j >= 0) cannot overflow before being zeroed
-        const float m = (float)(j <= r) * vr;
-        v[e] = to_e<E>(to_f(raw[e]) * (__expf(fminf(gr - (e < 4 ? g0[e] : g1[e - 4]), 0.f)) * m));
+        const int i = frag_k(s, quad, e);
+        vf[s][e] = (i < C) ? vr[i * BV + 16 * uw + l16] : to_e<E>(0.f);
       }
-      sm.pf[par][(nt * CKS + s) * 64 + lane] = v;
     }
+    f32x4 acc[CT];
+#pragma unroll
+    for (int rt = 0; rt < CT; ++rt) acc[rt] = zero4();
+#pragma unroll
+    for (int s = 0; s < CKS; ++s) {
+      Frag<E> tb[CT];
+#pragma unroll
+      for (int rt = 0; rt < CT; ++rt)
+        if (!causal_zero(rt, s)) tb[rt] = sm.tf[par][(rt * CKS + s) * 64 + lane];
+#pragma unroll
+      for (int rt = 0; rt < CT; ++rt)
+        if (!causal_zero(rt, s)) acc[rt] = mma(tb[rt], vf[s], acc[rt]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < CT; ++rt) sm.uf[par][(uw * CT + rt) * 64 + lane] = acc[rt];
   };
 
   // The three roles run separate loops with the same barrier sequence (one
   // after the prologue, one per iteration), so each keeps only its own
   // registers live. Iteration c: the scan waves process chunk c; the
-  // loaders copy chunk c+1's scan operands and chunk c+2's producer data
-  // into LDS and wait for them; the producers produce chunk c+1 (and the
-  // Ut wave loads chunk c+2's Tinv diag(b)).
+  // loaders copy chunk c+1's scan operands and chunk c+2's Ut operands into
+  // LDS and wait for them; the Ut waves form chunk c+1's Ut tiles, then
+  // warm L2 for chunk c+3.
   if (c1 > c0) {
     if (is_scan) {
 #pragma unroll
@@ -840,8 +822,8 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
         }
       }
     } else if (is_loader) {
-      // prologue: chunk c0's producer data (the scan-operand jobs are
-      // switched off by passing a chunk past the end)
+      // prologue: chunk c0's Ut operands (the scan-operand jobs are switched
+      // off by passing a chunk past the end)
       copy_window(c1, c0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
@@ -851,23 +833,13 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
         __syncthreads();
       }
     } else {
-      Frag<E> ta[G::T_FR], tbn[G::T_FR];
-      if (pw == 0) load_tb(ta, c0);
-      else { warm(c0 + 1); warm(c0 + 2); }
+      warm(c0 + 1);
+      warm(c0 + 2);
       __syncthreads();
-      // iteration c: produce chunk c+1 from one register set while chunk
-      // c+2's Tinv diag(b) arrives in the other
-      for (int c = c0 - 1; c < c1; c += 2) {
-        if (pw == 0) load_tb(tbn, c + 2);
-        if (c + 1 < c1) produce_chunk(c + 1, ta);
-        if (pw != 0) warm(c + 3);
+      for (int c = c0 - 1; c < c1; ++c) {
+        if (c + 1 < c1) produce_chunk(c + 1);
+        warm(c + 3);
         lds_barrier();
-        if (c + 1 < c1) {
-          if (pw == 0) load_tb(ta, c + 3);
-          if (c + 2 < c1) produce_chunk(c + 2, tbn);
-          if (pw != 0) warm(c + 4);
-          lds_barrier();
-        }
       }
     }
   } else if (is_scan && a.final_state) {

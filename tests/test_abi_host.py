@@ -78,7 +78,7 @@ def test_dims_validation(lib, kw, status):
 def test_workspace_size_formula(lib):
     # regions: chunk table, sequence offsets, gate prefixes, per-chunk b,
     # Tinv diag(b) and W fragments (per V head), K^T, q.k and Q fragments
-    # (per QK head); each
+    # (per QK head), masked q.k fragments and row factors (per V head); each
     # padded to 256 bytes. Fragments of a C x C tile take C*C elements, of a
     # D x C tile D*C elements (C = 64 is a whole number of 32-steps).
     d = dims(num_seqs=3, total_tokens=1000)
@@ -87,13 +87,13 @@ def test_workspace_size_formula(lib):
         return (x + 255) // 256 * 256
     want = (up(nc * 16) + up(4 * 4) + 2 * up(nc * 48 * 64 * 4) + up(nc * 48 * 64 * 64 * 2)
             + up(nc * 48 * 64 * 128 * 2) + up(nc * 16 * 128 * 64 * 2) + up(nc * 16 * 64 * 64 * 2)
-            + up(nc * 16 * 64 * 128 * 2))
+            + up(nc * 16 * 64 * 128 * 2) + up(nc * 48 * 64 * 64 * 2) + up(nc * 48 * (2 * 64 + 4) * 4))
     assert ws_bytes(lib, d) == want
     lay = B.GdnWorkspaceLayout()
     assert lib.gdn_chunk_fwd_workspace_layout(ctypes.byref(d), ctypes.byref(lay)) == 0
     assert lay.total == want and lay.max_chunks == nc
     offs = [lay.chunk_table, lay.seq_chunk_offset, lay.gate_prefix, lay.beta_chunk, lay.tinv,
-            lay.w, lay.key_t, lay.qk, lay.q_frag]
+            lay.w, lay.key_t, lay.qk, lay.q_frag, lay.pmask, lay.dtab]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
 
 

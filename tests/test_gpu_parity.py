@@ -199,6 +199,10 @@ def test_stage_outputs_match_oracle_chunks(chunk):
         nc, 2, ct, cks, 64, 8).double().numpy()
     qf = region(lay.q_frag, nc * 2 * ct * 4 * 512, torch.bfloat16).view(
         nc, 2, ct, 4, 64, 8).double().numpy()
+    pm = region(lay.pmask, nc * 6 * ct * cks * 512, torch.bfloat16).view(
+        nc, 6, ct, cks, 64, 8).double().numpy()
+    dtab = region(lay.dtab, nc * 6 * (2 * chunk + 4), torch.float32).view(
+        nc, 6, 2 * chunk + 4).double().numpy()
     _, _, stages = O.chunkwise(**oracle_args(inp), chunk=chunk, keep_stages=True)
     q64, k64, b64 = np64(inp["q"]), np64(inp["k"]), np64(inp["beta"])
     n_seq0 = -(-77 // chunk)
@@ -217,6 +221,20 @@ def test_stage_outputs_match_oracle_chunks(chunk):
             wm = unfrag(wf[c, h], chunk, 128)              # [token r][d]
             check(wm[:L], st["W"][h], torch.bfloat16, f"W chunk {c} head {h}")
             assert (wm[L:] == 0).all()
+            # masked, decayed q.k: P[r][j] = q_r . k_j exp(g_r - g_j) for j <= r
+            gh = st["g"][h]
+            hq_ = h // 3
+            qkd = q64[t0:t0 + L, hq_] @ k64[t0:t0 + L, hq_].T
+            dec = np.exp(np.minimum(gh[:, None] - gh[None, :], 0.0))
+            want_p = np.tril(qkd * dec)
+            pmm = unfrag(pm[c, h], chunk, chunk)           # [query r][key j]
+            check(pmm[:L, :L], want_p, torch.bfloat16, f"P chunk {c} head {h}")
+            assert (pmm[L:] == 0).all() and (pmm[:, L:] == 0).all()
+            # row factors exp(g_r), exp(g_L - g_r) (zero past the end), exp(g_L)
+            check(dtab[c, h, :L], np.exp(gh), torch.float32, f"exp(g) chunk {c} head {h}")
+            check(dtab[c, h, chunk:chunk + L], np.exp(gh[-1] - gh), torch.float32, f"exp(g_L-g) chunk {c} head {h}")
+            assert (dtab[c, h, L:chunk] == 0).all() and (dtab[c, h, chunk + L:2 * chunk] == 0).all()
+            check(dtab[c, h, 2 * chunk:2 * chunk + 1], np.exp(gh[-1:]), torch.float32, f"exp(g_L) chunk {c} head {h}")
         for hq in range(2):
             ktm = unfrag(kt[c, hq], 128, chunk)            # [d][i]
             assert np.array_equal(ktm[:, :L], k64[t0:t0 + L, hq].T) and (ktm[:, L:] == 0).all()

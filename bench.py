@@ -49,13 +49,16 @@ def algorithmic_work(T, HQ, HV, D, C, N, decode_batch):
         "gdn_k1_chunk_prep": (T * HQ * 2 * C * dk,
                               2 * T * HQ * dk * e + gates + T * HQ * (2 * dk + C) * e + gates),
         # K K^T per QK head, the triangular inverse and W per V head; reads k,
-        # K^T, g, b; writes Tinv diag(b) and W
+        # K^T, q.k, g, b; writes Tinv diag(b), W, the masked q.k fragments P
+        # and the row-factor table (2C + 4 fp32 per chunk and V head)
         "gdn_k2_inverse_w": (T * (HQ * 2 * C * dk + HV * (C * C / 3.0 + 2 * C * dk)),
-                             2 * T * HQ * dk * e + gates + T * HV * (C + dk) * e),
-        # Ut, W S, Q S, K^T U, (Q K^T) U per V head; reads q, v, K^T, q.k,
-        # Tinv diag(b), W, g, b and the initial states; writes o, final states
+                             T * HQ * (2 * dk + C) * e + gates
+                             + T * HV * (2 * C + dk) * e + T * HV * (2 * C + 4) * 4 / C),
+        # Ut, W S, Q S, K^T U, P U per V head; reads Q, K^T, P, V, Tinv
+        # diag(b), W, the row factors and the initial states; writes o and the
+        # final states
         "gdn_k3_scan": (T * HV * (6 * dk * dv + 4 * C * dv),
-                        T * HQ * (2 * dk + C) * e + T * HV * (dv + C + dk) * e + gates
+                        T * HQ * 2 * dk * e + T * HV * (dv + 2 * C + dk) * e + T * HV * (2 * C + 4) * 4 / C
                         + T * HV * dv * e + 2 * N * HV * dk * dv * 4),
     }
     per_token = HV * (6 * dk * dv + 2 * C * dk + 4 * C * dv + C * C / 3.0) + HQ * 4 * C * dk

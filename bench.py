@@ -117,6 +117,40 @@ def cpu_baseline(inp, seconds):
     return done / dt, done, dt
 
 
+def verify_bench(gdn, I, dev, decode_ms, kt=4, reps=5):
+    """Speculative verify of `kt` drafted tokens for the 256-sequence batch in
+    one gdn_decode_multi pass: with per-token snapshots (state read once,
+    kt states written) and committing in place (state read and written
+    once). Timed outside the prefill region; HBM bytes are the state traffic
+    plus the per-token inputs and outputs."""
+    import torch
+    spec = I.WORKLOADS["decode_256"]
+    dec = I.workload_inputs("decode_256", steps=kt)
+    args = [dec[x].to(dev) for x in ("q", "k", "v", "log_alpha", "beta")]
+    state = dec["state0"].to(dev)
+    snaps = torch.empty((kt,) + tuple(state.shape), dtype=torch.float32, device=dev)
+    o = torch.empty_like(args[2])
+    nb, hq, hv, d = spec["batch"], spec["h_qk"], spec["h_v"], spec["d"]
+    sbytes = nb * hv * d * d * 4
+    io = kt * nb * (2 * hq * d * 2 + 2 * hv * d * 2 + 2 * hv * 4)
+    out = {"tokens_per_seq": kt, "sequences": nb}
+    for name, snap, nbytes in (("snapshots", snaps, sbytes * (1 + kt) + io), ("commit", None, 2 * sbytes + io)):
+        gdn.gdn_decode_multi(*args, state, o=o, snapshots=snap)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(torch.cuda.current_stream(dev))
+        for _ in range(reps):
+            gdn.gdn_decode_multi(*args, state, o=o, snapshots=snap)
+        e1.record(torch.cuda.current_stream(dev))
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 4), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (ms * 1e-3) / PEAK_HBM_BYTES, 4),
+                     "tokens_per_s": round(kt * nb / (ms * 1e-3), 1)}
+    out["commit_vs_single_steps"] = round(kt * decode_ms / out["commit"]["ms"], 3)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +294,7 @@ def main():
             "value": round(rate, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n_tok} tokens of the same 64K-token input, all 48 V heads, "
                       f"token-serial fp64 recurrence, one thread, {secs:.1f} s"}
+    line["decode_verify"] = verify_bench(gdn, I, dev, decode_ms)
     print(json.dumps(line), flush=True)
 
 

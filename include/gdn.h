@@ -137,6 +137,32 @@ gdn_status_t gdn_decode_step(const gdn_dims_t* dims,
                              const float* log_alpha, const float* beta,
                              float* state, void* o, hipStream_t stream);
 
+/*
+ * Speculative multi-token verify for decode: K drafted tokens per sequence,
+ * applied in order as K successive steps of the single-token update of
+ * section 2.1 (the same update as gdn_decode_step), in one pass over the
+ * state. Result j equals the j-th of K gdn_decode_step calls on the same
+ * inputs.
+ *
+ *  num_tokens K >= 1 (K * N must fit int32)
+ *  q, k       [K, N, h_qk, dk] dtype   (token j's gdn_decode_step inputs at j)
+ *  v          [K, N, h_v, dv]  dtype
+ *  log_alpha  [K, N, h_v] fp32;  beta [K, N, h_v] fp32
+ *  state      [N, h_v, dk, dv] fp32
+ *  o          [K, N, h_v, dv] dtype, written; must not alias any input
+ *  snapshots  [K, N, h_v, dk, dv] fp32 or NULL. Non-NULL: snapshot j gets the
+ *             state after token j and `state` is only read, so the caller
+ *             can continue from any accepted prefix (from `state` itself if
+ *             none is accepted). NULL: `state` is overwritten with the state
+ *             after all K tokens. Must not alias `state`.
+ * dims->total_tokens must equal dims->num_seqs; dims->chunk is ignored.
+ */
+gdn_status_t gdn_decode_multi(const gdn_dims_t* dims, int32_t num_tokens,
+                              const void* q, const void* k, const void* v,
+                              const float* log_alpha, const float* beta,
+                              float* state, void* o, float* snapshots,
+                              hipStream_t stream);
+
 /* Static name of a status code. */
 const char* gdn_status_string(gdn_status_t status);
 

@@ -19,7 +19,7 @@ STATUS = {0: "GDN_SUCCESS", 1: "GDN_ERROR_INVALID_VALUE", 2: "GDN_ERROR_NOT_SUPP
 
 # Names the library must export (every function declared in include/gdn.h).
 EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_stages", "gdn_chunk_fwd_workspace_bytes",
-           "gdn_decode_step", "gdn_status_string", "gdn_last_error_message",
+           "gdn_decode_step", "gdn_decode_multi", "gdn_status_string", "gdn_last_error_message",
            "gdn_chunk_fwd_workspace_layout")
 
 
@@ -71,6 +71,8 @@ def load_library(path=None):
     lib.gdn_chunk_fwd_workspace_layout.restype = i32
     lib.gdn_decode_step.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_decode_step.restype = i32
+    lib.gdn_decode_multi.argtypes = [dims_p, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_decode_multi.restype = i32
     lib.gdn_status_string.argtypes = [i32]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error_message.argtypes = []
@@ -200,4 +202,36 @@ def gdn_decode_step(q, k, v, log_alpha, beta, state, o=None):
     dims = make_dims(n, n, h_qk, h_v, d, v.shape[2], 0, q.dtype)
     _check(lib.gdn_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                                _ptr(beta), _ptr(state), _ptr(o), _stream(dev)))
+    return o
+
+
+def gdn_decode_multi(q, k, v, log_alpha, beta, state, o=None, snapshots=None):
+    """K drafted tokens per sequence through gdn_decode_multi. q, k [K,N,Hqk,d];
+    v [K,N,Hv,d]; log_alpha, beta [K,N,Hv] fp32; state [N,Hv,d,d] fp32.
+    With `snapshots` ([K,N,Hv,d,d] fp32) the state after each token goes there
+    and `state` is only read; without, `state` ends as the state after all K
+    tokens. Returns o [K,N,Hv,d]."""
+    lib = load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_decode_multi needs CUDA (HIP) tensors")
+    kt, n, h_qk, d = q.shape
+    h_v, dv = v.shape[2], v.shape[3]
+    _need(q, "q", dev)
+    _need(k, "k", dev, q.dtype, (kt, n, h_qk, d))
+    _need(v, "v", dev, q.dtype, (kt, n, h_v, dv))
+    _need(log_alpha, "log_alpha", dev, torch.float32, (kt, n, h_v))
+    _need(beta, "beta", dev, torch.float32, (kt, n, h_v))
+    _need(state, "state", dev, torch.float32, (n, h_v, d, dv))
+    if q.dtype not in GDN_DTYPE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if o is None:
+        o = torch.empty_like(v)
+    _need(o, "o", dev, v.dtype, tuple(v.shape))
+    if snapshots is not None:
+        _need(snapshots, "snapshots", dev, torch.float32, (kt, n, h_v, d, dv))
+    dims = make_dims(n, n, h_qk, h_v, d, dv, 0, q.dtype)
+    _check(lib.gdn_decode_multi(ctypes.byref(dims), int(kt), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                _ptr(beta), _ptr(state), _ptr(o),
+                                _ptr(snapshots) if snapshots is not None else None, _stream(dev)))
     return o

@@ -234,7 +234,46 @@ gdn_status_t gdn_decode_step(const gdn_dims_t* dims, const void* q, const void* 
   a.h_qk = d.h_qk;
   a.h_v = d.h_v;
   a.group = d.h_v / d.h_qk;
+  a.num_tokens = 1;
+  a.snapshots = nullptr;
   return launch_status(gdn::launch_decode(a, d.dtype, d.dk, stream), "gdn_decode_step launch");
+}
+
+gdn_status_t gdn_decode_multi(const gdn_dims_t* dims, int32_t num_tokens, const void* q, const void* k,
+                              const void* v, const float* log_alpha, const float* beta, float* state,
+                              void* o, float* snapshots, hipStream_t stream) {
+  gdn_status_t st = check_dims(dims, true);
+  if (st != GDN_SUCCESS) return st;
+  const gdn_dims_t& d = *dims;
+  if (num_tokens < 1) return fail(GDN_ERROR_INVALID_VALUE, "num_tokens must be >= 1 (got %d)", num_tokens);
+  if ((int64_t)num_tokens * d.num_seqs > INT32_MAX)
+    return fail(GDN_ERROR_NOT_SUPPORTED, "num_tokens * num_seqs must fit int32");
+  const void* need[] = {q, k, v, state, o, log_alpha, beta};
+  const char* names[] = {"q", "k", "v", "state", "o", "log_alpha", "beta"};
+  for (int i = 0; i < 7; ++i) {
+    const size_t al = i < 5 ? 16 : 4;
+    if (!need[i]) return fail(GDN_ERROR_INVALID_VALUE, "%s is NULL", names[i]);
+    if (!aligned(need[i], al)) return fail(GDN_ERROR_INVALID_VALUE, "%s is not %zu-byte aligned", names[i], al);
+  }
+  if (o == q || o == k || o == v || o == log_alpha || o == beta || o == state || (snapshots && o == snapshots))
+    return fail(GDN_ERROR_INVALID_VALUE, "o must not alias an input");
+  if (snapshots && !aligned(snapshots, 16)) return fail(GDN_ERROR_INVALID_VALUE, "snapshots is not 16-byte aligned");
+  if (snapshots == state) return fail(GDN_ERROR_INVALID_VALUE, "snapshots must not alias state");
+  gdn::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_alpha = log_alpha;
+  a.beta = beta;
+  a.state = state;
+  a.o = o;
+  a.num_seqs = d.num_seqs;
+  a.h_qk = d.h_qk;
+  a.h_v = d.h_v;
+  a.group = d.h_v / d.h_qk;
+  a.num_tokens = num_tokens;
+  a.snapshots = snapshots;
+  return launch_status(gdn::launch_decode_multi(a, d.dtype, d.dk, stream), "gdn_decode_multi launch");
 }
 
 }  // extern "C"

@@ -89,6 +89,89 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
   }
 }
 
+// Speculative multi-token verify: K drafted tokens per sequence applied in
+// order, K successive steps of the update above in one pass over the state.
+// The workgroup's state slice stays in registers across the K tokens; each
+// token's column sums are reduced through LDS buffers alternating by token
+// parity (one barrier per token). Token j's output is written as it is
+// formed. With a snapshot buffer, the state after each token goes to
+// snapshot j and `state` is only read (so a caller can keep any accepted
+// prefix); without one, the final state replaces `state`. Each token's
+// arithmetic is the single-step kernel's, term for term.
+template <typename E, int D>
+__global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_multi(const DecodeArgs a) {
+  constexpr int CG = D / 4, RG = DecodeShape<D>::RG, RPT = D / RG;
+  __shared__ f32x4 red_p[2][RG][CG];
+  __shared__ f32x4 red_r[2][RG][CG];
+  __shared__ float red_kq[2][RG];
+  const int64_t nh = blockIdx.x;                 // sequence * h_v + V head
+  const int64_t n = nh / a.h_v;
+  const int hv = (int)(nh % a.h_v);
+  const int hq = hv / a.group;
+  const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
+  const int64_t tok_v = a.num_seqs * a.h_v;      // [N, HV] entries per token
+  const int64_t tok_q = a.num_seqs * a.h_qk;     // [N, HQ] entries per token
+
+  f32x4* sp = reinterpret_cast<f32x4*>(a.state + nh * D * D) + (rg * RPT) * CG + cg;
+  f32x4 s[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) s[r] = __builtin_nontemporal_load(sp + r * CG);
+
+  for (int j = 0; j < a.num_tokens; ++j) {
+    const int par = j & 1;
+    const E* kp = static_cast<const E*>(a.k) + (j * tok_q + n * a.h_qk + hq) * D + rg * RPT;
+    const E* qp = static_cast<const E*>(a.q) + (j * tok_q + n * a.h_qk + hq) * D + rg * RPT;
+    float kk[RPT], qq[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) { kk[r] = to_f(kp[r]); qq[r] = to_f(qp[r]); }
+    f32x4 p = zero4(), rq = zero4();
+    float kq = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      p += s[r] * kk[r];
+      rq += s[r] * qq[r];
+      kq += kk[r] * qq[r];
+    }
+    red_p[par][rg][cg] = p;
+    red_r[par][rg][cg] = rq;
+    if (cg == 0) red_kq[par][rg] = kq;
+    __syncthreads();
+    p = zero4();
+    rq = zero4();
+    kq = 0.f;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      p += red_p[par][g][cg];
+      rq += red_r[par][g][cg];
+      kq += red_kq[par][g];
+    }
+    const int64_t tv = j * tok_v + nh;
+    const float alpha = expf(a.log_alpha[tv]);
+    const float beta = a.beta[tv];
+    const E* vp = static_cast<const E*>(a.v) + tv * D + 4 * cg;
+    f32x4 u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = beta * (to_f(vp[e]) - alpha * p[e]);
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) s[r] = s[r] * alpha + u * kk[r];
+    if (a.snapshots) {
+      f32x4* snp = reinterpret_cast<f32x4*>(a.snapshots + tv * D * D) + (rg * RPT) * CG + cg;
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) __builtin_nontemporal_store(s[r], snp + r * CG);
+    }
+    if (rg == 0) {
+      Half<E> h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = to_e<E>(alpha * rq[e] + u[e] * kq);
+      *reinterpret_cast<Half<E>*>(static_cast<E*>(a.o) + tv * D + 4 * cg) = h;
+    }
+  }
+  if (!a.snapshots) {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) __builtin_nontemporal_store(s[r], sp + r * CG);
+  }
+}
+
 template <typename E, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   constexpr int threads = (D / 4) * DecodeShape<D>::RG;
@@ -97,7 +180,26 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename E, int D>
+hipError_t launch_decode_multi_t(const DecodeArgs& a, hipStream_t s) {
+  constexpr int threads = (D / 4) * DecodeShape<D>::RG;
+  const unsigned blocks = (unsigned)(a.num_seqs * a.h_v);
+  gdn_kd_decode_multi<E, D><<<dim3(blocks), dim3(threads), 0, s>>>(a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_decode_multi(const DecodeArgs& a, int dtype, int head_dim, hipStream_t s) {
+  if (dtype == 1) {
+    if (head_dim == 128) return launch_decode_multi_t<bf16_t, 128>(a, s);
+    if (head_dim == 16) return launch_decode_multi_t<bf16_t, 16>(a, s);
+  } else {
+    if (head_dim == 128) return launch_decode_multi_t<float, 128>(a, s);
+    if (head_dim == 16) return launch_decode_multi_t<float, 16>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t s) {
   if (dtype == 1) {

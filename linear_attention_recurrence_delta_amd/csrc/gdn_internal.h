@@ -51,6 +51,11 @@ struct DecodeArgs {
   int32_t h_qk;
   int32_t h_v;
   int32_t group;
+  // multi-token verify only: tokens per sequence (inputs and o gain a
+  // leading [K] dimension) and the per-token states [K, N, HV, D, D], or
+  // null to update `state` in place
+  int32_t num_tokens;
+  float* snapshots;
 };
 
 // Prefill launch stages (1-based): 1 chunk preparation (table, gate prefix sums,
@@ -65,5 +70,6 @@ bool prefill_supported(int dtype, int head_dim, int chunk);
 hipError_t launch_prefill(const PrefillArgs& args, int dtype, int head_dim, int chunk,
                           hipStream_t stream, int first_stage, int last_stage);
 hipError_t launch_decode(const DecodeArgs& args, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_decode_multi(const DecodeArgs& args, int dtype, int head_dim, hipStream_t stream);
 
 }  // namespace gdn

@@ -159,6 +159,26 @@ def test_decode_validation(lib):
     assert call(dims(num_seqs=4, total_tokens=4, dk=32, dv=32)) == NOT_SUPPORTED
 
 
+def test_decode_multi_validation(lib):
+    vp = ctypes.c_void_p
+    def call(d, kt=3, q=FAKE, k=FAKE, v=FAKE, la=FAKE, b=FAKE, s=FAKE * 8, o=FAKE * 2, snap=None):
+        return lib.gdn_decode_multi(ctypes.byref(d), kt, vp(q), vp(k), vp(v), vp(la), vp(b), vp(s),
+                                    vp(o), vp(snap), None)
+    d = dims(num_seqs=4, total_tokens=4)
+    assert call(d, kt=0) == INVALID
+    assert "num_tokens" in lib.gdn_last_error_message().decode()
+    assert call(d, kt=-2) == INVALID
+    assert call(dims(num_seqs=4, total_tokens=5)) == INVALID
+    assert call(d, v=None) == INVALID
+    assert call(d, s=FAKE * 8 + 4) == INVALID
+    assert call(d, o=FAKE * 8) == INVALID                        # o aliases state
+    assert call(d, snap=FAKE * 8) == INVALID                     # snapshots alias state
+    assert call(d, snap=FAKE * 16, o=FAKE * 16) == INVALID       # o aliases snapshots
+    assert call(d, snap=FAKE * 16 + 8) == INVALID                # misaligned snapshots
+    assert call(dims(num_seqs=4, total_tokens=4, dk=32, dv=32)) == NOT_SUPPORTED
+    assert call(dims(num_seqs=1 << 20, total_tokens=1 << 20), kt=1 << 12) == NOT_SUPPORTED
+
+
 def test_status_strings(lib):
     for code, name in B.STATUS.items():
         assert lib.gdn_status_string(code).decode() == name

@@ -328,3 +328,46 @@ def test_decode_matches_prefill_of_same_tokens():
     o_dec = torch.stack(outs).transpose(0, 1).reshape(n * steps, 6, 128)
     check(o_dec, np64(o_pf), torch.bfloat16, "decode vs prefill o")
     check(state, np64(f_pf), torch.bfloat16, "decode vs prefill state")
+
+
+# --- speculative multi-token verify (gdn_decode_multi) --------------------------
+
+@pytest.mark.parametrize("kt", [1, 4])
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (128, "f32"), (16, "bf16"), (16, "f32")])
+def test_decode_multi_equals_single_steps(d, dtype, kt):
+    say(f"decode_multi K={kt} N=5 d={d} {dtype} vs single steps")
+    inp = I.make_decode(40 + d + kt, 5, kt, 2, 6, d, dtype)
+    args = [inp[n].to(DEV) for n in ("q", "k", "v", "log_alpha", "beta")]
+    st1 = inp["state0"].to(DEV)
+    o1, states = [], []
+    for t in range(kt):
+        o1.append(gdn.gdn_decode_step(*[a[t] for a in args], st1))
+        states.append(st1.clone())
+    st2 = inp["state0"].to(DEV)
+    snaps = torch.full((kt,) + tuple(st2.shape), float("nan"), dtype=torch.float32, device=DEV)
+    o2 = gdn.gdn_decode_multi(*args, st2, snapshots=snaps)
+    st3 = inp["state0"].to(DEV)
+    o3 = gdn.gdn_decode_multi(*args, st3)
+    torch.cuda.synchronize()
+    # with snapshots the state is only read; without, it ends after the last token
+    assert torch.equal(st2, inp["state0"].to(DEV))
+    assert torch.equal(st3, states[-1])
+    for t in range(kt):
+        assert torch.equal(o2[t], o1[t]) and torch.equal(o3[t], o1[t]), f"o token {t}"
+        assert torch.equal(snaps[t], states[t]), f"snapshot {t}"
+
+
+def test_decode_multi_matches_oracle():
+    say("decode_multi K=8 N=3 d=128 bf16 vs oracle")
+    kt = 8
+    inp = I.make_decode(51, 3, kt, 2, 6, 128, "bf16")
+    args = [inp[n].to(DEV) for n in ("q", "k", "v", "log_alpha", "beta")]
+    state = inp["state0"].to(DEV)
+    snaps = torch.empty((kt,) + tuple(state.shape), dtype=torch.float32, device=DEV)
+    o = gdn.gdn_decode_multi(*args, state, snapshots=snaps)
+    torch.cuda.synchronize()
+    ref = np64(inp["state0"])
+    for t in range(kt):
+        want_o, ref = O.decode_step(ref, *[np64(inp[n][t]) for n in ("q", "k", "v", "log_alpha", "beta")])
+        check(o[t], want_o, torch.bfloat16, f"o token {t}")
+        check(snaps[t], ref, torch.bfloat16, f"state after token {t}")

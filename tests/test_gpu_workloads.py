@@ -99,3 +99,27 @@ def test_workload_decode_256_sampled_sequences():
     torch.cuda.synchronize()
     print(f"  worst per-step o rel-L2 {worst:.2e}", flush=True)
     check(state[seqs], ref, torch.bfloat16, "state after 128 steps")
+
+
+def test_workload_decode_256_verify_four_tokens():
+    say("decode_256 speculative verify: 4 drafted tokens for all 256 sequences in one pass")
+    kt = 4
+    dec = I.workload_inputs("decode_256", steps=kt)
+    args = [dec[x].to(DEV) for x in ("q", "k", "v", "log_alpha", "beta")]
+    single = dec["state0"].to(DEV)
+    o_single = [gdn.gdn_decode_step(*[a[t] for a in args], single) for t in range(kt)]
+    state = dec["state0"].to(DEV)
+    snaps = torch.empty((kt,) + tuple(state.shape), dtype=torch.float32, device=DEV)
+    o = gdn.gdn_decode_multi(*args, state, snapshots=snaps)
+    torch.cuda.synchronize()
+    for t in range(kt):
+        assert torch.equal(o[t], o_single[t]), f"o token {t}"
+    assert torch.equal(snaps[-1], single)
+    assert torch.equal(state, dec["state0"].to(DEV))
+    # oracle on sampled sequences
+    seqs = [0, 131, 255]
+    ref = np64(dec["state0"][seqs])
+    for t in range(kt):
+        want_o, ref = O.decode_step(ref, *[np64(dec[x][t][seqs]) for x in ("q", "k", "v", "log_alpha", "beta")])
+        check(o[t][seqs], want_o, torch.bfloat16, f"o token {t}")
+        check(snaps[t][seqs], ref, torch.bfloat16, f"state after token {t}")

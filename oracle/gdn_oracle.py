@@ -22,6 +22,11 @@ where the page is silent (each one is listed with the design notes):
                from its own initial state (zeros when none is given).
   R5 chunks    the chunkwise evaluation restarts chunks at every sequence
                start; the last chunk of a sequence may be partial.
+  R6 prep      fused input preparation (an option of the library): q and
+               k arrive raw and are L2-normalised per (token, head) as
+               x / sqrt(max(sum x^2, 1e-12)); the gates arrive as logits a,
+               b with log a_t = -softplus(a) and b_t = sigmoid(b), the maps
+               of the configured input recipe (a_t then lies in (0,1)).
 
 Array conventions (all functions): q, k [T, Hqk, dk]; v [T, Hv, dv];
 log_alpha, beta [T, Hv]; init_state / final_state [N, Hv, dk, dv];
@@ -44,6 +49,25 @@ def seq_bounds(total_tokens, cu_seqlens):
         return [(0, int(total_tokens))]
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     return [(int(cu[i]), int(cu[i + 1])) for i in range(len(cu) - 1)]
+
+
+def prepare_inputs(q_raw, k_raw, a_logit, b_logit):
+    """Reading R6: (q, k, log_alpha, beta) from raw q, k and gate logits.
+
+    q, k are divided by their Euclidean norm over the last axis (the
+    squared norm floored at 1e-12); log_alpha = -softplus(a) =
+    -(max(a, 0) + log(1 + exp(-|a|))); beta = sigmoid(b) = 1 / (1 + exp(-b)),
+    written in the overflow-free form for either sign of b.
+    """
+    def unit(x):
+        x = np.asarray(x, dtype=np.float64)
+        return x / np.sqrt(np.maximum(np.sum(x * x, axis=-1, keepdims=True), 1e-12))
+    a = np.asarray(a_logit, dtype=np.float64)
+    b = np.asarray(b_logit, dtype=np.float64)
+    log_alpha = -(np.maximum(a, 0.0) + np.log1p(np.exp(-np.abs(a))))
+    e = np.exp(-np.abs(b))
+    beta = np.where(b >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return unit(q_raw), unit(k_raw), log_alpha, beta
 
 
 def _prep(q, k, v, log_alpha, beta, init_state, cu_seqlens):

@@ -328,3 +328,54 @@ def test_decode_steps_equal_prefill():
         o_t, S = O.decode_step(S, q[idx], k[idx], v[idx], la[idx], b[idx])
         np.testing.assert_allclose(o_t, o_pf[idx], rtol=1e-11, atol=1e-13)
     np.testing.assert_allclose(S, f_pf, rtol=1e-11, atol=1e-13)
+
+
+# --- fused input preparation (reading R6) ---------------------------------
+
+def test_prepare_inputs_unit_norm_and_scale_invariance():
+    rng = np.random.default_rng(60)
+    q = rng.standard_normal((7, 3, 16))
+    k = rng.standard_normal((7, 3, 16)) * 5.0
+    qn, kn, _, _ = O.prepare_inputs(q, k, np.zeros((7, 2)), np.zeros((7, 2)))
+    assert np.allclose(np.linalg.norm(qn, axis=-1), 1.0, rtol=0, atol=1e-14)
+    assert np.allclose(np.linalg.norm(kn, axis=-1), 1.0, rtol=0, atol=1e-14)
+    # direction kept: a positive rescaling of the input changes nothing
+    qn2, kn2, _, _ = O.prepare_inputs(3.7 * q, 0.01 * k, np.zeros((7, 2)), np.zeros((7, 2)))
+    assert np.allclose(qn2, qn, rtol=0, atol=1e-14) and np.allclose(kn2, kn, rtol=0, atol=1e-14)
+    assert np.all(np.sum(qn * q, axis=-1) > 0)
+    # a zero vector stays zero (the floor on the squared norm)
+    z, _, _, _ = O.prepare_inputs(np.zeros((1, 1, 4)), np.ones((1, 1, 4)), np.zeros((1, 1)), np.zeros((1, 1)))
+    assert np.all(z == 0)
+
+
+def test_prepare_inputs_gates_match_library_routines():
+    from scipy.special import expit
+    a = np.concatenate([np.linspace(-60, 60, 241), np.random.default_rng(61).normal(-2, 1, 50)])
+    b = np.concatenate([np.linspace(-60, 60, 241), np.random.default_rng(62).normal(0, 1, 50)])
+    _, _, la, beta = O.prepare_inputs(np.ones((1, 1, 2)), np.ones((1, 1, 2)), a, b)
+    # log a = -softplus(a) = -log(1 + e^a) (numpy's logaddexp) = log(sigmoid(-a)); b = sigmoid(b)
+    assert np.allclose(la, -np.logaddexp(0.0, a), rtol=1e-12, atol=0)
+    from scipy.special import log_expit
+    assert np.allclose(la, log_expit(-a), rtol=1e-12, atol=0)
+    assert np.allclose(beta, expit(b), rtol=1e-12, atol=1e-300)
+    assert np.all(la < 0) and np.all(np.isfinite(la))
+    assert np.all((beta > 0) & (beta < 1) | (np.abs(b) > 36))
+    # the identity sigmoid(b) + sigmoid(-b) = 1 and the asymptote -softplus(a) ~ -a for large a
+    _, _, _, beta_neg = O.prepare_inputs(np.ones((1, 1, 2)), np.ones((1, 1, 2)), a, -b)
+    assert np.allclose(beta + beta_neg, 1.0, rtol=0, atol=1e-15)
+    assert abs(la[-51] + 60.0) < 1e-25 + 1e-12 * 60
+
+
+def test_prepared_inputs_give_unit_keys_so_recall_is_exact():
+    # with prepared (unit) keys, b = 1 (logit +inf approximated by a large
+    # value is avoided: use b logits that give b = 1/2) the state stays
+    # finite and o matches the recurrence on the prepared arrays
+    rng = np.random.default_rng(63)
+    T, hq, hv, d = 9, 1, 2, 8
+    q, k, la, beta = O.prepare_inputs(rng.standard_normal((T, hq, d)), rng.standard_normal((T, hq, d)),
+                                      rng.normal(-2, 1, (T, hv)), rng.normal(0, 1, (T, hv)))
+    v = rng.standard_normal((T, hv, d))
+    o1, s1 = O.recurrent_form1(q, k, v, la, beta)
+    o2, s2 = O.recurrent_form2(q, k, v, la, beta)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-13) and np.allclose(s1, s2, rtol=1e-12, atol=1e-13)
+    assert np.all(np.abs(s1) < 1e3)

@@ -295,6 +295,26 @@ def main():
             "sample": f"first {n_tok} tokens of the same 64K-token input, all 48 V heads, "
                       f"token-serial fp64 recurrence, one thread, {secs:.1f} s"}
     line["decode_verify"] = verify_bench(gdn, I, dev, decode_ms)
+    # fused input preparation (raw q, k and gate logits): the same workload
+    # with the flag set; the kernels' work does not depend on the values
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    pf_prep = timed(lambda: gdn.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                                              inp["init_state"], None, chunk=C, workspace=ws, o=o,
+                                              final_state=fin, prepare_inputs=True))
+    dec_prep = timed(lambda: gdn.gdn_decode_step(dec["q"][0], dec["k"][0], dec["v"][0], dec["log_alpha"][0],
+                                                 dec["beta"][0], state, o=o_dec, prepare_inputs=True))
+    line["prepare_inputs"] = {"prefill_ms": round(pf_prep, 4), "prefill_tokens_per_s": round(T / (pf_prep * 1e-3), 1),
+                              "decode_ms": round(dec_prep, 4),
+                              "decode_GBps": round(dec_bytes / (dec_prep * 1e-3) / 1e9, 1)}
     print(json.dumps(line), flush=True)
 
 

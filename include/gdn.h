@@ -50,6 +50,19 @@ typedef enum {
   GDN_DTYPE_BF16 = 1  /* bfloat16 q, k, v, o (fp32 accumulation and state) */
 } gdn_dtype_t;
 
+/*
+ * Flags (gdn_dims_t.flags).
+ * GDN_FLAG_PREPARE_INPUTS: fused input preparation. q and k are raw; every
+ *   kernel that reads them L2-normalises each (token, head) vector as
+ *   x / sqrt(max(sum x^2, 1e-12)) in fp32 (prefill then rounds the unit
+ *   vectors to the input dtype for its matrix products). The `log_alpha`
+ *   and `beta` arguments carry gate logits a and b, mapped to
+ *   log(alpha) = -softplus(a) and beta = sigmoid(b). Section 2.1 makes
+ *   the gates data-dependent; these maps are the ones of the configured
+ *   input recipe.
+ */
+enum { GDN_FLAG_PREPARE_INPUTS = 1 };
+
 typedef struct {
   int64_t num_seqs;     /* N >= 1: packed sequences (prefill) or batch (decode) */
   int64_t total_tokens; /* T >= 0: packed tokens; decode: must equal num_seqs */
@@ -59,6 +72,7 @@ typedef struct {
   int32_t dv;           /* value head dim (must equal dk) */
   int32_t chunk;        /* prefill chunk length C (ignored by decode) */
   int32_t dtype;        /* gdn_dtype_t of q, k, v, o */
+  int32_t flags;        /* 0 or GDN_FLAG_PREPARE_INPUTS */
 } gdn_dims_t;
 
 /*

@@ -27,7 +27,7 @@ class GdnDims(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int64), ("total_tokens", ctypes.c_int64),
                 ("h_qk", ctypes.c_int32), ("h_v", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
-                ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class GdnWorkspaceLayout(ctypes.Structure):
@@ -88,10 +88,13 @@ def _check(status):
         raise GdnError(status, msg)
 
 
-def make_dims(num_seqs, total_tokens, h_qk, h_v, dk, dv, chunk, dtype):
+GDN_FLAG_PREPARE_INPUTS = 1
+
+
+def make_dims(num_seqs, total_tokens, h_qk, h_v, dk, dv, chunk, dtype, flags=0):
     code = GDN_DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     return GdnDims(int(num_seqs), int(total_tokens), int(h_qk), int(h_v), int(dk), int(dv),
-                   int(chunk), code)
+                   int(chunk), code, int(flags))
 
 
 def _ptr(t):
@@ -132,12 +135,14 @@ def gdn_chunk_fwd_workspace_layout(dims):
 
 def gdn_chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, chunk=64,
                   output_final_state=True, workspace=None, o=None, final_state=None,
-                  stages=None):
+                  stages=None, prepare_inputs=False):
     """Prefill through gdn_chunk_fwd. Shapes: q, k [T,Hqk,d]; v [T,Hv,d];
     log_alpha, beta [T,Hv] fp32; init_state [N,Hv,d,d] fp32 or None;
     cu_seqlens int32 [N+1] or None. Returns (o, final_state or None).
     `workspace` (uint8 CUDA tensor) may be passed to reuse scratch memory.
-    `stages=(first, last)` calls gdn_chunk_fwd_stages instead (diagnostic)."""
+    `stages=(first, last)` calls gdn_chunk_fwd_stages instead (diagnostic).
+    `prepare_inputs=True` sets GDN_FLAG_PREPARE_INPUTS: q, k raw and
+    log_alpha, beta holding the gate logits."""
     lib = load_library()
     dev = q.device
     if dev.type != "cuda":
@@ -156,7 +161,8 @@ def gdn_chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, ch
         _need(cu_seqlens, "cu_seqlens", dev, torch.int32, (n + 1,))
     if q.dtype not in GDN_DTYPE:
         raise ValueError(f"unsupported dtype {q.dtype}")
-    dims = make_dims(n, T, h_qk, h_v, d, v.shape[2], chunk, q.dtype)
+    dims = make_dims(n, T, h_qk, h_v, d, v.shape[2], chunk, q.dtype,
+                     GDN_FLAG_PREPARE_INPUTS if prepare_inputs else 0)
     nbytes = gdn_chunk_fwd_workspace_bytes(dims)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -178,10 +184,10 @@ def gdn_chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, ch
     return o, final_state
 
 
-def gdn_decode_step(q, k, v, log_alpha, beta, state, o=None):
+def gdn_decode_step(q, k, v, log_alpha, beta, state, o=None, prepare_inputs=False):
     """One decode step through gdn_decode_step. q, k [N,Hqk,d]; v [N,Hv,d];
     log_alpha, beta [N,Hv] fp32; state [N,Hv,d,d] fp32 (updated in place).
-    Returns o [N,Hv,d]."""
+    Returns o [N,Hv,d]. `prepare_inputs` as for gdn_chunk_fwd."""
     lib = load_library()
     dev = q.device
     if dev.type != "cuda":
@@ -199,18 +205,19 @@ def gdn_decode_step(q, k, v, log_alpha, beta, state, o=None):
     if o is None:
         o = torch.empty_like(v)
     _need(o, "o", dev, v.dtype, tuple(v.shape))
-    dims = make_dims(n, n, h_qk, h_v, d, v.shape[2], 0, q.dtype)
+    dims = make_dims(n, n, h_qk, h_v, d, v.shape[2], 0, q.dtype,
+                     GDN_FLAG_PREPARE_INPUTS if prepare_inputs else 0)
     _check(lib.gdn_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                                _ptr(beta), _ptr(state), _ptr(o), _stream(dev)))
     return o
 
 
-def gdn_decode_multi(q, k, v, log_alpha, beta, state, o=None, snapshots=None):
+def gdn_decode_multi(q, k, v, log_alpha, beta, state, o=None, snapshots=None, prepare_inputs=False):
     """K drafted tokens per sequence through gdn_decode_multi. q, k [K,N,Hqk,d];
     v [K,N,Hv,d]; log_alpha, beta [K,N,Hv] fp32; state [N,Hv,d,d] fp32.
     With `snapshots` ([K,N,Hv,d,d] fp32) the state after each token goes there
     and `state` is only read; without, `state` ends as the state after all K
-    tokens. Returns o [K,N,Hv,d]."""
+    tokens. Returns o [K,N,Hv,d]. `prepare_inputs` as for gdn_chunk_fwd."""
     lib = load_library()
     dev = q.device
     if dev.type != "cuda":
@@ -230,7 +237,8 @@ def gdn_decode_multi(q, k, v, log_alpha, beta, state, o=None, snapshots=None):
     _need(o, "o", dev, v.dtype, tuple(v.shape))
     if snapshots is not None:
         _need(snapshots, "snapshots", dev, torch.float32, (kt, n, h_v, d, dv))
-    dims = make_dims(n, n, h_qk, h_v, d, dv, 0, q.dtype)
+    dims = make_dims(n, n, h_qk, h_v, d, dv, 0, q.dtype,
+                     GDN_FLAG_PREPARE_INPUTS if prepare_inputs else 0)
     _check(lib.gdn_decode_multi(ctypes.byref(dims), int(kt), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                                 _ptr(beta), _ptr(state), _ptr(o),
                                 _ptr(snapshots) if snapshots is not None else None, _stream(dev)))

@@ -31,7 +31,7 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
   constexpr int CG = D / 4, RG = DecodeShape<D>::RG, RPT = D / RG;
   __shared__ f32x4 red_p[RG][CG];
   __shared__ f32x4 red_r[RG][CG];
-  __shared__ float red_kq[RG];
+  __shared__ float red_kq[RG][4];                // k.q, then (raw inputs) |k|^2, |q|^2
   const int64_t nh = blockIdx.x;                 // sequence * h_v + V head
   const int64_t n = nh / a.h_v;
   const int hv = (int)(nh % a.h_v);
@@ -50,29 +50,50 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
   for (int r = 0; r < RPT; ++r) s[r] = __builtin_nontemporal_load(sp + r * CG);
 
   f32x4 p = zero4(), rq = zero4();
-  float kq = 0.f;
+  float kq = 0.f, k2 = 0.f, q2 = 0.f;
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
     p += s[r] * kk[r];
     rq += s[r] * qq[r];
     kq += kk[r] * qq[r];
   }
+  if (a.prep) {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) { k2 += kk[r] * kk[r]; q2 += qq[r] * qq[r]; }
+  }
   red_p[rg][cg] = p;
   red_r[rg][cg] = rq;
-  if (cg == 0) red_kq[rg] = kq;
+  if (cg == 0) { red_kq[rg][0] = kq; red_kq[rg][1] = k2; red_kq[rg][2] = q2; }
   __syncthreads();
   p = zero4();
   rq = zero4();
   kq = 0.f;
+  k2 = 0.f;
+  q2 = 0.f;
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
     p += red_p[g][cg];
     rq += red_r[g][cg];
-    kq += red_kq[g];
+    kq += red_kq[g][0];
+    k2 += red_kq[g][1];
+    q2 += red_kq[g][2];
   }
-
-  const float alpha = expf(a.log_alpha[nh]);
-  const float beta = a.beta[nh];
+  float alpha, beta;
+  if (a.prep) {
+    // raw inputs: S^T k, S^T q and k.q are linear in k and q, so the unit
+    // vectors' values are the raw sums times the inverse norms
+    const float ik = inv_norm(k2), iq = inv_norm(q2);
+    p *= ik;
+    rq *= iq;
+    kq *= ik * iq;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) kk[r] *= ik;
+    alpha = expf(neg_softplus(a.log_alpha[nh]));
+    beta = sigmoid_of(a.beta[nh]);
+  } else {
+    alpha = expf(a.log_alpha[nh]);
+    beta = a.beta[nh];
+  }
   const E* vp = static_cast<const E*>(a.v) + nh * D + 4 * cg;
   f32x4 u;
 #pragma unroll
@@ -89,6 +110,10 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
   }
 }
 
+// With fused input preparation, q and k arrive raw: their squared norms
+// join the column-sum reduction, and the raw sums S^T k, S^T q, k.q are
+// rescaled by the inverse norms (they are linear in k and q).
+//
 // Speculative multi-token verify: K drafted tokens per sequence applied in
 // order, K successive steps of the update above in one pass over the state.
 // The workgroup's state slice stays in registers across the K tokens; each
@@ -103,7 +128,7 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_mu
   constexpr int CG = D / 4, RG = DecodeShape<D>::RG, RPT = D / RG;
   __shared__ f32x4 red_p[2][RG][CG];
   __shared__ f32x4 red_r[2][RG][CG];
-  __shared__ float red_kq[2][RG];
+  __shared__ float red_kq[2][RG][4];             // k.q, then (raw inputs) |k|^2, |q|^2
   const int64_t nh = blockIdx.x;                 // sequence * h_v + V head
   const int64_t n = nh / a.h_v;
   const int hv = (int)(nh % a.h_v);
@@ -125,29 +150,49 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_mu
 #pragma unroll
     for (int r = 0; r < RPT; ++r) { kk[r] = to_f(kp[r]); qq[r] = to_f(qp[r]); }
     f32x4 p = zero4(), rq = zero4();
-    float kq = 0.f;
+    float kq = 0.f, k2 = 0.f, q2 = 0.f;
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
       p += s[r] * kk[r];
       rq += s[r] * qq[r];
       kq += kk[r] * qq[r];
     }
+    if (a.prep) {
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) { k2 += kk[r] * kk[r]; q2 += qq[r] * qq[r]; }
+    }
     red_p[par][rg][cg] = p;
     red_r[par][rg][cg] = rq;
-    if (cg == 0) red_kq[par][rg] = kq;
+    if (cg == 0) { red_kq[par][rg][0] = kq; red_kq[par][rg][1] = k2; red_kq[par][rg][2] = q2; }
     __syncthreads();
     p = zero4();
     rq = zero4();
     kq = 0.f;
+    k2 = 0.f;
+    q2 = 0.f;
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
       p += red_p[par][g][cg];
       rq += red_r[par][g][cg];
-      kq += red_kq[par][g];
+      kq += red_kq[par][g][0];
+      k2 += red_kq[par][g][1];
+      q2 += red_kq[par][g][2];
     }
     const int64_t tv = j * tok_v + nh;
-    const float alpha = expf(a.log_alpha[tv]);
-    const float beta = a.beta[tv];
+    float alpha, beta;
+    if (a.prep) {
+      const float ik = inv_norm(k2), iq = inv_norm(q2);
+      p *= ik;
+      rq *= iq;
+      kq *= ik * iq;
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) kk[r] *= ik;
+      alpha = expf(neg_softplus(a.log_alpha[tv]));
+      beta = sigmoid_of(a.beta[tv]);
+    } else {
+      alpha = expf(a.log_alpha[tv]);
+      beta = a.beta[tv];
+    }
     const E* vp = static_cast<const E*>(a.v) + tv * D + 4 * cg;
     f32x4 u;
 #pragma unroll

@@ -97,4 +97,38 @@ __device__ __forceinline__ Frag<E> acc_to_frag(const f32x4& lo, const f32x4& hi)
 
 __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
+// Fused input preparation (GDN_FLAG_PREPARE_INPUTS): the gate maps
+// log(alpha) = -softplus(a) and beta = sigmoid(b), written so that neither
+// overflows for any sign of the logit, and the L2 normalisation of q and k.
+__device__ __forceinline__ float neg_softplus(float a) { return -(fmaxf(a, 0.f) + log1pf(expf(-fabsf(a)))); }
+__device__ __forceinline__ float sigmoid_of(float b) {
+  const float e = expf(-fabsf(b));
+  return b >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
+}
+__device__ __forceinline__ float inv_norm(float sum_sq) { return rsqrtf(fmaxf(sum_sq, 1e-12f)); }
+
+// Normalises `rows` rows of length D (stride ld elements) in LDS in place,
+// two threads per row: thread 2r + h sums and scales half h of row r.
+// Threads t with t / 2 >= rows only take part in the pair exchange. The
+// caller synchronises the workgroup before and after.
+template <typename E, int D>
+__device__ __forceinline__ void normalize_rows(E* base, int ld, int rows, int t) {
+  constexpr int HD = D / 2;
+  const int r = t >> 1, h = t & 1;
+  float ss = 0.f;
+  if (r < rows) {
+#pragma unroll 8
+    for (int d = 0; d < HD; ++d) {
+      const float x = to_f(base[r * ld + h * HD + d]);
+      ss += x * x;
+    }
+  }
+  ss += __shfl_xor(ss, 1);
+  if (r < rows) {
+    const float inv = inv_norm(ss);
+#pragma unroll 8
+    for (int d = 0; d < HD; ++d) base[r * ld + h * HD + d] = to_e<E>(to_f(base[r * ld + h * HD + d]) * inv);
+  }
+}
+
 }  // namespace gdn

@@ -37,6 +37,7 @@ struct PrefillArgs {
   int32_t h_qk;             // HQ
   int32_t h_v;              // HV
   int32_t group;            // HV / HQ
+  int32_t prep;             // 1: raw q, k and gate logits (fused input preparation)
 };
 
 struct DecodeArgs {
@@ -56,6 +57,7 @@ struct DecodeArgs {
   // null to update `state` in place
   int32_t num_tokens;
   float* snapshots;
+  int32_t prep;             // 1: raw q, k and gate logits (fused input preparation)
 };
 
 // Prefill launch stages (1-based): 1 chunk preparation (table, gate prefix sums,

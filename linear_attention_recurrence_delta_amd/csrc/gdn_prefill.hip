@@ -168,6 +168,7 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
     if (lane < len) {
       g = a.log_alpha[(int64_t)(start + lane) * a.h_v + hv];
       b = a.beta[(int64_t)(start + lane) * a.h_v + hv];
+      if (a.prep) { g = neg_softplus(g); b = sigmoid_of(b); }
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -196,6 +197,13 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
     *reinterpret_cast<VLoad*>(&sm.qs[r * KLD + d]) = qv;
   }
   __syncthreads();
+  if (a.prep) {
+    // raw q and k: unit rows (threads [0, 2C) the keys, [2C, 4C) the queries)
+    static_assert(4 * C <= kBlock, "two threads per staged row");
+    if (tid < 2 * C) normalize_rows<E, D>(sm.ks, KLD, C, tid);
+    else normalize_rows<E, D>(sm.qs, KLD, C, tid - 2 * C);
+    __syncthreads();
+  }
 
   // K^T fragments: frag (dt, s), lane row d, elements token i
   Frag<E>* ktg = reinterpret_cast<Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
@@ -339,6 +347,11 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
     sm.gb[tid / C][tid % C] = (tid < C) ? a.gate_prefix[o] : a.beta_chunk[o];
   }
   __syncthreads();
+  if (a.prep) {
+    // raw keys: unit rows, as kernel 1 makes them for K^T and q.k
+    normalize_rows<E, D>(sm.u.ks, KLD, C, tid);
+    __syncthreads();
+  }
 
   // The scan's operands that depend on g: P = the masked, decayed q.k
   // fragments, P[r][j] = (q_r . k_j) exp(g_r - g_j) for j <= r < len, else 0

@@ -97,6 +97,65 @@ def make_decode(seed, batch, steps, h_qk, h_v, d, dtype="bf16"):
     )
 
 
+def make_prefill_raw(seed, seq_lens, h_qk, h_v, d, dtype="bf16", init="zeros"):
+    """Raw inputs for fused input preparation: q, k ~ N(0, 1) times a
+    per-(token, head) scale exp(N(0, 0.5^2)) (not normalised), v ~ N(0, 1),
+    gate logits a ~ N(-2, 1) and b ~ N(0, 1) in the log_alpha and beta
+    slots, init as in make_prefill. Draw order: q, k, v, a, b, init, the q
+    scales, the k scales. Same keys and shapes as make_prefill."""
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in seq_lens]
+    T = int(sum(lens))
+    tdt = _DTYPES[dtype]
+    q = rng.standard_normal((T, h_qk, d))
+    k = rng.standard_normal((T, h_qk, d))
+    v = rng.standard_normal((T, h_v, d))
+    a = rng.normal(-2.0, 1.0, (T, h_v))
+    b = rng.standard_normal((T, h_v))
+    init_state = None
+    if init == "randn":
+        init_state = torch.from_numpy(
+            rng.normal(0.0, 0.02, (len(lens), h_v, d, d)).astype(np.float32))
+    elif init != "zeros":
+        raise ValueError(init)
+    q = q * np.exp(rng.normal(0.0, 0.5, (T, h_qk, 1)))
+    k = k * np.exp(rng.normal(0.0, 0.5, (T, h_qk, 1)))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return dict(
+        q=torch.from_numpy(q).to(tdt),
+        k=torch.from_numpy(k).to(tdt),
+        v=torch.from_numpy(v).to(tdt),
+        log_alpha=torch.from_numpy(a.astype(np.float32)),
+        beta=torch.from_numpy(b.astype(np.float32)),
+        init_state=init_state,
+        cu_seqlens=torch.from_numpy(cu),
+    )
+
+
+def make_decode_raw(seed, batch, steps, h_qk, h_v, d, dtype="bf16"):
+    """Raw decode inputs for fused input preparation (see
+    make_prefill_raw); same keys and shapes as make_decode. Draw order:
+    state0, q, k, v, a, b, the q scales, the k scales."""
+    rng = np.random.default_rng(seed)
+    tdt = _DTYPES[dtype]
+    state0 = rng.normal(0.0, 0.02, (batch, h_v, d, d)).astype(np.float32)
+    q = rng.standard_normal((steps, batch, h_qk, d))
+    k = rng.standard_normal((steps, batch, h_qk, d))
+    v = rng.standard_normal((steps, batch, h_v, d))
+    a = rng.normal(-2.0, 1.0, (steps, batch, h_v))
+    b = rng.standard_normal((steps, batch, h_v))
+    q = q * np.exp(rng.normal(0.0, 0.5, (steps, batch, h_qk, 1)))
+    k = k * np.exp(rng.normal(0.0, 0.5, (steps, batch, h_qk, 1)))
+    return dict(
+        state0=torch.from_numpy(state0),
+        q=torch.from_numpy(q).to(tdt),
+        k=torch.from_numpy(k).to(tdt),
+        v=torch.from_numpy(v).to(tdt),
+        log_alpha=torch.from_numpy(a.astype(np.float32)),
+        beta=torch.from_numpy(b.astype(np.float32)),
+    )
+
+
 # The five workloads (sizes as named in the docs). Each entry is the
 # keyword arguments of make_prefill / make_decode.
 WORKLOADS = {

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def dims(**kw):
     base = dict(num_seqs=1, total_tokens=128, h_qk=16, h_v=48, dk=128, dv=128, chunk=64,
-                dtype=1)
+                dtype=1, flags=0)
     base.update(kw)
     return B.GdnDims(*[base[f] for f, _ in B.GdnDims._fields_])
 
@@ -66,6 +66,8 @@ def ws_bytes(lib, d):
     (dict(dk=128, dv=64), NOT_SUPPORTED),
     (dict(chunk=32), NOT_SUPPORTED),
     (dict(dtype=0), NOT_SUPPORTED),          # fp32 at head dim 128 needs chunk 16
+    (dict(flags=2), INVALID),                # unknown flag
+    (dict(flags=-1), INVALID),
 ])
 def test_dims_validation(lib, kw, status):
     d = dims(**kw)
@@ -177,6 +179,12 @@ def test_decode_multi_validation(lib):
     assert call(d, snap=FAKE * 16 + 8) == INVALID                # misaligned snapshots
     assert call(dims(num_seqs=4, total_tokens=4, dk=32, dv=32)) == NOT_SUPPORTED
     assert call(dims(num_seqs=1 << 20, total_tokens=1 << 20), kt=1 << 12) == NOT_SUPPORTED
+
+
+def test_prepare_inputs_flag_is_accepted(lib):
+    d = dims(flags=B.GDN_FLAG_PREPARE_INPUTS)
+    assert ws_bytes(lib, d) == ws_bytes(lib, dims())
+    assert ctypes.sizeof(B.GdnDims) == 48
 
 
 def test_status_strings(lib):

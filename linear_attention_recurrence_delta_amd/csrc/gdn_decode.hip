@@ -26,7 +26,7 @@ template <int D> struct DecodeShape;
 template <> struct DecodeShape<128> { static constexpr int RG = 8; };
 template <> struct DecodeShape<16> { static constexpr int RG = 4; };
 
-template <typename E, int D>
+template <typename E, int D, bool P>
 __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_step(const DecodeArgs a) {
   constexpr int CG = D / 4, RG = DecodeShape<D>::RG, RPT = D / RG;
   __shared__ f32x4 red_p[RG][CG];
@@ -57,13 +57,16 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
     rq += s[r] * qq[r];
     kq += kk[r] * qq[r];
   }
-  if (a.prep) {
+  if constexpr (P) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) { k2 += kk[r] * kk[r]; q2 += qq[r] * qq[r]; }
   }
   red_p[rg][cg] = p;
   red_r[rg][cg] = rq;
-  if (cg == 0) { red_kq[rg][0] = kq; red_kq[rg][1] = k2; red_kq[rg][2] = q2; }
+  if (cg == 0) {
+    red_kq[rg][0] = kq;
+    if constexpr (P) { red_kq[rg][1] = k2; red_kq[rg][2] = q2; }
+  }
   __syncthreads();
   p = zero4();
   rq = zero4();
@@ -75,11 +78,10 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
     p += red_p[g][cg];
     rq += red_r[g][cg];
     kq += red_kq[g][0];
-    k2 += red_kq[g][1];
-    q2 += red_kq[g][2];
+    if constexpr (P) { k2 += red_kq[g][1]; q2 += red_kq[g][2]; }
   }
   float alpha, beta;
-  if (a.prep) {
+  if constexpr (P) {
     // raw inputs: S^T k, S^T q and k.q are linear in k and q, so the unit
     // vectors' values are the raw sums times the inverse norms
     const float ik = inv_norm(k2), iq = inv_norm(q2);
@@ -123,7 +125,7 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
 // snapshot j and `state` is only read (so a caller can keep any accepted
 // prefix); without one, the final state replaces `state`. Each token's
 // arithmetic is the single-step kernel's, term for term.
-template <typename E, int D>
+template <typename E, int D, bool P>
 __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_multi(const DecodeArgs a) {
   constexpr int CG = D / 4, RG = DecodeShape<D>::RG, RPT = D / RG;
   __shared__ f32x4 red_p[2][RG][CG];
@@ -157,13 +159,16 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_mu
       rq += s[r] * qq[r];
       kq += kk[r] * qq[r];
     }
-    if (a.prep) {
+    if constexpr (P) {
 #pragma unroll
       for (int r = 0; r < RPT; ++r) { k2 += kk[r] * kk[r]; q2 += qq[r] * qq[r]; }
     }
     red_p[par][rg][cg] = p;
     red_r[par][rg][cg] = rq;
-    if (cg == 0) { red_kq[par][rg][0] = kq; red_kq[par][rg][1] = k2; red_kq[par][rg][2] = q2; }
+    if (cg == 0) {
+      red_kq[par][rg][0] = kq;
+      if constexpr (P) { red_kq[par][rg][1] = k2; red_kq[par][rg][2] = q2; }
+    }
     __syncthreads();
     p = zero4();
     rq = zero4();
@@ -175,12 +180,11 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_mu
       p += red_p[par][g][cg];
       rq += red_r[par][g][cg];
       kq += red_kq[par][g][0];
-      k2 += red_kq[par][g][1];
-      q2 += red_kq[par][g][2];
+      if constexpr (P) { k2 += red_kq[par][g][1]; q2 += red_kq[par][g][2]; }
     }
     const int64_t tv = j * tok_v + nh;
     float alpha, beta;
-    if (a.prep) {
+    if constexpr (P) {
       const float ik = inv_norm(k2), iq = inv_norm(q2);
       p *= ik;
       rq *= iq;
@@ -221,7 +225,10 @@ template <typename E, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   constexpr int threads = (D / 4) * DecodeShape<D>::RG;
   const unsigned blocks = (unsigned)(a.num_seqs * a.h_v);
-  gdn_kd_decode_step<E, D><<<dim3(blocks), dim3(threads), 0, s>>>(a);
+  if (a.prep)
+    gdn_kd_decode_step<E, D, true><<<dim3(blocks), dim3(threads), 0, s>>>(a);
+  else
+    gdn_kd_decode_step<E, D, false><<<dim3(blocks), dim3(threads), 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -229,7 +236,10 @@ template <typename E, int D>
 hipError_t launch_decode_multi_t(const DecodeArgs& a, hipStream_t s) {
   constexpr int threads = (D / 4) * DecodeShape<D>::RG;
   const unsigned blocks = (unsigned)(a.num_seqs * a.h_v);
-  gdn_kd_decode_multi<E, D><<<dim3(blocks), dim3(threads), 0, s>>>(a);
+  if (a.prep)
+    gdn_kd_decode_multi<E, D, true><<<dim3(blocks), dim3(threads), 0, s>>>(a);
+  else
+    gdn_kd_decode_multi<E, D, false><<<dim3(blocks), dim3(threads), 0, s>>>(a);
   return hipGetLastError();
 }
 

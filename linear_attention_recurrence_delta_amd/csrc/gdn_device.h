@@ -107,28 +107,26 @@ __device__ __forceinline__ float sigmoid_of(float b) {
 }
 __device__ __forceinline__ float inv_norm(float sum_sq) { return rsqrtf(fmaxf(sum_sq, 1e-12f)); }
 
-// Normalises `rows` rows of length D (stride ld elements) in LDS in place,
-// two threads per row: thread 2r + h sums and scales half h of row r.
-// Threads t with t / 2 >= rows only take part in the pair exchange. The
-// caller synchronises the workgroup before and after.
-template <typename E, int D>
-__device__ __forceinline__ void normalize_rows(E* base, int ld, int rows, int t) {
-  constexpr int HD = D / 2;
-  const int r = t >> 1, h = t & 1;
+// Scales one (token, head) vector of length D to unit L2 norm while it is
+// in registers: each of D / N consecutive lanes holds N of its elements in
+// `v`; the lanes add their squares in fp32 and combine the sums with lane
+// exchanges, so every lane of such a group must be active (groups are
+// aligned to D / N lanes).
+template <typename E, int D, int N, typename V>
+__device__ __forceinline__ void normalize_slice(V& v) {
+  constexpr int L = D / N;
+  static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "lanes per vector: a power of two within a wave");
   float ss = 0.f;
-  if (r < rows) {
-#pragma unroll 8
-    for (int d = 0; d < HD; ++d) {
-      const float x = to_f(base[r * ld + h * HD + d]);
-      ss += x * x;
-    }
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const float x = to_f(v[e]);
+    ss += x * x;
   }
-  ss += __shfl_xor(ss, 1);
-  if (r < rows) {
-    const float inv = inv_norm(ss);
-#pragma unroll 8
-    for (int d = 0; d < HD; ++d) base[r * ld + h * HD + d] = to_e<E>(to_f(base[r * ld + h * HD + d]) * inv);
-  }
+#pragma unroll
+  for (int m = 1; m < L; m <<= 1) ss += __shfl_xor(ss, m);
+  const float inv = inv_norm(ss);
+#pragma unroll
+  for (int e = 0; e < N; ++e) v[e] = to_e<E>(to_f(v[e]) * inv);
 }
 
 }  // namespace gdn

@@ -106,7 +106,7 @@ struct PrepSmem {
   int hit[2];
 };
 
-template <typename E, int D, int C>
+template <typename E, int D, int C, bool P>
 __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   using SM = PrepSmem<E, D, C>;
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
     if (lane < len) {
       g = a.log_alpha[(int64_t)(start + lane) * a.h_v + hv];
       b = a.beta[(int64_t)(start + lane) * a.h_v + hv];
-      if (a.prep) { g = neg_softplus(g); b = sigmoid_of(b); }
+      if constexpr (P) { g = neg_softplus(g); b = sigmoid_of(b); }
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -193,17 +193,16 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
       kv = *reinterpret_cast<const VLoad*>(kg + gi);
       qv = *reinterpret_cast<const VLoad*>(qg + gi);
     }
+    if constexpr (P) {
+      // raw q and k: the D / VE lanes holding a row (a whole, aligned group:
+      // the trip count is a multiple of it) scale it to unit length
+      normalize_slice<E, D, VE>(kv);
+      normalize_slice<E, D, VE>(qv);
+    }
     *reinterpret_cast<VLoad*>(&sm.ks[r * KLD + d]) = kv;
     *reinterpret_cast<VLoad*>(&sm.qs[r * KLD + d]) = qv;
   }
   __syncthreads();
-  if (a.prep) {
-    // raw q and k: unit rows (threads [0, 2C) the keys, [2C, 4C) the queries)
-    static_assert(4 * C <= kBlock, "two threads per staged row");
-    if (tid < 2 * C) normalize_rows<E, D>(sm.ks, KLD, C, tid);
-    else normalize_rows<E, D>(sm.qs, KLD, C, tid - 2 * C);
-    __syncthreads();
-  }
 
   // K^T fragments: frag (dt, s), lane row d, elements token i
   Frag<E>* ktg = reinterpret_cast<Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
@@ -290,7 +289,7 @@ struct InvSmem {
   float gb[2][C];                      // g and b of this V head
 };
 
-template <typename E, int D, int C>
+template <typename E, int D, int C, bool P>
 __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   using SM = InvSmem<E, D, C>;
@@ -340,6 +339,8 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
 #pragma unroll
     for (int e = 0; e < VE; ++e) kv[e] = to_e<E>(0.f);
     if (r < len) kv = *reinterpret_cast<const VLoad*>(kg + ((int64_t)(start + r) * a.h_qk + hq) * D + d);
+    // raw keys: unit rows, exactly as kernel 1 makes them for K^T and q.k
+    if constexpr (P) normalize_slice<E, D, VE>(kv);
     *reinterpret_cast<VLoad*>(&sm.u.ks[r * KLD + d]) = kv;
   }
   if (tid < 2 * C) {
@@ -347,11 +348,6 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
     sm.gb[tid / C][tid % C] = (tid < C) ? a.gate_prefix[o] : a.beta_chunk[o];
   }
   __syncthreads();
-  if (a.prep) {
-    // raw keys: unit rows, as kernel 1 makes them for K^T and q.k
-    normalize_rows<E, D>(sm.u.ks, KLD, C, tid);
-    __syncthreads();
-  }
 
   // The scan's operands that depend on g: P = the masked, decayed q.k
   // fragments, P[r][j] = (q_r . k_j) exp(g_r - g_j) for j <= r < len, else 0
@@ -875,8 +871,18 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
   const unsigned scan_groups = (unsigned)(a.num_seqs * a.h_v * G::NCB);
   for (int stage = first; stage <= last; ++stage) {
     switch (stage) {
-      case 1: gdn_k1_chunk_prep<E, D, C><<<dim3(nc, (unsigned)a.h_qk), dim3(kBlock), 0, s>>>(a); break;
-      case 2: gdn_k2_inverse_w<E, D, C><<<dim3(nc * (unsigned)a.h_v), dim3(kBlock), 0, s>>>(a); break;
+      case 1:
+        if (a.prep)
+          gdn_k1_chunk_prep<E, D, C, true><<<dim3(nc, (unsigned)a.h_qk), dim3(kBlock), 0, s>>>(a);
+        else
+          gdn_k1_chunk_prep<E, D, C, false><<<dim3(nc, (unsigned)a.h_qk), dim3(kBlock), 0, s>>>(a);
+        break;
+      case 2:
+        if (a.prep)
+          gdn_k2_inverse_w<E, D, C, true><<<dim3(nc * (unsigned)a.h_v), dim3(kBlock), 0, s>>>(a);
+        else
+          gdn_k2_inverse_w<E, D, C, false><<<dim3(nc * (unsigned)a.h_v), dim3(kBlock), 0, s>>>(a);
+        break;
       case 3: gdn_k3_scan<E, D, C><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a); break;
       default: return hipErrorInvalidValue;
     }

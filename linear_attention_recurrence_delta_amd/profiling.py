@@ -27,9 +27,13 @@ SOURCES = {"gdn_k1_chunk_prep": "gdn_prefill.hip", "gdn_k2_inverse_w": "gdn_pref
 
 
 def short_name(name):
+    """Kernel name without its template arguments; the instances compiled
+    for fused input preparation (bool template argument true: `Lb1E` when
+    mangled, `true>` when demangled) get the suffix `[prep]`."""
     m = re.search(r"(gdn_k\w+?)(?:I|\(|<|E|$)", name)
     if m:
-        return m.group(1)
+        prep = "Lb1E" in name or "true>" in name
+        return m.group(1) + (" [prep]" if prep else "")
     return name.split("(")[0][:60]
 
 

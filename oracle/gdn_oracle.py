@@ -27,6 +27,14 @@ where the page is silent (each one is listed with the design notes):
                x / sqrt(max(sum x^2, 1e-12)); the gates arrive as logits a,
                b with log a_t = -softplus(a) and b_t = sigmoid(b), the maps
                of the configured input recipe (a_t then lies in (0,1)).
+  R7 variants  the section sets the gated delta rule against its two
+               parents: the data-dependent forget gate alone (Mamba2) and
+               the delta rule alone (DeltaNet). DeltaNet is a_t = 1 in
+               form 1 (log a_t = 0, no separate code). The gate alone is
+               form 1 without the correction term: the new value is added,
+               not corrected, S_t = a_t S_{t-1} + b_t k_t v_t^T, keeping b_t
+               as the write strength (b_t = 1 gives plain gated linear
+               attention); readout as in R1.
 
 Array conventions (all functions): q, k [T, Hqk, dk]; v [T, Hv, dv];
 log_alpha, beta [T, Hv]; init_state / final_state [N, Hv, dk, dv];
@@ -109,6 +117,29 @@ def recurrent_form1(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None):
             u = b[t][:, None] * (v[t] - a[:, None] * pred)
             S = a[:, None, None] * S + kt[:, :, None] * u[:, None, :]
             o[t] = np.einsum("hkv,hk->hv", S, qt)         # S_t^T q_t
+        final[n] = S
+    return o, final
+
+
+def recurrent_gated_no_delta(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None):
+    """Token-serial recurrence of the gate-only variant (reading R7).
+
+    For each sequence and V head: S <- S_0; per token
+      a = exp(log_alpha), S <- a S + b k v^T, o = S^T q.
+    Returns (o [T,Hv,dv], final_state [N,Hv,dk,dv]).
+    """
+    q, k, v, la, b, s0, bounds, grp = _prep(q, k, v, log_alpha, beta,
+                                            init_state, cu_seqlens)
+    o = np.zeros(v.shape)
+    final = np.empty_like(s0)
+    for n, (t0, t1) in enumerate(bounds):
+        S = s0[n].copy()                                  # [Hv, dk, dv]
+        for t in range(t0, t1):
+            a = np.exp(la[t])                             # [Hv]
+            kt = k[t, grp]                                # [Hv, dk]
+            u = b[t][:, None] * v[t]                      # written as is
+            S = a[:, None, None] * S + kt[:, :, None] * u[:, None, :]
+            o[t] = np.einsum("hkv,hk->hv", S, q[t, grp])  # S_t^T q_t
         final[n] = S
     return o, final
 
@@ -225,3 +256,12 @@ def decode_step(state, q, k, v, log_alpha, beta):
     cu = np.arange(n + 1)
     return recurrent_form1(q, k, v, log_alpha, beta, init_state=state,
                            cu_seqlens=cu)
+
+
+def decode_step_no_delta(state, q, k, v, log_alpha, beta):
+    """One token per sequence of the gate-only variant (reading R7); same
+    arguments and results as decode_step."""
+    n = np.asarray(q).shape[0]
+    cu = np.arange(n + 1)
+    return recurrent_gated_no_delta(q, k, v, log_alpha, beta, init_state=state,
+                                    cu_seqlens=cu)

@@ -379,3 +379,70 @@ def test_prepared_inputs_give_unit_keys_so_recall_is_exact():
     o2, s2 = O.recurrent_form2(q, k, v, la, beta)
     assert np.allclose(o1, o2, rtol=1e-12, atol=1e-13) and np.allclose(s1, s2, rtol=1e-12, atol=1e-13)
     assert np.all(np.abs(s1) < 1e3)
+
+
+# --- gate-only variant (reading R7: S <- a S + b k v^T, o = S^T q) ---------
+
+def test_gate_only_equals_masked_attention_closed_form():
+    # Unrolling S_t = a_t S_{t-1} + b_t k_t v_t^T gives, with G the running
+    # sum of log a over the sequence,
+    #   o_t = exp(G_t) S_0^T q_t + sum_{i<=t} exp(G_t - G_i) b_i (q_t . k_i) v_i
+    #   S_T = exp(G_T) S_0 + sum_i exp(G_T - G_i) b_i k_i v_i^T,
+    # evaluated here as one dense masked product per head.
+    rng = np.random.default_rng(41)
+    T, h_qk, h_v, d = 23, 2, 4, 5
+    q, k, v, la, beta, s0 = rand_inputs(rng, T, h_qk, h_v, d, d, n_init=1)
+    o, fin = O.recurrent_gated_no_delta(q, k, v, la, beta, s0)
+    for h in range(h_v):
+        hq = h // (h_v // h_qk)
+        G = np.cumsum(la[:, h])
+        mask = np.tril(np.exp(G[:, None] - G[None, :]))
+        scores = (q[:, hq] @ k[:, hq].T) * mask
+        want_o = scores @ (beta[:, h, None] * v[:, h]) + np.exp(G)[:, None] * (q[:, hq] @ s0[0, h])
+        w = np.exp(G[-1] - G) * beta[:, h]
+        want_s = np.exp(G[-1]) * s0[0, h] + k[:, hq].T @ (w[:, None] * v[:, h])
+        assert rel(o[:, h], want_o) < 1e-12
+        assert rel(fin[0, h], want_s) < 1e-12
+
+
+def test_gate_only_is_causal_linear_attention_when_a_b_are_one():
+    # a = b = 1, S_0 = 0: o_t = sum_{i<=t} (q_t . k_i) v_i, written as a loop
+    # over pairs
+    rng = np.random.default_rng(42)
+    T, d = 9, 3
+    q, k, v, _, _, _ = rand_inputs(rng, T, 1, 1, d, d, unit=False)
+    o, _ = O.recurrent_gated_no_delta(q, k, v, np.zeros((T, 1)), np.ones((T, 1)))
+    for t in range(T):
+        want = sum(float(q[t, 0] @ k[i, 0]) * v[i, 0] for i in range(t + 1))
+        assert np.allclose(o[t, 0], want, rtol=0, atol=1e-13)
+
+
+def test_gate_only_equals_delta_rule_for_orthogonal_fresh_keys():
+    # With S_0 = 0 and mutually orthogonal keys, S_{t-1}^T k_t = 0 at every
+    # step, so the delta rule's correction vanishes and both rules agree;
+    # with a repeated key they must differ.
+    rng = np.random.default_rng(43)
+    T, d = 6, 8
+    q, _, v, la, beta, _ = rand_inputs(rng, T, 1, 2, d, d)
+    k = np.zeros((T, 1, d))
+    for t, j in enumerate(rng.permutation(d)[:T]):
+        k[t, 0, j] = 1.0
+    o1, f1 = O.recurrent_form1(q, k, v, la, beta)
+    o2, f2 = O.recurrent_gated_no_delta(q, k, v, la, beta)
+    assert rel(o2, o1) < 1e-14 and rel(f2, f1) < 1e-14
+    k[3] = k[1]
+    o1, _ = O.recurrent_form1(q, k, v, la, beta)
+    o2, _ = O.recurrent_gated_no_delta(q, k, v, la, beta)
+    assert rel(o2, o1) > 1e-3
+
+
+def test_gate_only_decode_steps_equal_prefill():
+    rng = np.random.default_rng(44)
+    T, h_qk, h_v, d = 7, 1, 3, 4
+    q, k, v, la, beta, s0 = rand_inputs(rng, T, h_qk, h_v, d, d, n_init=1)
+    want_o, want_f = O.recurrent_gated_no_delta(q, k, v, la, beta, s0)
+    S = s0
+    for t in range(T):
+        o, S = O.decode_step_no_delta(S, q[t:t + 1], k[t:t + 1], v[t:t + 1], la[t:t + 1], beta[t:t + 1])
+        assert rel(o[0], want_o[t]) < 1e-13
+    assert rel(S, want_f) < 1e-13

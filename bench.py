@@ -315,6 +315,19 @@ def main():
     line["prepare_inputs"] = {"prefill_ms": round(pf_prep, 4), "prefill_tokens_per_s": round(T / (pf_prep * 1e-3), 1),
                               "decode_ms": round(dec_prep, 4),
                               "decode_GBps": round(dec_bytes / (dec_prep * 1e-3) / 1e9, 1)}
+    # the gate-only variant (S <- a S + b k v^T) on the same inputs, per
+    # kernel; DeltaNet (log a = 0) runs the kernels timed above unchanged
+    def gate_only_stage(s):
+        gdn.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                          inp["init_state"], None, chunk=C, workspace=ws, o=o, final_state=fin,
+                          stages=(s, s), delta_rule=False)
+    go_ms = [timed(lambda s=s: gate_only_stage(s)) for s in range(1, NST + 1)]
+    dec_go = timed(lambda: gdn.gdn_decode_step(dec["q"][0], dec["k"][0], dec["v"][0], dec["log_alpha"][0],
+                                               dec["beta"][0], state, o=o_dec, delta_rule=False))
+    line["gate_only"] = {"prefill_ms": round(sum(go_ms), 4), "prefill_tokens_per_s": round(T / (sum(go_ms) * 1e-3), 1),
+                         "kernel_ms": {n: round(t, 4) for n, t in zip(STAGES, go_ms)},
+                         "decode_ms": round(dec_go, 4),
+                         "decode_GBps": round(dec_bytes / (dec_go * 1e-3) / 1e9, 1)}
     print(json.dumps(line), flush=True)
 
 

@@ -60,8 +60,15 @@ typedef enum {
  *   log(alpha) = -softplus(a) and beta = sigmoid(b). Section 2.1 makes
  *   the gates data-dependent; these maps are the ones of the configured
  *   input recipe.
+ * GDN_FLAG_NO_DELTA_RULE: the gate-only variant that section 2.1 sets
+ *   against the gated delta rule (the Mamba2-style forget gate without the
+ *   delta rule's correction): S_t = alpha_t S_{t-1} + beta_t k_t v_t^T, with
+ *   the same readout o_t = S_t^T q_t, gates, layouts and workspace. beta = 1
+ *   gives plain gated linear attention. The delta rule alone (DeltaNet)
+ *   needs no flag: it is log_alpha = 0.
+ * The flags combine.
  */
-enum { GDN_FLAG_PREPARE_INPUTS = 1 };
+enum { GDN_FLAG_PREPARE_INPUTS = 1, GDN_FLAG_NO_DELTA_RULE = 2 };
 
 typedef struct {
   int64_t num_seqs;     /* N >= 1: packed sequences (prefill) or batch (decode) */
@@ -72,7 +79,7 @@ typedef struct {
   int32_t dv;           /* value head dim (must equal dk) */
   int32_t chunk;        /* prefill chunk length C (ignored by decode) */
   int32_t dtype;        /* gdn_dtype_t of q, k, v, o */
-  int32_t flags;        /* 0 or GDN_FLAG_PREPARE_INPUTS */
+  int32_t flags;        /* 0 or an OR of GDN_FLAG_PREPARE_INPUTS, GDN_FLAG_NO_DELTA_RULE */
 } gdn_dims_t;
 
 /*

@@ -89,6 +89,11 @@ def _check(status):
 
 
 GDN_FLAG_PREPARE_INPUTS = 1
+GDN_FLAG_NO_DELTA_RULE = 2
+
+
+def _flags(prepare_inputs, delta_rule):
+    return (GDN_FLAG_PREPARE_INPUTS if prepare_inputs else 0) | (0 if delta_rule else GDN_FLAG_NO_DELTA_RULE)
 
 
 def make_dims(num_seqs, total_tokens, h_qk, h_v, dk, dv, chunk, dtype, flags=0):
@@ -135,14 +140,15 @@ def gdn_chunk_fwd_workspace_layout(dims):
 
 def gdn_chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, chunk=64,
                   output_final_state=True, workspace=None, o=None, final_state=None,
-                  stages=None, prepare_inputs=False):
+                  stages=None, prepare_inputs=False, delta_rule=True):
     """Prefill through gdn_chunk_fwd. Shapes: q, k [T,Hqk,d]; v [T,Hv,d];
     log_alpha, beta [T,Hv] fp32; init_state [N,Hv,d,d] fp32 or None;
     cu_seqlens int32 [N+1] or None. Returns (o, final_state or None).
     `workspace` (uint8 CUDA tensor) may be passed to reuse scratch memory.
     `stages=(first, last)` calls gdn_chunk_fwd_stages instead (diagnostic).
     `prepare_inputs=True` sets GDN_FLAG_PREPARE_INPUTS: q, k raw and
-    log_alpha, beta holding the gate logits."""
+    log_alpha, beta holding the gate logits. `delta_rule=False` sets
+    GDN_FLAG_NO_DELTA_RULE: the gate-only update S = a S + b k v^T."""
     lib = load_library()
     dev = q.device
     if dev.type != "cuda":
@@ -161,8 +167,7 @@ def gdn_chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, ch
         _need(cu_seqlens, "cu_seqlens", dev, torch.int32, (n + 1,))
     if q.dtype not in GDN_DTYPE:
         raise ValueError(f"unsupported dtype {q.dtype}")
-    dims = make_dims(n, T, h_qk, h_v, d, v.shape[2], chunk, q.dtype,
-                     GDN_FLAG_PREPARE_INPUTS if prepare_inputs else 0)
+    dims = make_dims(n, T, h_qk, h_v, d, v.shape[2], chunk, q.dtype, _flags(prepare_inputs, delta_rule))
     nbytes = gdn_chunk_fwd_workspace_bytes(dims)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -184,10 +189,10 @@ def gdn_chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, ch
     return o, final_state
 
 
-def gdn_decode_step(q, k, v, log_alpha, beta, state, o=None, prepare_inputs=False):
+def gdn_decode_step(q, k, v, log_alpha, beta, state, o=None, prepare_inputs=False, delta_rule=True):
     """One decode step through gdn_decode_step. q, k [N,Hqk,d]; v [N,Hv,d];
     log_alpha, beta [N,Hv] fp32; state [N,Hv,d,d] fp32 (updated in place).
-    Returns o [N,Hv,d]. `prepare_inputs` as for gdn_chunk_fwd."""
+    Returns o [N,Hv,d]. `prepare_inputs`, `delta_rule` as for gdn_chunk_fwd."""
     lib = load_library()
     dev = q.device
     if dev.type != "cuda":
@@ -205,19 +210,20 @@ def gdn_decode_step(q, k, v, log_alpha, beta, state, o=None, prepare_inputs=Fals
     if o is None:
         o = torch.empty_like(v)
     _need(o, "o", dev, v.dtype, tuple(v.shape))
-    dims = make_dims(n, n, h_qk, h_v, d, v.shape[2], 0, q.dtype,
-                     GDN_FLAG_PREPARE_INPUTS if prepare_inputs else 0)
+    dims = make_dims(n, n, h_qk, h_v, d, v.shape[2], 0, q.dtype, _flags(prepare_inputs, delta_rule))
     _check(lib.gdn_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                                _ptr(beta), _ptr(state), _ptr(o), _stream(dev)))
     return o
 
 
-def gdn_decode_multi(q, k, v, log_alpha, beta, state, o=None, snapshots=None, prepare_inputs=False):
+def gdn_decode_multi(q, k, v, log_alpha, beta, state, o=None, snapshots=None, prepare_inputs=False,
+                     delta_rule=True):
     """K drafted tokens per sequence through gdn_decode_multi. q, k [K,N,Hqk,d];
     v [K,N,Hv,d]; log_alpha, beta [K,N,Hv] fp32; state [N,Hv,d,d] fp32.
     With `snapshots` ([K,N,Hv,d,d] fp32) the state after each token goes there
     and `state` is only read; without, `state` ends as the state after all K
-    tokens. Returns o [K,N,Hv,d]. `prepare_inputs` as for gdn_chunk_fwd."""
+    tokens. Returns o [K,N,Hv,d]. `prepare_inputs`, `delta_rule` as for
+    gdn_chunk_fwd."""
     lib = load_library()
     dev = q.device
     if dev.type != "cuda":
@@ -237,8 +243,7 @@ def gdn_decode_multi(q, k, v, log_alpha, beta, state, o=None, snapshots=None, pr
     _need(o, "o", dev, v.dtype, tuple(v.shape))
     if snapshots is not None:
         _need(snapshots, "snapshots", dev, torch.float32, (kt, n, h_v, d, dv))
-    dims = make_dims(n, n, h_qk, h_v, d, dv, 0, q.dtype,
-                     GDN_FLAG_PREPARE_INPUTS if prepare_inputs else 0)
+    dims = make_dims(n, n, h_qk, h_v, d, dv, 0, q.dtype, _flags(prepare_inputs, delta_rule))
     _check(lib.gdn_decode_multi(ctypes.byref(dims), int(kt), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                                 _ptr(beta), _ptr(state), _ptr(o),
                                 _ptr(snapshots) if snapshots is not None else None, _stream(dev)))

@@ -48,7 +48,7 @@ gdn_status_t check_dims(const gdn_dims_t* d, bool decode) {
   if (d->dk < 1 || d->dv < 1) return fail(GDN_ERROR_INVALID_VALUE, "dk and dv must be >= 1");
   if (d->dtype != GDN_DTYPE_F32 && d->dtype != GDN_DTYPE_BF16)
     return fail(GDN_ERROR_INVALID_VALUE, "unknown dtype %d", d->dtype);
-  if (d->flags & ~GDN_FLAG_PREPARE_INPUTS) return fail(GDN_ERROR_INVALID_VALUE, "unknown flags 0x%x", d->flags);
+  if (d->flags & ~(GDN_FLAG_PREPARE_INPUTS | GDN_FLAG_NO_DELTA_RULE)) return fail(GDN_ERROR_INVALID_VALUE, "unknown flags 0x%x", d->flags);
   if (d->dk != d->dv) return fail(GDN_ERROR_NOT_SUPPORTED, "dk != dv is not supported (dk=%d dv=%d)", d->dk, d->dv);
   if (d->dk != 16 && d->dk != 128) return fail(GDN_ERROR_NOT_SUPPORTED, "head dim %d not supported (16 or 128)", d->dk);
   if (decode) {
@@ -205,6 +205,7 @@ gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims, const void* q, const v
   a.h_v = d.h_v;
   a.group = d.h_v / d.h_qk;
   a.prep = (d.flags & GDN_FLAG_PREPARE_INPUTS) ? 1 : 0;
+  a.no_delta = (d.flags & GDN_FLAG_NO_DELTA_RULE) ? 1 : 0;
   return launch_status(gdn::launch_prefill(a, d.dtype, d.dk, d.chunk, stream, first_stage, last_stage),
                        "gdn_chunk_fwd launch");
 }
@@ -239,6 +240,7 @@ gdn_status_t gdn_decode_step(const gdn_dims_t* dims, const void* q, const void* 
   a.num_tokens = 1;
   a.snapshots = nullptr;
   a.prep = (d.flags & GDN_FLAG_PREPARE_INPUTS) ? 1 : 0;
+  a.no_delta = (d.flags & GDN_FLAG_NO_DELTA_RULE) ? 1 : 0;
   return launch_status(gdn::launch_decode(a, d.dtype, d.dk, stream), "gdn_decode_step launch");
 }
 
@@ -277,6 +279,7 @@ gdn_status_t gdn_decode_multi(const gdn_dims_t* dims, int32_t num_tokens, const 
   a.num_tokens = num_tokens;
   a.snapshots = snapshots;
   a.prep = (d.flags & GDN_FLAG_PREPARE_INPUTS) ? 1 : 0;
+  a.no_delta = (d.flags & GDN_FLAG_NO_DELTA_RULE) ? 1 : 0;
   return launch_status(gdn::launch_decode_multi(a, d.dtype, d.dk, stream), "gdn_decode_multi launch");
 }
 

@@ -15,6 +15,9 @@
 // the update is applied from registers and stored. Loads and stores are
 // non-temporal: the state is touched once per step and is larger than the
 // last-level cache.
+//
+// The gate-only variant (S <- a S + b k v^T, the same readout) is the same
+// pass with u = b v: S^T k is then not formed.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -26,7 +29,7 @@ template <int D> struct DecodeShape;
 template <> struct DecodeShape<128> { static constexpr int RG = 8; };
 template <> struct DecodeShape<16> { static constexpr int RG = 4; };
 
-template <typename E, int D, bool P>
+template <typename E, int D, bool P, bool ND>
 __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_step(const DecodeArgs a) {
   constexpr int CG = D / 4, RG = DecodeShape<D>::RG, RPT = D / RG;
   __shared__ f32x4 red_p[RG][CG];
@@ -53,7 +56,7 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
   float kq = 0.f, k2 = 0.f, q2 = 0.f;
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
-    p += s[r] * kk[r];
+    if constexpr (!ND) p += s[r] * kk[r];
     rq += s[r] * qq[r];
     kq += kk[r] * qq[r];
   }
@@ -61,7 +64,7 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
 #pragma unroll
     for (int r = 0; r < RPT; ++r) { k2 += kk[r] * kk[r]; q2 += qq[r] * qq[r]; }
   }
-  red_p[rg][cg] = p;
+  if constexpr (!ND) red_p[rg][cg] = p;
   red_r[rg][cg] = rq;
   if (cg == 0) {
     red_kq[rg][0] = kq;
@@ -75,7 +78,7 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
   q2 = 0.f;
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
-    p += red_p[g][cg];
+    if constexpr (!ND) p += red_p[g][cg];
     rq += red_r[g][cg];
     kq += red_kq[g][0];
     if constexpr (P) { k2 += red_kq[g][1]; q2 += red_kq[g][2]; }
@@ -99,7 +102,7 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
   const E* vp = static_cast<const E*>(a.v) + nh * D + 4 * cg;
   f32x4 u;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) u[e] = beta * (to_f(vp[e]) - alpha * p[e]);
+  for (int e = 0; e < 4; ++e) u[e] = ND ? beta * to_f(vp[e]) : beta * (to_f(vp[e]) - alpha * p[e]);
 
 #pragma unroll
   for (int r = 0; r < RPT; ++r) __builtin_nontemporal_store(s[r] * alpha + u * kk[r], sp + r * CG);
@@ -125,7 +128,7 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
 // snapshot j and `state` is only read (so a caller can keep any accepted
 // prefix); without one, the final state replaces `state`. Each token's
 // arithmetic is the single-step kernel's, term for term.
-template <typename E, int D, bool P>
+template <typename E, int D, bool P, bool ND>
 __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_multi(const DecodeArgs a) {
   constexpr int CG = D / 4, RG = DecodeShape<D>::RG, RPT = D / RG;
   __shared__ f32x4 red_p[2][RG][CG];
@@ -155,7 +158,7 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_mu
     float kq = 0.f, k2 = 0.f, q2 = 0.f;
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-      p += s[r] * kk[r];
+      if constexpr (!ND) p += s[r] * kk[r];
       rq += s[r] * qq[r];
       kq += kk[r] * qq[r];
     }
@@ -163,7 +166,7 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_mu
 #pragma unroll
       for (int r = 0; r < RPT; ++r) { k2 += kk[r] * kk[r]; q2 += qq[r] * qq[r]; }
     }
-    red_p[par][rg][cg] = p;
+    if constexpr (!ND) red_p[par][rg][cg] = p;
     red_r[par][rg][cg] = rq;
     if (cg == 0) {
       red_kq[par][rg][0] = kq;
@@ -177,7 +180,7 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_mu
     q2 = 0.f;
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
-      p += red_p[par][g][cg];
+      if constexpr (!ND) p += red_p[par][g][cg];
       rq += red_r[par][g][cg];
       kq += red_kq[par][g][0];
       if constexpr (P) { k2 += red_kq[par][g][1]; q2 += red_kq[par][g][2]; }
@@ -200,7 +203,7 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_mu
     const E* vp = static_cast<const E*>(a.v) + tv * D + 4 * cg;
     f32x4 u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) u[e] = beta * (to_f(vp[e]) - alpha * p[e]);
+    for (int e = 0; e < 4; ++e) u[e] = ND ? beta * to_f(vp[e]) : beta * (to_f(vp[e]) - alpha * p[e]);
 #pragma unroll
     for (int r = 0; r < RPT; ++r) s[r] = s[r] * alpha + u * kk[r];
     if (a.snapshots) {
@@ -225,10 +228,14 @@ template <typename E, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   constexpr int threads = (D / 4) * DecodeShape<D>::RG;
   const unsigned blocks = (unsigned)(a.num_seqs * a.h_v);
-  if (a.prep)
-    gdn_kd_decode_step<E, D, true><<<dim3(blocks), dim3(threads), 0, s>>>(a);
-  else
-    gdn_kd_decode_step<E, D, false><<<dim3(blocks), dim3(threads), 0, s>>>(a);
+  const dim3 g(blocks), b(threads);
+  if (a.prep) {
+    if (a.no_delta) gdn_kd_decode_step<E, D, true, true><<<g, b, 0, s>>>(a);
+    else gdn_kd_decode_step<E, D, true, false><<<g, b, 0, s>>>(a);
+  } else {
+    if (a.no_delta) gdn_kd_decode_step<E, D, false, true><<<g, b, 0, s>>>(a);
+    else gdn_kd_decode_step<E, D, false, false><<<g, b, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -236,10 +243,14 @@ template <typename E, int D>
 hipError_t launch_decode_multi_t(const DecodeArgs& a, hipStream_t s) {
   constexpr int threads = (D / 4) * DecodeShape<D>::RG;
   const unsigned blocks = (unsigned)(a.num_seqs * a.h_v);
-  if (a.prep)
-    gdn_kd_decode_multi<E, D, true><<<dim3(blocks), dim3(threads), 0, s>>>(a);
-  else
-    gdn_kd_decode_multi<E, D, false><<<dim3(blocks), dim3(threads), 0, s>>>(a);
+  const dim3 g(blocks), b(threads);
+  if (a.prep) {
+    if (a.no_delta) gdn_kd_decode_multi<E, D, true, true><<<g, b, 0, s>>>(a);
+    else gdn_kd_decode_multi<E, D, true, false><<<g, b, 0, s>>>(a);
+  } else {
+    if (a.no_delta) gdn_kd_decode_multi<E, D, false, true><<<g, b, 0, s>>>(a);
+    else gdn_kd_decode_multi<E, D, false, false><<<g, b, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -38,6 +38,7 @@ struct PrefillArgs {
   int32_t h_v;              // HV
   int32_t group;            // HV / HQ
   int32_t prep;             // 1: raw q, k and gate logits (fused input preparation)
+  int32_t no_delta;         // 1: gate-only update S = a S + b k v^T
 };
 
 struct DecodeArgs {
@@ -58,6 +59,7 @@ struct DecodeArgs {
   int32_t num_tokens;
   float* snapshots;
   int32_t prep;             // 1: raw q, k and gate logits (fused input preparation)
+  int32_t no_delta;         // 1: gate-only update S = a S + b k v^T
 };
 
 // Prefill launch stages (1-based): 1 chunk preparation (table, gate prefix sums,

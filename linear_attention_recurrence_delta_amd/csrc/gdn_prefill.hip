@@ -289,7 +289,7 @@ struct InvSmem {
   float gb[2][C];                      // g and b of this V head
 };
 
-template <typename E, int D, int C, bool P>
+template <typename E, int D, int C, bool P, bool ND>
 __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   using SM = InvSmem<E, D, C>;
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
   // that they arrive during the inverse
   const int ksd = wave;
   Frag<E> kta[CKS], ktb[CKS];
-  if (ksd < DKS) {
+  if (!ND && ksd < DKS) {
     const Frag<E>* ktg = reinterpret_cast<const Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
 #pragma unroll
     for (int s = 0; s < CKS; ++s) {
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
       if (tid + p * kBlock < G::QK_FR * 64) qkr[p] = qkg[tid + p * kBlock];
   }
   const E* kg = static_cast<const E*>(a.k);
-  for (int idx = tid; idx < C * D / VE; idx += kBlock) {
+  for (int idx = tid; !ND && idx < C * D / VE; idx += kBlock) {
     const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
     VLoad kv;
 #pragma unroll
@@ -381,6 +381,23 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
     } else if (tid < C + 4) {
       dtg[C + tid] = (tid == C) ? __expf(gl) : 0.f;
     }
+  }
+  if constexpr (ND) {
+    // gate-only variant: no delta rule, so Tinv = I; the scan's Ut = diag(b) V
+    // takes diag(b) in place of Tinv diag(b), and W is not used
+    Frag<E>* tg = reinterpret_cast<Frag<E>*>(a.tinv) + (c * a.h_v + hv) * G::T_FR * 64;
+    for (int it = tid; it < G::T_FR * 64; it += kBlock) {
+      const int f = it / 64, ln = it % 64, rt = f / CKS, s = f % CKS, q4 = ln >> 4;
+      const int r = 16 * rt + (ln & 15);
+      Frag<E> vb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = frag_k(s, q4, e);
+        vb[e] = to_e<E>((i == r) ? sm.gb[1][r] : 0.f);
+      }
+      tg[it] = vb;
+    }
+    return;
   }
 
   // K K^T tiles on and below the diagonal, lower tile t -> (mi, ni)
@@ -548,7 +565,7 @@ __device__ __forceinline__ void copy_1k(const char* src, char* dst, int bytes, i
   if (16 * lane < bytes) __builtin_amdgcn_global_load_lds(src + 16 * lane, (lds_ptr_t)dst, 16, 0, 0);
 }
 
-template <typename E, int D, int C>
+template <typename E, int D, int C, bool ND>
 __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   constexpr int DT = G::DT, CT = G::CT, DKS = G::DKS, CKS = G::CKS, NS = G::NS, BV = G::BV;
@@ -585,7 +602,9 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
 
   // ---- direct copies into LDS: chunk xs's scan operands, chunk xp's Ut
   // operands; the window's jobs are dealt round-robin to the loader waves ----
-  constexpr int B_KT = G::KT_FR * FB, B_W = G::W_FR * FB, B_Q = G::Q_FR * FB, B_P = G::QK_FR * FB;
+  // (the gate-only variant reads no W: its region, copies and warm-up lines
+  // have zero size)
+  constexpr int B_KT = G::KT_FR * FB, B_W = ND ? 0 : G::W_FR * FB, B_Q = G::Q_FR * FB, B_P = G::QK_FR * FB;
   constexpr int B_T = G::T_FR * FB, B_V = C * BV * ESZ, B_D = (2 * C + 4) * 4;
   constexpr int NREG = 7;
   constexpr int JOBS[NREG] = {(B_KT + 1023) / 1024, (B_W + 1023) / 1024, (B_Q + 1023) / 1024,
@@ -691,7 +710,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
 #pragma unroll
     for (int t = 0; t < CT; ++t) {
       qa[t] = sm.qf[par][(t * DKS) * 64 + lane];
-      wa[t] = sm.wf[par][(t * DKS) * 64 + lane];
+      if constexpr (!ND) wa[t] = sm.wf[par][(t * DKS) * 64 + lane];
     }
 #pragma unroll
     for (int ks = 0; ks < DKS; ++ks) {
@@ -700,17 +719,20 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
 #pragma unroll
         for (int t = 0; t < CT; ++t) {
           qn[t] = sm.qf[par][(t * DKS + ks + 1) * 64 + lane];
-          wn[t] = sm.wf[par][(t * DKS + ks + 1) * 64 + lane];
+          if constexpr (!ND) wn[t] = sm.wf[par][(t * DKS + ks + 1) * 64 + lane];
         }
       }
 #pragma unroll
       for (int t = 0; t < CT; ++t) {
         O[t] = mma(Sf[ks], qa[t], O[t]);
-        WS[t] = mma(wa[t], Sf[ks], WS[t]);
+        if constexpr (!ND) WS[t] = mma(wa[t], Sf[ks], WS[t]);
       }
       if (ks + 1 < DKS) {
 #pragma unroll
-        for (int t = 0; t < CT; ++t) { qa[t] = qn[t]; wa[t] = wn[t]; }
+        for (int t = 0; t < CT; ++t) {
+          qa[t] = qn[t];
+          if constexpr (!ND) wa[t] = wn[t];
+        }
       }
     }
     // U = Ut - W S; the inter-chunk output takes exp(g_r); the row factors
@@ -720,7 +742,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     f32x4 U[CT];
 #pragma unroll
     for (int t = 0; t < CT; ++t) {
-      U[t] = sm.uf[par][(slice * CT + t) * 64 + lane] - WS[t];
+      U[t] = ND ? sm.uf[par][(slice * CT + t) * 64 + lane] : sm.uf[par][(slice * CT + t) * 64 + lane] - WS[t];
       O[t] *= ea[16 * t + l16];
     }
     Frag<E> Uk[CKS];
@@ -871,19 +893,27 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
   const unsigned scan_groups = (unsigned)(a.num_seqs * a.h_v * G::NCB);
   for (int stage = first; stage <= last; ++stage) {
     switch (stage) {
-      case 1:
-        if (a.prep)
-          gdn_k1_chunk_prep<E, D, C, true><<<dim3(nc, (unsigned)a.h_qk), dim3(kBlock), 0, s>>>(a);
-        else
-          gdn_k1_chunk_prep<E, D, C, false><<<dim3(nc, (unsigned)a.h_qk), dim3(kBlock), 0, s>>>(a);
+      case 1: {
+        const dim3 g(nc, (unsigned)a.h_qk);
+        if (a.prep) gdn_k1_chunk_prep<E, D, C, true><<<g, dim3(kBlock), 0, s>>>(a);
+        else gdn_k1_chunk_prep<E, D, C, false><<<g, dim3(kBlock), 0, s>>>(a);
         break;
-      case 2:
-        if (a.prep)
-          gdn_k2_inverse_w<E, D, C, true><<<dim3(nc * (unsigned)a.h_v), dim3(kBlock), 0, s>>>(a);
-        else
-          gdn_k2_inverse_w<E, D, C, false><<<dim3(nc * (unsigned)a.h_v), dim3(kBlock), 0, s>>>(a);
+      }
+      case 2: {
+        const dim3 g(nc * (unsigned)a.h_v);
+        if (a.prep) {
+          if (a.no_delta) gdn_k2_inverse_w<E, D, C, true, true><<<g, dim3(kBlock), 0, s>>>(a);
+          else gdn_k2_inverse_w<E, D, C, true, false><<<g, dim3(kBlock), 0, s>>>(a);
+        } else {
+          if (a.no_delta) gdn_k2_inverse_w<E, D, C, false, true><<<g, dim3(kBlock), 0, s>>>(a);
+          else gdn_k2_inverse_w<E, D, C, false, false><<<g, dim3(kBlock), 0, s>>>(a);
+        }
         break;
-      case 3: gdn_k3_scan<E, D, C><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a); break;
+      }
+      case 3:
+        if (a.no_delta) gdn_k3_scan<E, D, C, true><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a);
+        else gdn_k3_scan<E, D, C, false><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a);
+        break;
       default: return hipErrorInvalidValue;
     }
   }

@@ -66,7 +66,7 @@ def ws_bytes(lib, d):
     (dict(dk=128, dv=64), NOT_SUPPORTED),
     (dict(chunk=32), NOT_SUPPORTED),
     (dict(dtype=0), NOT_SUPPORTED),          # fp32 at head dim 128 needs chunk 16
-    (dict(flags=2), INVALID),                # unknown flag
+    (dict(flags=4), INVALID),                # unknown flag
     (dict(flags=-1), INVALID),
 ])
 def test_dims_validation(lib, kw, status):
@@ -181,10 +181,18 @@ def test_decode_multi_validation(lib):
     assert call(dims(num_seqs=1 << 20, total_tokens=1 << 20), kt=1 << 12) == NOT_SUPPORTED
 
 
-def test_prepare_inputs_flag_is_accepted(lib):
-    d = dims(flags=B.GDN_FLAG_PREPARE_INPUTS)
+@pytest.mark.parametrize("flags", [1, 2, 3])
+def test_flags_are_accepted_and_keep_the_workspace(lib, flags):
+    assert B.GDN_FLAG_PREPARE_INPUTS == 1 and B.GDN_FLAG_NO_DELTA_RULE == 2
+    d = dims(flags=flags)
     assert ws_bytes(lib, d) == ws_bytes(lib, dims())
     assert ctypes.sizeof(B.GdnDims) == 48
+
+
+def test_header_flag_values_match_the_binding():
+    text = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    assert re.search(r"GDN_FLAG_PREPARE_INPUTS = 1\b", text)
+    assert re.search(r"GDN_FLAG_NO_DELTA_RULE = 2\b", text)
 
 
 def test_status_strings(lib):

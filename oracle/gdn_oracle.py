@@ -35,6 +35,13 @@ where the page is silent (each one is listed with the design notes):
                not corrected, S_t = a_t S_{t-1} + b_t k_t v_t^T, keeping b_t
                as the write strength (b_t = 1 gives plain gated linear
                attention); readout as in R1.
+  R8 gradients the pages train the layer but print no backward pass. The
+               gradient of a scalar loss L is its definition: given dL/do
+               for every token and dL/dS for each sequence's final state,
+               backpropagation through the form-1 steps of R1, token by
+               token in reverse, gives dL/dq, dL/dk, dL/dv, dL/dlog a, dL/db
+               and dL/dS_0. A QK head's dq and dk sum over the V heads that
+               read it.
 
 Array conventions (all functions): q, k [T, Hqk, dk]; v [T, Hv, dv];
 log_alpha, beta [T, Hv]; init_state / final_state [N, Hv, dk, dv];
@@ -142,6 +149,73 @@ def recurrent_gated_no_delta(q, k, v, log_alpha, beta, init_state=None, cu_seqle
             o[t] = np.einsum("hkv,hk->hv", S, q[t, grp])  # S_t^T q_t
         final[n] = S
     return o, final
+
+
+def recurrent_form1_backward(q, k, v, log_alpha, beta, do, dfinal=None, init_state=None,
+                             cu_seqlens=None):
+    """Gradients through the form-1 recurrence (reading R8).
+
+    do = dL/do [T,Hv,dv]; dfinal = dL/dS_final [N,Hv,dk,dv] or None (zero).
+    Returns a dict: dq, dk [T,Hqk,dk]; dv [T,Hv,dv]; dlog_alpha, dbeta
+    [T,Hv]; dinit [N,Hv,dk,dv]. Per token, with G = dL/dS_t carried from the
+    end of the sequence backwards:
+      o = S_t^T q             ->  G += q do^T,  dq += S_t do
+      S_t = a S_{t-1} + k u^T ->  du = G^T k,  dk += G u,
+                                  da = <S_{t-1}, G>,  dS_{t-1} = a G
+      u = b (v - a p)         ->  db = (v - a p).du,  dv = b du,
+                                  da -= b p.du,  dp = -a b du
+      p = S_{t-1}^T k         ->  dS_{t-1} += k dp^T,  dk += S_{t-1} dp
+      a = exp(log a)          ->  dlog a = a da
+    and dL/dS_0 is G after the first token.
+    """
+    q, k, v, la, b, s0, bounds, grp = _prep(q, k, v, log_alpha, beta,
+                                            init_state, cu_seqlens)
+    do = np.asarray(do, dtype=np.float64)
+    out = dict(dq=np.zeros(q.shape), dk=np.zeros(k.shape), dv=np.zeros(v.shape),
+               dlog_alpha=np.zeros(la.shape), dbeta=np.zeros(b.shape), dinit=np.zeros(s0.shape))
+    for n, (t0, t1) in enumerate(bounds):
+        # forward pass, keeping the state before every token
+        S = s0[n].copy()
+        before = []
+        for t in range(t0, t1):
+            before.append(S)
+            a = np.exp(la[t])
+            kt = k[t, grp]
+            pred = np.einsum("hkv,hk->hv", S, kt)
+            u = b[t][:, None] * (v[t] - a[:, None] * pred)
+            S = a[:, None, None] * S + kt[:, :, None] * u[:, None, :]
+        G = np.zeros_like(S) if dfinal is None else np.asarray(dfinal, dtype=np.float64)[n].copy()
+        for t in range(t1 - 1, t0 - 1, -1):
+            Sp = before[t - t0]
+            a = np.exp(la[t])
+            kt = k[t, grp]
+            qt = q[t, grp]
+            pred = np.einsum("hkv,hk->hv", Sp, kt)
+            resid = v[t] - a[:, None] * pred
+            u = b[t][:, None] * resid
+            St = a[:, None, None] * Sp + kt[:, :, None] * u[:, None, :]
+            # readout
+            G = G + qt[:, :, None] * do[t][:, None, :]
+            dq_h = np.einsum("hkv,hv->hk", St, do[t])
+            # state update
+            du = np.einsum("hkv,hk->hv", G, kt)
+            dk_h = np.einsum("hkv,hv->hk", G, u)
+            da = np.sum(G * Sp, axis=(1, 2))
+            Gp = a[:, None, None] * G
+            # corrected value
+            out["dbeta"][t] = np.sum(resid * du, axis=1)
+            out["dv"][t] = b[t][:, None] * du
+            da -= b[t] * np.sum(pred * du, axis=1)
+            dp = -(a * b[t])[:, None] * du
+            # prediction
+            Gp += kt[:, :, None] * dp[:, None, :]
+            dk_h += np.einsum("hkv,hv->hk", Sp, dp)
+            out["dlog_alpha"][t] = a * da
+            np.add.at(out["dq"][t], grp, dq_h)
+            np.add.at(out["dk"][t], grp, dk_h)
+            G = Gp
+        out["dinit"][n] = G
+    return out
 
 
 def recurrent_form2(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None):

@@ -446,3 +446,75 @@ def test_gate_only_decode_steps_equal_prefill():
         o, S = O.decode_step_no_delta(S, q[t:t + 1], k[t:t + 1], v[t:t + 1], la[t:t + 1], beta[t:t + 1])
         assert rel(o[0], want_o[t]) < 1e-13
     assert rel(S, want_f) < 1e-13
+
+
+# --- gradients (reading R8: backpropagation through form 1) ----------------
+
+def _loss(q, k, v, la, beta, s0, cu, ro, rf):
+    o, fin = O.recurrent_form1(q, k, v, la, beta, s0, cu)
+    return float(np.sum(o * ro) + np.sum(fin * rf))
+
+
+def test_backward_equals_central_differences_on_every_input():
+    # L = <o, R_o> + <S_final, R_f>; each partial derivative is checked by a
+    # central difference of the forward oracle (step 1e-5, error O(1e-10))
+    rng = np.random.default_rng(51)
+    lens = [3, 2]
+    T, h_qk, h_v, d = sum(lens), 1, 2, 3
+    q, k, v, la, beta, s0 = rand_inputs(rng, T, h_qk, h_v, d, d, n_init=2)
+    beta = beta * 1.5                       # b over (0, 1.5): exercises b > 1 too
+    cu = np.array([0, 3, 5])
+    ro = rng.standard_normal((T, h_v, d))
+    rf = rng.standard_normal((2, h_v, d, d))
+    g = O.recurrent_form1_backward(q, k, v, la, beta, ro, rf, s0, cu)
+    args = dict(q=q, k=k, v=v, la=la, beta=beta, s0=s0)
+    names = dict(q="dq", k="dk", v="dv", la="dlog_alpha", beta="dbeta", s0="dinit")
+    eps = 1e-5
+    for name, x in args.items():
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp = _loss(cu=cu, ro=ro, rf=rf, **args)
+            x[idx] = keep - eps
+            lm = _loss(cu=cu, ro=ro, rf=rf, **args)
+            x[idx] = keep
+            num[idx] = (lp - lm) / (2 * eps)
+        assert rel(g[names[name]], num) < 1e-8, name
+
+
+def test_backward_with_head_groups_and_no_final_gradient():
+    # two V heads per QK head: dq and dk sum over the group; dfinal = None
+    rng = np.random.default_rng(52)
+    T, h_qk, h_v, d = 4, 2, 4, 2
+    q, k, v, la, beta, s0 = rand_inputs(rng, T, h_qk, h_v, d, d, n_init=1)
+    ro = rng.standard_normal((T, h_v, d))
+    g = O.recurrent_form1_backward(q, k, v, la, beta, ro, None, s0)
+    eps = 1e-5
+    for name, x in (("dq", q), ("dk", k)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp = _loss(q, k, v, la, beta, s0, None, ro, 0.0)
+            x[idx] = keep - eps
+            lm = _loss(q, k, v, la, beta, s0, None, ro, 0.0)
+            x[idx] = keep
+            num[idx] = (lp - lm) / (2 * eps)
+        assert rel(g[name], num) < 1e-8, name
+
+
+def test_backward_closed_form_for_pure_decay():
+    # b = 0 and do = 0: S_T = exp(sum log a) S_0, so dL/dS_0 = exp(sum log a) R
+    # and dL/dlog a_t = <S_T, R> for every token; nothing else has gradient
+    rng = np.random.default_rng(53)
+    T, d = 6, 4
+    q, k, v, la, _, s0 = rand_inputs(rng, T, 1, 1, d, d, n_init=1)
+    beta = np.zeros((T, 1))
+    R = rng.standard_normal((1, 1, d, d))
+    g = O.recurrent_form1_backward(q, k, v, la, beta, np.zeros((T, 1, d)), R, s0)
+    decay = np.exp(la[:, 0].sum())
+    assert rel(g["dinit"], decay * R) < 1e-14
+    assert np.allclose(g["dlog_alpha"][:, 0], np.sum(decay * s0 * R), rtol=1e-13, atol=0)
+    for name in ("dq", "dk", "dv"):
+        assert np.abs(g[name]).max() == 0.0

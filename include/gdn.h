@@ -142,6 +142,64 @@ gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims,
 size_t gdn_chunk_fwd_workspace_bytes(const gdn_dims_t* dims);
 
 /*
+ * Backward pass of gdn_chunk_fwd: gradients of a scalar loss L with respect
+ * to every input, given dL/do and dL/d(final state). Section 2.1 presents
+ * the chunkwise algorithm as the way to train the layer; the gradients are
+ * the derivative of the token-serial update (backpropagation through it),
+ * evaluated chunkwise: the forward kernels are run again, the state
+ * gradient is carried over the chunks in reverse order, and the per-chunk
+ * gradients are formed from it. flags must be 0 (GDN_ERROR_NOT_SUPPORTED
+ * otherwise).
+ *
+ *  q, k, v, log_alpha, beta, init_state, cu_seqlens: as for gdn_chunk_fwd
+ *  d_o          [T, h_v, dv] dtype: dL/do
+ *  d_final_state [N, h_v, dk, dv] fp32 or NULL (zero): dL/d(final state)
+ *  dq, dk       [T, h_qk, dk] dtype, written: a QK head's gradient sums
+ *               over the V heads that read it
+ *  dv           [T, h_v, dv] dtype, written
+ *  dlog_alpha, dbeta [T, h_v] fp32, written: dL/d(log a_t), dL/db_t
+ *  d_init_state [N, h_v, dk, dv] fp32 or NULL: dL/d(init_state), written;
+ *               may alias d_final_state exactly, not init_state
+ *  workspace    device scratch of at least gdn_chunk_bwd_workspace_bytes()
+ *               bytes, 256-byte aligned, owned by the caller; contents on
+ *               return unspecified
+ * The gradients must not alias an input or each other. Returns GDN_SUCCESS
+ * once all kernels are enqueued.
+ */
+gdn_status_t gdn_chunk_bwd(const gdn_dims_t* dims,
+                           const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta,
+                           const float* init_state, const int32_t* cu_seqlens,
+                           const void* d_o, const float* d_final_state,
+                           void* dq, void* dk, void* dv,
+                           float* dlog_alpha, float* dbeta, float* d_init_state,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
+ * Diagnostic variant of gdn_chunk_bwd enqueuing launches first..last only
+ * (for events between them): 1-3 = the forward kernels (also writing the
+ * backward operands; stage 3 stores the state at each chunk start and the
+ * chunk's U rows instead of outputs), 4 = the reverse state scan, 5 = the
+ * gradient kernel. A call starting at stage s > 1 must follow calls that ran
+ * stages 1..s-1 with identical arguments and workspace on the same stream.
+ * Returns GDN_ERROR_INVALID_VALUE unless 1 <= first_stage <= last_stage <= 5.
+ */
+gdn_status_t gdn_chunk_bwd_stages(const gdn_dims_t* dims,
+                                  const void* q, const void* k, const void* v,
+                                  const float* log_alpha, const float* beta,
+                                  const float* init_state, const int32_t* cu_seqlens,
+                                  const void* d_o, const float* d_final_state,
+                                  void* dq, void* dk, void* dv,
+                                  float* dlog_alpha, float* dbeta, float* d_init_state,
+                                  void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream, int first_stage, int last_stage);
+
+/* Workspace bytes gdn_chunk_bwd needs (gdn_chunk_fwd's and the backward
+ * operands); 0 if dims are invalid or unsupported. */
+size_t gdn_chunk_bwd_workspace_bytes(const gdn_dims_t* dims);
+
+/*
  * One decode step: one new token for each of N independent sequences, the
  * single-token form of the update in section 2.1 applied in place:
  *     p = S^T k, u = b (v - a p), S <- a S + k u^T, o = S^T q.

@@ -19,6 +19,7 @@ STATUS = {0: "GDN_SUCCESS", 1: "GDN_ERROR_INVALID_VALUE", 2: "GDN_ERROR_NOT_SUPP
 
 # Names the library must export (every function declared in include/gdn.h).
 EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_stages", "gdn_chunk_fwd_workspace_bytes",
+           "gdn_chunk_bwd", "gdn_chunk_bwd_stages", "gdn_chunk_bwd_workspace_bytes",
            "gdn_decode_step", "gdn_decode_multi", "gdn_status_string", "gdn_last_error_message",
            "gdn_chunk_fwd_workspace_layout")
 
@@ -69,6 +70,13 @@ def load_library(path=None):
     lib.gdn_chunk_fwd_workspace_bytes.restype = sz
     lib.gdn_chunk_fwd_workspace_layout.argtypes = [dims_p, ctypes.POINTER(GdnWorkspaceLayout)]
     lib.gdn_chunk_fwd_workspace_layout.restype = i32
+    bwd = [dims_p, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_chunk_bwd.argtypes = bwd
+    lib.gdn_chunk_bwd.restype = i32
+    lib.gdn_chunk_bwd_stages.argtypes = bwd + [i32, i32]
+    lib.gdn_chunk_bwd_stages.restype = i32
+    lib.gdn_chunk_bwd_workspace_bytes.argtypes = [dims_p]
+    lib.gdn_chunk_bwd_workspace_bytes.restype = sz
     lib.gdn_decode_step.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_decode_step.restype = i32
     lib.gdn_decode_multi.argtypes = [dims_p, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -187,6 +195,67 @@ def gdn_chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, ch
     else:
         _check(lib.gdn_chunk_fwd_stages(*args, int(stages[0]), int(stages[1])))
     return o, final_state
+
+
+def gdn_chunk_bwd_workspace_bytes(dims):
+    n = load_library().gdn_chunk_bwd_workspace_bytes(ctypes.byref(dims))
+    if n == 0:
+        raise GdnError(2 if dims.flags else 1, load_library().gdn_last_error_message().decode())
+    return n
+
+
+def gdn_chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, cu_seqlens=None, d_final_state=None,
+                  chunk=64, workspace=None, grads=None, stages=None):
+    """Backward pass through gdn_chunk_bwd: gradients of a scalar loss given
+    d_o = dL/do [T,Hv,d] (dtype of v) and d_final_state = dL/d(final state)
+    [N,Hv,d,d] fp32 or None. Other arguments as for gdn_chunk_fwd. Returns a
+    dict dq, dk [T,Hqk,d]; dv [T,Hv,d] (input dtype); dlog_alpha, dbeta
+    [T,Hv] fp32; d_init_state [N,Hv,d,d] fp32. `grads` (a dict of the same
+    tensors) may be passed to reuse outputs; `stages=(first, last)` calls
+    gdn_chunk_bwd_stages (diagnostic)."""
+    lib = load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_chunk_bwd needs CUDA (HIP) tensors")
+    T, h_qk, d = q.shape
+    h_v, dv = v.shape[1], v.shape[2]
+    n = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _need(q, "q", dev, shape=(T, h_qk, d))
+    _need(k, "k", dev, q.dtype, (T, h_qk, d))
+    _need(v, "v", dev, q.dtype, (T, h_v, dv))
+    _need(log_alpha, "log_alpha", dev, torch.float32, (T, h_v))
+    _need(beta, "beta", dev, torch.float32, (T, h_v))
+    _need(d_o, "d_o", dev, q.dtype, (T, h_v, dv))
+    if init_state is not None:
+        _need(init_state, "init_state", dev, torch.float32, (n, h_v, d, dv))
+    if d_final_state is not None:
+        _need(d_final_state, "d_final_state", dev, torch.float32, (n, h_v, d, dv))
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", dev, torch.int32, (n + 1,))
+    if q.dtype not in GDN_DTYPE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dims = make_dims(n, T, h_qk, h_v, d, dv, chunk, q.dtype)
+    nbytes = gdn_chunk_bwd_workspace_bytes(dims)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", dev, torch.uint8)
+    if grads is None:
+        grads = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                     dlog_alpha=torch.empty_like(log_alpha), dbeta=torch.empty_like(beta),
+                     d_init_state=torch.empty((n, h_v, d, dv), dtype=torch.float32, device=dev))
+    for name, ref in (("dq", q), ("dk", k), ("dv", v), ("dlog_alpha", log_alpha), ("dbeta", beta)):
+        _need(grads[name], name, dev, ref.dtype, tuple(ref.shape))
+    if grads.get("d_init_state") is not None:
+        _need(grads["d_init_state"], "d_init_state", dev, torch.float32, (n, h_v, d, dv))
+    args = (ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state),
+            _ptr(cu_seqlens), _ptr(d_o), _ptr(d_final_state), _ptr(grads["dq"]), _ptr(grads["dk"]),
+            _ptr(grads["dv"]), _ptr(grads["dlog_alpha"]), _ptr(grads["dbeta"]), _ptr(grads.get("d_init_state")),
+            _ptr(workspace), workspace.numel(), _stream(dev))
+    if stages is None:
+        _check(lib.gdn_chunk_bwd(*args))
+    else:
+        _check(lib.gdn_chunk_bwd_stages(*args, int(stages[0]), int(stages[1])))
+    return grads
 
 
 def gdn_decode_step(q, k, v, log_alpha, beta, state, o=None, prepare_inputs=False, delta_rule=True):

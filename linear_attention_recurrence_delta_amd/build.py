@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_prefill.hip", "gdn_decode.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_prefill.hip", "gdn_decode.hip", "gdn_backward.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are disabled for all device code. MFMA results

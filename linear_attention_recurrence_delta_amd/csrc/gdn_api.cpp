@@ -98,6 +98,41 @@ Layout compute_layout(const gdn_dims_t& d) {
   return L;
 }
 
+// Backward workspace: the forward regions, then the backward operands, each
+// 256-byte aligned.
+struct BwdLayout {
+  Layout fwd;
+  size_t k_frag, q_t, kq, pt, wt, tt, sc, ub, dsl, du, total;
+};
+
+BwdLayout compute_bwd_layout(const gdn_dims_t& d) {
+  const size_t esz = d.dtype == GDN_DTYPE_F32 ? 4 : 2;
+  const size_t D = d.dk, C = d.chunk, N = d.num_seqs, T = d.total_tokens;
+  const size_t HQ = d.h_qk, HV = d.h_v;
+  const size_t CT = C / 16, DT = D / 16, CKS = (CT + 1) / 2, DKS = (DT + 1) / 2;
+  const size_t NC = T / C + N;
+  BwdLayout L;
+  L.fwd = compute_layout(d);
+  size_t off = L.fwd.v.total;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes, 256);
+    return o;
+  };
+  L.k_frag = take(NC * HQ * CT * DKS * 512 * esz);
+  L.q_t = take(NC * HQ * DT * CKS * 512 * esz);
+  L.kq = take(NC * HQ * CT * CKS * 512 * esz);
+  L.pt = take(NC * HV * CT * CKS * 512 * esz);
+  L.wt = take(NC * HV * DT * CKS * 512 * esz);
+  L.tt = take(NC * HV * C * C * esz);
+  L.sc = take(NC * HV * D * D * esz);
+  L.ub = take(NC * HV * C * D * esz);
+  L.dsl = take(NC * HV * D * D * esz);
+  L.du = take(NC * HV * C * D * esz);
+  L.total = off;
+  return L;
+}
+
 gdn_status_t launch_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(GDN_ERROR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -208,6 +243,123 @@ gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims, const void* q, const v
   a.no_delta = (d.flags & GDN_FLAG_NO_DELTA_RULE) ? 1 : 0;
   return launch_status(gdn::launch_prefill(a, d.dtype, d.dk, d.chunk, stream, first_stage, last_stage),
                        "gdn_chunk_fwd launch");
+}
+
+size_t gdn_chunk_bwd_workspace_bytes(const gdn_dims_t* dims) {
+  if (check_dims(dims, false) != GDN_SUCCESS) return 0;
+  if (dims->flags) {
+    fail(GDN_ERROR_NOT_SUPPORTED, "the backward pass takes no flags (got 0x%x)", dims->flags);
+    return 0;
+  }
+  ok();
+  return compute_bwd_layout(*dims).total;
+}
+
+gdn_status_t gdn_chunk_bwd(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, const float* init_state,
+                           const int32_t* cu_seqlens, const void* d_o, const float* d_final_state, void* dq,
+                           void* dk, void* dv, float* dlog_alpha, float* dbeta, float* d_init_state,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return gdn_chunk_bwd_stages(dims, q, k, v, log_alpha, beta, init_state, cu_seqlens, d_o, d_final_state, dq, dk,
+                              dv, dlog_alpha, dbeta, d_init_state, workspace, workspace_bytes, stream, 1,
+                              gdn::kBackwardStages);
+}
+
+gdn_status_t gdn_chunk_bwd_stages(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+                                  const float* log_alpha, const float* beta, const float* init_state,
+                                  const int32_t* cu_seqlens, const void* d_o, const float* d_final_state,
+                                  void* dq, void* dk, void* dv, float* dlog_alpha, float* dbeta,
+                                  float* d_init_state, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream, int first_stage, int last_stage) {
+  if (first_stage < 1 || last_stage > gdn::kBackwardStages || first_stage > last_stage)
+    return fail(GDN_ERROR_INVALID_VALUE, "stages %d..%d: need 1 <= first <= last <= %d", first_stage,
+                last_stage, gdn::kBackwardStages);
+  gdn_status_t st = check_dims(dims, false);
+  if (st != GDN_SUCCESS) return st;
+  const gdn_dims_t& d = *dims;
+  if (d.flags) return fail(GDN_ERROR_NOT_SUPPORTED, "the backward pass takes no flags (got 0x%x)", d.flags);
+  if (!cu_seqlens && d.num_seqs != 1)
+    return fail(GDN_ERROR_INVALID_VALUE, "cu_seqlens is NULL but num_seqs = %lld", (long long)d.num_seqs);
+  if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(GDN_ERROR_INVALID_VALUE, "cu_seqlens is not 4-byte aligned");
+  if (d.total_tokens > 0) {
+    const void* need[] = {q, k, v, d_o, dq, dk, dv, log_alpha, beta, dlog_alpha, dbeta};
+    const char* names[] = {"q", "k", "v", "d_o", "dq", "dk", "dv", "log_alpha", "beta", "dlog_alpha", "dbeta"};
+    for (int i = 0; i < 11; ++i) {
+      const size_t al = i < 7 ? 16 : 4;
+      if (!need[i]) return fail(GDN_ERROR_INVALID_VALUE, "%s is NULL", names[i]);
+      if (!aligned(need[i], al)) return fail(GDN_ERROR_INVALID_VALUE, "%s is not %zu-byte aligned", names[i], al);
+    }
+    const void* ins[] = {q, k, v, log_alpha, beta, d_o};
+    const void* outs[] = {dq, dk, dv, dlog_alpha, dbeta};
+    for (const void* o : outs) {
+      for (const void* i : ins)
+        if (o == i) return fail(GDN_ERROR_INVALID_VALUE, "the gradients must not alias an input");
+    }
+    for (int i = 0; i < 5; ++i)
+      for (int j = i + 1; j < 5; ++j)
+        if (outs[i] == outs[j]) return fail(GDN_ERROR_INVALID_VALUE, "two gradient outputs alias");
+  }
+  if (init_state && !aligned(init_state, 16)) return fail(GDN_ERROR_INVALID_VALUE, "init_state is not 16-byte aligned");
+  if (d_final_state && !aligned(d_final_state, 16))
+    return fail(GDN_ERROR_INVALID_VALUE, "d_final_state is not 16-byte aligned");
+  if (d_init_state && !aligned(d_init_state, 16))
+    return fail(GDN_ERROR_INVALID_VALUE, "d_init_state is not 16-byte aligned");
+  if (d_init_state && d_init_state == init_state)
+    return fail(GDN_ERROR_INVALID_VALUE, "d_init_state must not alias init_state");
+  const BwdLayout L = compute_bwd_layout(d);
+  if (!workspace) return fail(GDN_ERROR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
+  if (!aligned(workspace, 256)) return fail(GDN_ERROR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(GDN_ERROR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, L.total);
+
+  char* ws = static_cast<char*>(workspace);
+  const gdn_workspace_layout_t& F = L.fwd.v;
+  gdn::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_alpha = log_alpha;
+  a.beta = beta;
+  a.init_state = init_state;
+  a.cu_seqlens = cu_seqlens;
+  a.chunk_table = reinterpret_cast<int32_t*>(ws + F.chunk_table);
+  a.seq_chunk_offset = reinterpret_cast<int32_t*>(ws + F.seq_chunk_offset);
+  a.gate_prefix = reinterpret_cast<float*>(ws + F.gate_prefix);
+  a.beta_chunk = reinterpret_cast<float*>(ws + F.beta_chunk);
+  a.tinv = ws + F.tinv;
+  a.w = ws + F.w;
+  a.key_t = ws + F.key_t;
+  a.qk = ws + F.qk;
+  a.q_frag = ws + F.q_frag;
+  a.pmask = ws + F.pmask;
+  a.dtab = reinterpret_cast<float*>(ws + F.dtab);
+  a.k_frag = ws + L.k_frag;
+  a.q_t = ws + L.q_t;
+  a.kq = ws + L.kq;
+  a.pt = ws + L.pt;
+  a.wt = ws + L.wt;
+  a.tt = ws + L.tt;
+  a.sc = ws + L.sc;
+  a.ub = ws + L.ub;
+  a.dsl = ws + L.dsl;
+  a.du = ws + L.du;
+  a.d_o = d_o;
+  a.d_final = d_final_state;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dlog_alpha = dlog_alpha;
+  a.dbeta = dbeta;
+  a.d_init = d_init_state;
+  a.num_seqs = d.num_seqs;
+  a.total_tokens = d.total_tokens;
+  a.max_chunks = F.max_chunks;
+  a.h_qk = d.h_qk;
+  a.h_v = d.h_v;
+  a.group = d.h_v / d.h_qk;
+  return launch_status(gdn::launch_backward(a, d.dtype, d.dk, d.chunk, stream, first_stage, last_stage),
+                       "gdn_chunk_bwd launch");
 }
 
 gdn_status_t gdn_decode_step(const gdn_dims_t* dims, const void* q, const void* k, const void* v,

@@ -1,0 +1,648 @@
+// Backward pass (gdn_chunk_bwd): gradients of a scalar loss through the
+// chunkwise evaluation of the gated delta rule of page "Qwen3.8-Flash-Next
+// 技术总结", section 2.1 (Gated DeltaNet). The section presents the chunkwise
+// algorithm as the way to train the layer; it prints no backward pass, so
+// the formulas below are the derivative of the forward block formulas
+// (gdn_prefill.hip). For one V head and a chunk entering with state S0 and
+// leaving with S_L, with dO = dL/dO and dS_L = dL/dS_L (ea_r = exp(g_r),
+// ed_r = exp(g_L - g_r), P = Q K^T * Dincl, Gm[r,i] = exp(g_r - g_i)):
+//
+//   reverse state scan, chunks in reverse order (dS carries dL/dS):
+//     dU     = diag(ed) K dS_L + P^T dO
+//     dS0    = exp(g_L) dS_L + Q^T diag(ea) dO - W^T dU
+//   per chunk and V head (gradient kernel):
+//     dQ     = diag(ea) dO S0^T + (dP * Dincl) K,     dP = dO U^T
+//     dK     = (dP * Dincl)^T Q + diag(ed) U dS_L^T + diag(b ea) Tinv^T dW
+//              + (B + B^T) K,                          dW = -dU S0^T
+//     dV     = diag(b) Tinv^T dU
+//     dA     = -Tinv^T dT Tinv^T (strictly lower),    dT = dU (diag(b) V)^T + dW (diag(b ea) K)^T
+//     B      = dA * b_r Gm,  M = B * (K K^T)
+//     db_r   = (Tinv^T dU)_r . v_r + ea_r (Tinv^T dW)_r . k_r + sum_i dA[r,i] (k_r . k_i) Gm[r,i]
+//     dg_r   = b_r ea_r (Tinv^T dW)_r . k_r + rowsum(M)_r - colsum(M)_r
+//              + q_r . (ea_r (dO S0^T)_r) + rowsum(dP * P)_r - colsum(dP * P)_r
+//              - ed_r k_r . (U dS_L^T)_r    (+ at r = L: the sum of those terms
+//              and exp(g_L) <S0, dS_L>)
+//     dlog a = the suffix sums of dg within the chunk.
+// A QK head's dq and dk sum over its V heads.
+//
+// Launches: kernel 1 and kernel 2 of the forward pass, also writing the
+// backward operands (K and Q^T fragments, the query-indexed q.k products,
+// P^T and W^T fragments, Tinv^T); kernel 3 in its saving form (the state at
+// every chunk start and the U rows, no outputs); the reverse state scan
+// (gdn_kb_dstate); the gradient kernel (gdn_kb_grad).
+#include <type_traits>
+
+#include "gdn_device.h"
+#include "gdn_internal.h"
+#include "gdn_tiles.h"
+
+namespace gdn {
+
+namespace {
+
+// --------------------------------------------------------------------------
+// Reverse state scan: one workgroup per (sequence, V head, block of BV state
+// columns); the NS scan waves hold dS for their 16-column slices in MFMA
+// accumulators and walk the chunks from last to first; the other waves
+// copy chunk c-1's operands into the idle LDS buffer (direct global-to-LDS
+// loads) while chunk c is processed. Per chunk the scan waves store dS_L
+// and dU (rounded to the input dtype, as the gradient kernel's products use
+// them); after the first chunk dS is dL/dS0 of the sequence.
+// --------------------------------------------------------------------------
+template <typename E, int D, int C>
+struct DScanSmem {
+  using G = Cfg<E, D, C>;
+  Frag<E> kf[2][G::Q_FR * 64];       // K fragments (row r, k = d)
+  Frag<E> pt[2][G::QK_FR * 64];      // P^T fragments (row key j, k = query r)
+  Frag<E> qt[2][G::KT_FR * 64];      // Q^T fragments (row d, k = token r)
+  Frag<E> wt[2][G::KT_FR * 64];      // W^T fragments (row d, k = token r)
+  E dor[2][C * G::BV];               // dL/do rows, this block's columns
+  float dtab[2][2 * C + 4] __attribute__((aligned(16)));
+};
+
+template <typename E, int D, int C>
+__global__ __launch_bounds__(kBlock) void gdn_kb_dstate(const PrefillArgs a) {
+  using G = Cfg<E, D, C>;
+  constexpr int DT = G::DT, CT = G::CT, DKS = G::DKS, CKS = G::CKS, NS = G::NS, BV = G::BV;
+  constexpr int NLD = kBlock / 64 - NS;
+  constexpr int FB = (int)sizeof(Frag<E>) * 64;
+  constexpr int ESZ = (int)sizeof(E);
+  __shared__ DScanSmem<E, D, C> sm;
+  const int tid = threadIdx.x, lane = tid & 63, quad = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bid = xcd_local_id(blockIdx.x, gridDim.x);
+  const int cb = (int)(bid % G::NCB);
+  const int hv = (int)((bid / G::NCB) % a.h_v);
+  const int64_t n = bid / ((int64_t)G::NCB * a.h_v);
+  const int hq = hv / a.group;
+  const int c0 = a.seq_chunk_offset[n], c1 = a.seq_chunk_offset[n + 1];
+  const int seq_start = a.cu_seqlens ? a.cu_seqlens[n] : 0;
+  const int seq_end = a.cu_seqlens ? a.cu_seqlens[n + 1] : (int)a.total_tokens;
+  auto chunk_start = [&](int x) { return seq_start + (x - c0) * C; };
+  auto chunk_len = [&](int x) { return min(C, seq_end - chunk_start(x)); };
+  const bool is_scan = wave < NS;
+  const int slice = wave, lw = wave - NS;
+  const int col0 = cb * BV;
+  const int64_t state_base = (n * a.h_v + hv) * D * D;
+
+  constexpr int B_KF = G::Q_FR * FB, B_PT = G::QK_FR * FB, B_QT = G::KT_FR * FB, B_WT = G::KT_FR * FB;
+  constexpr int B_O = C * BV * ESZ, B_D = (2 * C + 4) * 4;
+  constexpr int NREG = 6;
+  constexpr int JOBS[NREG] = {(B_KF + 1023) / 1024, (B_PT + 1023) / 1024, (B_QT + 1023) / 1024,
+                              (B_WT + 1023) / 1024, (B_D + 1023) / 1024,  (B_O + 1023) / 1024};
+  constexpr int CUM[NREG] = {0, JOBS[0], JOBS[0] + JOBS[1], JOBS[0] + JOBS[1] + JOBS[2],
+                             JOBS[0] + JOBS[1] + JOBS[2] + JOBS[3],
+                             JOBS[0] + JOBS[1] + JOBS[2] + JOBS[3] + JOBS[4]};
+  auto copy_region = [&](int r, const char* src, char* dst, int bytes) __attribute__((always_inline)) {
+    for (int jj = ((lw - CUM[r]) % NLD + NLD) % NLD; jj < JOBS[r]; jj += NLD)
+      copy_1k(src + 1024 * jj, dst + 1024 * jj, bytes - 1024 * jj, lane);
+  };
+  // chunk x's operands into buffer x & 1 (nothing before the sequence's
+  // first chunk)
+  auto copy_chunk = [&](int x) __attribute__((always_inline)) {
+    if (x < c0) return;
+    const int b = x & 1;
+    copy_region(0, static_cast<const char*>(a.k_frag) + ((int64_t)x * a.h_qk + hq) * B_KF,
+                reinterpret_cast<char*>(sm.kf[b]), B_KF);
+    copy_region(1, static_cast<const char*>(a.pt) + ((int64_t)x * a.h_v + hv) * B_PT,
+                reinterpret_cast<char*>(sm.pt[b]), B_PT);
+    copy_region(2, static_cast<const char*>(a.q_t) + ((int64_t)x * a.h_qk + hq) * B_QT,
+                reinterpret_cast<char*>(sm.qt[b]), B_QT);
+    copy_region(3, static_cast<const char*>(a.wt) + ((int64_t)x * a.h_v + hv) * B_WT,
+                reinterpret_cast<char*>(sm.wt[b]), B_WT);
+    copy_region(4, reinterpret_cast<const char*>(a.dtab + ((int64_t)x * a.h_v + hv) * (2 * C + 4)),
+                reinterpret_cast<char*>(sm.dtab[b]), B_D);
+    // dL/do rows of the block's columns, row i at byte i * BV * ESZ; rows
+    // past the chunk end repeat its last row (every product that reads
+    // them has zero factors there)
+    const int p_start = chunk_start(x), p_last = chunk_len(x) - 1;
+    char* dst = reinterpret_cast<char*>(sm.dor[b]);
+    for (int jj = ((lw - CUM[5]) % NLD + NLD) % NLD; jj < JOBS[5]; jj += NLD) {
+      const int o = 1024 * jj + 16 * lane;
+      const int i = min(o / (BV * ESZ), p_last);
+      const char* src = static_cast<const char*>(a.d_o) +
+                        (((int64_t)(p_start + i) * a.h_v + hv) * D + col0) * ESZ + o % (BV * ESZ);
+      if (o < B_O) __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(dst + 1024 * jj), 16, 0, 0);
+    }
+  };
+
+  f32x4 dS[DT];
+  auto dscan_chunk = [&](int c) __attribute__((always_inline)) {
+    const int par = c & 1;
+    // dS is dL/d(state at chunk c's end)
+    E* dslg = static_cast<E*>(a.dsl) + ((int64_t)c * a.h_v + hv) * D * D + col0 + 16 * slice + l16;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dslg[(16 * dt + 4 * quad + i) * D] = to_e<E>(dS[dt][i]);
+    }
+    Frag<E> dSf[DKS];
+#pragma unroll
+    for (int ks = 0; ks < DKS; ++ks) dSf[ks] = acc_to_frag<E>(dS[2 * ks], (2 * ks + 1 < DT) ? dS[2 * ks + 1] : zero4());
+    const float* ea = sm.dtab[par];
+    const float* ed = sm.dtab[par] + C;
+    // dU = diag(ed) K dS_L + P^T dO
+    f32x4 dU[CT];
+#pragma unroll
+    for (int t = 0; t < CT; ++t) {
+      dU[t] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks) dU[t] = mma(sm.kf[par][(t * DKS + ks) * 64 + lane], dSf[ks], dU[t]);
+      dU[t] *= *reinterpret_cast<const f32x4*>(&ed[16 * t + 4 * quad]);
+    }
+    // dL/do fragments (k = token r, column = state column), plain and
+    // scaled by exp(g_r)
+    Frag<E> dOf[CKS], gOf[CKS];
+#pragma unroll
+    for (int s = 0; s < CKS; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = frag_k(s, quad, e);
+        const E x = (r < C) ? sm.dor[par][r * BV + 16 * slice + l16] : to_e<E>(0.f);
+        dOf[s][e] = x;
+        gOf[s][e] = to_e<E>((r < C) ? to_f(x) * ea[r] : 0.f);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < CT; ++t) {
+#pragma unroll
+      for (int s = 0; s < CKS; ++s)
+        if (32 * s + 31 >= 16 * t) dU[t] = mma(sm.pt[par][(t * CKS + s) * 64 + lane], dOf[s], dU[t]);
+    }
+    E* dug = static_cast<E*>(a.du) + ((int64_t)c * a.h_v + hv) * C * D + col0 + 16 * slice + l16;
+#pragma unroll
+    for (int t = 0; t < CT; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dug[(16 * t + 4 * quad + i) * D] = to_e<E>(dU[t][i]);
+    }
+    Frag<E> nUf[CKS];
+#pragma unroll
+    for (int s = 0; s < CKS; ++s) nUf[s] = acc_to_frag<E>(-dU[2 * s], (2 * s + 1 < CT) ? -dU[2 * s + 1] : zero4());
+    // dS0 = exp(g_L) dS_L + Q^T diag(ea) dO - W^T dU
+    const float gam = sm.dtab[par][2 * C];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) dS[dt] *= gam;
+#pragma unroll
+    for (int s = 0; s < CKS; ++s) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dS[dt] = mma(sm.qt[par][(dt * CKS + s) * 64 + lane], gOf[s], dS[dt]);
+        dS[dt] = mma(sm.wt[par][(dt * CKS + s) * 64 + lane], nUf[s], dS[dt]);
+      }
+    }
+  };
+
+  auto state_index = [&](int dt, int i) {
+    return state_base + (int64_t)(16 * dt + 4 * quad + i) * D + col0 + 16 * slice + l16;
+  };
+  if (c1 > c0) {
+    if (is_scan) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dS[dt][i] = a.d_final ? a.d_final[state_index(dt, i)] : 0.f;
+      }
+      __syncthreads();
+      for (int c = c1 - 1; c >= c0; --c) {
+        dscan_chunk(c);
+        lds_barrier();
+      }
+      if (a.d_init) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a.d_init[state_index(dt, i)] = dS[dt][i];
+        }
+      }
+    } else {
+      copy_chunk(c1 - 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      for (int c = c1 - 1; c >= c0; --c) {
+        copy_chunk(c - 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
+    }
+  } else if (is_scan && a.d_init) {
+    // empty sequence: dL/dS0 is dL/d(final state)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a.d_init[state_index(dt, i)] = a.d_final ? a.d_final[state_index(dt, i)] : 0.f;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Gradient kernel: one workgroup per (chunk slot, QK head), 8 waves; the V
+// heads of the group are taken in turn and their dq, dk contributions stay
+// in registers (wave w owns the C x D output tiles t = w, w + 8, ...).
+// Operands are staged in LDS as rows; products with the chunk-start state
+// and dS_L read those row-major matrices straight from the workspace; the
+// C x C x C products of dA run in fp32 (v_mfma_f32_16x16x4_f32), every other
+// product on bf16 (or fp32) MFMA with fp32 accumulation. Row and column sums
+// of the per-element terms go through lane exchanges and LDS atomics.
+// --------------------------------------------------------------------------
+constexpr int kGradBlock = 512;
+
+template <typename E, int D, int C>
+struct GradSmem {
+  static constexpr int KLD = D + 8;    // row stride of the staged D-wide rows
+  static constexpr int FLD = C + 4;    // row stride of the fp32 C x C scratch
+  static constexpr int TLD = C + 8;    // row stride of Tinv^T
+  E ks[C * KLD] __attribute__((aligned(16)));
+  E qs[C * KLD] __attribute__((aligned(16)));
+  E r1[C * KLD] __attribute__((aligned(16)));   // dL/do rows, later v rows
+  E r2[C * KLD] __attribute__((aligned(16)));   // U rows, later dW rows
+  E r3[C * KLD] __attribute__((aligned(16)));   // dU rows
+  E tt[C * TLD] __attribute__((aligned(16)));   // Tinv^T rows
+  float x1[C * FLD] __attribute__((aligned(16)));
+  float x2[C * FLD] __attribute__((aligned(16)));
+  float g[C], b[C], ea[C], ed[C], dg[C], db[C];
+  float sums[2];                       // <S0, dS_L>; sum of the state-term row factors
+};
+
+// sum over the 16 lanes that hold one accumulator row's columns
+__device__ __forceinline__ float row_sum16(float x) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+// sum over the 4 lane quads (the rows of a column, after the lane's own 4)
+__device__ __forceinline__ float col_sum4q(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <typename E, int D, int C>
+__global__ __launch_bounds__(kGradBlock) void gdn_kb_grad(const PrefillArgs a) {
+  using G = Cfg<E, D, C>;
+  using SM = GradSmem<E, D, C>;
+  constexpr int DT = G::DT, CT = G::CT, DKS = G::DKS, CKS = G::CKS;
+  constexpr int KLD = SM::KLD, FLD = SM::FLD, TLD = SM::TLD;
+  constexpr int NW = kGradBlock / 64;
+  constexpr int NCD = CT * DT, TPW = (NCD + NW - 1) / NW;      // C x D tiles, per wave
+  constexpr int NCC = CT * CT, TPC = (NCC + NW - 1) / NW;      // C x C tiles, per wave
+  constexpr int VE = 16 / (int)sizeof(E);
+  typedef E VLoad __attribute__((ext_vector_type(VE)));
+  __shared__ SM sm;
+  const int64_t c = blockIdx.x;
+  const int hq = blockIdx.y;
+  const int4 tab = reinterpret_cast<const int4*>(a.chunk_table)[c];
+  if (tab.x < 0) return;
+  const int start = tab.y, len = tab.z;
+  // lane indices are re-made opaque at the top of every V head's pass (see
+  // there); the wave index is uniform
+  int tid = threadIdx.x, lane = tid & 63, quad = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // rows [0, C) of a [T][H][D] input into LDS (zero past the chunk end)
+  auto stage_rows = [&](E* dst, const void* src, int heads, int head) __attribute__((always_inline)) {
+    const E* sg = static_cast<const E*>(src);
+    for (int idx = tid; idx < C * D / VE; idx += kGradBlock) {
+      const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
+      VLoad x;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) x[e] = to_e<E>(0.f);
+      if (r < len) x = *reinterpret_cast<const VLoad*>(sg + ((int64_t)(start + r) * heads + head) * D + d);
+      *reinterpret_cast<VLoad*>(&dst[r * KLD + d]) = x;
+    }
+  };
+  // rows of a [C][D] workspace matrix into LDS
+  auto stage_ws = [&](E* dst, const E* src) __attribute__((always_inline)) {
+    for (int idx = tid; idx < C * D / VE; idx += kGradBlock) {
+      const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
+      *reinterpret_cast<VLoad*>(&dst[r * KLD + d]) = *reinterpret_cast<const VLoad*>(src + r * D + d);
+    }
+  };
+  // operand fragments: rows (contraction along a row) and columns
+  // (contraction down a column) of LDS matrices, for 32-step s
+  auto frag_row = [&](const E* m, int ld, int row0, int s, int kext) __attribute__((always_inline)) {
+    return load_frag<E>(m + (row0 + l16) * ld + 32 * s, quad, kext - 32 * s);
+  };
+  auto frag_row32 = [&](const float* m, int ld, int row0, int s, int kext) __attribute__((always_inline)) {
+    const float* p = m + (row0 + l16) * ld + 32 * s;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(p + 4 * quad);
+    const f32x4 hi = (kext - 32 * s > 16) ? *reinterpret_cast<const f32x4*>(p + 16 + 4 * quad) : zero4();
+    return acc_to_frag<E>(lo, hi);
+  };
+  auto frag_col = [&](const auto* m, int ld, int col0, int s, int kext) __attribute__((always_inline)) {
+    Frag<E> f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = frag_k(s, quad, e);
+      f[e] = to_e<E>((k < kext) ? to_f(m[k * ld + col0 + l16]) : 0.f);
+    }
+    return f;
+  };
+
+  stage_rows(sm.ks, a.k, a.h_qk, hq);
+  stage_rows(sm.qs, a.q, a.h_qk, hq);
+  f32x4 dQ[TPW], dK[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) { dQ[u] = zero4(); dK[u] = zero4(); }
+  const Frag<E>* ktf = reinterpret_cast<const Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
+  const Frag<E>* qtf = reinterpret_cast<const Frag<E>*>(a.q_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
+
+  for (int h = 0; h < a.group; ++h) {
+    const int hv = hq * a.group + h;
+    const int64_t ch = c * a.h_v + hv;
+    // keeps the compiler from hoisting every lane-dependent address out of
+    // this loop (they would stay live across it and spill); recomputing
+    // them is a few ALU operations
+    asm volatile("" : "+v"(tid), "+v"(lane), "+v"(quad), "+v"(l16));
+    __syncthreads();                   // the previous V head's LDS reads are done
+    if (tid < C) {
+      sm.g[tid] = a.gate_prefix[ch * C + tid];
+      sm.b[tid] = a.beta_chunk[ch * C + tid];
+      sm.ea[tid] = a.dtab[ch * (2 * C + 4) + tid];
+      sm.ed[tid] = a.dtab[ch * (2 * C + 4) + C + tid];
+      sm.dg[tid] = 0.f;
+      sm.db[tid] = 0.f;
+    }
+    if (tid < 2) sm.sums[tid] = 0.f;
+    const float gl = a.dtab[ch * (2 * C + 4) + 2 * C];
+    stage_rows(sm.r1, a.d_o, a.h_v, hv);
+    stage_ws(sm.r2, static_cast<const E*>(a.ub) + ch * C * D);
+    stage_ws(sm.r3, static_cast<const E*>(a.du) + ch * C * D);
+    {
+      const E* tg = static_cast<const E*>(a.tt) + ch * C * C;
+      for (int idx = tid; idx < C * C; idx += kGradBlock) sm.tt[(idx / C) * TLD + idx % C] = tg[idx];
+    }
+    __syncthreads();
+
+    // dO S0^T, U dS_L^T, -dU S0^T and <S0, dS_L>
+    const E* scg = static_cast<const E*>(a.sc) + ch * D * D;
+    const E* dsg = static_cast<const E*>(a.dsl) + ch * D * D;
+    f32x4 dW[TPW];
+    float fro = 0.f;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = wave + NW * u;
+      dW[u] = zero4();
+      if (t >= NCD) continue;
+      const int rt = t / DT, dt = t % DT;
+      f32x4 aq = zero4(), ak = zero4(), aw = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks) {
+        const Frag<E> bs = load_frag<E>(scg + (16 * dt + l16) * D + 32 * ks, quad, D - 32 * ks);
+        const Frag<E> bl = load_frag<E>(dsg + (16 * dt + l16) * D + 32 * ks, quad, D - 32 * ks);
+        aq = mma(frag_row(sm.r1, KLD, 16 * rt, ks, D), bs, aq);
+        ak = mma(frag_row(sm.r2, KLD, 16 * rt, ks, D), bl, ak);
+        aw = mma(frag_row(sm.r3, KLD, 16 * rt, ks, D), bs, aw);
+        if (rt == 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) fro += to_f(bs[e]) * to_f(bl[e]);
+        }
+      }
+      dW[u] = -aw;
+      const int d = 16 * dt + l16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * quad + i;
+        const float eq = aq[i] * sm.ea[r];
+        dQ[u][i] += eq;
+        dK[u][i] += ak[i] * sm.ed[r];
+        const float pq = row_sum16(eq * to_f(sm.qs[r * KLD + d]));
+        const float pk = row_sum16(sm.ed[r] * ak[i] * to_f(sm.ks[r * KLD + d]));
+        if (l16 == 0) {
+          atomicAdd(&sm.dg[r], pq - pk);
+          atomicAdd(&sm.sums[1], pk);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one tile's operands live at a time
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) fro += __shfl_xor(fro, m);
+    if (lane == 0) atomicAdd(&sm.sums[0], fro);
+
+    // dP = dO U^T: dP * P into dg, dPm = dP * Dincl into x1
+    const Frag<E>* ptf = reinterpret_cast<const Frag<E>*>(a.pt) + ch * G::QK_FR * 64;
+#pragma unroll
+    for (int u = 0; u < TPC; ++u) {
+      const int t = wave + NW * u;
+      if (t >= NCC) continue;
+      const int rt = t / CT, jt = t % CT;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks) acc = mma(frag_row(sm.r1, KLD, 16 * rt, ks, D), frag_row(sm.r2, KLD, 16 * jt, ks, D), acc);
+      // P[r][j] for this tile's elements: fragment (jt, rt/2) of P^T holds
+      // row 16 rt + 4 quad + i at element i (+4 for an odd rt)
+      const Frag<E> pv = ptf[(jt * CKS + (rt >> 1)) * 64 + lane];
+      const int j = 16 * jt + l16;
+      float colp = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * quad + i;
+        const float m2 = acc[i] * to_f(pv[i + 4 * (rt & 1)]);
+        const float rs = row_sum16(m2);
+        if (l16 == 0) atomicAdd(&sm.dg[r], rs);
+        colp += m2;
+        const float gm = (j <= r && r < len) ? __expf(fminf(sm.g[r] - sm.g[j], 0.f)) : 0.f;
+        sm.x1[r * FLD + j] = acc[i] * gm;
+      }
+      colp = col_sum4q(colp);
+      if (quad == 0) atomicAdd(&sm.dg[j], -colp);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();                   // x1 complete; U rows dead
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = wave + NW * u;
+      if (t >= NCD) continue;
+      const int rt = t / DT, dt = t % DT;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.r2[(16 * rt + 4 * quad + i) * KLD + 16 * dt + l16] = to_e<E>(dW[u][i]);
+      // dQ += dPm K, dK += dPm^T Q
+#pragma unroll
+      for (int s = 0; s < CKS; ++s) {
+        dQ[u] = mma(frag_row32(sm.x1, FLD, 16 * rt, s, C), ktf[(dt * CKS + s) * 64 + lane], dQ[u]);
+        dK[u] = mma(frag_col(sm.x1, FLD, 16 * rt, s, C), qtf[(dt * CKS + s) * 64 + lane], dK[u]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();                   // dL/do rows and x1 dead; dW rows complete
+    stage_rows(sm.r1, a.v, a.h_v, hv);
+    __syncthreads();
+
+    // dT = (dU V^T) diag(b) + (dW K^T) diag(b ea) into x1
+#pragma unroll
+    for (int u = 0; u < TPC; ++u) {
+      const int t = wave + NW * u;
+      if (t >= NCC) continue;
+      const int rt = t / CT, it = t % CT;
+      f32x4 a1 = zero4(), a2 = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks) {
+        a1 = mma(frag_row(sm.r3, KLD, 16 * rt, ks, D), frag_row(sm.r1, KLD, 16 * it, ks, D), a1);
+        a2 = mma(frag_row(sm.r2, KLD, 16 * rt, ks, D), frag_row(sm.ks, KLD, 16 * it, ks, D), a2);
+      }
+      const int i = 16 * it + l16;
+      const float bi = sm.b[i], bgi = sm.b[i] * sm.ea[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.x1[(16 * rt + 4 * quad + e) * FLD + i] = a1[e] * bi + a2[e] * bgi;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    // Y = dT Tinv^T into x2 (fp32)
+#pragma unroll
+    for (int u = 0; u < TPC; ++u) {
+      const int t = wave + NW * u;
+      if (t >= NCC) continue;
+      const int rt = t / CT, it = t % CT;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int mb = 0; mb < CT; ++mb)
+        acc = mma16_f32(&sm.x1[(16 * rt) * FLD + 16 * mb], FLD, 1, &sm.tt[(16 * mb) * TLD + 16 * it], TLD, 1, acc, lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.x2[(16 * rt + 4 * quad + e) * FLD + 16 * it + l16] = acc[e];
+    }
+    __syncthreads();
+    // dA = -Tinv^T Y (strictly lower), K K^T; b and g terms of A; B into x1
+#pragma unroll
+    for (int u = 0; u < TPC; ++u) {
+      const int t = wave + NW * u;
+      if (t >= NCC) continue;
+      const int rt = t / CT, it = t % CT;
+      f32x4 acc = zero4(), kk = zero4();
+#pragma unroll
+      for (int mb = 0; mb < CT; ++mb)
+        acc = mma16_f32(&sm.tt[(16 * rt) * TLD + 16 * mb], TLD, 1, &sm.x2[(16 * mb) * FLD + 16 * it], FLD, 1, acc, lane);
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks) kk = mma(frag_row(sm.ks, KLD, 16 * rt, ks, D), frag_row(sm.ks, KLD, 16 * it, ks, D), kk);
+      const int i = 16 * it + l16;
+      float colm = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * quad + e;
+        const bool lower = i < r && r < len;
+        const float gm = lower ? __expf(fminf(sm.g[r] - sm.g[i], 0.f)) : 0.f;
+        const float da = lower ? -acc[e] : 0.f;
+        const float bm = da * sm.b[r] * gm;
+        const float mb2 = bm * kk[e];
+        const float rdb = row_sum16(da * kk[e] * gm);
+        const float rdg = row_sum16(mb2);
+        if (l16 == 0) {
+          atomicAdd(&sm.db[r], rdb);
+          atomicAdd(&sm.dg[r], rdg);
+        }
+        colm += mb2;
+        sm.x1[r * FLD + i] = bm;
+      }
+      colm = col_sum4q(colm);
+      if (quad == 0) atomicAdd(&sm.dg[i], -colm);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    // dK += (B + B^T) K; dV = diag(b) Tinv^T dU and its b term;
+    // Tinv^T dW into dK and the b, g terms of W
+    E* dvg = static_cast<E*>(a.dv);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = wave + NW * u;
+      if (t >= NCD) continue;
+      const int rt = t / DT, dt = t % DT;
+      f32x4 au = zero4(), aw = zero4();
+#pragma unroll
+      for (int s = 0; s < CKS; ++s) {
+        const Frag<E> kb = ktf[(dt * CKS + s) * 64 + lane];
+        dK[u] = mma(frag_row32(sm.x1, FLD, 16 * rt, s, C), kb, dK[u]);
+        dK[u] = mma(frag_col(sm.x1, FLD, 16 * rt, s, C), kb, dK[u]);
+        const Frag<E> ta = frag_row(sm.tt, TLD, 16 * rt, s, C);
+        au = mma(ta, frag_col(sm.r3, KLD, 16 * dt, s, C), au);
+        aw = mma(ta, frag_col(sm.r2, KLD, 16 * dt, s, C), aw);
+      }
+      const int d = 16 * dt + l16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * quad + e;
+        const float br = sm.b[r], bgr = sm.b[r] * sm.ea[r];
+        if (r < len) dvg[((int64_t)(start + r) * a.h_v + hv) * D + d] = to_e<E>(br * au[e]);
+        dK[u][e] += bgr * aw[e];
+        const float rv = row_sum16(au[e] * to_f(sm.r1[r * KLD + d]));
+        const float rk = row_sum16(aw[e] * to_f(sm.ks[r * KLD + d]));
+        if (l16 == 0) {
+          atomicAdd(&sm.db[r], rv + sm.ea[r] * rk);
+          atomicAdd(&sm.dg[r], bgr * rk);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    if (tid == 0 && len > 0) sm.dg[len - 1] += gl * sm.sums[0] + sm.sums[1];
+    __syncthreads();
+    if (tid < len) {
+      float acc = 0.f;
+      for (int j = len - 1; j >= tid; --j) acc += sm.dg[j];
+      a.dlog_alpha[(int64_t)(start + tid) * a.h_v + hv] = acc;
+      a.dbeta[(int64_t)(start + tid) * a.h_v + hv] = sm.db[tid];
+    }
+  }
+
+  E* dqg = static_cast<E*>(a.dq);
+  E* dkg = static_cast<E*>(a.dk);
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int t = wave + NW * u;
+    if (t >= NCD) continue;
+    const int rt = t / DT, dt = t % DT;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * rt + 4 * quad + e;
+      if (r < len) {
+        const int64_t o = ((int64_t)(start + r) * a.h_qk + hq) * D + 16 * dt + l16;
+        dqg[o] = to_e<E>(dQ[u][e]);
+        dkg[o] = to_e<E>(dK[u][e]);
+      }
+    }
+  }
+}
+
+template <typename E, int D, int C>
+hipError_t launch_backward_t(const PrefillArgs& a, hipStream_t s, int first, int last) {
+  using G = Cfg<E, D, C>;
+  for (int stage = first; stage <= last; ++stage) {
+    switch (stage) {
+      case 4:
+        gdn_kb_dstate<E, D, C><<<dim3((unsigned)(a.num_seqs * a.h_v * G::NCB)), dim3(kBlock), 0, s>>>(a);
+        break;
+      case 5:
+        gdn_kb_grad<E, D, C><<<dim3((unsigned)a.max_chunks, (unsigned)a.h_qk), dim3(kGradBlock), 0, s>>>(a);
+        break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_backward_e(const PrefillArgs& a, int d, int c, hipStream_t s, int first, int last) {
+  if (d == 128 && c == 64) {
+    if constexpr (std::is_same<E, float>::value) return hipErrorInvalidValue;
+    else return launch_backward_t<E, 128, 64>(a, s, first, last);
+  }
+  if (d == 128 && c == 16) return launch_backward_t<E, 128, 16>(a, s, first, last);
+  if (d == 16 && c == 64) return launch_backward_t<E, 16, 64>(a, s, first, last);
+  if (d == 16 && c == 16) return launch_backward_t<E, 16, 16>(a, s, first, last);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_backward(const PrefillArgs& a, int dtype, int head_dim, int chunk, hipStream_t stream,
+                           int first_stage, int last_stage) {
+  // stages 1-3: the forward kernels with their backward outputs (the
+  // workspace pointers for those are set in `a`)
+  if (first_stage <= 3) {
+    const hipError_t e = launch_prefill(a, dtype, head_dim, chunk, stream, first_stage, last_stage < 3 ? last_stage : 3);
+    if (e != hipSuccess) return e;
+  }
+  const int f = first_stage > 4 ? first_stage : 4;
+  if (last_stage < f) return hipSuccess;
+  if (dtype == 1) return launch_backward_e<bf16_t>(a, head_dim, chunk, stream, f, last_stage);
+  return launch_backward_e<float>(a, head_dim, chunk, stream, f, last_stage);
+}
+
+}  // namespace gdn

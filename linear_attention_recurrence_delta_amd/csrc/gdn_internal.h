@@ -31,6 +31,25 @@ struct PrefillArgs {
   void* q_frag;             // [NC][HQ] fragments of Q
   void* pmask;              // [NC][HV] fragments of the masked, decayed q.k products
   float* dtab;              // [NC][HV][2C+4] scan row factors exp(g), exp(g_L - g), exp(g_L)
+  // backward pass only (null in the forward pass); E = the q/k/v dtype
+  void* k_frag;             // [NC][HQ] fragments of K (row r, k = d)             kernel 1
+  void* q_t;                // [NC][HQ] fragments of Q^T (row d, k = token r)     kernel 1
+  void* kq;                 // [NC][HQ] fragments of (q_r . k_j) (col j = key, k = query r)  kernel 1
+  void* pt;                 // [NC][HV] fragments of P^T (row j = key, k = query r)  kernel 2
+  void* wt;                 // [NC][HV] fragments of W^T (row d, k = token r)     kernel 2
+  void* tt;                 // [NC][HV][C][C] E, Tinv^T row-major (tt[i][r] = Tinv[r][i])  kernel 2
+  void* sc;                 // [NC][HV][D][D] E, state at each chunk's start      kernel 3
+  void* ub;                 // [NC][HV][C][D] E, the chunk's U rows               kernel 3
+  void* dsl;                // [NC][HV][D][D] E, dL/d(state at each chunk's end)  reverse scan
+  void* du;                 // [NC][HV][C][D] E, dL/dU rows                       reverse scan
+  const void* d_o;          // [T, HV, D] dL/do
+  const float* d_final;     // [N, HV, D, D] dL/d(final state), or null (zero)
+  void* dq;                 // [T, HQ, D]
+  void* dk;                 // [T, HQ, D]
+  void* dv;                 // [T, HV, D]
+  float* dlog_alpha;        // [T, HV]
+  float* dbeta;             // [T, HV]
+  float* d_init;            // [N, HV, D, D] or null
   int64_t num_seqs;         // N
   int64_t total_tokens;     // T
   int64_t max_chunks;       // NC = floor(T/C) + N
@@ -74,6 +93,13 @@ bool prefill_supported(int dtype, int head_dim, int chunk);
 hipError_t launch_prefill(const PrefillArgs& args, int dtype, int head_dim, int chunk,
                           hipStream_t stream, int first_stage, int last_stage);
 hipError_t launch_decode(const DecodeArgs& args, int dtype, int head_dim, hipStream_t stream);
+// Backward pass: kernels 1 and 2 with their backward outputs, the saving
+// scan, the reverse state scan and the gradient kernel (gdn_backward.hip).
+// Stages (1-based): 1-3 the forward kernels with their backward outputs,
+// 4 the reverse state scan, 5 the gradient kernel.
+constexpr int kBackwardStages = 5;
+hipError_t launch_backward(const PrefillArgs& args, int dtype, int head_dim, int chunk, hipStream_t stream,
+                           int first_stage, int last_stage);
 hipError_t launch_decode_multi(const DecodeArgs& args, int dtype, int head_dim, hipStream_t stream);
 
 }  // namespace gdn

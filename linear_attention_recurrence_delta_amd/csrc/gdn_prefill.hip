@@ -40,48 +40,11 @@
 
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_tiles.h"
 
 namespace gdn {
 
 namespace {
-
-constexpr int kBlock = 256;
-
-template <typename E, int D, int C>
-struct Cfg {
-  static constexpr int DT = D / 16, CT = C / 16;
-  static constexpr int DKS = (DT + 1) / 2, CKS = (CT + 1) / 2;
-  static constexpr int NS = DT >= 2 ? 2 : 1;   // 16-column state slices per scan workgroup
-  static constexpr int BV = 16 * NS;           // state columns per scan workgroup
-  static constexpr int NCB = D / BV;           // scan workgroups per (sequence, V head)
-  static constexpr int NW = 4;                 // waves per scan workgroup
-  static constexpr int NPROD = NW - NS;        // producer waves
-  static constexpr int KT_FR = DT * CKS;       // K^T fragments per chunk
-  static constexpr int T_FR = CT * CKS;        // Tinv fragments per chunk
-  static constexpr int QK_FR = CT * CKS;       // q.k fragments per chunk
-  static constexpr int Q_FR = CT * DKS;        // Q fragments per chunk
-  static constexpr int W_FR = CT * DKS;        // W fragments per chunk
-  static constexpr int VLD = C + 8;            // row stride of the transposed V slice
-};
-
-// Workgroups are dispatched round-robin over the chip's 8 XCDs (each with
-// its own L2): workgroup b runs on XCD b % 8. Renumbering so that logical
-// ids [k n/8, (k+1) n/8) all run on XCD k keeps workgroups that read the
-// same operands (consecutive logical ids) behind one L2.
-constexpr int kXcds = 8;
-__device__ __forceinline__ int64_t xcd_local_id(int64_t b, int64_t n) {
-  if (n % kXcds) return b;
-  return (b % kXcds) * (n / kXcds) + b / kXcds;
-}
-
-// Contraction index of fragment element e at 32-step s for lane quad q.
-__device__ __forceinline__ int frag_k(int s, int quad, int e) {
-  return 32 * s + (e < 4 ? 4 * quad + e : 16 + 4 * quad + (e - 4));
-}
-
-// True when fragment step s of query tile nt holds only keys after every
-// query of the tile (the causal mask makes it zero).
-__device__ __forceinline__ constexpr bool causal_zero(int nt, int s) { return 32 * s > 16 * nt + 15; }
 
 // --------------------------------------------------------------------------
 // Kernel 1: per (chunk slot c, QK head hq): the chunk table, the in-chunk
@@ -239,6 +202,44 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
     }
     qkg[f * 64 + lane] = acc_to_frag<E>(t2[0], t2[1]);
   }
+  if (a.k_frag) {
+    // backward-pass operands (uniform branch): K fragments (row r, k = d),
+    // Q^T fragments (row d, k = token r), and the q.k products with the
+    // query as contraction index: fragment (jt, s) is the pair of tiles
+    // Q_r K_j^T of query tiles 2s and 2s + 1 (zero before the key tile)
+    Frag<E>* kfg = reinterpret_cast<Frag<E>*>(a.k_frag) + (c * a.h_qk + hq) * G::Q_FR * 64;
+    for (int it = tid; it < G::Q_FR * 64; it += kBlock) {
+      const int f = it / 64, ln = it % 64, nt = f / DKS, s = f % DKS;
+      kfg[it] = load_frag<E>(&sm.ks[(16 * nt + (ln & 15)) * KLD + 32 * s], ln >> 4, D - 32 * s);
+    }
+    Frag<E>* qtg = reinterpret_cast<Frag<E>*>(a.q_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
+    for (int it = tid; it < G::KT_FR * 64; it += kBlock) {
+      const int f = it / 64, ln = it % 64, dt = f / CKS, s = f % CKS, q4 = ln >> 4;
+      const int d = 16 * dt + (ln & 15);
+      Frag<E> v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = frag_k(s, q4, e);
+        v[e] = (i < C) ? sm.qs[i * KLD + d] : to_e<E>(0.f);
+      }
+      qtg[it] = v;
+    }
+    Frag<E>* kqg = reinterpret_cast<Frag<E>*>(a.kq) + (c * a.h_qk + hq) * G::QK_FR * 64;
+    for (int f = wave; f < G::QK_FR; f += NW) {
+      const int jt = f / CKS, s = f % CKS;
+      f32x4 t2[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int rt = 2 * s + h;
+        if (rt < jt || rt >= CT) continue;
+#pragma unroll
+        for (int ks = 0; ks < DKS; ++ks)
+          t2[h] = mma(load_frag<E>(&sm.qs[(16 * rt + l16) * KLD + 32 * ks], quad, D - 32 * ks),
+                      load_frag<E>(&sm.ks[(16 * jt + l16) * KLD + 32 * ks], quad, D - 32 * ks), t2[h]);
+      }
+      kqg[f * 64 + lane] = acc_to_frag<E>(t2[0], t2[1]);
+    }
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -261,18 +262,6 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
 // (Tinv diag(b exp(g)))^T is contracted over tokens, wave w taking d-tiles
 // 2w and 2w + 1, whose accumulator pairs are W's fragments (rt, w).
 // --------------------------------------------------------------------------
-
-// acc += X Y for 16 x 16 fp32 tiles in LDS; X(m, k) = X[m xr + k xc] and
-// Y(k, m) = Y[k yr + m yc] (strides give either storage order)
-__device__ __forceinline__ f32x4 mma16_f32(const float* X, int xr, int xc, const float* Y, int yr, int yc,
-                                           f32x4 acc, int lane) {
-  const int m = lane & 15, k = lane >> 4;
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[m * xr + (4 * kk + k) * xc], Y[(4 * kk + k) * yr + m * yc], acc,
-                                               0, 0, 0);
-  return acc;
-}
 
 template <typename E, int D, int C>
 struct InvSmem {
@@ -382,6 +371,26 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
       dtg[C + tid] = (tid == C) ? __expf(gl) : 0.f;
     }
   }
+  if (a.pt) {
+    // backward pass: P^T fragments (jt, s), lane row key j, elements query r,
+    // from kernel 1's query-indexed q.k fragments
+    const Frag<E>* kqg = reinterpret_cast<const Frag<E>*>(a.kq) + (c * a.h_qk + hq) * G::QK_FR * 64;
+    Frag<E>* ptg = reinterpret_cast<Frag<E>*>(a.pt) + (c * a.h_v + hv) * G::QK_FR * 64;
+    for (int it = tid; it < G::QK_FR * 64; it += kBlock) {
+      const int f = it / 64, ln = it % 64, jt = f / CKS, s = f % CKS, q4 = ln >> 4;
+      const int j = 16 * jt + (ln & 15);
+      const Frag<E> x = kqg[it];
+      const float gj = sm.gb[0][j];
+      Frag<E> v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = frag_k(s, q4, e);
+        const float m = (float)(j <= r && r < len);
+        v[e] = to_e<E>(to_f(x[e]) * (__expf(fminf(sm.gb[0][min(r, C - 1)] - gj, 0.f)) * m));
+      }
+      ptg[it] = v;
+    }
+  }
   if constexpr (ND) {
     // gate-only variant: no delta rule, so Tinv = I; the scan's Ut = diag(b) V
     // takes diag(b) in place of Tinv diag(b), and W is not used
@@ -472,6 +481,15 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
     }
     __syncthreads();
   }
+  if (a.tt) {
+    // backward pass: Tinv^T row-major, tt[i][r] = Tinv[r][i]
+    E* ttg = static_cast<E*>(a.tt) + (c * a.h_v + hv) * C * C;
+    for (int idx = tid; idx < C * C; idx += kBlock) {
+      const int i = idx / C, r = idx % C;
+      const float t = ((r >> 4) > (i >> 4)) ? at[i * FLD + r] : (((r >> 4) == (i >> 4)) ? at[r * FLD + i] : 0.f);
+      ttg[idx] = to_e<E>(t);
+    }
+  }
   // Tinv diag(b) fragments to the workspace, Tinv diag(b exp(g)) to LDS
   Frag<E>* tg = reinterpret_cast<Frag<E>*>(a.tinv) + (c * a.h_v + hv) * G::T_FR * 64;
   for (int it = tid; it < G::T_FR * 64; it += kBlock) {
@@ -506,6 +524,30 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
         if (2 * ksd + 1 < DT) acc1 = mma(ktb[s], tb, acc1);
       }
       wg[(rt * DKS + ksd) * 64 + lane] = acc_to_frag<E>(acc0, acc1);
+    }
+    if (a.wt) {
+      // backward pass: W^T fragments (dt, s), lane row d, elements token r:
+      // the pair of W tiles (r-tiles 2s, 2s + 1; d-tile dt) formed as
+      // Tinv diag(b exp(g)) K
+      Frag<E>* wtg = reinterpret_cast<Frag<E>*>(a.wt) + (c * a.h_v + hv) * G::KT_FR * 64;
+#pragma unroll
+      for (int s = 0; s < CKS; ++s) {
+        f32x4 pa[2] = {zero4(), zero4()}, pb[2] = {zero4(), zero4()};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int rt = 2 * s + h;
+          if (rt >= CT) continue;
+#pragma unroll
+          for (int s2 = 0; s2 < CKS; ++s2) {
+            if (causal_zero(rt, s2)) continue;
+            const Frag<E> tb = sm.tbg[(rt * CKS + s2) * 64 + lane];
+            pa[h] = mma(tb, kta[s2], pa[h]);
+            if (2 * ksd + 1 < DT) pb[h] = mma(tb, ktb[s2], pb[h]);
+          }
+        }
+        wtg[((2 * ksd) * CKS + s) * 64 + lane] = acc_to_frag<E>(pa[0], pa[1]);
+        if (2 * ksd + 1 < DT) wtg[((2 * ksd + 1) * CKS + s) * 64 + lane] = acc_to_frag<E>(pb[0], pb[1]);
+      }
     }
   }
 }
@@ -551,21 +593,7 @@ struct ScanSmem {
   float touch[kScanBlock / 64][64];    // landing place of the L2 warm-up loads
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Workgroup barrier for the scan and Ut waves: it waits only for this
-// wave's LDS operations, not for global stores or L2 warm-up loads (nothing
-// in the workgroup reads those back).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// One direct global-to-LDS copy of up to 1 KB: lane l copies the 16 bytes
-// at src + 16 l to dst + 16 l (dst is the same for the whole wave); lanes
-// at or past `bytes` copy nothing.
-__device__ __forceinline__ void copy_1k(const char* src, char* dst, int bytes, int lane) {
-  if (16 * lane < bytes) __builtin_amdgcn_global_load_lds(src + 16 * lane, (lds_ptr_t)dst, 16, 0, 0);
-}
-
-template <typename E, int D, int C, bool ND>
+template <typename E, int D, int C, bool ND, bool SV>
 __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   constexpr int DT = G::DT, CT = G::CT, DKS = G::DKS, CKS = G::CKS, NS = G::NS, BV = G::BV;
@@ -695,6 +723,16 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
 
   auto scan_chunk = [&](int c) __attribute__((always_inline)) {
     const int start = chunk_start(c), len = chunk_len(c), par = c & 1;
+    if constexpr (SV) {
+      // backward pass: the state at the chunk's start, rounded as the
+      // products below use it
+      E* scg = static_cast<E*>(a.sc) + ((int64_t)c * a.h_v + hv) * D * D + col0 + 16 * slice + l16;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) scg[(16 * dt + 4 * quad + i) * D] = to_e<E>(S[dt][i]);
+      }
+    }
     Frag<E> Sf[DKS];
 #pragma unroll
     for (int ks = 0; ks < DKS; ++ks) Sf[ks] = acc_to_frag<E>(S[2 * ks], (2 * ks + 1 < DT) ? S[2 * ks + 1] : zero4());
@@ -748,6 +786,15 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     Frag<E> Uk[CKS];
 #pragma unroll
     for (int ks = 0; ks < CKS; ++ks) Uk[ks] = acc_to_frag<E>(U[2 * ks], (2 * ks + 1 < CT) ? U[2 * ks + 1] : zero4());
+    if constexpr (SV) {
+      // backward pass: the chunk's U rows, rounded as the products use them
+      E* ubg = static_cast<E*>(a.ub) + ((int64_t)c * a.h_v + hv) * C * D + col0 + 16 * slice + l16;
+#pragma unroll
+      for (int t = 0; t < CT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ubg[(16 * t + 4 * quad + i) * D] = to_e<E>(U[t][i]);
+      }
+    }
     // decayed rows exp(g_L - g_r) U_r
 #pragma unroll
     for (int t = 0; t < CT; ++t) U[t] *= *reinterpret_cast<const f32x4*>(&ed[16 * t + 4 * quad]);
@@ -782,7 +829,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
 #pragma unroll
     for (int nt = 0; nt < CT; ++nt) {
       const int r = 16 * nt + l16;
-      if (r < len) {
+      if (!SV && r < len) {
         Half<E> h;
 #pragma unroll
         for (int i = 0; i < 4; ++i) h[i] = to_e<E>(O[nt][i]);
@@ -911,8 +958,9 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
         break;
       }
       case 3:
-        if (a.no_delta) gdn_k3_scan<E, D, C, true><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a);
-        else gdn_k3_scan<E, D, C, false><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a);
+        if (a.sc) gdn_k3_scan<E, D, C, false, true><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a);
+        else if (a.no_delta) gdn_k3_scan<E, D, C, true, false><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a);
+        else gdn_k3_scan<E, D, C, false, false><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a);
         break;
       default: return hipErrorInvalidValue;
     }

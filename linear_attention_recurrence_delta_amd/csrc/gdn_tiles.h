@@ -1,0 +1,76 @@
+// Tile configuration and helpers shared by the prefill and backward kernels
+// (gfx950 only). Internal; included by gdn_prefill.hip and gdn_backward.hip.
+#pragma once
+
+#include "gdn_device.h"
+
+namespace gdn {
+
+constexpr int kBlock = 256;
+
+template <typename E, int D, int C>
+struct Cfg {
+  static constexpr int DT = D / 16, CT = C / 16;
+  static constexpr int DKS = (DT + 1) / 2, CKS = (CT + 1) / 2;
+  static constexpr int NS = DT >= 2 ? 2 : 1;   // 16-column state slices per scan workgroup
+  static constexpr int BV = 16 * NS;           // state columns per scan workgroup
+  static constexpr int NCB = D / BV;           // scan workgroups per (sequence, V head)
+  static constexpr int NW = 4;                 // waves per scan workgroup
+  static constexpr int NPROD = NW - NS;        // producer waves
+  static constexpr int KT_FR = DT * CKS;       // K^T fragments per chunk
+  static constexpr int T_FR = CT * CKS;        // Tinv fragments per chunk
+  static constexpr int QK_FR = CT * CKS;       // q.k fragments per chunk
+  static constexpr int Q_FR = CT * DKS;        // Q fragments per chunk
+  static constexpr int W_FR = CT * DKS;        // W fragments per chunk
+  static constexpr int VLD = C + 8;            // row stride of the transposed V slice
+};
+
+// Workgroups are dispatched round-robin over the chip's 8 XCDs (each with
+// its own L2): workgroup b runs on XCD b % 8. Renumbering so that logical
+// ids [k n/8, (k+1) n/8) all run on XCD k keeps workgroups that read the
+// same operands (consecutive logical ids) behind one L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_local_id(int64_t b, int64_t n) {
+  if (n % kXcds) return b;
+  return (b % kXcds) * (n / kXcds) + b / kXcds;
+}
+
+// Contraction index of fragment element e at 32-step s for lane quad q.
+__device__ __forceinline__ int frag_k(int s, int quad, int e) {
+  return 32 * s + (e < 4 ? 4 * quad + e : 16 + 4 * quad + (e - 4));
+}
+
+// True when fragment step s of query tile nt holds only keys after every
+// query of the tile (the causal mask makes it zero).
+__device__ __forceinline__ constexpr bool causal_zero(int nt, int s) { return 32 * s > 16 * nt + 15; }
+
+// acc += X Y for 16 x 16 tiles held in LDS, in fp32 (v_mfma_f32_16x16x4_f32;
+// bf16 elements are widened); X(m, k) = X[m xr + k xc] and
+// Y(k, m) = Y[k yr + m yc], so strides give either storage order
+template <typename TX, typename TY>
+__device__ __forceinline__ f32x4 mma16_f32(const TX* X, int xr, int xc, const TY* Y, int yr, int yc,
+                                           f32x4 acc, int lane) {
+  const int m = lane & 15, k = lane >> 4;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(to_f(X[m * xr + (4 * kk + k) * xc]), to_f(Y[(4 * kk + k) * yr + m * yc]),
+                                               acc, 0, 0, 0);
+  return acc;
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Workgroup barrier for the scan and Ut waves: it waits only for this
+// wave's LDS operations, not for global stores or L2 warm-up loads (nothing
+// in the workgroup reads those back).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One direct global-to-LDS copy of up to 1 KB: lane l copies the 16 bytes
+// at src + 16 l to dst + 16 l (dst is the same for the whole wave); lanes
+// at or past `bytes` copy nothing.
+__device__ __forceinline__ void copy_1k(const char* src, char* dst, int bytes, int lane) {
+  if (16 * lane < bytes) __builtin_amdgcn_global_load_lds(src + 16 * lane, (lds_ptr_t)dst, 16, 0, 0);
+}
+
+
+}  // namespace gdn

@@ -1,0 +1,118 @@
+"""GPU parity of the backward pass (gdn_chunk_bwd) against the oracle's
+backpropagation through the form-1 recurrence (oracle.gdn_oracle.
+recurrent_form1_backward), through the C ABI.
+
+Tolerances, per gradient tensor (rel-L2 = ||x - y|| / ||y||):
+  fp32 inputs: rel-L2 <= 1e-5.
+  bf16 inputs: rel-L2 <= 1e-2 and max|x - y| <= 2e-2 max|y|. The gradient
+    kernels round the stored states, U, dU and dS and every matrix-product
+    operand to bf16 (fp32 accumulation), as the forward pass does; an fp64
+    emulation of exactly those roundings at head dim 128 gives rel-L2
+    1.7e-3 to 2.8e-3 and max error <= 4e-3 of max|y| for every gradient, and
+    the bound leaves a factor of about 4.
+The loss is L = <o, R_o> + <S_final, R_f> with seeded random R_o, R_f.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_recurrence_delta_amd as gdn
+from linear_attention_recurrence_delta_amd import inputs as I
+from oracle import gdn_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+NAMES = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dinit")
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def np64(t):
+    return None if t is None else t.detach().to("cpu", torch.float64).numpy()
+
+
+def compare(got, want, dtype):
+    """Errors of every gradient; one assertion naming all that fail."""
+    bad, report = [], []
+    for name in NAMES:
+        g, w = got[name], want[name]
+        assert np.isfinite(g).all(), f"{name}: non-finite values"
+        rel = np.linalg.norm(g - w) / max(np.linalg.norm(w), 1e-30)
+        mx = np.abs(g - w).max() / max(np.abs(w).max(), 1e-30) if w.size else 0.0
+        report.append(f"{name} rel {rel:.2e} max {mx:.2e}")
+        ok = rel <= 1e-5 if dtype == "f32" else (rel <= 1e-2 and mx <= 2e-2)
+        if not ok:
+            bad.append(name)
+    print("  " + "; ".join(report), flush=True)
+    assert not bad, f"gradients off: {bad}; " + "; ".join(report)
+
+
+def run_case(seed, lens, h_qk, h_v, d, chunk, dtype, d_final=True):
+    inp = I.make_prefill(seed, lens, h_qk, h_v, d, dtype, "randn")
+    T = sum(lens)
+    rng = np.random.default_rng(seed + 1000)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    d_o = torch.from_numpy(rng.standard_normal((T, h_v, d))).to(tdt)
+    dfin = torch.from_numpy(rng.standard_normal((len(lens), h_v, d, d)).astype(np.float32)) if d_final else None
+    dv_ = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    g = gdn.gdn_chunk_bwd(dv_["q"], dv_["k"], dv_["v"], dv_["log_alpha"], dv_["beta"], d_o.to(DEV),
+                          dv_["init_state"], dv_["cu_seqlens"], None if dfin is None else dfin.to(DEV), chunk=chunk)
+    torch.cuda.synchronize()
+    got = {"dq": np64(g["dq"]), "dk": np64(g["dk"]), "dv": np64(g["dv"]), "dlog_alpha": np64(g["dlog_alpha"]),
+           "dbeta": np64(g["dbeta"]), "dinit": np64(g["d_init_state"])}
+    want = O.recurrent_form1_backward(np64(inp["q"]), np64(inp["k"]), np64(inp["v"]), np64(inp["log_alpha"]),
+                                      np64(inp["beta"]), np64(d_o), np64(dfin), np64(inp["init_state"]),
+                                      inp["cu_seqlens"].numpy())
+    return got, want, inp, dfin
+
+
+@pytest.mark.parametrize("d,chunk,dtype,lens", [
+    (16, 16, "f32", [64]),
+    (16, 16, "f32", [37]),
+    (16, 64, "f32", [77, 123]),
+    (128, 16, "f32", [40, 9]),
+])
+def test_backward_fp32(d, chunk, dtype, lens):
+    say(f"backward d={d} C={chunk} {dtype} lens={lens}")
+    got, want, _, _ = run_case(300 + d + chunk + len(lens), lens, 2, 6, d, chunk, dtype)
+    compare(got, want, dtype)
+
+
+@pytest.mark.parametrize("d,chunk,lens", [
+    (128, 64, [200]),
+    (128, 64, [77, 0, 1, 130]),
+    (128, 16, [100]),
+    (16, 64, [150]),
+    (16, 16, [45, 64]),
+])
+def test_backward_bf16(d, chunk, lens):
+    say(f"backward d={d} C={chunk} bf16 lens={lens}")
+    got, want, _, _ = run_case(400 + d + chunk + len(lens), lens, 2, 6, d, chunk, "bf16")
+    compare(got, want, "bf16")
+
+
+def test_backward_without_final_state_gradient():
+    say("backward d=128 C=64 bf16 T=150, d_final_state = None")
+    got, want, _, _ = run_case(450, [150], 2, 6, 128, 64, "bf16", d_final=False)
+    compare(got, want, "bf16")
+
+
+def test_backward_head_group_of_four():
+    say("backward h_qk=3 h_v=12 d=128 C=64 bf16 T=90")
+    got, want, _, _ = run_case(460, [90], 3, 12, 128, 64, "bf16")
+    compare(got, want, "bf16")
+
+
+def test_backward_empty_sequences_pass_the_state_gradient_through():
+    say("backward T=0, two empty sequences")
+    inp = I.make_prefill(470, [0, 0], 1, 3, 128, "bf16", "randn")
+    dfin = torch.randn(2, 3, 128, 128, device=DEV)
+    dv_ = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    g = gdn.gdn_chunk_bwd(dv_["q"], dv_["k"], dv_["v"], dv_["log_alpha"], dv_["beta"],
+                          torch.empty_like(dv_["v"]), dv_["init_state"], dv_["cu_seqlens"], dfin, chunk=64)
+    torch.cuda.synchronize()
+    assert g["dq"].numel() == 0
+    assert torch.equal(g["d_init_state"], dfin)

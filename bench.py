@@ -73,6 +73,100 @@ def algorithmic_work(T, HQ, HV, D, C, N, decode_batch):
     return out, per_token
 
 
+BWD_STAGES = ["gdn_k1_chunk_prep [bwd]", "gdn_k2_inverse_w [bwd]", "gdn_k3_scan [save]", "gdn_kb_dstate",
+              "gdn_kb_grad"]
+
+
+def algorithmic_work_bwd(T, HQ, HV, D, C, N):
+    """Per-launch algorithmic flops and HBM bytes of the backward pass's
+    kernels (gdn_chunk_bwd's five launches), counted as for the forward:
+    dense C x C in-chunk products, compulsory reads and writes of each
+    launch (bf16 rows and fragments, fp32 gates and states). Returns
+    {kernel: (bound, flops, bytes)}."""
+    dk = dv = D
+    e = 2
+    gates = T * HV * 8
+    dtab = T * HV * (2 * C + 4) * 4 / C
+    states = N * HV * dk * dv * 4
+    chunk_states = T / C * HV * dk * dv * e     # one dk x dv matrix per chunk and V head
+    work = {
+        # Q K^T (query-indexed) per QK head; reads q, k, log a, b; writes g, b,
+        # K^T, K and Q^T fragments, the query-indexed q.k fragments
+        "gdn_k1_chunk_prep [bwd]": (T * HQ * 2 * C * dk,
+                                    2 * T * HQ * dk * e + 2 * gates + 3 * T * HQ * dk * e + T * HQ * C * e),
+        # K K^T, the inverse, W and W^T; reads k, K^T, q.k, g, b; writes Tinv
+        # diag(b), W, the row factors, P^T, W^T and Tinv^T
+        "gdn_k2_inverse_w [bwd]": (T * (HQ * 2 * C * dk + HV * (C * C / 3.0 + 4 * C * dk)),
+                                   T * HQ * (2 * dk + C) * e + gates
+                                   + T * HV * (3 * C + 2 * dk) * e + dtab),
+        # Ut, W S, K^T U; reads K^T, V, Tinv diag(b), W, the row factors and
+        # the initial states; writes the chunk-start states and U
+        "gdn_k3_scan [save]": (T * HV * (4 * dk * dv + 2 * C * dv),
+                               T * HQ * dk * e + T * HV * (dv + C + dk) * e + dtab + states
+                               + chunk_states + T * HV * dv * e),
+        # K dS, P^T dO, Q^T dO, W^T dU; reads K and Q^T, P^T and W^T
+        # fragments, the row factors, dL/do, dL/dS_final; writes dL/dS_end per
+        # chunk, dL/dU, dL/dS_0
+        "gdn_kb_dstate": (T * HV * (6 * dk * dv + 2 * C * dv),
+                          2 * T * HQ * dk * e + T * HV * (C + dk + dv) * e + dtab + states
+                          + chunk_states + T * HV * dv * e + states),
+        # dO S0^T, U dS^T, dU S0^T, dO U^T, dPm K, dPm^T Q, dT, K K^T,
+        # (B + B^T) K, Tinv^T dU, Tinv^T dW (and the fp32 C^3 products of dA);
+        # reads q, k, their fragments, dL/do, v, U, dL/dU, Tinv^T, P^T, the
+        # states, g, b, the row factors; writes dq, dk, dv, dlog a, db
+        "gdn_kb_grad": (T * HV * (6 * dk * dv + 4 * C * dv + 10 * C * dk + 4 * C * C),
+                        4 * T * HQ * dk * e + 4 * T * HV * dv * e + 2 * T * HV * C * e + 2 * chunk_states
+                        + gates + dtab + 2 * T * HQ * dk * e + T * HV * dv * e + gates),
+    }
+    return {k: ("mfma" if f / PEAK_BF16_FLOPS > b / PEAK_HBM_BYTES else "hbm", float(f), float(b))
+            for k, (f, b) in work.items()}
+
+
+def backward_bench(gdn, I, inp, dev, stream, T, HQ, HV, D, C, reps=3):
+    """The backward pass of the same 64K-token layer (seeded dL/do and
+    dL/dS_final), per launch, with events between its five stages."""
+    import torch
+    seeds = I.make_backward_seeds(31, [T], HV, D, "bf16")
+    d_o, dfin = seeds["d_o"].to(dev), seeds["d_final"].to(dev)
+    dims = gdn.make_dims(1, T, HQ, HV, D, D, C, torch.bfloat16)
+    ws = torch.empty(gdn.gdn_chunk_bwd_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+    grads = dict(dq=torch.empty_like(inp["q"]), dk=torch.empty_like(inp["k"]), dv=torch.empty_like(inp["v"]),
+                 dlog_alpha=torch.empty_like(inp["log_alpha"]), dbeta=torch.empty_like(inp["beta"]),
+                 d_init_state=torch.empty_like(inp["init_state"]))
+
+    def stage(s):
+        gdn.gdn_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], d_o, inp["init_state"],
+                          None, dfin, chunk=C, workspace=ws, grads=grads, stages=(s, s))
+    n = len(BWD_STAGES)
+    for s in range(1, n + 1):
+        stage(s)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(reps)]
+    for i in range(reps):
+        for s in range(n):
+            ev[i][s].record(stream)
+            stage(s + 1)
+        ev[i][n].record(stream)
+    torch.cuda.synchronize()
+    ms = {name: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(reps)) / reps
+          for j, name in enumerate(BWD_STAGES)}
+    total = sum(ms.values())
+    work = algorithmic_work_bwd(T, HQ, HV, D, C, 1)
+    kernels = {}
+    for name in BWD_STAGES:
+        bound, flops, nbytes = work[name]
+        amount = flops if bound == "mfma" else nbytes
+        rate = amount / (ms[name] * 1e-3)
+        peak = PEAK_BF16_FLOPS if bound == "mfma" else PEAK_HBM_BYTES
+        kernels[name] = {"ms": round(ms[name], 4), "bound": bound,
+                         "achieved": round(rate / (1e12 if bound == "mfma" else 1e9), 3),
+                         "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": round(rate / peak, 4)}
+    del ws
+    return {"ms": round(total, 4), "tokens_per_s": round(T / (total * 1e-3), 1),
+            "mfma_frac": round(sum(work[k][1] for k in BWD_STAGES) / (total * 1e-3) / PEAK_BF16_FLOPS, 4),
+            "kernels": kernels}
+
+
 def load_traffic(kernel):
     """Measured HBM bytes per launch of `kernel` from the committed counter
     summary (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or
@@ -324,6 +418,7 @@ def main():
     go_ms = [timed(lambda s=s: gate_only_stage(s)) for s in range(1, NST + 1)]
     dec_go = timed(lambda: gdn.gdn_decode_step(dec["q"][0], dec["k"][0], dec["v"][0], dec["log_alpha"][0],
                                                dec["beta"][0], state, o=o_dec, delta_rule=False))
+    line["backward"] = backward_bench(gdn, I, inp, dev, stream, T, HQ, HV, D, C)
     line["gate_only"] = {"prefill_ms": round(sum(go_ms), 4), "prefill_tokens_per_s": round(T / (sum(go_ms) * 1e-3), 1),
                          "kernel_ms": {n: round(t, 4) for n, t in zip(STAGES, go_ms)},
                          "decode_ms": round(dec_go, 4),

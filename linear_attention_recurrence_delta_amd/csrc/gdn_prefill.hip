@@ -69,7 +69,7 @@ struct PrepSmem {
   int hit[2];
 };
 
-template <typename E, int D, int C, bool P>
+template <typename E, int D, int C, bool P, bool BW>
 __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   using SM = PrepSmem<E, D, C>;
@@ -180,15 +180,17 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
     }
     ktg[it] = v;
   }
-  // Q fragments: frag (nt, s), lane row r, elements d
+  // Q fragments: frag (nt, s), lane row r, elements d (the forward pass's
+  // outputs only: the backward pass's scan forms none)
   Frag<E>* qfg = reinterpret_cast<Frag<E>*>(a.q_frag) + (c * a.h_qk + hq) * G::Q_FR * 64;
-  for (int it = tid; it < G::Q_FR * 64; it += kBlock) {
+  for (int it = tid; !BW && it < G::Q_FR * 64; it += kBlock) {
     const int f = it / 64, ln = it % 64, nt = f / DKS, s = f % DKS;
     qfg[it] = load_frag<E>(&sm.qs[(16 * nt + (ln & 15)) * KLD + 32 * s], ln >> 4, D - 32 * s);
   }
-  // q.k fragments: frag (nt, s), lane col = query r, elements key j
+  // q.k fragments: frag (nt, s), lane col = query r, elements key j (for
+  // the forward pass's outputs only)
   Frag<E>* qkg = reinterpret_cast<Frag<E>*>(a.qk) + (c * a.h_qk + hq) * G::QK_FR * 64;
-  for (int f = wave; f < G::QK_FR; f += NW) {
+  for (int f = wave; !BW && f < G::QK_FR; f += NW) {
     const int nt = f / CKS, s = f % CKS;
     f32x4 t2[2] = {zero4(), zero4()};
 #pragma unroll
@@ -202,8 +204,8 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
     }
     qkg[f * 64 + lane] = acc_to_frag<E>(t2[0], t2[1]);
   }
-  if (a.k_frag) {
-    // backward-pass operands (uniform branch): K fragments (row r, k = d),
+  if constexpr (BW) {
+    // backward-pass operands: K fragments (row r, k = d),
     // Q^T fragments (row d, k = token r), and the q.k products with the
     // query as contraction index: fragment (jt, s) is the pair of tiles
     // Q_r K_j^T of query tiles 2s and 2s + 1 (zero before the key tile)
@@ -278,7 +280,7 @@ struct InvSmem {
   float gb[2][C];                      // g and b of this V head
 };
 
-template <typename E, int D, int C, bool P, bool ND>
+template <typename E, int D, int C, bool P, bool ND, bool BW>
 __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   using SM = InvSmem<E, D, C>;
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
     const Frag<E>* qkg = reinterpret_cast<const Frag<E>*>(a.qk) + (c * a.h_qk + hq) * G::QK_FR * 64;
 #pragma unroll
     for (int p = 0; p < PQ; ++p)
-      if (tid + p * kBlock < G::QK_FR * 64) qkr[p] = qkg[tid + p * kBlock];
+      if (!BW && tid + p * kBlock < G::QK_FR * 64) qkr[p] = qkg[tid + p * kBlock];
   }
   const E* kg = static_cast<const E*>(a.k);
   for (int idx = tid; !ND && idx < C * D / VE; idx += kBlock) {
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
 #pragma unroll
     for (int p = 0; p < PQ; ++p) {
       const int it = tid + p * kBlock;
-      if (it >= G::QK_FR * 64) continue;
+      if (BW || it >= G::QK_FR * 64) continue;       // the backward pass uses P^T (below)
       const int f = it / 64, ln = it % 64, nt = f / CKS, s = f % CKS, q4 = ln >> 4;
       const int r = 16 * nt + (ln & 15);
       const float gr = sm.gb[0][r], vr = (float)(r < len);
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
       dtg[C + tid] = (tid == C) ? __expf(gl) : 0.f;
     }
   }
-  if (a.pt) {
+  if constexpr (BW) {
     // backward pass: P^T fragments (jt, s), lane row key j, elements query r,
     // from kernel 1's query-indexed q.k fragments
     const Frag<E>* kqg = reinterpret_cast<const Frag<E>*>(a.kq) + (c * a.h_qk + hq) * G::QK_FR * 64;
@@ -481,7 +483,7 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
     }
     __syncthreads();
   }
-  if (a.tt) {
+  if constexpr (BW) {
     // backward pass: Tinv^T row-major, tt[i][r] = Tinv[r][i]
     E* ttg = static_cast<E*>(a.tt) + (c * a.h_v + hv) * C * C;
     for (int idx = tid; idx < C * C; idx += kBlock) {
@@ -525,7 +527,7 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
       }
       wg[(rt * DKS + ksd) * 64 + lane] = acc_to_frag<E>(acc0, acc1);
     }
-    if (a.wt) {
+    if constexpr (BW) {
       // backward pass: W^T fragments (dt, s), lane row d, elements token r:
       // the pair of W tiles (r-tiles 2s, 2s + 1; d-tile dt) formed as
       // Tinv diag(b exp(g)) K
@@ -630,9 +632,11 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
 
   // ---- direct copies into LDS: chunk xs's scan operands, chunk xp's Ut
   // operands; the window's jobs are dealt round-robin to the loader waves ----
-  // (the gate-only variant reads no W: its region, copies and warm-up lines
-  // have zero size)
-  constexpr int B_KT = G::KT_FR * FB, B_W = ND ? 0 : G::W_FR * FB, B_Q = G::Q_FR * FB, B_P = G::QK_FR * FB;
+  // (the gate-only variant reads no W, and the saving form for the backward
+  // pass, which writes no outputs, no Q and P: their regions, copies and
+  // warm-up lines have zero size)
+  constexpr int B_KT = G::KT_FR * FB, B_W = ND ? 0 : G::W_FR * FB;
+  constexpr int B_Q = SV ? 0 : G::Q_FR * FB, B_P = SV ? 0 : G::QK_FR * FB;
   constexpr int B_T = G::T_FR * FB, B_V = C * BV * ESZ, B_D = (2 * C + 4) * 4;
   constexpr int NREG = 7;
   constexpr int JOBS[NREG] = {(B_KT + 1023) / 1024, (B_W + 1023) / 1024, (B_Q + 1023) / 1024,
@@ -747,7 +751,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     Frag<E> qa[CT], wa[CT];
 #pragma unroll
     for (int t = 0; t < CT; ++t) {
-      qa[t] = sm.qf[par][(t * DKS) * 64 + lane];
+      if constexpr (!SV) qa[t] = sm.qf[par][(t * DKS) * 64 + lane];
       if constexpr (!ND) wa[t] = sm.wf[par][(t * DKS) * 64 + lane];
     }
 #pragma unroll
@@ -756,19 +760,19 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       if (ks + 1 < DKS) {
 #pragma unroll
         for (int t = 0; t < CT; ++t) {
-          qn[t] = sm.qf[par][(t * DKS + ks + 1) * 64 + lane];
+          if constexpr (!SV) qn[t] = sm.qf[par][(t * DKS + ks + 1) * 64 + lane];
           if constexpr (!ND) wn[t] = sm.wf[par][(t * DKS + ks + 1) * 64 + lane];
         }
       }
 #pragma unroll
       for (int t = 0; t < CT; ++t) {
-        O[t] = mma(Sf[ks], qa[t], O[t]);
+        if constexpr (!SV) O[t] = mma(Sf[ks], qa[t], O[t]);
         if constexpr (!ND) WS[t] = mma(wa[t], Sf[ks], WS[t]);
       }
       if (ks + 1 < DKS) {
 #pragma unroll
         for (int t = 0; t < CT; ++t) {
-          qa[t] = qn[t];
+          if constexpr (!SV) qa[t] = qn[t];
           if constexpr (!ND) wa[t] = wn[t];
         }
       }
@@ -806,6 +810,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     // accumulators per step)
 #pragma unroll
     for (int ks = 0; ks < CKS; ++ks) {
+      if constexpr (SV) break;
       Frag<E> pa[CT];
 #pragma unroll
       for (int nt = 0; nt < CT; ++nt)
@@ -940,20 +945,24 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
   const unsigned scan_groups = (unsigned)(a.num_seqs * a.h_v * G::NCB);
   for (int stage = first; stage <= last; ++stage) {
     switch (stage) {
+      // the backward pass (backward workspace pointers set) takes no flags
       case 1: {
         const dim3 g(nc, (unsigned)a.h_qk);
-        if (a.prep) gdn_k1_chunk_prep<E, D, C, true><<<g, dim3(kBlock), 0, s>>>(a);
-        else gdn_k1_chunk_prep<E, D, C, false><<<g, dim3(kBlock), 0, s>>>(a);
+        if (a.k_frag) gdn_k1_chunk_prep<E, D, C, false, true><<<g, dim3(kBlock), 0, s>>>(a);
+        else if (a.prep) gdn_k1_chunk_prep<E, D, C, true, false><<<g, dim3(kBlock), 0, s>>>(a);
+        else gdn_k1_chunk_prep<E, D, C, false, false><<<g, dim3(kBlock), 0, s>>>(a);
         break;
       }
       case 2: {
         const dim3 g(nc * (unsigned)a.h_v);
-        if (a.prep) {
-          if (a.no_delta) gdn_k2_inverse_w<E, D, C, true, true><<<g, dim3(kBlock), 0, s>>>(a);
-          else gdn_k2_inverse_w<E, D, C, true, false><<<g, dim3(kBlock), 0, s>>>(a);
+        if (a.pt) {
+          gdn_k2_inverse_w<E, D, C, false, false, true><<<g, dim3(kBlock), 0, s>>>(a);
+        } else if (a.prep) {
+          if (a.no_delta) gdn_k2_inverse_w<E, D, C, true, true, false><<<g, dim3(kBlock), 0, s>>>(a);
+          else gdn_k2_inverse_w<E, D, C, true, false, false><<<g, dim3(kBlock), 0, s>>>(a);
         } else {
-          if (a.no_delta) gdn_k2_inverse_w<E, D, C, false, true><<<g, dim3(kBlock), 0, s>>>(a);
-          else gdn_k2_inverse_w<E, D, C, false, false><<<g, dim3(kBlock), 0, s>>>(a);
+          if (a.no_delta) gdn_k2_inverse_w<E, D, C, false, true, false><<<g, dim3(kBlock), 0, s>>>(a);
+          else gdn_k2_inverse_w<E, D, C, false, false, false><<<g, dim3(kBlock), 0, s>>>(a);
         }
         break;
       }

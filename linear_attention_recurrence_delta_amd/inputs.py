@@ -97,6 +97,18 @@ def make_decode(seed, batch, steps, h_qk, h_v, d, dtype="bf16"):
     )
 
 
+def make_backward_seeds(seed, seq_lens, h_v, d, dtype="bf16"):
+    """Upstream gradients for the backward pass: d_o = dL/do ~ N(0, 1)
+    [T, h_v, d] in the input dtype, and d_final = dL/d(final state) ~ N(0, 1)
+    [N, h_v, d, d] fp32 (a loss L = <o, R_o> + <S_final, R_f> with Gaussian
+    R). Draw order: d_o, d_final."""
+    rng = np.random.default_rng(seed)
+    T = int(sum(int(x) for x in seq_lens))
+    d_o = torch.from_numpy(rng.standard_normal((T, h_v, d))).to(_DTYPES[dtype])
+    d_final = torch.from_numpy(rng.standard_normal((len(seq_lens), h_v, d, d)).astype(np.float32))
+    return dict(d_o=d_o, d_final=d_final)
+
+
 def make_prefill_raw(seed, seq_lens, h_qk, h_v, d, dtype="bf16", init="zeros"):
     """Raw inputs for fused input preparation: q, k ~ N(0, 1) times a
     per-(token, head) scale exp(N(0, 0.5^2)) (not normalised), v ~ N(0, 1),

@@ -26,15 +26,25 @@ SOURCES = {"gdn_k1_chunk_prep": "gdn_prefill.hip", "gdn_k2_inverse_w": "gdn_pref
            "gdn_k3_scan": "gdn_prefill.hip", "gdn_kd_decode_step": "gdn_decode.hip"}
 
 
+# compile-time switches of each kernel, in template-argument order (the bool
+# arguments follow the dtype and sizes); a true switch labels the instance
+FLAGS = {"gdn_k1_chunk_prep": ("prep", "bwd"), "gdn_k2_inverse_w": ("prep", "gate-only", "bwd"),
+         "gdn_k3_scan": ("gate-only", "save"), "gdn_kd_decode_step": ("prep", "gate-only"),
+         "gdn_kd_decode_multi": ("prep", "gate-only")}
+
+
 def short_name(name):
-    """Kernel name without its template arguments; the instances compiled
-    for fused input preparation (bool template argument true: `Lb1E` when
-    mangled, `true>` when demangled) get the suffix `[prep]`."""
+    """Kernel name without template arguments, with the names of the
+    instance's true compile-time switches in brackets (from the mangled
+    `Lb1E` / demangled `true` bool arguments)."""
     m = re.search(r"(gdn_k\w+?)(?:I|\(|<|E|$)", name)
-    if m:
-        prep = "Lb1E" in name or "true>" in name
-        return m.group(1) + (" [prep]" if prep else "")
-    return name.split("(")[0][:60]
+    if not m:
+        return name.split("(")[0][:60]
+    base = m.group(1)
+    bools = re.findall(r"Lb([01])E", name) or [("1" if b == "true" else "0")
+                                                for b in re.findall(r"\b(true|false)\b", name)]
+    on = [f for f, b in zip(FLAGS.get(base, ()), bools) if b == "1"]
+    return base + (f" [{', '.join(on)}]" if on else "")
 
 
 def kernel_stats(path):

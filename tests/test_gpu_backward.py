@@ -116,3 +116,40 @@ def test_backward_empty_sequences_pass_the_state_gradient_through():
     torch.cuda.synchronize()
     assert g["dq"].numel() == 0
     assert torch.equal(g["d_init_state"], dfin)
+
+
+def test_backward_long_64k_tail_of_sampled_group():
+    # Full size, in the launch configuration bench.py times: one
+    # gdn_chunk_bwd over the 64K-token layer (16 QK / 48 V heads, d = 128,
+    # chunk 64, bf16). The gradients of the last L tokens depend on earlier
+    # tokens only through the state entering them, so for one sampled QK
+    # group the oracle runs its forward recurrence to token T - L and then
+    # backpropagates over the last L tokens from that state.
+    T, L, hq = 65536, 512, 13
+    say(f"backward long_64k: tail of {L} tokens, QK group {hq}")
+    inp = I.workload_inputs("long_64k")
+    seeds = I.make_backward_seeds(31, [T], 48, 128, "bf16")
+    dv_ = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    g = gdn.gdn_chunk_bwd(dv_["q"], dv_["k"], dv_["v"], dv_["log_alpha"], dv_["beta"], seeds["d_o"].to(DEV),
+                          dv_["init_state"], None, seeds["d_final"].to(DEV), chunk=64)
+    torch.cuda.synchronize()
+    hv = slice(3 * hq, 3 * hq + 3)
+    head = dict(q=np64(inp["q"][:, hq:hq + 1]), k=np64(inp["k"][:, hq:hq + 1]), v=np64(inp["v"][:, hv]),
+                log_alpha=np64(inp["log_alpha"][:, hv]), beta=np64(inp["beta"][:, hv]))
+    _, s_mid = O.recurrent_form1(**{n: x[:T - L] for n, x in head.items()},
+                                 init_state=np64(inp["init_state"][:, hv]))
+    want = O.recurrent_form1_backward(**{n: x[T - L:] for n, x in head.items()},
+                                      do=np64(seeds["d_o"][T - L:, hv]), dfinal=np64(seeds["d_final"][:, hv]),
+                                      init_state=s_mid)
+    got = {"dq": np64(g["dq"][T - L:, hq:hq + 1]), "dk": np64(g["dk"][T - L:, hq:hq + 1]),
+           "dv": np64(g["dv"][T - L:, hv]), "dlog_alpha": np64(g["dlog_alpha"][T - L:, hv]),
+           "dbeta": np64(g["dbeta"][T - L:, hv])}
+    want = {n: want[n] for n in got}
+    bad = []
+    for name in got:
+        rel = np.linalg.norm(got[name] - want[name]) / np.linalg.norm(want[name])
+        mx = np.abs(got[name] - want[name]).max() / np.abs(want[name]).max()
+        print(f"  {name}: rel-L2 {rel:.2e} max {mx:.2e}", flush=True)
+        if not (rel <= 1e-2 and mx <= 2e-2):
+            bad.append(name)
+    assert not bad, bad

@@ -263,19 +263,6 @@ struct GradSmem {
   float sums[2];                       // <S0, dS_L>; sum of the state-term row factors
 };
 
-// sum over the 16 lanes that hold one accumulator row's columns
-__device__ __forceinline__ float row_sum16(float x) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m);
-  return x;
-}
-// sum over the 4 lane quads (the rows of a column, after the lane's own 4)
-__device__ __forceinline__ float col_sum4q(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
-
 template <typename E, int D, int C>
 __global__ __launch_bounds__(kGradBlock) void gdn_kb_grad(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
@@ -405,8 +392,8 @@ __global__ __launch_bounds__(kGradBlock) void gdn_kb_grad(const PrefillArgs a) {
         const float eq = aq[i] * sm.ea[r];
         dQ[u][i] += eq;
         dK[u][i] += ak[i] * sm.ed[r];
-        const float pq = row_sum16(eq * to_f(sm.qs[r * KLD + d]));
-        const float pk = row_sum16(sm.ed[r] * ak[i] * to_f(sm.ks[r * KLD + d]));
+        const float pq = sum16(eq * to_f(sm.qs[r * KLD + d]));
+        const float pk = sum16(sm.ed[r] * ak[i] * to_f(sm.ks[r * KLD + d]));
         if (l16 == 0) {
           atomicAdd(&sm.dg[r], pq - pk);
           atomicAdd(&sm.sums[1], pk);
@@ -414,8 +401,7 @@ __global__ __launch_bounds__(kGradBlock) void gdn_kb_grad(const PrefillArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);   // one tile's operands live at a time
     }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) fro += __shfl_xor(fro, m);
+    fro = sum_rows4(sum16(fro));
     if (lane == 0) atomicAdd(&sm.sums[0], fro);
 
     // dP = dO U^T: dP * P into dg, dPm = dP * Dincl into x1
@@ -437,13 +423,13 @@ __global__ __launch_bounds__(kGradBlock) void gdn_kb_grad(const PrefillArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * quad + i;
         const float m2 = acc[i] * to_f(pv[i + 4 * (rt & 1)]);
-        const float rs = row_sum16(m2);
+        const float rs = sum16(m2);
         if (l16 == 0) atomicAdd(&sm.dg[r], rs);
         colp += m2;
         const float gm = (j <= r && r < len) ? __expf(fminf(sm.g[r] - sm.g[j], 0.f)) : 0.f;
         sm.x1[r * FLD + j] = acc[i] * gm;
       }
-      colp = col_sum4q(colp);
+      colp = sum_rows4(colp);
       if (quad == 0) atomicAdd(&sm.dg[j], -colp);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -522,8 +508,8 @@ __global__ __launch_bounds__(kGradBlock) void gdn_kb_grad(const PrefillArgs a) {
         const float da = lower ? -acc[e] : 0.f;
         const float bm = da * sm.b[r] * gm;
         const float mb2 = bm * kk[e];
-        const float rdb = row_sum16(da * kk[e] * gm);
-        const float rdg = row_sum16(mb2);
+        const float rdb = sum16(da * kk[e] * gm);
+        const float rdg = sum16(mb2);
         if (l16 == 0) {
           atomicAdd(&sm.db[r], rdb);
           atomicAdd(&sm.dg[r], rdg);
@@ -531,7 +517,7 @@ __global__ __launch_bounds__(kGradBlock) void gdn_kb_grad(const PrefillArgs a) {
         colm += mb2;
         sm.x1[r * FLD + i] = bm;
       }
-      colm = col_sum4q(colm);
+      colm = sum_rows4(colm);
       if (quad == 0) atomicAdd(&sm.dg[i], -colm);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -561,8 +547,8 @@ __global__ __launch_bounds__(kGradBlock) void gdn_kb_grad(const PrefillArgs a) {
         const float br = sm.b[r], bgr = sm.b[r] * sm.ea[r];
         if (r < len) dvg[((int64_t)(start + r) * a.h_v + hv) * D + d] = to_e<E>(br * au[e]);
         dK[u][e] += bgr * aw[e];
-        const float rv = row_sum16(au[e] * to_f(sm.r1[r * KLD + d]));
-        const float rk = row_sum16(aw[e] * to_f(sm.ks[r * KLD + d]));
+        const float rv = sum16(au[e] * to_f(sm.r1[r * KLD + d]));
+        const float rk = sum16(aw[e] * to_f(sm.ks[r * KLD + d]));
         if (l16 == 0) {
           atomicAdd(&sm.db[r], rv + sm.ea[r] * rk);
           atomicAdd(&sm.dg[r], bgr * rk);

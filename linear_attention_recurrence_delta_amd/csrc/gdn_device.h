@@ -97,6 +97,27 @@ __device__ __forceinline__ Frag<E> acc_to_frag(const f32x4& lo, const f32x4& hi)
 
 __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
+// Cross-lane sums without LDS round trips. The accumulator of a 16x16 tile
+// holds one row in each 16-lane row of the wave, so a row's sum over its
+// columns is a sum over those 16 lanes (DPP: swap neighbours, then pairs,
+// then mirror within 8 and within 16 lanes; every lane gets the sum). Sums
+// across the four 16-lane rows use the lane-row swaps (v_permlane16_swap
+// and v_permlane32_swap: with both operands x, the two results add up to
+// x[l] + x[l ^ 16], respectively x[l] + x[l ^ 32]).
+__device__ __forceinline__ float sum16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // row_mirror
+  return x;
+}
+__device__ __forceinline__ float sum_rows4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = __int_as_float(a[0]) + __int_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(b[0]) + __int_as_float(b[1]);
+}
+
 // Fused input preparation (GDN_FLAG_PREPARE_INPUTS): the gate maps
 // log(alpha) = -softplus(a) and beta = sigmoid(b), written so that neither
 // overflows for any sign of the logit, and the L2 normalisation of q and k.

@@ -198,3 +198,58 @@ def test_header_flag_values_match_the_binding():
 def test_status_strings(lib):
     for code, name in B.STATUS.items():
         assert lib.gdn_status_string(code).decode() == name
+
+
+# --- backward pass ---------------------------------------------------------
+
+def bwd_bytes(lib, d):
+    return lib.gdn_chunk_bwd_workspace_bytes(ctypes.byref(d))
+
+
+def call_bwd(lib, d, q=FAKE, k=FAKE, v=FAKE, la=FAKE, b=FAKE, init=None, cu=None, do=FAKE * 3,
+             dfin=None, dq=FAKE * 5, dk=FAKE * 6, dv=FAKE * 7, dla=FAKE * 9, db=FAKE * 10, dinit=None,
+             ws=FAKE * 12, wsb=None, stages=None):
+    if wsb is None:
+        wsb = bwd_bytes(lib, d) if bwd_bytes(lib, d) else 1 << 40
+    vp = ctypes.c_void_p
+    args = [ctypes.byref(d), vp(q), vp(k), vp(v), vp(la), vp(b), vp(init), vp(cu), vp(do), vp(dfin), vp(dq),
+            vp(dk), vp(dv), vp(dla), vp(db), vp(dinit), vp(ws), wsb, None]
+    if stages is None:
+        return lib.gdn_chunk_bwd(*args)
+    return lib.gdn_chunk_bwd_stages(*args, *stages)
+
+
+def test_bwd_workspace_size_formula(lib):
+    # the forward workspace, then K, Q^T, query-indexed q.k fragments (per QK
+    # head), P^T, W^T fragments, Tinv^T, the chunk-start states, U, dS_end
+    # and dU (per V head), each padded to 256 bytes
+    d = dims(num_seqs=3, total_tokens=1000)
+    nc = 1000 // 64 + 3
+    def up(x):
+        return (x + 255) // 256 * 256
+    want = (ws_bytes(lib, d) + up(nc * 16 * 64 * 128 * 2) + up(nc * 16 * 128 * 64 * 2) + up(nc * 16 * 64 * 64 * 2)
+            + up(nc * 48 * 64 * 64 * 2) + up(nc * 48 * 128 * 64 * 2) + up(nc * 48 * 64 * 64 * 2)
+            + up(nc * 48 * 128 * 128 * 2) + up(nc * 48 * 64 * 128 * 2) + up(nc * 48 * 128 * 128 * 2)
+            + up(nc * 48 * 64 * 128 * 2))
+    assert bwd_bytes(lib, d) == want
+
+
+def test_bwd_rejects_flags_and_bad_arguments(lib):
+    d = dims()
+    for flags in (1, 2, 3):
+        assert bwd_bytes(lib, dims(flags=flags)) == 0
+        assert call_bwd(lib, dims(flags=flags), wsb=1 << 40) == NOT_SUPPORTED
+    assert call_bwd(lib, d, do=None) == INVALID
+    assert "d_o is NULL" in lib.gdn_last_error_message().decode()
+    assert call_bwd(lib, d, dla=FAKE * 9 + 2) == INVALID          # 4-byte alignment
+    assert call_bwd(lib, d, dq=FAKE) == INVALID                   # dq aliases q
+    assert call_bwd(lib, d, dv=FAKE * 5) == INVALID               # dv aliases dq
+    assert call_bwd(lib, d, db=FAKE * 3) == INVALID               # dbeta aliases d_o
+    assert call_bwd(lib, d, init=FAKE * 14, dinit=FAKE * 14) == INVALID
+    assert call_bwd(lib, d, dfin=FAKE * 14 + 4) == INVALID
+    assert call_bwd(lib, dims(num_seqs=2), cu=None) == INVALID
+    assert call_bwd(lib, d, ws=None) == WORKSPACE
+    assert call_bwd(lib, d, wsb=bwd_bytes(lib, d) - 1) == WORKSPACE
+    assert call_bwd(lib, dims(dtype=0)) == NOT_SUPPORTED          # fp32 at head dim 128 needs chunk 16
+    for st in ((0, 5), (1, 6), (4, 3)):
+        assert call_bwd(lib, d, stages=st) == INVALID

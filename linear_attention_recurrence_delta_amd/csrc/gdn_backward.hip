@@ -235,46 +235,58 @@ __global__ __launch_bounds__(kBlock) void gdn_kb_dstate(const PrefillArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// Gradient kernel: one workgroup per (chunk slot, QK head), 8 waves; the V
-// heads of the group are taken in turn and their dq, dk contributions stay
-// in registers (wave w owns the C x D output tiles t = w, w + 8, ...).
-// Operands are staged in LDS as rows; products with the chunk-start state
-// and dS_L read those row-major matrices straight from the workspace; the
+// Gradient kernel: one workgroup per (chunk slot, QK head), 4 waves, 80 KB
+// of LDS so that two workgroups share a CU (one's barriers and loads overlap
+// the other's products). The V heads of the group are taken in turn; their
+// dq, dk contributions stay in registers (wave w owns the C x D output
+// tiles t = w, w + 4, ...). Per V head, dL/do, U and dU rows and Tinv^T are
+// staged in LDS; the chunk-start state and dS_L are read straight from the
+// workspace as fragments of their transposes; K and Q come from the
+// fragments kernel 1 wrote: K fragments (row r, k = d) for the products
+// that contract over d, K^T and Q^T fragments (row d, k = token) for those
+// that contract over tokens and for their elements, since fragment
+// (dt, rt/2) of K^T holds, at element i + 4 (rt & 1), exactly the element
+// (16 rt + 4 quad + i, 16 dt + l16) of a C x D accumulator tile. The
 // C x C x C products of dA run in fp32 (v_mfma_f32_16x16x4_f32), every other
-// product on bf16 (or fp32) MFMA with fp32 accumulation. Row and column sums
-// of the per-element terms go through lane exchanges and LDS atomics.
+// product on the input dtype's MFMA with fp32 accumulation. Row and column
+// sums of the per-element terms use DPP and lane-row swaps, then LDS
+// atomics.
 // --------------------------------------------------------------------------
-constexpr int kGradBlock = 512;
+constexpr int kGradBlock = 256;
 
 template <typename E, int D, int C>
 struct GradSmem {
   static constexpr int KLD = D + 8;    // row stride of the staged D-wide rows
   static constexpr int FLD = C + 4;    // row stride of the fp32 C x C scratch
   static constexpr int TLD = C + 8;    // row stride of Tinv^T
-  E ks[C * KLD] __attribute__((aligned(16)));
-  E qs[C * KLD] __attribute__((aligned(16)));
-  E r1[C * KLD] __attribute__((aligned(16)));   // dL/do rows, later v rows
-  E r2[C * KLD] __attribute__((aligned(16)));   // U rows, later dW rows
+  union {
+    E r1[C * KLD];                     // dL/do rows, then v rows
+    float y[C * FLD];                  // then Y = dT Tinv^T (fp32)
+  } __attribute__((aligned(16))) u1;
+  E r2[C * KLD] __attribute__((aligned(16)));   // U rows, then dW rows
   E r3[C * KLD] __attribute__((aligned(16)));   // dU rows
   E tt[C * TLD] __attribute__((aligned(16)));   // Tinv^T rows
   float x1[C * FLD] __attribute__((aligned(16)));
-  float x2[C * FLD] __attribute__((aligned(16)));
   float g[C], b[C], ea[C], ed[C], dg[C], db[C];
   float sums[2];                       // <S0, dS_L>; sum of the state-term row factors
 };
 
 template <typename E, int D, int C>
-__global__ __launch_bounds__(kGradBlock) void gdn_kb_grad(const PrefillArgs a) {
+__global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   using SM = GradSmem<E, D, C>;
   constexpr int DT = G::DT, CT = G::CT, DKS = G::DKS, CKS = G::CKS;
   constexpr int KLD = SM::KLD, FLD = SM::FLD, TLD = SM::TLD;
   constexpr int NW = kGradBlock / 64;
-  constexpr int NCD = CT * DT, TPW = (NCD + NW - 1) / NW;      // C x D tiles, per wave
-  constexpr int NCC = CT * CT, TPC = (NCC + NW - 1) / NW;      // C x C tiles, per wave
+  // wave w owns the C x D tiles of d-tiles w, w + NW, ... (all row tiles)
+  // and the C x C tiles of column tiles w, w + NW, ...: the operand of a
+  // column tile is loaded once and used for every row tile
+  constexpr int DPW = (DT + NW - 1) / NW, TPW = DPW * CT;     // d-tiles, C x D tiles per wave
+  constexpr int JPW = (CT + NW - 1) / NW;                     // C x C column tiles per wave
   constexpr int VE = 16 / (int)sizeof(E);
   typedef E VLoad __attribute__((ext_vector_type(VE)));
   __shared__ SM sm;
+  float* ys = sm.u1.y;
   const int64_t c = blockIdx.x;
   const int hq = blockIdx.y;
   const int4 tab = reinterpret_cast<const int4*>(a.chunk_table)[c];
@@ -325,13 +337,21 @@ __global__ __launch_bounds__(kGradBlock) void gdn_kb_grad(const PrefillArgs a) {
     return f;
   };
 
-  stage_rows(sm.ks, a.k, a.h_qk, hq);
-  stage_rows(sm.qs, a.q, a.h_qk, hq);
   f32x4 dQ[TPW], dK[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) { dQ[u] = zero4(); dK[u] = zero4(); }
   const Frag<E>* ktf = reinterpret_cast<const Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
   const Frag<E>* qtf = reinterpret_cast<const Frag<E>*>(a.q_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
+  const Frag<E>* kff = reinterpret_cast<const Frag<E>*>(a.k_frag) + (c * a.h_qk + hq) * G::Q_FR * 64;
+  // element (16 rt + 4 quad + i, 16 dt + l16) of K or Q, for i = 0..3, from
+  // their transposed fragments
+  auto tile_elems = [&](const Frag<E>* tf, int rt, int dt) __attribute__((always_inline)) {
+    const Frag<E> f = tf[(dt * CKS + (rt >> 1)) * 64 + lane];
+    f32x4 x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = to_f(f[i + 4 * (rt & 1)]);
+    return x;
+  };
 
   for (int h = 0; h < a.group; ++h) {
     const int hv = hq * a.group + h;
@@ -351,7 +371,7 @@ __global__ __launch_bounds__(kGradBlock) void gdn_kb_grad(const PrefillArgs a) {
     }
     if (tid < 2) sm.sums[tid] = 0.f;
     const float gl = a.dtab[ch * (2 * C + 4) + 2 * C];
-    stage_rows(sm.r1, a.d_o, a.h_v, hv);
+    stage_rows(sm.u1.r1, a.d_o, a.h_v, hv);
     stage_ws(sm.r2, static_cast<const E*>(a.ub) + ch * C * D);
     stage_ws(sm.r3, static_cast<const E*>(a.du) + ch * C * D);
     {
@@ -366,40 +386,46 @@ __global__ __launch_bounds__(kGradBlock) void gdn_kb_grad(const PrefillArgs a) {
     f32x4 dW[TPW];
     float fro = 0.f;
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int t = wave + NW * u;
-      dW[u] = zero4();
-      if (t >= NCD) continue;
-      const int rt = t / DT, dt = t % DT;
-      f32x4 aq = zero4(), ak = zero4(), aw = zero4();
+    for (int j = 0; j < DPW; ++j) {
+      const int dt = wave + NW * j;
+#pragma unroll
+      for (int rt = 0; rt < CT; ++rt) dW[j * CT + rt] = zero4();
+      if (dt >= DT) continue;
+      Frag<E> bs[DKS], bl[DKS];
 #pragma unroll
       for (int ks = 0; ks < DKS; ++ks) {
-        const Frag<E> bs = load_frag<E>(scg + (16 * dt + l16) * D + 32 * ks, quad, D - 32 * ks);
-        const Frag<E> bl = load_frag<E>(dsg + (16 * dt + l16) * D + 32 * ks, quad, D - 32 * ks);
-        aq = mma(frag_row(sm.r1, KLD, 16 * rt, ks, D), bs, aq);
-        ak = mma(frag_row(sm.r2, KLD, 16 * rt, ks, D), bl, ak);
-        aw = mma(frag_row(sm.r3, KLD, 16 * rt, ks, D), bs, aw);
-        if (rt == 0) {
+        bs[ks] = load_frag<E>(scg + (16 * dt + l16) * D + 32 * ks, quad, D - 32 * ks);
+        bl[ks] = load_frag<E>(dsg + (16 * dt + l16) * D + 32 * ks, quad, D - 32 * ks);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) fro += to_f(bs[e]) * to_f(bl[e]);
+        for (int e = 0; e < 8; ++e) fro += to_f(bs[ks][e]) * to_f(bl[ks][e]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < CT; ++rt) {
+        const int u = j * CT + rt;
+        f32x4 aq = zero4(), ak = zero4(), aw = zero4();
+#pragma unroll
+        for (int ks = 0; ks < DKS; ++ks) {
+          aq = mma(frag_row(sm.u1.r1, KLD, 16 * rt, ks, D), bs[ks], aq);
+          ak = mma(frag_row(sm.r2, KLD, 16 * rt, ks, D), bl[ks], ak);
+          aw = mma(frag_row(sm.r3, KLD, 16 * rt, ks, D), bs[ks], aw);
+        }
+        dW[u] = -aw;
+        const f32x4 qv = tile_elems(qtf, rt, dt), kv = tile_elems(ktf, rt, dt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * quad + i;
+          const float eq = aq[i] * sm.ea[r];
+          dQ[u][i] += eq;
+          dK[u][i] += ak[i] * sm.ed[r];
+          const float pq = sum16(eq * qv[i]);
+          const float pk = sum16(sm.ed[r] * ak[i] * kv[i]);
+          if (l16 == 0) {
+            atomicAdd(&sm.dg[r], pq - pk);
+            atomicAdd(&sm.sums[1], pk);
+          }
         }
       }
-      dW[u] = -aw;
-      const int d = 16 * dt + l16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * quad + i;
-        const float eq = aq[i] * sm.ea[r];
-        dQ[u][i] += eq;
-        dK[u][i] += ak[i] * sm.ed[r];
-        const float pq = sum16(eq * to_f(sm.qs[r * KLD + d]));
-        const float pk = sum16(sm.ed[r] * ak[i] * to_f(sm.ks[r * KLD + d]));
-        if (l16 == 0) {
-          atomicAdd(&sm.dg[r], pq - pk);
-          atomicAdd(&sm.sums[1], pk);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);   // one tile's operands live at a time
+      __builtin_amdgcn_sched_barrier(0);   // one d-tile's operands live at a time
     }
     fro = sum_rows4(sum16(fro));
     if (lane == 0) atomicAdd(&sm.sums[0], fro);
@@ -407,151 +433,189 @@ __global__ __launch_bounds__(kGradBlock) void gdn_kb_grad(const PrefillArgs a) {
     // dP = dO U^T: dP * P into dg, dPm = dP * Dincl into x1
     const Frag<E>* ptf = reinterpret_cast<const Frag<E>*>(a.pt) + ch * G::QK_FR * 64;
 #pragma unroll
-    for (int u = 0; u < TPC; ++u) {
-      const int t = wave + NW * u;
-      if (t >= NCC) continue;
-      const int rt = t / CT, jt = t % CT;
-      f32x4 acc = zero4();
+    for (int j2 = 0; j2 < JPW; ++j2) {
+      const int jt = wave + NW * j2;
+      if (jt >= CT) continue;
+      Frag<E> ub[DKS];
 #pragma unroll
-      for (int ks = 0; ks < DKS; ++ks) acc = mma(frag_row(sm.r1, KLD, 16 * rt, ks, D), frag_row(sm.r2, KLD, 16 * jt, ks, D), acc);
-      // P[r][j] for this tile's elements: fragment (jt, rt/2) of P^T holds
-      // row 16 rt + 4 quad + i at element i (+4 for an odd rt)
-      const Frag<E> pv = ptf[(jt * CKS + (rt >> 1)) * 64 + lane];
+      for (int ks = 0; ks < DKS; ++ks) ub[ks] = frag_row(sm.r2, KLD, 16 * jt, ks, D);
       const int j = 16 * jt + l16;
       float colp = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * quad + i;
-        const float m2 = acc[i] * to_f(pv[i + 4 * (rt & 1)]);
-        const float rs = sum16(m2);
-        if (l16 == 0) atomicAdd(&sm.dg[r], rs);
-        colp += m2;
-        const float gm = (j <= r && r < len) ? __expf(fminf(sm.g[r] - sm.g[j], 0.f)) : 0.f;
-        sm.x1[r * FLD + j] = acc[i] * gm;
+      for (int rt = 0; rt < CT; ++rt) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < DKS; ++ks) acc = mma(frag_row(sm.u1.r1, KLD, 16 * rt, ks, D), ub[ks], acc);
+        // P[r][j] for this tile's elements: fragment (jt, rt/2) of P^T holds
+        // row 16 rt + 4 quad + i at element i (+4 for an odd rt)
+        const Frag<E> pv = ptf[(jt * CKS + (rt >> 1)) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * quad + i;
+          const float m2 = acc[i] * to_f(pv[i + 4 * (rt & 1)]);
+          const float rs = sum16(m2);
+          if (l16 == 0) atomicAdd(&sm.dg[r], rs);
+          colp += m2;
+          const float gm = (j <= r && r < len) ? __expf(fminf(sm.g[r] - sm.g[j], 0.f)) : 0.f;
+          sm.x1[r * FLD + j] = acc[i] * gm;
+        }
       }
       colp = sum_rows4(colp);
       if (quad == 0) atomicAdd(&sm.dg[j], -colp);
-      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();                   // x1 complete; U rows dead
+    __syncthreads();                   // x1 complete; dL/do and U rows dead
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int t = wave + NW * u;
-      if (t >= NCD) continue;
-      const int rt = t / DT, dt = t % DT;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm.r2[(16 * rt + 4 * quad + i) * KLD + 16 * dt + l16] = to_e<E>(dW[u][i]);
-      // dQ += dPm K, dK += dPm^T Q
+    for (int j = 0; j < DPW; ++j) {
+      const int dt = wave + NW * j;
+      if (dt >= DT) continue;
+      Frag<E> kb[CKS], qb[CKS];
 #pragma unroll
       for (int s = 0; s < CKS; ++s) {
-        dQ[u] = mma(frag_row32(sm.x1, FLD, 16 * rt, s, C), ktf[(dt * CKS + s) * 64 + lane], dQ[u]);
-        dK[u] = mma(frag_col(sm.x1, FLD, 16 * rt, s, C), qtf[(dt * CKS + s) * 64 + lane], dK[u]);
+        kb[s] = ktf[(dt * CKS + s) * 64 + lane];
+        qb[s] = qtf[(dt * CKS + s) * 64 + lane];
+      }
+#pragma unroll
+      for (int rt = 0; rt < CT; ++rt) {
+        const int u = j * CT + rt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.r2[(16 * rt + 4 * quad + i) * KLD + 16 * dt + l16] = to_e<E>(dW[u][i]);
+        // dQ += dPm K, dK += dPm^T Q
+#pragma unroll
+        for (int s = 0; s < CKS; ++s) {
+          dQ[u] = mma(frag_row32(sm.x1, FLD, 16 * rt, s, C), kb[s], dQ[u]);
+          dK[u] = mma(frag_col(sm.x1, FLD, 16 * rt, s, C), qb[s], dK[u]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();                   // dL/do rows and x1 dead; dW rows complete
-    stage_rows(sm.r1, a.v, a.h_v, hv);
-    __syncthreads();
+    stage_rows(sm.u1.r1, a.v, a.h_v, hv);
+    __syncthreads();                   // v rows and dW rows complete; x1 dead
 
     // dT = (dU V^T) diag(b) + (dW K^T) diag(b ea) into x1
 #pragma unroll
-    for (int u = 0; u < TPC; ++u) {
-      const int t = wave + NW * u;
-      if (t >= NCC) continue;
-      const int rt = t / CT, it = t % CT;
-      f32x4 a1 = zero4(), a2 = zero4();
+    for (int j2 = 0; j2 < JPW; ++j2) {
+      const int it = wave + NW * j2;
+      if (it >= CT) continue;
+      Frag<E> vb[DKS], kb[DKS];
 #pragma unroll
       for (int ks = 0; ks < DKS; ++ks) {
-        a1 = mma(frag_row(sm.r3, KLD, 16 * rt, ks, D), frag_row(sm.r1, KLD, 16 * it, ks, D), a1);
-        a2 = mma(frag_row(sm.r2, KLD, 16 * rt, ks, D), frag_row(sm.ks, KLD, 16 * it, ks, D), a2);
+        vb[ks] = frag_row(sm.u1.r1, KLD, 16 * it, ks, D);
+        kb[ks] = kff[(it * DKS + ks) * 64 + lane];
       }
       const int i = 16 * it + l16;
       const float bi = sm.b[i], bgi = sm.b[i] * sm.ea[i];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.x1[(16 * rt + 4 * quad + e) * FLD + i] = a1[e] * bi + a2[e] * bgi;
-      __builtin_amdgcn_sched_barrier(0);
+      for (int rt = 0; rt < CT; ++rt) {
+        f32x4 a1 = zero4(), a2 = zero4();
+#pragma unroll
+        for (int ks = 0; ks < DKS; ++ks) {
+          a1 = mma(frag_row(sm.r3, KLD, 16 * rt, ks, D), vb[ks], a1);
+          a2 = mma(frag_row(sm.r2, KLD, 16 * rt, ks, D), kb[ks], a2);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.x1[(16 * rt + 4 * quad + e) * FLD + i] = a1[e] * bi + a2[e] * bgi;
+      }
     }
-    __syncthreads();
-    // Y = dT Tinv^T into x2 (fp32)
+    __syncthreads();                   // x1 = dT complete; v rows dead
+    // Y = dT Tinv^T (fp32) over the v rows' buffer
 #pragma unroll
-    for (int u = 0; u < TPC; ++u) {
-      const int t = wave + NW * u;
-      if (t >= NCC) continue;
-      const int rt = t / CT, it = t % CT;
-      f32x4 acc = zero4();
+    for (int j2 = 0; j2 < JPW; ++j2) {
+      const int it = wave + NW * j2;
+      if (it >= CT) continue;
 #pragma unroll
-      for (int mb = 0; mb < CT; ++mb)
-        acc = mma16_f32(&sm.x1[(16 * rt) * FLD + 16 * mb], FLD, 1, &sm.tt[(16 * mb) * TLD + 16 * it], TLD, 1, acc, lane);
+      for (int rt = 0; rt < CT; ++rt) {
+        f32x4 acc = zero4();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.x2[(16 * rt + 4 * quad + e) * FLD + 16 * it + l16] = acc[e];
+        for (int mb = 0; mb < CT; ++mb)
+          acc = mma16_f32(&sm.x1[(16 * rt) * FLD + 16 * mb], FLD, 1, &sm.tt[(16 * mb) * TLD + 16 * it], TLD, 1, acc, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ys[(16 * rt + 4 * quad + e) * FLD + 16 * it + l16] = acc[e];
+      }
     }
     __syncthreads();
     // dA = -Tinv^T Y (strictly lower), K K^T; b and g terms of A; B into x1
 #pragma unroll
-    for (int u = 0; u < TPC; ++u) {
-      const int t = wave + NW * u;
-      if (t >= NCC) continue;
-      const int rt = t / CT, it = t % CT;
-      f32x4 acc = zero4(), kk = zero4();
+    for (int j2 = 0; j2 < JPW; ++j2) {
+      const int it = wave + NW * j2;
+      if (it >= CT) continue;
+      Frag<E> kb[DKS];
 #pragma unroll
-      for (int mb = 0; mb < CT; ++mb)
-        acc = mma16_f32(&sm.tt[(16 * rt) * TLD + 16 * mb], TLD, 1, &sm.x2[(16 * mb) * FLD + 16 * it], FLD, 1, acc, lane);
-#pragma unroll
-      for (int ks = 0; ks < DKS; ++ks) kk = mma(frag_row(sm.ks, KLD, 16 * rt, ks, D), frag_row(sm.ks, KLD, 16 * it, ks, D), kk);
+      for (int ks = 0; ks < DKS; ++ks) kb[ks] = kff[(it * DKS + ks) * 64 + lane];
       const int i = 16 * it + l16;
       float colm = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rt + 4 * quad + e;
-        const bool lower = i < r && r < len;
-        const float gm = lower ? __expf(fminf(sm.g[r] - sm.g[i], 0.f)) : 0.f;
-        const float da = lower ? -acc[e] : 0.f;
-        const float bm = da * sm.b[r] * gm;
-        const float mb2 = bm * kk[e];
-        const float rdb = sum16(da * kk[e] * gm);
-        const float rdg = sum16(mb2);
-        if (l16 == 0) {
-          atomicAdd(&sm.db[r], rdb);
-          atomicAdd(&sm.dg[r], rdg);
+      for (int rt = 0; rt < CT; ++rt) {
+        f32x4 acc = zero4(), kk = zero4();
+#pragma unroll
+        for (int mb = 0; mb < CT; ++mb)
+          acc = mma16_f32(&sm.tt[(16 * rt) * TLD + 16 * mb], TLD, 1, &ys[(16 * mb) * FLD + 16 * it], FLD, 1, acc, lane);
+#pragma unroll
+        for (int ks = 0; ks < DKS; ++ks) kk = mma(kff[(rt * DKS + ks) * 64 + lane], kb[ks], kk);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rt + 4 * quad + e;
+          const bool lower = i < r && r < len;
+          const float gm = lower ? __expf(fminf(sm.g[r] - sm.g[i], 0.f)) : 0.f;
+          const float da = lower ? -acc[e] : 0.f;
+          const float bm = da * sm.b[r] * gm;
+          const float mb2 = bm * kk[e];
+          const float rdb = sum16(da * kk[e] * gm);
+          const float rdg = sum16(mb2);
+          if (l16 == 0) {
+            atomicAdd(&sm.db[r], rdb);
+            atomicAdd(&sm.dg[r], rdg);
+          }
+          colm += mb2;
+          sm.x1[r * FLD + i] = bm;
         }
-        colm += mb2;
-        sm.x1[r * FLD + i] = bm;
       }
       colm = sum_rows4(colm);
       if (quad == 0) atomicAdd(&sm.dg[i], -colm);
-      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
-    // dK += (B + B^T) K; dV = diag(b) Tinv^T dU and its b term;
-    // Tinv^T dW into dK and the b, g terms of W
+    // dK += (B + B^T) K; dV = diag(b) Tinv^T dU and its b term (v read from
+    // global); Tinv^T dW into dK and the b, g terms of W
     E* dvg = static_cast<E*>(a.dv);
+    const E* vg = static_cast<const E*>(a.v);
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int t = wave + NW * u;
-      if (t >= NCD) continue;
-      const int rt = t / DT, dt = t % DT;
-      f32x4 au = zero4(), aw = zero4();
+    for (int j = 0; j < DPW; ++j) {
+      const int dt = wave + NW * j;
+      if (dt >= DT) continue;
+      Frag<E> kb[CKS], ub[CKS], wb[CKS];
 #pragma unroll
       for (int s = 0; s < CKS; ++s) {
-        const Frag<E> kb = ktf[(dt * CKS + s) * 64 + lane];
-        dK[u] = mma(frag_row32(sm.x1, FLD, 16 * rt, s, C), kb, dK[u]);
-        dK[u] = mma(frag_col(sm.x1, FLD, 16 * rt, s, C), kb, dK[u]);
-        const Frag<E> ta = frag_row(sm.tt, TLD, 16 * rt, s, C);
-        au = mma(ta, frag_col(sm.r3, KLD, 16 * dt, s, C), au);
-        aw = mma(ta, frag_col(sm.r2, KLD, 16 * dt, s, C), aw);
+        kb[s] = ktf[(dt * CKS + s) * 64 + lane];
+        ub[s] = frag_col(sm.r3, KLD, 16 * dt, s, C);
+        wb[s] = frag_col(sm.r2, KLD, 16 * dt, s, C);
       }
       const int d = 16 * dt + l16;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rt + 4 * quad + e;
-        const float br = sm.b[r], bgr = sm.b[r] * sm.ea[r];
-        if (r < len) dvg[((int64_t)(start + r) * a.h_v + hv) * D + d] = to_e<E>(br * au[e]);
-        dK[u][e] += bgr * aw[e];
-        const float rv = sum16(au[e] * to_f(sm.r1[r * KLD + d]));
-        const float rk = sum16(aw[e] * to_f(sm.ks[r * KLD + d]));
-        if (l16 == 0) {
-          atomicAdd(&sm.db[r], rv + sm.ea[r] * rk);
-          atomicAdd(&sm.dg[r], bgr * rk);
+      for (int rt = 0; rt < CT; ++rt) {
+        const int u = j * CT + rt;
+        f32x4 au = zero4(), aw = zero4();
+#pragma unroll
+        for (int s = 0; s < CKS; ++s) {
+          dK[u] = mma(frag_row32(sm.x1, FLD, 16 * rt, s, C), kb[s], dK[u]);
+          dK[u] = mma(frag_col(sm.x1, FLD, 16 * rt, s, C), kb[s], dK[u]);
+          const Frag<E> ta = frag_row(sm.tt, TLD, 16 * rt, s, C);
+          au = mma(ta, ub[s], au);
+          aw = mma(ta, wb[s], aw);
+        }
+        const f32x4 kv = tile_elems(ktf, rt, dt);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rt + 4 * quad + e;
+          const float br = sm.b[r], bgr = sm.b[r] * sm.ea[r];
+          const int64_t row = ((int64_t)(start + r) * a.h_v + hv) * D + d;
+          const float vv = (r < len) ? to_f(vg[row]) : 0.f;
+          if (r < len) dvg[row] = to_e<E>(br * au[e]);
+          dK[u][e] += bgr * aw[e];
+          const float rv = sum16(au[e] * vv);
+          const float rk = sum16(aw[e] * kv[e]);
+          if (l16 == 0) {
+            atomicAdd(&sm.db[r], rv + sm.ea[r] * rk);
+            atomicAdd(&sm.dg[r], bgr * rk);
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -570,17 +634,20 @@ __global__ __launch_bounds__(kGradBlock) void gdn_kb_grad(const PrefillArgs a) {
   E* dqg = static_cast<E*>(a.dq);
   E* dkg = static_cast<E*>(a.dk);
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int t = wave + NW * u;
-    if (t >= NCD) continue;
-    const int rt = t / DT, dt = t % DT;
+  for (int j = 0; j < DPW; ++j) {
+    const int dt = wave + NW * j;
+    if (dt >= DT) continue;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * rt + 4 * quad + e;
-      if (r < len) {
-        const int64_t o = ((int64_t)(start + r) * a.h_qk + hq) * D + 16 * dt + l16;
-        dqg[o] = to_e<E>(dQ[u][e]);
-        dkg[o] = to_e<E>(dK[u][e]);
+    for (int rt = 0; rt < CT; ++rt) {
+      const int u = j * CT + rt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * quad + e;
+        if (r < len) {
+          const int64_t o = ((int64_t)(start + r) * a.h_qk + hq) * D + 16 * dt + l16;
+          dqg[o] = to_e<E>(dQ[u][e]);
+          dkg[o] = to_e<E>(dK[u][e]);
+        }
       }
     }
   }

@@ -258,6 +258,7 @@ template <typename E, int D, int C>
 struct GradSmem {
   static constexpr int KLD = D + 8;    // row stride of the staged D-wide rows
   static constexpr int FLD = C + 4;    // row stride of the fp32 C x C scratch
+  static constexpr int ELD = C + 8;    // row stride of the same scratch holding input-dtype matrices
   static constexpr int TLD = C + 8;    // row stride of Tinv^T
   union {
     E r1[C * KLD];                     // dL/do rows, then v rows
@@ -266,7 +267,10 @@ struct GradSmem {
   E r2[C * KLD] __attribute__((aligned(16)));   // U rows, then dW rows
   E r3[C * KLD] __attribute__((aligned(16)));   // dU rows
   E tt[C * TLD] __attribute__((aligned(16)));   // Tinv^T rows
-  float x1[C * FLD] __attribute__((aligned(16)));
+  union {
+    float f[C * FLD];                  // dT (fp32)
+    E e[C * ELD];                      // dP * Dincl, then B + B^T (MFMA operands only)
+  } __attribute__((aligned(16))) x1;
   float g[C], b[C], ea[C], ed[C], dg[C], db[C];
   float sums[2];                       // <S0, dS_L>; sum of the state-term row factors
 };
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
   using G = Cfg<E, D, C>;
   using SM = GradSmem<E, D, C>;
   constexpr int DT = G::DT, CT = G::CT, DKS = G::DKS, CKS = G::CKS;
-  constexpr int KLD = SM::KLD, FLD = SM::FLD, TLD = SM::TLD;
+  constexpr int KLD = SM::KLD, FLD = SM::FLD, ELD = SM::ELD, TLD = SM::TLD;
   constexpr int NW = kGradBlock / 64;
   // wave w owns the C x D tiles of d-tiles w, w + NW, ... (all row tiles)
   // and the C x C tiles of column tiles w, w + NW, ...: the operand of a
@@ -296,16 +300,18 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
   // there); the wave index is uniform
   int tid = threadIdx.x, lane = tid & 63, quad = lane >> 4, l16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool has_dt = wave < DT;       // the wave owns at least one d-tile
 
-  // rows [0, C) of a [T][H][D] input into LDS (zero past the chunk end)
+  // rows [0, C) of a [T][H][D] input into LDS (zero past the chunk end);
+  // a uniform base pointer and 32-bit lane offsets
   auto stage_rows = [&](E* dst, const void* src, int heads, int head) __attribute__((always_inline)) {
-    const E* sg = static_cast<const E*>(src);
+    const E* sg = static_cast<const E*>(src) + ((int64_t)start * heads + head) * D;
     for (int idx = tid; idx < C * D / VE; idx += kGradBlock) {
       const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
       VLoad x;
 #pragma unroll
       for (int e = 0; e < VE; ++e) x[e] = to_e<E>(0.f);
-      if (r < len) x = *reinterpret_cast<const VLoad*>(sg + ((int64_t)(start + r) * heads + head) * D + d);
+      if (r < len) x = *reinterpret_cast<const VLoad*>(sg + r * heads * D + d);
       *reinterpret_cast<VLoad*>(&dst[r * KLD + d]) = x;
     }
   };
@@ -316,23 +322,17 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
       *reinterpret_cast<VLoad*>(&dst[r * KLD + d]) = *reinterpret_cast<const VLoad*>(src + r * D + d);
     }
   };
-  // operand fragments: rows (contraction along a row) and columns
-  // (contraction down a column) of LDS matrices, for 32-step s
+  // operand fragments of LDS matrices for 32-step s: along a row (the
+  // contraction runs along the row) or down a column
   auto frag_row = [&](const E* m, int ld, int row0, int s, int kext) __attribute__((always_inline)) {
     return load_frag<E>(m + (row0 + l16) * ld + 32 * s, quad, kext - 32 * s);
   };
-  auto frag_row32 = [&](const float* m, int ld, int row0, int s, int kext) __attribute__((always_inline)) {
-    const float* p = m + (row0 + l16) * ld + 32 * s;
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(p + 4 * quad);
-    const f32x4 hi = (kext - 32 * s > 16) ? *reinterpret_cast<const f32x4*>(p + 16 + 4 * quad) : zero4();
-    return acc_to_frag<E>(lo, hi);
-  };
-  auto frag_col = [&](const auto* m, int ld, int col0, int s, int kext) __attribute__((always_inline)) {
+  auto frag_col = [&](const E* m, int ld, int col0, int s, int kext) __attribute__((always_inline)) {
     Frag<E> f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int k = frag_k(s, quad, e);
-      f[e] = to_e<E>((k < kext) ? to_f(m[k * ld + col0 + l16]) : 0.f);
+      f[e] = (k < kext) ? m[k * ld + col0 + l16] : to_e<E>(0.f);
     }
     return f;
   };
@@ -380,11 +380,14 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     }
     __syncthreads();
 
-    // dO S0^T, U dS_L^T, -dU S0^T and <S0, dS_L>
+    // dO S0^T, U dS_L^T, -dU S0^T and <S0, dS_L>; the row terms of dg are
+    // summed over the wave's d-tiles before the lane reductions
     const E* scg = static_cast<const E*>(a.sc) + ch * D * D;
     const E* dsg = static_cast<const E*>(a.dsl) + ch * D * D;
-    f32x4 dW[TPW];
-    float fro = 0.f;
+    f32x4 dW[TPW], prow[CT];
+    float fro = 0.f, pk_all = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < CT; ++rt) prow[rt] = zero4();
 #pragma unroll
     for (int j = 0; j < DPW; ++j) {
       const int dt = wave + NW * j;
@@ -414,23 +417,34 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * rt + 4 * quad + i;
-          const float eq = aq[i] * sm.ea[r];
+          const float eq = aq[i] * sm.ea[r], ek = ak[i] * sm.ed[r];
           dQ[u][i] += eq;
-          dK[u][i] += ak[i] * sm.ed[r];
-          const float pq = sum16(eq * qv[i]);
-          const float pk = sum16(sm.ed[r] * ak[i] * kv[i]);
-          if (l16 == 0) {
-            atomicAdd(&sm.dg[r], pq - pk);
-            atomicAdd(&sm.sums[1], pk);
-          }
+          dK[u][i] += ek;
+          const float pk = ek * kv[i];
+          prow[rt][i] += eq * qv[i] - pk;
+          pk_all += pk;
         }
       }
       __builtin_amdgcn_sched_barrier(0);   // one d-tile's operands live at a time
     }
-    fro = sum_rows4(sum16(fro));
-    if (lane == 0) atomicAdd(&sm.sums[0], fro);
+    if (has_dt) {
+#pragma unroll
+      for (int rt = 0; rt < CT; ++rt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float s = sum16(prow[rt][i]);
+          if (l16 == 0) atomicAdd(&sm.dg[16 * rt + 4 * quad + i], s);
+        }
+      }
+      fro = sum_rows4(sum16(fro));
+      pk_all = sum_rows4(sum16(pk_all));
+      if (lane == 0) {
+        atomicAdd(&sm.sums[0], fro);
+        atomicAdd(&sm.sums[1], pk_all);
+      }
+    }
 
-    // dP = dO U^T: dP * P into dg, dPm = dP * Dincl into x1
+    // dP = dO U^T: dP * P into dg, dPm = dP * Dincl into x1 (input dtype)
     const Frag<E>* ptf = reinterpret_cast<const Frag<E>*>(a.pt) + ch * G::QK_FR * 64;
 #pragma unroll
     for (int j2 = 0; j2 < JPW; ++j2) {
@@ -457,7 +471,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
           if (l16 == 0) atomicAdd(&sm.dg[r], rs);
           colp += m2;
           const float gm = (j <= r && r < len) ? __expf(fminf(sm.g[r] - sm.g[j], 0.f)) : 0.f;
-          sm.x1[r * FLD + j] = acc[i] * gm;
+          sm.x1.e[r * ELD + j] = to_e<E>(acc[i] * gm);
         }
       }
       colp = sum_rows4(colp);
@@ -482,8 +496,8 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         // dQ += dPm K, dK += dPm^T Q
 #pragma unroll
         for (int s = 0; s < CKS; ++s) {
-          dQ[u] = mma(frag_row32(sm.x1, FLD, 16 * rt, s, C), kb[s], dQ[u]);
-          dK[u] = mma(frag_col(sm.x1, FLD, 16 * rt, s, C), qb[s], dK[u]);
+          dQ[u] = mma(frag_row(sm.x1.e, ELD, 16 * rt, s, C), kb[s], dQ[u]);
+          dK[u] = mma(frag_col(sm.x1.e, ELD, 16 * rt, s, C), qb[s], dK[u]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -491,7 +505,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     stage_rows(sm.u1.r1, a.v, a.h_v, hv);
     __syncthreads();                   // v rows and dW rows complete; x1 dead
 
-    // dT = (dU V^T) diag(b) + (dW K^T) diag(b ea) into x1
+    // dT = (dU V^T) diag(b) + (dW K^T) diag(b ea) into x1 (fp32)
 #pragma unroll
     for (int j2 = 0; j2 < JPW; ++j2) {
       const int it = wave + NW * j2;
@@ -513,7 +527,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
           a2 = mma(frag_row(sm.r2, KLD, 16 * rt, ks, D), kb[ks], a2);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.x1[(16 * rt + 4 * quad + e) * FLD + i] = a1[e] * bi + a2[e] * bgi;
+        for (int e = 0; e < 4; ++e) sm.x1.f[(16 * rt + 4 * quad + e) * FLD + i] = a1[e] * bi + a2[e] * bgi;
       }
     }
     __syncthreads();                   // x1 = dT complete; v rows dead
@@ -527,13 +541,14 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         f32x4 acc = zero4();
 #pragma unroll
         for (int mb = 0; mb < CT; ++mb)
-          acc = mma16_f32(&sm.x1[(16 * rt) * FLD + 16 * mb], FLD, 1, &sm.tt[(16 * mb) * TLD + 16 * it], TLD, 1, acc, lane);
+          acc = mma16_f32(&sm.x1.f[(16 * rt) * FLD + 16 * mb], FLD, 1, &sm.tt[(16 * mb) * TLD + 16 * it], TLD, 1, acc, lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) ys[(16 * rt + 4 * quad + e) * FLD + 16 * it + l16] = acc[e];
       }
     }
     __syncthreads();
-    // dA = -Tinv^T Y (strictly lower), K K^T; b and g terms of A; B into x1
+    // dA = -Tinv^T Y (strictly lower), K K^T; b and g terms of A; B is
+    // strictly lower, so B + B^T is written as B at (r, i) and at (i, r)
 #pragma unroll
     for (int j2 = 0; j2 < JPW; ++j2) {
       const int it = wave + NW * j2;
@@ -566,7 +581,12 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
             atomicAdd(&sm.dg[r], rdg);
           }
           colm += mb2;
-          sm.x1[r * FLD + i] = bm;
+          if (i < r) {
+            sm.x1.e[r * ELD + i] = to_e<E>(bm);
+            sm.x1.e[i * ELD + r] = to_e<E>(bm);
+          } else if (i == r) {
+            sm.x1.e[r * ELD + i] = to_e<E>(0.f);
+          }
         }
       }
       colm = sum_rows4(colm);
@@ -575,8 +595,11 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     __syncthreads();
     // dK += (B + B^T) K; dV = diag(b) Tinv^T dU and its b term (v read from
     // global); Tinv^T dW into dK and the b, g terms of W
-    E* dvg = static_cast<E*>(a.dv);
-    const E* vg = static_cast<const E*>(a.v);
+    E* dvg = static_cast<E*>(a.dv) + ((int64_t)start * a.h_v + hv) * D;
+    const E* vg = static_cast<const E*>(a.v) + ((int64_t)start * a.h_v + hv) * D;
+    f32x4 rdb_acc[CT], rdg_acc[CT];
+#pragma unroll
+    for (int rt = 0; rt < CT; ++rt) { rdb_acc[rt] = zero4(); rdg_acc[rt] = zero4(); }
 #pragma unroll
     for (int j = 0; j < DPW; ++j) {
       const int dt = wave + NW * j;
@@ -595,8 +618,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         f32x4 au = zero4(), aw = zero4();
 #pragma unroll
         for (int s = 0; s < CKS; ++s) {
-          dK[u] = mma(frag_row32(sm.x1, FLD, 16 * rt, s, C), kb[s], dK[u]);
-          dK[u] = mma(frag_col(sm.x1, FLD, 16 * rt, s, C), kb[s], dK[u]);
+          dK[u] = mma(frag_row(sm.x1.e, ELD, 16 * rt, s, C), kb[s], dK[u]);
           const Frag<E> ta = frag_row(sm.tt, TLD, 16 * rt, s, C);
           au = mma(ta, ub[s], au);
           aw = mma(ta, wb[s], aw);
@@ -605,20 +627,30 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * rt + 4 * quad + e;
-          const float br = sm.b[r], bgr = sm.b[r] * sm.ea[r];
-          const int64_t row = ((int64_t)(start + r) * a.h_v + hv) * D + d;
-          const float vv = (r < len) ? to_f(vg[row]) : 0.f;
-          if (r < len) dvg[row] = to_e<E>(br * au[e]);
+          const float bgr = sm.b[r] * sm.ea[r];
+          const int off = r * a.h_v * D + d;
+          const float vv = (r < len) ? to_f(vg[off]) : 0.f;
+          if (r < len) dvg[off] = to_e<E>(sm.b[r] * au[e]);
           dK[u][e] += bgr * aw[e];
-          const float rv = sum16(au[e] * vv);
-          const float rk = sum16(aw[e] * kv[e]);
-          if (l16 == 0) {
-            atomicAdd(&sm.db[r], rv + sm.ea[r] * rk);
-            atomicAdd(&sm.dg[r], bgr * rk);
-          }
+          const float rk = aw[e] * kv[e];
+          rdb_acc[rt][e] += au[e] * vv + sm.ea[r] * rk;
+          rdg_acc[rt][e] += bgr * rk;
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if (has_dt) {
+#pragma unroll
+      for (int rt = 0; rt < CT; ++rt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sb = sum16(rdb_acc[rt][e]), sg = sum16(rdg_acc[rt][e]);
+          if (l16 == 0) {
+            atomicAdd(&sm.db[16 * rt + 4 * quad + e], sb);
+            atomicAdd(&sm.dg[16 * rt + 4 * quad + e], sg);
+          }
+        }
+      }
     }
     __syncthreads();
     if (tid == 0 && len > 0) sm.dg[len - 1] += gl * sm.sums[0] + sm.sums[1];
@@ -631,8 +663,8 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     }
   }
 
-  E* dqg = static_cast<E*>(a.dq);
-  E* dkg = static_cast<E*>(a.dk);
+  E* dqg = static_cast<E*>(a.dq) + ((int64_t)start * a.h_qk + hq) * D;
+  E* dkg = static_cast<E*>(a.dk) + ((int64_t)start * a.h_qk + hq) * D;
 #pragma unroll
   for (int j = 0; j < DPW; ++j) {
     const int dt = wave + NW * j;
@@ -644,7 +676,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rt + 4 * quad + e;
         if (r < len) {
-          const int64_t o = ((int64_t)(start + r) * a.h_qk + hq) * D + 16 * dt + l16;
+          const int o = r * a.h_qk * D + 16 * dt + l16;
           dqg[o] = to_e<E>(dQ[u][e]);
           dkg[o] = to_e<E>(dK[u][e]);
         }

@@ -246,31 +246,29 @@ __global__ __launch_bounds__(kBlock) void gdn_kb_dstate(const PrefillArgs a) {
 // that contract over d, K^T and Q^T fragments (row d, k = token) for those
 // that contract over tokens and for their elements, since fragment
 // (dt, rt/2) of K^T holds, at element i + 4 (rt & 1), exactly the element
-// (16 rt + 4 quad + i, 16 dt + l16) of a C x D accumulator tile. The
-// C x C x C products of dA run in fp32 (v_mfma_f32_16x16x4_f32), every other
-// product on the input dtype's MFMA with fp32 accumulation. Row and column
-// sums of the per-element terms use DPP and lane-row swaps, then LDS
-// atomics.
+// (16 rt + 4 quad + i, 16 dt + l16) of a C x D accumulator tile. Every
+// product runs on the input dtype's MFMA with fp32 accumulation; the C x C
+// matrices that only feed products (dP * Dincl, dT, Y, B + B^T) are held in
+// the input dtype. Row and column sums of the per-element terms use DPP and
+// lane-row swaps, then LDS atomics.
 // --------------------------------------------------------------------------
 constexpr int kGradBlock = 256;
 
 template <typename E, int D, int C>
 struct GradSmem {
   static constexpr int KLD = D + 8;    // row stride of the staged D-wide rows
-  static constexpr int FLD = C + 4;    // row stride of the fp32 C x C scratch
-  static constexpr int ELD = C + 8;    // row stride of the same scratch holding input-dtype matrices
+  static constexpr int ELD = C + 8;    // row stride of the C x C matrices
   static constexpr int TLD = C + 8;    // row stride of Tinv^T
   union {
     E r1[C * KLD];                     // dL/do rows, then v rows
-    float y[C * FLD];                  // then Y = dT Tinv^T (fp32)
+    E y[C * ELD];                      // then Y = dT Tinv^T
   } __attribute__((aligned(16))) u1;
   E r2[C * KLD] __attribute__((aligned(16)));   // U rows, then dW rows
   E r3[C * KLD] __attribute__((aligned(16)));   // dU rows
   E tt[C * TLD] __attribute__((aligned(16)));   // Tinv^T rows
-  union {
-    float f[C * FLD];                  // dT (fp32)
-    E e[C * ELD];                      // dP * Dincl, then B + B^T (MFMA operands only)
-  } __attribute__((aligned(16))) x1;
+  // dP * Dincl, then dT, then B + B^T (each only an MFMA operand, so held
+  // in the input dtype)
+  E x1[C * ELD] __attribute__((aligned(16)));
   float g[C], b[C], ea[C], ed[C], dg[C], db[C];
   float sums[2];                       // <S0, dS_L>; sum of the state-term row factors
 };
@@ -280,7 +278,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
   using G = Cfg<E, D, C>;
   using SM = GradSmem<E, D, C>;
   constexpr int DT = G::DT, CT = G::CT, DKS = G::DKS, CKS = G::CKS;
-  constexpr int KLD = SM::KLD, FLD = SM::FLD, ELD = SM::ELD, TLD = SM::TLD;
+  constexpr int KLD = SM::KLD, ELD = SM::ELD, TLD = SM::TLD;
   constexpr int NW = kGradBlock / 64;
   // wave w owns the C x D tiles of d-tiles w, w + NW, ... (all row tiles)
   // and the C x C tiles of column tiles w, w + NW, ...: the operand of a
@@ -290,7 +288,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
   constexpr int VE = 16 / (int)sizeof(E);
   typedef E VLoad __attribute__((ext_vector_type(VE)));
   __shared__ SM sm;
-  float* ys = sm.u1.y;
+  E* ys = sm.u1.y;
   const int64_t c = blockIdx.x;
   const int hq = blockIdx.y;
   const int4 tab = reinterpret_cast<const int4*>(a.chunk_table)[c];
@@ -471,7 +469,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
           if (l16 == 0) atomicAdd(&sm.dg[r], rs);
           colp += m2;
           const float gm = (j <= r && r < len) ? __expf(fminf(sm.g[r] - sm.g[j], 0.f)) : 0.f;
-          sm.x1.e[r * ELD + j] = to_e<E>(acc[i] * gm);
+          sm.x1[r * ELD + j] = to_e<E>(acc[i] * gm);
         }
       }
       colp = sum_rows4(colp);
@@ -496,8 +494,8 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         // dQ += dPm K, dK += dPm^T Q
 #pragma unroll
         for (int s = 0; s < CKS; ++s) {
-          dQ[u] = mma(frag_row(sm.x1.e, ELD, 16 * rt, s, C), kb[s], dQ[u]);
-          dK[u] = mma(frag_col(sm.x1.e, ELD, 16 * rt, s, C), qb[s], dK[u]);
+          dQ[u] = mma(frag_row(sm.x1, ELD, 16 * rt, s, C), kb[s], dQ[u]);
+          dK[u] = mma(frag_col(sm.x1, ELD, 16 * rt, s, C), qb[s], dK[u]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -505,7 +503,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     stage_rows(sm.u1.r1, a.v, a.h_v, hv);
     __syncthreads();                   // v rows and dW rows complete; x1 dead
 
-    // dT = (dU V^T) diag(b) + (dW K^T) diag(b ea) into x1 (fp32)
+    // dT = (dU V^T) diag(b) + (dW K^T) diag(b ea) into x1
 #pragma unroll
     for (int j2 = 0; j2 < JPW; ++j2) {
       const int it = wave + NW * j2;
@@ -527,23 +525,26 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
           a2 = mma(frag_row(sm.r2, KLD, 16 * rt, ks, D), kb[ks], a2);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.x1.f[(16 * rt + 4 * quad + e) * FLD + i] = a1[e] * bi + a2[e] * bgi;
+        for (int e = 0; e < 4; ++e) sm.x1[(16 * rt + 4 * quad + e) * ELD + i] = to_e<E>(a1[e] * bi + a2[e] * bgi);
       }
     }
     __syncthreads();                   // x1 = dT complete; v rows dead
-    // Y = dT Tinv^T (fp32) over the v rows' buffer
+    // Y = dT Tinv^T over the v rows' buffer; Tinv^T (k = m, column i) is
+    // read down tt's columns, once per column tile
 #pragma unroll
     for (int j2 = 0; j2 < JPW; ++j2) {
       const int it = wave + NW * j2;
       if (it >= CT) continue;
+      Frag<E> tb[CKS];
+#pragma unroll
+      for (int s = 0; s < CKS; ++s) tb[s] = frag_col(sm.tt, TLD, 16 * it, s, C);
 #pragma unroll
       for (int rt = 0; rt < CT; ++rt) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int mb = 0; mb < CT; ++mb)
-          acc = mma16_f32(&sm.x1.f[(16 * rt) * FLD + 16 * mb], FLD, 1, &sm.tt[(16 * mb) * TLD + 16 * it], TLD, 1, acc, lane);
+        for (int s = 0; s < CKS; ++s) acc = mma(frag_row(sm.x1, ELD, 16 * rt, s, C), tb[s], acc);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ys[(16 * rt + 4 * quad + e) * FLD + 16 * it + l16] = acc[e];
+        for (int e = 0; e < 4; ++e) ys[(16 * rt + 4 * quad + e) * ELD + 16 * it + l16] = to_e<E>(acc[e]);
       }
     }
     __syncthreads();
@@ -553,17 +554,18 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     for (int j2 = 0; j2 < JPW; ++j2) {
       const int it = wave + NW * j2;
       if (it >= CT) continue;
-      Frag<E> kb[DKS];
+      Frag<E> kb[DKS], yb[CKS];
 #pragma unroll
       for (int ks = 0; ks < DKS; ++ks) kb[ks] = kff[(it * DKS + ks) * 64 + lane];
+#pragma unroll
+      for (int s = 0; s < CKS; ++s) yb[s] = frag_col(ys, ELD, 16 * it, s, C);
       const int i = 16 * it + l16;
       float colm = 0.f;
 #pragma unroll
       for (int rt = 0; rt < CT; ++rt) {
         f32x4 acc = zero4(), kk = zero4();
 #pragma unroll
-        for (int mb = 0; mb < CT; ++mb)
-          acc = mma16_f32(&sm.tt[(16 * rt) * TLD + 16 * mb], TLD, 1, &ys[(16 * mb) * FLD + 16 * it], FLD, 1, acc, lane);
+        for (int s = 0; s < CKS; ++s) acc = mma(frag_row(sm.tt, TLD, 16 * rt, s, C), yb[s], acc);
 #pragma unroll
         for (int ks = 0; ks < DKS; ++ks) kk = mma(kff[(rt * DKS + ks) * 64 + lane], kb[ks], kk);
 #pragma unroll
@@ -582,10 +584,10 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
           }
           colm += mb2;
           if (i < r) {
-            sm.x1.e[r * ELD + i] = to_e<E>(bm);
-            sm.x1.e[i * ELD + r] = to_e<E>(bm);
+            sm.x1[r * ELD + i] = to_e<E>(bm);
+            sm.x1[i * ELD + r] = to_e<E>(bm);
           } else if (i == r) {
-            sm.x1.e[r * ELD + i] = to_e<E>(0.f);
+            sm.x1[r * ELD + i] = to_e<E>(0.f);
           }
         }
       }
@@ -618,7 +620,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         f32x4 au = zero4(), aw = zero4();
 #pragma unroll
         for (int s = 0; s < CKS; ++s) {
-          dK[u] = mma(frag_row(sm.x1.e, ELD, 16 * rt, s, C), kb[s], dK[u]);
+          dK[u] = mma(frag_row(sm.x1, ELD, 16 * rt, s, C), kb[s], dK[u]);
           const Frag<E> ta = frag_row(sm.tt, TLD, 16 * rt, s, C);
           au = mma(ta, ub[s], au);
           aw = mma(ta, wb[s], aw);

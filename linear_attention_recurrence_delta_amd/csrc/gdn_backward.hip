@@ -49,6 +49,8 @@ namespace {
 // and dU (rounded to the input dtype, as the gradient kernel's products use
 // them); after the first chunk dS is dL/dS0 of the sequence.
 // --------------------------------------------------------------------------
+constexpr int kDScanBlock = 256;
+
 template <typename E, int D, int C>
 struct DScanSmem {
   using G = Cfg<E, D, C>;
@@ -61,10 +63,10 @@ struct DScanSmem {
 };
 
 template <typename E, int D, int C>
-__global__ __launch_bounds__(kBlock) void gdn_kb_dstate(const PrefillArgs a) {
+__global__ __launch_bounds__(kDScanBlock) void gdn_kb_dstate(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   constexpr int DT = G::DT, CT = G::CT, DKS = G::DKS, CKS = G::CKS, NS = G::NS, BV = G::BV;
-  constexpr int NLD = kBlock / 64 - NS;
+  constexpr int NLD = kDScanBlock / 64 - NS;
   constexpr int FB = (int)sizeof(Frag<E>) * 64;
   constexpr int ESZ = (int)sizeof(E);
   __shared__ DScanSmem<E, D, C> sm;
@@ -693,7 +695,7 @@ hipError_t launch_backward_t(const PrefillArgs& a, hipStream_t s, int first, int
   for (int stage = first; stage <= last; ++stage) {
     switch (stage) {
       case 4:
-        gdn_kb_dstate<E, D, C><<<dim3((unsigned)(a.num_seqs * a.h_v * G::NCB)), dim3(kBlock), 0, s>>>(a);
+        gdn_kb_dstate<E, D, C><<<dim3((unsigned)(a.num_seqs * a.h_v * G::NCB)), dim3(kDScanBlock), 0, s>>>(a);
         break;
       case 5:
         gdn_kb_grad<E, D, C><<<dim3((unsigned)a.max_chunks, (unsigned)a.h_qk), dim3(kGradBlock), 0, s>>>(a);

@@ -23,7 +23,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 # kernel -> source file that defines it
 SOURCES = {"gdn_k1_chunk_prep": "gdn_prefill.hip", "gdn_k2_inverse_w": "gdn_prefill.hip",
-           "gdn_k3_scan": "gdn_prefill.hip", "gdn_kd_decode_step": "gdn_decode.hip"}
+           "gdn_k3_scan": "gdn_prefill.hip", "gdn_kd_decode_step": "gdn_decode.hip",
+           "gdn_kd_decode_multi": "gdn_decode.hip", "gdn_kb_dstate": "gdn_backward.hip",
+           "gdn_kb_grad": "gdn_backward.hip"}
+
+
+def source_of(kernel):
+    """Source file of a kernel summary name (instance labels ignored)."""
+    return SOURCES.get(kernel.split(" [")[0])
 
 
 # compile-time switches of each kernel, in template-argument order (the bool
@@ -87,16 +94,38 @@ def traffic(fetch, write, copy_fetch, copy_write, copy_bytes):
     out = {"_calibration": {"copy_bytes_each_way": copy_bytes, "fetch_scale": round(fsc, 4),
                             "write_scale": round(wsc, 4)}}
     for k in sorted(set(f) & set(w)):
-        if k not in SOURCES:
+        if source_of(k) is None:
             continue
-        src = os.path.join(HERE, "csrc", SOURCES[k])
+        src = os.path.join(HERE, "csrc", source_of(k))
         with open(src, "rb") as fh:
             sha = hashlib.sha256(fh.read()).hexdigest()
         fb, wb = f[k] * 1024.0 * fsc, w[k] * 1024.0 * wsc
-        out[k] = {"source": SOURCES[k], "source_sha256": sha, "fetch_kib_raw": f[k],
+        out[k] = {"source": source_of(k), "source_sha256": sha, "fetch_kib_raw": f[k],
                   "write_kib_raw": w[k], "fetch_bytes": round(fb), "write_bytes": round(wb),
                   "bytes_per_launch": round(fb + wb)}
     return out
+
+
+def traffic_table(traffic_path, bench_path):
+    """Markdown table: measured HBM bytes per launch (traffic.json) beside the
+    algorithmic bytes bench.py counts (its achieved GB/s times the launch's
+    mean time), for every kernel in both."""
+    with open(traffic_path) as f:
+        tr = json.load(f)
+    with open(bench_path) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    kernels = dict(line.get("kernels", {}))
+    kernels.update(line.get("backward", {}).get("kernels", {}))
+    rows = ["| kernel | fetch (GB) | write (GB) | measured total (GB) | algorithmic (GB) | ratio |",
+            "|---|---|---|---|---|---|"]
+    for k, rec in kernels.items():
+        if k not in tr or rec.get("unit") != "GB/s":
+            continue
+        alg = rec["achieved"] * 1e9 * rec["ms"] * 1e-3
+        m = tr[k]
+        rows.append(f"| {k} | {m['fetch_bytes'] / 1e9:.3f} | {m['write_bytes'] / 1e9:.3f} | "
+                    f"{m['bytes_per_launch'] / 1e9:.3f} | {alg / 1e9:.3f} | {m['bytes_per_launch'] / alg:.2f} |")
+    return "\n".join(rows)
 
 
 def main():
@@ -111,7 +140,13 @@ def main():
         t.add_argument(a, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--out")
+    tt = sub.add_parser("traffic-table")
+    tt.add_argument("traffic_json")
+    tt.add_argument("bench_json")
     args = ap.parse_args()
+    if args.cmd == "traffic-table":
+        print(traffic_table(args.traffic_json, args.bench_json))
+        return
     if args.cmd == "stats":
         print(f"# {args.title}\n\nCommand (GPU box, repo root):\n\n    {args.command}\n")
         print(kernel_stats(args.csv))

@@ -303,23 +303,46 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
   const bool has_dt = wave < DT;       // the wave owns at least one d-tile
 
   // rows [0, C) of a [T][H][D] input into LDS (zero past the chunk end);
-  // a uniform base pointer and 32-bit lane offsets
+  // a uniform base pointer and 32-bit lane offsets. Every load is issued
+  // unconditionally (rows past the end read the last row, then select
+  // zero), so all of a thread's loads are in flight before the first wait.
+  constexpr int SPT = (C * D / VE + kGradBlock - 1) / kGradBlock;   // 16-byte loads per thread
   auto stage_rows = [&](E* dst, const void* src, int heads, int head) __attribute__((always_inline)) {
     const E* sg = static_cast<const E*>(src) + ((int64_t)start * heads + head) * D;
-    for (int idx = tid; idx < C * D / VE; idx += kGradBlock) {
-      const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
-      VLoad x;
+    VLoad x[SPT];
 #pragma unroll
-      for (int e = 0; e < VE; ++e) x[e] = to_e<E>(0.f);
-      if (r < len) x = *reinterpret_cast<const VLoad*>(sg + r * heads * D + d);
-      *reinterpret_cast<VLoad*>(&dst[r * KLD + d]) = x;
+    for (int p = 0; p < SPT; ++p) {
+      const int idx = tid + p * kGradBlock;
+      const int r = min(idx / (D / VE), len - 1), d = (idx % (D / VE)) * VE;
+      if (idx < C * D / VE) x[p] = *reinterpret_cast<const VLoad*>(sg + r * heads * D + d);
+    }
+#pragma unroll
+    for (int p = 0; p < SPT; ++p) {
+      const int idx = tid + p * kGradBlock;
+      const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
+      if (idx < C * D / VE) {
+        VLoad v = x[p];
+        if (r >= len) {
+#pragma unroll
+          for (int e = 0; e < VE; ++e) v[e] = to_e<E>(0.f);
+        }
+        *reinterpret_cast<VLoad*>(&dst[r * KLD + d]) = v;
+      }
     }
   };
   // rows of a [C][D] workspace matrix into LDS
   auto stage_ws = [&](E* dst, const E* src) __attribute__((always_inline)) {
-    for (int idx = tid; idx < C * D / VE; idx += kGradBlock) {
+    VLoad x[SPT];
+#pragma unroll
+    for (int p = 0; p < SPT; ++p) {
+      const int idx = tid + p * kGradBlock;
+      if (idx < C * D / VE) x[p] = *reinterpret_cast<const VLoad*>(src + idx * VE);
+    }
+#pragma unroll
+    for (int p = 0; p < SPT; ++p) {
+      const int idx = tid + p * kGradBlock;
       const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
-      *reinterpret_cast<VLoad*>(&dst[r * KLD + d]) = *reinterpret_cast<const VLoad*>(src + r * D + d);
+      if (idx < C * D / VE) *reinterpret_cast<VLoad*>(&dst[r * KLD + d]) = x[p];
     }
   };
   // operand fragments of LDS matrices for 32-step s: along a row (the
@@ -375,8 +398,20 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     stage_ws(sm.r2, static_cast<const E*>(a.ub) + ch * C * D);
     stage_ws(sm.r3, static_cast<const E*>(a.du) + ch * C * D);
     {
+      // Tinv^T rows, 16-byte loads
+      constexpr int TPT = (C * C / VE + kGradBlock - 1) / kGradBlock;
       const E* tg = static_cast<const E*>(a.tt) + ch * C * C;
-      for (int idx = tid; idx < C * C; idx += kGradBlock) sm.tt[(idx / C) * TLD + idx % C] = tg[idx];
+      VLoad x[TPT];
+#pragma unroll
+      for (int p = 0; p < TPT; ++p) {
+        const int idx = tid + p * kGradBlock;
+        if (idx < C * C / VE) x[p] = *reinterpret_cast<const VLoad*>(tg + idx * VE);
+      }
+#pragma unroll
+      for (int p = 0; p < TPT; ++p) {
+        const int idx = tid + p * kGradBlock;
+        if (idx < C * C / VE) *reinterpret_cast<VLoad*>(&sm.tt[(idx * VE / C) * TLD + (idx * VE) % C]) = x[p];
+      }
     }
     __syncthreads();
 
@@ -633,7 +668,8 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
           const int r = 16 * rt + 4 * quad + e;
           const float bgr = sm.b[r] * sm.ea[r];
           const int off = r * a.h_v * D + d;
-          const float vv = (r < len) ? to_f(vg[off]) : 0.f;
+          const float vl = to_f(vg[min(r, len - 1) * a.h_v * D + d]);    // issued unconditionally
+          const float vv = (r < len) ? vl : 0.f;
           if (r < len) dvg[off] = to_e<E>(sm.b[r] * au[e]);
           dK[u][e] += bgr * aw[e];
           const float rk = aw[e] * kv[e];

@@ -60,6 +60,8 @@ struct DScanSmem {
   Frag<E> wt[2][G::KT_FR * 64];      // W^T fragments (row d, k = token r)
   E dor[2][C * G::BV];               // dL/do rows, this block's columns
   float dtab[2][2 * C + 4] __attribute__((aligned(16)));
+  // per scan wave: staging for the row-major stores of dS_L and dU
+  E stage[G::NS][stage_elems<E>()] __attribute__((aligned(16)));
 };
 
 template <typename E, int D, int C>
@@ -132,12 +134,8 @@ __global__ __launch_bounds__(kDScanBlock) void gdn_kb_dstate(const PrefillArgs a
   auto dscan_chunk = [&](int c) __attribute__((always_inline)) {
     const int par = c & 1;
     // dS is dL/d(state at chunk c's end)
-    E* dslg = static_cast<E*>(a.dsl) + ((int64_t)c * a.h_v + hv) * D * D + col0 + 16 * slice + l16;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dslg[(16 * dt + 4 * quad + i) * D] = to_e<E>(dS[dt][i]);
-    }
+    store_tiles_rows<E, DT>(dS, sm.stage[slice],
+                            static_cast<E*>(a.dsl) + ((int64_t)c * a.h_v + hv) * D * D + col0 + 16 * slice, D, lane);
     Frag<E> dSf[DKS];
 #pragma unroll
     for (int ks = 0; ks < DKS; ++ks) dSf[ks] = acc_to_frag<E>(dS[2 * ks], (2 * ks + 1 < DT) ? dS[2 * ks + 1] : zero4());
@@ -171,12 +169,8 @@ __global__ __launch_bounds__(kDScanBlock) void gdn_kb_dstate(const PrefillArgs a
       for (int s = 0; s < CKS; ++s)
         if (32 * s + 31 >= 16 * t) dU[t] = mma(sm.pt[par][(t * CKS + s) * 64 + lane], dOf[s], dU[t]);
     }
-    E* dug = static_cast<E*>(a.du) + ((int64_t)c * a.h_v + hv) * C * D + col0 + 16 * slice + l16;
-#pragma unroll
-    for (int t = 0; t < CT; ++t) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dug[(16 * t + 4 * quad + i) * D] = to_e<E>(dU[t][i]);
-    }
+    store_tiles_rows<E, CT>(dU, sm.stage[slice],
+                            static_cast<E*>(a.du) + ((int64_t)c * a.h_v + hv) * C * D + col0 + 16 * slice, D, lane);
     Frag<E> nUf[CKS];
 #pragma unroll
     for (int s = 0; s < CKS; ++s) nUf[s] = acc_to_frag<E>(-dU[2 * s], (2 * s + 1 < CT) ? -dU[2 * s + 1] : zero4());

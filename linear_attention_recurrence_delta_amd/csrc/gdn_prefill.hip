@@ -722,6 +722,10 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       __builtin_amdgcn_global_load_lds(line_addr(x, t), (lds_ptr_t)sm.touch[wave], 4, 0, 0);
   };
 
+  // the saving form stages its row-major stores in the Q and P fragment
+  // buffers, which it does not use
+  static_assert(!SV || NS * stage_elems<E>() * (int)sizeof(E) <=
+                           (int)(sizeof(sm.qf) + sizeof(sm.pf)), "staging fits the unused buffers");
   // scan waves: the slice's D x 16 state columns in accumulator tiles
   f32x4 S[DT];
 
@@ -729,13 +733,10 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     const int start = chunk_start(c), len = chunk_len(c), par = c & 1;
     if constexpr (SV) {
       // backward pass: the state at the chunk's start, rounded as the
-      // products below use it
-      E* scg = static_cast<E*>(a.sc) + ((int64_t)c * a.h_v + hv) * D * D + col0 + 16 * slice + l16;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) scg[(16 * dt + 4 * quad + i) * D] = to_e<E>(S[dt][i]);
-      }
+      // products below use it; row-major through the (here unused) Q
+      // fragment buffers
+      store_tiles_rows<E, DT>(S, reinterpret_cast<E*>(sm.qf) + slice * stage_elems<E>(),
+                              static_cast<E*>(a.sc) + ((int64_t)c * a.h_v + hv) * D * D + col0 + 16 * slice, D, lane);
     }
     Frag<E> Sf[DKS];
 #pragma unroll
@@ -792,12 +793,8 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     for (int ks = 0; ks < CKS; ++ks) Uk[ks] = acc_to_frag<E>(U[2 * ks], (2 * ks + 1 < CT) ? U[2 * ks + 1] : zero4());
     if constexpr (SV) {
       // backward pass: the chunk's U rows, rounded as the products use them
-      E* ubg = static_cast<E*>(a.ub) + ((int64_t)c * a.h_v + hv) * C * D + col0 + 16 * slice + l16;
-#pragma unroll
-      for (int t = 0; t < CT; ++t) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ubg[(16 * t + 4 * quad + i) * D] = to_e<E>(U[t][i]);
-      }
+      store_tiles_rows<E, CT>(U, reinterpret_cast<E*>(sm.qf) + slice * stage_elems<E>(),
+                              static_cast<E*>(a.ub) + ((int64_t)c * a.h_v + hv) * C * D + col0 + 16 * slice, D, lane);
     }
     // decayed rows exp(g_L - g_r) U_r
 #pragma unroll

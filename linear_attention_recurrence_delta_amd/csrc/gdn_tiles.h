@@ -73,4 +73,43 @@ __device__ __forceinline__ void copy_1k(const char* src, char* dst, int bytes, i
 }
 
 
+// Stores NT 16 x 16 fp32 accumulator tiles of one wave (tile t holds rows
+// 16 t .. 16 t + 15 and, in lane l, rows 16 t + 4 (l / 16) + i of column
+// l % 16) to a row-major matrix g (row stride ld elements), rounded to E,
+// through a wave-private LDS area of stage_elems<E>() elements, up to four
+// tiles at a time: lanes write their elements, then read back 16-byte row
+// segments, so the global writes are 16-byte stores (two or four lanes per
+// 16-column row segment) instead of one 2- or 4-byte store per element. The
+// area may be reused once the call returns.
+template <typename E> constexpr int stage_elems() { return 64 * (16 + 16 / (int)sizeof(E)); }
+
+template <typename E, int NT>
+__device__ __forceinline__ void store_tiles_rows(const f32x4 (&acc)[NT], E* area, E* g, int ld, int lane) {
+  constexpr int VE = 16 / (int)sizeof(E);     // elements per 16 bytes
+  constexpr int SLD = 16 + VE;                // staging row stride (rows stay 16-byte aligned)
+  constexpr int LPR = 16 / VE;                // lanes per 16-column row segment
+  constexpr int RPI = 64 / LPR;               // rows per store instruction
+  constexpr int NG = NT < 4 ? NT : 4;         // tiles per staging round
+  static_assert(NT % NG == 0, "whole staging rounds");
+  typedef E Vec __attribute__((ext_vector_type(VE)));
+  const int q = lane >> 4, col = lane & 15;
+#pragma unroll
+  for (int t0 = 0; t0 < NT; t0 += NG) {
+#pragma unroll
+    for (int t = 0; t < NG; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) area[(16 * t + 4 * q + i) * SLD + col] = to_e<E>(acc[t0 + t][i]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int p = 0; p < (NG * 16 + RPI - 1) / RPI; ++p) {
+      const int row = lane / LPR + RPI * p, c = (lane % LPR) * VE;
+      if (NG * 16 % RPI == 0 || row < NG * 16) {
+        const Vec v = *reinterpret_cast<const Vec*>(&area[row * SLD + c]);
+        *reinterpret_cast<Vec*>(&g[(int64_t)(16 * t0 + row) * ld + c]) = v;
+      }
+    }
+  }
+}
+
 }  // namespace gdn

@@ -45,11 +45,14 @@ namespace {
 // columns); the NS scan waves hold dS for their 16-column slices in MFMA
 // accumulators and walk the chunks from last to first; the other waves
 // copy chunk c-1's operands into the idle LDS buffer (direct global-to-LDS
-// loads) while chunk c is processed. Per chunk the scan waves store dS_L
+// loads) while chunk c is processed. Per chunk the scan waves leave dS_L
 // and dU (rounded to the input dtype, as the gradient kernel's products use
-// them); after the first chunk dS is dL/dS0 of the sequence.
+// them) in an LDS staging area, double-buffered by chunk parity, and store
+// waves write the previous chunk's as 16-byte row segments after each
+// barrier, so that no wave waits for those stores. After the first chunk
+// dS is dL/dS0 of the sequence.
 // --------------------------------------------------------------------------
-constexpr int kDScanBlock = 256;
+constexpr int kDScanBlock = 384;
 
 template <typename E, int D, int C>
 struct DScanSmem {
@@ -60,17 +63,20 @@ struct DScanSmem {
   Frag<E> wt[2][G::KT_FR * 64];      // W^T fragments (row d, k = token r)
   E dor[2][C * G::BV];               // dL/do rows, this block's columns
   float dtab[2][2 * C + 4] __attribute__((aligned(16)));
-  // per scan wave: staging for the row-major stores of dS_L and dU
-  E stage[G::NS][stage_elems<E>()] __attribute__((aligned(16)));
+  // per chunk parity and scan wave: dS_L (D rows) then dU (C rows) of the
+  // wave's 16 columns, row-major with stride 16 + VE, for the loaders' stores
+  E stage[2][G::NS][(D + C) * (16 + 16 / sizeof(E))] __attribute__((aligned(16)));
 };
 
 template <typename E, int D, int C>
 __global__ __launch_bounds__(kDScanBlock) void gdn_kb_dstate(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   constexpr int DT = G::DT, CT = G::CT, DKS = G::DKS, CKS = G::CKS, NS = G::NS, BV = G::BV;
-  constexpr int NLD = kDScanBlock / 64 - NS;
+  constexpr int NLD = kDScanBlock / 64 - 2 * NS;          // loader waves (then NS store waves)
   constexpr int FB = (int)sizeof(Frag<E>) * 64;
   constexpr int ESZ = (int)sizeof(E);
+  constexpr int VE = 16 / ESZ, SLD = 16 + VE;          // staging: 16-byte segments, row stride
+  typedef E Vec __attribute__((ext_vector_type(VE)));
   __shared__ DScanSmem<E, D, C> sm;
   const int tid = threadIdx.x, lane = tid & 63, quad = lane >> 4, l16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -84,8 +90,8 @@ __global__ __launch_bounds__(kDScanBlock) void gdn_kb_dstate(const PrefillArgs a
   const int seq_end = a.cu_seqlens ? a.cu_seqlens[n + 1] : (int)a.total_tokens;
   auto chunk_start = [&](int x) { return seq_start + (x - c0) * C; };
   auto chunk_len = [&](int x) { return min(C, seq_end - chunk_start(x)); };
-  const bool is_scan = wave < NS;
-  const int slice = wave, lw = wave - NS;
+  const bool is_scan = wave < NS, is_loader = !is_scan && wave < NS + NLD;
+  const int slice = wave, lw = wave - NS, sw = wave - NS - NLD;
   const int col0 = cb * BV;
   const int64_t state_base = (n * a.h_v + hv) * D * D;
 
@@ -130,12 +136,34 @@ __global__ __launch_bounds__(kDScanBlock) void gdn_kb_dstate(const PrefillArgs a
     }
   };
 
+  // store waves: chunk x's staged dS_L and dU rows (all slices) to the
+  // row-major workspace matrices, 16-byte stores; nothing in the kernel
+  // reads them back, so no wave waits for them
+  auto store_staged = [&](int x) __attribute__((always_inline)) {
+    if (x < c0 || x >= c1) return;
+    constexpr int SEG = NS * (D + C) * (16 / VE);      // 16-byte segments per chunk
+    E* dslg = static_cast<E*>(a.dsl) + ((int64_t)x * a.h_v + hv) * D * D + col0;
+    E* dug = static_cast<E*>(a.du) + ((int64_t)x * a.h_v + hv) * C * D + col0;
+    for (int sgi = 64 * sw + lane; sgi < SEG; sgi += 64 * NS) {
+      const int sl = sgi / ((D + C) * (16 / VE)), rem = sgi % ((D + C) * (16 / VE));
+      const int row = rem / (16 / VE), cc = (rem % (16 / VE)) * VE;
+      const Vec v = *reinterpret_cast<const Vec*>(&sm.stage[x & 1][sl][row * SLD + cc]);
+      if (row < D) *reinterpret_cast<Vec*>(&dslg[row * D + 16 * sl + cc]) = v;
+      else *reinterpret_cast<Vec*>(&dug[(row - D) * D + 16 * sl + cc]) = v;
+    }
+  };
+
   f32x4 dS[DT];
   auto dscan_chunk = [&](int c) __attribute__((always_inline)) {
     const int par = c & 1;
-    // dS is dL/d(state at chunk c's end)
-    store_tiles_rows<E, DT>(dS, sm.stage[slice],
-                            static_cast<E*>(a.dsl) + ((int64_t)c * a.h_v + hv) * D * D + col0 + 16 * slice, D, lane);
+    // dS is dL/d(state at chunk c's end); it and dU go to the staging area,
+    // which the loaders store after the barrier
+    E* stg = sm.stage[par][slice];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) stg[(16 * dt + 4 * quad + i) * SLD + l16] = to_e<E>(dS[dt][i]);
+    }
     Frag<E> dSf[DKS];
 #pragma unroll
     for (int ks = 0; ks < DKS; ++ks) dSf[ks] = acc_to_frag<E>(dS[2 * ks], (2 * ks + 1 < DT) ? dS[2 * ks + 1] : zero4());
@@ -169,8 +197,11 @@ __global__ __launch_bounds__(kDScanBlock) void gdn_kb_dstate(const PrefillArgs a
       for (int s = 0; s < CKS; ++s)
         if (32 * s + 31 >= 16 * t) dU[t] = mma(sm.pt[par][(t * CKS + s) * 64 + lane], dOf[s], dU[t]);
     }
-    store_tiles_rows<E, CT>(dU, sm.stage[slice],
-                            static_cast<E*>(a.du) + ((int64_t)c * a.h_v + hv) * C * D + col0 + 16 * slice, D, lane);
+#pragma unroll
+    for (int t = 0; t < CT; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) stg[(D + 16 * t + 4 * quad + i) * SLD + l16] = to_e<E>(dU[t][i]);
+    }
     Frag<E> nUf[CKS];
 #pragma unroll
     for (int s = 0; s < CKS; ++s) nUf[s] = acc_to_frag<E>(-dU[2 * s], (2 * s + 1 < CT) ? -dU[2 * s + 1] : zero4());
@@ -210,7 +241,7 @@ __global__ __launch_bounds__(kDScanBlock) void gdn_kb_dstate(const PrefillArgs a
           for (int i = 0; i < 4; ++i) a.d_init[state_index(dt, i)] = dS[dt][i];
         }
       }
-    } else {
+    } else if (is_loader) {
       copy_chunk(c1 - 1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
@@ -219,6 +250,13 @@ __global__ __launch_bounds__(kDScanBlock) void gdn_kb_dstate(const PrefillArgs a
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
       }
+    } else {
+      lds_barrier();
+      for (int c = c1 - 1; c >= c0; --c) {
+        store_staged(c + 1);
+        lds_barrier();
+      }
+      store_staged(c0);
     }
   } else if (is_scan && a.d_init) {
     // empty sequence: dL/dS0 is dL/d(final state)

@@ -85,7 +85,31 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
   if (tid == 0) { sm.hit[0] = -1; sm.hit[1] = 0; }
   __syncthreads();
   int carry = 0;
-  for (int64_t base = 0; base < a.num_seqs; base += kBlock) {
+  if (a.num_seqs <= 64) {
+    // up to 64 sequences: one wave's prefix sum, lane n holding sequence n
+    if (wave == 0) {
+      int cnt = 0;
+      if (lane < a.num_seqs) {
+        const int s0 = a.cu_seqlens ? a.cu_seqlens[lane] : 0;
+        const int s1 = a.cu_seqlens ? a.cu_seqlens[lane + 1] : (int)a.total_tokens;
+        cnt = (s1 - s0 + C - 1) / C;
+      }
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int x = __shfl_up(incl, off);
+        if (lane >= off) incl += x;
+      }
+      const int excl = incl - cnt;
+      if (lane < a.num_seqs) {
+        if (c >= excl && c < incl) { sm.hit[0] = lane; sm.hit[1] = (int)(c - excl); }
+        if (c == 0 && publish) a.seq_chunk_offset[lane] = excl;
+      }
+      carry = __shfl(incl, 63);
+    }
+    __syncthreads();
+  }
+  for (int64_t base = 0; a.num_seqs > 64 && base < a.num_seqs; base += kBlock) {
     const int64_t n = base + tid;
     int cnt = 0;
     if (n < a.num_seqs) {
@@ -124,15 +148,30 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
   const int len = min(C, s1 - start);
   if (publish && tid == 0) table[c] = make_int4(n, start, len, j);
 
+  // the chunk's key and query rows: every load is issued before the first
+  // is used (rows past the chunk end read its last row and are zeroed;
+  // threads past the C x D block repeat its last load and store nothing)
+  const E* kg = static_cast<const E*>(a.k);
+  const E* qg = static_cast<const E*>(a.q);
+  constexpr int NV = C * D / VE, NL = (NV + kBlock - 1) / kBlock;
+  VLoad kv[NL], qv[NL];
+#pragma unroll
+  for (int p = 0; p < NL; ++p) {
+    const int idx = min(tid + p * kBlock, NV - 1);
+    const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
+    const int64_t gi = ((int64_t)(start + min(r, len - 1)) * a.h_qk + hq) * D + d;
+    kv[p] = *reinterpret_cast<const VLoad*>(kg + gi);
+    qv[p] = *reinterpret_cast<const VLoad*>(qg + gi);
+  }
   // gates: one wave per V head of the group, lane r holding token r
   for (int h = wave; h < a.group; h += NW) {
     const int hv = hq * a.group + h;
-    float g = 0.f, b = 0.f;
-    if (lane < len) {
-      g = a.log_alpha[(int64_t)(start + lane) * a.h_v + hv];
-      b = a.beta[(int64_t)(start + lane) * a.h_v + hv];
-      if constexpr (P) { g = neg_softplus(g); b = sigmoid_of(b); }
-    }
+    // lanes past the chunk end read its last token and then take the no-op
+    // values (a load under a branch would be waited for on its own)
+    const int64_t gi = (int64_t)(start + min(lane, len - 1)) * a.h_v + hv;
+    float g = a.log_alpha[gi], b = a.beta[gi];
+    if constexpr (P) { g = neg_softplus(g); b = sigmoid_of(b); }
+    if (lane >= len) { g = 0.f; b = 0.f; }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float x = __shfl_up(g, off);
@@ -144,26 +183,24 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
     }
   }
 
-  const E* kg = static_cast<const E*>(a.k);
-  const E* qg = static_cast<const E*>(a.q);
-  for (int idx = tid; idx < C * D / VE; idx += kBlock) {
-    const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
-    VLoad kv, qv;
 #pragma unroll
-    for (int e = 0; e < VE; ++e) { kv[e] = to_e<E>(0.f); qv[e] = to_e<E>(0.f); }
-    if (r < len) {
-      const int64_t gi = ((int64_t)(start + r) * a.h_qk + hq) * D + d;
-      kv = *reinterpret_cast<const VLoad*>(kg + gi);
-      qv = *reinterpret_cast<const VLoad*>(qg + gi);
+  for (int p = 0; p < NL; ++p) {
+    const int idx = tid + p * kBlock;
+    const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
+    if (r >= len) {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) { kv[p][e] = to_e<E>(0.f); qv[p][e] = to_e<E>(0.f); }
     }
     if constexpr (P) {
-      // raw q and k: the D / VE lanes holding a row (a whole, aligned group:
-      // the trip count is a multiple of it) scale it to unit length
-      normalize_slice<E, D, VE>(kv);
-      normalize_slice<E, D, VE>(qv);
+      // raw q and k: the D / VE lanes holding a row (a whole, aligned group)
+      // scale it to unit length
+      normalize_slice<E, D, VE>(kv[p]);
+      normalize_slice<E, D, VE>(qv[p]);
     }
-    *reinterpret_cast<VLoad*>(&sm.ks[r * KLD + d]) = kv;
-    *reinterpret_cast<VLoad*>(&sm.qs[r * KLD + d]) = qv;
+    if (idx < NV) {
+      *reinterpret_cast<VLoad*>(&sm.ks[r * KLD + d]) = kv[p];
+      *reinterpret_cast<VLoad*>(&sm.qs[r * KLD + d]) = qv[p];
+    }
   }
   __syncthreads();
 
@@ -323,21 +360,39 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
     for (int p = 0; p < PQ; ++p)
       if (!BW && tid + p * kBlock < G::QK_FR * 64) qkr[p] = qkg[tid + p * kBlock];
   }
-  const E* kg = static_cast<const E*>(a.k);
-  for (int idx = tid; !ND && idx < C * D / VE; idx += kBlock) {
-    const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
-    VLoad kv;
-#pragma unroll
-    for (int e = 0; e < VE; ++e) kv[e] = to_e<E>(0.f);
-    if (r < len) kv = *reinterpret_cast<const VLoad*>(kg + ((int64_t)(start + r) * a.h_qk + hq) * D + d);
-    // raw keys: unit rows, exactly as kernel 1 makes them for K^T and q.k
-    if constexpr (P) normalize_slice<E, D, VE>(kv);
-    *reinterpret_cast<VLoad*>(&sm.u.ks[r * KLD + d]) = kv;
-  }
+  // g and b of this V head (threads below 2 C)
+  float gbv = 0.f;
   if (tid < 2 * C) {
     const int64_t o = (c * a.h_v + hv) * C + (tid % C);
-    sm.gb[tid / C][tid % C] = (tid < C) ? a.gate_prefix[o] : a.beta_chunk[o];
+    gbv = (tid < C) ? a.gate_prefix[o] : a.beta_chunk[o];
   }
+  // the chunk's keys, all loads issued before the first is used (rows past
+  // the chunk end read its last row and are zeroed; threads past the C x D
+  // block repeat its last load and store nothing)
+  const E* kg = static_cast<const E*>(a.k);
+  constexpr int NV = C * D / VE, NL = (NV + kBlock - 1) / kBlock;
+  if constexpr (!ND) {
+    VLoad kv[NL];
+#pragma unroll
+    for (int p = 0; p < NL; ++p) {
+      const int idx = min(tid + p * kBlock, NV - 1);
+      const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
+      kv[p] = *reinterpret_cast<const VLoad*>(kg + ((int64_t)(start + min(r, len - 1)) * a.h_qk + hq) * D + d);
+    }
+#pragma unroll
+    for (int p = 0; p < NL; ++p) {
+      const int idx = tid + p * kBlock;
+      const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
+      if (r >= len) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) kv[p][e] = to_e<E>(0.f);
+      }
+      // raw keys: unit rows, exactly as kernel 1 makes them for K^T and q.k
+      if constexpr (P) normalize_slice<E, D, VE>(kv[p]);
+      if (idx < NV) *reinterpret_cast<VLoad*>(&sm.u.ks[r * KLD + d]) = kv[p];
+    }
+  }
+  if (tid < 2 * C) sm.gb[tid / C][tid % C] = gbv;
   __syncthreads();
 
   // The scan's operands that depend on g: P = the masked, decayed q.k

@@ -312,13 +312,16 @@ struct InvSmem {
     E ks[C * KLD];                     // keys of the chunk, rows past its end zero
     float at[C * FLD];                 // A and Tinv (see above)
   } u;
-  float x[4][16 * XLD];                // one 16 x 16 scratch tile per wave
-  Frag<E> tbg[G::T_FR * 64];           // Tinv diag(b exp(g)) fragments
+  union {
+    float x[4][16 * XLD];              // one 16 x 16 scratch tile per wave (blocks below the diagonal)
+    Frag<E> tbg[G::T_FR * 64];         // then the Tinv diag(b exp(g)) fragments
+  } v;
   float gb[2][C];                      // g and b of this V head
 };
 
 template <typename E, int D, int C, bool P, bool ND, bool BW>
-__global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) {
+// six workgroups per CU: 26 KB of LDS and at most 80 VGPRs each
+__global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   using SM = InvSmem<E, D, C>;
   constexpr int CT = G::CT, CKS = G::CKS, DT = G::DT, DKS = G::DKS, KLD = SM::KLD, FLD = SM::FLD, XLD = SM::XLD;
@@ -523,7 +526,7 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
   for (int dist = 1; dist < CT; ++dist) {
     for (int bi = dist + wave; bi < CT; bi += NW) {
       const int bj = bi - dist;
-      float* X = sm.x[wave];
+      float* X = sm.v.x[wave];
       f32x4 acc = zero4();
       for (int bm = bj; bm < bi; ++bm) {
         const float* Am = &at[(16 * bi) * FLD + 16 * bm];
@@ -565,7 +568,7 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
       vg[e] = to_e<E>((i < C) ? t * __expf(sm.gb[0][i]) : 0.f);
     }
     tg[it] = vb;
-    sm.tbg[it] = vg;
+    sm.v.tbg[it] = vg;
   }
   __syncthreads();
   if (ksd < DKS) {
@@ -576,7 +579,7 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
 #pragma unroll
       for (int s = 0; s < CKS; ++s) {
         if (causal_zero(rt, s)) continue;              // Tinv is lower triangular
-        const Frag<E> tb = sm.tbg[(rt * CKS + s) * 64 + lane];
+        const Frag<E> tb = sm.v.tbg[(rt * CKS + s) * 64 + lane];
         acc0 = mma(kta[s], tb, acc0);
         if (2 * ksd + 1 < DT) acc1 = mma(ktb[s], tb, acc1);
       }
@@ -597,7 +600,7 @@ __global__ __launch_bounds__(kBlock) void gdn_k2_inverse_w(const PrefillArgs a) 
 #pragma unroll
           for (int s2 = 0; s2 < CKS; ++s2) {
             if (causal_zero(rt, s2)) continue;
-            const Frag<E> tb = sm.tbg[(rt * CKS + s2) * 64 + lane];
+            const Frag<E> tb = sm.v.tbg[(rt * CKS + s2) * 64 + lane];
             pa[h] = mma(tb, kta[s2], pa[h]);
             if (2 * ksd + 1 < DT) pb[h] = mma(tb, ktb[s2], pb[h]);
           }

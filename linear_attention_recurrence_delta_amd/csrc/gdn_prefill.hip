@@ -410,6 +410,7 @@ __global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs 
       const int it = tid + p * kBlock;
       if (BW || it >= G::QK_FR * 64) continue;       // the backward pass uses P^T (below)
       const int f = it / 64, ln = it % 64, nt = f / CKS, s = f % CKS, q4 = ln >> 4;
+      if (causal_zero(nt, s)) continue;              // all zero; the scan neither copies nor reads it
       const int r = 16 * nt + (ln & 15);
       const float gr = sm.gb[0][r], vr = (float)(r < len);
       Frag<E> v;
@@ -457,6 +458,7 @@ __global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs 
     Frag<E>* tg = reinterpret_cast<Frag<E>*>(a.tinv) + (c * a.h_v + hv) * G::T_FR * 64;
     for (int it = tid; it < G::T_FR * 64; it += kBlock) {
       const int f = it / 64, ln = it % 64, rt = f / CKS, s = f % CKS, q4 = ln >> 4;
+      if (causal_zero(rt, s)) continue;              // all zero; the scan neither copies nor reads it
       const int r = 16 * rt + (ln & 15);
       Frag<E> vb;
 #pragma unroll
@@ -554,6 +556,7 @@ __global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs 
   Frag<E>* tg = reinterpret_cast<Frag<E>*>(a.tinv) + (c * a.h_v + hv) * G::T_FR * 64;
   for (int it = tid; it < G::T_FR * 64; it += kBlock) {
     const int f = it / 64, ln = it % 64, rt = f / CKS, s = f % CKS, q4 = ln >> 4;
+    if (causal_zero(rt, s)) continue;                // all zero; no product reads it
     const int r = 16 * rt + (ln & 15);
     Frag<E> vb, vg;
 #pragma unroll
@@ -704,27 +707,32 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
                              JOBS[0] + JOBS[1] + JOBS[2] + JOBS[3],
                              JOBS[0] + JOBS[1] + JOBS[2] + JOBS[3] + JOBS[4],
                              JOBS[0] + JOBS[1] + JOBS[2] + JOBS[3] + JOBS[4] + JOBS[5]};
-  // loader wave lw takes the jobs whose window-wide index is lw mod NLD
-  auto copy_region = [&](int r, const char* src, char* dst, int bytes) __attribute__((always_inline)) {
-    for (int jj = ((lw - CUM[r]) % NLD + NLD) % NLD; jj < JOBS[r]; jj += NLD)
+  // loader wave lw takes the jobs whose window-wide index is lw mod NLD; in
+  // the causal regions (P, Tinv diag(b)) the jobs of fragments that the mask
+  // makes zero copy nothing (the products never read them)
+  auto copy_region = [&](int r, const char* src, char* dst, int bytes, bool causal) __attribute__((always_inline)) {
+    for (int jj = ((lw - CUM[r]) % NLD + NLD) % NLD; jj < JOBS[r]; jj += NLD) {
+      const int f = 1024 * jj / FB;
+      if (causal && causal_zero(f / CKS, f % CKS)) continue;
       copy_1k(src + 1024 * jj, dst + 1024 * jj, bytes - 1024 * jj, lane);
+    }
   };
   auto copy_window = [&](int xs, int xp) __attribute__((always_inline)) {
     if (xs < c1) {
       copy_region(0, static_cast<const char*>(a.key_t) + ((int64_t)xs * a.h_qk + hq) * B_KT,
-                  reinterpret_cast<char*>(sm.kt[xs & 1]), B_KT);
+                  reinterpret_cast<char*>(sm.kt[xs & 1]), B_KT, false);
       copy_region(1, static_cast<const char*>(a.w) + ((int64_t)xs * a.h_v + hv) * B_W,
-                  reinterpret_cast<char*>(sm.wf[xs & 1]), B_W);
+                  reinterpret_cast<char*>(sm.wf[xs & 1]), B_W, false);
       copy_region(2, static_cast<const char*>(a.q_frag) + ((int64_t)xs * a.h_qk + hq) * B_Q,
-                  reinterpret_cast<char*>(sm.qf[xs & 1]), B_Q);
+                  reinterpret_cast<char*>(sm.qf[xs & 1]), B_Q, false);
       copy_region(3, static_cast<const char*>(a.pmask) + ((int64_t)xs * a.h_v + hv) * B_P,
-                  reinterpret_cast<char*>(sm.pf[xs & 1]), B_P);
+                  reinterpret_cast<char*>(sm.pf[xs & 1]), B_P, true);
       copy_region(4, reinterpret_cast<const char*>(a.dtab + ((int64_t)xs * a.h_v + hv) * (2 * C + 4)),
-                  reinterpret_cast<char*>(sm.dtab[xs & 1]), B_D);
+                  reinterpret_cast<char*>(sm.dtab[xs & 1]), B_D, false);
     }
     if (xp < c1) {
       copy_region(5, static_cast<const char*>(a.tinv) + ((int64_t)xp * a.h_v + hv) * B_T,
-                  reinterpret_cast<char*>(sm.tf[xp & 1]), B_T);
+                  reinterpret_cast<char*>(sm.tf[xp & 1]), B_T, true);
       // the V columns, row i of the chunk at byte 16 l of its job; rows
       // past the chunk end repeat its last row (Tinv diag(b) has zero
       // columns there)
@@ -757,6 +765,11 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   auto line_addr = [&](int x, int t) -> const char* {
     if (t < nv) {
       const int o = 128 * (cb + G::NCB * t);
+      // lines of the P and Tinv diag(b) fragments that the causal mask makes
+      // zero are neither copied nor touched
+      const int fp = (o - B_W) / FB, ft = (o - B_W - B_P) / FB;
+      if (o >= B_W && o < B_W + B_P && causal_zero(fp / CKS, fp % CKS)) return nullptr;
+      if (o >= B_W + B_P && o < B_W + B_P + B_T && causal_zero(ft / CKS, ft % CKS)) return nullptr;
       return o < B_W ? static_cast<const char*>(a.w) + ((int64_t)x * a.h_v + hv) * B_W + o
            : o < B_W + B_P ? static_cast<const char*>(a.pmask) + ((int64_t)x * a.h_v + hv) * B_P + (o - B_W)
            : o < B_W + B_P + B_T ? static_cast<const char*>(a.tinv) + ((int64_t)x * a.h_v + hv) * B_T + (o - B_W - B_P)
@@ -776,8 +789,10 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   auto warm = [&](int x) __attribute__((always_inline)) {
     if (x >= c1) return;
     const int total = nv + nq + C;
-    for (int t = 64 * uw + lane; t < total; t += 64 * NS)
-      __builtin_amdgcn_global_load_lds(line_addr(x, t), (lds_ptr_t)sm.touch[wave], 4, 0, 0);
+    for (int t = 64 * uw + lane; t < total; t += 64 * NS) {
+      const char* p = line_addr(x, t);
+      if (p) __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)sm.touch[wave], 4, 0, 0);
+    }
   };
 
   // the saving form stages its row-major stores in the Q and P fragment

@@ -37,12 +37,14 @@ DECODE_KERNEL = "gdn_kd_decode_step"
 def algorithmic_work(T, HQ, HV, D, C, N, decode_batch):
     """Per-launch algorithmic flops and HBM bytes of each kernel, from the
     chunkwise method's operation counts (dense C x C in-chunk products, bf16
-    q/k/v/o and fragments, fp32 gates and states), and the resource that
-    bounds it (the one whose time at peak is larger); see the design notes.
-    Returns ({kernel: (bound, flops, bytes)}, flops per token)."""
+    q/k/v/o and fragments, fp32 gates and states; the causal C x C operands
+    Tinv diag(b) and P count the bytes of their lower triangles), and the
+    resource that bounds it (the one whose time at peak is larger); see the
+    design notes. Returns ({kernel: (bound, flops, bytes)}, flops per token)."""
     dk = dv = D
     e = 2                                       # bytes per bf16 element
     gates = T * HV * 8                          # log a and b (fp32), or g and b
+    tri = (C + 1) / 2.0                         # lower-triangle elements per token of a causal C x C operand
     work = {
         # Q K^T per QK head; reads q, k, log a, b; writes K^T, Q and q.k
         # fragments, g, b
@@ -53,12 +55,12 @@ def algorithmic_work(T, HQ, HV, D, C, N, decode_batch):
         # and the row-factor table (2C + 4 fp32 per chunk and V head)
         "gdn_k2_inverse_w": (T * (HQ * 2 * C * dk + HV * (C * C / 3.0 + 2 * C * dk)),
                              T * HQ * (2 * dk + C) * e + gates
-                             + T * HV * (2 * C + dk) * e + T * HV * (2 * C + 4) * 4 / C),
+                             + T * HV * (2 * tri + dk) * e + T * HV * (2 * C + 4) * 4 / C),
         # Ut, W S, Q S, K^T U, P U per V head; reads Q, K^T, P, V, Tinv
         # diag(b), W, the row factors and the initial states; writes o and the
         # final states
         "gdn_k3_scan": (T * HV * (6 * dk * dv + 4 * C * dv),
-                        T * HQ * 2 * dk * e + T * HV * (dv + 2 * C + dk) * e + T * HV * (2 * C + 4) * 4 / C
+                        T * HQ * 2 * dk * e + T * HV * (dv + 2 * tri + dk) * e + T * HV * (2 * C + 4) * 4 / C
                         + T * HV * dv * e + 2 * N * HV * dk * dv * 4),
     }
     per_token = HV * (6 * dk * dv + 2 * C * dk + 4 * C * dv + C * C / 3.0) + HQ * 4 * C * dk
@@ -81,11 +83,13 @@ def algorithmic_work_bwd(T, HQ, HV, D, C, N):
     """Per-launch algorithmic flops and HBM bytes of the backward pass's
     kernels (gdn_chunk_bwd's five launches), counted as for the forward:
     dense C x C in-chunk products, compulsory reads and writes of each
-    launch (bf16 rows and fragments, fp32 gates and states). Returns
+    launch (bf16 rows and fragments, fp32 gates and states; Tinv diag(b)
+    counts its lower triangle). Returns
     {kernel: (bound, flops, bytes)}."""
     dk = dv = D
     e = 2
     gates = T * HV * 8
+    tri = (C + 1) / 2.0                         # lower-triangle elements per token of a causal C x C operand
     dtab = T * HV * (2 * C + 4) * 4 / C
     states = N * HV * dk * dv * 4
     chunk_states = T / C * HV * dk * dv * e     # one dk x dv matrix per chunk and V head
@@ -98,11 +102,11 @@ def algorithmic_work_bwd(T, HQ, HV, D, C, N):
         # diag(b), W, the row factors, P^T, W^T and Tinv^T
         "gdn_k2_inverse_w [bwd]": (T * (HQ * 2 * C * dk + HV * (C * C / 3.0 + 4 * C * dk)),
                                    T * HQ * (2 * dk + C) * e + gates
-                                   + T * HV * (3 * C + 2 * dk) * e + dtab),
+                                   + T * HV * (2 * C + tri + 2 * dk) * e + dtab),
         # Ut, W S, K^T U; reads K^T, V, Tinv diag(b), W, the row factors and
         # the initial states; writes the chunk-start states and U
         "gdn_k3_scan [save]": (T * HV * (4 * dk * dv + 2 * C * dv),
-                               T * HQ * dk * e + T * HV * (dv + C + dk) * e + dtab + states
+                               T * HQ * dk * e + T * HV * (dv + tri + dk) * e + dtab + states
                                + chunk_states + T * HV * dv * e),
         # K dS, P^T dO, Q^T dO, W^T dU; reads K and Q^T, P^T and W^T
         # fragments, the row factors, dL/do, dL/dS_final; writes dL/dS_end per

@@ -79,8 +79,11 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
   typedef E VLoad __attribute__((ext_vector_type(VE)));
   __shared__ SM sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, l16 = lane & 15;
-  const int64_t c = blockIdx.x;
-  const int hq = blockIdx.y;
+  // the QK heads of one chunk slot, which read the same gate lines, are
+  // consecutive logical ids and so share an XCD
+  const int64_t lid = xcd_local_id(blockIdx.x, gridDim.x);
+  const int64_t c = lid / a.h_qk;
+  const int hq = (int)(lid % a.h_qk);
   const bool publish = hq == 0;
   if (tid == 0) { sm.hit[0] = -1; sm.hit[1] = 0; }
   __syncthreads();
@@ -1017,7 +1020,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
     switch (stage) {
       // the backward pass (backward workspace pointers set) takes no flags
       case 1: {
-        const dim3 g(nc, (unsigned)a.h_qk);
+        const dim3 g(nc * (unsigned)a.h_qk);
         if (a.k_frag) gdn_k1_chunk_prep<E, D, C, false, true><<<g, dim3(kBlock), 0, s>>>(a);
         else if (a.prep) gdn_k1_chunk_prep<E, D, C, true, false><<<g, dim3(kBlock), 0, s>>>(a);
         else gdn_k1_chunk_prep<E, D, C, false, false><<<g, dim3(kBlock), 0, s>>>(a);

@@ -100,6 +100,33 @@ def test_backward_without_final_state_gradient():
     compare(got, want, "bf16")
 
 
+def test_backward_reads_only_what_it_writes():
+    # as for the forward pass: a NaN-filled workspace gives the same
+    # gradients as a zeroed one; bit for bit except dlog_alpha and dbeta,
+    # which are summed with LDS atomics in no fixed order (a NaN read would
+    # still make them non-finite)
+    say("backward with a NaN-filled workspace, d=128 C=64 bf16")
+    inp = I.make_prefill(455, [77, 0, 130], 2, 6, 128, "bf16", "randn")
+    seeds = I.make_backward_seeds(456, [77, 0, 130], 6, 128, "bf16")
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    dims = gdn.make_dims(3, 207, 2, 6, 128, 128, 64, torch.bfloat16)
+    nbytes = gdn.gdn_chunk_bwd_workspace_bytes(dims)
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV)
+        outs.append(gdn.gdn_chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], seeds["d_o"].to(DEV),
+                                      d["init_state"], d["cu_seqlens"], seeds["d_final"].to(DEV), chunk=64,
+                                      workspace=ws))
+    torch.cuda.synchronize()
+    for name in outs[0]:
+        a, b = outs[0][name], outs[1][name]
+        if name in ("dlog_alpha", "dbeta"):
+            assert torch.isfinite(b).all(), name
+            assert (a - b).abs().max() <= 1e-5 * a.abs().max(), name
+        else:
+            assert torch.equal(a, b), name
+
+
 def test_backward_head_group_of_four():
     say("backward h_qk=3 h_v=12 d=128 C=64 bf16 T=90")
     got, want, _, _ = run_case(460, [90], 3, 12, 128, 64, "bf16")

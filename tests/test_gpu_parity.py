@@ -106,6 +106,37 @@ def test_prefill_varlen_with_empty_and_short_sequences(dtype, chunk):
         assert torch.equal(fin[n].cpu(), inp["init_state"][n])
 
 
+def test_prefill_many_sequences():
+    # more sequences than one wave's prefix sum covers (64): the chunk table
+    # comes from the block scan, here over two 256-sequence passes
+    rng = np.random.default_rng(41)
+    lens = [int(x) for x in rng.integers(0, 41, size=300)]
+    say(f"prefill, {len(lens)} sequences, {sum(lens)} tokens, bf16 C=64")
+    inp = random_prefill(42, lens, 2, 6, 128, "bf16")
+    o, fin = run_gpu(inp, 64)
+    want_o, want_f = O.recurrent_form1(**oracle_args(inp))
+    check(o, want_o, torch.bfloat16, "o")
+    check(fin, want_f, torch.bfloat16, "final")
+
+
+@pytest.mark.parametrize("chunk", [64, 16])
+def test_prefill_reads_only_what_it_writes(chunk):
+    # the kernels never read workspace bytes that no kernel wrote (e.g. the
+    # fragments that the causal mask makes zero): a workspace full of NaN
+    # bytes gives the same outputs, bit for bit, as a zeroed one
+    say(f"prefill with a NaN-filled workspace, C={chunk}")
+    inp = on_dev(random_prefill(43, [77, 0, 130], 2, 6, 128, "bf16"))
+    dims = gdn.make_dims(3, 207, 2, 6, 128, 128, chunk, torch.bfloat16)
+    nbytes = gdn.gdn_chunk_fwd_workspace_bytes(dims)
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV)
+        outs.append(gdn.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                                      inp["init_state"], inp["cu_seqlens"], chunk=chunk, workspace=ws))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 def test_zero_tokens():
     say("T=0, two empty sequences")
     inp = random_prefill(8, [0, 0], 1, 3, 128, "bf16")

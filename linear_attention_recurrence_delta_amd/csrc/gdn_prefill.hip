@@ -905,14 +905,38 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       for (int dt = 0; dt < DT; ++dt) S[dt] = mma(ka[dt], Ud[ks], S[dt]);
     }
     E* og = static_cast<E*>(a.o);
+    if constexpr (!SV && std::is_same<E, bf16_t>::value && CT % 2 == 0) {
+      // bf16 outputs, 16 bytes per lane: for each pair of row tiles, lanes
+      // 16..31 and 32..47 trade halves (v_permlane16_swap exchanges the odd
+      // 16-lane rows of its first operand with the even rows of its second),
+      // after which lane (quad, l) holds eight consecutive columns,
+      // 8 (quad / 2) .. +7, of row l of tile 2 p + quad % 2
 #pragma unroll
-    for (int nt = 0; nt < CT; ++nt) {
-      const int r = 16 * nt + l16;
-      if (!SV && r < len) {
-        Half<E> h;
+      for (int p = 0; p < CT / 2; ++p) {
+        Half<E> hx, hy;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = to_e<E>(O[nt][i]);
-        *reinterpret_cast<Half<E>*>(og + ((int64_t)(start + r) * a.h_v + hv) * D + col0 + 16 * slice + 4 * quad) = h;
+        for (int i = 0; i < 4; ++i) {
+          hx[i] = to_e<E>(O[2 * p][i]);
+          hy[i] = to_e<E>(O[2 * p + 1][i]);
+        }
+        const u32x2 ux = __builtin_bit_cast(u32x2, hx), uy = __builtin_bit_cast(u32x2, hy);
+        const auto s0 = __builtin_amdgcn_permlane16_swap(ux[0], uy[0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(ux[1], uy[1], false, false);
+        const u32x4 val = {s0[0], s1[0], s0[1], s1[1]};
+        const int r = 16 * (2 * p + (quad & 1)) + l16;
+        if (r < len)
+          *reinterpret_cast<u32x4*>(og + ((int64_t)(start + r) * a.h_v + hv) * D + col0 + 16 * slice + 8 * (quad >> 1)) = val;
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < CT; ++nt) {
+        const int r = 16 * nt + l16;
+        if (!SV && r < len) {
+          Half<E> h;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h[i] = to_e<E>(O[nt][i]);
+          *reinterpret_cast<Half<E>*>(og + ((int64_t)(start + r) * a.h_v + hv) * D + col0 + 16 * slice + 4 * quad) = h;
+        }
       }
     }
   };

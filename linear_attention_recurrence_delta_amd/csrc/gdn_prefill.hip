@@ -666,6 +666,9 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   // roles: NS scan waves, NS Ut waves, and loader waves (direct copies only,
   // so that their stalls on the memory pipeline hold up nothing else)
   constexpr int NLD = kScanBlock / 64 - 2 * NS;
+  // bf16 outputs leave through LDS and the Ut waves (the fp32 ones from the
+  // scan waves' registers)
+  constexpr bool STAGE_O = std::is_same<E, bf16_t>::value;
   constexpr int FB = (int)sizeof(Frag<E>) * 64;            // bytes per fragment
   constexpr int ESZ = (int)sizeof(E);
   __shared__ ScanSmem<E, D, C> sm;
@@ -904,40 +907,57 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) S[dt] = mma(ka[dt], Ud[ks], S[dt]);
     }
-    E* og = static_cast<E*>(a.o);
-    if constexpr (!SV && std::is_same<E, bf16_t>::value && CT % 2 == 0) {
-      // bf16 outputs, 16 bytes per lane: for each pair of row tiles, lanes
-      // 16..31 and 32..47 trade halves (v_permlane16_swap exchanges the odd
-      // 16-lane rows of its first operand with the even rows of its second),
-      // after which lane (quad, l) holds eight consecutive columns,
-      // 8 (quad / 2) .. +7, of row l of tile 2 p + quad % 2
+    if constexpr (!SV && STAGE_O) {
+      // bf16 outputs: row-major (16 columns, 32 bytes a row) into this
+      // slice's Ut slot, whose tiles this wave has read above; the slice's
+      // Ut wave stores them in the next iteration, before it forms new
+      // tiles there
+      E* ost = reinterpret_cast<E*>(&sm.uf[par][slice * CT * 64]);
 #pragma unroll
-      for (int p = 0; p < CT / 2; ++p) {
-        Half<E> hx, hy;
+      for (int nt = 0; nt < CT; ++nt) {
+        Half<E> h;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hx[i] = to_e<E>(O[2 * p][i]);
-          hy[i] = to_e<E>(O[2 * p + 1][i]);
-        }
-        const u32x2 ux = __builtin_bit_cast(u32x2, hx), uy = __builtin_bit_cast(u32x2, hy);
-        const auto s0 = __builtin_amdgcn_permlane16_swap(ux[0], uy[0], false, false);
-        const auto s1 = __builtin_amdgcn_permlane16_swap(ux[1], uy[1], false, false);
-        const u32x4 val = {s0[0], s1[0], s0[1], s1[1]};
-        const int r = 16 * (2 * p + (quad & 1)) + l16;
-        if (r < len)
-          *reinterpret_cast<u32x4*>(og + ((int64_t)(start + r) * a.h_v + hv) * D + col0 + 16 * slice + 8 * (quad >> 1)) = val;
+        for (int i = 0; i < 4; ++i) h[i] = to_e<E>(O[nt][i]);
+        *reinterpret_cast<Half<E>*>(ost + (16 * nt + l16) * 16 + 4 * quad) = h;
       }
-    } else {
+    } else if constexpr (!SV) {
+      E* og = static_cast<E*>(a.o);
 #pragma unroll
       for (int nt = 0; nt < CT; ++nt) {
         const int r = 16 * nt + l16;
-        if (!SV && r < len) {
+        if (r < len) {
           Half<E> h;
 #pragma unroll
           for (int i = 0; i < 4; ++i) h[i] = to_e<E>(O[nt][i]);
           *reinterpret_cast<Half<E>*>(og + ((int64_t)(start + r) * a.h_v + hv) * D + col0 + 16 * slice + 4 * quad) = h;
         }
       }
+    }
+  };
+
+  // Ut wave uw: chunk x's outputs for slice uw, staged by that slice's scan
+  // wave in its Ut slot of parity x (only this wave writes that slot next).
+  // They are read out before the slot takes new tiles and stored after
+  // those are formed, so the stores do not queue behind the loaders' copies
+  // ahead of the tiles: 16 bytes a lane, 32 rows of 16 columns per
+  // instruction.
+  constexpr int OJ = (C + 31) / 32;
+  auto read_outputs = [&](int x, u32x4 (&val)[OJ]) __attribute__((always_inline)) {
+    const E* st = reinterpret_cast<const E*>(&sm.uf[x & 1][uw * CT * 64]);
+#pragma unroll
+    for (int j = 0; j < OJ; ++j) {
+      const int r = min(32 * j + lane / 2, C - 1);
+      val[j] = *reinterpret_cast<const u32x4*>(st + r * 16 + 8 * (lane & 1));
+    }
+  };
+  auto store_outputs = [&](int x, const u32x4 (&val)[OJ]) __attribute__((always_inline)) {
+    const int start = chunk_start(x), len = chunk_len(x);
+#pragma unroll
+    for (int j = 0; j < OJ; ++j) {
+      const int r = 32 * j + lane / 2;
+      if (r < C && r < len)
+        *reinterpret_cast<u32x4*>(static_cast<E*>(a.o) + ((int64_t)(start + r) * a.h_v + hv) * D + col0 + 16 * uw +
+                                  8 * (lane & 1)) = val[j];
     }
   };
 
@@ -1017,10 +1037,20 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       warm(c0 + 1);
       warm(c0 + 2);
       __syncthreads();
+      u32x4 ov[OJ];
       for (int c = c0 - 1; c < c1; ++c) {
+        // chunk c - 1's outputs leave the Ut slot that chunk c + 1's tiles
+        // take next
+        const bool st = !SV && STAGE_O && c > c0;
+        if (st) read_outputs(c - 1, ov);
         if (c + 1 < c1) produce_chunk(c + 1);
+        if (st) store_outputs(c - 1, ov);
         warm(c + 3);
         lds_barrier();
+      }
+      if (!SV && STAGE_O) {
+        read_outputs(c1 - 1, ov);
+        store_outputs(c1 - 1, ov);
       }
     }
   } else if (is_scan && a.final_state) {

@@ -669,6 +669,13 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   // bf16 outputs leave through LDS and the Ut waves (the fp32 ones from the
   // scan waves' registers)
   constexpr bool STAGE_O = std::is_same<E, bf16_t>::value;
+  // the saving form's S and U rows: staged in the (here unused) Q and P
+  // fragment buffers by the scan waves, double-buffered by chunk parity, and
+  // stored by the slice's Ut wave in the next iteration, where they fit
+  constexpr int SLD = staged_ld<E>(), SV_AREA = (D + C) * SLD;
+  constexpr bool SV_STAGE =
+      SV && 2 * NS * SV_AREA * (int)sizeof(E) <= (int)(sizeof(ScanSmem<E, D, C>::qf) + sizeof(ScanSmem<E, D, C>::pf)) &&
+      D % StagedRows<E>::RPI == 0 && C % StagedRows<E>::RPI == 0;
   constexpr int FB = (int)sizeof(Frag<E>) * 64;            // bytes per fragment
   constexpr int ESZ = (int)sizeof(E);
   __shared__ ScanSmem<E, D, C> sm;
@@ -806,15 +813,18 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   // buffers, which it does not use
   static_assert(!SV || NS * stage_elems<E>() * (int)sizeof(E) <=
                            (int)(sizeof(sm.qf) + sizeof(sm.pf)), "staging fits the unused buffers");
+  auto sv_area = [&](int par, int sl) { return reinterpret_cast<E*>(sm.qf) + (par * NS + sl) * SV_AREA; };
   // scan waves: the slice's D x 16 state columns in accumulator tiles
   f32x4 S[DT];
 
   auto scan_chunk = [&](int c) __attribute__((always_inline)) {
     const int start = chunk_start(c), len = chunk_len(c), par = c & 1;
-    if constexpr (SV) {
+    if constexpr (SV_STAGE) {
       // backward pass: the state at the chunk's start, rounded as the
-      // products below use it; row-major through the (here unused) Q
-      // fragment buffers
+      // products below use it, staged for the slice's Ut wave
+      stage_tiles_rows<E, DT>(S, sv_area(par, slice), lane);
+    } else if constexpr (SV) {
+      // (the same, stored row-major through the unused Q fragment buffers)
       store_tiles_rows<E, DT>(S, reinterpret_cast<E*>(sm.qf) + slice * stage_elems<E>(),
                               static_cast<E*>(a.sc) + ((int64_t)c * a.h_v + hv) * D * D + col0 + 16 * slice, D, lane);
     }
@@ -871,8 +881,10 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     Frag<E> Uk[CKS];
 #pragma unroll
     for (int ks = 0; ks < CKS; ++ks) Uk[ks] = acc_to_frag<E>(U[2 * ks], (2 * ks + 1 < CT) ? U[2 * ks + 1] : zero4());
-    if constexpr (SV) {
+    if constexpr (SV_STAGE) {
       // backward pass: the chunk's U rows, rounded as the products use them
+      stage_tiles_rows<E, CT>(U, sv_area(par, slice) + D * SLD, lane);
+    } else if constexpr (SV) {
       store_tiles_rows<E, CT>(U, reinterpret_cast<E*>(sm.qf) + slice * stage_elems<E>(),
                               static_cast<E*>(a.ub) + ((int64_t)c * a.h_v + hv) * C * D + col0 + 16 * slice, D, lane);
     }
@@ -961,6 +973,28 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     }
   };
 
+  // Ut wave uw, saving form: chunk x's staged S rows (D) and U rows (C) of
+  // slice uw, read out in one iteration and stored after the Ut tiles
+  using SR = StagedRows<E>;
+  constexpr int NSV = (D + C) / SR::RPI;
+  auto read_saved = [&](int x, u32x4 (&val)[NSV]) __attribute__((always_inline)) {
+    const E* ar = sv_area(x & 1, uw);
+#pragma unroll
+    for (int j = 0; j < NSV; ++j)
+      val[j] = *reinterpret_cast<const u32x4*>(&ar[(j * SR::RPI + lane / SR::LPR) * SLD + (lane % SR::LPR) * SR::VE]);
+  };
+  auto store_saved = [&](int x, const u32x4 (&val)[NSV]) __attribute__((always_inline)) {
+    const int cix = col0 + 16 * uw + (lane % SR::LPR) * SR::VE;
+    E* gs = static_cast<E*>(a.sc) + ((int64_t)x * a.h_v + hv) * D * D + cix;
+    E* gu = static_cast<E*>(a.ub) + ((int64_t)x * a.h_v + hv) * C * D + cix;
+#pragma unroll
+    for (int j = 0; j < NSV; ++j) {
+      const int row = j * SR::RPI + lane / SR::LPR;
+      if (j * SR::RPI < D) *reinterpret_cast<u32x4*>(gs + (int64_t)row * D) = val[j];
+      else *reinterpret_cast<u32x4*>(gu + (int64_t)(row - D) * D) = val[j];
+    }
+  };
+
   // Ut wave uw: chunk p's Ut tiles Tinv diag(b) V of slice uw; V's
   // fragments (col = state column, k = token) are gathered from the
   // row-major V columns
@@ -1037,20 +1071,27 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       warm(c0 + 1);
       warm(c0 + 2);
       __syncthreads();
-      u32x4 ov[OJ];
+      u32x4 ov[OJ], sv[NSV];
       for (int c = c0 - 1; c < c1; ++c) {
         // chunk c - 1's outputs leave the Ut slot that chunk c + 1's tiles
-        // take next
-        const bool st = !SV && STAGE_O && c > c0;
+        // take next (saving form: its S and U rows, whose staging area the
+        // scan waves write again in the next iteration)
+        const bool st = !SV && STAGE_O && c > c0, ss = SV_STAGE && c > c0;
         if (st) read_outputs(c - 1, ov);
+        if (ss) read_saved(c - 1, sv);
         if (c + 1 < c1) produce_chunk(c + 1);
         if (st) store_outputs(c - 1, ov);
+        if (ss) store_saved(c - 1, sv);
         warm(c + 3);
         lds_barrier();
       }
       if (!SV && STAGE_O) {
         read_outputs(c1 - 1, ov);
         store_outputs(c1 - 1, ov);
+      }
+      if (SV_STAGE) {
+        read_saved(c1 - 1, sv);
+        store_saved(c1 - 1, sv);
       }
     }
   } else if (is_scan && a.final_state) {

@@ -83,6 +83,27 @@ __device__ __forceinline__ void copy_1k(const char* src, char* dst, int bytes, i
 // area may be reused once the call returns.
 template <typename E> constexpr int stage_elems() { return 64 * (16 + 16 / (int)sizeof(E)); }
 
+// The first half of store_tiles_rows on its own: NT accumulator tiles (rows
+// 16 t + 4 q + i, column l) written row-major into `area` with the padded
+// row stride 16 + 16 / sizeof(E), for another wave to read back as 16-byte
+// row segments (load_staged_rows) once an LDS barrier has passed.
+template <typename E> constexpr int staged_ld() { return 16 + 16 / (int)sizeof(E); }
+template <typename E, int NT>
+__device__ __forceinline__ void stage_tiles_rows(const f32x4 (&acc)[NT], E* area, int lane) {
+  constexpr int SLD = staged_ld<E>();
+  const int q = lane >> 4, col = lane & 15;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) area[(16 * t + 4 * q + i) * SLD + col] = to_e<E>(acc[t][i]);
+  }
+}
+// Lane `lane`'s 16-byte piece of instruction j over staged rows: row
+// j * RPI + lane / LPR, columns (lane % LPR) * VE .. + VE - 1.
+template <typename E> struct StagedRows {
+  static constexpr int VE = 16 / (int)sizeof(E), LPR = 16 / VE, RPI = 64 / LPR;
+};
+
 template <typename E, int NT>
 __device__ __forceinline__ void store_tiles_rows(const f32x4 (&acc)[NT], E* area, E* g, int ld, int lane) {
   constexpr int VE = 16 / (int)sizeof(E);     // elements per 16 bytes

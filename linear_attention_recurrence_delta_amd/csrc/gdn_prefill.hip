@@ -831,53 +831,45 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     Frag<E> Sf[DKS];
 #pragma unroll
     for (int ks = 0; ks < DKS; ++ks) Sf[ks] = acc_to_frag<E>(S[2 * ks], (2 * ks + 1 < DT) ? S[2 * ks + 1] : zero4());
-    // Both products that read the state run together, contraction step
-    // outermost so that 2 CT independent accumulators interleave, with the
-    // next step's LDS fragments loaded before this step's MFMAs:
-    //   O^T[col][r] = sum_d S[d][col] q_r[d]   (inter-chunk output)
+    // Only W S -> U -> K^T U lies on the recurrence's path from one chunk's
+    // state to the next: W S goes first, Q S (inter-chunk output) runs while
+    // its results land, and P U (intra-chunk output) after the state update.
     //   WS[r][col]  = sum_d W[r][d] S[d][col]
-    f32x4 O[CT], WS[CT];
+    f32x4 WS[CT];
 #pragma unroll
-    for (int t = 0; t < CT; ++t) { O[t] = zero4(); WS[t] = zero4(); }
-    Frag<E> qa[CT], wa[CT];
+    for (int t = 0; t < CT; ++t) WS[t] = zero4();
+    if constexpr (!ND) {
 #pragma unroll
-    for (int t = 0; t < CT; ++t) {
-      if constexpr (!SV) qa[t] = sm.qf[par][(t * DKS) * 64 + lane];
-      if constexpr (!ND) wa[t] = sm.wf[par][(t * DKS) * 64 + lane];
-    }
+      for (int ks = 0; ks < DKS; ++ks) {
+        Frag<E> wa[CT];
 #pragma unroll
-    for (int ks = 0; ks < DKS; ++ks) {
-      Frag<E> qn[CT], wn[CT];
-      if (ks + 1 < DKS) {
+        for (int t = 0; t < CT; ++t) wa[t] = sm.wf[par][(t * DKS + ks) * 64 + lane];
 #pragma unroll
-        for (int t = 0; t < CT; ++t) {
-          if constexpr (!SV) qn[t] = sm.qf[par][(t * DKS + ks + 1) * 64 + lane];
-          if constexpr (!ND) wn[t] = sm.wf[par][(t * DKS + ks + 1) * 64 + lane];
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < CT; ++t) {
-        if constexpr (!SV) O[t] = mma(Sf[ks], qa[t], O[t]);
-        if constexpr (!ND) WS[t] = mma(wa[t], Sf[ks], WS[t]);
-      }
-      if (ks + 1 < DKS) {
-#pragma unroll
-        for (int t = 0; t < CT; ++t) {
-          if constexpr (!SV) qa[t] = qn[t];
-          if constexpr (!ND) wa[t] = wn[t];
-        }
+        for (int t = 0; t < CT; ++t) WS[t] = mma(wa[t], Sf[ks], WS[t]);
       }
     }
-    // U = Ut - W S; the inter-chunk output takes exp(g_r); the row factors
-    // come from the chunk's table (zero past the chunk end)
+    //   O^T[col][r] = sum_d S[d][col] q_r[d]
+    f32x4 O[CT];
+#pragma unroll
+    for (int t = 0; t < CT; ++t) O[t] = zero4();
+    if constexpr (!SV) {
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks) {
+        Frag<E> qa[CT];
+#pragma unroll
+        for (int t = 0; t < CT; ++t) qa[t] = sm.qf[par][(t * DKS + ks) * 64 + lane];
+#pragma unroll
+        for (int t = 0; t < CT; ++t) O[t] = mma(Sf[ks], qa[t], O[t]);
+      }
+    }
+    // U = Ut - W S; the row factors come from the chunk's table (zero past
+    // the chunk end)
     const float* ea = sm.dtab[par];
     const float* ed = sm.dtab[par] + C;
     f32x4 U[CT];
 #pragma unroll
-    for (int t = 0; t < CT; ++t) {
+    for (int t = 0; t < CT; ++t)
       U[t] = ND ? sm.uf[par][(slice * CT + t) * 64 + lane] : sm.uf[par][(slice * CT + t) * 64 + lane] - WS[t];
-      O[t] *= ea[16 * t + l16];
-    }
     Frag<E> Uk[CKS];
 #pragma unroll
     for (int ks = 0; ks < CKS; ++ks) Uk[ks] = acc_to_frag<E>(U[2 * ks], (2 * ks + 1 < CT) ? U[2 * ks + 1] : zero4());
@@ -894,20 +886,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     Frag<E> Ud[CKS];
 #pragma unroll
     for (int ks = 0; ks < CKS; ++ks) Ud[ks] = acc_to_frag<E>(U[2 * ks], (2 * ks + 1 < CT) ? U[2 * ks + 1] : zero4());
-    // the intra-chunk output O^T += U^T P^T first, so that O is final while
-    // the state update S <- exp(g_L) S + K^T Ud runs (DT independent
-    // accumulators per step)
-#pragma unroll
-    for (int ks = 0; ks < CKS; ++ks) {
-      if constexpr (SV) break;
-      Frag<E> pa[CT];
-#pragma unroll
-      for (int nt = 0; nt < CT; ++nt)
-        if (!causal_zero(nt, ks)) pa[nt] = sm.pf[par][(nt * CKS + ks) * 64 + lane];
-#pragma unroll
-      for (int nt = 0; nt < CT; ++nt)
-        if (!causal_zero(nt, ks)) O[nt] = mma(Uk[ks], pa[nt], O[nt]);
-    }
+    // S <- exp(g_L) S + K^T Ud (DT independent accumulators per step)
     const float gam = sm.dtab[par][2 * C];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) S[dt] *= gam;
@@ -918,6 +897,22 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       for (int dt = 0; dt < DT; ++dt) ka[dt] = sm.kt[par][(dt * CKS + ks) * 64 + lane];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) S[dt] = mma(ka[dt], Ud[ks], S[dt]);
+    }
+    // the inter-chunk output takes exp(g_r); then O^T += U^T P^T,
+    // P = (Q K^T * Dincl), while the state update's results land
+    if constexpr (!SV) {
+#pragma unroll
+      for (int t = 0; t < CT; ++t) O[t] *= ea[16 * t + l16];
+#pragma unroll
+      for (int ks = 0; ks < CKS; ++ks) {
+        Frag<E> pa[CT];
+#pragma unroll
+        for (int nt = 0; nt < CT; ++nt)
+          if (!causal_zero(nt, ks)) pa[nt] = sm.pf[par][(nt * CKS + ks) * 64 + lane];
+#pragma unroll
+        for (int nt = 0; nt < CT; ++nt)
+          if (!causal_zero(nt, ks)) O[nt] = mma(Uk[ks], pa[nt], O[nt]);
+      }
     }
     if constexpr (!SV && STAGE_O) {
       // bf16 outputs: row-major (16 columns, 32 bytes a row) into this

@@ -64,7 +64,7 @@ struct DScanSmem {
   E dor[2][C * G::BV];               // dL/do rows, this block's columns
   float dtab[2][2 * C + 4] __attribute__((aligned(16)));
   // per chunk parity and scan wave: dS_L (D rows) then dU (C rows) of the
-  // wave's 16 columns, row-major with stride 16 + VE, for the loaders' stores
+  // wave's 16 columns, row-major with stride 16 + VE, for the store waves
   E stage[2][G::NS][(D + C) * (16 + 16 / sizeof(E))] __attribute__((aligned(16)));
 };
 
@@ -157,27 +157,30 @@ __global__ __launch_bounds__(kDScanBlock) void gdn_kb_dstate(const PrefillArgs a
   auto dscan_chunk = [&](int c) __attribute__((always_inline)) {
     const int par = c & 1;
     // dS is dL/d(state at chunk c's end); it and dU go to the staging area,
-    // which the loaders store after the barrier
+    // which the store waves store after the barrier
     E* stg = sm.stage[par][slice];
+    auto stage4 = [&](int row0, const f32x4& v) __attribute__((always_inline)) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) stg[(16 * dt + 4 * quad + i) * SLD + l16] = to_e<E>(dS[dt][i]);
-    }
+      for (int i = 0; i < 4; ++i) stg[(row0 + 4 * quad + i) * SLD + l16] = to_e<E>(v[i]);
+    };
     Frag<E> dSf[DKS];
 #pragma unroll
     for (int ks = 0; ks < DKS; ++ks) dSf[ks] = acc_to_frag<E>(dS[2 * ks], (2 * ks + 1 < DT) ? dS[2 * ks + 1] : zero4());
     const float* ea = sm.dtab[par];
     const float* ed = sm.dtab[par] + C;
-    // dU = diag(ed) K dS_L + P^T dO
-    f32x4 dU[CT];
+    // Only K dS_L -> dU -> W^T dU lies on the path from one chunk's dS to
+    // the previous one's; P^T dO and Q^T diag(ea) dO, which do not read dS,
+    // run while K dS_L's results land.
+    //   KdS = K dS_L
+    f32x4 KdS[CT];
 #pragma unroll
     for (int t = 0; t < CT; ++t) {
-      dU[t] = zero4();
+      KdS[t] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < DKS; ++ks) dU[t] = mma(sm.kf[par][(t * DKS + ks) * 64 + lane], dSf[ks], dU[t]);
-      dU[t] *= *reinterpret_cast<const f32x4*>(&ed[16 * t + 4 * quad]);
+      for (int ks = 0; ks < DKS; ++ks) KdS[t] = mma(sm.kf[par][(t * DKS + ks) * 64 + lane], dSf[ks], KdS[t]);
     }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) stage4(16 * dt, dS[dt]);
     // dL/do fragments (k = token r, column = state column), plain and
     // scaled by exp(g_r)
     Frag<E> dOf[CKS], gOf[CKS];
@@ -191,32 +194,38 @@ __global__ __launch_bounds__(kDScanBlock) void gdn_kb_dstate(const PrefillArgs a
         gOf[s][e] = to_e<E>((r < C) ? to_f(x) * ea[r] : 0.f);
       }
     }
+    //   PdO = P^T dO
+    f32x4 dU[CT];
 #pragma unroll
     for (int t = 0; t < CT; ++t) {
+      dU[t] = zero4();
 #pragma unroll
       for (int s = 0; s < CKS; ++s)
         if (32 * s + 31 >= 16 * t) dU[t] = mma(sm.pt[par][(t * CKS + s) * 64 + lane], dOf[s], dU[t]);
     }
-#pragma unroll
-    for (int t = 0; t < CT; ++t) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) stg[(D + 16 * t + 4 * quad + i) * SLD + l16] = to_e<E>(dU[t][i]);
-    }
-    Frag<E> nUf[CKS];
-#pragma unroll
-    for (int s = 0; s < CKS; ++s) nUf[s] = acc_to_frag<E>(-dU[2 * s], (2 * s + 1 < CT) ? -dU[2 * s + 1] : zero4());
-    // dS0 = exp(g_L) dS_L + Q^T diag(ea) dO - W^T dU
+    //   dS0 = exp(g_L) dS_L + Q^T diag(ea) dO - W^T dU: the first two terms
     const float gam = sm.dtab[par][2 * C];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) dS[dt] *= gam;
 #pragma unroll
     for (int s = 0; s < CKS; ++s) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        dS[dt] = mma(sm.qt[par][(dt * CKS + s) * 64 + lane], gOf[s], dS[dt]);
-        dS[dt] = mma(sm.wt[par][(dt * CKS + s) * 64 + lane], nUf[s], dS[dt]);
-      }
+      for (int dt = 0; dt < DT; ++dt) dS[dt] = mma(sm.qt[par][(dt * CKS + s) * 64 + lane], gOf[s], dS[dt]);
     }
+    // dU = diag(ed) K dS_L + P^T dO
+#pragma unroll
+    for (int t = 0; t < CT; ++t) dU[t] += KdS[t] * *reinterpret_cast<const f32x4*>(&ed[16 * t + 4 * quad]);
+    Frag<E> nUf[CKS];
+#pragma unroll
+    for (int s = 0; s < CKS; ++s) nUf[s] = acc_to_frag<E>(-dU[2 * s], (2 * s + 1 < CT) ? -dU[2 * s + 1] : zero4());
+    //   ... - W^T dU
+#pragma unroll
+    for (int s = 0; s < CKS; ++s) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dS[dt] = mma(sm.wt[par][(dt * CKS + s) * 64 + lane], nUf[s], dS[dt]);
+    }
+#pragma unroll
+    for (int t = 0; t < CT; ++t) stage4(D + 16 * t, dU[t]);
   };
 
   auto state_index = [&](int dt, int i) {

@@ -66,6 +66,7 @@ struct DScanSmem {
   // per chunk parity and scan wave: dS_L (D rows) then dU (C rows) of the
   // wave's 16 columns, row-major with stride 16 + VE, for the store waves
   E stage[2][G::NS][(D + C) * (16 + 16 / sizeof(E))] __attribute__((aligned(16)));
+  float touch[G::NS][64];            // landing place of the L2 warm-up loads
 };
 
 template <typename E, int D, int C>
@@ -151,6 +152,44 @@ __global__ __launch_bounds__(kDScanBlock) void gdn_kb_dstate(const PrefillArgs a
       if (row < D) *reinterpret_cast<Vec*>(&dslg[row * D + 16 * sl + cc]) = v;
       else *reinterpret_cast<Vec*>(&dug[(row - D) * D + 16 * sl + cc]) = v;
     }
+  };
+
+  // L2 warm-up, issued by the store waves after their stores (they load
+  // nothing into registers, so nothing ever waits on these) three chunks
+  // ahead in the reverse walk: one 4-byte load per 128-byte line of the
+  // chunk's streamed operands, each line touched by one of the workgroups
+  // that read it (per V head: P^T, W^T and the row-factor table, shared by
+  // the NCB column blocks; per QK head: K and Q^T, shared by the group's V
+  // heads too), plus this workgroup's own dL/do rows
+  constexpr int LV = (B_PT + B_WT + B_D + 127) / 128;              // lines per (chunk, V head)
+  constexpr int LQ = (B_KF + B_QT + 127) / 128;                    // lines per (chunk, QK head)
+  const int gi = hv % a.group;
+  const int nv = (LV - cb + G::NCB - 1) / G::NCB;
+  const int qs = gi * G::NCB + cb, qstride = a.group * G::NCB;
+  const int nq = qs < LQ ? (LQ - qs + qstride - 1) / qstride : 0;
+  auto line_addr = [&](int x, int t) -> const char* {
+    if (t < nv) {
+      const int o = 128 * (cb + G::NCB * t);
+      return o < B_PT ? static_cast<const char*>(a.pt) + ((int64_t)x * a.h_v + hv) * B_PT + o
+           : o < B_PT + B_WT ? static_cast<const char*>(a.wt) + ((int64_t)x * a.h_v + hv) * B_WT + (o - B_PT)
+           : reinterpret_cast<const char*>(a.dtab + ((int64_t)x * a.h_v + hv) * (2 * C + 4)) +
+                 min(o - B_PT - B_WT, B_D - 4);
+    }
+    t -= nv;
+    if (t < nq) {
+      const int o = 128 * (qs + qstride * t);
+      return o < B_KF ? static_cast<const char*>(a.k_frag) + ((int64_t)x * a.h_qk + hq) * B_KF + o
+           : static_cast<const char*>(a.q_t) + ((int64_t)x * a.h_qk + hq) * B_QT + min(o - B_KF, B_QT - 4);
+    }
+    t -= nq;
+    const int i = min(t, chunk_len(x) - 1);
+    return static_cast<const char*>(a.d_o) + (((int64_t)(chunk_start(x) + i) * a.h_v + hv) * D + col0) * ESZ;
+  };
+  auto warm = [&](int x) __attribute__((always_inline)) {
+    if (x < c0) return;
+    const int total = nv + nq + C;
+    for (int t = 64 * sw + lane; t < total; t += 64 * NS)
+      __builtin_amdgcn_global_load_lds(line_addr(x, t), (lds_ptr_t)sm.touch[sw], 4, 0, 0);
   };
 
   f32x4 dS[DT];
@@ -260,9 +299,12 @@ __global__ __launch_bounds__(kDScanBlock) void gdn_kb_dstate(const PrefillArgs a
         __syncthreads();
       }
     } else {
+      warm(c1 - 2);
+      warm(c1 - 3);
       lds_barrier();
       for (int c = c1 - 1; c >= c0; --c) {
         store_staged(c + 1);
+        warm(c - 3);
         lds_barrier();
       }
       store_staged(c0);

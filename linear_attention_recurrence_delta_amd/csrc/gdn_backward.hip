@@ -52,7 +52,7 @@ namespace {
 // barrier, so that no wave waits for those stores. After the first chunk
 // dS is dL/dS0 of the sequence.
 // --------------------------------------------------------------------------
-constexpr int kDScanBlock = 384;
+constexpr int kDScanBlock = 512;
 
 template <typename E, int D, int C>
 struct DScanSmem {

@@ -433,12 +433,22 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
   auto frag_row = [&](const E* m, int ld, int row0, int s, int kext) __attribute__((always_inline)) {
     return load_frag<E>(m + (row0 + l16) * ld + 32 * s, quad, kext - 32 * s);
   };
+  // (a column fragment is read element by element: through an LDS-space
+  // pointer, so its addresses are 32-bit, and unconditionally, with rows
+  // past kext clamped and then zeroed, unless the whole step lies inside)
   auto frag_col = [&](const E* m, int ld, int col0, int s, int kext) __attribute__((always_inline)) {
+    typedef const __attribute__((address_space(3))) E* LdsPtr;
+    const LdsPtr ml = (LdsPtr)m;
     Frag<E> f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int k = frag_k(s, quad, e);
-      f[e] = (k < kext) ? m[k * ld + col0 + l16] : to_e<E>(0.f);
+      if (32 * s + 32 <= kext) {
+        f[e] = ml[k * ld + col0 + l16];
+      } else {
+        const E x = ml[min(k, kext - 1) * ld + col0 + l16];
+        f[e] = (k < kext) ? x : to_e<E>(0.f);
+      }
     }
     return f;
   };

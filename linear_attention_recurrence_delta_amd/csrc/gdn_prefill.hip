@@ -819,11 +819,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
 
   auto scan_chunk = [&](int c) __attribute__((always_inline)) {
     const int start = chunk_start(c), len = chunk_len(c), par = c & 1;
-    if constexpr (SV_STAGE) {
-      // backward pass: the state at the chunk's start, rounded as the
-      // products below use it, staged for the slice's Ut wave
-      stage_tiles_rows<E, DT>(S, sv_area(par, slice), lane);
-    } else if constexpr (SV) {
+    if constexpr (SV && !SV_STAGE) {
       // (the same, stored row-major through the unused Q fragment buffers)
       store_tiles_rows<E, DT>(S, reinterpret_cast<E*>(sm.qf) + slice * stage_elems<E>(),
                               static_cast<E*>(a.sc) + ((int64_t)c * a.h_v + hv) * D * D + col0 + 16 * slice, D, lane);
@@ -897,6 +893,20 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       for (int dt = 0; dt < DT; ++dt) ka[dt] = sm.kt[par][(dt * CKS + ks) * 64 + lane];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) S[dt] = mma(ka[dt], Ud[ks], S[dt]);
+    }
+    if constexpr (SV_STAGE) {
+      // backward pass: the state at the chunk's start, rounded as the
+      // products above used it (the elements of Sf), staged for the slice's
+      // Ut wave; written after the step's operand reads have been issued,
+      // since one wave's LDS operations complete in order
+      __builtin_amdgcn_sched_barrier(0);
+      E* ar = sv_area(par, slice);
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (2 * ks + (e >> 2) < DT) ar[frag_k(ks, quad, e) * SLD + l16] = Sf[ks][e];   // (rows < D only)
+      }
     }
     // the inter-chunk output takes exp(g_r); then O^T += U^T P^T,
     // P = (Q K^T * Dincl), while the state update's results land

@@ -49,8 +49,9 @@ namespace {
 // and dU (rounded to the input dtype, as the gradient kernel's products use
 // them) in an LDS staging area, double-buffered by chunk parity, and store
 // waves write the previous chunk's as 16-byte row segments after each
-// barrier, so that no wave waits for those stores. After the first chunk
-// dS is dL/dS0 of the sequence.
+// barrier, so that no wave waits for those stores; the store waves also
+// warm L2 three chunks ahead. After the first chunk dS is dL/dS0 of the
+// sequence.
 // --------------------------------------------------------------------------
 constexpr int kDScanBlock = 512;
 

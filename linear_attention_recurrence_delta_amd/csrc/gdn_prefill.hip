@@ -631,16 +631,19 @@ __global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs 
 //                                                   the B fragments here)
 //       O^T += U^T P^T, P = (Q K^T * Dincl)         (U's tiles are the A fragments)
 //       S    = exp(g_L) S + K^T (exp(g_L - g) * U)
-//     and store the chunk's outputs for their columns;
-//   Ut waves (one per slice), meanwhile, form chunk c+1's Ut tiles
-//     Tinv diag(b) V in LDS;
+//     and leave the chunk's (bf16) outputs in their slice's Ut slot: the
+//     scan waves touch no global memory per chunk;
+//   Ut waves (one per slice), meanwhile, read chunk c-1's outputs from their
+//     slot, form chunk c+1's Ut tiles Tinv diag(b) V there, store the
+//     outputs, and warm L2 for chunk c+3;
 //   loader waves copy chunk c+1's K^T, W, Q and P fragments and row-factor
 //     table, and chunk c+2's Tinv diag(b) fragments and V columns, from
 //     global memory straight into LDS (direct global-to-LDS loads, 1 KB per
 //     wave instruction, no register staging) and wait for them before the
 //     barrier.
 // Every LDS region is double-buffered by chunk parity; between two barriers
-// a slot is either only read or only written.
+// a slot is either only read or only written, except a Ut slot, which its
+// one Ut wave reads and then writes, in program order.
 // --------------------------------------------------------------------------
 constexpr int kScanBlock = 768;
 

@@ -334,6 +334,7 @@ gdn_status_t gdn_chunk_bwd_stages(const gdn_dims_t* dims, const void* q, const v
   a.q_frag = ws + F.q_frag;
   a.pmask = ws + F.pmask;
   a.dtab = reinterpret_cast<float*>(ws + F.dtab);
+  a.backward = 1;
   a.k_frag = ws + L.k_frag;
   a.q_t = ws + L.q_t;
   a.kq = ws + L.kq;

@@ -58,6 +58,9 @@ struct PrefillArgs {
   int32_t group;            // HV / HQ
   int32_t prep;             // 1: raw q, k and gate logits (fused input preparation)
   int32_t no_delta;         // 1: gate-only update S = a S + b k v^T
+  int32_t backward;         // 1: kernels 1-3 in their backward-pass modes (the fields
+                            //    marked backward pass only are set); chosen by this flag,
+                            //    not by which workspace pointers happen to be set
 };
 
 struct DecodeArgs {

@@ -1122,17 +1122,17 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
   const unsigned scan_groups = (unsigned)(a.num_seqs * a.h_v * G::NCB);
   for (int stage = first; stage <= last; ++stage) {
     switch (stage) {
-      // the backward pass (backward workspace pointers set) takes no flags
+      // the backward pass (a.backward) takes no flags
       case 1: {
         const dim3 g(nc * (unsigned)a.h_qk);
-        if (a.k_frag) gdn_k1_chunk_prep<E, D, C, false, true><<<g, dim3(kBlock), 0, s>>>(a);
+        if (a.backward) gdn_k1_chunk_prep<E, D, C, false, true><<<g, dim3(kBlock), 0, s>>>(a);
         else if (a.prep) gdn_k1_chunk_prep<E, D, C, true, false><<<g, dim3(kBlock), 0, s>>>(a);
         else gdn_k1_chunk_prep<E, D, C, false, false><<<g, dim3(kBlock), 0, s>>>(a);
         break;
       }
       case 2: {
         const dim3 g(nc * (unsigned)a.h_v);
-        if (a.pt) {
+        if (a.backward) {
           gdn_k2_inverse_w<E, D, C, false, false, true><<<g, dim3(kBlock), 0, s>>>(a);
         } else if (a.prep) {
           if (a.no_delta) gdn_k2_inverse_w<E, D, C, true, true, false><<<g, dim3(kBlock), 0, s>>>(a);
@@ -1144,7 +1144,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
         break;
       }
       case 3:
-        if (a.sc) gdn_k3_scan<E, D, C, false, true><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a);
+        if (a.backward) gdn_k3_scan<E, D, C, false, true><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a);
         else if (a.no_delta) gdn_k3_scan<E, D, C, true, false><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a);
         else gdn_k3_scan<E, D, C, false, false><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a);
         break;

@@ -39,6 +39,27 @@
 namespace gdn {
 
 namespace {
+// Raw buffer accesses for the gradient kernel's per-element global reads and
+// writes: the base sits in a resource descriptor (uniform), the lane offset
+// is a 32-bit byte count, so no 64-bit address arithmetic is needed per
+// element. Accesses at or past `bytes` are dropped (reads return zero).
+// Descriptor word 3 is gfx9's raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+template <typename E>
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, E x) {
+  if constexpr (sizeof(E) == 2) __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r, (int)byte_off, 0, 0);
+  else __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, (int)byte_off, 0, 0);
+}
+template <typename E>
+__device__ __forceinline__ E buf_load(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  if constexpr (sizeof(E) == 2) return __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b16(r, (int)byte_off, 0, 0));
+  else return __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0));
+}
+}  // namespace
+
+namespace {
 
 // --------------------------------------------------------------------------
 // Reverse state scan: one workgroup per (sequence, V head, block of BV state
@@ -728,8 +749,10 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     __syncthreads();
     // dK += (B + B^T) K; dV = diag(b) Tinv^T dU and its b term (v read from
     // global); Tinv^T dW into dK and the b, g terms of W
-    E* dvg = static_cast<E*>(a.dv) + ((int64_t)start * a.h_v + hv) * D;
-    const E* vg = static_cast<const E*>(a.v) + ((int64_t)start * a.h_v + hv) * D;
+    // this chunk's rows of dv and v for this V head, as raw buffers
+    const uint32_t v_bytes = (uint32_t)(len * a.h_v * D) * (uint32_t)sizeof(E);
+    const auto dvb = raw_rsrc(static_cast<E*>(a.dv) + ((int64_t)start * a.h_v + hv) * D, v_bytes);
+    const auto vb_ = raw_rsrc(static_cast<const E*>(a.v) + ((int64_t)start * a.h_v + hv) * D, v_bytes);
     f32x4 rdb_acc[CT], rdg_acc[CT];
 #pragma unroll
     for (int rt = 0; rt < CT; ++rt) { rdb_acc[rt] = zero4(); rdg_acc[rt] = zero4(); }
@@ -761,10 +784,10 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * rt + 4 * quad + e;
           const float bgr = sm.b[r] * sm.ea[r];
-          const int off = r * a.h_v * D + d;
-          const float vl = to_f(vg[min(r, len - 1) * a.h_v * D + d]);    // issued unconditionally
+          const uint32_t off = (uint32_t)(r * a.h_v * D + d) * (uint32_t)sizeof(E);
+          const float vl = to_f(buf_load<E>(vb_, (uint32_t)(min(r, len - 1) * a.h_v * D + d) * (uint32_t)sizeof(E)));    // issued unconditionally
           const float vv = (r < len) ? vl : 0.f;
-          if (r < len) dvg[off] = to_e<E>(sm.b[r] * au[e]);
+          if (r < len) buf_store<E>(dvb, off, to_e<E>(sm.b[r] * au[e]));
           dK[u][e] += bgr * aw[e];
           const float rk = aw[e] * kv[e];
           rdb_acc[rt][e] += au[e] * vv + sm.ea[r] * rk;
@@ -797,8 +820,10 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     }
   }
 
-  E* dqg = static_cast<E*>(a.dq) + ((int64_t)start * a.h_qk + hq) * D;
-  E* dkg = static_cast<E*>(a.dk) + ((int64_t)start * a.h_qk + hq) * D;
+  // this chunk's rows of dq and dk for this QK head, as raw buffers
+  const uint32_t qk_bytes = (uint32_t)(len * a.h_qk * D) * (uint32_t)sizeof(E);
+  const auto dqb = raw_rsrc(static_cast<E*>(a.dq) + ((int64_t)start * a.h_qk + hq) * D, qk_bytes);
+  const auto dkb = raw_rsrc(static_cast<E*>(a.dk) + ((int64_t)start * a.h_qk + hq) * D, qk_bytes);
 #pragma unroll
   for (int j = 0; j < DPW; ++j) {
     const int dt = wave + NW * j;
@@ -810,9 +835,9 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rt + 4 * quad + e;
         if (r < len) {
-          const int o = r * a.h_qk * D + 16 * dt + l16;
-          dqg[o] = to_e<E>(dQ[u][e]);
-          dkg[o] = to_e<E>(dK[u][e]);
+          const uint32_t o = (uint32_t)(r * a.h_qk * D + 16 * dt + l16) * (uint32_t)sizeof(E);
+          buf_store<E>(dqb, o, to_e<E>(dQ[u][e]));
+          buf_store<E>(dkb, o, to_e<E>(dK[u][e]));
         }
       }
     }

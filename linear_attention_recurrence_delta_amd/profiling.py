@@ -148,7 +148,7 @@ def main():
         print(traffic_table(args.traffic_json, args.bench_json))
         return
     if args.cmd == "stats":
-        print(f"# {args.title}\n\nCommand (GPU box, repo root):\n\n    {args.command}\n")
+        print(f"# {args.title}\n\nCommand (MI355X, repo root):\n\n    {args.command}\n")
         print(kernel_stats(args.csv))
     else:
         res = traffic(args.fetch, args.write, args.copy_fetch, args.copy_write, args.copy_bytes)

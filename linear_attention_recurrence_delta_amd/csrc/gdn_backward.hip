@@ -750,7 +750,8 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     // dK += (B + B^T) K; dV = diag(b) Tinv^T dU and its b term (v read from
     // global); Tinv^T dW into dK and the b, g terms of W
     // this chunk's rows of dv and v for this V head, as raw buffers
-    const uint32_t v_bytes = (uint32_t)(len * a.h_v * D) * (uint32_t)sizeof(E);
+    const uint32_t v_row = (uint32_t)(a.h_v * D);    // elements between consecutive tokens
+    const uint32_t v_bytes = (uint32_t)len * v_row * (uint32_t)sizeof(E);
     const auto dvb = raw_rsrc(static_cast<E*>(a.dv) + ((int64_t)start * a.h_v + hv) * D, v_bytes);
     const auto vb_ = raw_rsrc(static_cast<const E*>(a.v) + ((int64_t)start * a.h_v + hv) * D, v_bytes);
     f32x4 rdb_acc[CT], rdg_acc[CT];
@@ -768,6 +769,8 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         wb[s] = frag_col(sm.r2, KLD, 16 * dt, s, C);
       }
       const int d = 16 * dt + l16;
+      // byte offset of (row 4 quad, column d); each row adds the uniform row stride
+      const uint32_t lane_off = ((uint32_t)(4 * quad) * v_row + (uint32_t)d) * (uint32_t)sizeof(E);
 #pragma unroll
       for (int rt = 0; rt < CT; ++rt) {
         const int u = j * CT + rt;
@@ -784,10 +787,10 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * rt + 4 * quad + e;
           const float bgr = sm.b[r] * sm.ea[r];
-          const uint32_t off = (uint32_t)(r * a.h_v * D + d) * (uint32_t)sizeof(E);
-          const float vl = to_f(buf_load<E>(vb_, (uint32_t)(min(r, len - 1) * a.h_v * D + d) * (uint32_t)sizeof(E)));    // issued unconditionally
-          const float vv = (r < len) ? vl : 0.f;
-          if (r < len) buf_store<E>(dvb, off, to_e<E>(sm.b[r] * au[e]));
+          // rows at or past len fall outside both descriptors: v reads as 0, the dv store is dropped
+          const uint32_t off = lane_off + (uint32_t)(16 * rt + e) * v_row * (uint32_t)sizeof(E);
+          const float vv = to_f(buf_load<E>(vb_, off));
+          buf_store<E>(dvb, off, to_e<E>(sm.b[r] * au[e]));
           dK[u][e] += bgr * aw[e];
           const float rk = aw[e] * kv[e];
           rdb_acc[rt][e] += au[e] * vv + sm.ea[r] * rk;
@@ -821,7 +824,8 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
   }
 
   // this chunk's rows of dq and dk for this QK head, as raw buffers
-  const uint32_t qk_bytes = (uint32_t)(len * a.h_qk * D) * (uint32_t)sizeof(E);
+  const uint32_t qk_row = (uint32_t)(a.h_qk * D);
+  const uint32_t qk_bytes = (uint32_t)len * qk_row * (uint32_t)sizeof(E);
   const auto dqb = raw_rsrc(static_cast<E*>(a.dq) + ((int64_t)start * a.h_qk + hq) * D, qk_bytes);
   const auto dkb = raw_rsrc(static_cast<E*>(a.dk) + ((int64_t)start * a.h_qk + hq) * D, qk_bytes);
 #pragma unroll
@@ -833,12 +837,11 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
       const int u = j * CT + rt;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rt + 4 * quad + e;
-        if (r < len) {
-          const uint32_t o = (uint32_t)(r * a.h_qk * D + 16 * dt + l16) * (uint32_t)sizeof(E);
-          buf_store<E>(dqb, o, to_e<E>(dQ[u][e]));
-          buf_store<E>(dkb, o, to_e<E>(dK[u][e]));
-        }
+        // rows at or past len fall outside both descriptors and are dropped
+        const uint32_t o = ((uint32_t)(4 * quad) * qk_row + (uint32_t)(16 * dt + l16)) * (uint32_t)sizeof(E) +
+                           (uint32_t)(16 * rt + e) * qk_row * (uint32_t)sizeof(E);
+        buf_store<E>(dqb, o, to_e<E>(dQ[u][e]));
+        buf_store<E>(dkb, o, to_e<E>(dK[u][e]));
       }
     }
   }

@@ -498,6 +498,8 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     // this loop (they would stay live across it and spill); recomputing
     // them is a few ALU operations
     asm volatile("" : "+v"(tid), "+v"(lane), "+v"(quad), "+v"(l16));
+    // restore their ranges, so that index products take 24-bit multiplies
+    tid &= kGradBlock - 1; lane &= 63; quad &= 3; l16 &= 15;
     __syncthreads();                   // the previous V head's LDS reads are done
     if (tid < C) {
       sm.g[tid] = a.gate_prefix[ch * C + tid];

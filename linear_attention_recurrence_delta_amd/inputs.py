@@ -168,6 +168,54 @@ def make_decode_raw(seed, batch, steps, h_qk, h_v, d, dtype="bf16"):
     )
 
 
+def make_prefill_wide(seed, seq_lens, h_qk, h_v, d, dtype="bf16", kind="beta_to_2"):
+    """Prefill inputs outside the main recipe's ranges, for the method's
+    edge cases (same keys and shapes as make_prefill, nonzero initial
+    states N(0, 0.02^2)). Draw order: q, k, v, log_alpha, beta, init, then
+    the kind's extra draws.
+
+    kind "beta_to_2":  beta = 1 + U(0, 1), every seventh (token, head) set
+                       to exactly 2 (the write strength above 1; with unit
+                       keys the transition still does not expand).
+    kind "deep_decay": log_alpha ~ U(-30, 0) (alpha down to about 1e-13),
+                       every fifth (token, head) exactly -30.
+    kind "raw_qk":     q and k not normalised: unit vectors scaled per
+                       (token, head) by U(0.7, 1.3) (k) and exp(N(0, 0.5^2))
+                       (q); beta and log_alpha as in the main recipe.
+    """
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in seq_lens]
+    T = int(sum(lens))
+    tdt = _DTYPES[dtype]
+    q = _unit_rows(rng.standard_normal((T, h_qk, d)))
+    k = _unit_rows(rng.standard_normal((T, h_qk, d)))
+    v = rng.standard_normal((T, h_v, d))
+    la = -_softplus(rng.normal(-2.0, 1.0, (T, h_v)))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((T, h_v))))
+    init_state = rng.normal(0.0, 0.02, (len(lens), h_v, d, d)).astype(np.float32)
+    if kind == "beta_to_2":
+        beta = 1.0 + rng.uniform(0.0, 1.0, (T, h_v))
+        beta.reshape(-1)[::7] = 2.0
+    elif kind == "deep_decay":
+        la = rng.uniform(-30.0, 0.0, (T, h_v))
+        la.reshape(-1)[::5] = -30.0
+    elif kind == "raw_qk":
+        k = k * rng.uniform(0.7, 1.3, (T, h_qk, 1))
+        q = q * np.exp(rng.normal(0.0, 0.5, (T, h_qk, 1)))
+    else:
+        raise ValueError(kind)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return dict(
+        q=torch.from_numpy(q).to(tdt),
+        k=torch.from_numpy(k).to(tdt),
+        v=torch.from_numpy(v).to(tdt),
+        log_alpha=torch.from_numpy(la.astype(np.float32)),
+        beta=torch.from_numpy(beta.astype(np.float32)),
+        init_state=torch.from_numpy(init_state),
+        cu_seqlens=torch.from_numpy(cu),
+    )
+
+
 # The five workloads (sizes as named in the docs). Each entry is the
 # keyword arguments of make_prefill / make_decode.
 WORKLOADS = {

@@ -137,6 +137,40 @@ def test_prefill_reads_only_what_it_writes(chunk):
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.parametrize("dtype,chunk", [("bf16", 64), ("bf16", 16), ("f32", 16)])
+@pytest.mark.parametrize("kind", ["beta_to_2", "deep_decay", "raw_qk"])
+def test_prefill_wide_input_ranges(kind, dtype, chunk):
+    # the method's ranges beyond the main recipe: write strength in (1, 2],
+    # forget gates down to exp(-30), keys and queries not of unit length
+    lens = [300, 1, 129]
+    say(f"prefill {kind} {lens} d=128 C={chunk} {dtype}")
+    inp = I.make_prefill_wide(60 + chunk, lens, 2, 6, 128, dtype, kind)
+    o, fin = run_gpu(inp, chunk)
+    want_o, want_f = O.recurrent_form1(**oracle_args(inp))
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    rel_o, mx_o = check(o, want_o, tdt, "o")
+    rel_f, mx_f = check(fin, want_f, tdt, "final")
+    print(f"  o rel-L2 {rel_o:.2e} max-abs {mx_o:.2e}; final rel-L2 {rel_f:.2e} max-abs {mx_f:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("kind", ["beta_to_2", "deep_decay", "raw_qk"])
+def test_decode_wide_input_ranges(kind):
+    # the same ranges through the decode step: 130 sequences, one token each,
+    # three successive steps
+    say(f"decode {kind} N=130 d=128 bf16 x3 steps")
+    steps = [I.make_prefill_wide(70 + t, [130], 2, 6, 128, "bf16", kind) for t in range(3)]
+    state0 = I.make_decode(73, 130, 1, 2, 6, 128, "bf16")["state0"]
+    state = state0.to(DEV)
+    ref = np64(state0)
+    for t, inp in enumerate(steps):
+        args = [inp[x] for x in ("q", "k", "v", "log_alpha", "beta")]
+        o = gdn.gdn_decode_step(*[a.to(DEV) for a in args], state)
+        torch.cuda.synchronize()
+        want_o, ref = O.decode_step(ref, *[np64(a) for a in args])
+        check(o, want_o, torch.bfloat16, f"o step {t}")
+    check(state, ref, torch.bfloat16, "state after 3 steps")
+
+
 def test_zero_tokens():
     say("T=0, two empty sequences")
     inp = random_prefill(8, [0, 0], 1, 3, 128, "bf16")

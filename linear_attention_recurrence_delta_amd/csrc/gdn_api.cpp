@@ -3,9 +3,11 @@
 // until every argument has been checked.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <string>
+#include <vector>
 
 #include "gdn.h"
 #include "gdn_internal.h"
@@ -59,7 +61,8 @@ gdn_status_t check_dims(const gdn_dims_t* d, bool decode) {
     if (d->chunk < 1) return fail(GDN_ERROR_INVALID_VALUE, "chunk must be >= 1");
     if (d->chunk != 16 && d->chunk != 64) return fail(GDN_ERROR_NOT_SUPPORTED, "chunk %d not supported (16 or 64)", d->chunk);
     if (!gdn::prefill_supported(d->dtype, d->dk, d->chunk))
-      return fail(GDN_ERROR_NOT_SUPPORTED, "prefill with fp32 inputs at head dim %d needs chunk 16", d->dk);
+      return fail(GDN_ERROR_NOT_SUPPORTED, "no prefill instance for dtype %d, head dim %d, chunk %d", d->dtype,
+                  d->dk, d->chunk);
   }
   return GDN_SUCCESS;
 }
@@ -133,9 +136,58 @@ BwdLayout compute_bwd_layout(const gdn_dims_t& d) {
   return L;
 }
 
-gdn_status_t launch_status(hipError_t e, const char* what) {
+// Opt-in debug checks, read from the environment at every call (a value
+// other than empty or "0" turns them on):
+//   GDN_DEBUG       prefill entry points copy cu_seqlens to the host (on
+//                   the call's stream, then wait for it) and reject a table
+//                   that is not 0 = c_0 <= c_1 <= ... <= c_N = T with
+//                   GDN_ERROR_INVALID_VALUE before enqueueing anything;
+//   GDN_DEBUG_SYNC  every entry point waits for its stream after enqueueing
+//                   and reports a kernel that failed or faulted as
+//                   GDN_ERROR_HIP, naming the entry point.
+// Both synchronise with the host, which the calls otherwise never do.
+bool env_on(const char* name) {
+  const char* v = getenv(name);
+  return v && *v && strcmp(v, "0") != 0;
+}
+
+gdn_status_t check_cu_seqlens_contents(const int32_t* h, int64_t n, int64_t total) {
+  if (h[0] != 0) return fail(GDN_ERROR_INVALID_VALUE, "GDN_DEBUG: cu_seqlens[0] = %d, must be 0", h[0]);
+  for (int64_t i = 0; i < n; ++i)
+    if (h[i + 1] < h[i])
+      return fail(GDN_ERROR_INVALID_VALUE, "GDN_DEBUG: cu_seqlens decreases at %lld (%d > %d)",
+                  (long long)(i + 1), h[i], h[i + 1]);
+  if (h[n] != total)
+    return fail(GDN_ERROR_INVALID_VALUE, "GDN_DEBUG: cu_seqlens[%lld] = %d, must equal total_tokens %lld",
+                (long long)n, h[n], (long long)total);
+  return GDN_SUCCESS;
+}
+
+gdn_status_t debug_check_cu_seqlens(const int32_t* cu, int64_t n, int64_t total, hipStream_t stream) {
+  if (!cu || !env_on("GDN_DEBUG")) return GDN_SUCCESS;
+  std::vector<int32_t> h((size_t)n + 1);
+  hipError_t e = hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(GDN_ERROR_HIP, "GDN_DEBUG: reading cu_seqlens: %s", hipGetErrorString(e));
+  return check_cu_seqlens_contents(h.data(), n, total);
+}
+
+gdn_status_t launch_status(hipError_t e, const char* what, hipStream_t stream) {
   if (e != hipSuccess) return fail(GDN_ERROR_HIP, "%s: %s", what, hipGetErrorString(e));
+  if (env_on("GDN_DEBUG_SYNC")) {
+    e = hipStreamSynchronize(stream);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return fail(GDN_ERROR_HIP, "GDN_DEBUG_SYNC: %s: %s", what, hipGetErrorString(e));
+  }
   return ok();
+}
+
+// The backward pass's own support check, after check_dims.
+gdn_status_t check_backward(const gdn_dims_t& d) {
+  if (d.flags) return fail(GDN_ERROR_NOT_SUPPORTED, "the backward pass takes no flags (got 0x%x)", d.flags);
+  if (!gdn::backward_supported(d.dtype, d.dk, d.chunk))
+    return fail(GDN_ERROR_NOT_SUPPORTED, "the backward pass with fp32 inputs at head dim %d needs chunk 16", d.dk);
+  return GDN_SUCCESS;
 }
 
 }  // namespace
@@ -210,6 +262,8 @@ gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims, const void* q, const v
   if (workspace_bytes < L.v.total)
     return fail(GDN_ERROR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, L.v.total);
 
+  st = debug_check_cu_seqlens(cu_seqlens, d.num_seqs, d.total_tokens, stream);
+  if (st != GDN_SUCCESS) return st;
   char* ws = static_cast<char*>(workspace);
   gdn::PrefillArgs a;
   memset(&a, 0, sizeof(a));
@@ -242,11 +296,12 @@ gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims, const void* q, const v
   a.prep = (d.flags & GDN_FLAG_PREPARE_INPUTS) ? 1 : 0;
   a.no_delta = (d.flags & GDN_FLAG_NO_DELTA_RULE) ? 1 : 0;
   return launch_status(gdn::launch_prefill(a, d.dtype, d.dk, d.chunk, stream, first_stage, last_stage),
-                       "gdn_chunk_fwd launch");
+                       "gdn_chunk_fwd launch", stream);
 }
 
 size_t gdn_chunk_bwd_workspace_bytes(const gdn_dims_t* dims) {
   if (check_dims(dims, false) != GDN_SUCCESS) return 0;
+  if (check_backward(*dims) != GDN_SUCCESS) return 0;
   if (dims->flags) {
     fail(GDN_ERROR_NOT_SUPPORTED, "the backward pass takes no flags (got 0x%x)", dims->flags);
     return 0;
@@ -277,7 +332,8 @@ gdn_status_t gdn_chunk_bwd_stages(const gdn_dims_t* dims, const void* q, const v
   gdn_status_t st = check_dims(dims, false);
   if (st != GDN_SUCCESS) return st;
   const gdn_dims_t& d = *dims;
-  if (d.flags) return fail(GDN_ERROR_NOT_SUPPORTED, "the backward pass takes no flags (got 0x%x)", d.flags);
+  st = check_backward(d);
+  if (st != GDN_SUCCESS) return st;
   if (!cu_seqlens && d.num_seqs != 1)
     return fail(GDN_ERROR_INVALID_VALUE, "cu_seqlens is NULL but num_seqs = %lld", (long long)d.num_seqs);
   if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(GDN_ERROR_INVALID_VALUE, "cu_seqlens is not 4-byte aligned");
@@ -312,6 +368,8 @@ gdn_status_t gdn_chunk_bwd_stages(const gdn_dims_t* dims, const void* q, const v
   if (workspace_bytes < L.total)
     return fail(GDN_ERROR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, L.total);
 
+  st = debug_check_cu_seqlens(cu_seqlens, d.num_seqs, d.total_tokens, stream);
+  if (st != GDN_SUCCESS) return st;
   char* ws = static_cast<char*>(workspace);
   const gdn_workspace_layout_t& F = L.fwd.v;
   gdn::PrefillArgs a;
@@ -360,7 +418,7 @@ gdn_status_t gdn_chunk_bwd_stages(const gdn_dims_t* dims, const void* q, const v
   a.h_v = d.h_v;
   a.group = d.h_v / d.h_qk;
   return launch_status(gdn::launch_backward(a, d.dtype, d.dk, d.chunk, stream, first_stage, last_stage),
-                       "gdn_chunk_bwd launch");
+                       "gdn_chunk_bwd launch", stream);
 }
 
 gdn_status_t gdn_decode_step(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
@@ -394,7 +452,7 @@ gdn_status_t gdn_decode_step(const gdn_dims_t* dims, const void* q, const void* 
   a.snapshots = nullptr;
   a.prep = (d.flags & GDN_FLAG_PREPARE_INPUTS) ? 1 : 0;
   a.no_delta = (d.flags & GDN_FLAG_NO_DELTA_RULE) ? 1 : 0;
-  return launch_status(gdn::launch_decode(a, d.dtype, d.dk, stream), "gdn_decode_step launch");
+  return launch_status(gdn::launch_decode(a, d.dtype, d.dk, stream), "gdn_decode_step launch", stream);
 }
 
 gdn_status_t gdn_decode_multi(const gdn_dims_t* dims, int32_t num_tokens, const void* q, const void* k,
@@ -433,7 +491,7 @@ gdn_status_t gdn_decode_multi(const gdn_dims_t* dims, int32_t num_tokens, const 
   a.snapshots = snapshots;
   a.prep = (d.flags & GDN_FLAG_PREPARE_INPUTS) ? 1 : 0;
   a.no_delta = (d.flags & GDN_FLAG_NO_DELTA_RULE) ? 1 : 0;
-  return launch_status(gdn::launch_decode_multi(a, d.dtype, d.dk, stream), "gdn_decode_multi launch");
+  return launch_status(gdn::launch_decode_multi(a, d.dtype, d.dk, stream), "gdn_decode_multi launch", stream);
 }
 
 }  // extern "C"

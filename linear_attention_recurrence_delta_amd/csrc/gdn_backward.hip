@@ -108,9 +108,9 @@ __global__ __launch_bounds__(kDScanBlock) void gdn_kb_dstate(const PrefillArgs a
   const int hv = (int)((bid / G::NCB) % a.h_v);
   const int64_t n = bid / ((int64_t)G::NCB * a.h_v);
   const int hq = hv / a.group;
-  const int c0 = a.seq_chunk_offset[n], c1 = a.seq_chunk_offset[n + 1];
-  const int seq_start = a.cu_seqlens ? a.cu_seqlens[n] : 0;
-  const int seq_end = a.cu_seqlens ? a.cu_seqlens[n + 1] : (int)a.total_tokens;
+  const int2 cr = chunk_range(a, n), sr = seq_range(a, n);
+  const int c0 = cr.x, c1 = cr.y;
+  const int seq_start = sr.x, seq_end = sr.y;
   auto chunk_start = [&](int x) { return seq_start + (x - c0) * C; };
   auto chunk_len = [&](int x) { return min(C, seq_end - chunk_start(x)); };
   const bool is_scan = wave < NS, is_loader = !is_scan && wave < NS + NLD;

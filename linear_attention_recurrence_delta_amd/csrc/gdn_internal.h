@@ -88,8 +88,17 @@ struct DecodeArgs {
 // K^T and q.k), 2 (I + A)^{-1} and W, 3 fused scan.
 constexpr int kPrefillStages = 3;
 
-// True when the fused scan kernel has an instance for (dtype, head_dim, chunk).
-bool prefill_supported(int dtype, int head_dim, int chunk);
+// True when the prefill kernels have an instance for (dtype, head_dim, chunk).
+inline bool prefill_supported(int dtype, int head_dim, int chunk) {
+  if (head_dim != 16 && head_dim != 128) return false;
+  if (chunk != 16 && chunk != 64) return false;
+  return dtype == 0 || dtype == 1;
+}
+// The backward pass has every prefill instance except fp32 at head dim 128
+// with 64-token chunks (its reverse scan's fp32 fragments do not fit LDS).
+inline bool backward_supported(int dtype, int head_dim, int chunk) {
+  return prefill_supported(dtype, head_dim, chunk) && !(dtype == 0 && head_dim == 128 && chunk == 64);
+}
 
 // dtype: 0 = fp32, 1 = bf16. Returns the first launch error, if any.
 // Runs stages first..last (1-based, inclusive).

@@ -93,9 +93,8 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
     if (wave == 0) {
       int cnt = 0;
       if (lane < a.num_seqs) {
-        const int s0 = a.cu_seqlens ? a.cu_seqlens[lane] : 0;
-        const int s1 = a.cu_seqlens ? a.cu_seqlens[lane + 1] : (int)a.total_tokens;
-        cnt = (s1 - s0 + C - 1) / C;
+        const int2 r = seq_range(a, lane);
+        cnt = (r.y - r.x + C - 1) / C;
       }
       int incl = cnt;
 #pragma unroll
@@ -116,9 +115,8 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
     const int64_t n = base + tid;
     int cnt = 0;
     if (n < a.num_seqs) {
-      const int s0 = a.cu_seqlens ? a.cu_seqlens[n] : 0;
-      const int s1 = a.cu_seqlens ? a.cu_seqlens[n + 1] : (int)a.total_tokens;
-      cnt = (s1 - s0 + C - 1) / C;
+      const int2 r = seq_range(a, n);
+      cnt = (r.y - r.x + C - 1) / C;
     }
     sm.scan[tid] = cnt;
     __syncthreads();
@@ -145,10 +143,9 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
     return;
   }
   const int j = sm.hit[1];
-  const int s0 = a.cu_seqlens ? a.cu_seqlens[n] : 0;
-  const int s1 = a.cu_seqlens ? a.cu_seqlens[n + 1] : (int)a.total_tokens;
-  const int start = s0 + j * C;
-  const int len = min(C, s1 - start);
+  const int2 sr = seq_range(a, n);
+  const int start = sr.x + j * C;
+  const int len = min(C, sr.y - start);
   if (publish && tid == 0) table[c] = make_int4(n, start, len, j);
 
   // the chunk's key and query rows: every load is issued before the first
@@ -648,24 +645,45 @@ __global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs 
 constexpr int kScanBlock = 768;
 
 template <typename E, int D, int C>
+struct ScanCfg {
+  using G = Cfg<E, D, C>;
+  // fp32 operands at head dim 128 with 64-token chunks do not fit two slots
+  // per region in LDS: there the workgroup takes one 16-column slice, each
+  // operand region has one slot, and every iteration has a compute phase and
+  // a copy phase separated by a barrier
+  static constexpr bool WIDE = sizeof(E) == 4 && D == 128 && C == 64;
+  static constexpr int NS = WIDE ? 1 : G::NS;      // 16-column state slices per workgroup
+  static constexpr int BV = 16 * NS;               // state columns per workgroup
+  static constexpr int NCB = D / BV;               // workgroups per (sequence, V head)
+  static constexpr int NB = WIDE ? 1 : 2;          // slots per operand region
+};
+
+template <typename E, int D, int C>
 struct ScanSmem {
   using G = Cfg<E, D, C>;
-  Frag<E> kt[2][G::KT_FR * 64];        // K^T fragments
-  Frag<E> wf[2][G::W_FR * 64];         // W fragments
-  Frag<E> qf[2][G::Q_FR * 64];         // Q fragments
-  Frag<E> pf[2][G::QK_FR * 64];        // masked, decayed q.k fragments
-  Frag<E> tf[2][G::T_FR * 64];         // Tinv diag(b) fragments
-  f32x4 uf[2][G::NS * G::CT * 64];     // Ut accumulator tiles
-  E vr[2][C * G::BV];                  // the block's V columns, row-major
+  using SC = ScanCfg<E, D, C>;
+  static constexpr int NB = SC::NB;
+  Frag<E> kt[NB][G::KT_FR * 64];       // K^T fragments
+  Frag<E> wf[NB][G::W_FR * 64];        // W fragments
+  Frag<E> qf[NB][G::Q_FR * 64];        // Q fragments
+  Frag<E> pf[NB][G::QK_FR * 64];       // masked, decayed q.k fragments
+  Frag<E> tf[NB][G::T_FR * 64];        // Tinv diag(b) fragments
+  f32x4 uf[2][SC::NS * G::CT * 64];    // Ut accumulator tiles
+  E vr[NB][C * SC::BV];                // the block's V columns, row-major
   // exp(g_r) [C], exp(min(g_L - g_r, 0)) [C], exp(g_L), 3 pad
-  float dtab[2][2 * C + 4] __attribute__((aligned(16)));
+  float dtab[NB][2 * C + 4] __attribute__((aligned(16)));
   float touch[kScanBlock / 64][64];    // landing place of the L2 warm-up loads
 };
 
 template <typename E, int D, int C, bool ND, bool SV>
 __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
-  constexpr int DT = G::DT, CT = G::CT, DKS = G::DKS, CKS = G::CKS, NS = G::NS, BV = G::BV;
+  using SC = ScanCfg<E, D, C>;
+  constexpr int DT = G::DT, CT = G::CT, DKS = G::DKS, CKS = G::CKS, NS = SC::NS, BV = SC::BV, NCB = SC::NCB;
+  constexpr int NB = SC::NB;
+  static_assert(sizeof(ScanSmem<E, D, C>) <= 160 * 1024, "scan LDS");
+  // operand region slot of chunk x (the Ut tiles always alternate)
+  auto slot = [](int x) { return NB == 2 ? (x & 1) : 0; };
   // roles: NS scan waves, NS Ut waves, and loader waves (direct copies only,
   // so that their stalls on the memory pipeline hold up nothing else)
   constexpr int NLD = kScanBlock / 64 - 2 * NS;
@@ -689,15 +707,15 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   // the column blocks and V heads of one QK head, which read the same K^T
   // and Q fragments, are consecutive logical ids and so share an XCD
   const int64_t bid = xcd_local_id(blockIdx.x, gridDim.x);
-  const int cb = (int)(bid % G::NCB);
-  const int hv = (int)((bid / G::NCB) % a.h_v);
-  const int64_t n = bid / ((int64_t)G::NCB * a.h_v);
+  const int cb = (int)(bid % NCB);
+  const int hv = (int)((bid / NCB) % a.h_v);
+  const int64_t n = bid / ((int64_t)NCB * a.h_v);
   const int hq = hv / a.group;
-  const int c0 = a.seq_chunk_offset[n], c1 = a.seq_chunk_offset[n + 1];
+  const int2 cr = chunk_range(a, n), sr = seq_range(a, n);
+  const int c0 = cr.x, c1 = cr.y;
   // chunk x of this sequence starts at seq_start + (x - c0) * C; computing
   // start and length here keeps table reads off the per-chunk critical path
-  const int seq_start = a.cu_seqlens ? a.cu_seqlens[n] : 0;
-  const int seq_end = a.cu_seqlens ? a.cu_seqlens[n + 1] : (int)a.total_tokens;
+  const int seq_start = sr.x, seq_end = sr.y;
   auto chunk_start = [&](int x) { return seq_start + (x - c0) * C; };
   auto chunk_len = [&](int x) { return min(C, seq_end - chunk_start(x)); };
   const bool is_scan = wave < NS, is_loader = !is_scan && wave < NS + NLD;
@@ -736,24 +754,24 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   auto copy_window = [&](int xs, int xp) __attribute__((always_inline)) {
     if (xs < c1) {
       copy_region(0, static_cast<const char*>(a.key_t) + ((int64_t)xs * a.h_qk + hq) * B_KT,
-                  reinterpret_cast<char*>(sm.kt[xs & 1]), B_KT, false);
+                  reinterpret_cast<char*>(sm.kt[slot(xs)]), B_KT, false);
       copy_region(1, static_cast<const char*>(a.w) + ((int64_t)xs * a.h_v + hv) * B_W,
-                  reinterpret_cast<char*>(sm.wf[xs & 1]), B_W, false);
+                  reinterpret_cast<char*>(sm.wf[slot(xs)]), B_W, false);
       copy_region(2, static_cast<const char*>(a.q_frag) + ((int64_t)xs * a.h_qk + hq) * B_Q,
-                  reinterpret_cast<char*>(sm.qf[xs & 1]), B_Q, false);
+                  reinterpret_cast<char*>(sm.qf[slot(xs)]), B_Q, false);
       copy_region(3, static_cast<const char*>(a.pmask) + ((int64_t)xs * a.h_v + hv) * B_P,
-                  reinterpret_cast<char*>(sm.pf[xs & 1]), B_P, true);
+                  reinterpret_cast<char*>(sm.pf[slot(xs)]), B_P, true);
       copy_region(4, reinterpret_cast<const char*>(a.dtab + ((int64_t)xs * a.h_v + hv) * (2 * C + 4)),
-                  reinterpret_cast<char*>(sm.dtab[xs & 1]), B_D, false);
+                  reinterpret_cast<char*>(sm.dtab[slot(xs)]), B_D, false);
     }
     if (xp < c1) {
       copy_region(5, static_cast<const char*>(a.tinv) + ((int64_t)xp * a.h_v + hv) * B_T,
-                  reinterpret_cast<char*>(sm.tf[xp & 1]), B_T, true);
+                  reinterpret_cast<char*>(sm.tf[slot(xp)]), B_T, true);
       // the V columns, row i of the chunk at byte 16 l of its job; rows
       // past the chunk end repeat its last row (Tinv diag(b) has zero
       // columns there)
       const int p_start = chunk_start(xp), p_last = chunk_len(xp) - 1;
-      char* vdst = reinterpret_cast<char*>(sm.vr[xp & 1]);
+      char* vdst = reinterpret_cast<char*>(sm.vr[slot(xp)]);
       for (int jj = ((lw - CUM[6]) % NLD + NLD) % NLD; jj < JOBS[6]; jj += NLD) {
         const int o = 1024 * jj + 16 * lane;
         const int i = min(o / (BV * ESZ), p_last);
@@ -775,12 +793,12 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   constexpr int LV = (B_W + B_P + B_T + B_D + 127) / 128;        // lines per (chunk, V head)
   constexpr int LQ = (B_KT + B_Q + 127) / 128;                   // lines per (chunk, QK head)
   const int gi = hv % a.group;
-  const int nv = (LV - cb + G::NCB - 1) / G::NCB;
-  const int qs = gi * G::NCB + cb, qstride = a.group * G::NCB;
+  const int nv = (LV - cb + NCB - 1) / NCB;
+  const int qs = gi * NCB + cb, qstride = a.group * NCB;
   const int nq = qs < LQ ? (LQ - qs + qstride - 1) / qstride : 0;
   auto line_addr = [&](int x, int t) -> const char* {
     if (t < nv) {
-      const int o = 128 * (cb + G::NCB * t);
+      const int o = 128 * (cb + NCB * t);
       // lines of the P and Tinv diag(b) fragments that the causal mask makes
       // zero are not copied; the forward pass does not touch them either
       // (the saving form measured faster touching its Tinv lines all)
@@ -821,7 +839,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   f32x4 S[DT];
 
   auto scan_chunk = [&](int c) __attribute__((always_inline)) {
-    const int start = chunk_start(c), len = chunk_len(c), par = c & 1;
+    const int start = chunk_start(c), len = chunk_len(c), par = slot(c), upar = c & 1;
     if constexpr (SV && !SV_STAGE) {
       // (the same, stored row-major through the unused Q fragment buffers)
       store_tiles_rows<E, DT>(S, reinterpret_cast<E*>(sm.qf) + slice * stage_elems<E>(),
@@ -868,13 +886,13 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     f32x4 U[CT];
 #pragma unroll
     for (int t = 0; t < CT; ++t)
-      U[t] = ND ? sm.uf[par][(slice * CT + t) * 64 + lane] : sm.uf[par][(slice * CT + t) * 64 + lane] - WS[t];
+      U[t] = ND ? sm.uf[upar][(slice * CT + t) * 64 + lane] : sm.uf[upar][(slice * CT + t) * 64 + lane] - WS[t];
     Frag<E> Uk[CKS];
 #pragma unroll
     for (int ks = 0; ks < CKS; ++ks) Uk[ks] = acc_to_frag<E>(U[2 * ks], (2 * ks + 1 < CT) ? U[2 * ks + 1] : zero4());
     if constexpr (SV_STAGE) {
       // backward pass: the chunk's U rows, rounded as the products use them
-      stage_tiles_rows<E, CT>(U, sv_area(par, slice) + D * SLD, lane);
+      stage_tiles_rows<E, CT>(U, sv_area(upar, slice) + D * SLD, lane);
     } else if constexpr (SV) {
       store_tiles_rows<E, CT>(U, reinterpret_cast<E*>(sm.qf) + slice * stage_elems<E>(),
                               static_cast<E*>(a.ub) + ((int64_t)c * a.h_v + hv) * C * D + col0 + 16 * slice, D, lane);
@@ -903,7 +921,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       // Ut wave; written after the step's operand reads have been issued,
       // since one wave's LDS operations complete in order
       __builtin_amdgcn_sched_barrier(0);
-      E* ar = sv_area(par, slice);
+      E* ar = sv_area(upar, slice);
 #pragma unroll
       for (int ks = 0; ks < DKS; ++ks) {
 #pragma unroll
@@ -932,7 +950,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       // slice's Ut slot, whose tiles this wave has read above; the slice's
       // Ut wave stores them in the next iteration, before it forms new
       // tiles there
-      E* ost = reinterpret_cast<E*>(&sm.uf[par][slice * CT * 64]);
+      E* ost = reinterpret_cast<E*>(&sm.uf[upar][slice * CT * 64]);
 #pragma unroll
       for (int nt = 0; nt < CT; ++nt) {
         Half<E> h;
@@ -1007,7 +1025,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   // fragments (col = state column, k = token) are gathered from the
   // row-major V columns
   auto produce_chunk = [&](int p) __attribute__((always_inline)) {
-    const int par = p & 1;
+    const int par = slot(p), upar = p & 1;
     const E* vr = sm.vr[par];
     Frag<E> vf[CKS];
 #pragma unroll
@@ -1032,7 +1050,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
         if (!causal_zero(rt, s)) acc[rt] = mma(tb[rt], vf[s], acc[rt]);
     }
 #pragma unroll
-    for (int rt = 0; rt < CT; ++rt) sm.uf[par][(uw * CT + rt) * 64 + lane] = acc[rt];
+    for (int rt = 0; rt < CT; ++rt) sm.uf[upar][(uw * CT + rt) * 64 + lane] = acc[rt];
   };
 
   // The three roles run separate loops with the same barrier sequence (one
@@ -1054,6 +1072,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       __syncthreads();
       for (int c = c0 - 1; c < c1; ++c) {
         if (c >= c0) scan_chunk(c);
+        if (NB == 1) lds_barrier();    // compute phase ends: the loaders may refill
         lds_barrier();
       }
       if (a.final_state) {
@@ -1071,6 +1090,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       for (int c = c0 - 1; c < c1; ++c) {
+        if (NB == 1) __syncthreads();  // one slot per region: wait for the compute phase
         copy_window(c + 1, c + 2);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -1091,6 +1111,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
         if (st) store_outputs(c - 1, ov);
         if (ss) store_saved(c - 1, sv);
         warm(c + 3);
+        if (NB == 1) lds_barrier();
         lds_barrier();
       }
       if (!SV && STAGE_O) {
@@ -1117,9 +1138,8 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
 
 template <typename E, int D, int C>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int last) {
-  using G = Cfg<E, D, C>;
   const unsigned nc = (unsigned)a.max_chunks;
-  const unsigned scan_groups = (unsigned)(a.num_seqs * a.h_v * G::NCB);
+  const unsigned scan_groups = (unsigned)(a.num_seqs * a.h_v * ScanCfg<E, D, C>::NCB);
   for (int stage = first; stage <= last; ++stage) {
     switch (stage) {
       // the backward pass (a.backward) takes no flags
@@ -1156,12 +1176,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
 
 template <typename E>
 hipError_t launch_prefill_e(const PrefillArgs& a, int d, int c, hipStream_t s, int first, int last) {
-  if (d == 128 && c == 64) {
-    // fp32 at head dim 128 with 64-token chunks would need ~250 KB of LDS
-    // for the fused scan's double-buffered fragments; it is not built.
-    if constexpr (std::is_same<E, float>::value) return hipErrorInvalidValue;
-    else return launch_prefill_t<E, 128, 64>(a, s, first, last);
-  }
+  if (d == 128 && c == 64) return launch_prefill_t<E, 128, 64>(a, s, first, last);
   if (d == 128 && c == 16) return launch_prefill_t<E, 128, 16>(a, s, first, last);
   if (d == 16 && c == 64) return launch_prefill_t<E, 16, 64>(a, s, first, last);
   if (d == 16 && c == 16) return launch_prefill_t<E, 16, 16>(a, s, first, last);
@@ -1169,13 +1184,6 @@ hipError_t launch_prefill_e(const PrefillArgs& a, int d, int c, hipStream_t s, i
 }
 
 }  // namespace
-
-bool prefill_supported(int dtype, int head_dim, int chunk) {
-  if (head_dim != 16 && head_dim != 128) return false;
-  if (chunk != 16 && chunk != 64) return false;
-  if (dtype == 0 && head_dim == 128 && chunk == 64) return false;
-  return dtype == 0 || dtype == 1;
-}
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int chunk, hipStream_t s,
                           int first_stage, int last_stage) {

@@ -3,8 +3,30 @@
 #pragma once
 
 #include "gdn_device.h"
+#include "gdn_internal.h"
 
 namespace gdn {
+
+// Token range [x, y) of sequence n (the whole input when cu_seqlens is
+// null). The table's contents are a precondition of the entry points (0 =
+// c_0 <= ... <= c_N = T; checked on the host only under GDN_DEBUG). The
+// kernels clamp each bound into [0, T] with y >= x, so a table that breaks
+// it yields unspecified outputs but no access outside the arguments.
+__device__ __forceinline__ int2 seq_range(const PrefillArgs& a, int64_t n) {
+  const int t = (int)a.total_tokens;
+  if (!a.cu_seqlens) return make_int2(0, t);
+  const int s0 = min(max(a.cu_seqlens[n], 0), t);
+  return make_int2(s0, min(max(a.cu_seqlens[n + 1], s0), t));
+}
+
+// Chunk-slot range [x, y) of sequence n from kernel 1's offsets, clamped
+// into [0, max_chunks] likewise (with a table that breaks the precondition
+// the offsets could pass the workspace's chunk count).
+__device__ __forceinline__ int2 chunk_range(const PrefillArgs& a, int64_t n) {
+  const int nc = (int)a.max_chunks;
+  const int c0 = min(max(a.seq_chunk_offset[n], 0), nc);
+  return make_int2(c0, min(max(a.seq_chunk_offset[n + 1], c0), nc));
+}
 
 constexpr int kBlock = 256;
 
@@ -15,14 +37,11 @@ struct Cfg {
   static constexpr int NS = DT >= 2 ? 2 : 1;   // 16-column state slices per scan workgroup
   static constexpr int BV = 16 * NS;           // state columns per scan workgroup
   static constexpr int NCB = D / BV;           // scan workgroups per (sequence, V head)
-  static constexpr int NW = 4;                 // waves per scan workgroup
-  static constexpr int NPROD = NW - NS;        // producer waves
   static constexpr int KT_FR = DT * CKS;       // K^T fragments per chunk
   static constexpr int T_FR = CT * CKS;        // Tinv fragments per chunk
   static constexpr int QK_FR = CT * CKS;       // q.k fragments per chunk
   static constexpr int Q_FR = CT * DKS;        // Q fragments per chunk
   static constexpr int W_FR = CT * DKS;        // W fragments per chunk
-  static constexpr int VLD = C + 8;            // row stride of the transposed V slice
 };
 
 // Workgroups are dispatched round-robin over the chip's 8 XCDs (each with

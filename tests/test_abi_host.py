@@ -65,7 +65,6 @@ def ws_bytes(lib, d):
     (dict(dk=64, dv=64), NOT_SUPPORTED),
     (dict(dk=128, dv=64), NOT_SUPPORTED),
     (dict(chunk=32), NOT_SUPPORTED),
-    (dict(dtype=0), NOT_SUPPORTED),          # fp32 at head dim 128 needs chunk 16
     (dict(flags=4), INVALID),                # unknown flag
     (dict(flags=-1), INVALID),
 ])
@@ -133,7 +132,7 @@ def test_fwd_rejects_bad_workspace(lib):
 def test_fwd_rejects_unsupported(lib):
     assert call_fwd(lib, dims(dk=64, dv=64)) == NOT_SUPPORTED
     assert call_fwd(lib, dims(chunk=128)) == NOT_SUPPORTED
-    assert call_fwd(lib, dims(dtype=0)) == NOT_SUPPORTED
+    assert ws_bytes(lib, dims(dtype=0)) > 0                       # fp32 at head dim 128, chunk 64
     assert ws_bytes(lib, dims(dtype=0, chunk=16)) > 0
     assert ws_bytes(lib, dims(dtype=0, dk=16, dv=16)) > 0
 
@@ -251,5 +250,40 @@ def test_bwd_rejects_flags_and_bad_arguments(lib):
     assert call_bwd(lib, d, ws=None) == WORKSPACE
     assert call_bwd(lib, d, wsb=bwd_bytes(lib, d) - 1) == WORKSPACE
     assert call_bwd(lib, dims(dtype=0)) == NOT_SUPPORTED          # fp32 at head dim 128 needs chunk 16
+    assert bwd_bytes(lib, dims(dtype=0)) == 0
+    assert bwd_bytes(lib, dims(dtype=0, chunk=16)) > 0
     for st in ((0, 5), (1, 6), (4, 3)):
         assert call_bwd(lib, d, stages=st) == INVALID
+
+
+# --- the host code under AddressSanitizer and UndefinedBehaviorSanitizer ----
+
+def test_abi_host_code_under_sanitizers(tmp_path):
+    """gdn_api.cpp built with g++ -fsanitize=address,undefined against host
+    stand-ins of the HIP calls and launchers (tests/host_asan), driven through
+    every entry point: validation, workspace carving, the launch arguments,
+    GDN_DEBUG's cu_seqlens check and GDN_DEBUG_SYNC. No GPU involved."""
+    import shutil
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    here = os.path.join(ROOT, "tests", "host_asan")
+    csrc = os.path.join(ROOT, "linear_attention_recurrence_delta_amd", "csrc")
+    exe = str(tmp_path / "abi_driver")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", csrc, "-I", here, "-I", "/opt/rocm/include", os.path.join(csrc, "gdn_api.cpp"),
+           os.path.join(here, "hip_stub.cpp"), os.path.join(here, "abi_driver.cpp"), "-o", exe]
+    build = subprocess.run(cmd, capture_output=True, text=True)
+    if build.returncode and "asan" in build.stderr.lower() and "cannot find" in build.stderr.lower():
+        pytest.skip("sanitizer runtime not installed")
+    assert build.returncode == 0, build.stderr[-3000:]
+    # (verify_asan_link_order=0: a library that the environment preloads may
+    # come before the sanitizer runtime; it is left in place)
+    env = dict(os.environ, ASAN_OPTIONS="halt_on_error=1:detect_leaks=1:verify_asan_link_order=0",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    env.pop("GDN_DEBUG", None)
+    env.pop("GDN_DEBUG_SYNC", None)
+    run = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    assert run.returncode == 0, run.stdout[-2000:] + run.stderr[-3000:]
+    assert "checks ok" in run.stdout

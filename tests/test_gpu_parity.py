@@ -80,7 +80,7 @@ def test_tiny_fp32_workload():
 
 @pytest.mark.parametrize("d,chunk,dtype", [
     (128, 64, "bf16"), (128, 16, "bf16"), (16, 64, "bf16"), (16, 16, "bf16"),
-    (16, 16, "f32"), (128, 16, "f32"), (16, 64, "f32")])
+    (16, 16, "f32"), (128, 16, "f32"), (16, 64, "f32"), (128, 64, "f32")])
 def test_prefill_ragged_single_sequence(d, chunk, dtype):
     say(f"prefill T=300 d={d} C={chunk} {dtype}")
     inp = random_prefill(100 + d + chunk, [300], 2, 6, d, dtype)
@@ -137,7 +137,7 @@ def test_prefill_reads_only_what_it_writes(chunk):
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
-@pytest.mark.parametrize("dtype,chunk", [("bf16", 64), ("bf16", 16), ("f32", 16)])
+@pytest.mark.parametrize("dtype,chunk", [("bf16", 64), ("bf16", 16), ("f32", 16), ("f32", 64)])
 @pytest.mark.parametrize("kind", ["beta_to_2", "deep_decay", "raw_qk"])
 def test_prefill_wide_input_ranges(kind, dtype, chunk):
     # the method's ranges beyond the main recipe: write strength in (1, 2],
@@ -171,6 +171,29 @@ def test_decode_wide_input_ranges(kind):
     check(state, ref, torch.bfloat16, "state after 3 steps")
 
 
+def test_debug_check_of_cu_seqlens(monkeypatch):
+    # GDN_DEBUG: the prefill entry points read cu_seqlens on the host and
+    # reject a table that is not 0 = c_0 <= ... <= c_N = T before enqueueing
+    # anything; a valid table gives the same result, bit for bit
+    say("GDN_DEBUG cu_seqlens check and GDN_DEBUG_SYNC")
+    inp = on_dev(random_prefill(19, [50, 30, 20], 2, 6, 128, "bf16"))
+    args = [inp[x] for x in ("q", "k", "v", "log_alpha", "beta", "init_state")]
+    o_ref, f_ref = gdn.gdn_chunk_fwd(*args, inp["cu_seqlens"], chunk=64)
+    monkeypatch.setenv("GDN_DEBUG", "1")
+    monkeypatch.setenv("GDN_DEBUG_SYNC", "1")
+    o, f = gdn.gdn_chunk_fwd(*args, inp["cu_seqlens"], chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(f, f_ref)
+    for bad in ([1, 50, 80, 100], [0, 50, 40, 100], [0, 50, 80, 99], [0, 150, 80, 100]):
+        cu = torch.tensor(bad, dtype=torch.int32, device=DEV)
+        with pytest.raises(gdn.GdnError, match="GDN_DEBUG"):
+            gdn.gdn_chunk_fwd(*args, cu, chunk=64)
+        seeds = I.make_backward_seeds(20, [50, 30, 20], 6, 128, "bf16")
+        with pytest.raises(gdn.GdnError, match="GDN_DEBUG"):
+            gdn.gdn_chunk_bwd(*args[:5], seeds["d_o"].to(DEV), args[5], cu, seeds["d_final"].to(DEV), chunk=64)
+    torch.cuda.synchronize()
+
+
 def test_zero_tokens():
     say("T=0, two empty sequences")
     inp = random_prefill(8, [0, 0], 1, 3, 128, "bf16")
@@ -188,11 +211,20 @@ def test_head_group_of_four():
     check(fin, want_f, torch.bfloat16, "final")
 
 
-def test_fp32_head_dim_128_chunk_64_is_rejected():
-    say("fp32 d=128 C=64 -> not supported")
-    inp = random_prefill(18, [70], 1, 3, 128, "f32")
-    with pytest.raises(gdn.GdnError, match="NOT_SUPPORTED"):
-        run_gpu(inp, 64, use_cu=False)
+@pytest.mark.parametrize("lens", [[70], [300, 0, 1, 129]])
+def test_fp32_head_dim_128_chunk_64(lens):
+    # fp32 operands at head dim 128 with 64-token chunks: the scan's
+    # single-slot instance (16-column slices, compute and copy phases)
+    say(f"fp32 d=128 C=64 {lens}")
+    inp = random_prefill(18, lens, 2, 6, 128, "f32")
+    o, fin = run_gpu(inp, 64)
+    want_o, want_f = O.recurrent_form1(**oracle_args(inp))
+    check(o, want_o, torch.float32, "o")
+    check(fin, want_f, torch.float32, "final")
+    # its backward pass is not built
+    dims = gdn.make_dims(len(lens), sum(lens), 2, 6, 128, 128, 64, torch.float32)
+    with pytest.raises(gdn.GdnError, match="chunk 16"):
+        gdn.gdn_chunk_bwd_workspace_bytes(dims)
 
 
 def test_invariants_beta_zero_and_exact_recall():

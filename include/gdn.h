@@ -136,6 +136,29 @@ gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims,
                                   void* workspace, size_t workspace_bytes,
                                   hipStream_t stream, int first_stage, int last_stage);
 
+/*
+ * gdn_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, arguments and results, with the workspace taken
+ * from a device array of GDN_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on each GPU it runs on until the process ends. The caller still
+ * passes inputs and outputs. Makes no hipMalloc, hipFree or other
+ * allocating call. Dims whose gdn_chunk_fwd_workspace_bytes() exceeds
+ * GDN_NOALLOC_SCRATCH_BYTES (at 16 QK / 48 V heads, head dim 128, bf16,
+ * chunk 64: about 5,700 tokens) return GDN_ERROR_WORKSPACE before anything
+ * is enqueued. The array belongs to the device current at the call, which
+ * must be the device of `stream`; its address is looked up once per device
+ * on the first call there. All calls on one GPU share that GPU's array:
+ * calls that overlap on one GPU (other streams, other threads) race, so a
+ * caller serialises them. Nothing carries over between calls.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+gdn_status_t gdn_chunk_fwd_noalloc(const gdn_dims_t* dims,
+                                   const void* q, const void* k, const void* v,
+                                   const float* log_alpha, const float* beta,
+                                   const float* init_state, const int32_t* cu_seqlens,
+                                   void* o, float* final_state, hipStream_t stream);
+
 /* Workspace bytes gdn_chunk_fwd needs for these dims; 0 if dims are invalid
  * or unsupported (gdn_last_error_message() says why). The size depends on
  * (num_seqs, total_tokens, h_qk, h_v, dk, chunk, dtype) only. */

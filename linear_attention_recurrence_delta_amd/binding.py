@@ -21,7 +21,10 @@ STATUS = {0: "GDN_SUCCESS", 1: "GDN_ERROR_INVALID_VALUE", 2: "GDN_ERROR_NOT_SUPP
 EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_stages", "gdn_chunk_fwd_workspace_bytes",
            "gdn_chunk_bwd", "gdn_chunk_bwd_stages", "gdn_chunk_bwd_workspace_bytes",
            "gdn_decode_step", "gdn_decode_multi", "gdn_status_string", "gdn_last_error_message",
-           "gdn_chunk_fwd_workspace_layout")
+           "gdn_chunk_fwd_workspace_layout", "gdn_chunk_fwd_noalloc")
+
+# GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class GdnDims(ctypes.Structure):
@@ -66,6 +69,8 @@ def load_library(path=None):
     lib.gdn_chunk_fwd_stages.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                          i32, i32]
     lib.gdn_chunk_fwd_stages.restype = i32
+    lib.gdn_chunk_fwd_noalloc.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_chunk_fwd_noalloc.restype = i32
     lib.gdn_chunk_fwd_workspace_bytes.argtypes = [dims_p]
     lib.gdn_chunk_fwd_workspace_bytes.restype = sz
     lib.gdn_chunk_fwd_workspace_layout.argtypes = [dims_p, ctypes.POINTER(GdnWorkspaceLayout)]
@@ -194,6 +199,45 @@ def gdn_chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, ch
         _check(lib.gdn_chunk_fwd(*args))
     else:
         _check(lib.gdn_chunk_fwd_stages(*args, int(stages[0]), int(stages[1])))
+    return o, final_state
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, chunk=64,
+                          output_final_state=True, o=None, final_state=None, prepare_inputs=False,
+                          delta_rule=True):
+    """Prefill through gdn_chunk_fwd_noalloc: gdn_chunk_fwd with the
+    library's own device scratch array as its workspace (no workspace
+    argument; the library allocates nothing). Same arguments and results as
+    gdn_chunk_fwd otherwise; `o` and `final_state` are allocated here by
+    torch when not given."""
+    lib = load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_chunk_fwd_noalloc needs CUDA (HIP) tensors")
+    T, h_qk, d = q.shape
+    h_v = v.shape[1]
+    n = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _need(q, "q", dev, shape=(T, h_qk, d))
+    _need(k, "k", dev, q.dtype, (T, h_qk, d))
+    _need(v, "v", dev, q.dtype, (T, h_v, v.shape[2]))
+    _need(log_alpha, "log_alpha", dev, torch.float32, (T, h_v))
+    _need(beta, "beta", dev, torch.float32, (T, h_v))
+    if init_state is not None:
+        _need(init_state, "init_state", dev, torch.float32, (n, h_v, d, v.shape[2]))
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", dev, torch.int32, (n + 1,))
+    if q.dtype not in GDN_DTYPE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dims = make_dims(n, T, h_qk, h_v, d, v.shape[2], chunk, q.dtype, _flags(prepare_inputs, delta_rule))
+    if o is None:
+        o = torch.empty_like(v)
+    _need(o, "o", dev, v.dtype, tuple(v.shape))
+    if output_final_state and final_state is None:
+        final_state = torch.empty((n, h_v, d, v.shape[2]), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", dev, torch.float32, (n, h_v, d, v.shape[2]))
+    _check(lib.gdn_chunk_fwd_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                     _ptr(init_state), _ptr(cu_seqlens), _ptr(o), _ptr(final_state), _stream(dev)))
     return o, final_state
 
 

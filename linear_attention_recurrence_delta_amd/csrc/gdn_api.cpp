@@ -192,6 +192,16 @@ gdn_status_t check_backward(const gdn_dims_t& d) {
 
 }  // namespace
 
+gdn_status_t gdn::api_fail(gdn_status_t status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
 extern "C" {
 
 const char* gdn_status_string(gdn_status_t s) {

@@ -5,7 +5,13 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include "gdn.h"
+
 namespace gdn {
+
+// Sets the calling thread's error message (gdn_last_error_message) and
+// returns `status`; for entry points defined outside gdn_api.cpp.
+gdn_status_t api_fail(gdn_status_t status, const char* fmt, ...);
 
 // Everything one gdn_chunk_fwd call needs on the device. Workspace regions
 // are typed pointers carved by the host (see the layout in gdn_api.cpp).

@@ -22,9 +22,9 @@ ARCH = "gfx950"
 # Packed-fp32 instructions are disabled for all device code. MFMA results
 # are kept in ordinary VGPRs (the accumulation-register form makes the
 # compiler shuffle accumulator arrays through v_accvgpr moves every loop).
-# The atomic optimizer is off: the kernels' LDS atomics are issued by one
-# lane per already-reduced row, and the optimizer would wrap each in a
-# wave-wide scan.
+# The atomic optimizer is off: the gradient kernel's LDS atomics are issued
+# by one lane per already-reduced row, and the optimizer would wrap each in
+# a wave-wide scan.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-mllvm", "-amdgpu-mfma-vgpr-form",
                 "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]

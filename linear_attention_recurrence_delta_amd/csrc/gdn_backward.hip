@@ -357,7 +357,8 @@ __global__ __launch_bounds__(kDScanBlock) void gdn_kb_dstate(const PrefillArgs a
 // product runs on the input dtype's MFMA with fp32 accumulation; the C x C
 // matrices that only feed products (dP * Dincl, dT, Y, B + B^T) are held in
 // the input dtype. Row and column sums of the per-element terms use DPP and
-// lane-row swaps, then LDS atomics.
+// lane-row swaps, then LDS atomics into each wave's own row sums, which
+// are added in wave order at the end.
 // --------------------------------------------------------------------------
 constexpr int kGradBlock = 256;
 
@@ -377,7 +378,12 @@ struct GradSmem {
   // in the input dtype)
   E x1[C * ELD] __attribute__((aligned(16)));
   float g[C], b[C], ea[C], ed[C], dg[C], db[C];
-  float sums[2];                       // <S0, dS_L>; sum of the state-term row factors
+  // each wave's own row sums of the dlog a and db terms, and of <S0, dS_L>
+  // and the state-term row factors (LDS atomics, which one wave executes in
+  // program order); added across waves in wave order once all are in, so
+  // the gradients do not depend on which wave got there first
+  float dgw[kGradBlock / 64][C], dbw[kGradBlock / 64][C];
+  float sumw[kGradBlock / 64][2];
 };
 
 template <typename E, int D, int C>
@@ -506,10 +512,10 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
       sm.b[tid] = a.beta_chunk[ch * C + tid];
       sm.ea[tid] = a.dtab[ch * (2 * C + 4) + tid];
       sm.ed[tid] = a.dtab[ch * (2 * C + 4) + C + tid];
-      sm.dg[tid] = 0.f;
-      sm.db[tid] = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) { sm.dgw[w][tid] = 0.f; sm.dbw[w][tid] = 0.f; }
     }
-    if (tid < 2) sm.sums[tid] = 0.f;
+    if (tid < 2 * NW) sm.sumw[tid / 2][tid % 2] = 0.f;
     const float gl = a.dtab[ch * (2 * C + 4) + 2 * C];
     stage_rows(sm.u1.r1, a.d_o, a.h_v, hv);
     stage_ws(sm.r2, static_cast<const E*>(a.ub) + ch * C * D);
@@ -585,14 +591,14 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float s = sum16(prow[rt][i]);
-          if (l16 == 0) atomicAdd(&sm.dg[16 * rt + 4 * quad + i], s);
+          if (l16 == 0) atomicAdd(&sm.dgw[wave][16 * rt + 4 * quad + i], s);
         }
       }
       fro = sum_rows4(sum16(fro));
       pk_all = sum_rows4(sum16(pk_all));
       if (lane == 0) {
-        atomicAdd(&sm.sums[0], fro);
-        atomicAdd(&sm.sums[1], pk_all);
+        atomicAdd(&sm.sumw[wave][0], fro);
+        atomicAdd(&sm.sumw[wave][1], pk_all);
       }
     }
 
@@ -620,14 +626,14 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
           const int r = 16 * rt + 4 * quad + i;
           const float m2 = acc[i] * to_f(pv[i + 4 * (rt & 1)]);
           const float rs = sum16(m2);
-          if (l16 == 0) atomicAdd(&sm.dg[r], rs);
+          if (l16 == 0) atomicAdd(&sm.dgw[wave][r], rs);
           colp += m2;
           const float gm = (j <= r && r < len) ? __expf(fminf(sm.g[r] - sm.g[j], 0.f)) : 0.f;
           sm.x1[r * ELD + j] = to_e<E>(acc[i] * gm);
         }
       }
       colp = sum_rows4(colp);
-      if (quad == 0) atomicAdd(&sm.dg[j], -colp);
+      if (quad == 0) atomicAdd(&sm.dgw[wave][j], -colp);
     }
     __syncthreads();                   // x1 complete; dL/do and U rows dead
 #pragma unroll
@@ -733,8 +739,8 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
           const float rdb = sum16(da * kk[e] * gm);
           const float rdg = sum16(mb2);
           if (l16 == 0) {
-            atomicAdd(&sm.db[r], rdb);
-            atomicAdd(&sm.dg[r], rdg);
+            atomicAdd(&sm.dbw[wave][r], rdb);
+            atomicAdd(&sm.dgw[wave][r], rdg);
           }
           colm += mb2;
           if (i < r) {
@@ -746,7 +752,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         }
       }
       colm = sum_rows4(colm);
-      if (quad == 0) atomicAdd(&sm.dg[i], -colm);
+      if (quad == 0) atomicAdd(&sm.dgw[wave][i], -colm);
     }
     __syncthreads();
     // dK += (B + B^T) K; dV = diag(b) Tinv^T dU and its b term (v read from
@@ -808,14 +814,27 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         for (int e = 0; e < 4; ++e) {
           const float sb = sum16(rdb_acc[rt][e]), sg = sum16(rdg_acc[rt][e]);
           if (l16 == 0) {
-            atomicAdd(&sm.db[16 * rt + 4 * quad + e], sb);
-            atomicAdd(&sm.dg[16 * rt + 4 * quad + e], sg);
+            atomicAdd(&sm.dbw[wave][16 * rt + 4 * quad + e], sb);
+            atomicAdd(&sm.dgw[wave][16 * rt + 4 * quad + e], sg);
           }
         }
       }
     }
     __syncthreads();
-    if (tid == 0 && len > 0) sm.dg[len - 1] += gl * sm.sums[0] + sm.sums[1];
+    if (tid < C) {
+      // the waves' sums in wave order; the state terms go to the last row
+      float tg = 0.f, tb = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) { tg += sm.dgw[w][tid]; tb += sm.dbw[w][tid]; }
+      if (tid == len - 1) {
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) { s0 += sm.sumw[w][0]; s1 += sm.sumw[w][1]; }
+        tg += gl * s0 + s1;
+      }
+      sm.dg[tid] = tg;
+      sm.db[tid] = tb;
+    }
     __syncthreads();
     if (tid < len) {
       float acc = 0.f;

@@ -40,7 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN prefill tokens/s at T=64K (48 V heads, d=128) + decode state GB/s"
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
-STAGES = ["gdn_k1_chunk_prep", "gdn_k2_inverse_w", "gdn_k3_scan"]
+STAGES = ["gdn_k2_inverse_w", "gdn_k3_scan"]
 DECODE_KERNEL = "gdn_kd_decode_step"
 
 
@@ -56,15 +56,12 @@ def algorithmic_work(T, HQ, HV, D, C, N, decode_batch):
     gates = T * HV * 8                          # log a and b (fp32), or g and b
     tri = (C + 1) / 2.0                         # lower-triangle elements per token of a causal C x C operand
     work = {
-        # Q K^T per QK head; reads q, k, log a, b; writes K^T, Q and q.k
-        # fragments, g, b
-        "gdn_k1_chunk_prep": (T * HQ * 2 * C * dk,
-                              2 * T * HQ * dk * e + gates + T * HQ * (2 * dk + C) * e + gates),
-        # K K^T per QK head, the triangular inverse and W per V head; reads k,
-        # K^T, q.k, g, b; writes Tinv diag(b), W, the masked q.k fragments P
-        # and the row-factor table (2C + 4 fp32 per chunk and V head)
-        "gdn_k2_inverse_w": (T * (HQ * 2 * C * dk + HV * (C * C / 3.0 + 2 * C * dk)),
-                             T * HQ * (2 * dk + C) * e + gates
+        # K K^T and Q K^T per QK head, the triangular inverse and W per V
+        # head; reads q, k, log a, b; writes the K^T and Q fragments (once per
+        # QK head), Tinv diag(b), W, the masked q.k fragments P and the
+        # row-factor table (2C + 4 fp32 per chunk and V head)
+        "gdn_k2_inverse_w": (T * (HQ * 4 * C * dk + HV * (C * C / 3.0 + 2 * C * dk)),
+                             2 * T * HQ * dk * e + gates + T * HQ * 2 * dk * e
                              + T * HV * (2 * tri + dk) * e + T * HV * (2 * C + 4) * 4 / C),
         # Ut, W S, Q S, K^T U, P U per V head; reads Q, K^T, P, V, Tinv
         # diag(b), W, the row factors and the initial states; writes o and the

@@ -119,14 +119,14 @@ gdn_status_t gdn_chunk_fwd(const gdn_dims_t* dims,
 /*
  * Diagnostic variant of gdn_chunk_fwd that enqueues only launches
  * first_stage..last_stage, so a profiler or benchmark can put events between
- * them: 1 = chunk table, gate prefix sums, K^T, Q and Q K^T; 2 = K K^T,
- * (I + A)^{-1}, W, the masked and decayed Q K^T and the row factors; 3 = the
- * fused U construction, inter-chunk state scan and output products. Arguments are those of gdn_chunk_fwd. Stages after the
- * first read what earlier stages left in `workspace`, so a call starting at
- * stage s > 1 must follow calls that ran stages 1..s-1 with identical
- * arguments and workspace on the same stream. gdn_chunk_fwd is
- * gdn_chunk_fwd_stages(..., 1, 3). Returns GDN_ERROR_INVALID_VALUE unless
- * 1 <= first_stage <= last_stage <= 3.
+ * them: 1 = chunk table, gate prefix sums, the K^T and Q layouts, Q K^T and
+ * K K^T, (I + A)^{-1}, W, the masked and decayed Q K^T and the row factors;
+ * 2 = the fused U construction, inter-chunk state scan and output products.
+ * Arguments are those of gdn_chunk_fwd. Stage 2 reads what stage 1 left in
+ * `workspace`, so a call starting at stage 2 must follow a call that ran
+ * stage 1 with identical arguments and workspace on the same stream.
+ * gdn_chunk_fwd is gdn_chunk_fwd_stages(..., 1, 2). Returns
+ * GDN_ERROR_INVALID_VALUE unless 1 <= first_stage <= last_stage <= 2.
  */
 gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims,
                                   const void* q, const void* k, const void* v,
@@ -281,12 +281,12 @@ const char* gdn_last_error_message(void);
 typedef struct {
   size_t chunk_table;  /* int32 [max_chunks][4]: seq, first token, length, index in seq */
   size_t seq_chunk_offset; /* int32 [N+1]: first compact chunk of each sequence */
-  size_t gate_prefix;  /* fp32 [max_chunks][h_v][C]: in-chunk inclusive prefix of log a */
-  size_t beta_chunk;   /* fp32 [max_chunks][h_v][C]: b of each chunk row, 0 past its end */
+  size_t gate_prefix;  /* fp32 [max_chunks][h_v][C]: in-chunk inclusive prefix of log a (backward pass) */
+  size_t beta_chunk;   /* fp32 [max_chunks][h_v][C]: b of each chunk row, 0 past its end (backward pass) */
   size_t tinv;         /* dtype [max_chunks][h_v]: (I + A)^{-1} diag(b) as MFMA fragments */
   size_t w;            /* dtype [max_chunks][h_v]: W = (I + A)^{-1} diag(b exp(g)) K as MFMA fragments */
   size_t key_t;        /* dtype [max_chunks][h_qk]: K^T as MFMA fragments */
-  size_t qk;           /* dtype [max_chunks][h_qk]: q_r . k_j (j-tile <= r-tile) as fragments */
+  size_t qk;           /* dtype [max_chunks][h_qk]: q_r . k_j (j-tile <= r-tile) as fragments (backward pass) */
   size_t q_frag;       /* dtype [max_chunks][h_qk]: Q as MFMA fragments */
   size_t pmask;        /* dtype [max_chunks][h_v]: q_r . k_j exp(g_r - g_j), j <= r, as fragments */
   size_t dtab;         /* fp32 [max_chunks][h_v][2C+4]: exp(g_r), exp(g_L - g_r), exp(g_L), pad */

@@ -90,9 +90,11 @@ struct DecodeArgs {
   int32_t no_delta;         // 1: gate-only update S = a S + b k v^T
 };
 
-// Prefill launch stages (1-based): 1 chunk preparation (table, gate prefix sums,
-// K^T and q.k), 2 (I + A)^{-1} and W, 3 fused scan.
-constexpr int kPrefillStages = 3;
+// Prefill launch stages (1-based): 1 chunk preparation and inverse (kernel
+// 2: chunk table, gate prefix sums, K^T and Q fragments, (I + A)^{-1}, W, P,
+// row factors), 2 the fused scan. The backward pass runs kernels 1, 2 and 3
+// as its stages 1-3 (PrefillArgs::backward).
+constexpr int kPrefillStages = 2;
 
 // True when the prefill kernels have an instance for (dtype, head_dim, chunk).
 inline bool prefill_supported(int dtype, int head_dim, int chunk) {

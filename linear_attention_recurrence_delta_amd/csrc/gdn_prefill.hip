@@ -60,6 +60,81 @@ namespace {
 // the query tile nt stays zero): two vertically adjacent accumulator tiles
 // are a fragment as they stand.
 // --------------------------------------------------------------------------
+// Which sequence owns chunk slot c: every thread of the block calls this
+// (it synchronises the block) and gets (sequence, index in the sequence),
+// or sequence -1 for a slot past the last chunk. It scans the per-sequence
+// chunk counts ceil(L_n / C): in one wave for up to 64 sequences, else with
+// a block scan in `scan` (kBlock ints). When `publish` is set the block
+// writes the slot's chunk table entry, and slot 0's block also the
+// per-sequence first-chunk offsets.
+template <int C>
+__device__ int2 locate_chunk(const PrefillArgs& a, int64_t c, bool publish, int* scan, int* hit) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) { hit[0] = -1; hit[1] = 0; }
+  __syncthreads();
+  int carry = 0;
+  if (a.num_seqs <= 64) {
+    // up to 64 sequences: one wave's prefix sum, lane n holding sequence n
+    if (wave == 0) {
+      int cnt = 0;
+      if (lane < a.num_seqs) {
+        const int2 r = seq_range(a, lane);
+        cnt = (r.y - r.x + C - 1) / C;
+      }
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int x = __shfl_up(incl, off);
+        if (lane >= off) incl += x;
+      }
+      const int excl = incl - cnt;
+      if (lane < a.num_seqs) {
+        if (c >= excl && c < incl) { hit[0] = lane; hit[1] = (int)(c - excl); }
+        if (c == 0 && publish) a.seq_chunk_offset[lane] = excl;
+      }
+      carry = __shfl(incl, 63);
+    }
+    __syncthreads();
+  }
+  for (int64_t base = 0; a.num_seqs > 64 && base < a.num_seqs; base += kBlock) {
+    const int64_t n = base + tid;
+    int cnt = 0;
+    if (n < a.num_seqs) {
+      const int2 r = seq_range(a, n);
+      cnt = (r.y - r.x + C - 1) / C;
+    }
+    scan[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < kBlock; off <<= 1) {
+      const int x = (tid >= off) ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += x;
+      __syncthreads();
+    }
+    const int incl = carry + scan[tid];
+    const int excl = incl - cnt;
+    if (n < a.num_seqs) {
+      if (c >= excl && c < incl) { hit[0] = (int)n; hit[1] = (int)(c - excl); }
+      if (c == 0 && publish) a.seq_chunk_offset[n] = excl;
+    }
+    carry += scan[kBlock - 1];
+    __syncthreads();
+  }
+  if (c == 0 && publish && tid == 0) a.seq_chunk_offset[a.num_seqs] = carry;
+  const int n = hit[0], j = hit[1];
+  if (publish && tid == 0) {
+    int4* table = reinterpret_cast<int4*>(a.chunk_table);
+    if (n < 0) {
+      table[c] = make_int4(-1, 0, 0, 0);
+    } else {
+      const int2 sr = seq_range(a, n);
+      const int st = sr.x + j * C;
+      table[c] = make_int4(n, st, min(C, sr.y - st), j);
+    }
+  }
+  return make_int2(n, j);
+}
+
 template <typename E, int D, int C>
 struct PrepSmem {
   static constexpr int KLD = D + 8;    // row stride of the staged keys and queries
@@ -84,69 +159,11 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
   const int64_t lid = xcd_local_id(blockIdx.x, gridDim.x);
   const int64_t c = lid / a.h_qk;
   const int hq = (int)(lid % a.h_qk);
-  const bool publish = hq == 0;
-  if (tid == 0) { sm.hit[0] = -1; sm.hit[1] = 0; }
-  __syncthreads();
-  int carry = 0;
-  if (a.num_seqs <= 64) {
-    // up to 64 sequences: one wave's prefix sum, lane n holding sequence n
-    if (wave == 0) {
-      int cnt = 0;
-      if (lane < a.num_seqs) {
-        const int2 r = seq_range(a, lane);
-        cnt = (r.y - r.x + C - 1) / C;
-      }
-      int incl = cnt;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int x = __shfl_up(incl, off);
-        if (lane >= off) incl += x;
-      }
-      const int excl = incl - cnt;
-      if (lane < a.num_seqs) {
-        if (c >= excl && c < incl) { sm.hit[0] = lane; sm.hit[1] = (int)(c - excl); }
-        if (c == 0 && publish) a.seq_chunk_offset[lane] = excl;
-      }
-      carry = __shfl(incl, 63);
-    }
-    __syncthreads();
-  }
-  for (int64_t base = 0; a.num_seqs > 64 && base < a.num_seqs; base += kBlock) {
-    const int64_t n = base + tid;
-    int cnt = 0;
-    if (n < a.num_seqs) {
-      const int2 r = seq_range(a, n);
-      cnt = (r.y - r.x + C - 1) / C;
-    }
-    sm.scan[tid] = cnt;
-    __syncthreads();
-    for (int off = 1; off < kBlock; off <<= 1) {
-      const int x = (tid >= off) ? sm.scan[tid - off] : 0;
-      __syncthreads();
-      sm.scan[tid] += x;
-      __syncthreads();
-    }
-    const int incl = carry + sm.scan[tid];
-    const int excl = incl - cnt;
-    if (n < a.num_seqs) {
-      if (c >= excl && c < incl) { sm.hit[0] = (int)n; sm.hit[1] = (int)(c - excl); }
-      if (c == 0 && publish) a.seq_chunk_offset[n] = excl;
-    }
-    carry += sm.scan[kBlock - 1];
-    __syncthreads();
-  }
-  if (c == 0 && publish && tid == 0) a.seq_chunk_offset[a.num_seqs] = carry;
-  const int n = sm.hit[0];
-  int4* table = reinterpret_cast<int4*>(a.chunk_table);
-  if (n < 0) {
-    if (publish && tid == 0) table[c] = make_int4(-1, 0, 0, 0);
-    return;
-  }
-  const int j = sm.hit[1];
-  const int2 sr = seq_range(a, n);
-  const int start = sr.x + j * C;
+  const int2 loc = locate_chunk<C>(a, c, hq == 0, sm.scan, sm.hit);
+  if (loc.x < 0) return;
+  const int2 sr = seq_range(a, loc.x);
+  const int start = sr.x + loc.y * C;
   const int len = min(C, sr.y - start);
-  if (publish && tid == 0) table[c] = make_int4(n, start, len, j);
 
   // the chunk's key and query rows: every load is issued before the first
   // is used (rows past the chunk end read its last row and are zeroed;
@@ -313,6 +330,10 @@ struct InvSmem {
     float at[C * FLD];                 // A and Tinv (see above)
   } u;
   union {
+    struct {
+      int scan[kBlock];                // the chunk lookup's block scan (forward pass)
+      int hit[2];
+    } loc;
     float x[4][16 * XLD];              // one 16 x 16 scratch tile per wave (blocks below the diagonal)
     Frag<E> tbg[G::T_FR * 64];         // then the Tinv diag(b exp(g)) fragments
   } v;
@@ -335,18 +356,35 @@ __global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs 
   const int64_t lid = xcd_local_id(blockIdx.x, gridDim.x);
   const int64_t c = lid / a.h_v;
   const int hv = (int)(lid % a.h_v);
-  const int4 tab = reinterpret_cast<const int4*>(a.chunk_table)[c];
-  if (tab.x < 0) return;
-  const int start = tab.y, len = tab.z;
   const int hq = hv / a.group;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, l16 = lane & 15;
+  // The forward pass does kernel 1's work here, for this V head: the chunk
+  // lookup, the gate prefix sums and the q.k products; the QK head's first
+  // V head also lays out the K^T and Q fragments for the scan. The backward
+  // pass reads those from kernel 1.
+  constexpr bool FU = !BW;
+  int start, len;
+  if constexpr (FU) {
+    const int2 loc = locate_chunk<C>(a, c, hv == 0, sm.v.loc.scan, sm.v.loc.hit);
+    if (loc.x < 0) return;
+    const int2 sr = seq_range(a, loc.x);
+    start = sr.x + loc.y * C;
+    len = min(C, sr.y - start);
+  } else {
+    const int4 tab = reinterpret_cast<const int4*>(a.chunk_table)[c];
+    if (tab.x < 0) return;
+    start = tab.y;
+    len = tab.z;
+  }
+  const bool lead = hv % a.group == 0;
   float* at = sm.u.at;
 
-  // K^T fragments of this wave's W d-tiles, from kernel 1; issued first so
-  // that they arrive during the inverse
+  // K^T fragments of this wave's W d-tiles: from kernel 1, issued first so
+  // that they arrive during the inverse (backward pass), or gathered from
+  // the staged keys below (forward pass)
   const int ksd = wave;
   Frag<E> kta[CKS], ktb[CKS];
-  if (!ND && ksd < DKS) {
+  if (BW && ksd < DKS) {
     const Frag<E>* ktg = reinterpret_cast<const Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
 #pragma unroll
     for (int s = 0; s < CKS; ++s) {
@@ -354,27 +392,34 @@ __global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs 
       if (2 * ksd + 1 < DT) ktb[s] = ktg[((2 * ksd + 1) * CKS + s) * 64 + lane];
     }
   }
-  // the QK head's q.k fragments, which this V head masks and decays below
-  constexpr int PQ = (G::QK_FR * 64 + kBlock - 1) / kBlock;
-  Frag<E> qkr[PQ];
-  {
-    const Frag<E>* qkg = reinterpret_cast<const Frag<E>*>(a.qk) + (c * a.h_qk + hq) * G::QK_FR * 64;
+  // forward pass: wave w's query tile w, its Q fragments straight from q
+  // (rows past the chunk end read its last row and are zeroed below)
+  Frag<E> qf[DKS];
+  if (FU && wave < CT) {
+    const E* row = static_cast<const E*>(a.q) + ((int64_t)(start + min(16 * wave + l16, len - 1)) * a.h_qk + hq) * D;
 #pragma unroll
-    for (int p = 0; p < PQ; ++p)
-      if (!BW && tid + p * kBlock < G::QK_FR * 64) qkr[p] = qkg[tid + p * kBlock];
+    for (int ks = 0; ks < DKS; ++ks) qf[ks] = load_frag<E>(row + 32 * ks, quad, D - 32 * ks);
   }
-  // g and b of this V head (threads below 2 C)
-  float gbv = 0.f;
-  if (tid < 2 * C) {
+  // g and b of this V head: from kernel 1 (threads below 2 C), or the
+  // in-chunk prefix sum of log a in wave 0, lane r holding token r (lanes
+  // past the chunk end read its last token and then take the no-op values
+  // log a = 0, b = 0)
+  float gbv = 0.f, gw = 0.f, bw = 0.f;
+  if (BW && tid < 2 * C) {
     const int64_t o = (c * a.h_v + hv) * C + (tid % C);
     gbv = (tid < C) ? a.gate_prefix[o] : a.beta_chunk[o];
+  }
+  if (FU && wave == 0) {
+    const int64_t gi = (int64_t)(start + min(lane, len - 1)) * a.h_v + hv;
+    gw = a.log_alpha[gi];
+    bw = a.beta[gi];
   }
   // the chunk's keys, all loads issued before the first is used (rows past
   // the chunk end read its last row and are zeroed; threads past the C x D
   // block repeat its last load and store nothing)
   const E* kg = static_cast<const E*>(a.k);
   constexpr int NV = C * D / VE, NL = (NV + kBlock - 1) / kBlock;
-  if constexpr (!ND) {
+  if constexpr (!ND || FU) {
     VLoad kv[NL];
 #pragma unroll
     for (int p = 0; p < NL; ++p) {
@@ -390,38 +435,110 @@ __global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs 
 #pragma unroll
         for (int e = 0; e < VE; ++e) kv[p][e] = to_e<E>(0.f);
       }
-      // raw keys: unit rows, exactly as kernel 1 makes them for K^T and q.k
+      // raw keys: unit rows
       if constexpr (P) normalize_slice<E, D, VE>(kv[p]);
       if (idx < NV) *reinterpret_cast<VLoad*>(&sm.u.ks[r * KLD + d]) = kv[p];
     }
   }
-  if (tid < 2 * C) sm.gb[tid / C][tid % C] = gbv;
+  if (BW && tid < 2 * C) sm.gb[tid / C][tid % C] = gbv;
+  if (FU && wave == 0) {
+    if constexpr (P) { gw = neg_softplus(gw); bw = sigmoid_of(bw); }
+    if (lane >= len) { gw = 0.f; bw = 0.f; }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float x = __shfl_up(gw, off);
+      if (lane >= off) gw += x;
+    }
+    if (lane < C) { sm.gb[0][lane] = gw; sm.gb[1][lane] = bw; }
+  }
   __syncthreads();
 
-  // The scan's operands that depend on g: P = the masked, decayed q.k
-  // fragments, P[r][j] = (q_r . k_j) exp(g_r - g_j) for j <= r < len, else 0
-  // (the exponent is clamped at 0 so that masked entries cannot overflow
-  // before being zeroed), and the row-factor table exp(g_r), exp(min(g_L -
-  // g_r, 0)) (both zero past the chunk end), exp(g_L).
-  {
-    Frag<E>* pg = reinterpret_cast<Frag<E>*>(a.pmask) + (c * a.h_v + hv) * G::QK_FR * 64;
+  if constexpr (FU) {
+    // K^T fragments (row d, k = token) gathered from the staged keys: this
+    // wave's W d-tiles; the QK head's first V head also writes them for the
+    // scan (the waves' d-tiles cover all of them)
+    if (ksd < DKS) {
 #pragma unroll
-    for (int p = 0; p < PQ; ++p) {
-      const int it = tid + p * kBlock;
-      if (BW || it >= G::QK_FR * 64) continue;       // the backward pass uses P^T (below)
-      const int f = it / 64, ln = it % 64, nt = f / CKS, s = f % CKS, q4 = ln >> 4;
-      if (causal_zero(nt, s)) continue;              // all zero; the scan neither copies nor reads it
-      const int r = 16 * nt + (ln & 15);
-      const float gr = sm.gb[0][r], vr = (float)(r < len);
-      Frag<E> v;
+      for (int s = 0; s < CKS; ++s) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = frag_k(s, q4, e);
-        const float m = (float)(j <= r) * vr;
-        v[e] = to_e<E>(to_f(qkr[p][e]) * (__expf(fminf(gr - sm.gb[0][min(j, C - 1)], 0.f)) * m));
+        for (int e = 0; e < 8; ++e) {
+          const int i = frag_k(s, quad, e);
+          kta[s][e] = (i < C) ? sm.u.ks[i * KLD + 32 * ksd + l16] : to_e<E>(0.f);
+          if (2 * ksd + 1 < DT) ktb[s][e] = (i < C) ? sm.u.ks[i * KLD + 32 * ksd + 16 + l16] : to_e<E>(0.f);
+        }
       }
-      pg[it] = v;
+      if (lead) {
+        Frag<E>* ktg = reinterpret_cast<Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
+#pragma unroll
+        for (int s = 0; s < CKS; ++s) {
+          ktg[((2 * ksd) * CKS + s) * 64 + lane] = kta[s];
+          if (2 * ksd + 1 < DT) ktg[((2 * ksd + 1) * CKS + s) * 64 + lane] = ktb[s];
+        }
+      }
     }
+    // q.k for query tile nt = wave and the scan's P fragments from it,
+    // P[r][j] = (q_r . k_j) exp(g_r - g_j) for j <= r < len, else 0 (the
+    // exponent is clamped at 0 so that masked entries cannot overflow
+    // before being zeroed). The pair of accumulator tiles K_j Q_r^T of key
+    // tiles 2s and 2s + 1 is fragment (nt, s) as it stands. The QK head's
+    // first V head writes the Q fragments.
+    if (wave < CT) {
+      const int nt = wave, r = 16 * nt + l16;
+      if (r >= len) {
+#pragma unroll
+        for (int ks = 0; ks < DKS; ++ks) qf[ks] = join<E>(zero_half<E>(), zero_half<E>());
+      }
+      if constexpr (P) {
+        // raw queries: the four lanes holding a row (one per quad) add their
+        // sums of squares, then scale it to unit length
+        float ss = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < DKS; ++ks) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss += to_f(qf[ks][e]) * to_f(qf[ks][e]);
+        }
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        const float inv = inv_norm(ss);
+#pragma unroll
+        for (int ks = 0; ks < DKS; ++ks) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qf[ks][e] = to_e<E>(to_f(qf[ks][e]) * inv);
+        }
+      }
+      if (lead) {
+        Frag<E>* qfg = reinterpret_cast<Frag<E>*>(a.q_frag) + (c * a.h_qk + hq) * G::Q_FR * 64;
+#pragma unroll
+        for (int ks = 0; ks < DKS; ++ks) qfg[(nt * DKS + ks) * 64 + lane] = qf[ks];
+      }
+      Frag<E>* pg = reinterpret_cast<Frag<E>*>(a.pmask) + (c * a.h_v + hv) * G::QK_FR * 64;
+      const float gr = sm.gb[0][r], vr = (float)(r < len);
+#pragma unroll
+      for (int s = 0; s < CKS; ++s) {
+        if (causal_zero(nt, s)) continue;            // all zero; the scan neither copies nor reads it
+        f32x4 t2[2] = {zero4(), zero4()};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int kt = 2 * s + h;
+          if (kt > nt || kt >= CT) continue;
+#pragma unroll
+          for (int ks = 0; ks < DKS; ++ks)
+            t2[h] = mma(load_frag<E>(&sm.u.ks[(16 * kt + l16) * KLD + 32 * ks], quad, D - 32 * ks), qf[ks], t2[h]);
+        }
+        Frag<E> v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = frag_k(s, quad, e);
+          const float m = (float)(j <= r) * vr;
+          v[e] = to_e<E>(t2[e >> 2][e & 3] * (__expf(fminf(gr - sm.gb[0][min(j, C - 1)], 0.f)) * m));
+        }
+        pg[(nt * CKS + s) * 64 + lane] = v;
+      }
+    }
+  }
+  {
+    // the scan's row-factor table exp(g_r), exp(min(g_L - g_r, 0)) (both
+    // zero past the chunk end), exp(g_L)
     float* dtg = a.dtab + (c * a.h_v + hv) * (2 * C + 4);
     const float gl = sm.gb[0][len - 1];
     if (tid < C) {
@@ -1140,33 +1257,34 @@ template <typename E, int D, int C>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int last) {
   const unsigned nc = (unsigned)a.max_chunks;
   const unsigned scan_groups = (unsigned)(a.num_seqs * a.h_v * ScanCfg<E, D, C>::NCB);
+  const dim3 g_qk(nc * (unsigned)a.h_qk), g_v(nc * (unsigned)a.h_v), g_scan(scan_groups);
   for (int stage = first; stage <= last; ++stage) {
-    switch (stage) {
-      // the backward pass (a.backward) takes no flags
-      case 1: {
-        const dim3 g(nc * (unsigned)a.h_qk);
-        if (a.backward) gdn_k1_chunk_prep<E, D, C, false, true><<<g, dim3(kBlock), 0, s>>>(a);
-        else if (a.prep) gdn_k1_chunk_prep<E, D, C, true, false><<<g, dim3(kBlock), 0, s>>>(a);
-        else gdn_k1_chunk_prep<E, D, C, false, false><<<g, dim3(kBlock), 0, s>>>(a);
-        break;
+    if (a.backward) {
+      // the backward pass (which takes no flags): kernel 1 lays out the
+      // fragments both directions need, kernel 2 adds its own, and the scan
+      // saves the chunk-start states and U
+      switch (stage) {
+        case 1: gdn_k1_chunk_prep<E, D, C, false, true><<<g_qk, dim3(kBlock), 0, s>>>(a); break;
+        case 2: gdn_k2_inverse_w<E, D, C, false, false, true><<<g_v, dim3(kBlock), 0, s>>>(a); break;
+        case 3: gdn_k3_scan<E, D, C, false, true><<<g_scan, dim3(kScanBlock), 0, s>>>(a); break;
+        default: return hipErrorInvalidValue;
       }
-      case 2: {
-        const dim3 g(nc * (unsigned)a.h_v);
-        if (a.backward) {
-          gdn_k2_inverse_w<E, D, C, false, false, true><<<g, dim3(kBlock), 0, s>>>(a);
-        } else if (a.prep) {
-          if (a.no_delta) gdn_k2_inverse_w<E, D, C, true, true, false><<<g, dim3(kBlock), 0, s>>>(a);
-          else gdn_k2_inverse_w<E, D, C, true, false, false><<<g, dim3(kBlock), 0, s>>>(a);
+      continue;
+    }
+    // the forward pass: kernel 2 (with kernel 1's work for its V head), then the scan
+    switch (stage) {
+      case 1:
+        if (a.prep) {
+          if (a.no_delta) gdn_k2_inverse_w<E, D, C, true, true, false><<<g_v, dim3(kBlock), 0, s>>>(a);
+          else gdn_k2_inverse_w<E, D, C, true, false, false><<<g_v, dim3(kBlock), 0, s>>>(a);
         } else {
-          if (a.no_delta) gdn_k2_inverse_w<E, D, C, false, true, false><<<g, dim3(kBlock), 0, s>>>(a);
-          else gdn_k2_inverse_w<E, D, C, false, false, false><<<g, dim3(kBlock), 0, s>>>(a);
+          if (a.no_delta) gdn_k2_inverse_w<E, D, C, false, true, false><<<g_v, dim3(kBlock), 0, s>>>(a);
+          else gdn_k2_inverse_w<E, D, C, false, false, false><<<g_v, dim3(kBlock), 0, s>>>(a);
         }
         break;
-      }
-      case 3:
-        if (a.backward) gdn_k3_scan<E, D, C, false, true><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a);
-        else if (a.no_delta) gdn_k3_scan<E, D, C, true, false><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a);
-        else gdn_k3_scan<E, D, C, false, false><<<dim3(scan_groups), dim3(kScanBlock), 0, s>>>(a);
+      case 2:
+        if (a.no_delta) gdn_k3_scan<E, D, C, true, false><<<g_scan, dim3(kScanBlock), 0, s>>>(a);
+        else gdn_k3_scan<E, D, C, false, false><<<g_scan, dim3(kScanBlock), 0, s>>>(a);
         break;
       default: return hipErrorInvalidValue;
     }

@@ -103,7 +103,7 @@ static void test_prefill_args() {
   CHECK(lay.total == p.ws.n && lay.max_chunks == 250 / 64 + 3);
   const int before = g_stub.launches;
   CHECK(p.run() == GDN_SUCCESS);
-  CHECK(g_stub.launches == before + 1 && g_stub.first == 1 && g_stub.last == 3);
+  CHECK(g_stub.launches == before + 1 && g_stub.first == 1 && g_stub.last == 2);
   const gdn::PrefillArgs& a = g_stub.prefill;
   CHECK(a.q == p.q.p && a.k == p.k.p && a.v == p.v.p && a.o == p.o.p && a.cu_seqlens == p.cu.p);
   CHECK(a.num_seqs == 3 && a.total_tokens == 250 && a.group == 3 && a.max_chunks == lay.max_chunks);

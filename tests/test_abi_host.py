@@ -140,7 +140,7 @@ def test_fwd_rejects_unsupported(lib):
 def test_stage_range_validation(lib):
     d = dims()
     vp = ctypes.c_void_p
-    for first, last in ((0, 3), (1, 4), (3, 2)):
+    for first, last in ((0, 2), (1, 3), (2, 1)):
         st = lib.gdn_chunk_fwd_stages(ctypes.byref(d), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
                                       vp(FAKE), None, None, vp(FAKE * 2), None, vp(FAKE * 4),
                                       ws_bytes(lib, d), None, first, last)

@@ -284,16 +284,12 @@ def test_stage_outputs_match_oracle_chunks(chunk):
         return wsc[off:off + count * torch.tensor([], dtype=dt).element_size()].view(dt)
 
     table = region(lay.chunk_table, nc * 4, torch.int32).view(nc, 4).numpy()
-    g = region(lay.gate_prefix, nc * 6 * chunk, torch.float32).view(nc, 6, chunk).double().numpy()
-    b = region(lay.beta_chunk, nc * 6 * chunk, torch.float32).view(nc, 6, chunk).double().numpy()
     tf = region(lay.tinv, nc * 6 * ct * cks * 512, torch.bfloat16).view(
         nc, 6, ct, cks, 64, 8).double().numpy()
     wf = region(lay.w, nc * 6 * ct * 4 * 512, torch.bfloat16).view(
         nc, 6, ct, 4, 64, 8).double().numpy()
     kt = region(lay.key_t, nc * 2 * 8 * cks * 512, torch.bfloat16).view(
         nc, 2, 8, cks, 64, 8).double().numpy()
-    qk = region(lay.qk, nc * 2 * ct * cks * 512, torch.bfloat16).view(
-        nc, 2, ct, cks, 64, 8).double().numpy()
     qf = region(lay.q_frag, nc * 2 * ct * 4 * 512, torch.bfloat16).view(
         nc, 2, ct, 4, 64, 8).double().numpy()
     pm = region(lay.pmask, nc * 6 * ct * cks * 512, torch.bfloat16).view(
@@ -307,8 +303,6 @@ def test_stage_outputs_match_oracle_chunks(chunk):
     for c, st in enumerate(stages):
         L, t0 = st["len"], st["start"]
         assert list(table[c]) == [st["seq"], t0, L, c - (0 if st["seq"] == 0 else n_seq0)]
-        check(g[c][:, :L], st["g"], torch.float32, f"g chunk {c}")
-        assert (b[c][:, :L] == b64[t0:t0 + L].T).all() and (b[c][:, L:] == 0).all()
         for h in range(6):
             # Tinv diag(b) against the oracle's Tinv, W against the oracle's W
             bh = b64[t0:t0 + L, h]
@@ -337,12 +331,6 @@ def test_stage_outputs_match_oracle_chunks(chunk):
             assert np.array_equal(ktm[:, :L], k64[t0:t0 + L, hq].T) and (ktm[:, L:] == 0).all()
             qfm = unfrag(qf[c, hq], chunk, 128)            # [r][d]
             assert np.array_equal(qfm[:L], q64[t0:t0 + L, hq]) and (qfm[L:] == 0).all()
-            qkm = unfrag(qk[c, hq], chunk, chunk)          # [query r][key j]
-            want = q64[t0:t0 + L, hq] @ k64[t0:t0 + L, hq].T
-            causal = np.tril(np.ones((L, L)), 0) > 0
-            tiles = (np.arange(L)[None, :] // 16) <= (np.arange(L)[:, None] // 16)
-            assert np.abs(qkm[:L, :L][causal] - want[causal]).max() < 2e-2
-            assert (qkm[:L, :L][~tiles] == 0).all()
     assert (table[len(stages):, 0] == -1).all()
 
 

@@ -5,6 +5,10 @@
     python -m linear_attention_recurrence_delta_amd.profiling traffic \
         --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV --copy-bytes N [--out JSON]
         -> HBM bytes per launch of each libgdn kernel
+    python -m linear_attention_recurrence_delta_amd.profiling mfma COUNTER_CSV KERNEL_STATS_CSV BENCH_JSON
+        -> per kernel: MFMA busy fraction, bf16 MFMA flops executed per launch,
+           the rate those flops give over the traced mean duration, and the
+           method's algorithmic flops beside them
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
 counter reads for a plain device copy of known size (bench.py
@@ -119,12 +123,58 @@ def traffic_table(traffic_path, bench_path):
     rows = ["| kernel | fetch (GB) | write (GB) | measured total (GB) | algorithmic (GB) | ratio |",
             "|---|---|---|---|---|---|"]
     for k, rec in kernels.items():
-        if k not in tr or rec.get("unit") != "GB/s":
+        if k not in tr or "hbm_frac" not in rec:
             continue
-        alg = rec["achieved"] * 1e9 * rec["ms"] * 1e-3
+        alg = rec["hbm_frac"] * PEAK_HBM_BYTES * rec["ms"] * 1e-3
         m = tr[k]
         rows.append(f"| {k} | {m['fetch_bytes'] / 1e9:.3f} | {m['write_bytes'] / 1e9:.3f} | "
                     f"{m['bytes_per_launch'] / 1e9:.3f} | {alg / 1e9:.3f} | {m['bytes_per_launch'] / alg:.2f} |")
+    return "\n".join(rows)
+
+
+PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+SIMD_NUM = 256 * 4            # MI355X: 256 CUs of 4 SIMDs
+
+
+def mean_durations(stats_csv):
+    """Kernel summary name -> mean duration (s) from a --stats CSV (the
+    calls of instances that share a summary name pooled)."""
+    tot, calls = {}, {}
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            k = short_name(r["Name"])
+            tot[k] = tot.get(k, 0.0) + float(r["TotalDurationNs"]) * 1e-9
+            calls[k] = calls.get(k, 0) + int(r["Calls"])
+    return {k: tot[k] / calls[k] for k in tot}
+
+
+def mfma_table(counter_csv, stats_csv, bench_path):
+    """Markdown table of the MFMA counters of each libgdn kernel: MfmaUtil
+    (busy MFMA cycles summed over SIMDs / (GRBM_GUI_ACTIVE x SIMD count)),
+    MfmaFlopsBF16 (512 x SQ_INSTS_VALU_MFMA_MOPS_BF16: the flops of the bf16
+    MFMA instructions the kernel executed, padding included) and the rate
+    those give over the kernel's mean traced duration, beside the method's
+    algorithmic flops from bench.py's line."""
+    util = counter_per_kernel(counter_csv, "MfmaUtil")
+    flops = counter_per_kernel(counter_csv, "MfmaFlopsBF16")
+    dur = mean_durations(stats_csv)
+    with open(bench_path) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    kernels = dict(line.get("kernels", {}))
+    kernels.update(line.get("backward", {}).get("kernels", {}))
+    rows = ["| kernel | MfmaUtil (%) | bf16 MFMA flops executed (G) | mean traced duration (us) | "
+            "executed rate (TFLOP/s) | executed / peak | algorithmic flops (G) | algorithmic / executed |",
+            "|---|---|---|---|---|---|---|---|"]
+    for k in sorted(set(util) & set(flops)):
+        if source_of(k) is None or k not in dur:
+            continue
+        rate = flops[k] / dur[k]
+        rec = kernels.get(k)
+        alg = rec["mfma_frac"] * PEAK_BF16_FLOPS * rec["ms"] * 1e-3 if rec and "mfma_frac" in rec else None
+        rows.append(f"| {k} | {util[k]:.1f} | {flops[k] / 1e9:.1f} | {dur[k] * 1e6:.1f} | {rate / 1e12:.1f} | "
+                    f"{rate / PEAK_BF16_FLOPS:.4f} | " + ("-" if alg is None else f"{alg / 1e9:.1f}") + " | "
+                    + ("-" if alg is None or not flops[k] else f"{alg / flops[k]:.2f}") + " |")
     return "\n".join(rows)
 
 
@@ -143,7 +193,14 @@ def main():
     tt = sub.add_parser("traffic-table")
     tt.add_argument("traffic_json")
     tt.add_argument("bench_json")
+    mf = sub.add_parser("mfma")
+    mf.add_argument("counter_csv")
+    mf.add_argument("stats_csv")
+    mf.add_argument("bench_json")
     args = ap.parse_args()
+    if args.cmd == "mfma":
+        print(mfma_table(args.counter_csv, args.stats_csv, args.bench_json))
+        return
     if args.cmd == "traffic-table":
         print(traffic_table(args.traffic_json, args.bench_json))
         return

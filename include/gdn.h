@@ -16,15 +16,23 @@
  *    contiguous row-major with the last dimension fastest; q, k, v, o and
  *    states must be 16-byte aligned, log_alpha, beta and cu_seqlens 4-byte.
  *  - The library allocates no device memory and keeps no global state
- *    besides a thread-local error string.
+ *    besides a thread-local error string (gdn_chunk_fwd_noalloc adds its
+ *    static device array, described there).
  *  - Calls enqueue work on `stream` (NULL = the default stream) and return
  *    without synchronising; device faults surface at the caller's next sync.
  *  - Invalid arguments return an error status before anything is enqueued;
  *    gdn_last_error_message() then says which argument.
  *  - Supported: dk == dv in {16, 128}; chunk in {16, 64}; h_v % h_qk == 0;
- *    dtype GDN_DTYPE_F32 or GDN_DTYPE_BF16 for q, k, v and o, except fp32
- *    prefill at head dim 128 with chunk 64 (GDN_ERROR_NOT_SUPPORTED; use
- *    chunk 16). Gates and states are always fp32.
+ *    dtype GDN_DTYPE_F32 or GDN_DTYPE_BF16 for q, k, v and o, except the
+ *    fp32 backward pass at head dim 128 with chunk 64
+ *    (GDN_ERROR_NOT_SUPPORTED; use chunk 16). Gates and states are always
+ *    fp32.
+ *  - Environment (read at each call, for debugging): GDN_DEBUG=1 makes the
+ *    prefill entry points (forward and backward) copy cu_seqlens to the host
+ *    and check it before launching, returning GDN_ERROR_INVALID_VALUE for a
+ *    table that breaks its contract (this synchronises the stream);
+ *    GDN_DEBUG_SYNC=1 makes every entry point wait for its stream after
+ *    enqueueing and report a failed kernel as GDN_ERROR_HIP.
  */
 #ifndef GDN_H_
 #define GDN_H_
@@ -97,8 +105,11 @@ typedef struct {
  *  cu_seqlens  [N+1] int32 device array: 0 = c_0 <= c_1 <= ... <= c_N = T,
  *              sequence n holds tokens [c_n, c_{n+1}); NULL means one
  *              sequence of T tokens (N must be 1). The contents are a
- *              precondition and are not checked. Empty sequences are allowed
- *              (their final state equals their initial state).
+ *              precondition, checked only under GDN_DEBUG=1; the kernels
+ *              clamp every entry into [0, T] (and each end to at least its
+ *              start), so a bad table gives wrong results but no access
+ *              outside the buffers described here. Empty sequences are
+ *              allowed (their final state equals their initial state).
  *  o           [T, h_v, dv]   dtype, written; must not alias any input
  *  final_state [N, h_v, dk, dv] fp32 or NULL; may alias init_state exactly
  *  workspace   device scratch of at least gdn_chunk_fwd_workspace_bytes()

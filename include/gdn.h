@@ -297,7 +297,6 @@ typedef struct {
   size_t tinv;         /* dtype [max_chunks][h_v]: (I + A)^{-1} diag(b) as MFMA fragments */
   size_t w;            /* dtype [max_chunks][h_v]: W = (I + A)^{-1} diag(b exp(g)) K as MFMA fragments */
   size_t key_t;        /* dtype [max_chunks][h_qk]: K^T as MFMA fragments */
-  size_t qk;           /* dtype [max_chunks][h_qk]: q_r . k_j (j-tile <= r-tile) as fragments (backward pass) */
   size_t q_frag;       /* dtype [max_chunks][h_qk]: Q as MFMA fragments */
   size_t pmask;        /* dtype [max_chunks][h_v]: q_r . k_j exp(g_r - g_j), j <= r, as fragments */
   size_t dtab;         /* fp32 [max_chunks][h_v][2C+4]: exp(g_r), exp(g_L - g_r), exp(g_L), pad */

@@ -38,7 +38,7 @@ class GdnWorkspaceLayout(ctypes.Structure):
     _fields_ = [("chunk_table", ctypes.c_size_t), ("seq_chunk_offset", ctypes.c_size_t),
                 ("gate_prefix", ctypes.c_size_t), ("beta_chunk", ctypes.c_size_t),
                 ("tinv", ctypes.c_size_t), ("w", ctypes.c_size_t), ("key_t", ctypes.c_size_t),
-                ("qk", ctypes.c_size_t), ("q_frag", ctypes.c_size_t), ("pmask", ctypes.c_size_t),
+                ("q_frag", ctypes.c_size_t), ("pmask", ctypes.c_size_t),
                 ("dtab", ctypes.c_size_t), ("total", ctypes.c_size_t),
                 ("max_chunks", ctypes.c_int64)]
 

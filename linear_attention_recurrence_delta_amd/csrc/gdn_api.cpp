@@ -93,7 +93,6 @@ Layout compute_layout(const gdn_dims_t& d) {
   L.v.tinv = take(NC * HV * CT * CKS * 512 * esz);
   L.v.w = take(NC * HV * CT * ((DT + 1) / 2) * 512 * esz);
   L.v.key_t = take(NC * HQ * DT * CKS * 512 * esz);
-  L.v.qk = take(NC * HQ * CT * CKS * 512 * esz);
   L.v.q_frag = take(NC * HQ * CT * ((DT + 1) / 2) * 512 * esz);
   L.v.pmask = take(NC * HV * CT * CKS * 512 * esz);
   L.v.dtab = take(NC * HV * (2 * C + 4) * 4);
@@ -293,7 +292,6 @@ gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims, const void* q, const v
   a.tinv = ws + L.v.tinv;
   a.w = ws + L.v.w;
   a.key_t = ws + L.v.key_t;
-  a.qk = ws + L.v.qk;
   a.q_frag = ws + L.v.q_frag;
   a.pmask = ws + L.v.pmask;
   a.dtab = reinterpret_cast<float*>(ws + L.v.dtab);
@@ -398,7 +396,6 @@ gdn_status_t gdn_chunk_bwd_stages(const gdn_dims_t* dims, const void* q, const v
   a.tinv = ws + F.tinv;
   a.w = ws + F.w;
   a.key_t = ws + F.key_t;
-  a.qk = ws + F.qk;
   a.q_frag = ws + F.q_frag;
   a.pmask = ws + F.pmask;
   a.dtab = reinterpret_cast<float*>(ws + F.dtab);

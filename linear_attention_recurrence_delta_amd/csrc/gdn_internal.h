@@ -33,7 +33,6 @@ struct PrefillArgs {
   void* tinv;               // [NC][HV] fragments of (I + A)^{-1} diag(b)
   void* w;                  // [NC][HV] fragments of W = (I + A)^{-1} diag(b exp(g)) K
   void* key_t;              // [NC][HQ] fragments of K^T
-  void* qk;                 // [NC][HQ] fragments of (q_r . k_j)
   void* q_frag;             // [NC][HQ] fragments of Q
   void* pmask;              // [NC][HV] fragments of the masked, decayed q.k products
   float* dtab;              // [NC][HV][2C+4] scan row factors exp(g), exp(g_L - g), exp(g_L)

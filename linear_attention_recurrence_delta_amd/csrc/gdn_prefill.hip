@@ -6,7 +6,7 @@
 // the first form of its update equation. For one V head and a chunk of L <= C
 // tokens entering with state S0 (r, i index tokens in the chunk):
 //
-//   g_r    = sum_{j<=r} log a_j                          kernel 1
+//   g_r    = sum_{j<=r} log a_j                          kernel 2 (kernel 1 in the backward pass)
 //   A[r,i] = b_r (k_r . k_i) exp(g_r - g_i)  (i < r)     kernel 2
 //   Tinv   = (I + A)^{-1}                                kernel 2
 //   W      = Tinv diag(b exp(g)) K                       kernel 2
@@ -22,10 +22,14 @@
 // scan splits a head's state into 16-column slices. exp() is only ever taken
 // of g_r - g_i with i <= r, a non-positive number.
 //
-// Kernel 1 also lays out K^T and the q.k products once per QK head, which
-// every V head of the group reads. Kernel 3 fuses the Ut construction, the
-// inter-chunk state scan and the output products: Ut, U and the per-chunk
-// states never leave the chip.
+// The forward pass is two launches. Kernel 2 runs once per (chunk, QK head):
+// it lays out K^T and Q once for the group's V heads, forms q.k and K K^T
+// once, and then each V head's gate prefix, inverse, W and masked q.k.
+// Kernel 3 fuses the Ut construction, the inter-chunk state scan and the
+// output products: Ut, U and the per-chunk states never leave the chip. The
+// backward pass runs kernel 1 first (the chunk table, g, b and the fragments
+// both directions need), then kernel 2's per-V-head form and the saving
+// form of kernel 3.
 //
 // Fragment layouts (see gdn_device.h for the lane/element order): a
 // "fragment" is 64 lanes x 8 elements; "frag (a, s)" of a matrix X means
@@ -33,8 +37,9 @@
 //   key_t [c][hq][D/16][C32] : frag (dt, s) of K^T   (row d,     k = token i)
 //   tinv  [c][hv][C/16][C32] : frag (rt, s) of Tinv diag(b) (row r, k = token i)
 //   w     [c][hv][C/16][D32] : frag (rt, s) of W     (row r,     k = d)
-//   qk    [c][hq][C/16][C32] : frag (nt, s) of (q_r . k_j) (col r = query, k = key j)
 //   q_frag[c][hq][C/16][D32] : frag (nt, s) of Q     (row r,     k = d)
+//   pmask [c][hv][C/16][C32] : frag (nt, s) of P = (q_r . k_j) exp(g_r - g_j) masked to
+//                              j <= r < L (col r = query, k = key j)
 // with C32 = ceil(C/32), D32 = ceil(D/32); entries past the chunk end are zero.
 #include <type_traits>
 
@@ -47,18 +52,18 @@ namespace gdn {
 namespace {
 
 // --------------------------------------------------------------------------
-// Kernel 1: per (chunk slot c, QK head hq): the chunk table, the in-chunk
-// prefix sums of log a and the per-chunk b of the QK head's V heads, and the
-// chunk's K^T, Q and q.k fragments (shared by the QK head's V heads).
+// Kernel 1 (backward pass): per (chunk slot c, QK head hq): the chunk
+// table, the in-chunk prefix sums of log a and the per-chunk b of the QK
+// head's V heads, and the chunk's K^T, K, Q^T and query-indexed q.k
+// fragments (shared by the QK head's V heads).
 // Every group scans the per-sequence chunk counts ceil(L_n / C) to find
 // which sequence owns slot c (slots past the last chunk are marked
 // seq = -1); the groups of QK head 0 publish the table entry, and slot 0's
 // the per-sequence first-chunk offsets. One wave per V head forms g with a
 // wavefront prefix sum; past a partial chunk's end g repeats the last valid
-// prefix (log a taken as 0) and b is 0. The q.k fragment (nt, s) is the pair
-// of accumulator tiles K_j Q_r^T of key tiles 2s and 2s + 1 (a tile after
-// the query tile nt stays zero): two vertically adjacent accumulator tiles
-// are a fragment as they stand.
+// prefix (log a taken as 0) and b is 0. Two vertically adjacent accumulator
+// tiles are a fragment as they stand, which is how the q.k fragments are
+// written.
 // --------------------------------------------------------------------------
 // Which sequence owns chunk slot c: every thread of the block calls this
 // (it synchronises the block) and gets (sequence, index in the sequence),
@@ -144,7 +149,7 @@ struct PrepSmem {
   int hit[2];
 };
 
-template <typename E, int D, int C, bool P, bool BW>
+template <typename E, int D, int C>
 __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   using SM = PrepSmem<E, D, C>;
@@ -187,7 +192,6 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
     // values (a load under a branch would be waited for on its own)
     const int64_t gi = (int64_t)(start + min(lane, len - 1)) * a.h_v + hv;
     float g = a.log_alpha[gi], b = a.beta[gi];
-    if constexpr (P) { g = neg_softplus(g); b = sigmoid_of(b); }
     if (lane >= len) { g = 0.f; b = 0.f; }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -207,12 +211,6 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
     if (r >= len) {
 #pragma unroll
       for (int e = 0; e < VE; ++e) { kv[p][e] = to_e<E>(0.f); qv[p][e] = to_e<E>(0.f); }
-    }
-    if constexpr (P) {
-      // raw q and k: the D / VE lanes holding a row (a whole, aligned group)
-      // scale it to unit length
-      normalize_slice<E, D, VE>(kv[p]);
-      normalize_slice<E, D, VE>(qv[p]);
     }
     if (idx < NV) {
       *reinterpret_cast<VLoad*>(&sm.ks[r * KLD + d]) = kv[p];
@@ -234,35 +232,11 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
     }
     ktg[it] = v;
   }
-  // Q fragments: frag (nt, s), lane row r, elements d (the forward pass's
-  // outputs only: the backward pass's scan forms none)
-  Frag<E>* qfg = reinterpret_cast<Frag<E>*>(a.q_frag) + (c * a.h_qk + hq) * G::Q_FR * 64;
-  for (int it = tid; !BW && it < G::Q_FR * 64; it += kBlock) {
-    const int f = it / 64, ln = it % 64, nt = f / DKS, s = f % DKS;
-    qfg[it] = load_frag<E>(&sm.qs[(16 * nt + (ln & 15)) * KLD + 32 * s], ln >> 4, D - 32 * s);
-  }
-  // q.k fragments: frag (nt, s), lane col = query r, elements key j (for
-  // the forward pass's outputs only)
-  Frag<E>* qkg = reinterpret_cast<Frag<E>*>(a.qk) + (c * a.h_qk + hq) * G::QK_FR * 64;
-  for (int f = wave; !BW && f < G::QK_FR; f += NW) {
-    const int nt = f / CKS, s = f % CKS;
-    f32x4 t2[2] = {zero4(), zero4()};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kt = 2 * s + h;
-      if (kt > nt || kt >= CT) continue;
-#pragma unroll
-      for (int ks = 0; ks < DKS; ++ks)
-        t2[h] = mma(load_frag<E>(&sm.ks[(16 * kt + l16) * KLD + 32 * ks], quad, D - 32 * ks),
-                    load_frag<E>(&sm.qs[(16 * nt + l16) * KLD + 32 * ks], quad, D - 32 * ks), t2[h]);
-    }
-    qkg[f * 64 + lane] = acc_to_frag<E>(t2[0], t2[1]);
-  }
-  if constexpr (BW) {
-    // backward-pass operands: K fragments (row r, k = d),
-    // Q^T fragments (row d, k = token r), and the q.k products with the
-    // query as contraction index: fragment (jt, s) is the pair of tiles
-    // Q_r K_j^T of query tiles 2s and 2s + 1 (zero before the key tile)
+  {
+    // K fragments (row r, k = d), Q^T fragments (row d, k = token r), and
+    // the q.k products with the query as contraction index: fragment
+    // (jt, s) is the pair of tiles Q_r K_j^T of query tiles 2s and 2s + 1
+    // (zero before the key tile)
     Frag<E>* kfg = reinterpret_cast<Frag<E>*>(a.k_frag) + (c * a.h_qk + hq) * G::Q_FR * 64;
     for (int it = tid; it < G::Q_FR * 64; it += kBlock) {
       const int f = it / 64, ln = it % 64, nt = f / DKS, s = f % DKS;
@@ -299,16 +273,16 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
 }
 
 // --------------------------------------------------------------------------
-// Kernel 2: per (chunk, V head): A = strict_lower(b_r (k_r . k_i)
-// exp(g_r - g_i)), Tinv = (I + A)^{-1}, and the operands the scan takes from
-// it: the fragments of Tinv diag(b) (the right factor of Ut) and of
+// Kernel 2: A = strict_lower(b_r (k_r . k_i) exp(g_r - g_i)) and
+// Tinv = (I + A)^{-1} per (chunk, V head), and the operands the scan takes
+// from them: the fragments of Tinv diag(b) (the right factor of Ut) and of
 // W = Tinv diag(b exp(g)) K; also the V head's masked, decayed q.k
 // fragments and the scan's row-factor table.
-// K K^T is formed with MFMA from the staged keys; A's entries are made in
-// the products' epilogue. A and Tinv share one C x C fp32 array in LDS (over
-// the keys, which are dead by then): A's blocks below the diagonal stay in
-// place, Tinv's diagonal blocks replace A's, and Tinv's blocks below the
-// diagonal are stored transposed in the blocks above it, so that
+// K K^T is formed with MFMA from the staged keys; A's entries are made from
+// the products' accumulators. A and Tinv share one C x C fp32 array in LDS
+// (over the keys, which are dead by then): A's blocks below the diagonal
+// stay in place, Tinv's diagonal blocks replace A's, and Tinv's blocks below
+// the diagonal are stored transposed in the blocks above it, so that
 // Tinv[r][i] sits at [i][r] when r's block is below i's. Tinv is assembled
 // blockwise in fp32: the 16 x 16 diagonal blocks by forward substitution
 // (one lane per column, the four blocks side by side in one wave), then the
@@ -317,6 +291,11 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
 // with fp32 16x16x4 MFMAs, one block per wave per distance. W^T = K^T
 // (Tinv diag(b exp(g)))^T is contracted over tokens, wave w taking d-tiles
 // 2w and 2w + 1, whose accumulator pairs are W's fragments (rt, w).
+// Two forms share that code (k2_invert_and_write): the forward pass runs
+// one workgroup per (chunk, QK head), which does the QK head's work once
+// and then takes the group's V heads in turn (gdn_k2_group_fwd); the
+// backward pass one per (chunk, V head), reading kernel 1's outputs
+// (gdn_k2_inverse_w).
 // --------------------------------------------------------------------------
 
 template <typename E, int D, int C>
@@ -337,286 +316,57 @@ struct InvSmem {
     float x[4][16 * XLD];              // one 16 x 16 scratch tile per wave (blocks below the diagonal)
     Frag<E> tbg[G::T_FR * 64];         // then the Tinv diag(b exp(g)) fragments
   } v;
-  float gb[2][C];                      // g and b of this V head
+  float gb[2][C];                      // g and b of the current V head
 };
 
-template <typename E, int D, int C, bool P, bool ND, bool BW>
-// six workgroups per CU: 26 KB of LDS and at most 80 VGPRs each
-__global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs a) {
+// Lower tile t of a CT x CT tile grid (on and below the diagonal, row by
+// row) -> its row and column tile.
+__device__ __forceinline__ int2 lower_tile(int t) {
+  int mi = 0;
+  while ((mi + 1) * (mi + 2) / 2 <= t) ++mi;
+  return make_int2(mi, t - mi * (mi + 1) / 2);
+}
+
+// The scan's row-factor table of one (chunk, V head): exp(g_r),
+// exp(min(g_L - g_r, 0)) (both zero past the chunk end), exp(g_L); from g
+// in sm.gb.
+template <typename E, int D, int C>
+__device__ __forceinline__ void write_row_factors(const InvSmem<E, D, C>& sm, float* dtg, int len, int tid) {
+  const float gl = sm.gb[0][len - 1];
+  if (tid < C) {
+    const float valid = (float)(tid < len);
+    dtg[tid] = __expf(sm.gb[0][tid]) * valid;
+    dtg[C + tid] = __expf(fminf(gl - sm.gb[0][tid], 0.f)) * valid;
+  } else if (tid < C + 4) {
+    dtg[C + tid] = (tid == C) ? __expf(gl) : 0.f;
+  }
+}
+
+// A from the K K^T tiles and this V head's g and b (sm.gb), the blocked
+// inverse, and the Tinv diag(b) and W fragments of (chunk, V head) ch
+// (backward form: also Tinv^T and the W^T fragments). Every thread of the
+// block calls it; it synchronises the block. kk holds this wave's lower K K^T
+// tiles (wave + NW u); kta, ktb the K^T fragments of its W d-tiles.
+template <typename E, int D, int C, bool BW, int TPW>
+__device__ __forceinline__ void k2_invert_and_write(InvSmem<E, D, C>& sm, const PrefillArgs& a, int64_t ch,
+                                                    const f32x4 (&kk)[TPW], const Frag<E> (&kta)[Cfg<E, D, C>::CKS],
+                                                    const Frag<E> (&ktb)[Cfg<E, D, C>::CKS], int tid, int lane,
+                                                    int wave, int quad, int l16) {
   using G = Cfg<E, D, C>;
   using SM = InvSmem<E, D, C>;
-  constexpr int CT = G::CT, CKS = G::CKS, DT = G::DT, DKS = G::DKS, KLD = SM::KLD, FLD = SM::FLD, XLD = SM::XLD;
-  constexpr int NW = kBlock / 64;
-  static_assert(DKS <= NW && CT <= 4, "one W d-step pair per wave, diagonal blocks in one wave");
-  constexpr int VE = 16 / (int)sizeof(E);                 // elements per 16-byte load
-  typedef E VLoad __attribute__((ext_vector_type(VE)));
-  __shared__ SM sm;
-  // the V heads of one (chunk, QK head), which read the same keys, are
-  // consecutive logical ids and so share an XCD
-  const int64_t lid = xcd_local_id(blockIdx.x, gridDim.x);
-  const int64_t c = lid / a.h_v;
-  const int hv = (int)(lid % a.h_v);
-  const int hq = hv / a.group;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, l16 = lane & 15;
-  // The forward pass does kernel 1's work here, for this V head: the chunk
-  // lookup, the gate prefix sums and the q.k products; the QK head's first
-  // V head also lays out the K^T and Q fragments for the scan. The backward
-  // pass reads those from kernel 1.
-  constexpr bool FU = !BW;
-  int start, len;
-  if constexpr (FU) {
-    const int2 loc = locate_chunk<C>(a, c, hv == 0, sm.v.loc.scan, sm.v.loc.hit);
-    if (loc.x < 0) return;
-    const int2 sr = seq_range(a, loc.x);
-    start = sr.x + loc.y * C;
-    len = min(C, sr.y - start);
-  } else {
-    const int4 tab = reinterpret_cast<const int4*>(a.chunk_table)[c];
-    if (tab.x < 0) return;
-    start = tab.y;
-    len = tab.z;
-  }
-  const bool lead = hv % a.group == 0;
+  constexpr int CT = G::CT, CKS = G::CKS, DT = G::DT, DKS = G::DKS, FLD = SM::FLD, XLD = SM::XLD;
+  constexpr int NW = kBlock / 64, NTILE = CT * (CT + 1) / 2;
   float* at = sm.u.at;
-
-  // K^T fragments of this wave's W d-tiles: from kernel 1, issued first so
-  // that they arrive during the inverse (backward pass), or gathered from
-  // the staged keys below (forward pass)
-  const int ksd = wave;
-  Frag<E> kta[CKS], ktb[CKS];
-  if (BW && ksd < DKS) {
-    const Frag<E>* ktg = reinterpret_cast<const Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
-#pragma unroll
-    for (int s = 0; s < CKS; ++s) {
-      kta[s] = ktg[((2 * ksd) * CKS + s) * 64 + lane];
-      if (2 * ksd + 1 < DT) ktb[s] = ktg[((2 * ksd + 1) * CKS + s) * 64 + lane];
-    }
-  }
-  // forward pass: wave w's query tile w, its Q fragments straight from q
-  // (rows past the chunk end read its last row and are zeroed below)
-  Frag<E> qf[DKS];
-  if (FU && wave < CT) {
-    const E* row = static_cast<const E*>(a.q) + ((int64_t)(start + min(16 * wave + l16, len - 1)) * a.h_qk + hq) * D;
-#pragma unroll
-    for (int ks = 0; ks < DKS; ++ks) qf[ks] = load_frag<E>(row + 32 * ks, quad, D - 32 * ks);
-  }
-  // g and b of this V head: from kernel 1 (threads below 2 C), or the
-  // in-chunk prefix sum of log a in wave 0, lane r holding token r (lanes
-  // past the chunk end read its last token and then take the no-op values
-  // log a = 0, b = 0)
-  float gbv = 0.f, gw = 0.f, bw = 0.f;
-  if (BW && tid < 2 * C) {
-    const int64_t o = (c * a.h_v + hv) * C + (tid % C);
-    gbv = (tid < C) ? a.gate_prefix[o] : a.beta_chunk[o];
-  }
-  if (FU && wave == 0) {
-    const int64_t gi = (int64_t)(start + min(lane, len - 1)) * a.h_v + hv;
-    gw = a.log_alpha[gi];
-    bw = a.beta[gi];
-  }
-  // the chunk's keys, all loads issued before the first is used (rows past
-  // the chunk end read its last row and are zeroed; threads past the C x D
-  // block repeat its last load and store nothing)
-  const E* kg = static_cast<const E*>(a.k);
-  constexpr int NV = C * D / VE, NL = (NV + kBlock - 1) / kBlock;
-  if constexpr (!ND || FU) {
-    VLoad kv[NL];
-#pragma unroll
-    for (int p = 0; p < NL; ++p) {
-      const int idx = min(tid + p * kBlock, NV - 1);
-      const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
-      kv[p] = *reinterpret_cast<const VLoad*>(kg + ((int64_t)(start + min(r, len - 1)) * a.h_qk + hq) * D + d);
-    }
-#pragma unroll
-    for (int p = 0; p < NL; ++p) {
-      const int idx = tid + p * kBlock;
-      const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
-      if (r >= len) {
-#pragma unroll
-        for (int e = 0; e < VE; ++e) kv[p][e] = to_e<E>(0.f);
-      }
-      // raw keys: unit rows
-      if constexpr (P) normalize_slice<E, D, VE>(kv[p]);
-      if (idx < NV) *reinterpret_cast<VLoad*>(&sm.u.ks[r * KLD + d]) = kv[p];
-    }
-  }
-  if (BW && tid < 2 * C) sm.gb[tid / C][tid % C] = gbv;
-  if (FU && wave == 0) {
-    if constexpr (P) { gw = neg_softplus(gw); bw = sigmoid_of(bw); }
-    if (lane >= len) { gw = 0.f; bw = 0.f; }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float x = __shfl_up(gw, off);
-      if (lane >= off) gw += x;
-    }
-    if (lane < C) { sm.gb[0][lane] = gw; sm.gb[1][lane] = bw; }
-  }
-  __syncthreads();
-
-  if constexpr (FU) {
-    // K^T fragments (row d, k = token) gathered from the staged keys: this
-    // wave's W d-tiles; the QK head's first V head also writes them for the
-    // scan (the waves' d-tiles cover all of them)
-    if (ksd < DKS) {
-#pragma unroll
-      for (int s = 0; s < CKS; ++s) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = frag_k(s, quad, e);
-          kta[s][e] = (i < C) ? sm.u.ks[i * KLD + 32 * ksd + l16] : to_e<E>(0.f);
-          if (2 * ksd + 1 < DT) ktb[s][e] = (i < C) ? sm.u.ks[i * KLD + 32 * ksd + 16 + l16] : to_e<E>(0.f);
-        }
-      }
-      if (lead) {
-        Frag<E>* ktg = reinterpret_cast<Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
-#pragma unroll
-        for (int s = 0; s < CKS; ++s) {
-          ktg[((2 * ksd) * CKS + s) * 64 + lane] = kta[s];
-          if (2 * ksd + 1 < DT) ktg[((2 * ksd + 1) * CKS + s) * 64 + lane] = ktb[s];
-        }
-      }
-    }
-    // q.k for query tile nt = wave and the scan's P fragments from it,
-    // P[r][j] = (q_r . k_j) exp(g_r - g_j) for j <= r < len, else 0 (the
-    // exponent is clamped at 0 so that masked entries cannot overflow
-    // before being zeroed). The pair of accumulator tiles K_j Q_r^T of key
-    // tiles 2s and 2s + 1 is fragment (nt, s) as it stands. The QK head's
-    // first V head writes the Q fragments.
-    if (wave < CT) {
-      const int nt = wave, r = 16 * nt + l16;
-      if (r >= len) {
-#pragma unroll
-        for (int ks = 0; ks < DKS; ++ks) qf[ks] = join<E>(zero_half<E>(), zero_half<E>());
-      }
-      if constexpr (P) {
-        // raw queries: the four lanes holding a row (one per quad) add their
-        // sums of squares, then scale it to unit length
-        float ss = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < DKS; ++ks) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ss += to_f(qf[ks][e]) * to_f(qf[ks][e]);
-        }
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
-        const float inv = inv_norm(ss);
-#pragma unroll
-        for (int ks = 0; ks < DKS; ++ks) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qf[ks][e] = to_e<E>(to_f(qf[ks][e]) * inv);
-        }
-      }
-      if (lead) {
-        Frag<E>* qfg = reinterpret_cast<Frag<E>*>(a.q_frag) + (c * a.h_qk + hq) * G::Q_FR * 64;
-#pragma unroll
-        for (int ks = 0; ks < DKS; ++ks) qfg[(nt * DKS + ks) * 64 + lane] = qf[ks];
-      }
-      Frag<E>* pg = reinterpret_cast<Frag<E>*>(a.pmask) + (c * a.h_v + hv) * G::QK_FR * 64;
-      const float gr = sm.gb[0][r], vr = (float)(r < len);
-#pragma unroll
-      for (int s = 0; s < CKS; ++s) {
-        if (causal_zero(nt, s)) continue;            // all zero; the scan neither copies nor reads it
-        f32x4 t2[2] = {zero4(), zero4()};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int kt = 2 * s + h;
-          if (kt > nt || kt >= CT) continue;
-#pragma unroll
-          for (int ks = 0; ks < DKS; ++ks)
-            t2[h] = mma(load_frag<E>(&sm.u.ks[(16 * kt + l16) * KLD + 32 * ks], quad, D - 32 * ks), qf[ks], t2[h]);
-        }
-        Frag<E> v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = frag_k(s, quad, e);
-          const float m = (float)(j <= r) * vr;
-          v[e] = to_e<E>(t2[e >> 2][e & 3] * (__expf(fminf(gr - sm.gb[0][min(j, C - 1)], 0.f)) * m));
-        }
-        pg[(nt * CKS + s) * 64 + lane] = v;
-      }
-    }
-  }
-  {
-    // the scan's row-factor table exp(g_r), exp(min(g_L - g_r, 0)) (both
-    // zero past the chunk end), exp(g_L)
-    float* dtg = a.dtab + (c * a.h_v + hv) * (2 * C + 4);
-    const float gl = sm.gb[0][len - 1];
-    if (tid < C) {
-      const float valid = (float)(tid < len);
-      dtg[tid] = __expf(sm.gb[0][tid]) * valid;
-      dtg[C + tid] = __expf(fminf(gl - sm.gb[0][tid], 0.f)) * valid;
-    } else if (tid < C + 4) {
-      dtg[C + tid] = (tid == C) ? __expf(gl) : 0.f;
-    }
-  }
-  if constexpr (BW) {
-    // backward pass: P^T fragments (jt, s), lane row key j, elements query r,
-    // from kernel 1's query-indexed q.k fragments
-    const Frag<E>* kqg = reinterpret_cast<const Frag<E>*>(a.kq) + (c * a.h_qk + hq) * G::QK_FR * 64;
-    Frag<E>* ptg = reinterpret_cast<Frag<E>*>(a.pt) + (c * a.h_v + hv) * G::QK_FR * 64;
-    for (int it = tid; it < G::QK_FR * 64; it += kBlock) {
-      const int f = it / 64, ln = it % 64, jt = f / CKS, s = f % CKS, q4 = ln >> 4;
-      const int j = 16 * jt + (ln & 15);
-      const Frag<E> x = kqg[it];
-      const float gj = sm.gb[0][j];
-      Frag<E> v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = frag_k(s, q4, e);
-        const float m = (float)(j <= r && r < len);
-        v[e] = to_e<E>(to_f(x[e]) * (__expf(fminf(sm.gb[0][min(r, C - 1)] - gj, 0.f)) * m));
-      }
-      ptg[it] = v;
-    }
-  }
-  if constexpr (ND) {
-    // gate-only variant: no delta rule, so Tinv = I; the scan's Ut = diag(b) V
-    // takes diag(b) in place of Tinv diag(b), and W is not used
-    Frag<E>* tg = reinterpret_cast<Frag<E>*>(a.tinv) + (c * a.h_v + hv) * G::T_FR * 64;
-    for (int it = tid; it < G::T_FR * 64; it += kBlock) {
-      const int f = it / 64, ln = it % 64, rt = f / CKS, s = f % CKS, q4 = ln >> 4;
-      if (causal_zero(rt, s)) continue;              // all zero; the scan neither copies nor reads it
-      const int r = 16 * rt + (ln & 15);
-      Frag<E> vb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = frag_k(s, q4, e);
-        vb[e] = to_e<E>((i == r) ? sm.gb[1][r] : 0.f);
-      }
-      tg[it] = vb;
-    }
-    return;
-  }
-
-  // K K^T tiles on and below the diagonal, lower tile t -> (mi, ni)
-  constexpr int NTILE = CT * (CT + 1) / 2, TPW = (NTILE + NW - 1) / NW;
-  f32x4 kk[TPW];
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int t = wave + u * NW;
-    kk[u] = zero4();
-    if (t < NTILE) {
-      int mi = 0;
-      while ((mi + 1) * (mi + 2) / 2 <= t) ++mi;
-      const int ni = t - mi * (mi + 1) / 2;
-#pragma unroll
-      for (int ks = 0; ks < DKS; ++ks)
-        kk[u] = mma(load_frag<E>(&sm.u.ks[(16 * mi + l16) * KLD + 32 * ks], quad, D - 32 * ks),
-                    load_frag<E>(&sm.u.ks[(16 * ni + l16) * KLD + 32 * ks], quad, D - 32 * ks), kk[u]);
-    }
-  }
-  __syncthreads();     // the keys are dead from here on; their LDS holds A and Tinv
+  // A = strict_lower(b_r (k_r . k_i) exp(g_r - g_i))
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int t = wave + u * NW;
     if (t >= NTILE) continue;
-    int mi = 0;
-    while ((mi + 1) * (mi + 2) / 2 <= t) ++mi;
-    const int ni = t - mi * (mi + 1) / 2;
-    const int i = 16 * ni + l16;
+    const int2 tl = lower_tile(t);
+    const int i = 16 * tl.y + l16;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 16 * mi + 4 * quad + e;
+      const int r = 16 * tl.x + 4 * quad + e;
       if (i < r) at[r * FLD + i] = sm.gb[1][r] * kk[u][e] * __expf(fminf(sm.gb[0][r] - sm.gb[0][i], 0.f));
     }
   }
@@ -662,7 +412,7 @@ __global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs 
   }
   if constexpr (BW) {
     // backward pass: Tinv^T row-major, tt[i][r] = Tinv[r][i]
-    E* ttg = static_cast<E*>(a.tt) + (c * a.h_v + hv) * C * C;
+    E* ttg = static_cast<E*>(a.tt) + ch * C * C;
     for (int idx = tid; idx < C * C; idx += kBlock) {
       const int i = idx / C, r = idx % C;
       const float t = ((r >> 4) > (i >> 4)) ? at[i * FLD + r] : (((r >> 4) == (i >> 4)) ? at[r * FLD + i] : 0.f);
@@ -670,7 +420,7 @@ __global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs 
     }
   }
   // Tinv diag(b) fragments to the workspace, Tinv diag(b exp(g)) to LDS
-  Frag<E>* tg = reinterpret_cast<Frag<E>*>(a.tinv) + (c * a.h_v + hv) * G::T_FR * 64;
+  Frag<E>* tg = reinterpret_cast<Frag<E>*>(a.tinv) + ch * G::T_FR * 64;
   for (int it = tid; it < G::T_FR * 64; it += kBlock) {
     const int f = it / 64, ln = it % 64, rt = f / CKS, s = f % CKS, q4 = ln >> 4;
     if (causal_zero(rt, s)) continue;                // all zero; no product reads it
@@ -691,8 +441,9 @@ __global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs 
     sm.v.tbg[it] = vg;
   }
   __syncthreads();
+  const int ksd = wave;
   if (ksd < DKS) {
-    Frag<E>* wg = reinterpret_cast<Frag<E>*>(a.w) + (c * a.h_v + hv) * G::W_FR * 64;
+    Frag<E>* wg = reinterpret_cast<Frag<E>*>(a.w) + ch * G::W_FR * 64;
 #pragma unroll
     for (int rt = 0; rt < CT; ++rt) {
       f32x4 acc0 = zero4(), acc1 = zero4();
@@ -709,7 +460,7 @@ __global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs 
       // backward pass: W^T fragments (dt, s), lane row d, elements token r:
       // the pair of W tiles (r-tiles 2s, 2s + 1; d-tile dt) formed as
       // Tinv diag(b exp(g)) K
-      Frag<E>* wtg = reinterpret_cast<Frag<E>*>(a.wt) + (c * a.h_v + hv) * G::KT_FR * 64;
+      Frag<E>* wtg = reinterpret_cast<Frag<E>*>(a.wt) + ch * G::KT_FR * 64;
 #pragma unroll
       for (int s = 0; s < CKS; ++s) {
         f32x4 pa[2] = {zero4(), zero4()}, pb[2] = {zero4(), zero4()};
@@ -730,6 +481,320 @@ __global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs 
       }
     }
   }
+}
+
+// the chunk's keys into sm.u.ks, all loads issued before the first is used
+// (rows past the chunk end read its last row and are zeroed; threads past
+// the C x D block repeat its last load and store nothing); P: raw keys,
+// scaled to unit rows
+template <typename E, int D, int C, bool P>
+__device__ __forceinline__ void stage_keys(InvSmem<E, D, C>& sm, const PrefillArgs& a, int start, int len, int hq,
+                                           int tid) {
+  constexpr int VE = 16 / (int)sizeof(E), KLD = InvSmem<E, D, C>::KLD;
+  typedef E VLoad __attribute__((ext_vector_type(VE)));
+  const E* kg = static_cast<const E*>(a.k);
+  constexpr int NV = C * D / VE, NL = (NV + kBlock - 1) / kBlock;
+  VLoad kv[NL];
+#pragma unroll
+  for (int p = 0; p < NL; ++p) {
+    const int idx = min(tid + p * kBlock, NV - 1);
+    const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
+    kv[p] = *reinterpret_cast<const VLoad*>(kg + ((int64_t)(start + min(r, len - 1)) * a.h_qk + hq) * D + d);
+  }
+#pragma unroll
+  for (int p = 0; p < NL; ++p) {
+    const int idx = tid + p * kBlock;
+    const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
+    if (r >= len) {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) kv[p][e] = to_e<E>(0.f);
+    }
+    if constexpr (P) normalize_slice<E, D, VE>(kv[p]);
+    if (idx < NV) *reinterpret_cast<VLoad*>(&sm.u.ks[r * KLD + d]) = kv[p];
+  }
+}
+
+// K K^T tiles on and below the diagonal from the staged keys: wave w's
+// lower tiles w + NW u
+template <typename E, int D, int C, int TPW>
+__device__ __forceinline__ void key_products(const InvSmem<E, D, C>& sm, f32x4 (&kk)[TPW], int wave, int quad,
+                                             int l16) {
+  using G = Cfg<E, D, C>;
+  constexpr int DKS = G::DKS, KLD = InvSmem<E, D, C>::KLD, NW = kBlock / 64, NTILE = G::CT * (G::CT + 1) / 2;
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int t = wave + u * NW;
+    kk[u] = zero4();
+    if (t < NTILE) {
+      const int2 tl = lower_tile(t);
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks)
+        kk[u] = mma(load_frag<E>(&sm.u.ks[(16 * tl.x + l16) * KLD + 32 * ks], quad, D - 32 * ks),
+                    load_frag<E>(&sm.u.ks[(16 * tl.y + l16) * KLD + 32 * ks], quad, D - 32 * ks), kk[u]);
+    }
+  }
+}
+
+// Forward form: one workgroup per (chunk, QK head). What depends only on
+// the QK head is done once: the chunk lookup, the keys and queries, the K^T
+// and Q fragments the scan reads, the q.k products and K K^T (both kept in
+// registers). The group's V heads are then taken in turn: the gate prefix,
+// the P fragments and row-factor table, then A, the inverse, Tinv diag(b)
+// and W. The gates of each V head are requested while the previous one is
+// processed. (One workgroup per V head, each repeating the QK head's work,
+// took 0.63 ms against 0.51 ms on the 64K-token layer.)
+// five workgroups per CU: 26 KB of LDS and at most 96 VGPRs each
+template <typename E, int D, int C, bool P, bool ND>
+__global__ __launch_bounds__(kBlock, 5) void gdn_k2_group_fwd(const PrefillArgs a) {
+  using G = Cfg<E, D, C>;
+  using SM = InvSmem<E, D, C>;
+  constexpr int CT = G::CT, CKS = G::CKS, DT = G::DT, DKS = G::DKS, KLD = SM::KLD;
+  constexpr int NW = kBlock / 64, NTILE = CT * (CT + 1) / 2, TPW = (NTILE + NW - 1) / NW;
+  static_assert(DKS <= NW && CT <= 4, "one W d-step pair per wave, diagonal blocks in one wave");
+  __shared__ SM sm;
+  // the QK heads of one chunk, which read the same gate lines, are
+  // consecutive logical ids and so share an XCD
+  const int64_t lid = xcd_local_id(blockIdx.x, gridDim.x);
+  const int64_t c = lid / a.h_qk;
+  const int hq = (int)(lid % a.h_qk);
+  // lane indices are re-made opaque at the top of every V head's pass (see
+  // there); the wave index is uniform
+  int tid = threadIdx.x, lane = tid & 63, quad = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int2 loc = locate_chunk<C>(a, c, hq == 0, sm.v.loc.scan, sm.v.loc.hit);
+  if (loc.x < 0) return;
+  const int2 sr = seq_range(a, loc.x);
+  const int start = sr.x + loc.y * C;
+  const int len = min(C, sr.y - start);
+
+  // wave w's query tile w: its Q fragments straight from q (rows past the
+  // chunk end read its last row and are zeroed below)
+  Frag<E> qf[DKS];
+  if (wave < CT) {
+    const E* row = static_cast<const E*>(a.q) + ((int64_t)(start + min(16 * wave + l16, len - 1)) * a.h_qk + hq) * D;
+#pragma unroll
+    for (int ks = 0; ks < DKS; ++ks) qf[ks] = load_frag<E>(row + 32 * ks, quad, D - 32 * ks);
+  }
+  // the gates of V head h of the group: wave 0, lane r holding token r
+  // (lanes past the chunk end read its last token)
+  float gw = 0.f, bw = 0.f;
+  auto load_gates = [&](int h) __attribute__((always_inline)) {
+    const int64_t gi = (int64_t)(start + min(lane, len - 1)) * a.h_v + hq * a.group + h;
+    gw = a.log_alpha[gi];
+    bw = a.beta[gi];
+  };
+  if (wave == 0) load_gates(0);
+  stage_keys<E, D, C, P>(sm, a, start, len, hq, tid);
+  __syncthreads();
+
+  // K^T fragments (row d, k = token) of this wave's W d-tiles, gathered
+  // from the staged keys and written for the scan (the waves' d-tiles
+  // cover all of them)
+  const int ksd = wave;
+  Frag<E> kta[CKS], ktb[CKS];
+  if (ksd < DKS) {
+#pragma unroll
+    for (int s = 0; s < CKS; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = frag_k(s, quad, e);
+        kta[s][e] = (i < C) ? sm.u.ks[i * KLD + 32 * ksd + l16] : to_e<E>(0.f);
+        if (2 * ksd + 1 < DT) ktb[s][e] = (i < C) ? sm.u.ks[i * KLD + 32 * ksd + 16 + l16] : to_e<E>(0.f);
+      }
+    }
+    Frag<E>* ktg = reinterpret_cast<Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
+#pragma unroll
+    for (int s = 0; s < CKS; ++s) {
+      ktg[((2 * ksd) * CKS + s) * 64 + lane] = kta[s];
+      if (2 * ksd + 1 < DT) ktg[((2 * ksd + 1) * CKS + s) * 64 + lane] = ktb[s];
+    }
+  }
+  // q.k of query tile nt = wave: the pair of accumulator tiles K_j Q_r^T of
+  // key tiles 2s and 2s + 1 (a key tile after the query tile stays zero);
+  // the Q fragments are written for the scan
+  const int nt = wave;
+  int rq = 16 * nt + l16;
+  f32x4 qk[CKS][2];
+#pragma unroll
+  for (int s = 0; s < CKS; ++s) { qk[s][0] = zero4(); qk[s][1] = zero4(); }
+  if (wave < CT) {
+    if (rq >= len) {
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks) qf[ks] = join<E>(zero_half<E>(), zero_half<E>());
+    }
+    if constexpr (P) {
+      // raw queries: the four lanes holding a row (one per quad) add their
+      // sums of squares, then scale it to unit length
+      float ss = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += to_f(qf[ks][e]) * to_f(qf[ks][e]);
+      }
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      const float inv = inv_norm(ss);
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][e] = to_e<E>(to_f(qf[ks][e]) * inv);
+      }
+    }
+    Frag<E>* qfg = reinterpret_cast<Frag<E>*>(a.q_frag) + (c * a.h_qk + hq) * G::Q_FR * 64;
+#pragma unroll
+    for (int ks = 0; ks < DKS; ++ks) qfg[(nt * DKS + ks) * 64 + lane] = qf[ks];
+#pragma unroll
+    for (int s = 0; s < CKS; ++s) {
+      if (causal_zero(nt, s)) continue;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kt = 2 * s + h;
+        if (kt > nt || kt >= CT) continue;
+#pragma unroll
+        for (int ks = 0; ks < DKS; ++ks)
+          qk[s][h] = mma(load_frag<E>(&sm.u.ks[(16 * kt + l16) * KLD + 32 * ks], quad, D - 32 * ks), qf[ks], qk[s][h]);
+      }
+    }
+  }
+  f32x4 kk[TPW];
+  if constexpr (!ND) key_products<E, D, C, TPW>(sm, kk, wave, quad, l16);
+  __syncthreads();     // the keys are dead from here on; their LDS holds A and Tinv
+
+  for (int h = 0; h < a.group; ++h) {
+    const int64_t ch = c * a.h_v + hq * a.group + h;
+    // keeps the compiler from hoisting every lane-dependent LDS address out
+    // of this loop (they would stay live across it and spill); recomputing
+    // them is a few ALU operations. The masks restore their ranges.
+    asm volatile("" : "+v"(tid), "+v"(lane), "+v"(quad), "+v"(l16), "+v"(rq));
+    tid &= kBlock - 1; lane &= 63; quad &= 3; l16 &= 15; rq &= 63;
+    if (wave == 0) {
+      // in-chunk prefix of log a (past the chunk end: log a = 0, b = 0),
+      // then the next V head's gates are requested
+      float g = gw, b = bw;
+      if constexpr (P) { g = neg_softplus(g); b = sigmoid_of(b); }
+      if (lane >= len) { g = 0.f; b = 0.f; }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float x = __shfl_up(g, off);
+        if (lane >= off) g += x;
+      }
+      if (lane < C) { sm.gb[0][lane] = g; sm.gb[1][lane] = b; }
+      if (h + 1 < a.group) load_gates(h + 1);
+    }
+    // (also: the previous V head's last readers of g, b and the LDS
+    // fragments are done)
+    __syncthreads();
+    // the scan's P fragments: P[r][j] = (q_r . k_j) exp(g_r - g_j) for
+    // j <= r < len, else 0 (the exponent is clamped at 0 so that masked
+    // entries cannot overflow before being zeroed)
+    if (wave < CT) {
+      Frag<E>* pg = reinterpret_cast<Frag<E>*>(a.pmask) + ch * G::QK_FR * 64;
+      const float gr = sm.gb[0][rq], vr = (float)(rq < len);
+#pragma unroll
+      for (int s = 0; s < CKS; ++s) {
+        if (causal_zero(nt, s)) continue;            // all zero; the scan neither copies nor reads it
+        Frag<E> v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = frag_k(s, quad, e);
+          const float m = (float)(j <= rq) * vr;
+          v[e] = to_e<E>(qk[s][e >> 2][e & 3] * (__expf(fminf(gr - sm.gb[0][min(j, C - 1)], 0.f)) * m));
+        }
+        pg[(nt * CKS + s) * 64 + lane] = v;
+      }
+    }
+    write_row_factors(sm, a.dtab + ch * (2 * C + 4), len, tid);
+    if constexpr (ND) {
+      // gate-only variant: no delta rule, so Tinv = I; the scan's Ut = diag(b) V
+      // takes diag(b) in place of Tinv diag(b), and W is not used
+      Frag<E>* tg = reinterpret_cast<Frag<E>*>(a.tinv) + ch * G::T_FR * 64;
+      for (int it = tid; it < G::T_FR * 64; it += kBlock) {
+        const int f = it / 64, ln = it % 64, rt = f / CKS, s = f % CKS, q4 = ln >> 4;
+        if (causal_zero(rt, s)) continue;            // all zero; the scan neither copies nor reads it
+        const int r = 16 * rt + (ln & 15);
+        Frag<E> vb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = frag_k(s, q4, e);
+          vb[e] = to_e<E>((i == r) ? sm.gb[1][r] : 0.f);
+        }
+        tg[it] = vb;
+      }
+      __syncthreads();   // the next V head's prefix overwrites g and b
+    } else {
+      k2_invert_and_write<E, D, C, false, TPW>(sm, a, ch, kk, kta, ktb, tid, lane, wave, quad, l16);
+    }
+  }
+}
+
+// Backward form: one workgroup per (chunk, V head), from kernel 1's chunk
+// table, gate prefix, per-chunk b and K^T fragments; it also writes the
+// P^T fragments (from kernel 1's query-indexed q.k), Tinv^T and the W^T
+// fragments that the gradient kernel reads.
+// six workgroups per CU: 26 KB of LDS and at most 80 VGPRs each
+template <typename E, int D, int C>
+__global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs a) {
+  using G = Cfg<E, D, C>;
+  using SM = InvSmem<E, D, C>;
+  constexpr int CT = G::CT, CKS = G::CKS, DT = G::DT, DKS = G::DKS;
+  constexpr int NW = kBlock / 64, NTILE = CT * (CT + 1) / 2, TPW = (NTILE + NW - 1) / NW;
+  static_assert(DKS <= NW && CT <= 4, "one W d-step pair per wave, diagonal blocks in one wave");
+  __shared__ SM sm;
+  // the V heads of one (chunk, QK head), which read the same keys, are
+  // consecutive logical ids and so share an XCD
+  const int64_t lid = xcd_local_id(blockIdx.x, gridDim.x);
+  const int64_t c = lid / a.h_v;
+  const int hv = (int)(lid % a.h_v);
+  const int hq = hv / a.group;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, l16 = lane & 15;
+  const int4 tab = reinterpret_cast<const int4*>(a.chunk_table)[c];
+  if (tab.x < 0) return;
+  const int start = tab.y, len = tab.z;
+  const int64_t ch = c * a.h_v + hv;
+
+  // K^T fragments of this wave's W d-tiles, issued first so that they
+  // arrive during the inverse
+  const int ksd = wave;
+  Frag<E> kta[CKS], ktb[CKS];
+  if (ksd < DKS) {
+    const Frag<E>* ktg = reinterpret_cast<const Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
+#pragma unroll
+    for (int s = 0; s < CKS; ++s) {
+      kta[s] = ktg[((2 * ksd) * CKS + s) * 64 + lane];
+      if (2 * ksd + 1 < DT) ktb[s] = ktg[((2 * ksd + 1) * CKS + s) * 64 + lane];
+    }
+  }
+  // g and b of this V head (threads below 2 C)
+  float gbv = 0.f;
+  if (tid < 2 * C) gbv = (tid < C) ? a.gate_prefix[ch * C + tid] : a.beta_chunk[ch * C + tid - C];
+  stage_keys<E, D, C, false>(sm, a, start, len, hq, tid);
+  if (tid < 2 * C) sm.gb[tid / C][tid % C] = gbv;
+  __syncthreads();
+  write_row_factors(sm, a.dtab + ch * (2 * C + 4), len, tid);
+  {
+    // P^T fragments (jt, s), lane row key j, elements query r, from kernel
+    // 1's query-indexed q.k fragments
+    const Frag<E>* kqg = reinterpret_cast<const Frag<E>*>(a.kq) + (c * a.h_qk + hq) * G::QK_FR * 64;
+    Frag<E>* ptg = reinterpret_cast<Frag<E>*>(a.pt) + ch * G::QK_FR * 64;
+    for (int it = tid; it < G::QK_FR * 64; it += kBlock) {
+      const int f = it / 64, ln = it % 64, jt = f / CKS, s = f % CKS, q4 = ln >> 4;
+      const int j = 16 * jt + (ln & 15);
+      const Frag<E> x = kqg[it];
+      const float gj = sm.gb[0][j];
+      Frag<E> v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = frag_k(s, q4, e);
+        const float m = (float)(j <= r && r < len);
+        v[e] = to_e<E>(to_f(x[e]) * (__expf(fminf(sm.gb[0][min(r, C - 1)] - gj, 0.f)) * m));
+      }
+      ptg[it] = v;
+    }
+  }
+  f32x4 kk[TPW];
+  key_products<E, D, C, TPW>(sm, kk, wave, quad, l16);
+  __syncthreads();     // the keys are dead from here on; their LDS holds A and Tinv
+  k2_invert_and_write<E, D, C, true, TPW>(sm, a, ch, kk, kta, ktb, tid, lane, wave, quad, l16);
 }
 
 // --------------------------------------------------------------------------
@@ -1264,22 +1329,22 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
       // fragments both directions need, kernel 2 adds its own, and the scan
       // saves the chunk-start states and U
       switch (stage) {
-        case 1: gdn_k1_chunk_prep<E, D, C, false, true><<<g_qk, dim3(kBlock), 0, s>>>(a); break;
-        case 2: gdn_k2_inverse_w<E, D, C, false, false, true><<<g_v, dim3(kBlock), 0, s>>>(a); break;
+        case 1: gdn_k1_chunk_prep<E, D, C><<<g_qk, dim3(kBlock), 0, s>>>(a); break;
+        case 2: gdn_k2_inverse_w<E, D, C><<<g_v, dim3(kBlock), 0, s>>>(a); break;
         case 3: gdn_k3_scan<E, D, C, false, true><<<g_scan, dim3(kScanBlock), 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
       }
       continue;
     }
-    // the forward pass: kernel 2 (with kernel 1's work for its V head), then the scan
+    // the forward pass: kernel 2 (per chunk and QK head, with kernel 1's work), then the scan
     switch (stage) {
       case 1:
         if (a.prep) {
-          if (a.no_delta) gdn_k2_inverse_w<E, D, C, true, true, false><<<g_v, dim3(kBlock), 0, s>>>(a);
-          else gdn_k2_inverse_w<E, D, C, true, false, false><<<g_v, dim3(kBlock), 0, s>>>(a);
+          if (a.no_delta) gdn_k2_group_fwd<E, D, C, true, true><<<g_qk, dim3(kBlock), 0, s>>>(a);
+          else gdn_k2_group_fwd<E, D, C, true, false><<<g_qk, dim3(kBlock), 0, s>>>(a);
         } else {
-          if (a.no_delta) gdn_k2_inverse_w<E, D, C, false, true, false><<<g_v, dim3(kBlock), 0, s>>>(a);
-          else gdn_k2_inverse_w<E, D, C, false, false, false><<<g_v, dim3(kBlock), 0, s>>>(a);
+          if (a.no_delta) gdn_k2_group_fwd<E, D, C, false, true><<<g_qk, dim3(kBlock), 0, s>>>(a);
+          else gdn_k2_group_fwd<E, D, C, false, false><<<g_qk, dim3(kBlock), 0, s>>>(a);
         }
         break;
       case 2:

@@ -110,7 +110,7 @@ static void test_prefill_args() {
   CHECK(a.backward == 0 && a.prep == 0 && a.no_delta == 0);
   // every workspace region starts inside the workspace, 256-byte aligned
   const void* regions[] = {a.chunk_table, a.seq_chunk_offset, a.gate_prefix, a.beta_chunk, a.tinv, a.w,
-                           a.key_t, a.qk, a.q_frag, a.pmask, a.dtab};
+                           a.key_t, a.q_frag, a.pmask, a.dtab};
   for (const void* r : regions) {
     CHECK(p.ws.holds(r, 1));
     CHECK((reinterpret_cast<uintptr_t>(r) - reinterpret_cast<uintptr_t>(p.ws.p)) % 256 == 0);

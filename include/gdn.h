@@ -156,7 +156,7 @@ gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims,
  * passes inputs and outputs. Makes no hipMalloc, hipFree or other
  * allocating call. Dims whose gdn_chunk_fwd_workspace_bytes() exceeds
  * GDN_NOALLOC_SCRATCH_BYTES (at 16 QK / 48 V heads, head dim 128, bf16,
- * chunk 64: about 5,700 tokens) return GDN_ERROR_WORKSPACE before anything
+ * chunk 64: about 3,900 tokens) return GDN_ERROR_WORKSPACE before anything
  * is enqueued. The array belongs to the device current at the call, which
  * must be the device of `stream`; its address is looked up once per device
  * on the first call there. All calls on one GPU share that GPU's array:

@@ -316,7 +316,8 @@ struct InvSmem {
     float x[4][16 * XLD];              // one 16 x 16 scratch tile per wave (blocks below the diagonal)
     Frag<E> tbg[G::T_FR * 64];         // then the Tinv diag(b exp(g)) fragments
   } v;
-  float gb[2][C];                      // g and b of the current V head
+  float gb[2][C] __attribute__((aligned(16)));   // g and b of the current V head
+  float eg[C] __attribute__((aligned(16)));      // exp(g), zero past the chunk end
 };
 
 // Lower tile t of a CT x CT tile grid (on and below the diagonal, row by
@@ -329,13 +330,16 @@ __device__ __forceinline__ int2 lower_tile(int t) {
 
 // The scan's row-factor table of one (chunk, V head): exp(g_r),
 // exp(min(g_L - g_r, 0)) (both zero past the chunk end), exp(g_L); from g
-// in sm.gb.
+// in sm.gb. exp(g_r) is also kept in sm.eg for the Tinv diag(b exp(g))
+// fragments.
 template <typename E, int D, int C>
-__device__ __forceinline__ void write_row_factors(const InvSmem<E, D, C>& sm, float* dtg, int len, int tid) {
+__device__ __forceinline__ void write_row_factors(InvSmem<E, D, C>& sm, float* dtg, int len, int tid) {
   const float gl = sm.gb[0][len - 1];
   if (tid < C) {
     const float valid = (float)(tid < len);
-    dtg[tid] = __expf(sm.gb[0][tid]) * valid;
+    const float eg = __expf(sm.gb[0][tid]) * valid;
+    dtg[tid] = eg;
+    sm.eg[tid] = eg;
     dtg[C + tid] = __expf(fminf(gl - sm.gb[0][tid], 0.f)) * valid;
   } else if (tid < C + 4) {
     dtg[C + tid] = (tid == C) ? __expf(gl) : 0.f;
@@ -363,11 +367,13 @@ __device__ __forceinline__ void k2_invert_and_write(InvSmem<E, D, C>& sm, const 
     const int t = wave + u * NW;
     if (t >= NTILE) continue;
     const int2 tl = lower_tile(t);
-    const int i = 16 * tl.y + l16;
+    const int i = 16 * tl.y + l16, r0 = 16 * tl.x + 4 * quad;   // rows r0 .. r0 + 3
+    const float gi = sm.gb[0][i];
+    const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.gb[0][r0]);
+    const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.gb[1][r0]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 16 * tl.x + 4 * quad + e;
-      if (i < r) at[r * FLD + i] = sm.gb[1][r] * kk[u][e] * __expf(fminf(sm.gb[0][r] - sm.gb[0][i], 0.f));
+      if (i < r0 + e) at[(r0 + e) * FLD + i] = br[e] * kk[u][e] * __expf(fminf(gr[e] - gi, 0.f));
     }
   }
   __syncthreads();
@@ -427,15 +433,27 @@ __device__ __forceinline__ void k2_invert_and_write(InvSmem<E, D, C>& sm, const 
     const int r = 16 * rt + (ln & 15);
     Frag<E> vb, vg;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int i = frag_k(s, q4, e);
-      float t = 0.f;
-      if (i < C) {
-        const float tri = ((r >> 4) > (i >> 4)) ? at[i * FLD + r] : (((r >> 4) == (i >> 4)) ? at[r * FLD + i] : 0.f);
-        t = tri * sm.gb[1][i];
+    for (int hh = 0; hh < 2; ++hh) {
+      // elements 4 hh .. 4 hh + 3 of the fragment: tokens i0 .. i0 + 3, in
+      // one 16-token block (b and exp(g) are zero past the chunk end, so
+      // those tokens give zeros)
+      const int i0 = 32 * s + 16 * hh + 4 * q4;
+      f32x4 bi = zero4(), ei = zero4();
+      if (i0 < C) {
+        bi = *reinterpret_cast<const f32x4*>(&sm.gb[1][i0]);
+        ei = *reinterpret_cast<const f32x4*>(&sm.eg[i0]);
       }
-      vb[e] = to_e<E>(t);
-      vg[e] = to_e<E>((i < C) ? t * __expf(sm.gb[0][i]) : 0.f);
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int i = i0 + e4;
+        float t = 0.f;
+        if (i < C) {
+          const float tri = ((r >> 4) > (i >> 4)) ? at[i * FLD + r] : (((r >> 4) == (i >> 4)) ? at[r * FLD + i] : 0.f);
+          t = tri * bi[e4];
+        }
+        vb[4 * hh + e4] = to_e<E>(t);
+        vg[4 * hh + e4] = to_e<E>(t * ei[e4]);
+      }
     }
     tg[it] = vb;
     sm.v.tbg[it] = vg;

@@ -40,7 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN prefill tokens/s at T=64K (48 V heads, d=128) + decode state GB/s"
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
-STAGES = ["gdn_k2_group_fwd", "gdn_k3_scan"]
+STAGES = ["gdn_k2_inverse_w", "gdn_k3_scan"]
 DECODE_KERNEL = "gdn_kd_decode_step"
 
 
@@ -60,7 +60,7 @@ def algorithmic_work(T, HQ, HV, D, C, N, decode_batch):
         # head; reads q, k, log a, b; writes the K^T and Q fragments (once per
         # QK head), Tinv diag(b), W, the masked q.k fragments P and the
         # row-factor table (2C + 4 fp32 per chunk and V head)
-        "gdn_k2_group_fwd": (T * (HQ * 4 * C * dk + HV * (C * C / 3.0 + 2 * C * dk)),
+        "gdn_k2_inverse_w": (T * (HQ * 4 * C * dk + HV * (C * C / 3.0 + 2 * C * dk)),
                              2 * T * HQ * dk * e + gates + T * HQ * 2 * dk * e
                              + T * HV * (2 * tri + dk) * e + T * HV * (2 * C + 4) * 4 / C),
         # Ut, W S, Q S, K^T U, P U per V head; reads Q, K^T, P, V, Tinv
@@ -82,7 +82,7 @@ def algorithmic_work(T, HQ, HV, D, C, N, decode_batch):
     return out, per_token
 
 
-BWD_STAGES = ["gdn_k1_chunk_prep", "gdn_k2_inverse_w", "gdn_k3_scan [save]", "gdn_kb_dstate",
+BWD_STAGES = ["gdn_k1_chunk_prep", "gdn_k2_inverse_w [bwd]", "gdn_k3_scan [save]", "gdn_kb_dstate",
               "gdn_kb_grad"]
 
 
@@ -105,11 +105,11 @@ def algorithmic_work_bwd(T, HQ, HV, D, C, N):
         # K^T, K and Q^T fragments, the query-indexed q.k fragments
         "gdn_k1_chunk_prep": (T * HQ * 2 * C * dk,
                               2 * T * HQ * dk * e + 2 * gates + 3 * T * HQ * dk * e + T * HQ * C * e),
-        # K K^T, the inverse, W and W^T; reads k, K^T, q.k, g, b; writes Tinv
+        # K K^T, the inverse, W and W^T; reads k, q.k, g, b; writes Tinv
         # diag(b), W, the row factors, P^T, W^T and Tinv^T
-        "gdn_k2_inverse_w": (T * (HQ * 2 * C * dk + HV * (C * C / 3.0 + 4 * C * dk)),
-                             T * HQ * (2 * dk + C) * e + gates
-                             + T * HV * (2 * C + tri + 2 * dk) * e + dtab),
+        "gdn_k2_inverse_w [bwd]": (T * (HQ * 2 * C * dk + HV * (C * C / 3.0 + 4 * C * dk)),
+                                   T * HQ * (dk + C) * e + gates
+                                   + T * HV * (2 * C + tri + 2 * dk) * e + dtab),
         # Ut, W S, K^T U; reads K^T, V, Tinv diag(b), W, the row factors and
         # the initial states; writes the chunk-start states and U
         "gdn_k3_scan [save]": (T * HV * (4 * dk * dv + 2 * C * dv),
@@ -171,7 +171,9 @@ def backward_bench(gdn, I, inp, dev, stream, T, HQ, HV, D, C, reps=3):
         peak = PEAK_BF16_FLOPS if bound == "mfma" else PEAK_HBM_BYTES
         kernels[name] = {"ms": round(ms[name], 4), "bound": bound,
                          "achieved": round(rate / (1e12 if bound == "mfma" else 1e9), 3),
-                         "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": round(rate / peak, 4)}
+                         "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": round(rate / peak, 4),
+                         "mfma_frac": round(flops / (ms[name] * 1e-3) / PEAK_BF16_FLOPS, 4),
+                         "hbm_frac": round(nbytes / (ms[name] * 1e-3) / PEAK_HBM_BYTES, 4)}
     del ws
     return {"ms": round(total, 4), "tokens_per_s": round(T / (total * 1e-3), 1),
             "mfma_frac": round(sum(work[k][1] for k in BWD_STAGES) / (total * 1e-3) / PEAK_BF16_FLOPS, 4),

@@ -291,11 +291,9 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
 // with fp32 16x16x4 MFMAs, one block per wave per distance. W^T = K^T
 // (Tinv diag(b exp(g)))^T is contracted over tokens, wave w taking d-tiles
 // 2w and 2w + 1, whose accumulator pairs are W's fragments (rt, w).
-// Two forms share that code (k2_invert_and_write): the forward pass runs
-// one workgroup per (chunk, QK head), which does the QK head's work once
-// and then takes the group's V heads in turn (gdn_k2_group_fwd); the
-// backward pass one per (chunk, V head), reading kernel 1's outputs
-// (gdn_k2_inverse_w).
+// One workgroup per (chunk, QK head) does the QK head's work once and then
+// takes the group's V heads in turn; the backward pass's form reads kernel
+// 1's outputs and also writes the operands of the gradient kernel.
 // --------------------------------------------------------------------------
 
 template <typename E, int D, int C>
@@ -319,6 +317,13 @@ struct InvSmem {
   float gb[2][C] __attribute__((aligned(16)));   // g and b of the current V head
   float eg[C] __attribute__((aligned(16)));      // exp(g), zero past the chunk end
 };
+
+// Kernel 2's workgroups per CU: `want`, or fewer where its LDS allows
+// fewer (fp32 operands at C = 64)
+template <typename E, int D, int C>
+constexpr int k2_occupancy(int want) {
+  return (int)(160 * 1024 / sizeof(InvSmem<E, D, C>)) < want ? (int)(160 * 1024 / sizeof(InvSmem<E, D, C>)) : want;
+}
 
 // Lower tile t of a CT x CT tile grid (on and below the diagonal, row by
 // row) -> its row and column tile.
@@ -553,22 +558,27 @@ __device__ __forceinline__ void key_products(const InvSmem<E, D, C>& sm, f32x4 (
   }
 }
 
-// Forward form: one workgroup per (chunk, QK head). What depends only on
-// the QK head is done once: the chunk lookup, the keys and queries, the K^T
-// and Q fragments the scan reads, the q.k products and K K^T (both kept in
-// registers). The group's V heads are then taken in turn: the gate prefix,
-// the P fragments and row-factor table, then A, the inverse, Tinv diag(b)
-// and W. The gates of each V head are requested while the previous one is
-// processed. (One workgroup per V head, each repeating the QK head's work,
-// took 0.63 ms against 0.51 ms on the 64K-token layer.)
-// five workgroups per CU: 26 KB of LDS and at most 96 VGPRs each
-template <typename E, int D, int C, bool P, bool ND>
-__global__ __launch_bounds__(kBlock, 5) void gdn_k2_group_fwd(const PrefillArgs a) {
+// One workgroup per (chunk, QK head). What depends only on the QK head is
+// done once: the keys are staged, the K^T fragments gathered from them, and
+// K K^T formed (kept in registers). Forward pass: also the chunk lookup, the
+// K^T and Q fragments the scan reads, and the q.k products (kept in
+// registers). The group's V heads are then taken in turn: the gate prefix
+// (forward) or kernel 1's g and b (backward), the P fragments (forward) or
+// the P^T fragments from kernel 1's query-indexed q.k (backward), the
+// row-factor table, then A, the inverse, Tinv diag(b) and W. Each V head's
+// gates are requested while the previous one is processed. (One workgroup
+// per V head, each repeating the QK head's work, took 0.63 ms against
+// 0.51 ms for the forward pass on the 64K-token layer.)
+// bf16: five workgroups per CU, 26 KB of LDS and at most 96 VGPRs each
+template <typename E, int D, int C, bool P, bool ND, bool BW>
+__global__ __launch_bounds__(kBlock, (k2_occupancy<E, D, C>(5))) void gdn_k2_inverse_w(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   using SM = InvSmem<E, D, C>;
   constexpr int CT = G::CT, CKS = G::CKS, DT = G::DT, DKS = G::DKS, KLD = SM::KLD;
   constexpr int NW = kBlock / 64, NTILE = CT * (CT + 1) / 2, TPW = (NTILE + NW - 1) / NW;
+  constexpr int KQPT = (G::QK_FR * 64 + kBlock - 1) / kBlock;   // backward: q.k fragments per thread
   static_assert(DKS <= NW && CT <= 4, "one W d-step pair per wave, diagonal blocks in one wave");
+  static_assert(!BW || (!P && !ND), "the backward pass takes no flags");
   __shared__ SM sm;
   // the QK heads of one chunk, which read the same gate lines, are
   // consecutive logical ids and so share an XCD
@@ -579,35 +589,57 @@ __global__ __launch_bounds__(kBlock, 5) void gdn_k2_group_fwd(const PrefillArgs 
   // there); the wave index is uniform
   int tid = threadIdx.x, lane = tid & 63, quad = lane >> 4, l16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int2 loc = locate_chunk<C>(a, c, hq == 0, sm.v.loc.scan, sm.v.loc.hit);
-  if (loc.x < 0) return;
-  const int2 sr = seq_range(a, loc.x);
-  const int start = sr.x + loc.y * C;
-  const int len = min(C, sr.y - start);
+  int start, len;
+  if constexpr (BW) {
+    const int4 tab = reinterpret_cast<const int4*>(a.chunk_table)[c];
+    if (tab.x < 0) return;
+    start = tab.y;
+    len = tab.z;
+  } else {
+    const int2 loc = locate_chunk<C>(a, c, hq == 0, sm.v.loc.scan, sm.v.loc.hit);
+    if (loc.x < 0) return;
+    const int2 sr = seq_range(a, loc.x);
+    start = sr.x + loc.y * C;
+    len = min(C, sr.y - start);
+  }
 
-  // wave w's query tile w: its Q fragments straight from q (rows past the
-  // chunk end read its last row and are zeroed below)
+  // forward pass: wave w's query tile w, its Q fragments straight from q
+  // (rows past the chunk end read its last row and are zeroed below)
   Frag<E> qf[DKS];
-  if (wave < CT) {
+  if (!BW && wave < CT) {
     const E* row = static_cast<const E*>(a.q) + ((int64_t)(start + min(16 * wave + l16, len - 1)) * a.h_qk + hq) * D;
 #pragma unroll
     for (int ks = 0; ks < DKS; ++ks) qf[ks] = load_frag<E>(row + 32 * ks, quad, D - 32 * ks);
   }
-  // the gates of V head h of the group: wave 0, lane r holding token r
-  // (lanes past the chunk end read its last token)
+  // the gates of V head h of the group, wave 0: forward, log a and b with
+  // lane r holding token r (lanes past the chunk end read its last token);
+  // backward, kernel 1's g and b of chunk row r
   float gw = 0.f, bw = 0.f;
   auto load_gates = [&](int h) __attribute__((always_inline)) {
-    const int64_t gi = (int64_t)(start + min(lane, len - 1)) * a.h_v + hq * a.group + h;
-    gw = a.log_alpha[gi];
-    bw = a.beta[gi];
+    if constexpr (BW) {
+      const int64_t o = (c * a.h_v + hq * a.group + h) * C + min(lane, C - 1);
+      gw = a.gate_prefix[o];
+      bw = a.beta_chunk[o];
+    } else {
+      const int64_t gi = (int64_t)(start + min(lane, len - 1)) * a.h_v + hq * a.group + h;
+      gw = a.log_alpha[gi];
+      bw = a.beta[gi];
+    }
   };
   if (wave == 0) load_gates(0);
+  // backward pass: kernel 1's query-indexed q.k fragments, kept for every V head
+  Frag<E> kqf[KQPT];
+  if constexpr (BW) {
+    const Frag<E>* kqg = reinterpret_cast<const Frag<E>*>(a.kq) + (c * a.h_qk + hq) * G::QK_FR * 64;
+#pragma unroll
+    for (int p = 0; p < KQPT; ++p) kqf[p] = kqg[min(tid + p * kBlock, G::QK_FR * 64 - 1)];
+  }
   stage_keys<E, D, C, P>(sm, a, start, len, hq, tid);
   __syncthreads();
 
   // K^T fragments (row d, k = token) of this wave's W d-tiles, gathered
-  // from the staged keys and written for the scan (the waves' d-tiles
-  // cover all of them)
+  // from the staged keys; the forward pass writes them for the scan (the
+  // waves' d-tiles cover all of them; kernel 1 wrote them in the backward)
   const int ksd = wave;
   Frag<E> kta[CKS], ktb[CKS];
   if (ksd < DKS) {
@@ -620,22 +652,24 @@ __global__ __launch_bounds__(kBlock, 5) void gdn_k2_group_fwd(const PrefillArgs 
         if (2 * ksd + 1 < DT) ktb[s][e] = (i < C) ? sm.u.ks[i * KLD + 32 * ksd + 16 + l16] : to_e<E>(0.f);
       }
     }
-    Frag<E>* ktg = reinterpret_cast<Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
+    if constexpr (!BW) {
+      Frag<E>* ktg = reinterpret_cast<Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
 #pragma unroll
-    for (int s = 0; s < CKS; ++s) {
-      ktg[((2 * ksd) * CKS + s) * 64 + lane] = kta[s];
-      if (2 * ksd + 1 < DT) ktg[((2 * ksd + 1) * CKS + s) * 64 + lane] = ktb[s];
+      for (int s = 0; s < CKS; ++s) {
+        ktg[((2 * ksd) * CKS + s) * 64 + lane] = kta[s];
+        if (2 * ksd + 1 < DT) ktg[((2 * ksd + 1) * CKS + s) * 64 + lane] = ktb[s];
+      }
     }
   }
-  // q.k of query tile nt = wave: the pair of accumulator tiles K_j Q_r^T of
-  // key tiles 2s and 2s + 1 (a key tile after the query tile stays zero);
-  // the Q fragments are written for the scan
+  // forward pass: q.k of query tile nt = wave, the pair of accumulator
+  // tiles K_j Q_r^T of key tiles 2s and 2s + 1 (a key tile after the query
+  // tile stays zero); the Q fragments are written for the scan
   const int nt = wave;
   int rq = 16 * nt + l16;
   f32x4 qk[CKS][2];
 #pragma unroll
   for (int s = 0; s < CKS; ++s) { qk[s][0] = zero4(); qk[s][1] = zero4(); }
-  if (wave < CT) {
+  if (!BW && wave < CT) {
     if (rq >= len) {
 #pragma unroll
       for (int ks = 0; ks < DKS; ++ks) qf[ks] = join<E>(zero_half<E>(), zero_half<E>());
@@ -686,26 +720,48 @@ __global__ __launch_bounds__(kBlock, 5) void gdn_k2_group_fwd(const PrefillArgs 
     asm volatile("" : "+v"(tid), "+v"(lane), "+v"(quad), "+v"(l16), "+v"(rq));
     tid &= kBlock - 1; lane &= 63; quad &= 3; l16 &= 15; rq &= 63;
     if (wave == 0) {
-      // in-chunk prefix of log a (past the chunk end: log a = 0, b = 0),
-      // then the next V head's gates are requested
-      float g = gw, b = bw;
-      if constexpr (P) { g = neg_softplus(g); b = sigmoid_of(b); }
-      if (lane >= len) { g = 0.f; b = 0.f; }
+      if constexpr (BW) {
+        if (lane < C) { sm.gb[0][lane] = gw; sm.gb[1][lane] = bw; }
+      } else {
+        // in-chunk prefix of log a (past the chunk end: log a = 0, b = 0)
+        float g = gw, b = bw;
+        if constexpr (P) { g = neg_softplus(g); b = sigmoid_of(b); }
+        if (lane >= len) { g = 0.f; b = 0.f; }
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float x = __shfl_up(g, off);
-        if (lane >= off) g += x;
+        for (int off = 1; off < 64; off <<= 1) {
+          const float x = __shfl_up(g, off);
+          if (lane >= off) g += x;
+        }
+        if (lane < C) { sm.gb[0][lane] = g; sm.gb[1][lane] = b; }
       }
-      if (lane < C) { sm.gb[0][lane] = g; sm.gb[1][lane] = b; }
       if (h + 1 < a.group) load_gates(h + 1);
     }
     // (also: the previous V head's last readers of g, b and the LDS
     // fragments are done)
     __syncthreads();
-    // the scan's P fragments: P[r][j] = (q_r . k_j) exp(g_r - g_j) for
-    // j <= r < len, else 0 (the exponent is clamped at 0 so that masked
-    // entries cannot overflow before being zeroed)
-    if (wave < CT) {
+    if constexpr (BW) {
+      // P^T fragments (jt, s), lane row key j, elements query r
+      Frag<E>* ptg = reinterpret_cast<Frag<E>*>(a.pt) + ch * G::QK_FR * 64;
+#pragma unroll
+      for (int p = 0; p < KQPT; ++p) {
+        const int it = tid + p * kBlock;
+        if (it >= G::QK_FR * 64) continue;
+        const int f = it / 64, ln = it % 64, jt = f / CKS, s = f % CKS, q4 = ln >> 4;
+        const int j = 16 * jt + (ln & 15);
+        const float gj = sm.gb[0][j];
+        Frag<E> v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = frag_k(s, q4, e);
+          const float m = (float)(j <= r && r < len);
+          v[e] = to_e<E>(to_f(kqf[p][e]) * (__expf(fminf(sm.gb[0][min(r, C - 1)] - gj, 0.f)) * m));
+        }
+        ptg[it] = v;
+      }
+    } else if (wave < CT) {
+      // the scan's P fragments: P[r][j] = (q_r . k_j) exp(g_r - g_j) for
+      // j <= r < len, else 0 (the exponent is clamped at 0 so that masked
+      // entries cannot overflow before being zeroed)
       Frag<E>* pg = reinterpret_cast<Frag<E>*>(a.pmask) + ch * G::QK_FR * 64;
       const float gr = sm.gb[0][rq], vr = (float)(rq < len);
 #pragma unroll
@@ -740,79 +796,9 @@ __global__ __launch_bounds__(kBlock, 5) void gdn_k2_group_fwd(const PrefillArgs 
       }
       __syncthreads();   // the next V head's prefix overwrites g and b
     } else {
-      k2_invert_and_write<E, D, C, false, TPW>(sm, a, ch, kk, kta, ktb, tid, lane, wave, quad, l16);
+      k2_invert_and_write<E, D, C, BW, TPW>(sm, a, ch, kk, kta, ktb, tid, lane, wave, quad, l16);
     }
   }
-}
-
-// Backward form: one workgroup per (chunk, V head), from kernel 1's chunk
-// table, gate prefix, per-chunk b and K^T fragments; it also writes the
-// P^T fragments (from kernel 1's query-indexed q.k), Tinv^T and the W^T
-// fragments that the gradient kernel reads.
-// six workgroups per CU: 26 KB of LDS and at most 80 VGPRs each
-template <typename E, int D, int C>
-__global__ __launch_bounds__(kBlock, 6) void gdn_k2_inverse_w(const PrefillArgs a) {
-  using G = Cfg<E, D, C>;
-  using SM = InvSmem<E, D, C>;
-  constexpr int CT = G::CT, CKS = G::CKS, DT = G::DT, DKS = G::DKS;
-  constexpr int NW = kBlock / 64, NTILE = CT * (CT + 1) / 2, TPW = (NTILE + NW - 1) / NW;
-  static_assert(DKS <= NW && CT <= 4, "one W d-step pair per wave, diagonal blocks in one wave");
-  __shared__ SM sm;
-  // the V heads of one (chunk, QK head), which read the same keys, are
-  // consecutive logical ids and so share an XCD
-  const int64_t lid = xcd_local_id(blockIdx.x, gridDim.x);
-  const int64_t c = lid / a.h_v;
-  const int hv = (int)(lid % a.h_v);
-  const int hq = hv / a.group;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, l16 = lane & 15;
-  const int4 tab = reinterpret_cast<const int4*>(a.chunk_table)[c];
-  if (tab.x < 0) return;
-  const int start = tab.y, len = tab.z;
-  const int64_t ch = c * a.h_v + hv;
-
-  // K^T fragments of this wave's W d-tiles, issued first so that they
-  // arrive during the inverse
-  const int ksd = wave;
-  Frag<E> kta[CKS], ktb[CKS];
-  if (ksd < DKS) {
-    const Frag<E>* ktg = reinterpret_cast<const Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
-#pragma unroll
-    for (int s = 0; s < CKS; ++s) {
-      kta[s] = ktg[((2 * ksd) * CKS + s) * 64 + lane];
-      if (2 * ksd + 1 < DT) ktb[s] = ktg[((2 * ksd + 1) * CKS + s) * 64 + lane];
-    }
-  }
-  // g and b of this V head (threads below 2 C)
-  float gbv = 0.f;
-  if (tid < 2 * C) gbv = (tid < C) ? a.gate_prefix[ch * C + tid] : a.beta_chunk[ch * C + tid - C];
-  stage_keys<E, D, C, false>(sm, a, start, len, hq, tid);
-  if (tid < 2 * C) sm.gb[tid / C][tid % C] = gbv;
-  __syncthreads();
-  write_row_factors(sm, a.dtab + ch * (2 * C + 4), len, tid);
-  {
-    // P^T fragments (jt, s), lane row key j, elements query r, from kernel
-    // 1's query-indexed q.k fragments
-    const Frag<E>* kqg = reinterpret_cast<const Frag<E>*>(a.kq) + (c * a.h_qk + hq) * G::QK_FR * 64;
-    Frag<E>* ptg = reinterpret_cast<Frag<E>*>(a.pt) + ch * G::QK_FR * 64;
-    for (int it = tid; it < G::QK_FR * 64; it += kBlock) {
-      const int f = it / 64, ln = it % 64, jt = f / CKS, s = f % CKS, q4 = ln >> 4;
-      const int j = 16 * jt + (ln & 15);
-      const Frag<E> x = kqg[it];
-      const float gj = sm.gb[0][j];
-      Frag<E> v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = frag_k(s, q4, e);
-        const float m = (float)(j <= r && r < len);
-        v[e] = to_e<E>(to_f(x[e]) * (__expf(fminf(sm.gb[0][min(r, C - 1)] - gj, 0.f)) * m));
-      }
-      ptg[it] = v;
-    }
-  }
-  f32x4 kk[TPW];
-  key_products<E, D, C, TPW>(sm, kk, wave, quad, l16);
-  __syncthreads();     // the keys are dead from here on; their LDS holds A and Tinv
-  k2_invert_and_write<E, D, C, true, TPW>(sm, a, ch, kk, kta, ktb, tid, lane, wave, quad, l16);
 }
 
 // --------------------------------------------------------------------------
@@ -1340,7 +1326,7 @@ template <typename E, int D, int C>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int last) {
   const unsigned nc = (unsigned)a.max_chunks;
   const unsigned scan_groups = (unsigned)(a.num_seqs * a.h_v * ScanCfg<E, D, C>::NCB);
-  const dim3 g_qk(nc * (unsigned)a.h_qk), g_v(nc * (unsigned)a.h_v), g_scan(scan_groups);
+  const dim3 g_qk(nc * (unsigned)a.h_qk), g_scan(scan_groups);
   for (int stage = first; stage <= last; ++stage) {
     if (a.backward) {
       // the backward pass (which takes no flags): kernel 1 lays out the
@@ -1348,7 +1334,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
       // saves the chunk-start states and U
       switch (stage) {
         case 1: gdn_k1_chunk_prep<E, D, C><<<g_qk, dim3(kBlock), 0, s>>>(a); break;
-        case 2: gdn_k2_inverse_w<E, D, C><<<g_v, dim3(kBlock), 0, s>>>(a); break;
+        case 2: gdn_k2_inverse_w<E, D, C, false, false, true><<<g_qk, dim3(kBlock), 0, s>>>(a); break;
         case 3: gdn_k3_scan<E, D, C, false, true><<<g_scan, dim3(kScanBlock), 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
       }
@@ -1358,11 +1344,11 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
     switch (stage) {
       case 1:
         if (a.prep) {
-          if (a.no_delta) gdn_k2_group_fwd<E, D, C, true, true><<<g_qk, dim3(kBlock), 0, s>>>(a);
-          else gdn_k2_group_fwd<E, D, C, true, false><<<g_qk, dim3(kBlock), 0, s>>>(a);
+          if (a.no_delta) gdn_k2_inverse_w<E, D, C, true, true, false><<<g_qk, dim3(kBlock), 0, s>>>(a);
+          else gdn_k2_inverse_w<E, D, C, true, false, false><<<g_qk, dim3(kBlock), 0, s>>>(a);
         } else {
-          if (a.no_delta) gdn_k2_group_fwd<E, D, C, false, true><<<g_qk, dim3(kBlock), 0, s>>>(a);
-          else gdn_k2_group_fwd<E, D, C, false, false><<<g_qk, dim3(kBlock), 0, s>>>(a);
+          if (a.no_delta) gdn_k2_inverse_w<E, D, C, false, true, false><<<g_qk, dim3(kBlock), 0, s>>>(a);
+          else gdn_k2_inverse_w<E, D, C, false, false, false><<<g_qk, dim3(kBlock), 0, s>>>(a);
         }
         break;
       case 2:

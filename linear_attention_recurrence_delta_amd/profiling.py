@@ -27,7 +27,6 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 # kernel -> source file that defines it
 SOURCES = {"gdn_k1_chunk_prep": "gdn_prefill.hip", "gdn_k2_inverse_w": "gdn_prefill.hip",
-           "gdn_k2_group_fwd": "gdn_prefill.hip",
            "gdn_k3_scan": "gdn_prefill.hip", "gdn_kd_decode_step": "gdn_decode.hip",
            "gdn_kd_decode_multi": "gdn_decode.hip", "gdn_kb_dstate": "gdn_backward.hip",
            "gdn_kb_grad": "gdn_backward.hip"}
@@ -40,7 +39,7 @@ def source_of(kernel):
 
 # compile-time switches of each kernel, in template-argument order (the bool
 # arguments follow the dtype and sizes); a true switch labels the instance
-FLAGS = {"gdn_k2_group_fwd": ("prep", "gate-only"),
+FLAGS = {"gdn_k2_inverse_w": ("prep", "gate-only", "bwd"),
          "gdn_k3_scan": ("gate-only", "save"), "gdn_kd_decode_step": ("prep", "gate-only"),
          "gdn_kd_decode_multi": ("prep", "gate-only")}
 

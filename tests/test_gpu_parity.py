@@ -211,6 +211,22 @@ def test_head_group_of_four():
     check(fin, want_f, torch.bfloat16, "final")
 
 
+@pytest.mark.parametrize("h_qk,h_v,d,chunk,dtype", [
+    (4, 4, 128, 64, "bf16"), (1, 8, 128, 64, "bf16"), (2, 10, 128, 16, "bf16"), (3, 3, 16, 64, "f32"),
+    (1, 5, 16, 16, "bf16")])
+def test_head_group_sizes(h_qk, h_v, d, chunk, dtype):
+    # the forward's kernel 2 takes a QK head's V heads in turn (one per
+    # group member, each with its own gates), so group sizes 1, 5 and 8 run
+    # that loop a different number of times; two sequences, one ragged
+    say(f"h_qk={h_qk} h_v={h_v} (groups of {h_v // h_qk}) d={d} C={chunk} {dtype}, lens [150, 41]")
+    inp = random_prefill(500 + h_v + d + chunk, [150, 41], h_qk, h_v, d, dtype)
+    o, fin = run_gpu(inp, chunk)
+    want_o, want_f = O.recurrent_form1(**oracle_args(inp))
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    check(o, want_o, tdt, "o")
+    check(fin, want_f, tdt, "final")
+
+
 @pytest.mark.parametrize("lens", [[70], [300, 0, 1, 129]])
 def test_fp32_head_dim_128_chunk_64(lens):
     # fp32 operands at head dim 128 with 64-token chunks: the scan's

@@ -450,8 +450,8 @@ def main():
                 "flops_per_launch": d_flops, "flops_per_token": d_flops / T}
     # the whole prefill: the method's flops against MFMA peak; its bytes
     # split into the layer's compulsory I/O (q, k, v, o, gates, states) and
-    # what this design adds (the workspace intermediates kernel 1 and 2
-    # write and the next kernels read)
+    # what this design adds (the workspace intermediates kernel 2 writes
+    # and the scan reads)
     compulsory = T * (2 * HQ * D * 2 + 2 * HV * D * 2 + 2 * HV * 4) + 2 * HV * D * D * 4
     design = sum(work[n][2] for n in STAGES)
     measured = [load_traffic(n) for n in STAGES]

@@ -212,10 +212,11 @@ gdn_status_t gdn_chunk_bwd(const gdn_dims_t* dims,
 
 /*
  * Diagnostic variant of gdn_chunk_bwd enqueuing launches first..last only
- * (for events between them): 1-3 = the forward kernels (also writing the
- * backward operands; stage 3 stores the state at each chunk start and the
- * chunk's U rows instead of outputs), 4 = the reverse state scan, 5 = the
- * gradient kernel. A call starting at stage s > 1 must follow calls that ran
+ * (for events between them): 1 = chunk table, gate prefix sums and the K^T,
+ * K, Q^T and query-indexed Q K^T layouts; 2 = (I + A)^{-1}, W and the
+ * backward operands P^T, W^T and Tinv^T; 3 = the state scan, storing the
+ * state at each chunk start and the chunk's U rows instead of outputs;
+ * 4 = the reverse state scan; 5 = the gradient kernel. A call starting at stage s > 1 must follow calls that ran
  * stages 1..s-1 with identical arguments and workspace on the same stream.
  * Returns GDN_ERROR_INVALID_VALUE unless 1 <= first_stage <= last_stage <= 5.
  */

@@ -25,9 +25,9 @@
 //     dlog a = the suffix sums of dg within the chunk.
 // A QK head's dq and dk sum over its V heads.
 //
-// Launches: kernel 1 and kernel 2 of the forward pass, also writing the
-// backward operands (K and Q^T fragments, the query-indexed q.k products,
-// P^T and W^T fragments, Tinv^T); kernel 3 in its saving form (the state at
+// Launches: kernel 1 (chunk table, g and b, the K^T, K and Q^T fragments
+// and the query-indexed q.k products), kernel 2 in its backward form (also
+// writing the P^T and W^T fragments and Tinv^T); kernel 3 in its saving form (the state at
 // every chunk start and the U rows, no outputs); the reverse state scan
 // (gdn_kb_dstate); the gradient kernel (gdn_kb_grad).
 #include <type_traits>

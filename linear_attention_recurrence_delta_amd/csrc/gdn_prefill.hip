@@ -274,8 +274,8 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
 
 // --------------------------------------------------------------------------
 // Kernel 2: A = strict_lower(b_r (k_r . k_i) exp(g_r - g_i)) and
-// Tinv = (I + A)^{-1} per (chunk, V head), and the operands the scan takes
-// from them: the fragments of Tinv diag(b) (the right factor of Ut) and of
+// Tinv = (I + A)^{-1} for each (chunk, V head), and the operands the scan
+// takes from them: the fragments of Tinv diag(b) (the right factor of Ut) and of
 // W = Tinv diag(b exp(g)) K; also the V head's masked, decayed q.k
 // fragments and the scan's row-factor table.
 // K K^T is formed with MFMA from the staged keys; A's entries are made from
@@ -1329,9 +1329,10 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
   const dim3 g_qk(nc * (unsigned)a.h_qk), g_scan(scan_groups);
   for (int stage = first; stage <= last; ++stage) {
     if (a.backward) {
-      // the backward pass (which takes no flags): kernel 1 lays out the
-      // fragments both directions need, kernel 2 adds its own, and the scan
-      // saves the chunk-start states and U
+      // the backward pass (which takes no flags): kernel 1 finds the chunks,
+      // forms g and b and lays out the K, K^T, Q^T and q.k fragments;
+      // kernel 2 adds its own, and the scan saves the chunk-start states
+      // and U
       switch (stage) {
         case 1: gdn_k1_chunk_prep<E, D, C><<<g_qk, dim3(kBlock), 0, s>>>(a); break;
         case 2: gdn_k2_inverse_w<E, D, C, false, false, true><<<g_qk, dim3(kBlock), 0, s>>>(a); break;

@@ -19,7 +19,8 @@ __device__ __forceinline__ int2 seq_range(const PrefillArgs& a, int64_t n) {
   return make_int2(s0, min(max(a.cu_seqlens[n + 1], s0), t));
 }
 
-// Chunk-slot range [x, y) of sequence n from kernel 1's offsets, clamped
+// Chunk-slot range [x, y) of sequence n from the per-sequence chunk offsets
+// (written by the chunk lookup of kernel 2, or of kernel 1 in the backward pass), clamped
 // into [0, max_chunks] likewise (with a table that breaks the precondition
 // the offsets could pass the workspace's chunk count).
 __device__ __forceinline__ int2 chunk_range(const PrefillArgs& a, int64_t n) {

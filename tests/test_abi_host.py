@@ -78,8 +78,8 @@ def test_dims_validation(lib, kw, status):
 
 def test_workspace_size_formula(lib):
     # regions: chunk table, sequence offsets, gate prefixes, per-chunk b,
-    # Tinv diag(b) and W fragments (per V head), K^T, q.k and Q fragments
-    # (per QK head), masked q.k fragments and row factors (per V head); each
+    # Tinv diag(b) and W fragments (per V head), K^T and Q fragments (per
+    # QK head), masked q.k fragments and row factors (per V head); each
     # padded to 256 bytes. Fragments of a C x C tile take C*C elements, of a
     # D x C tile D*C elements (C = 64 is a whole number of 32-steps).
     d = dims(num_seqs=3, total_tokens=1000)

@@ -497,6 +497,25 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     return x;
   };
 
+  // K K^T tiles (rt, it) of this wave's column tiles it = wave + NW j2:
+  // the same for every V head of the group, so formed once
+  f32x4 kkh[JPW][CT];
+#pragma unroll
+  for (int j2 = 0; j2 < JPW; ++j2) {
+    const int it = wave + NW * j2;
+#pragma unroll
+    for (int rt = 0; rt < CT; ++rt) kkh[j2][rt] = zero4();
+    if (it >= CT) continue;
+    Frag<E> kb[DKS];
+#pragma unroll
+    for (int ks = 0; ks < DKS; ++ks) kb[ks] = kff[(it * DKS + ks) * 64 + lane];
+#pragma unroll
+    for (int rt = 0; rt < CT; ++rt) {
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks) kkh[j2][rt] = mma(kff[(rt * DKS + ks) * 64 + lane], kb[ks], kkh[j2][rt]);
+    }
+  }
+
   for (int h = 0; h < a.group; ++h) {
     const int hv = hq * a.group + h;
     const int64_t ch = c * a.h_v + hv;
@@ -714,20 +733,17 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     for (int j2 = 0; j2 < JPW; ++j2) {
       const int it = wave + NW * j2;
       if (it >= CT) continue;
-      Frag<E> kb[DKS], yb[CKS];
-#pragma unroll
-      for (int ks = 0; ks < DKS; ++ks) kb[ks] = kff[(it * DKS + ks) * 64 + lane];
+      Frag<E> yb[CKS];
 #pragma unroll
       for (int s = 0; s < CKS; ++s) yb[s] = frag_col(ys, ELD, 16 * it, s, C);
       const int i = 16 * it + l16;
       float colm = 0.f;
 #pragma unroll
       for (int rt = 0; rt < CT; ++rt) {
-        f32x4 acc = zero4(), kk = zero4();
+        f32x4 acc = zero4();
+        const f32x4 kk = kkh[j2][rt];
 #pragma unroll
         for (int s = 0; s < CKS; ++s) acc = mma(frag_row(sm.tt, TLD, 16 * rt, s, C), yb[s], acc);
-#pragma unroll
-        for (int ks = 0; ks < DKS; ++ks) kk = mma(kff[(rt * DKS + ks) * 64 + lane], kb[ks], kk);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * rt + 4 * quad + e;

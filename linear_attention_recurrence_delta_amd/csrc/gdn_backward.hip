@@ -461,10 +461,27 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
   auto frag_row = [&](const E* m, int ld, int row0, int s, int kext) __attribute__((always_inline)) {
     return load_frag<E>(m + (row0 + l16) * ld + 32 * s, quad, kext - 32 * s);
   };
-  // (a column fragment is read element by element: through an LDS-space
+  // (a bf16 column fragment is two transposing LDS reads, one per half of
+  // 16 rows: in each 16-lane row of the wave, lane 4 e + j addresses the 4
+  // elements at row k0 + e, columns col0 + 4 j .. + 3, and lane i receives
+  // element i % 4 of the pieces that lanes 4 e + i / 4 address, e = 0..3,
+  // that is column col0 + i at rows k0 .. k0 + 3; halves at or past kext
+  // are zero. Otherwise it is read element by element: through an LDS-space
   // pointer, so its addresses are 32-bit, and unconditionally, with rows
   // past kext clamped and then zeroed, unless the whole step lies inside)
   auto frag_col = [&](const E* m, int ld, int col0, int s, int kext) __attribute__((always_inline)) {
+    if constexpr (sizeof(E) == 2) {
+      if (kext % 16 == 0) {
+        typedef __attribute__((address_space(3))) bf16x4* TrPtr;
+        E* mt = const_cast<E*>(m) + (32 * s + 4 * quad + (l16 >> 2)) * ld + col0 + 4 * (l16 & 3);
+        Half<E> hv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          hv[h] = (32 * s + 16 * h < kext) ? __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TrPtr)(mt + 16 * h * ld))
+                                           : zero_half<E>();
+        return join<E>(hv[0], hv[1]);
+      }
+    }
     typedef const __attribute__((address_space(3))) E* LdsPtr;
     const LdsPtr ml = (LdsPtr)m;
     Frag<E> f;

@@ -398,6 +398,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
   // column tile is loaded once and used for every row tile
   constexpr int DPW = (DT + NW - 1) / NW, TPW = DPW * CT;     // d-tiles, C x D tiles per wave
   constexpr int JPW = (CT + NW - 1) / NW;                     // C x C column tiles per wave
+  static_assert(C <= 64, "a chunk's rows fit one wave (the dlog a scan)");
   constexpr int VE = 16 / (int)sizeof(E);
   typedef E VLoad __attribute__((ext_vector_type(VE)));
   __shared__ SM sm;
@@ -417,43 +418,47 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
   // a uniform base pointer and 32-bit lane offsets. Every load is issued
   // unconditionally (rows past the end read the last row, then select
   // zero), so all of a thread's loads are in flight before the first wait.
+  // Loads and LDS stores are separate steps, so that a phase can request
+  // all of its global reads before it waits for any of them (the compiler
+  // keeps a load that follows an LDS store after it).
   constexpr int SPT = (C * D / VE + kGradBlock - 1) / kGradBlock;   // 16-byte loads per thread
-  auto stage_rows = [&](E* dst, const void* src, int heads, int head) __attribute__((always_inline)) {
+  struct Rows { VLoad x[SPT]; };
+  auto load_rows = [&](const void* src, int heads, int head) __attribute__((always_inline)) {
     const E* sg = static_cast<const E*>(src) + ((int64_t)start * heads + head) * D;
-    VLoad x[SPT];
+    Rows t;
 #pragma unroll
     for (int p = 0; p < SPT; ++p) {
       const int idx = tid + p * kGradBlock;
       const int r = min(idx / (D / VE), len - 1), d = (idx % (D / VE)) * VE;
-      if (idx < C * D / VE) x[p] = *reinterpret_cast<const VLoad*>(sg + r * heads * D + d);
+      if (idx < C * D / VE) t.x[p] = *reinterpret_cast<const VLoad*>(sg + r * heads * D + d);
     }
+    return t;
+  };
+  // the rows of a [C][D] workspace matrix
+  auto load_ws = [&](const E* src) __attribute__((always_inline)) {
+    Rows t;
+#pragma unroll
+    for (int p = 0; p < SPT; ++p) {
+      const int idx = tid + p * kGradBlock;
+      if (idx < C * D / VE) t.x[p] = *reinterpret_cast<const VLoad*>(src + idx * VE);
+    }
+    return t;
+  };
+  // into LDS rows of stride KLD; rows past the chunk end zero when
+  // `zero_tail` is set
+  auto store_rows = [&](E* dst, const Rows& t, bool zero_tail) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < SPT; ++p) {
       const int idx = tid + p * kGradBlock;
       const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
       if (idx < C * D / VE) {
-        VLoad v = x[p];
-        if (r >= len) {
+        VLoad v = t.x[p];
+        if (zero_tail && r >= len) {
 #pragma unroll
           for (int e = 0; e < VE; ++e) v[e] = to_e<E>(0.f);
         }
         *reinterpret_cast<VLoad*>(&dst[r * KLD + d]) = v;
       }
-    }
-  };
-  // rows of a [C][D] workspace matrix into LDS
-  auto stage_ws = [&](E* dst, const E* src) __attribute__((always_inline)) {
-    VLoad x[SPT];
-#pragma unroll
-    for (int p = 0; p < SPT; ++p) {
-      const int idx = tid + p * kGradBlock;
-      if (idx < C * D / VE) x[p] = *reinterpret_cast<const VLoad*>(src + idx * VE);
-    }
-#pragma unroll
-    for (int p = 0; p < SPT; ++p) {
-      const int idx = tid + p * kGradBlock;
-      const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
-      if (idx < C * D / VE) *reinterpret_cast<VLoad*>(&dst[r * KLD + d]) = x[p];
     }
   };
   // operand fragments of LDS matrices for 32-step s: along a row (the
@@ -504,15 +509,6 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
   const Frag<E>* ktf = reinterpret_cast<const Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
   const Frag<E>* qtf = reinterpret_cast<const Frag<E>*>(a.q_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
   const Frag<E>* kff = reinterpret_cast<const Frag<E>*>(a.k_frag) + (c * a.h_qk + hq) * G::Q_FR * 64;
-  // element (16 rt + 4 quad + i, 16 dt + l16) of K or Q, for i = 0..3, from
-  // their transposed fragments
-  auto tile_elems = [&](const Frag<E>* tf, int rt, int dt) __attribute__((always_inline)) {
-    const Frag<E> f = tf[(dt * CKS + (rt >> 1)) * 64 + lane];
-    f32x4 x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = to_f(f[i + 4 * (rt & 1)]);
-    return x;
-  };
 
   // K K^T tiles (rt, it) of this wave's column tiles it = wave + NW j2:
   // the same for every V head of the group, so formed once
@@ -543,41 +539,68 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     // restore their ranges, so that index products take 24-bit multiplies
     tid &= kGradBlock - 1; lane &= 63; quad &= 3; l16 &= 15;
     __syncthreads();                   // the previous V head's LDS reads are done
+    // every global read of this phase and the next is requested before the
+    // first wait: the gate tables, the dL/do, U and dU rows, Tinv^T, and the
+    // first d-tile's state fragments and K, Q elements
+    float gv = 0.f, bv = 0.f, eav = 0.f, edv = 0.f;
     if (tid < C) {
-      sm.g[tid] = a.gate_prefix[ch * C + tid];
-      sm.b[tid] = a.beta_chunk[ch * C + tid];
-      sm.ea[tid] = a.dtab[ch * (2 * C + 4) + tid];
-      sm.ed[tid] = a.dtab[ch * (2 * C + 4) + C + tid];
+      gv = a.gate_prefix[ch * C + tid];
+      bv = a.beta_chunk[ch * C + tid];
+      eav = a.dtab[ch * (2 * C + 4) + tid];
+      edv = a.dtab[ch * (2 * C + 4) + C + tid];
+    }
+    const float gl = a.dtab[ch * (2 * C + 4) + 2 * C];
+    const Rows xo = load_rows(a.d_o, a.h_v, hv);
+    const Rows xu = load_ws(static_cast<const E*>(a.ub) + ch * C * D);
+    const Rows xd = load_ws(static_cast<const E*>(a.du) + ch * C * D);
+    constexpr int TPT = (C * C / VE + kGradBlock - 1) / kGradBlock;   // Tinv^T rows, 16-byte loads
+    VLoad xt[TPT];
+    {
+      const E* tg = static_cast<const E*>(a.tt) + ch * C * C;
+#pragma unroll
+      for (int p = 0; p < TPT; ++p) {
+        const int idx = tid + p * kGradBlock;
+        if (idx < C * C / VE) xt[p] = *reinterpret_cast<const VLoad*>(tg + idx * VE);
+      }
+    }
+    // the state fragments of d-tile dt (chunk-start state S0 and dS_L, as
+    // fragments of their transposes) and the K, Q elements of its tiles
+    const E* scg = static_cast<const E*>(a.sc) + ch * D * D;
+    const E* dsg = static_cast<const E*>(a.dsl) + ch * D * D;
+    Frag<E> bs[DKS], bl[DKS], qe[CKS], ke[CKS];
+    auto load_dtile = [&](int dt) __attribute__((always_inline)) {
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks) {
+        bs[ks] = load_frag<E>(scg + (16 * dt + l16) * D + 32 * ks, quad, D - 32 * ks);
+        bl[ks] = load_frag<E>(dsg + (16 * dt + l16) * D + 32 * ks, quad, D - 32 * ks);
+      }
+#pragma unroll
+      for (int s = 0; s < CKS; ++s) {
+        qe[s] = qtf[(dt * CKS + s) * 64 + lane];
+        ke[s] = ktf[(dt * CKS + s) * 64 + lane];
+      }
+    };
+    if (tid < C) {
+      sm.g[tid] = gv;
+      sm.b[tid] = bv;
+      sm.ea[tid] = eav;
+      sm.ed[tid] = edv;
 #pragma unroll
       for (int w = 0; w < NW; ++w) { sm.dgw[w][tid] = 0.f; sm.dbw[w][tid] = 0.f; }
     }
     if (tid < 2 * NW) sm.sumw[tid / 2][tid % 2] = 0.f;
-    const float gl = a.dtab[ch * (2 * C + 4) + 2 * C];
-    stage_rows(sm.u1.r1, a.d_o, a.h_v, hv);
-    stage_ws(sm.r2, static_cast<const E*>(a.ub) + ch * C * D);
-    stage_ws(sm.r3, static_cast<const E*>(a.du) + ch * C * D);
-    {
-      // Tinv^T rows, 16-byte loads
-      constexpr int TPT = (C * C / VE + kGradBlock - 1) / kGradBlock;
-      const E* tg = static_cast<const E*>(a.tt) + ch * C * C;
-      VLoad x[TPT];
+    store_rows(sm.u1.r1, xo, true);
+    store_rows(sm.r2, xu, false);
+    store_rows(sm.r3, xd, false);
 #pragma unroll
-      for (int p = 0; p < TPT; ++p) {
-        const int idx = tid + p * kGradBlock;
-        if (idx < C * C / VE) x[p] = *reinterpret_cast<const VLoad*>(tg + idx * VE);
-      }
-#pragma unroll
-      for (int p = 0; p < TPT; ++p) {
-        const int idx = tid + p * kGradBlock;
-        if (idx < C * C / VE) *reinterpret_cast<VLoad*>(&sm.tt[(idx * VE / C) * TLD + (idx * VE) % C]) = x[p];
-      }
+    for (int p = 0; p < TPT; ++p) {
+      const int idx = tid + p * kGradBlock;
+      if (idx < C * C / VE) *reinterpret_cast<VLoad*>(&sm.tt[(idx * VE / C) * TLD + (idx * VE) % C]) = xt[p];
     }
     __syncthreads();
 
     // dO S0^T, U dS_L^T, -dU S0^T and <S0, dS_L>; the row terms of dg are
     // summed over the wave's d-tiles before the lane reductions
-    const E* scg = static_cast<const E*>(a.sc) + ch * D * D;
-    const E* dsg = static_cast<const E*>(a.dsl) + ch * D * D;
     f32x4 dW[TPW], prow[CT];
     float fro = 0.f, pk_all = 0.f;
 #pragma unroll
@@ -588,11 +611,9 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
 #pragma unroll
       for (int rt = 0; rt < CT; ++rt) dW[j * CT + rt] = zero4();
       if (dt >= DT) continue;
-      Frag<E> bs[DKS], bl[DKS];
+      load_dtile(dt);
 #pragma unroll
       for (int ks = 0; ks < DKS; ++ks) {
-        bs[ks] = load_frag<E>(scg + (16 * dt + l16) * D + 32 * ks, quad, D - 32 * ks);
-        bl[ks] = load_frag<E>(dsg + (16 * dt + l16) * D + 32 * ks, quad, D - 32 * ks);
 #pragma unroll
         for (int e = 0; e < 8; ++e) fro += to_f(bs[ks][e]) * to_f(bl[ks][e]);
       }
@@ -607,7 +628,14 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
           aw = mma(frag_row(sm.r3, KLD, 16 * rt, ks, D), bs[ks], aw);
         }
         dW[u] = -aw;
-        const f32x4 qv = tile_elems(qtf, rt, dt), kv = tile_elems(ktf, rt, dt);
+        // K and Q elements (16 rt + 4 quad + i, 16 dt + l16): fragment
+        // (dt, rt/2) of K^T or Q^T holds them at element i (+4 for an odd rt)
+        f32x4 qv, kv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          qv[i] = to_f(qe[rt >> 1][i + 4 * (rt & 1)]);
+          kv[i] = to_f(ke[rt >> 1][i + 4 * (rt & 1)]);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * rt + 4 * quad + i;
@@ -621,6 +649,8 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
       }
       __builtin_amdgcn_sched_barrier(0);   // one d-tile's operands live at a time
     }
+    // the dP phase's P^T fragments, requested before the row sums
+    const Frag<E>* ptf = reinterpret_cast<const Frag<E>*>(a.pt) + ch * G::QK_FR * 64;
     if (has_dt) {
 #pragma unroll
       for (int rt = 0; rt < CT; ++rt) {
@@ -639,12 +669,13 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     }
 
     // dP = dO U^T: dP * P into dg, dPm = dP * Dincl into x1 (input dtype)
-    const Frag<E>* ptf = reinterpret_cast<const Frag<E>*>(a.pt) + ch * G::QK_FR * 64;
 #pragma unroll
     for (int j2 = 0; j2 < JPW; ++j2) {
       const int jt = wave + NW * j2;
       if (jt >= CT) continue;
-      Frag<E> ub[DKS];
+      Frag<E> pvf[CKS], ub[DKS];
+#pragma unroll
+      for (int s2 = 0; s2 < CKS; ++s2) pvf[s2] = ptf[(jt * CKS + s2) * 64 + lane];
 #pragma unroll
       for (int ks = 0; ks < DKS; ++ks) ub[ks] = frag_row(sm.r2, KLD, 16 * jt, ks, D);
       const int j = 16 * jt + l16;
@@ -656,7 +687,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         for (int ks = 0; ks < DKS; ++ks) acc = mma(frag_row(sm.u1.r1, KLD, 16 * rt, ks, D), ub[ks], acc);
         // P[r][j] for this tile's elements: fragment (jt, rt/2) of P^T holds
         // row 16 rt + 4 quad + i at element i (+4 for an odd rt)
-        const Frag<E> pv = ptf[(jt * CKS + (rt >> 1)) * 64 + lane];
+        const Frag<E> pv = pvf[rt >> 1];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * rt + 4 * quad + i;
@@ -672,6 +703,8 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
       if (quad == 0) atomicAdd(&sm.dgw[wave][j], -colp);
     }
     __syncthreads();                   // x1 complete; dL/do and U rows dead
+    // requested before this phase's products: its K^T and Q^T fragments,
+    // the v rows and the dT phase's K fragments
 #pragma unroll
     for (int j = 0; j < DPW; ++j) {
       const int dt = wave + NW * j;
@@ -696,7 +729,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    stage_rows(sm.u1.r1, a.v, a.h_v, hv);
+    store_rows(sm.u1.r1, load_rows(a.v, a.h_v, hv), true);
     __syncthreads();                   // v rows and dW rows complete; x1 dead
 
     // dT = (dU V^T) diag(b) + (dW K^T) diag(b ea) into x1
@@ -704,12 +737,12 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     for (int j2 = 0; j2 < JPW; ++j2) {
       const int it = wave + NW * j2;
       if (it >= CT) continue;
-      Frag<E> vb[DKS], kb[DKS];
+      Frag<E> vb[DKS];
+      Frag<E> kb[DKS];
 #pragma unroll
-      for (int ks = 0; ks < DKS; ++ks) {
-        vb[ks] = frag_row(sm.u1.r1, KLD, 16 * it, ks, D);
-        kb[ks] = kff[(it * DKS + ks) * 64 + lane];
-      }
+      for (int ks = 0; ks < DKS; ++ks) kb[ks] = kff[(it * DKS + ks) * 64 + lane];
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks) vb[ks] = frag_row(sm.u1.r1, KLD, 16 * it, ks, D);
       const int i = 16 * it + l16;
       const float bi = sm.b[i], bgi = sm.b[i] * sm.ea[i];
 #pragma unroll
@@ -823,7 +856,10 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
           au = mma(ta, ub[s], au);
           aw = mma(ta, wb[s], aw);
         }
-        const f32x4 kv = tile_elems(ktf, rt, dt);
+        // K elements (16 rt + 4 quad + e, d): fragment (dt, rt/2) of K^T is kb[rt/2]
+        f32x4 kv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kv[e] = to_f(kb[rt >> 1][e + 4 * (rt & 1)]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * rt + 4 * quad + e;
@@ -869,11 +905,19 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
       sm.db[tid] = tb;
     }
     __syncthreads();
-    if (tid < len) {
-      float acc = 0.f;
-      for (int j = len - 1; j >= tid; --j) acc += sm.dg[j];
-      a.dlog_alpha[(int64_t)(start + tid) * a.h_v + hv] = acc;
-      a.dbeta[(int64_t)(start + tid) * a.h_v + hv] = sm.db[tid];
+    if (wave == 0) {
+      // dlog a: the suffix sums of dg within the chunk, as a wave-wide scan
+      // (lane r holds row r; rows past len hold 0), in a fixed order
+      float acc = (lane < len) ? sm.dg[lane] : 0.f;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float x = __shfl_down(acc, off);
+        if (lane + off < 64) acc += x;
+      }
+      if (lane < len) {
+        a.dlog_alpha[(int64_t)(start + lane) * a.h_v + hv] = acc;
+        a.dbeta[(int64_t)(start + lane) * a.h_v + hv] = sm.db[lane];
+      }
     }
   }
 

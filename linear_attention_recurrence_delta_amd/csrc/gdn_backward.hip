@@ -822,7 +822,11 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     }
     __syncthreads();
     // dK += (B + B^T) K; dV = diag(b) Tinv^T dU and its b term (v read from
-    // global); Tinv^T dW into dK and the b, g terms of W
+    // global); Tinv^T dW into dK and the b, g terms of W. dv is staged in
+    // the wave's own dU columns (which only this wave reads here, before it
+    // writes them) and stored as 16-byte row pieces after the products: the
+    // wave's loads wait on its earlier stores as well (one counter for both),
+    // so no store goes out between them
     // this chunk's rows of dv and v for this V head, as raw buffers
     const uint32_t v_row = (uint32_t)(a.h_v * D);    // elements between consecutive tokens
     const uint32_t v_bytes = (uint32_t)len * v_row * (uint32_t)sizeof(E);
@@ -843,8 +847,16 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         wb[s] = frag_col(sm.r2, KLD, 16 * dt, s, C);
       }
       const int d = 16 * dt + l16;
-      // byte offset of (row 4 quad, column d); each row adds the uniform row stride
+      // byte offset of (row 4 quad, column d); each row adds the uniform row
+      // stride. The d-tile's v elements are requested before its products.
       const uint32_t lane_off = ((uint32_t)(4 * quad) * v_row + (uint32_t)d) * (uint32_t)sizeof(E);
+      E vq[CT][4];
+#pragma unroll
+      for (int rt = 0; rt < CT; ++rt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          vq[rt][e] = buf_load<E>(vb_, lane_off + (uint32_t)(16 * rt + e) * v_row * (uint32_t)sizeof(E));
+      }
 #pragma unroll
       for (int rt = 0; rt < CT; ++rt) {
         const int u = j * CT + rt;
@@ -864,10 +876,9 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * rt + 4 * quad + e;
           const float bgr = sm.b[r] * sm.ea[r];
-          // rows at or past len fall outside both descriptors: v reads as 0, the dv store is dropped
-          const uint32_t off = lane_off + (uint32_t)(16 * rt + e) * v_row * (uint32_t)sizeof(E);
-          const float vv = to_f(buf_load<E>(vb_, off));
-          buf_store<E>(dvb, off, to_e<E>(sm.b[r] * au[e]));
+          // (rows at or past len fall outside the descriptor: v reads as 0)
+          const float vv = to_f(vq[rt][e]);
+          sm.r3[r * KLD + d] = to_e<E>(sm.b[r] * au[e]);
           dK[u][e] += bgr * aw[e];
           const float rk = aw[e] * kv[e];
           rdb_acc[rt][e] += au[e] * vv + sm.ea[r] * rk;
@@ -875,6 +886,23 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+    {
+      // the wave's dv columns, 16 bytes a lane (rows at or past len fall
+      // outside the buffer and are dropped)
+      constexpr int PPR = 16 / VE, NPC = (C * PPR + 63) / 64;
+#pragma unroll
+      for (int j = 0; j < DPW; ++j) {
+        const int dt = wave + NW * j;
+        if (dt >= DT) continue;
+#pragma unroll
+        for (int p = 0; p < NPC; ++p) {
+          const int pc = lane + 64 * p, row = pc / PPR, col = 16 * dt + (pc % PPR) * VE;
+          if (pc < C * PPR)
+            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(&sm.r3[row * KLD + col]), dvb,
+                                                   (int)(((uint32_t)row * v_row + (uint32_t)col) * sizeof(E)), 0, 0);
+        }
+      }
     }
     if (has_dt) {
 #pragma unroll
@@ -908,10 +936,12 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     if (wave == 0) {
       // dlog a: the suffix sums of dg within the chunk, as a wave-wide scan
       // (lane r holds row r; rows past len hold 0), in a fixed order
+      // (lane addresses from this V head's opaque lane index, so that none
+      // stays live across the loop)
       float acc = (lane < len) ? sm.dg[lane] : 0.f;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        const float x = __shfl_down(acc, off);
+        const float x = __int_as_float(__builtin_amdgcn_ds_bpermute(((lane + off) & 63) << 2, __float_as_int(acc)));
         if (lane + off < 64) acc += x;
       }
       if (lane < len) {
@@ -921,11 +951,11 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     }
   }
 
-  // this chunk's rows of dq and dk for this QK head, as raw buffers
-  const uint32_t qk_row = (uint32_t)(a.h_qk * D);
-  const uint32_t qk_bytes = (uint32_t)len * qk_row * (uint32_t)sizeof(E);
-  const auto dqb = raw_rsrc(static_cast<E*>(a.dq) + ((int64_t)start * a.h_qk + hq) * D, qk_bytes);
-  const auto dkb = raw_rsrc(static_cast<E*>(a.dk) + ((int64_t)start * a.h_qk + hq) * D, qk_bytes);
+  // this chunk's rows of dq and dk for this QK head: the tiles rounded to
+  // E into the (now free) dL/do and U row buffers, then stored as 16-byte
+  // row pieces through raw buffers (rows at or past len fall outside them
+  // and are dropped)
+  __syncthreads();                     // the last V head's LDS reads are done
 #pragma unroll
   for (int j = 0; j < DPW; ++j) {
     const int dt = wave + NW * j;
@@ -935,12 +965,25 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
       const int u = j * CT + rt;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        // rows at or past len fall outside both descriptors and are dropped
-        const uint32_t o = ((uint32_t)(4 * quad) * qk_row + (uint32_t)(16 * dt + l16)) * (uint32_t)sizeof(E) +
-                           (uint32_t)(16 * rt + e) * qk_row * (uint32_t)sizeof(E);
-        buf_store<E>(dqb, o, to_e<E>(dQ[u][e]));
-        buf_store<E>(dkb, o, to_e<E>(dK[u][e]));
+        const int r = 16 * rt + 4 * quad + e;
+        sm.u1.r1[r * KLD + 16 * dt + l16] = to_e<E>(dQ[u][e]);
+        sm.r2[r * KLD + 16 * dt + l16] = to_e<E>(dK[u][e]);
       }
+    }
+  }
+  __syncthreads();
+  const uint32_t qk_row = (uint32_t)(a.h_qk * D);
+  const uint32_t qk_bytes = (uint32_t)len * qk_row * (uint32_t)sizeof(E);
+  const auto dqb = raw_rsrc(static_cast<E*>(a.dq) + ((int64_t)start * a.h_qk + hq) * D, qk_bytes);
+  const auto dkb = raw_rsrc(static_cast<E*>(a.dk) + ((int64_t)start * a.h_qk + hq) * D, qk_bytes);
+#pragma unroll
+  for (int p = 0; p < SPT; ++p) {
+    const int idx = tid + p * kGradBlock;
+    const int r = idx / (D / VE), d = (idx % (D / VE)) * VE;
+    if (idx < C * D / VE) {
+      const int o = (int)(((uint32_t)r * qk_row + (uint32_t)d) * sizeof(E));
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(&sm.u1.r1[r * KLD + d]), dqb, o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(&sm.r2[r * KLD + d]), dkb, o, 0, 0);
     }
   }
 }

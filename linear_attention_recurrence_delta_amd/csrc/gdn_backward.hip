@@ -703,8 +703,6 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
       if (quad == 0) atomicAdd(&sm.dgw[wave][j], -colp);
     }
     __syncthreads();                   // x1 complete; dL/do and U rows dead
-    // requested before this phase's products: its K^T and Q^T fragments,
-    // the v rows and the dT phase's K fragments
 #pragma unroll
     for (int j = 0; j < DPW; ++j) {
       const int dt = wave + NW * j;

@@ -356,9 +356,11 @@ __global__ __launch_bounds__(kDScanBlock) void gdn_kb_dstate(const PrefillArgs a
 // (16 rt + 4 quad + i, 16 dt + l16) of a C x D accumulator tile. Every
 // product runs on the input dtype's MFMA with fp32 accumulation; the C x C
 // matrices that only feed products (dP * Dincl, dT, Y, B + B^T) are held in
-// the input dtype. Row and column sums of the per-element terms use DPP and
-// lane-row swaps, then LDS atomics into each wave's own row sums, which
-// are added in wave order at the end.
+// the input dtype. Row sums of the per-element terms are reduced within
+// each 16-lane row by a DPP butterfly that leaves one row's sum in each
+// lane, column sums by lane-row swaps; then LDS atomics (one per lane) add
+// them into each wave's own row sums, which are added in wave order at the
+// end.
 // --------------------------------------------------------------------------
 constexpr int kGradBlock = 256;
 
@@ -502,6 +504,15 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     }
     return f;
   };
+
+  // adds a value per row of the chunk to the wave's own row sums: lane
+  // (quad, l16) holds v[4 rt + i] for row 16 rt + 4 quad + i; the row's 16
+  // lanes are reduced in registers, then each lane adds one row's sum
+  auto add_row_sums = [&](float* dst, const float (&v)[4 * CT]) __attribute__((always_inline)) {
+    const float z = row_scatter_sum<4 * CT>(v, l16);
+    if (CT == 4 || l16 < 4) atomicAdd(&dst[16 * (l16 >> 2) + 4 * quad + (l16 & 3)], z);
+  };
+  static_assert(CT == 4 || CT == 1, "row sums of one or four row tiles");
 
   f32x4 dQ[TPW], dK[TPW];
 #pragma unroll
@@ -652,14 +663,13 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
     // the dP phase's P^T fragments, requested before the row sums
     const Frag<E>* ptf = reinterpret_cast<const Frag<E>*>(a.pt) + ch * G::QK_FR * 64;
     if (has_dt) {
+      float prv[4 * CT];
 #pragma unroll
       for (int rt = 0; rt < CT; ++rt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float s = sum16(prow[rt][i]);
-          if (l16 == 0) atomicAdd(&sm.dgw[wave][16 * rt + 4 * quad + i], s);
-        }
+        for (int i = 0; i < 4; ++i) prv[4 * rt + i] = prow[rt][i];
       }
+      add_row_sums(sm.dgw[wave], prv);
       fro = sum_rows4(sum16(fro));
       pk_all = sum_rows4(sum16(pk_all));
       if (lane == 0) {
@@ -679,7 +689,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
 #pragma unroll
       for (int ks = 0; ks < DKS; ++ks) ub[ks] = frag_row(sm.r2, KLD, 16 * jt, ks, D);
       const int j = 16 * jt + l16;
-      float colp = 0.f;
+      float colp = 0.f, m2v[4 * CT];
 #pragma unroll
       for (int rt = 0; rt < CT; ++rt) {
         f32x4 acc = zero4();
@@ -692,13 +702,13 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * rt + 4 * quad + i;
           const float m2 = acc[i] * to_f(pv[i + 4 * (rt & 1)]);
-          const float rs = sum16(m2);
-          if (l16 == 0) atomicAdd(&sm.dgw[wave][r], rs);
+          m2v[4 * rt + i] = m2;
           colp += m2;
           const float gm = (j <= r && r < len) ? __expf(fminf(sm.g[r] - sm.g[j], 0.f)) : 0.f;
           sm.x1[r * ELD + j] = to_e<E>(acc[i] * gm);
         }
       }
+      add_row_sums(sm.dgw[wave], m2v);
       colp = sum_rows4(colp);
       if (quad == 0) atomicAdd(&sm.dgw[wave][j], -colp);
     }
@@ -785,7 +795,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
 #pragma unroll
       for (int s = 0; s < CKS; ++s) yb[s] = frag_col(ys, ELD, 16 * it, s, C);
       const int i = 16 * it + l16;
-      float colm = 0.f;
+      float colm = 0.f, rdbv[4 * CT], rdgv[4 * CT];
 #pragma unroll
       for (int rt = 0; rt < CT; ++rt) {
         f32x4 acc = zero4();
@@ -800,12 +810,8 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
           const float da = lower ? -acc[e] : 0.f;
           const float bm = da * sm.b[r] * gm;
           const float mb2 = bm * kk[e];
-          const float rdb = sum16(da * kk[e] * gm);
-          const float rdg = sum16(mb2);
-          if (l16 == 0) {
-            atomicAdd(&sm.dbw[wave][r], rdb);
-            atomicAdd(&sm.dgw[wave][r], rdg);
-          }
+          rdbv[4 * rt + e] = da * kk[e] * gm;
+          rdgv[4 * rt + e] = mb2;
           colm += mb2;
           if (i < r) {
             sm.x1[r * ELD + i] = to_e<E>(bm);
@@ -815,6 +821,8 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
           }
         }
       }
+      add_row_sums(sm.dbw[wave], rdbv);
+      add_row_sums(sm.dgw[wave], rdgv);
       colm = sum_rows4(colm);
       if (quad == 0) atomicAdd(&sm.dgw[wave][i], -colm);
     }
@@ -903,17 +911,14 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
       }
     }
     if (has_dt) {
+      float sbv[4 * CT], sgv[4 * CT];
 #pragma unroll
       for (int rt = 0; rt < CT; ++rt) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float sb = sum16(rdb_acc[rt][e]), sg = sum16(rdg_acc[rt][e]);
-          if (l16 == 0) {
-            atomicAdd(&sm.dbw[wave][16 * rt + 4 * quad + e], sb);
-            atomicAdd(&sm.dgw[wave][16 * rt + 4 * quad + e], sg);
-          }
-        }
+        for (int e = 0; e < 4; ++e) { sbv[4 * rt + e] = rdb_acc[rt][e]; sgv[4 * rt + e] = rdg_acc[rt][e]; }
       }
+      add_row_sums(sm.dbw[wave], sbv);
+      add_row_sums(sm.dgw[wave], sgv);
     }
     __syncthreads();
     if (tid < C) {

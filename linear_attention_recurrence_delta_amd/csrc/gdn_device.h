@@ -112,6 +112,45 @@ __device__ __forceinline__ float sum16(float x) {
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // row_mirror
   return x;
 }
+// Reduce-scatter within each 16-lane row of the wave: lane i of a row gets
+// the sum over the row's 16 lanes of their values v[i] (NV = 16), or of
+// v[i % 4] (NV = 4, in every lane). A butterfly over the lane pairs i ^ 15,
+// i ^ 7 (within each half row), i ^ 2 and i ^ 1: at each step a lane keeps
+// the half of its values that its pair does not keep and adds the pair's
+// partial sums of that half, so each lane ends with one complete sum, added
+// in a fixed order (NV = 4 then sums the row's four groups of four lanes).
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int NV>
+__device__ __forceinline__ float row_scatter_sum(const float (&v)[NV], int l16) {
+  static_assert(NV == 16 || NV == 4, "16 or 4 values per lane");
+  float x[4];
+  if constexpr (NV == 16) {
+    float w[8];
+    const bool b3 = (l16 & 8) != 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = (b3 ? v[8 + k] : v[k]) + dpp_mov<0x140>(b3 ? v[k] : v[8 + k]);      // row_mirror
+    const bool b2 = (l16 & 4) != 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = (b2 ? w[4 + k] : w[k]) + dpp_mov<0x141>(b2 ? w[k] : w[4 + k]);      // row_half_mirror
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = v[k];
+  }
+  const bool b1 = (l16 & 2) != 0;
+  float y[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) y[k] = (b1 ? x[2 + k] : x[k]) + dpp_mov<0x4E>(b1 ? x[k] : x[2 + k]);         // quad_perm 2,3,0,1
+  const bool b0 = (l16 & 1) != 0;
+  float z = (b0 ? y[1] : y[0]) + dpp_mov<0xB1>(b0 ? y[0] : y[1]);                                          // quad_perm 1,0,3,2
+  if constexpr (NV == 4) {
+    z += dpp_mov<0x124>(z);    // row_ror:4
+    z += dpp_mov<0x128>(z);    // row_ror:8
+  }
+  return z;
+}
+
 __device__ __forceinline__ float sum_rows4(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
   x = __int_as_float(a[0]) + __int_as_float(a[1]);

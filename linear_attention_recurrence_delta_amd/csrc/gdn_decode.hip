@@ -43,9 +43,12 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
 
   const E* kp = static_cast<const E*>(a.k) + (n * a.h_qk + hq) * D + rg * RPT;
   const E* qp = static_cast<const E*>(a.q) + (n * a.h_qk + hq) * D + rg * RPT;
-  float kk[RPT], qq[RPT];
+  // k and q stay in the input dtype until used (fewer registers, so that
+  // v can be requested with the state without lowering occupancy)
+  E kk[RPT], qq[RPT];
 #pragma unroll
-  for (int r = 0; r < RPT; ++r) { kk[r] = to_f(kp[r]); qq[r] = to_f(qp[r]); }
+  for (int r = 0; r < RPT; ++r) { kk[r] = kp[r]; qq[r] = qp[r]; }
+  const Half<E> vh = *reinterpret_cast<const Half<E>*>(static_cast<const E*>(a.v) + nh * D + 4 * (tid % (D / 4)));
 
   f32x4* sp = reinterpret_cast<f32x4*>(a.state + nh * D * D) + (rg * RPT) * CG + cg;
   f32x4 s[RPT];
@@ -56,13 +59,14 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
   float kq = 0.f, k2 = 0.f, q2 = 0.f;
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
-    if constexpr (!ND) p += s[r] * kk[r];
-    rq += s[r] * qq[r];
-    kq += kk[r] * qq[r];
+    const float kr = to_f(kk[r]), qr = to_f(qq[r]);
+    if constexpr (!ND) p += s[r] * kr;
+    rq += s[r] * qr;
+    kq += kr * qr;
   }
   if constexpr (P) {
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) { k2 += kk[r] * kk[r]; q2 += qq[r] * qq[r]; }
+    for (int r = 0; r < RPT; ++r) { k2 += to_f(kk[r]) * to_f(kk[r]); q2 += to_f(qq[r]) * to_f(qq[r]); }
   }
   if constexpr (!ND) red_p[rg][cg] = p;
   red_r[rg][cg] = rq;
@@ -83,7 +87,7 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
     kq += red_kq[g][0];
     if constexpr (P) { k2 += red_kq[g][1]; q2 += red_kq[g][2]; }
   }
-  float alpha, beta;
+  float alpha, beta, kscale = 1.f;
   if constexpr (P) {
     // raw inputs: S^T k, S^T q and k.q are linear in k and q, so the unit
     // vectors' values are the raw sums times the inverse norms
@@ -91,21 +95,19 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
     p *= ik;
     rq *= iq;
     kq *= ik * iq;
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) kk[r] *= ik;
+    kscale = ik;
     alpha = expf(neg_softplus(a.log_alpha[nh]));
     beta = sigmoid_of(a.beta[nh]);
   } else {
     alpha = expf(a.log_alpha[nh]);
     beta = a.beta[nh];
   }
-  const E* vp = static_cast<const E*>(a.v) + nh * D + 4 * cg;
   f32x4 u;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) u[e] = ND ? beta * to_f(vp[e]) : beta * (to_f(vp[e]) - alpha * p[e]);
+  for (int e = 0; e < 4; ++e) u[e] = ND ? beta * to_f(vh[e]) : beta * (to_f(vh[e]) - alpha * p[e]);
 
 #pragma unroll
-  for (int r = 0; r < RPT; ++r) __builtin_nontemporal_store(s[r] * alpha + u * kk[r], sp + r * CG);
+  for (int r = 0; r < RPT; ++r) __builtin_nontemporal_store(s[r] * alpha + u * (to_f(kk[r]) * kscale), sp + r * CG);
 
   if (rg == 0) {
     Half<E> h;

@@ -107,12 +107,12 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_st
   for (int e = 0; e < 4; ++e) u[e] = ND ? beta * to_f(vh[e]) : beta * (to_f(vh[e]) - alpha * p[e]);
 
 #pragma unroll
-  for (int r = 0; r < RPT; ++r) __builtin_nontemporal_store(s[r] * alpha + u * (to_f(kk[r]) * kscale), sp + r * CG);
+  for (int r = 0; r < RPT; ++r) __builtin_nontemporal_store(decay_rank1(s[r], alpha, u, to_f(kk[r]) * kscale), sp + r * CG);
 
   if (rg == 0) {
     Half<E> h;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) h[e] = to_e<E>(alpha * rq[e] + u[e] * kq);
+    for (int e = 0; e < 4; ++e) h[e] = to_e<E>(fmaf(alpha, rq[e], u[e] * kq));
     *reinterpret_cast<Half<E>*>(static_cast<E*>(a.o) + nh * D + 4 * cg) = h;
   }
 }
@@ -207,7 +207,7 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_mu
 #pragma unroll
     for (int e = 0; e < 4; ++e) u[e] = ND ? beta * to_f(vp[e]) : beta * (to_f(vp[e]) - alpha * p[e]);
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) s[r] = s[r] * alpha + u * kk[r];
+    for (int r = 0; r < RPT; ++r) s[r] = decay_rank1(s[r], alpha, u, kk[r]);
     if (a.snapshots) {
       f32x4* snp = reinterpret_cast<f32x4*>(a.snapshots + tv * D * D) + (rg * RPT) * CG + cg;
 #pragma unroll
@@ -216,7 +216,7 @@ __global__ __launch_bounds__((D / 4) * DecodeShape<D>::RG) void gdn_kd_decode_mu
     if (rg == 0) {
       Half<E> h;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) h[e] = to_e<E>(alpha * rq[e] + u[e] * kq);
+      for (int e = 0; e < 4; ++e) h[e] = to_e<E>(fmaf(alpha, rq[e], u[e] * kq));
       *reinterpret_cast<Half<E>*>(static_cast<E*>(a.o) + tv * D + 4 * cg) = h;
     }
   }

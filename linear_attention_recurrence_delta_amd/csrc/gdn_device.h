@@ -98,6 +98,16 @@ __device__ __forceinline__ Frag<E> acc_to_frag(const f32x4& lo, const f32x4& hi)
 
 __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
+// Decay and rank-one update of four state entries, each fma(u_e, k, s_e * alpha):
+// the contraction is fixed here rather than left to the compiler, so that
+// kernels applying the same update agree bit for bit.
+__device__ __forceinline__ f32x4 decay_rank1(f32x4 s, float alpha, f32x4 u, float k) {
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = fmaf(u[e], k, s[e] * alpha);
+  return r;
+}
+
 // Cross-lane sums without LDS round trips. The accumulator of a 16x16 tile
 // holds one row in each 16-lane row of the wave, so a row's sum over its
 // columns is a sum over those 16 lanes (DPP: swap neighbours, then pairs,

@@ -117,6 +117,16 @@ typedef struct {
  *              return are unspecified. Calls that run concurrently need
  *              distinct workspaces.
  *
+ * Streams: the work is ordered on `stream` as if all of it were enqueued
+ * there. When the scan's workgroups (one per sequence, V head and 32 state
+ * columns) would leave at least a fifth of the CUs idle, the input has at
+ * least 256 chunk slots and final_state is given, the call also uses one
+ * stream per device that the library creates on first use (default
+ * priority) and keeps for the process: kernel 2 forms the later chunks there
+ * while the scan runs the earlier ones, joined to `stream` by events (the
+ * fork and join can be captured in a HIP graph). Results are bitwise those
+ * of the stage-by-stage calls below, which gdn_chunk_fwd_noalloc makes.
+ *
  * Returns GDN_SUCCESS once all kernels are enqueued.
  */
 gdn_status_t gdn_chunk_fwd(const gdn_dims_t* dims,
@@ -136,7 +146,8 @@ gdn_status_t gdn_chunk_fwd(const gdn_dims_t* dims,
  * Arguments are those of gdn_chunk_fwd. Stage 2 reads what stage 1 left in
  * `workspace`, so a call starting at stage 2 must follow a call that ran
  * stage 1 with identical arguments and workspace on the same stream.
- * gdn_chunk_fwd is gdn_chunk_fwd_stages(..., 1, 2). Returns
+ * gdn_chunk_fwd is gdn_chunk_fwd_stages(..., 1, 2); any other stage range
+ * enqueues one launch per stage on `stream`, one after the other. Returns
  * GDN_ERROR_INVALID_VALUE unless 1 <= first_stage <= last_stage <= 2.
  */
 gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims,
@@ -154,7 +165,7 @@ gdn_status_t gdn_chunk_fwd_stages(const gdn_dims_t* dims,
  * from a device array of GDN_NOALLOC_SCRATCH_BYTES bytes that the library
  * holds on each GPU it runs on until the process ends. The caller still
  * passes inputs and outputs. Makes no hipMalloc, hipFree or other
- * allocating call. Dims whose gdn_chunk_fwd_workspace_bytes() exceeds
+ * allocating call, and enqueues everything on `stream`. Dims whose gdn_chunk_fwd_workspace_bytes() exceeds
  * GDN_NOALLOC_SCRATCH_BYTES (at 16 QK / 48 V heads, head dim 128, bf16,
  * chunk 64: about 3,900 tokens) return GDN_ERROR_WORKSPACE before anything
  * is enqueued. The array belongs to the device current at the call, which

@@ -58,6 +58,8 @@ struct PrefillArgs {
   int64_t num_seqs;         // N
   int64_t total_tokens;     // T
   int64_t max_chunks;       // NC = floor(T/C) + N
+  int64_t win_lo;           // chunk-slot window [win_lo, win_hi) of one launch (set by the
+  int64_t win_hi;           //    launcher): kernel 2 forms those slots, the scan runs them
   int32_t h_qk;             // HQ
   int32_t h_v;              // HV
   int32_t group;            // HV / HQ

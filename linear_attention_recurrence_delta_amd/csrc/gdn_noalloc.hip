@@ -62,6 +62,12 @@ extern "C" gdn_status_t gdn_chunk_fwd_noalloc(const gdn_dims_t* dims, const void
     }
     ptr = g_scratch_ptr[dev];
   }
-  return gdn_chunk_fwd(dims, q, k, v, log_alpha, beta, init_state, cu_seqlens, o, final_state, ptr, kScratchBytes,
-                       stream);
+  // the stages one after the other on `stream`: gdn_chunk_fwd's two-stream
+  // form would create the library's second stream on first use
+  gdn_status_t r = gdn_chunk_fwd_stages(dims, q, k, v, log_alpha, beta, init_state, cu_seqlens, o, final_state, ptr,
+                                        kScratchBytes, stream, 1, 1);
+  if (r == GDN_SUCCESS)
+    r = gdn_chunk_fwd_stages(dims, q, k, v, log_alpha, beta, init_state, cu_seqlens, o, final_state, ptr,
+                             kScratchBytes, stream, 2, 2);
+  return r;
 }

@@ -41,6 +41,8 @@
 //   pmask [c][hv][C/16][C32] : frag (nt, s) of P = (q_r . k_j) exp(g_r - g_j) masked to
 //                              j <= r < L (col r = query, k = key j)
 // with C32 = ceil(C/32), D32 = ceil(D/32); entries past the chunk end are zero.
+#include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -570,7 +572,9 @@ __device__ __forceinline__ void key_products(const InvSmem<E, D, C>& sm, f32x4 (
 // per V head, each repeating the QK head's work, took 0.63 ms against
 // 0.51 ms for the forward pass on the 64K-token layer.)
 // bf16: five workgroups per CU, 26 KB of LDS and at most 96 VGPRs each
-template <typename E, int D, int C, bool P, bool ND, bool BW>
+// WIN marks the launches of a window beside the scan (the same code under
+// another name, so that traces keep them apart from whole launches)
+template <typename E, int D, int C, bool P, bool ND, bool BW, bool WIN = false>
 __global__ __launch_bounds__(kBlock, (k2_occupancy<E, D, C>(5))) void gdn_k2_inverse_w(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   using SM = InvSmem<E, D, C>;
@@ -583,7 +587,7 @@ __global__ __launch_bounds__(kBlock, (k2_occupancy<E, D, C>(5))) void gdn_k2_inv
   // the QK heads of one chunk, which read the same gate lines, are
   // consecutive logical ids and so share an XCD
   const int64_t lid = xcd_local_id(blockIdx.x, gridDim.x);
-  const int64_t c = lid / a.h_qk;
+  const int64_t c = a.win_lo + lid / a.h_qk;   // this launch's window of chunk slots
   const int hq = (int)(lid % a.h_qk);
   // lane indices are re-made opaque at the top of every V head's pass (see
   // there); the wave index is uniform
@@ -861,7 +865,8 @@ struct ScanSmem {
   float touch[kScanBlock / 64][64];    // landing place of the L2 warm-up loads
 };
 
-template <typename E, int D, int C, bool ND, bool SV>
+// WIN: as for kernel 2
+template <typename E, int D, int C, bool ND, bool SV, bool WIN = false>
 __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   using G = Cfg<E, D, C>;
   using SC = ScanCfg<E, D, C>;
@@ -899,6 +904,11 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   const int hq = hv / a.group;
   const int2 cr = chunk_range(a, n), sr = seq_range(a, n);
   const int c0 = cr.x, c1 = cr.y;
+  // the sequence's chunks in this launch's window of chunk slots: where the
+  // sequence began in an earlier window its state enters from final_state,
+  // and where it continues in a later one its state is left there
+  const int lo = max(c0, (int)a.win_lo), hi = min(c1, (int)a.win_hi);
+  const bool carried_in = lo > c0;
   // chunk x of this sequence starts at seq_start + (x - c0) * C; computing
   // start and length here keeps table reads off the per-chunk critical path
   const int seq_start = sr.x, seq_end = sr.y;
@@ -938,7 +948,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     }
   };
   auto copy_window = [&](int xs, int xp) __attribute__((always_inline)) {
-    if (xs < c1) {
+    if (xs < hi) {
       copy_region(0, static_cast<const char*>(a.key_t) + ((int64_t)xs * a.h_qk + hq) * B_KT,
                   reinterpret_cast<char*>(sm.kt[slot(xs)]), B_KT, false);
       copy_region(1, static_cast<const char*>(a.w) + ((int64_t)xs * a.h_v + hv) * B_W,
@@ -950,7 +960,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
       copy_region(4, reinterpret_cast<const char*>(a.dtab + ((int64_t)xs * a.h_v + hv) * (2 * C + 4)),
                   reinterpret_cast<char*>(sm.dtab[slot(xs)]), B_D, false);
     }
-    if (xp < c1) {
+    if (xp < hi) {
       copy_region(5, static_cast<const char*>(a.tinv) + ((int64_t)xp * a.h_v + hv) * B_T,
                   reinterpret_cast<char*>(sm.tf[slot(xp)]), B_T, true);
       // the V columns, row i of the chunk at byte 16 l of its job; rows
@@ -1008,7 +1018,7 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
     return static_cast<const char*>(a.v) + (((int64_t)(chunk_start(x) + i) * a.h_v + hv) * D + col0) * ESZ;
   };
   auto warm = [&](int x) __attribute__((always_inline)) {
-    if (x >= c1) return;
+    if (x >= hi) return;
     const int total = nv + nq + C;
     for (int t = 64 * uw + lane; t < total; t += 64 * NS) {
       const char* p = line_addr(x, t);
@@ -1245,19 +1255,18 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   // loaders copy chunk c+1's scan operands and chunk c+2's Ut operands into
   // LDS and wait for them; the Ut waves form chunk c+1's Ut tiles, then
   // warm L2 for chunk c+3.
-  if (c1 > c0) {
+  if (hi > lo) {
     if (is_scan) {
+      const float* s_in = carried_in ? a.final_state : a.init_state;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          S[dt][i] = a.init_state
-                         ? a.init_state[state_base + (int64_t)(16 * dt + 4 * quad + i) * D + col0 + 16 * slice + l16]
-                         : 0.f;
+          S[dt][i] = s_in ? s_in[state_base + (int64_t)(16 * dt + 4 * quad + i) * D + col0 + 16 * slice + l16] : 0.f;
       }
       __syncthreads();
-      for (int c = c0 - 1; c < c1; ++c) {
-        if (c >= c0) scan_chunk(c);
+      for (int c = lo - 1; c < hi; ++c) {
+        if (c >= lo) scan_chunk(c);
         if (NB == 1) lds_barrier();    // compute phase ends: the loaders may refill
         lds_barrier();
       }
@@ -1270,30 +1279,30 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
         }
       }
     } else if (is_loader) {
-      // prologue: chunk c0's Ut operands (the scan-operand jobs are switched
+      // prologue: chunk lo's Ut operands (the scan-operand jobs are switched
       // off by passing a chunk past the end)
-      copy_window(c1, c0);
+      copy_window(hi, lo);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      for (int c = c0 - 1; c < c1; ++c) {
+      for (int c = lo - 1; c < hi; ++c) {
         if (NB == 1) __syncthreads();  // one slot per region: wait for the compute phase
         copy_window(c + 1, c + 2);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
       }
     } else {
-      warm(c0 + 1);
-      warm(c0 + 2);
+      warm(lo + 1);
+      warm(lo + 2);
       __syncthreads();
       u32x4 ov[OJ], sv[NSV];
-      for (int c = c0 - 1; c < c1; ++c) {
+      for (int c = lo - 1; c < hi; ++c) {
         // chunk c - 1's outputs leave the Ut slot that chunk c + 1's tiles
         // take next (saving form: its S and U rows, whose staging area the
         // scan waves write again in the next iteration)
-        const bool st = !SV && STAGE_O && c > c0, ss = SV_STAGE && c > c0;
+        const bool st = !SV && STAGE_O && c > lo, ss = SV_STAGE && c > lo;
         if (st) read_outputs(c - 1, ov);
         if (ss) read_saved(c - 1, sv);
-        if (c + 1 < c1) produce_chunk(c + 1);
+        if (c + 1 < hi) produce_chunk(c + 1);
         if (st) store_outputs(c - 1, ov);
         if (ss) store_saved(c - 1, sv);
         warm(c + 3);
@@ -1301,16 +1310,17 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
         lds_barrier();
       }
       if (!SV && STAGE_O) {
-        read_outputs(c1 - 1, ov);
-        store_outputs(c1 - 1, ov);
+        read_outputs(hi - 1, ov);
+        store_outputs(hi - 1, ov);
       }
       if (SV_STAGE) {
-        read_saved(c1 - 1, sv);
-        store_saved(c1 - 1, sv);
+        read_saved(hi - 1, sv);
+        store_saved(hi - 1, sv);
       }
     }
-  } else if (is_scan && a.final_state) {
-    // empty sequence: the final state is the initial state
+  } else if (is_scan && a.final_state && c1 <= c0 && a.win_lo == 0) {
+    // empty sequence (written by the first window): the final state is the
+    // initial state
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -1322,11 +1332,118 @@ __global__ __launch_bounds__(kScanBlock) void gdn_k3_scan(const PrefillArgs a) {
   }
 }
 
+template <typename E, int D, int C, bool WIN>
+hipError_t launch_k2_fwd(PrefillArgs a, int64_t lo, int64_t hi, hipStream_t s) {
+  if (hi <= lo) return hipSuccess;
+  a.win_lo = lo;
+  a.win_hi = hi;
+  const dim3 g((unsigned)((hi - lo) * a.h_qk)), b(kBlock);
+  if (a.prep) {
+    if (a.no_delta) gdn_k2_inverse_w<E, D, C, true, true, false, WIN><<<g, b, 0, s>>>(a);
+    else gdn_k2_inverse_w<E, D, C, true, false, false, WIN><<<g, b, 0, s>>>(a);
+  } else {
+    if (a.no_delta) gdn_k2_inverse_w<E, D, C, false, true, false, WIN><<<g, b, 0, s>>>(a);
+    else gdn_k2_inverse_w<E, D, C, false, false, false, WIN><<<g, b, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+template <typename E, int D, int C, bool WIN>
+hipError_t launch_scan_fwd(PrefillArgs a, int64_t lo, int64_t hi, hipStream_t s) {
+  a.win_lo = lo;
+  a.win_hi = hi;
+  const dim3 g((unsigned)(a.num_seqs * a.h_v * ScanCfg<E, D, C>::NCB)), b(kScanBlock);
+  if (a.no_delta) gdn_k3_scan<E, D, C, true, false, WIN><<<g, b, 0, s>>>(a);
+  else gdn_k3_scan<E, D, C, false, false, WIN><<<g, b, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// Kernel 2 beside the scan. The scan holds one CU per workgroup (its LDS),
+// one workgroup per (sequence, V head, column block); a long sequence with
+// few heads leaves CUs idle for its whole length. Then the chunk slots are
+// cut in two windows: kernel 2 forms the first on the whole chip; while the
+// scan runs it, kernel 2 forms the second on a second stream, on the CUs the
+// scan leaves free; a second scan launch waits for it and enters with the
+// state the first left in final_state (fp32, so the results are bitwise
+// those of one launch). Neither stream's launches read what the other's
+// concurrent ones write: kernel 2 writes only its window's slots, and the
+// scan copies and prefetches only its own.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t first = nullptr;    // kernel 2's first window formed (caller's stream)
+  hipEvent_t rest = nullptr;     // kernel 2's second window formed (side stream)
+  int cus = 0;
+  int state = 0;                 // 0 not set up, 1 ready, -1 unavailable
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+// The side stream, its events and the CU count of the current device, set
+// up on first use (default priority, non-blocking); null if unavailable.
+// Called with g_side_mu held.
+SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& ss = g_side[dev];
+  if (ss.state == 0) {
+    ss.state = -1;
+    if (hipDeviceGetAttribute(&ss.cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ss.cus > 0 &&
+        hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) == hipSuccess &&
+        hipEventCreateWithFlags(&ss.first, hipEventDisableTiming) == hipSuccess &&
+        hipEventCreateWithFlags(&ss.rest, hipEventDisableTiming) == hipSuccess)
+      ss.state = 1;
+  }
+  return ss.state == 1 ? &ss : nullptr;
+}
+
+// The first window's share x of the chunk slots. With a fraction phi of the
+// CUs idle beside the scan, and kernel 2 on the whole chip taking r times
+// the scan's time, the second window lands as the scan reaches it when
+// (1 - x) r / phi = x, i.e. x = r / (r + phi). r is fitted to timings
+// (d = 128, C = 64, bf16; 48 V heads, phi = 1/4: x from 0.4 to 0.6 timed,
+// 0.5-0.55 best); kernel 2's own ratio, ~0.37, overstates it.
+constexpr double kK2OverScan = 0.28;
+// fewer chunk slots than this, or fewer than a fifth of the CUs idle beside
+// the scan: the two launches run one after the other
+constexpr int64_t kOverlapMinChunks = 256;
+
 template <typename E, int D, int C>
-hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int last) {
+hipError_t launch_fwd_overlapped(const PrefillArgs& a, hipStream_t s, bool* done) {
+  *done = false;
+  const int64_t nc = a.max_chunks;
+  const int64_t groups = a.num_seqs * a.h_v * ScanCfg<E, D, C>::NCB;
+  if (!a.final_state || nc < kOverlapMinChunks) return hipSuccess;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* ss = side_stream();
+  if (!ss || 5 * groups > 4 * (int64_t)ss->cus) return hipSuccess;
+  const double phi = 1.0 - (double)groups / ss->cus;
+  const int64_t x = std::min(nc - 1, std::max<int64_t>(1, (int64_t)(nc * kK2OverScan / (kK2OverScan + phi))));
+  hipError_t e = launch_k2_fwd<E, D, C, true>(a, 0, x, s);
+  if (e == hipSuccess) e = hipEventRecord(ss->first, s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->first, 0);
+  if (e == hipSuccess) e = launch_scan_fwd<E, D, C, true>(a, 0, x, s);
+  if (e == hipSuccess) e = launch_k2_fwd<E, D, C, true>(a, x, nc, ss->stream);
+  if (e == hipSuccess) e = hipEventRecord(ss->rest, ss->stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(s, ss->rest, 0);
+  if (e == hipSuccess) e = launch_scan_fwd<E, D, C, true>(a, x, nc, s);
+  *done = true;
+  return e;
+}
+
+template <typename E, int D, int C>
+hipError_t launch_prefill_t(const PrefillArgs& args, hipStream_t s, int first, int last) {
+  PrefillArgs a = args;
+  a.win_lo = 0;
+  a.win_hi = a.max_chunks;
   const unsigned nc = (unsigned)a.max_chunks;
   const unsigned scan_groups = (unsigned)(a.num_seqs * a.h_v * ScanCfg<E, D, C>::NCB);
   const dim3 g_qk(nc * (unsigned)a.h_qk), g_scan(scan_groups);
+  if (!a.backward && first == 1 && last == 2) {
+    bool done = false;
+    const hipError_t e = launch_fwd_overlapped<E, D, C>(a, s, &done);
+    if (done || e != hipSuccess) return e;
+  }
   for (int stage = first; stage <= last; ++stage) {
     if (a.backward) {
       // the backward pass (which takes no flags): kernel 1 finds the chunks,
@@ -1341,23 +1458,15 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s, int first, int 
       }
       continue;
     }
-    // the forward pass: kernel 2 (per chunk and QK head, with kernel 1's work), then the scan
+    // the forward pass: kernel 2 (per chunk and QK head, with kernel 1's
+    // work), then the scan
+    hipError_t e = hipSuccess;
     switch (stage) {
-      case 1:
-        if (a.prep) {
-          if (a.no_delta) gdn_k2_inverse_w<E, D, C, true, true, false><<<g_qk, dim3(kBlock), 0, s>>>(a);
-          else gdn_k2_inverse_w<E, D, C, true, false, false><<<g_qk, dim3(kBlock), 0, s>>>(a);
-        } else {
-          if (a.no_delta) gdn_k2_inverse_w<E, D, C, false, true, false><<<g_qk, dim3(kBlock), 0, s>>>(a);
-          else gdn_k2_inverse_w<E, D, C, false, false, false><<<g_qk, dim3(kBlock), 0, s>>>(a);
-        }
-        break;
-      case 2:
-        if (a.no_delta) gdn_k3_scan<E, D, C, true, false><<<g_scan, dim3(kScanBlock), 0, s>>>(a);
-        else gdn_k3_scan<E, D, C, false, false><<<g_scan, dim3(kScanBlock), 0, s>>>(a);
-        break;
+      case 1: e = launch_k2_fwd<E, D, C, false>(a, 0, a.max_chunks, s); break;
+      case 2: e = launch_scan_fwd<E, D, C, false>(a, 0, a.max_chunks, s); break;
       default: return hipErrorInvalidValue;
     }
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }

@@ -39,8 +39,8 @@ def source_of(kernel):
 
 # compile-time switches of each kernel, in template-argument order (the bool
 # arguments follow the dtype and sizes); a true switch labels the instance
-FLAGS = {"gdn_k2_inverse_w": ("prep", "gate-only", "bwd"),
-         "gdn_k3_scan": ("gate-only", "save"), "gdn_kd_decode_step": ("prep", "gate-only"),
+FLAGS = {"gdn_k2_inverse_w": ("prep", "gate-only", "bwd", "window"),
+         "gdn_k3_scan": ("gate-only", "save", "window"), "gdn_kd_decode_step": ("prep", "gate-only"),
          "gdn_kd_decode_multi": ("prep", "gate-only")}
 
 

@@ -6,10 +6,14 @@ import json
 
 from linear_attention_recurrence_delta_amd import profiling as P
 
-SCAN = "_ZN3gdn12_GLOBAL__N_111gdn_k3_scanIDF16bLi128ELi64ELb0ELb0EEEvNS_11PrefillArgsE"
-SCAN_SAVE = "_ZN3gdn12_GLOBAL__N_111gdn_k3_scanIDF16bLi128ELi64ELb0ELb1EEEvNS_11PrefillArgsE"
-K2_BWD = "_ZN3gdn12_GLOBAL__N_116gdn_k2_inverse_wIDF16bLi128ELi64ELb0ELb0ELb1EEEvNS_11PrefillArgsE"
-K2_PREP = "void gdn::(anonymous namespace)::gdn_k2_inverse_w<__hip_bfloat16, 128, 64, true, false, false>(gdn::PrefillArgs)"
+SCAN = "_ZN3gdn12_GLOBAL__N_111gdn_k3_scanIDF16bLi128ELi64ELb0ELb0ELb0EEEvNS_11PrefillArgsE"
+SCAN_SAVE = "_ZN3gdn12_GLOBAL__N_111gdn_k3_scanIDF16bLi128ELi64ELb0ELb1ELb0EEEvNS_11PrefillArgsE"
+SCAN_WIN = "_ZN3gdn12_GLOBAL__N_111gdn_k3_scanIDF16bLi128ELi64ELb0ELb0ELb1EEEvNS_11PrefillArgsE"
+K2_BWD = "_ZN3gdn12_GLOBAL__N_116gdn_k2_inverse_wIDF16bLi128ELi64ELb0ELb0ELb1ELb0EEEvNS_11PrefillArgsE"
+K2_PREP = ("void gdn::(anonymous namespace)::gdn_k2_inverse_w<__hip_bfloat16, 128, 64, true, false, false, "
+           "false>(gdn::PrefillArgs)")
+K2_WIN = ("void gdn::(anonymous namespace)::gdn_k2_inverse_w<__hip_bfloat16, 128, 64, false, false, false, "
+          "true>(gdn::PrefillArgs)")
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -26,6 +30,9 @@ def test_short_names_label_true_switches():
     assert P.short_name(SCAN_SAVE) == "gdn_k3_scan [save]"
     assert P.short_name(K2_BWD) == "gdn_k2_inverse_w [bwd]"
     assert P.short_name(K2_PREP) == "gdn_k2_inverse_w [prep]"
+    # the launches of a window beside the scan
+    assert P.short_name(SCAN_WIN) == "gdn_k3_scan [window]"
+    assert P.short_name(K2_WIN) == "gdn_k2_inverse_w [window]"
     assert P.source_of("gdn_k2_inverse_w [bwd]") == "gdn_prefill.hip"
     assert P.source_of(COPY) is None
 

@@ -462,7 +462,7 @@ __device__ __forceinline__ void k2_invert_and_write(InvSmem<E, D, C>& sm, const 
         vg[4 * hh + e4] = to_e<E>(t * ei[e4]);
       }
     }
-    tg[it] = vb;
+    __builtin_nontemporal_store(vb, &tg[it]);
     sm.v.tbg[it] = vg;
   }
   __syncthreads();
@@ -479,7 +479,7 @@ __device__ __forceinline__ void k2_invert_and_write(InvSmem<E, D, C>& sm, const 
         acc0 = mma(kta[s], tb, acc0);
         if (2 * ksd + 1 < DT) acc1 = mma(ktb[s], tb, acc1);
       }
-      wg[(rt * DKS + ksd) * 64 + lane] = acc_to_frag<E>(acc0, acc1);
+      __builtin_nontemporal_store(acc_to_frag<E>(acc0, acc1), &wg[(rt * DKS + ksd) * 64 + lane]);
     }
     if constexpr (BW) {
       // backward pass: W^T fragments (dt, s), lane row d, elements token r:
@@ -660,8 +660,8 @@ __global__ __launch_bounds__(kBlock, (k2_occupancy<E, D, C>(5))) void gdn_k2_inv
       Frag<E>* ktg = reinterpret_cast<Frag<E>*>(a.key_t) + (c * a.h_qk + hq) * G::KT_FR * 64;
 #pragma unroll
       for (int s = 0; s < CKS; ++s) {
-        ktg[((2 * ksd) * CKS + s) * 64 + lane] = kta[s];
-        if (2 * ksd + 1 < DT) ktg[((2 * ksd + 1) * CKS + s) * 64 + lane] = ktb[s];
+        __builtin_nontemporal_store(kta[s], &ktg[((2 * ksd) * CKS + s) * 64 + lane]);
+        if (2 * ksd + 1 < DT) __builtin_nontemporal_store(ktb[s], &ktg[((2 * ksd + 1) * CKS + s) * 64 + lane]);
       }
     }
   }
@@ -698,7 +698,7 @@ __global__ __launch_bounds__(kBlock, (k2_occupancy<E, D, C>(5))) void gdn_k2_inv
     }
     Frag<E>* qfg = reinterpret_cast<Frag<E>*>(a.q_frag) + (c * a.h_qk + hq) * G::Q_FR * 64;
 #pragma unroll
-    for (int ks = 0; ks < DKS; ++ks) qfg[(nt * DKS + ks) * 64 + lane] = qf[ks];
+    for (int ks = 0; ks < DKS; ++ks) __builtin_nontemporal_store(qf[ks], &qfg[(nt * DKS + ks) * 64 + lane]);
 #pragma unroll
     for (int s = 0; s < CKS; ++s) {
       if (causal_zero(nt, s)) continue;
@@ -778,7 +778,7 @@ __global__ __launch_bounds__(kBlock, (k2_occupancy<E, D, C>(5))) void gdn_k2_inv
           const float m = (float)(j <= rq) * vr;
           v[e] = to_e<E>(qk[s][e >> 2][e & 3] * (__expf(fminf(gr - sm.gb[0][min(j, C - 1)], 0.f)) * m));
         }
-        pg[(nt * CKS + s) * 64 + lane] = v;
+        __builtin_nontemporal_store(v, &pg[(nt * CKS + s) * 64 + lane]);
       }
     }
     write_row_factors(sm, a.dtab + ch * (2 * C + 4), len, tid);

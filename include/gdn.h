@@ -120,9 +120,10 @@ typedef struct {
  * Streams: the work is ordered on `stream` as if all of it were enqueued
  * there. When the scan's workgroups (one per sequence, V head and 32 state
  * columns) would leave at least a fifth of the CUs idle, the input has at
- * least 256 chunk slots and final_state is given, the call also uses one
- * stream per device that the library creates on first use (default
- * priority) and keeps for the process: kernel 2 forms the later chunks there
+ * least 256 chunk slots, final_state is given and `stream` belongs to the
+ * current device, the call also uses one stream per device that the
+ * library creates on first use (default priority, on the current device)
+ * and keeps for the process: kernel 2 forms the later chunks there
  * while the scan runs the earlier ones, joined to `stream` by events (the
  * fork and join can be captured in a HIP graph). Results are bitwise those
  * of the stage-by-stage calls below, which gdn_chunk_fwd_noalloc makes.

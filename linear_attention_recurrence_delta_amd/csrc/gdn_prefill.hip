@@ -1380,11 +1380,15 @@ std::mutex g_side_mu;
 SideStream g_side[kMaxDevices];
 
 // The side stream, its events and the CU count of the current device, set
-// up on first use (default priority, non-blocking); null if unavailable.
+// up on first use (default priority, non-blocking); null if unavailable, or
+// if `s` belongs to another device (the side stream's launches would then
+// run on the wrong GPU; the caller then runs the stages in order on `s`).
 // Called with g_side_mu held.
-SideStream* side_stream() {
+SideStream* side_stream(hipStream_t s) {
   int dev = 0;
+  hipDevice_t sdev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (hipStreamGetDevice(s, &sdev) != hipSuccess || (int)sdev != dev) return nullptr;
   SideStream& ss = g_side[dev];
   if (ss.state == 0) {
     ss.state = -1;
@@ -1415,7 +1419,7 @@ hipError_t launch_fwd_overlapped(const PrefillArgs& a, hipStream_t s, bool* done
   const int64_t groups = a.num_seqs * a.h_v * ScanCfg<E, D, C>::NCB;
   if (!a.final_state || nc < kOverlapMinChunks) return hipSuccess;
   std::lock_guard<std::mutex> lock(g_side_mu);
-  SideStream* ss = side_stream();
+  SideStream* ss = side_stream(s);
   if (!ss || 5 * groups > 4 * (int64_t)ss->cus) return hipSuccess;
   const double phi = 1.0 - (double)groups / ss->cus;
   const int64_t x = std::min(nc - 1, std::max<int64_t>(1, (int64_t)(nc * kK2OverScan / (kK2OverScan + phi))));

@@ -296,6 +296,12 @@ __global__ __launch_bounds__(kBlock) void gdn_k1_chunk_prep(const PrefillArgs a)
 // One workgroup per (chunk, QK head) does the QK head's work once and then
 // takes the group's V heads in turn; the backward pass's form reads kernel
 // 1's outputs and also writes the operands of the gradient kernel.
+// The fragments for the scan leave as non-temporal stores, each wave
+// instruction a whole 1 KB block: the scan reads them much later (from HBM
+// either way), and such stores leave alone the lines that the scan's
+// warm-up has brought into L2, which matters while kernel 2 forms a later
+// window beside the scan. (Partial-line writes, as the scan's outputs,
+// measured slower with the same hint.)
 // --------------------------------------------------------------------------
 
 template <typename E, int D, int C>
@@ -1405,8 +1411,10 @@ SideStream* side_stream(hipStream_t s) {
 // CUs idle beside the scan, and kernel 2 on the whole chip taking r times
 // the scan's time, the second window lands as the scan reaches it when
 // (1 - x) r / phi = x, i.e. x = r / (r + phi). r is fitted to timings
-// (d = 128, C = 64, bf16; 48 V heads, phi = 1/4: x from 0.4 to 0.6 timed,
-// 0.5-0.55 best); kernel 2's own ratio, ~0.37, overstates it.
+// (d = 128, C = 64, bf16; 48 V heads, phi = 1/4: r from 0.20 to 0.34 timed,
+// 0.26-0.28 best, x = 0.51-0.53); kernel 2's own ratio, ~0.38, overstates
+// it. More than two windows measured slower: at each later boundary the
+// next scan's workgroups, each needing an empty CU, wait behind kernel 2's.
 constexpr double kK2OverScan = 0.28;
 // fewer chunk slots than this, or fewer than a fifth of the CUs idle beside
 // the scan: the two launches run one after the other

@@ -233,6 +233,54 @@ WORKLOADS = {
 }
 
 
+def make_prefill_device(seed, seq_len, h_qk, h_v, d, device, dtype=torch.bfloat16):
+    """One sequence of the recipe above drawn on `device` (for inputs too
+    large to draw on the host): torch.Generator(device) seeded with `seed`,
+    float32 draws in the order q, k, v, log_alpha, beta, init (N(0, 0.02^2)),
+    q and k normalised in float32, then q/k/v cast to `dtype`. Same keys and
+    shapes as make_prefill with init="randn" (cu_seqlens None); the tensors
+    stay on `device`."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    T = int(seq_len)
+
+    def unit(shape):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        x /= torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+        return x.to(dtype)
+
+    q = unit((T, h_qk, d))
+    k = unit((T, h_qk, d))
+    v = torch.randn((T, h_v, d), generator=g, device=device, dtype=torch.float32).to(dtype)
+    la = -torch.nn.functional.softplus(torch.randn((T, h_v), generator=g, device=device) - 2.0)
+    beta = torch.sigmoid(torch.randn((T, h_v), generator=g, device=device))
+    init = 0.02 * torch.randn((1, h_v, d, d), generator=g, device=device)
+    return dict(q=q, k=k, v=v, log_alpha=la, beta=beta, init_state=init, cu_seqlens=None)
+
+
+def make_decode_device(seed, batch, h_qk, h_v, d, device, dtype=torch.bfloat16):
+    """One decode step of the recipe above for `batch` sequences, drawn on
+    `device` like make_prefill_device (order: state0, q, k, v, log_alpha,
+    beta). Keys as make_decode without the step axis: state0
+    [batch,h_v,d,d]; q, k [batch,h_qk,d]; v [batch,h_v,d]; log_alpha, beta
+    [batch,h_v]."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    state0 = 0.02 * torch.randn((batch, h_v, d, d), generator=g, device=device)
+
+    def unit(shape):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        x /= torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+        return x.to(dtype)
+
+    q = unit((batch, h_qk, d))
+    k = unit((batch, h_qk, d))
+    v = torch.randn((batch, h_v, d), generator=g, device=device, dtype=torch.float32).to(dtype)
+    la = -torch.nn.functional.softplus(torch.randn((batch, h_v), generator=g, device=device) - 2.0)
+    beta = torch.sigmoid(torch.randn((batch, h_v), generator=g, device=device))
+    return dict(state0=state0, q=q, k=k, v=v, log_alpha=la, beta=beta)
+
+
 def workload_inputs(name, **overrides):
     """Inputs of a named workload; overrides replace recipe fields (used to
     shrink a workload for a quick check, e.g. steps=4)."""

@@ -1,0 +1,109 @@
+"""GPU parity where element offsets pass 2^31: every global index product of
+the prefill and decode kernels must be formed in 64 bits.
+
+- Prefill of one sequence of 2^20 + 45 tokens at the pages' head layout (16
+  QK / 48 V heads, head dim 128, bf16, chunk 64; about 70 GB on the
+  device): v and o hold 6.4e9 elements, so every token past ~350K sits
+  beyond a 32-bit element offset. The last QK group (V heads 45..47, the
+  largest offsets at every token) is compared on every token and its final
+  state with the fp64 form-1 recurrence (the C oracle), within the bf16
+  tolerances of the other parity tests.
+- One decode step over 4,096 sequences (the fp32 state, 12.9 GB, holds
+  3.2e9 elements): the last three sequences, on every V head, against the
+  oracle's single step.
+
+Inputs are drawn on the device (inputs.make_prefill_device,
+make_decode_device: the same recipe in float32 draws); only the compared
+heads and sequences are copied to the host for the oracle. Skipped when
+the device has too little free memory.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_recurrence_delta_amd as gdn
+from linear_attention_recurrence_delta_amd import inputs as I
+from oracle import c_ref as CR
+from oracle import gdn_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+MAX_ABS, REL_L2 = 2e-2, 5e-3          # bf16 inputs, fp32 state
+HQ, HV, D, C = 16, 48, 128, 64
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def np64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def check(got, want, what):
+    err = got - want
+    rel = np.linalg.norm(err) / np.linalg.norm(want)
+    mx = np.abs(err).max()
+    say(f"  {what}: rel-L2 {rel:.2e} max-abs {mx:.2e}")
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    assert mx <= MAX_ABS and rel <= REL_L2, f"{what}: max-abs {mx:.3e}, rel-L2 {rel:.3e}"
+
+
+def need_free(nbytes):
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info(DEV)
+    if free < nbytes:
+        pytest.skip(f"needs {nbytes / 2**30:.0f} GiB of free device memory, {free / 2**30:.0f} GiB free")
+
+
+def test_prefill_beyond_32bit_element_offsets():
+    T = (1 << 20) + 45
+    assert T * HV * D > 2**31
+    dims = gdn.make_dims(1, T, HQ, HV, D, D, C, torch.bfloat16)
+    ws_bytes = gdn.gdn_chunk_fwd_workspace_bytes(dims)
+    # inputs and outputs (bf16 q, k, v, o; fp32 gates), workspace, and the
+    # float32 draws of v while it is made
+    io = 2 * T * HQ * D * 2 + 2 * T * HV * D * 2 + 2 * T * HV * 4
+    need_free(io + ws_bytes + T * HV * D * 4 + (4 << 30))
+    say(f"prefill T={T} heads {HQ}/{HV} d={D}: workspace {ws_bytes / 2**30:.1f} GiB")
+    inp = I.make_prefill_device(91, T, HQ, HV, D, DEV)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    o, fin = gdn.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                               inp["init_state"], None, chunk=C, workspace=ws)
+    torch.cuda.synchronize()
+    del ws
+    # the last QK group: QK head 15 and its V heads 45..47
+    hq, hv = slice(HQ - 1, HQ), slice(HV - 3, HV)
+    got_o, got_f = np64(o[:, hv]), np64(fin[:, hv])
+    args = [inp[x][:, s].float().cpu().numpy()
+            for x, s in (("q", hq), ("k", hq), ("v", hv), ("log_alpha", hv), ("beta", hv))]
+    init = inp["init_state"][:, hv].cpu().numpy()
+    del inp, o, fin
+    torch.cuda.empty_cache()
+    say("  oracle: C form-1 recurrence on V heads 45..47")
+    want_o, want_f = CR.recurrent_form1(*args, init_state=init, threads=3)
+    check(got_o, want_o, "o, V heads 45..47, every token")
+    tail = T - (1 << 19)
+    check(got_o[tail:], want_o[tail:], "o, V heads 45..47, tokens past 2^19")
+    check(got_f, want_f, "final state, V heads 45..47")
+
+
+def test_decode_beyond_32bit_state_offsets():
+    N = 4096
+    assert N * HV * D * D > 2**31
+    need_free(N * HV * D * D * 4 * 2 + (2 << 30))
+    say(f"decode N={N} heads {HQ}/{HV} d={D}: state {N * HV * D * D * 4 / 2**30:.1f} GiB")
+    dec = I.make_decode_device(92, N, HQ, HV, D, DEV)
+    last = slice(N - 3, N)
+    before = dec["state0"][last].cpu().numpy().astype(np.float64)
+    args = [dec[x][last].float().cpu().numpy().astype(np.float64)
+            for x in ("q", "k", "v", "log_alpha", "beta")]
+    o = gdn.gdn_decode_step(dec["q"], dec["k"], dec["v"], dec["log_alpha"], dec["beta"], dec["state0"])
+    torch.cuda.synchronize()
+    got_o, got_s = np64(o[last]), np64(dec["state0"][last])
+    del dec, o
+    torch.cuda.empty_cache()
+    want_o, want_s = O.decode_step(before, *args)
+    check(got_o, want_o, "decode o, last three sequences")
+    check(got_s, want_s, "decode state, last three sequences")

@@ -281,6 +281,16 @@ def make_decode_device(seed, batch, h_qk, h_v, d, device, dtype=torch.bfloat16):
     return dict(state0=state0, q=q, k=k, v=v, log_alpha=la, beta=beta)
 
 
+def make_backward_seeds_device(seed, seq_len, h_v, d, device, dtype=torch.bfloat16):
+    """make_backward_seeds for one sequence, drawn on `device` like
+    make_prefill_device (float32 draws, order d_o, d_final)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    d_o = torch.randn((int(seq_len), h_v, d), generator=g, device=device, dtype=torch.float32).to(dtype)
+    d_final = torch.randn((1, h_v, d, d), generator=g, device=device)
+    return dict(d_o=d_o, d_final=d_final)
+
+
 def workload_inputs(name, **overrides):
     """Inputs of a named workload; overrides replace recipe fields (used to
     shrink a workload for a quick check, e.g. steps=4)."""

@@ -8,6 +8,10 @@ the prefill and decode kernels must be formed in 64 bits.
   largest offsets at every token) is compared on every token and its final
   state with the fp64 form-1 recurrence (the C oracle), within the bf16
   tolerances of the other parity tests.
+- The backward pass of a 400,037-token sequence at the same layout (about
+  80 GB with its workspace): the gradients of the last 512 tokens of the
+  last QK group, which lie past 2^31 elements, against the oracle's
+  forward recurrence to their start and its backpropagation over them.
 - One decode step over 4,096 sequences (the fp32 state, 12.9 GB, holds
   3.2e9 elements): the last three sequences, on every V head, against the
   oracle's single step.
@@ -87,6 +91,52 @@ def test_prefill_beyond_32bit_element_offsets():
     tail = T - (1 << 19)
     check(got_o[tail:], want_o[tail:], "o, V heads 45..47, tokens past 2^19")
     check(got_f, want_f, "final state, V heads 45..47")
+
+
+def test_backward_beyond_32bit_element_offsets():
+    # The gradients of the last L tokens depend on earlier tokens only
+    # through the state entering them: the oracle runs the forward
+    # recurrence to token T - L (C oracle) and backpropagates over the last
+    # L tokens from that state (NumPy oracle), for the last QK group. Those
+    # tokens lie past 2^31 elements of v, o, dv and dL/do. Tolerances as in
+    # test_gpu_backward.py for bf16.
+    T, L = 400_037, 512
+    assert (T - L) * HV * D > 2**31
+    dims = gdn.make_dims(1, T, HQ, HV, D, D, C, torch.bfloat16)
+    ws_bytes = gdn.gdn_chunk_bwd_workspace_bytes(dims)
+    # q, k, dq, dk; v, dL/do, dv; gates and their gradients
+    io = 4 * T * HQ * D * 2 + 3 * T * HV * D * 2 + 4 * T * HV * 4
+    need_free(io + ws_bytes + T * HV * D * 4 + (4 << 30))
+    say(f"backward T={T} heads {HQ}/{HV} d={D}: workspace {ws_bytes / 2**30:.1f} GiB, tail of {L} tokens")
+    inp = I.make_prefill_device(93, T, HQ, HV, D, DEV)
+    seeds = I.make_backward_seeds_device(94, T, HV, D, DEV)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    g = gdn.gdn_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], seeds["d_o"],
+                          inp["init_state"], None, seeds["d_final"], chunk=C, workspace=ws)
+    torch.cuda.synchronize()
+    del ws
+    hq, hv = slice(HQ - 1, HQ), slice(HV - 3, HV)
+    got = {"dq": np64(g["dq"][T - L:, hq]), "dk": np64(g["dk"][T - L:, hq]), "dv": np64(g["dv"][T - L:, hv]),
+           "dlog_alpha": np64(g["dlog_alpha"][T - L:, hv]), "dbeta": np64(g["dbeta"][T - L:, hv])}
+    head = {x: inp[x][:, s].float().cpu().numpy()
+            for x, s in (("q", hq), ("k", hq), ("v", hv), ("log_alpha", hv), ("beta", hv))}
+    init = inp["init_state"][:, hv].cpu().numpy()
+    do_tail, dfin = np64(seeds["d_o"][T - L:, hv]), np64(seeds["d_final"][:, hv])
+    del inp, seeds, g
+    torch.cuda.empty_cache()
+    say("  oracle: C forward to T - L, NumPy backward over the tail")
+    _, s_mid = CR.recurrent_form1(*(head[x][:T - L] for x in ("q", "k", "v", "log_alpha", "beta")),
+                                  init_state=init, threads=3)
+    want = O.recurrent_form1_backward(**{x: head[x][T - L:].astype(np.float64) for x in head},
+                                      do=do_tail, dfinal=dfin, init_state=s_mid)
+    bad = []
+    for name in got:
+        rel = np.linalg.norm(got[name] - want[name]) / np.linalg.norm(want[name])
+        mx = np.abs(got[name] - want[name]).max() / np.abs(want[name]).max()
+        say(f"  {name}: rel-L2 {rel:.2e} max {mx:.2e}")
+        if not (np.isfinite(got[name]).all() and rel <= 1e-2 and mx <= 2e-2):
+            bad.append(name)
+    assert not bad, bad
 
 
 def test_decode_beyond_32bit_state_offsets():

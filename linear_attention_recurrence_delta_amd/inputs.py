@@ -258,26 +258,28 @@ def make_prefill_device(seed, seq_len, h_qk, h_v, d, device, dtype=torch.bfloat1
     return dict(q=q, k=k, v=v, log_alpha=la, beta=beta, init_state=init, cu_seqlens=None)
 
 
-def make_decode_device(seed, batch, h_qk, h_v, d, device, dtype=torch.bfloat16):
-    """One decode step of the recipe above for `batch` sequences, drawn on
+def make_decode_device(seed, batch, h_qk, h_v, d, device, dtype=torch.bfloat16, steps=None):
+    """Decode inputs of the recipe above for `batch` sequences, drawn on
     `device` like make_prefill_device (order: state0, q, k, v, log_alpha,
-    beta). Keys as make_decode without the step axis: state0
-    [batch,h_v,d,d]; q, k [batch,h_qk,d]; v [batch,h_v,d]; log_alpha, beta
-    [batch,h_v]."""
+    beta). With steps=None, one step: state0 [batch,h_v,d,d]; q, k
+    [batch,h_qk,d]; v [batch,h_v,d]; log_alpha, beta [batch,h_v]. Otherwise
+    the per-step inputs are stacked on a leading axis of `steps`, as in
+    make_decode."""
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     state0 = 0.02 * torch.randn((batch, h_v, d, d), generator=g, device=device)
+    lead = () if steps is None else (int(steps),)
 
     def unit(shape):
         x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
         x /= torch.linalg.vector_norm(x, dim=-1, keepdim=True)
         return x.to(dtype)
 
-    q = unit((batch, h_qk, d))
-    k = unit((batch, h_qk, d))
-    v = torch.randn((batch, h_v, d), generator=g, device=device, dtype=torch.float32).to(dtype)
-    la = -torch.nn.functional.softplus(torch.randn((batch, h_v), generator=g, device=device) - 2.0)
-    beta = torch.sigmoid(torch.randn((batch, h_v), generator=g, device=device))
+    q = unit(lead + (batch, h_qk, d))
+    k = unit(lead + (batch, h_qk, d))
+    v = torch.randn(lead + (batch, h_v, d), generator=g, device=device, dtype=torch.float32).to(dtype)
+    la = -torch.nn.functional.softplus(torch.randn(lead + (batch, h_v), generator=g, device=device) - 2.0)
+    beta = torch.sigmoid(torch.randn(lead + (batch, h_v), generator=g, device=device))
     return dict(state0=state0, q=q, k=k, v=v, log_alpha=la, beta=beta)
 
 

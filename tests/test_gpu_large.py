@@ -14,7 +14,9 @@ the prefill and decode kernels must be formed in 64 bits.
   forward recurrence to their start and its backpropagation over them.
 - One decode step over 4,096 sequences (the fp32 state, 12.9 GB, holds
   3.2e9 elements): the last three sequences, on every V head, against the
-  oracle's single step.
+  oracle's single step; and four drafted tokens over the same batch with a
+  snapshot of the state after each (1.3e10 snapshot elements), against four
+  successive oracle steps.
 
 Inputs are drawn on the device (inputs.make_prefill_device,
 make_decode_device: the same recipe in float32 draws); only the compared
@@ -157,3 +159,29 @@ def test_decode_beyond_32bit_state_offsets():
     want_o, want_s = O.decode_step(before, *args)
     check(got_o, want_o, "decode o, last three sequences")
     check(got_s, want_s, "decode state, last three sequences")
+
+
+def test_decode_multi_snapshots_beyond_32bit_offsets():
+    # four drafted tokens per sequence with a snapshot of the state after
+    # each (1.3e10 snapshot elements, 51.5 GB): the last three sequences'
+    # outputs and snapshots against four successive oracle steps
+    N, K = 4096, 4
+    assert K * N * HV * D * D > 2**33
+    need_free((K + 1) * N * HV * D * D * 4 + (2 << 30))
+    say(f"decode verify N={N} K={K}: snapshots {K * N * HV * D * D * 4 / 2**30:.1f} GiB")
+    dec = I.make_decode_device(95, N, HQ, HV, D, DEV, steps=K)
+    snaps = torch.empty((K, N, HV, D, D), dtype=torch.float32, device=DEV)
+    last = slice(N - 3, N)
+    state = dec["state0"][last].cpu().numpy().astype(np.float64)
+    args = [dec[x][:, last].float().cpu().numpy().astype(np.float64)
+            for x in ("q", "k", "v", "log_alpha", "beta")]
+    o = gdn.gdn_decode_multi(dec["q"], dec["k"], dec["v"], dec["log_alpha"], dec["beta"], dec["state0"],
+                             snapshots=snaps)
+    torch.cuda.synchronize()
+    got_o, got_s = np64(o[:, last]), np64(snaps[:, last])
+    del dec, o, snaps
+    torch.cuda.empty_cache()
+    for j in range(K):
+        want_o, state = O.decode_step(state, *(x[j] for x in args))
+        check(got_o[j], want_o, f"verify token {j} o, last three sequences")
+        check(got_s[j], state, f"snapshot {j}, last three sequences")

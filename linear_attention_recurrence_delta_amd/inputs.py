@@ -233,16 +233,22 @@ WORKLOADS = {
 }
 
 
-def make_prefill_device(seed, seq_len, h_qk, h_v, d, device, dtype=torch.bfloat16):
-    """One sequence of the recipe above drawn on `device` (for inputs too
-    large to draw on the host): torch.Generator(device) seeded with `seed`,
-    float32 draws in the order q, k, v, log_alpha, beta, init (N(0, 0.02^2)),
-    q and k normalised in float32, then q/k/v cast to `dtype`. Same keys and
-    shapes as make_prefill with init="randn" (cu_seqlens None); the tensors
-    stay on `device`."""
+def make_prefill_device(seed, seq_lens, h_qk, h_v, d, device, dtype=torch.bfloat16):
+    """The recipe above drawn on `device` (for inputs too large to draw on
+    the host): torch.Generator(device) seeded with `seed`, float32 draws in
+    the order q, k, v, log_alpha, beta, init (N(0, 0.02^2) per sequence), q
+    and k normalised in float32, then q/k/v cast to `dtype`. `seq_lens` is
+    one length (one sequence, cu_seqlens None) or a list of lengths packed
+    via cu_seqlens (int32 on `device`). Same keys and shapes as make_prefill
+    with init="randn"; the tensors stay on `device`."""
     g = torch.Generator(device=device)
     g.manual_seed(seed)
-    T = int(seq_len)
+    if isinstance(seq_lens, (int, np.integer)):
+        lens, cu = [int(seq_lens)], None
+    else:
+        lens = [int(x) for x in seq_lens]
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=device)
+    T = int(sum(lens))
 
     def unit(shape):
         x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
@@ -254,8 +260,8 @@ def make_prefill_device(seed, seq_len, h_qk, h_v, d, device, dtype=torch.bfloat1
     v = torch.randn((T, h_v, d), generator=g, device=device, dtype=torch.float32).to(dtype)
     la = -torch.nn.functional.softplus(torch.randn((T, h_v), generator=g, device=device) - 2.0)
     beta = torch.sigmoid(torch.randn((T, h_v), generator=g, device=device))
-    init = 0.02 * torch.randn((1, h_v, d, d), generator=g, device=device)
-    return dict(q=q, k=k, v=v, log_alpha=la, beta=beta, init_state=init, cu_seqlens=None)
+    init = 0.02 * torch.randn((len(lens), h_v, d, d), generator=g, device=device)
+    return dict(q=q, k=k, v=v, log_alpha=la, beta=beta, init_state=init, cu_seqlens=cu)
 
 
 def make_decode_device(seed, batch, h_qk, h_v, d, device, dtype=torch.bfloat16, steps=None):

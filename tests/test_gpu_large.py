@@ -7,7 +7,9 @@ the prefill and decode kernels must be formed in 64 bits.
   beyond a 32-bit element offset. The last QK group (V heads 45..47, the
   largest offsets at every token) is compared on every token and its final
   state with the fp64 form-1 recurrence (the C oracle), within the bf16
-  tolerances of the other parity tests.
+  tolerances of the other parity tests. Likewise 96 packed sequences (about
+  600K tokens, with an empty and a one-token sequence) on every token and
+  every final state of that group.
 - The backward pass of a 400,037-token sequence at the same layout (about
   80 GB with its workspace): the gradients of the last 512 tokens of the
   last QK group, which lie past 2^31 elements, against the oracle's
@@ -93,6 +95,41 @@ def test_prefill_beyond_32bit_element_offsets():
     tail = T - (1 << 19)
     check(got_o[tail:], want_o[tail:], "o, V heads 45..47, tokens past 2^19")
     check(got_f, want_f, "final state, V heads 45..47")
+
+
+def test_varlen_prefill_beyond_32bit_element_offsets():
+    # 96 packed sequences (one empty, one of one token, the rest uniform in
+    # [1, 12500] tokens), about 600K tokens: the chunk table of many
+    # sequences at large offsets. The last QK group on every token and
+    # every sequence's final state, against the C oracle.
+    lens = [int(x) for x in I.make_varlen_lengths(96, 94, 1, 12500)]
+    lens = lens[:40] + [0, 1] + lens[40:]
+    T = sum(lens)
+    assert T * HV * D > 2**31 and lens[-1] > 0
+    dims = gdn.make_dims(len(lens), T, HQ, HV, D, D, C, torch.bfloat16)
+    ws_bytes = gdn.gdn_chunk_fwd_workspace_bytes(dims)
+    io = 2 * T * HQ * D * 2 + 2 * T * HV * D * 2 + 2 * T * HV * 4
+    need_free(io + ws_bytes + T * HV * D * 4 + (4 << 30))
+    say(f"varlen prefill: {len(lens)} sequences, T={T}, heads {HQ}/{HV} d={D}")
+    inp = I.make_prefill_device(96, lens, HQ, HV, D, DEV)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    o, fin = gdn.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                               inp["init_state"], inp["cu_seqlens"], chunk=C, workspace=ws)
+    torch.cuda.synchronize()
+    del ws
+    hq, hv = slice(HQ - 1, HQ), slice(HV - 3, HV)
+    got_o, got_f = np64(o[:, hv]), np64(fin[:, hv])
+    args = [inp[x][:, s].float().cpu().numpy()
+            for x, s in (("q", hq), ("k", hq), ("v", hv), ("log_alpha", hv), ("beta", hv))]
+    init = inp["init_state"][:, hv].cpu().numpy()
+    cu = inp["cu_seqlens"].cpu().numpy()
+    del inp, o, fin
+    torch.cuda.empty_cache()
+    want_o, want_f = CR.recurrent_form1(*args, init_state=init, cu_seqlens=cu)
+    check(got_o, want_o, "o, V heads 45..47, every token")
+    last = slice(int(cu[-2]), int(cu[-1]))
+    check(got_o[last], want_o[last], "o, V heads 45..47, the last sequence")
+    check(got_f, want_f, "final states, V heads 45..47, every sequence")
 
 
 def test_backward_beyond_32bit_element_offsets():

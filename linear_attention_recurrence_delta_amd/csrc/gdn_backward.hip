@@ -468,6 +468,11 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
   auto frag_row = [&](const E* m, int ld, int row0, int s, int kext) __attribute__((always_inline)) {
     return load_frag<E>(m + (row0 + l16) * ld + 32 * s, quad, kext - 32 * s);
   };
+  // the same with 8 consecutive contraction indices per lane (load_frag8),
+  // for the products whose other operand is read that way too
+  auto frag_row8 = [&](const E* m, int ld, int row0, int s, int kext) __attribute__((always_inline)) {
+    return load_frag8<E>(m + (row0 + l16) * ld + 32 * s, quad, kext - 32 * s);
+  };
   // (a bf16 column fragment is two transposing LDS reads, one per half of
   // 16 rows: in each 16-lane row of the wave, lane 4 e + j addresses the 4
   // elements at row k0 + e, columns col0 + 4 j .. + 3, and lane i receives
@@ -575,15 +580,17 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
       }
     }
     // the state fragments of d-tile dt (chunk-start state S0 and dS_L, as
-    // fragments of their transposes) and the K, Q elements of its tiles
+    // fragments of their transposes) and the K, Q elements of its tiles.
+    // The products below contract them with rows staged in LDS, so both
+    // operands take 8 consecutive columns per lane: one 16-byte load each
     const E* scg = static_cast<const E*>(a.sc) + ch * D * D;
     const E* dsg = static_cast<const E*>(a.dsl) + ch * D * D;
     Frag<E> bs[DKS], bl[DKS], qe[CKS], ke[CKS];
     auto load_dtile = [&](int dt) __attribute__((always_inline)) {
 #pragma unroll
       for (int ks = 0; ks < DKS; ++ks) {
-        bs[ks] = load_frag<E>(scg + (16 * dt + l16) * D + 32 * ks, quad, D - 32 * ks);
-        bl[ks] = load_frag<E>(dsg + (16 * dt + l16) * D + 32 * ks, quad, D - 32 * ks);
+        bs[ks] = load_frag8<E>(scg + (16 * dt + l16) * D + 32 * ks, quad, D - 32 * ks);
+        bl[ks] = load_frag8<E>(dsg + (16 * dt + l16) * D + 32 * ks, quad, D - 32 * ks);
       }
 #pragma unroll
       for (int s = 0; s < CKS; ++s) {
@@ -634,9 +641,9 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         f32x4 aq = zero4(), ak = zero4(), aw = zero4();
 #pragma unroll
         for (int ks = 0; ks < DKS; ++ks) {
-          aq = mma(frag_row(sm.u1.r1, KLD, 16 * rt, ks, D), bs[ks], aq);
-          ak = mma(frag_row(sm.r2, KLD, 16 * rt, ks, D), bl[ks], ak);
-          aw = mma(frag_row(sm.r3, KLD, 16 * rt, ks, D), bs[ks], aw);
+          aq = mma(frag_row8(sm.u1.r1, KLD, 16 * rt, ks, D), bs[ks], aq);
+          ak = mma(frag_row8(sm.r2, KLD, 16 * rt, ks, D), bl[ks], ak);
+          aw = mma(frag_row8(sm.r3, KLD, 16 * rt, ks, D), bs[ks], aw);
         }
         dW[u] = -aw;
         // K and Q elements (16 rt + 4 quad + i, 16 dt + l16): fragment
@@ -687,14 +694,14 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
 #pragma unroll
       for (int s2 = 0; s2 < CKS; ++s2) pvf[s2] = ptf[(jt * CKS + s2) * 64 + lane];
 #pragma unroll
-      for (int ks = 0; ks < DKS; ++ks) ub[ks] = frag_row(sm.r2, KLD, 16 * jt, ks, D);
+      for (int ks = 0; ks < DKS; ++ks) ub[ks] = frag_row8(sm.r2, KLD, 16 * jt, ks, D);
       const int j = 16 * jt + l16;
       float colp = 0.f, m2v[4 * CT];
 #pragma unroll
       for (int rt = 0; rt < CT; ++rt) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int ks = 0; ks < DKS; ++ks) acc = mma(frag_row(sm.u1.r1, KLD, 16 * rt, ks, D), ub[ks], acc);
+        for (int ks = 0; ks < DKS; ++ks) acc = mma(frag_row8(sm.u1.r1, KLD, 16 * rt, ks, D), ub[ks], acc);
         // P[r][j] for this tile's elements: fragment (jt, rt/2) of P^T holds
         // row 16 rt + 4 quad + i at element i (+4 for an odd rt)
         const Frag<E> pv = pvf[rt >> 1];
@@ -750,7 +757,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
 #pragma unroll
       for (int ks = 0; ks < DKS; ++ks) kb[ks] = kff[(it * DKS + ks) * 64 + lane];
 #pragma unroll
-      for (int ks = 0; ks < DKS; ++ks) vb[ks] = frag_row(sm.u1.r1, KLD, 16 * it, ks, D);
+      for (int ks = 0; ks < DKS; ++ks) vb[ks] = frag_row8(sm.u1.r1, KLD, 16 * it, ks, D);
       const int i = 16 * it + l16;
       const float bi = sm.b[i], bgi = sm.b[i] * sm.ea[i];
 #pragma unroll
@@ -758,7 +765,7 @@ __global__ __launch_bounds__(kGradBlock, 2) void gdn_kb_grad(const PrefillArgs a
         f32x4 a1 = zero4(), a2 = zero4();
 #pragma unroll
         for (int ks = 0; ks < DKS; ++ks) {
-          a1 = mma(frag_row(sm.r3, KLD, 16 * rt, ks, D), vb[ks], a1);
+          a1 = mma(frag_row8(sm.r3, KLD, 16 * rt, ks, D), vb[ks], a1);
           a2 = mma(frag_row(sm.r2, KLD, 16 * rt, ks, D), kb[ks], a2);
         }
 #pragma unroll

@@ -79,6 +79,20 @@ __device__ __forceinline__ Frag<E> load_frag(const E* row, int quad, int kext) {
   return join<E>(lo, hi);
 }
 
+// The same fragment with the contraction index in another order: lane quad
+// q holds the 8 consecutive elements k0 + 8 q .. k0 + 8 q + 7 (one 16-byte
+// access for bf16), zero where 8 q >= kext. For a product whose other
+// operand is read the same way: the MFMA sums over k, so the two operands
+// need only agree on its order. `row` must be 16-byte aligned (32-byte for
+// fp32 elements).
+template <typename E>
+__device__ __forceinline__ Frag<E> load_frag8(const E* row, int quad, int kext) {
+  Frag<E> z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = to_e<E>(0.f);
+  return (8 * quad < kext) ? *reinterpret_cast<const Frag<E>*>(row + 8 * quad) : z;
+}
+
 // Same, with the whole row zero when `valid` is false (rows past the end of
 // a partial chunk).
 template <typename E>
